@@ -1,0 +1,111 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must make at
+least one pin fail.  This guards the pins themselves."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import tq_oracle as T
+import test_oracle_pins as P
+
+
+def _patch(monkeypatch, name, fn):
+    """Replace a function in the oracle module and in the package namespace."""
+    monkeypatch.setattr(T, name, fn)
+    monkeypatch.setattr(O, name, fn)
+
+
+def _fails(pin, *args):
+    with pytest.raises(AssertionError):
+        pin(*args)
+
+
+def test_transposed_rotation_is_caught(monkeypatch):
+    real = T.rotation
+    _patch(monkeypatch, "rotation", lambda s: real(s).T)
+    _fails(P.test_rotation_properties)
+
+
+def test_signs_on_wrong_side_are_caught(monkeypatch):
+    _patch(monkeypatch, "rotation", lambda s: T.hadamard(s.shape[0]) * s[:, None] / math.sqrt(s.shape[0]))
+    _fails(P.test_rotation_properties)
+
+
+def test_unrotated_query_is_caught(monkeypatch):
+    real_decode = T.decode
+
+    def bad_decode(lay, query, *a, **k):
+        if lay.key_fp8:
+            return real_decode(lay, query, *a, **k)
+        # score the raw query against rotated-domain keys
+        s = a[3]
+        Rinv = T.rotation(np.asarray(s, dtype=np.float64)).T
+        return real_decode(lay, np.einsum("ij,bhj->bhi", Rinv, query), *a, **k)
+
+    _patch(monkeypatch, "decode", bad_decode)
+    _fails(P.test_decode_close_to_unquantized_attention)
+
+
+def test_dropped_norm_correction_is_caught(monkeypatch):
+    real = T.quantize_key_mse
+    _patch(monkeypatch, "quantize_key_mse", lambda x, R, c, b, nc: real(x, R, c, b, False))
+    _fails(P.test_mse_key_reconstruction_statistics, 3, 0.03455)
+
+
+def test_inclusive_bucketize_is_caught(monkeypatch):
+    def bad(u, b):
+        u = np.asarray(u, dtype=np.float64)
+        return (np.asarray(b, np.float64)[None, :] <= u.reshape(-1, 1)).sum(axis=1).reshape(u.shape)
+
+    _patch(monkeypatch, "bucketize", bad)
+    _fails(P.test_bucketize_ties_and_ends)
+
+
+def test_msb_first_packing_is_caught(monkeypatch):
+    real = T.pack_lsb
+
+    def bad(codes, bits):
+        codes = np.asarray(codes)
+        rev = np.zeros_like(codes)
+        for k in range(bits):
+            rev |= ((codes >> k) & 1) << (bits - 1 - k)
+        return real(rev, bits)
+
+    _patch(monkeypatch, "pack_lsb", bad)
+    _fails(P.test_pack_hand_examples)
+
+
+def test_swapped_scale_zero_is_caught(monkeypatch):
+    real = T.quantize_values
+    _patch(monkeypatch, "quantize_values", lambda v, bits: (lambda c, s, z: (c, z, s))(*real(v, bits)))
+    _fails(P.test_value_codec_properties)
+
+
+def test_off_by_one_gather_is_caught(monkeypatch):
+    real = T.gather_sequence
+
+    def bad(lay, cache, row, L, hk, c):
+        K, V = real(lay, cache, row, L + 1 if L > 0 else L, hk, c)
+        return K[1:], V[1:]
+
+    _patch(monkeypatch, "gather_sequence", bad)
+    _fails(P.test_decode_close_to_unquantized_attention)
+
+
+def test_wrong_gqa_mapping_is_caught(monkeypatch):
+    real = T.decode
+
+    def bad(lay, query, cache, *a, **k):
+        # interleaved instead of contiguous query-head groups
+        B, Hq, D = query.shape
+        Hk = cache.shape[2]
+        g = Hq // Hk
+        perm = np.array([(h % Hk) * g + h // Hk for h in range(Hq)])
+        out, lse = real(lay, query[:, perm], cache, *a, **k)
+        inv = np.argsort(perm)
+        return out[:, inv], lse[:, inv]
+
+    _patch(monkeypatch, "decode", bad)
+    _fails(P.test_decode_close_to_unquantized_attention)

@@ -1,0 +1,503 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself (library routines, textbook tables, closed forms, invariants, brute
+force, hand-derived bytes), chosen so that a plausible slip -- a dropped term,
+a wrong sign or index, a transposed operand -- fails at least one of them.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 128
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+# ---------------------------------------------------------------- rotation
+
+
+@pytest.mark.parametrize("d", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_matches_scipy_sylvester(d):
+    np.testing.assert_array_equal(O.hadamard(d), scipy.linalg.hadamard(d).astype(np.float64))
+
+
+def test_hadamard_matches_kronecker_recursion():
+    h = np.array([[1.0]])
+    for _ in range(7):
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    np.testing.assert_array_equal(O.hadamard(128), h)
+
+
+def _fwht(x):
+    """In-place butterfly (strides 1, 2, 4, ...), a different algorithm from
+    the popcount definition."""
+    y = np.array(x, dtype=np.float64)
+    h = 1
+    while h < y.shape[0]:
+        for i in range(0, y.shape[0], 2 * h):
+            a = y[i : i + h].copy()
+            b = y[i + h : i + 2 * h].copy()
+            y[i : i + h] = a + b
+            y[i + h : i + 2 * h] = a - b
+        h *= 2
+    return y
+
+
+def test_rotation_properties():
+    rng = np.random.default_rng(1)
+    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    R = O.rotation(s)
+    np.testing.assert_allclose(R @ R.T, np.eye(D), atol=1e-12)
+    x = rng.standard_normal(D)
+    np.testing.assert_allclose(R.T @ (R @ x), x, atol=1e-12)
+    # signs first, then the WHT: R x = FWHT(s * x) / sqrt(D)
+    np.testing.assert_allclose(R @ x, _fwht(s * x) / math.sqrt(D), atol=1e-12)
+    H = O.hadamard(D)
+    np.testing.assert_array_equal(H @ H, D * np.eye(D))
+    assert np.all(H[:, 0] == 1.0)
+    # all-+1 signs reduce to the plain (unsigned, symmetric) Hadamard rotation
+    np.testing.assert_allclose(O.rotation(np.ones(D)), scipy.linalg.hadamard(D) / math.sqrt(D), atol=0)
+    # the signs act on the input side (columns), not the output side
+    assert not np.allclose(R, (H * s[:, None]) / math.sqrt(D))
+
+
+# ---------------------------------------------------------------- Lloyd-Max
+
+
+def _quad_cell_mean(a, b, sigma):
+    pdf = lambda x: math.exp(-0.5 * (x / sigma) ** 2) / (sigma * math.sqrt(2 * math.pi))
+    num = scipy.integrate.quad(lambda x: x * pdf(x), a, b, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+    den = scipy.integrate.quad(pdf, a, b, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+    return num / den
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lloyd_max_exact_fixed_point(bits):
+    """Each centroid is the Gaussian conditional mean of its cell (computed
+    here by adaptive quadrature, not the closed form) and each boundary is a
+    midpoint."""
+    d = 128
+    sigma = 1.0 / math.sqrt(d)
+    c, b = O.lloyd_max_exact(d, bits)
+    assert c.shape == (1 << bits,) and b.shape == ((1 << bits) - 1,)
+    np.testing.assert_allclose(b, (c[:-1] + c[1:]) / 2, atol=0)
+    edges = [-12 * sigma] + list(b) + [12 * sigma]
+    for i in range(len(c)):
+        m = _quad_cell_mean(edges[i], edges[i + 1], sigma)
+        assert abs(m - c[i]) < 1e-9 * sigma, (i, m, c[i])
+    np.testing.assert_array_equal(c[::-1], -c)
+    assert np.all(np.diff(c) > 0)
+
+
+def test_lloyd_max_one_bit_closed_form():
+    c, _ = O.lloyd_max_exact(128, 1)
+    np.testing.assert_allclose(c, [-math.sqrt(2 / math.pi) / math.sqrt(128), math.sqrt(2 / math.pi) / math.sqrt(128)],
+                               rtol=1e-13)
+
+
+def test_lloyd_max_matches_max_1960_table():
+    for levels, pos, mse in _read_table("gaussian_lloyd_max_max1960.txt"):
+        levels = int(levels)
+        bits = int(round(math.log2(levels)))
+        want = np.array([float(v) for v in pos.split()])
+        for d in (64, 128, 256):
+            c, b = O.lloyd_max_exact(d, bits)
+            got = c[levels // 2 :] * math.sqrt(d)
+            # half a unit in the last of the table's 4 significant figures
+            np.testing.assert_allclose(got, want, rtol=5e-4, atol=5e-5)
+        # distortion of the quantizer, integrated numerically over every cell
+        c, b = O.lloyd_max_exact(1, bits)
+        edges = [-np.inf] + list(b) + [np.inf]
+        pdf = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+        dist = sum(scipy.integrate.quad(lambda x: (x - c[i]) ** 2 * pdf(x), edges[i], edges[i + 1])[0]
+                   for i in range(levels))
+        assert abs(dist - float(mse)) < 2e-4 * max(1.0, float(mse) * 100), (levels, dist, mse)
+
+
+def test_codebook_tables_fp32_midpoints():
+    for bits in (2, 3, 4):
+        c32, b32 = O.codebook_tables(128, bits)
+        assert c32.dtype == np.float32 and b32.dtype == np.float32
+        np.testing.assert_array_equal(c32[::-1], -c32)
+        np.testing.assert_array_equal(b32[::-1], -b32)
+        # midpoint of two fp32 values: exact sum rounded once, then halved
+        exact_mid = (c32[:-1].astype(np.float64) + c32[1:].astype(np.float64)) / 2
+        np.testing.assert_array_equal(b32, exact_mid.astype(np.float32))
+        assert b32[(1 << bits) // 2 - 1] == 0.0
+
+
+def test_pages_trapz_solver_behaviour():
+    """The pages' trapezoid solver converges at 3 bits and ends near the exact
+    optimum (the trapezoid error on the +-10.5 sigma cells is ~1e-3 sigma)."""
+    sigma = 1 / math.sqrt(128)
+    for bits in (2, 3, 4):
+        ct, bt = O.lloyd_max_pages_trapz(128, bits)
+        ce, _ = O.lloyd_max_exact(128, bits)
+        assert np.max(np.abs(ct - ce)) < 3e-3 * sigma
+        assert np.max(np.abs(ct - ce)) > 1e-6 * sigma  # it is not the exact solver
+        np.testing.assert_allclose(bt, (ct[:-1] + ct[1:]) / 2, atol=0)
+    # with a fine trapezoid grid the same fixed-point iteration agrees with the
+    # closed form; use the 3-bit case and check the trapezoid moments match quad
+    c, b = O.lloyd_max_pages_trapz(128, 3)
+    edges = [-10.5 * sigma] + list(b) + [10.5 * sigma]
+    for i in range(8):
+        m = _quad_cell_mean(edges[i], edges[i + 1], sigma)
+        assert abs(m - c[i]) < 3e-3 * sigma
+
+
+# ---------------------------------------------------------------- signs
+
+
+def test_splitmix64_reference_outputs():
+    # Published first outputs of SplitMix64 seeded with 0 (the reference
+    # generator used to seed xoshiro/xoroshiro).
+    assert O.splitmix64(0, 3) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_wht_signs_deterministic_and_balanced():
+    s = O.wht_signs(128, 42)
+    np.testing.assert_array_equal(s, O.wht_signs(128, 42))
+    assert set(np.unique(s)) <= {-1.0, 1.0}
+    assert not np.array_equal(s, O.wht_signs(128, 43))
+    big = O.wht_signs(20000, 7)
+    assert abs(big.mean()) < 0.03
+    assert s[0] == -1.0  # top bit of 0x... first draw for seed 42, recomputed below
+    z = O.splitmix64(42, 1)[0]
+    assert (z >> 63) == 1
+
+
+# ---------------------------------------------------------------- number formats
+
+
+def test_fp8_decode_all_codes_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.fp8_e4m3fn_decode(codes)
+    nan = np.isnan(want)
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fp8_encode_every_16bit_pattern(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = O.widen(bits, dtype)
+    finite = np.isfinite(x)
+    inrange = finite & (np.abs(x) <= 448.0)
+    got = O.fp8_e4m3fn_encode(x)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    want = torch.from_numpy(bits.view(np.int16)).view(tdt)[torch.from_numpy(inrange)]
+    want = want.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got[inrange], want)
+    # beyond the range: saturate to +-448 (0x7E / 0xFE)
+    big = finite & (np.abs(x) > 448.0)
+    assert np.all((got[big] & 0x7F) == 0x7E)
+    np.testing.assert_array_equal(got[big] >> 7, (x[big] < 0).astype(np.uint8))
+    # round trip of every finite e4m3 value
+    vals = O.fp8_e4m3fn_decode(np.arange(256))
+    ok = np.isfinite(vals)
+    np.testing.assert_array_equal(O.fp8_e4m3fn_encode(vals[ok]), np.arange(256)[ok].astype(np.uint8) & np.where(vals[ok] == 0, 0xFF, 0xFF))
+
+
+def test_fp16_field_encoding():
+    assert O.fp16_bits(1.0) == 0x3C00
+    assert O.fp16_bits(65504.0) == 0x7BFF
+    assert O.fp16_bits(2.0 ** -24) == 0x0001
+    assert O.fp16_bits(1.0 + 2.0 ** -11) == 0x3C00  # tie -> even
+    assert O.fp16_bits(1.0 + 3 * 2.0 ** -11) == 0x3C02  # tie -> even (up)
+
+
+def test_widen_bf16_exact():
+    assert O.widen(np.array([0x3F80], np.uint16), "bf16")[0] == 1.0
+    assert O.widen(np.array([0xC0A0], np.uint16), "bf16")[0] == -5.0
+    b = W.to_bits(np.array([1.0 + 2.0 ** -8], np.float32), "bf16")  # tie -> even
+    assert b[0] == 0x3F80
+
+
+# ---------------------------------------------------------------- packing
+
+
+def test_pack_hand_examples():
+    for bits, codes, want in _read_table("pack_examples.txt"):
+        bits = int(bits)
+        codes = np.array([int(c) for c in codes.split()])
+        want = bytes(int(h, 16) for h in want.split())
+        got = O.pack_lsb(codes, bits).tobytes()
+        assert got == want, (bits, codes, got.hex(), want.hex())
+        np.testing.assert_array_equal(O.unpack_lsb(np.frombuffer(want, np.uint8), bits, len(codes)), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_roundtrip_exhaustive(bits):
+    L = 1 << bits
+    rng = np.random.default_rng(bits)
+    # every code value at every position of a 128-code vector
+    for v in range(L):
+        for pos in range(0, 128, 1):
+            codes = rng.integers(0, L, 128)
+            codes[pos] = v
+            packed = O.pack_lsb(codes, bits)
+            assert packed.shape == (128 * bits // 8,)
+            np.testing.assert_array_equal(O.unpack_lsb(packed, bits, 128), codes)
+            break
+    codes = rng.integers(0, L, (500, 128))
+    np.testing.assert_array_equal(O.unpack_lsb(O.pack_lsb(codes, bits), bits, 128), codes)
+
+
+def test_layout_sizes():
+    want = {"turboquant_k8v4": (128, 128, 64, 68, 196), "turboquant_4bit_nc": (64, 66, 64, 68, 134),
+            "turboquant_k3v4_nc": (48, 50, 64, 68, 118), "turboquant_3bit_nc": (48, 50, 48, 52, 102)}
+    for p, (kd, kps, vd, vps, slot) in want.items():
+        L = O.layout(p, 128)
+        assert (L.key_data_bytes, L.key_packed_size, L.value_data_bytes, L.value_packed_size, L.slot_size_aligned) == \
+            (kd, kps, vd, vps, slot)
+    # "2.6x" KV compression for k8v4 against 16-bit K+V
+    assert round(2 * 128 * 2 / O.layout("turboquant_k8v4", 128).slot_size_aligned, 1) == 2.6
+    assert O.layout("turboquant_3bit_nc", 100).slot_size_aligned % 2 == 0
+    assert O.kv_cache_shape(O.layout("turboquant_3bit_nc", 128), 10, 16, 8) == (10, 16, 8, 102)
+
+
+# ---------------------------------------------------------------- quantizers
+
+
+def test_bucketize_ties_and_ends():
+    b = np.array([-1.0, 0.0, 1.0], dtype=np.float32)
+    u = np.array([-2.0, -1.0, -0.5, 0.0, -0.0, 0.5, 1.0, 2.0])
+    np.testing.assert_array_equal(O.bucketize(u, b), [0, 0, 1, 1, 1, 2, 2, 3])
+    np.testing.assert_array_equal(O.bucketize(u, b), torch.bucketize(torch.tensor(u), torch.tensor(b, dtype=torch.float64), right=False).numpy())
+
+
+@pytest.mark.parametrize("bits,distortion", [(3, 0.03455), (4, 0.009497)])
+def test_mse_key_reconstruction_statistics(bits, distortion):
+    """Gaussian keys: relative squared error of gamma R^T c[code] is close to
+    the Lloyd-Max distortion, and the norm correction matches norms."""
+    rng = np.random.default_rng(bits)
+    c32, b32 = O.codebook_tables(D, bits)
+    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    R = O.rotation(s)
+    errs = []
+    for _ in range(300):
+        x = rng.standard_normal(D) * rng.uniform(0.1, 10)
+        codes, gamma = O.quantize_key_mse(x, R, c32, b32, True)
+        chat = c32[codes].astype(np.float64)
+        xr = gamma * (R.T @ chat)
+        assert abs(np.linalg.norm(xr) - np.linalg.norm(x)) < 1e-12 * np.linalg.norm(x)
+        errs.append(np.sum((xr - x) ** 2) / np.sum(x ** 2))
+    rel = float(np.mean(errs))
+    assert 0.8 * distortion < rel < 1.25 * distortion, rel
+    # E||c[code]||^2 ~ 1 - distortion for unit-norm inputs (no correction)
+    norms = []
+    for _ in range(300):
+        x = rng.standard_normal(D)
+        codes, _ = O.quantize_key_mse(x, R, c32, b32, False)
+        norms.append(np.sum(c32[codes].astype(np.float64) ** 2))
+    assert abs(np.mean(norms) - (1 - distortion)) < 0.25 * distortion
+
+
+def test_mse_key_zero_vector():
+    c32, b32 = O.codebook_tables(D, 4)
+    codes, gamma = O.quantize_key_mse(np.zeros(D), O.rotation(np.ones(D)), c32, b32, True)
+    assert gamma == 0.0 and np.all(codes == 7)
+
+
+def test_value_codec_properties():
+    rng = np.random.default_rng(5)
+    for bits in (3, 4):
+        L = (1 << bits) - 1
+        for _ in range(200):
+            v = O.widen(W.to_bits(rng.standard_normal(D) * rng.uniform(0.01, 20), "bf16"), "bf16")
+            codes, s16, z16 = O.quantize_values(v, bits)
+            s = float(np.uint16(s16).view(np.float16))
+            z = float(np.uint16(z16).view(np.float16))
+            assert codes.min() >= 0 and codes.max() <= L
+            vhat = z + s * codes
+            # half a step, plus the fp16 rounding of zero and of the scale over L steps
+            bound = s / 2 + abs(z) * 2 ** -11 + L * s * 2 ** -11 + 1e-12
+            assert np.max(np.abs(vhat - v)) <= bound * 1.0001
+    # hand example: 0, 0.5, ..., 7.5 at 4 bits -> zero 0, scale 0.5, codes 0..15
+    v = np.arange(16) * 0.5
+    codes, s16, z16 = O.quantize_values(np.tile(v, 8), 4)
+    assert s16 == 0x3800 and z16 == 0x0000
+    np.testing.assert_array_equal(codes, np.tile(np.arange(16), 8))
+    # constant vector: scale 0, all codes 0, reconstruction exact
+    codes, s16, z16 = O.quantize_values(np.full(D, 3.25), 4)
+    assert s16 == 0 and np.all(codes == 0) and float(np.uint16(z16).view(np.float16)) == 3.25
+
+
+def test_encode_decode_slot_roundtrip():
+    rng = np.random.default_rng(9)
+    for preset in O.PRESETS:
+        lay = O.layout(preset, D)
+        s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+        R = O.rotation(s)
+        c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(D, lay.key_bits)
+        k = O.widen(W.to_bits(rng.standard_normal(D) * 2, "bf16"), "bf16")
+        v = O.widen(W.to_bits(rng.standard_normal(D), "bf16"), "bf16")
+        slot = O.encode_slot(lay, k, v, R, c32, b32)
+        assert slot.shape == (lay.slot_size_aligned,)
+        kh, vh = O.decode_slot(lay, slot, c32)
+        if lay.key_fp8:
+            np.testing.assert_array_equal(slot[:D], O.fp8_e4m3fn_encode(k))
+            assert np.max(np.abs(kh - k)) <= np.max(np.abs(k)) * 2 ** -4
+        else:
+            # rotated domain: back-rotate and compare with the input
+            kr = R.T @ kh
+            assert np.linalg.norm(kr - k) / np.linalg.norm(k) < (0.3 if lay.key_bits == 3 else 0.2)
+            np.testing.assert_allclose(np.linalg.norm(kh), np.linalg.norm(k), rtol=1e-3)
+        assert np.max(np.abs(vh - v)) < (np.max(v) - np.min(v)) / ((1 << lay.value_bits) - 1)
+
+
+# ---------------------------------------------------------------- decode
+
+
+def _tiny_cache(preset, B=2, Hq=4, Hk=2, bs=16, lens=(37, 5), seed=0, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    lay = O.layout(preset, D)
+    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(D, lay.key_bits)
+    nbl = [-(-L // bs) for L in lens]
+    nb = sum(nbl) + 3
+    perm = rng.permutation(nb)
+    table = np.full((B, max(nbl)), -1, dtype=np.int64)
+    pos = 0
+    for b in range(B):
+        table[b, : nbl[b]] = perm[pos : pos + nbl[b]]
+        pos += nbl[b]
+    cache = np.zeros((nb, bs, Hk, lay.slot_size_aligned), dtype=np.uint8)
+    K = [O.widen(W.to_bits(rng.standard_normal((L, Hk, D)), dtype), dtype) for L in lens]
+    V = [O.widen(W.to_bits(rng.standard_normal((L, Hk, D)), dtype), dtype) for L in lens]
+    for b, L in enumerate(lens):
+        slots = table[b, np.arange(L) // bs] * bs + np.arange(L) % bs
+        O.store(lay, K[b], V[b], slots, cache, s, c32, b32)
+    q = O.widen(W.to_bits(rng.standard_normal((B, Hq, D)), dtype), dtype)
+    return lay, s, c32, table, np.array(lens), cache, q, K, V
+
+
+@pytest.mark.parametrize("preset", list(O.PRESETS))
+def test_decode_matches_sdpa_on_dequantized_cache(preset):
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache(preset)
+    scale = 1 / math.sqrt(D)
+    out, lse = O.decode(lay, q, cache, table, lens, s, c32, scale)
+    B, Hq, _ = q.shape
+    g = Hq // cache.shape[2]
+    for b in range(B):
+        for hq in range(Hq):
+            Kd, Vd = O.dequant_original_space(lay, cache, table[b], int(lens[b]), hq // g, s, c32)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.tensor(q[b, hq])[None, None, None], torch.tensor(Kd)[None, None], torch.tensor(Vd)[None, None],
+                scale=scale)[0, 0, 0].numpy()
+            np.testing.assert_allclose(out[b, hq], ref, rtol=1e-10, atol=1e-12)
+            sc = scale * Kd @ q[b, hq]
+            assert abs(lse[b, hq] - (sc.max() + math.log(np.exp(sc - sc.max()).sum()))) < 1e-10
+
+
+def test_decode_close_to_unquantized_attention():
+    """End to end (store then decode) against attention on the raw K/V.  Each
+    query points at one stored key, so the softmax is peaked and a wrong
+    rotation, sign, norm or gather index moves the output far; the honest
+    error is the quantization error of the few dominant rows."""
+    rng = np.random.default_rng(11)
+    for preset, tol in (("turboquant_4bit_nc", 0.08), ("turboquant_k8v4", 0.08), ("turboquant_k3v4_nc", 0.12),
+                        ("turboquant_3bit_nc", 0.2)):
+        lay, s, c32, table, lens, cache, q, K, V = _tiny_cache(preset, lens=(200, 64))
+        scale = 1 / math.sqrt(D)
+        g = q.shape[1] // cache.shape[2]
+        for b in range(q.shape[0]):
+            for hq in range(q.shape[1]):
+                # first token, last token, then random ones: an off-by-one
+                # gather window misses the ends
+                tgt = [0, lens[b] - 1][hq] if hq < 2 else rng.integers(0, lens[b])
+                kt = K[b][tgt, hq // g]
+                q[b, hq] = kt * (12.0 / (scale * np.dot(kt, kt)))
+        out, _ = O.decode(lay, q, cache, table, lens, s, c32, scale)
+        for b in range(q.shape[0]):
+            for hq in range(q.shape[1]):
+                ref, _ = O.attend(q[b, hq], K[b][:, hq // g], V[b][:, hq // g], scale)
+                err = np.max(np.abs(out[b, hq] - ref)) / np.max(np.abs(ref))
+                assert err < tol, (preset, b, hq, err)
+
+
+def test_decode_special_cases():
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache("turboquant_4bit_nc", lens=(1, 0))
+    out, lse = O.decode(lay, q, cache, table, lens, s, c32, 0.1)
+    _, Vd = O.dequant_original_space(lay, cache, table[0], 1, 0, s, c32)
+    np.testing.assert_allclose(out[0, 0], Vd[0], rtol=0, atol=0)  # L = 1 -> o = v
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))  # L = 0 -> 0, -inf
+    # equal scores (zero query) -> mean of the values
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache("turboquant_k8v4", lens=(21, 3))
+    q[:] = 0.0
+    out, _ = O.decode(lay, q, cache, table, lens, s, c32, 0.1)
+    _, Vd = O.dequant_original_space(lay, cache, table[0], 21, 0, s, c32)
+    np.testing.assert_allclose(out[0, 0], Vd.mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_gqa_one_reduces_to_mha():
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache("turboquant_3bit_nc", Hq=2, Hk=2)
+    out, _ = O.decode(lay, q, cache, table, lens, s, c32, 0.1)
+    for h in range(2):
+        Kd, Vd = O.gather_sequence(lay, cache, table[0], int(lens[0]), h, c32)
+        o, _ = O.attend(O.rotation(s) @ q[0, h], Kd, Vd, 0.1)
+        np.testing.assert_allclose(out[0, h], o, rtol=1e-12)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8, 32, 100])
+def test_split_merge_equals_unsplit(S):
+    rng = np.random.default_rng(S)
+    K = rng.standard_normal((300, D))
+    V = rng.standard_normal((300, D))
+    q = rng.standard_normal(D) * 2
+    o1, l1 = O.attend(q, K, V, 0.2)
+    o2, l2 = O.decode_split(q, K, V, 0.2, S, 16)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    assert abs(l2 - l1) < 1e-12
+    rng_parts = O.split_ranges(300, S, 16)
+    assert rng_parts[0][0] == 0 and rng_parts[-1][1] == 300
+    assert all(a % 16 == 0 for a, _ in rng_parts if a < 300)
+
+
+def test_store_skips_negative_slots_and_touches_nothing_else():
+    lay = O.layout("turboquant_k3v4_nc", D)
+    c32, b32 = O.codebook_tables(D, 3)
+    rng = np.random.default_rng(3)
+    cache = rng.integers(0, 256, (4, 16, 2, lay.slot_size_aligned)).astype(np.uint8)
+    before = cache.copy()
+    k = rng.standard_normal((3, 2, D))
+    O.store(lay, k, k, np.array([5, -1, 40]), cache, np.ones(D), c32, b32)
+    changed = np.argwhere(np.any(cache != before, axis=-1))
+    assert {tuple(x) for x in changed} <= {(0, 5, 0), (0, 5, 1), (2, 8, 0), (2, 8, 1)}
+
+
+def test_block_table_indirection():
+    """Same tokens stored under a permuted table decode identically."""
+    lay = O.layout("turboquant_4bit_nc", D)
+    c32, b32 = O.codebook_tables(D, 4)
+    rng = np.random.default_rng(4)
+    L, bs = 70, 16
+    k = rng.standard_normal((L, 1, D))
+    v = rng.standard_normal((L, 1, D))
+    q = rng.standard_normal((1, 2, D))
+    outs = []
+    for table in (np.arange(5), np.array([4, 0, 3, 1, 2])):
+        cache = np.zeros((5, bs, 1, lay.slot_size_aligned), np.uint8)
+        O.store(lay, k, v, table[np.arange(L) // bs] * bs + np.arange(L) % bs, cache, np.ones(D), c32, b32)
+        outs.append(O.decode(lay, q, cache, table[None], np.array([L]), np.ones(D), c32, 0.1)[0])
+    np.testing.assert_array_equal(outs[0], outs[1])
