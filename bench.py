@@ -1,0 +1,301 @@
+"""Benchmark of the TurboQuant decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline]
+
+A step is one decode step of one attention layer: tq_store of the step's new
+K/V token for every sequence (B tokens x Hk heads), then tq_decode_attention
+(stage 1 + stage 2) of one query per sequence over the whole compressed
+cache.  The headline workload is the Llama-3-8B-shaped layer (k8v4, 32
+sequences x 4096 tokens, 32/8 heads, block 16).  ``value`` is the effective
+decode-attention bandwidth: compressed-cache bytes the step reads
+(sum_b L_b * Hk * slot_size) over the step's wall time, inputs resident in HBM.
+
+Timing: HIP graphs of the step are replayed on torch's current stream,
+rotating over 3 copies of the cache (3 x 411 MB for the headline) so that the
+256 MB Infinity Cache cannot serve the next step's reads; K steps are
+bracketed by events after a synchronize.  The roofline figure times stage-1
+launches alone with events on the same stream.  The CPU baseline is the
+oracle (NumPy) decoding a bounded sample of the same workload.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+N_COPIES = 3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev16(torch, bits, dtype):
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return x.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+class DecodeBench:
+    """Device state of one decode workload: N_COPIES caches, the step's new
+    tokens, queries, tables, workspace."""
+
+    def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int):
+        self.torch, self.tq, self.w = torch, tq, w
+        self.S = num_kv_splits
+        self.lay = tq.layout_init(w.preset)
+        self.lens = W.seq_lens(w)
+        table = W.block_table(w)
+        self.table_np = table
+        self.nb = W.num_blocks(w)
+        self.tab = tq.Tables(self.lay, W.signs(w))
+        shape = tq.kv_cache_shape(self.lay, self.nb, w.block_size, w.num_kv_heads)
+        log(f"[{w.name}] generating inputs")
+        t0 = time.time()
+        K, V = W.kv_all(w, threads=16)
+        log(f"[{w.name}] inputs in {time.time() - t0:.1f}s; storing the context")
+        cache = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        newk, newv, newslots = [], [], []
+        for b in range(w.batch):
+            L = int(self.lens[b])
+            slots = W.slot_mapping_for_sequence(w, b, table, self.lens)
+            kd, vd = dev16(torch, K[b], w.dtype), dev16(torch, V[b], w.dtype)
+            tq.store(self.lay, kd, vd, torch.from_numpy(slots).cuda(), cache, self.tab.signs, self.tab.centroids,
+                     self.tab.boundaries)
+            newk.append(K[b][L - 1 : L])
+            newv.append(V[b][L - 1 : L])
+            newslots.append(slots[L - 1 : L])
+        del K, V
+        torch.cuda.synchronize()
+        self.caches = [cache] + [cache.clone() for _ in range(N_COPIES - 1)]
+        # the step re-stores each sequence's last token (its new token)
+        self.knew = dev16(torch, np.concatenate(newk), w.dtype)
+        self.vnew = dev16(torch, np.concatenate(newv), w.dtype)
+        self.snew = torch.from_numpy(np.concatenate(newslots)).cuda()
+        self.q = dev16(torch, W.queries(w), w.dtype)
+        self.bt = torch.from_numpy(table).cuda()
+        self.sl = torch.from_numpy(self.lens).cuda()
+        self.ws = torch.empty(tq.decode_workspace_bytes(w.batch, w.num_q_heads, 128, self.S), dtype=torch.uint8,
+                              device="cuda")
+        self.out = torch.empty((w.batch, w.num_q_heads, 128), dtype=self.q.dtype, device="cuda")
+        self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
+        self.scale = 1.0 / math.sqrt(128)
+        self.bytes_read = int(self.lens.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
+        torch.cuda.synchronize()
+
+    def store(self, i):
+        self.tq.store(self.lay, self.knew, self.vnew, self.snew, self.caches[i], self.tab.signs, self.tab.centroids,
+                      self.tab.boundaries)
+
+    def stage1(self, i):
+        self.tq.decode_stage1(self.lay, self.q, self.caches[i], self.bt, self.sl, self.tab.signs, self.tab.centroids,
+                              self.scale, self.S, self.ws)
+
+    def stage2(self):
+        self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, 128, self.S, self.ws, self.out, self.lse)
+
+    def step(self, i):
+        self.store(i)
+        self.stage1(i)
+        self.stage2()
+
+    def graphs(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(N_COPIES):  # warm the launch path once outside capture
+                self.step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gs = []
+        for i in range(N_COPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(i)
+            gs.append(g)
+        torch.cuda.synchronize()
+        return gs
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        gs = self.graphs()
+        for i in range(warmup):
+            gs[i % N_COPIES].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            gs[i % N_COPIES].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per step
+
+    def time_stage1(self, launches):
+        """Average stage-1 kernel duration (ms) from events around each launch."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for i in range(N_COPIES):
+            self.stage1(i)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            self.stage1(i % N_COPIES)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def store_sweep(torch, tq, steps):
+    """Store sweep: 65536 tokens x 8 KV heads, bs 32, per preset (Mtok/s)."""
+    s = W.STORE_WORKLOAD
+    K, V, slots, nb = W.store_inputs()
+    kd, vd = dev16(torch, K, s["dtype"]), dev16(torch, V, s["dtype"])
+    sd = torch.from_numpy(slots).cuda()
+    res = {}
+    for preset in s["presets"]:
+        lay = tq.layout_init(preset)
+        tab = tq.Tables(lay, W.signs(s["seed"]))
+        caches = [torch.zeros(tq.kv_cache_shape(lay, nb, s["block_size"], s["num_kv_heads"]), dtype=torch.uint8,
+                              device="cuda") for _ in range(N_COPIES)]
+        for c in caches:
+            tq.store(lay, kd, vd, sd, c, tab.signs, tab.centroids, tab.boundaries)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            tq.store(lay, kd, vd, sd, caches[i % N_COPIES], tab.signs, tab.centroids, tab.boundaries)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        n = s["num_tokens"]
+        bytes_moved = n * s["num_kv_heads"] * (2 * 128 * 2 + lay.slot_size_aligned) + n * 8
+        res[preset] = {"mtok_s": n / (ms * 1e-3) / 1e6, "ms": ms, "gbs": bytes_moved / (ms * 1e-3) / 1e9,
+                       "frac_hbm": bytes_moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del caches
+    return res
+
+
+def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
+    """The oracle decoding whole (sequence, KV head) groups of the workload,
+    stored by the oracle, until the time budget is spent."""
+    import oracle as O
+
+    lay = O.layout(w.preset, 128)
+    lens = W.seq_lens(w)
+    signs = W.signs(w).astype(np.float64)
+    c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(128, lay.key_bits)
+    R = None if lay.key_fp8 else O.rotation(signs)
+    q = O.widen(W.queries(w), w.dtype)
+    g = w.num_q_heads // w.num_kv_heads
+    scale = 1.0 / math.sqrt(128)
+    spent, nbytes, groups = 0.0, 0, 0
+    for b in range(w.batch):
+        K, V = W.kv_sequence(w, b, lens)
+        for hk in range(w.num_kv_heads):
+            slots = O.encode_slots(lay, O.widen(K[:, hk], w.dtype), O.widen(V[:, hk], w.dtype), R, c32, b32)
+            t0 = time.perf_counter()
+            Kd, Vd = O.decode_slots(lay, slots, c32)
+            for j in range(g):
+                qq = q[b, hk * g + j] if lay.key_fp8 else R @ q[b, hk * g + j]
+                O.attend(qq, Kd, Vd, scale)
+            spent += time.perf_counter() - t0
+            nbytes += int(lens[b]) * lay.slot_size_aligned
+            groups += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{groups} (sequence, KV head) groups of the {w.name} workload ({nbytes} compressed bytes), "
+                      f"oracle-stored, decoded with all {g} query heads each; {spent:.1f}s of CPU time; NumPy/BLAS "
+                      f"threads up to the {cores} cores in the affinity mask"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--splits", type=int, default=8)
+    ap.add_argument("--only", choices=["all", "headline"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_decode_attention_tq_amd as tq
+
+    w = W.WORKLOADS["llama8b"]
+    hb = DecodeBench(torch, tq, w, args.splits)
+    ms = hb.time_steps(args.steps, args.warmup)
+    st1_ms = hb.time_stage1(max(30, args.steps // 4))
+    gbs = hb.bytes_read / (ms * 1e-3) / 1e9
+    st1_gbs = hb.bytes_read / (st1_ms * 1e-3) / 1e9
+    log(f"[llama8b] step {ms * 1e3:.1f} us  -> {gbs:.0f} GB/s; stage1 {st1_ms * 1e3:.1f} us -> {st1_gbs:.0f} GB/s")
+    head_bytes = hb.bytes_read
+    del hb
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if args.only == "all":
+        for name, S in (("longctx", 32), ("qwen32b", args.splits)):
+            wk = W.WORKLOADS[name]
+            b = DecodeBench(torch, tq, wk, S)
+            m = b.time_steps(max(20, args.steps // 4), max(5, args.warmup // 4))
+            s1 = b.time_stage1(20)
+            extra[name] = {"preset": wk.preset, "ms_per_step": m, "decode_gbs": b.bytes_read / (m * 1e-3) / 1e9,
+                           "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9,
+                           "frac_hbm": b.bytes_read / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, "num_kv_splits": S,
+                           "bytes_read": b.bytes_read}
+            log(f"[{name}] step {m * 1e3:.1f} us -> {extra[name]['decode_gbs']:.0f} GB/s")
+            del b
+            torch.cuda.empty_cache()
+        extra["store_sweep"] = store_sweep(torch, tq, 50)
+        log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items()})}")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    line = {
+        "metric": "TQ decode-attn effective HBM GB/s (% of peak) + store Mtok/s, k8v4/3bit_nc",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama8b: k8v4 decode step, 32 seqs x 4096 tokens, 32/8 heads, head_dim 128, block 16",
+                   "global_batch": w.batch, "seq_len": int(w.seq_len), "num_kv_splits": args.splits,
+                   "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head_bytes},
+        "roofline": {"bound": "hbm", "achieved": st1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": st1_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "tq_decode_stage1_kernel<k8v4>",
+                     "stage1_us": st1_ms * 1e3},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

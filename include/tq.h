@@ -1,0 +1,227 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant KV-cache store and decode attention on
+ * AMD MI355X (gfx950).
+ *
+ * Sources (the method is defined by these pages; cited by title + section):
+ *   [PR]   prhub summary of vLLM PR #38479 (TurboQuant attention backend),
+ *          sections "实现拆解" (implementation breakdown) and "关键源码片段"
+ *          (source excerpts: turboquant_attn.py, centroids.py,
+ *          attention.py::_init_turboquant_buffers).
+ *   [API]  vLLM API docs "vllm.v1.attention.backends.turboquant_attn":
+ *          TurboQuantAttentionBackend, TurboQuantAttentionImpl.__init__,
+ *          _ensure_on_device, do_kv_cache_update, _store_kv,
+ *          _continuation_prefill, _decode_attention.
+ *   [TQ+]  Atlas docs "TurboQuant+ -- KV-cache compression beyond the Google
+ *          baseline", sections "Background" and "What landed".
+ *   [TRACK] vLLM issue #40069 "TurboQuant/HIGGS Attention follow-ups".
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: TQ_OK (0) or a negative tq_status.  Arguments are checked
+ *     on the host before anything is launched; on error nothing is launched
+ *     and no memory is touched.
+ *   - Ownership: every pointer belongs to the caller.  "device" pointers must
+ *     be GPU memory visible to the current HIP device; "host" pointers are
+ *     ordinary CPU memory.  The library allocates nothing, keeps no global
+ *     state, never synchronizes the stream and never reads device memory
+ *     from the host, so calls are reentrant and can be captured in a HIP
+ *     graph (no hipMemset is issued).
+ *   - stream: a hipStream_t passed as void* (NULL = the default stream).
+ *     Kernels are enqueued on it; results are valid once the stream has
+ *     reached them.
+ *   - Element types: tq_dtype.  16-bit tensors are little-endian IEEE fp16
+ *     or bfloat16.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,       /* null pointer, negative size, misaligned tensor   */
+  TQ_EPRESET = -2,      /* unknown preset id or name                        */
+  TQ_EHEADDIM = -3,     /* head_dim unsupported (kernels: 128)              */
+  TQ_EBLOCK = -4,       /* block_size not one of 16, 32, 64, 128            */
+  TQ_EGQA = -5,         /* num_q_heads not a multiple of num_kv_heads       */
+  TQ_EWORKSPACE = -6,   /* workspace smaller than tq_decode_workspace_bytes */
+  TQ_EDTYPE = -7,       /* element type not allowed for that argument       */
+  TQ_EHIP = -8,         /* a HIP launch failed (hipGetLastError)            */
+  TQ_EUNSUPPORTED = -9  /* valid but unsupported combination                */
+} tq_status;
+
+/* Presets: [PR] "实现拆解" item 1; [API] TurboQuantAttentionBackend
+ * supported_kv_cache_dtypes.  k8v4 = FP8 (E4M3) keys + 4-bit values;
+ * 4bit_nc = 4-bit Lloyd-Max keys + 4-bit values; k3v4_nc = 3-bit keys +
+ * 4-bit values; 3bit_nc = 3-bit keys + 3-bit values; "nc" = norm
+ * correction (stored key norm is ||x|| / ||c[code]||, [TQ+] "Background"). */
+typedef enum { TQ_K8V4 = 0, TQ_4BIT_NC = 1, TQ_K3V4_NC = 2, TQ_3BIT_NC = 3 } tq_preset;
+
+typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
+
+/* Byte layout of one combined slot (one token, one KV head):
+ *   MSE keys: [key codes (key_data_bytes) | fp16 key norm] [value codes
+ *             (value_data_bytes) | fp16 scale | fp16 zero] [pad to even]
+ *   FP8 keys: [head_dim x fp8 key] [value region] [pad]
+ * key_data_bytes = ceil(head_dim*key_bits/8) (head_dim for FP8),
+ * value_data_bytes = ceil(head_dim*value_bits/8), slot_size_aligned =
+ * slot_size rounded up to even ([API] TurboQuantAttentionImpl.__init__ and
+ * _continuation_prefill; [PR] get_kv_cache_shape).  Codes are packed as one
+ * little-endian bit stream, code j in bits [b*j, b*j+b) (3-bit: 8 codes per
+ * 3 bytes, [TQ+] "Background"). */
+typedef struct tq_layout {
+  int32_t preset;
+  int32_t head_dim;
+  int32_t key_fp8;
+  int32_t key_bits;        /* 8 for FP8 keys */
+  int32_t value_bits;
+  int32_t norm_correction;
+  int32_t n_centroids;     /* 2^key_bits, 0 for FP8 keys */
+  int32_t key_data_bytes;
+  int32_t key_packed_size;
+  int32_t value_data_bytes;
+  int32_t value_packed_size;
+  int32_t slot_size;
+  int32_t slot_size_aligned;
+} tq_layout;
+
+/* Library version string (static storage). */
+const char* tq_version(void);
+
+/* Human-readable text for a tq_status (static storage). */
+const char* tq_status_str(int status);
+
+/* "turboquant_k8v4" | "turboquant_4bit_nc" | "turboquant_k3v4_nc" |
+ * "turboquant_3bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
+int tq_preset_from_name(const char* name, int32_t* preset);
+
+/* Fill *out for (preset, head_dim) (host).  head_dim must be a positive
+ * multiple of 8; the kernels additionally need head_dim == 128. */
+int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out);
+
+/* Cache tensor shape (num_blocks, block_size, num_kv_heads,
+ * slot_size_aligned), no leading K/V dimension ([PR] get_kv_cache_shape).
+ * The cache is a byte tensor of that shape; slot m of KV head h is at byte
+ * (m*num_kv_heads + h)*slot_size_aligned (host). */
+int tq_kv_cache_shape(const tq_layout* layout, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int64_t shape_out[4]);
+
+/* Lloyd-Max codebook for the rotated-coordinate marginal N(0, 1/d) ([PR]
+ * "关键源码片段", centroids.py), host.  mode 0 = exact (closed-form Gaussian
+ * cell means iterated to a float64 fixed point, antisymmetric); mode 1 =
+ * the pages' trapezoid solver (200 intervals, cells closed at +-10.5 sigma,
+ * 200 rounds, tol 1e-10).  Writes 2^bits fp32 centroids (ascending) and
+ * 2^bits - 1 fp32 boundaries = fp32 midpoints of adjacent fp32 centroids
+ * ([API] _ensure_on_device).  bits in 1..4. */
+int tq_lloyd_max(int32_t d, int32_t bits, int32_t mode, float* centroids, float* boundaries);
+
+/* d Rademacher signs (+1.0f / -1.0f) for the rotation (host): sign i is -1
+ * when the top bit of the i-th SplitMix64 output from `seed` is set.  The
+ * pages derive a per-layer seed ([PR] attention.py excerpt); the caller owns
+ * that policy. */
+int tq_wht_signs(int32_t d, uint64_t seed, float* signs);
+
+/* Bytes of device workspace tq_decode_attention needs: the stage-1 partials
+ * (batch, num_q_heads, num_kv_splits, head_dim + 1) fp32 ([PR] attention.py
+ * excerpt, the mid_o buffer; [API] _decode_attention), rounded up to 256. */
+int tq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
+                              size_t* bytes);
+
+/* Quantize num_tokens new K/V rows and write their slots ([API]
+ * do_kv_cache_update / _store_kv; [PR] "实现拆解" item 4: one fused launch).
+ * Per (token n, KV head h):
+ *   MSE keys: nu = ||k||, y = H (s .* k) / sqrt(D) (s = signs, H the
+ *     Sylvester Walsh-Hadamard matrix), code_i = #{j : boundaries[j] < y_i/nu},
+ *     stored norm = nu / ||centroids[code]|| (norm correction) or nu;
+ *   FP8 keys: E4M3 round-to-nearest-even, saturating at +-448;
+ *   values: zero = fp16(min v), scale = fp16((max v - min v)/(2^b - 1)),
+ *     code = clamp(floor(fl32(fl32(v - zero) * fl32(1/scale)) + 0.5)).
+ * Arguments:
+ *   key, value       device, dtype in_dtype (TQ_F16 | TQ_BF16); row (n, h)
+ *                    starts at element n*key_tok_stride + h*head_dim (heads
+ *                    contiguous); base 16-byte aligned, strides multiples of 8.
+ *   num_tokens       N >= 0; N == 0 returns TQ_OK with no launch.
+ *   slot_mapping     device int64 [N]; slot m < 0 skips the token.
+ *   kv_cache         device bytes, shape tq_kv_cache_shape(...).  Only the
+ *                    addressed slots are written.  Slots must be distinct
+ *                    (two tokens mapped to one slot race).
+ *   signs            device fp32 [head_dim] (MSE presets; may be NULL for FP8).
+ *   centroids        device fp32 [n_centroids]; boundaries device fp32
+ *                    [n_centroids - 1] (MSE presets; NULL for FP8 keys).
+ * Supported: head_dim 128, block_size 16/32/64/128, num_kv_heads >= 1. */
+int tq_store(const tq_layout* layout, const void* key, const void* value, int32_t in_dtype, int64_t num_tokens,
+             int32_t num_kv_heads, int64_t key_tok_stride, int64_t val_tok_stride, const int64_t* slot_mapping,
+             void* kv_cache, int64_t num_blocks, int32_t block_size, const float* signs, const float* centroids,
+             const float* boundaries, void* stream);
+
+/* Host-only check of tq_store's arguments (no launch, no device access). */
+int tq_store_validate(const tq_layout* layout, const void* key, const void* value, int32_t in_dtype,
+                      int64_t num_tokens, int32_t num_kv_heads, int64_t key_tok_stride, int64_t val_tok_stride,
+                      const int64_t* slot_mapping, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                      const float* signs, const float* centroids, const float* boundaries);
+
+/* Decode attention of one query per sequence over the compressed cache
+ * ([API] _decode_attention; [PR] "实现拆解" item 4: stage 1 scores and
+ * accumulates values per KV split, stage 2 merges the splits with a
+ * log-sum-exp reduction).  Query head hq reads KV head hq / (Hq/Hk).  MSE
+ * keys are scored against the query rotated by the same transform;
+ * FP8 keys against the raw query.  Result = softmax(scale * q.k) v over
+ * tokens [0, seq_lens[b]) of each sequence; seq_lens[b] == 0 gives o = 0
+ * and lse = -inf.
+ * Arguments:
+ *   query        device [batch, num_q_heads, head_dim], dtype q_dtype
+ *                (TQ_F16 | TQ_BF16), contiguous.
+ *   kv_cache     device bytes written by tq_store (same layout, block_size).
+ *   block_table  device int32 [batch, block_table_stride]; entries past
+ *                ceil(seq_lens[b]/block_size) are never read.
+ *   seq_lens     device int32 [batch], each in [0, block_table_stride*block_size].
+ *   signs, centroids  as for tq_store (MSE presets).
+ *   scale        softmax scale (1/sqrt(head_dim) for standard attention).
+ *   num_kv_splits S >= 1: each sequence's tokens are cut into S contiguous
+ *                ranges (16-token granularity); fixed per call so the launch
+ *                shape never depends on device data.
+ *   workspace    device, >= tq_decode_workspace_bytes(batch, num_q_heads,
+ *                head_dim, S) bytes, 16-byte aligned; contents are scratch.
+ *   out          device [batch, num_q_heads, head_dim], dtype out_dtype
+ *                (TQ_F16 | TQ_BF16 | TQ_F32), contiguous.
+ *   lse_out      device fp32 [batch, num_q_heads] natural-log LSE, or NULL.
+ * Supported: head_dim 128, block_size 16/32/64/128, num_q_heads a multiple
+ * of num_kv_heads. */
+int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
+                        int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
+                        int32_t num_kv_splits, void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                        float* lse_out, void* stream);
+
+/* Host-only check of tq_decode_attention's arguments. */
+int tq_decode_validate(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
+                       int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, const float* signs, const float* centroids, int32_t num_kv_splits,
+                       const void* workspace, size_t workspace_bytes, const void* out, int32_t out_dtype);
+
+/* The two launches of tq_decode_attention, exposed separately so that each
+ * can be timed on its own.  Stage 1 writes the workspace partials
+ * [b][hq][split] = (normalized partial output[head_dim], natural-log LSE);
+ * stage 2 merges them into out / lse_out.  Same arguments and checks as
+ * tq_decode_attention. */
+int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+                     const float* signs, const float* centroids, float scale, int32_t num_kv_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
+                     const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -480,6 +480,74 @@ def encode_slot(lay: Layout, k, v, R, centroids32, boundaries32) -> np.ndarray:
     return out
 
 
+def encode_slots(lay: Layout, K, V, R, centroids32, boundaries32) -> np.ndarray:
+    """``encode_slot`` applied to every row of K, V (R rows x D), the same
+    steps written over arrays of rows.  Returns (rows, slot_size_aligned)."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    rows, D = K.shape
+    out = np.zeros((rows, lay.slot_size_aligned), dtype=np.uint8)
+    if lay.key_fp8:
+        out[:, :D] = fp8_e4m3fn_encode(K)
+    else:
+        nu = np.sqrt(np.sum(K * K, axis=1))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            U = np.where(nu[:, None] > 0, (K @ R.T) / nu[:, None], 0.0)
+        codes = (np.asarray(boundaries32, np.float64)[None, None, :] < U[:, :, None]).sum(axis=2)
+        chat = np.asarray(centroids32, dtype=np.float64)[codes]
+        r = np.sqrt(np.sum(chat * chat, axis=1))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            gamma = np.where(nu > 0, nu / r if lay.norm_correction else nu, 0.0)
+        out[:, : lay.key_data_bytes] = pack_lsb(codes, lay.key_bits)
+        out[:, lay.key_data_bytes : lay.key_data_bytes + 2] = _u16_le(fp16_bits(gamma))
+    # values: the fp32 steps of quantize_values, per row
+    v32 = V.astype(np.float32)
+    levels = (1 << lay.value_bits) - 1
+    vmin = v32.min(axis=1)
+    vmax = v32.max(axis=1)
+    scale32 = ((vmax - vmin).astype(np.float32) / np.float32(levels)).astype(np.float32)
+    s16 = scale32.astype(np.float16)
+    z16 = vmin.astype(np.float16)
+    with np.errstate(all="ignore"):
+        inv = (np.float32(1.0) / s16.astype(np.float32)).astype(np.float32)
+        t = (v32 - z16.astype(np.float32)[:, None]).astype(np.float32)
+        q = (t * inv[:, None]).astype(np.float32)
+        rr = (q + np.float32(0.5)).astype(np.float32)
+        rr = np.where(np.isnan(rr), np.float32(0.0), rr)
+        vc = np.clip(np.floor(rr), 0, levels).astype(np.int64)
+    vc[s16.astype(np.float32) == 0.0] = 0
+    o = lay.key_packed_size
+    out[:, o : o + lay.value_data_bytes] = pack_lsb(vc, lay.value_bits)
+    o += lay.value_data_bytes
+    out[:, o : o + 2] = _u16_le(s16.view(np.uint16))
+    out[:, o + 2 : o + 4] = _u16_le(z16.view(np.uint16))
+    return out
+
+
+def key_units(lay: Layout, K, R):
+    """The rotated, normalized key coordinates u = R k / ||k|| of every row
+    (float64), the quantity each key code is decided on."""
+    K = np.asarray(K, dtype=np.float64)
+    nu = np.sqrt(np.sum(K * K, axis=1))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.where(nu[:, None] > 0, (K @ R.T) / nu[:, None], 0.0)
+
+
+def store_rows(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, boundaries32):
+    """``store`` with the rows encoded by ``encode_slots``."""
+    key = np.asarray(key, dtype=np.float64)
+    value = np.asarray(value, dtype=np.float64)
+    N, Hk, D = key.shape
+    bs = kv_cache.shape[1]
+    R = None if lay.key_fp8 else rotation(np.asarray(signs, dtype=np.float64))
+    slots = encode_slots(lay, key.reshape(N * Hk, D), value.reshape(N * Hk, D), R, centroids32,
+                         boundaries32).reshape(N, Hk, -1)
+    m = np.asarray(slot_mapping, dtype=np.int64)
+    keep = m >= 0
+    kv_cache[m[keep] // bs, m[keep] % bs] = slots[keep]
+    return kv_cache
+
+
 def store(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, boundaries32):
     """Quantize N tokens x Hk heads and write their slots into the paged cache.
 
@@ -530,18 +598,35 @@ def decode_slot(lay: Layout, slot, centroids32):
     return k, z + s * vc.astype(np.float64)
 
 
+def decode_slots(lay: Layout, slots, centroids32):
+    """``decode_slot`` applied to every row of slots (rows, slot bytes)."""
+    slots = np.asarray(slots, dtype=np.uint8)
+    D = lay.head_dim
+    if lay.key_fp8:
+        K = fp8_e4m3fn_decode(slots[:, :D])
+    else:
+        codes = unpack_lsb(slots[:, : lay.key_data_bytes], lay.key_bits, D)
+        gamma = _from_u16_le(slots[:, lay.key_data_bytes : lay.key_data_bytes + 2]).view(np.float16).astype(np.float64)
+        K = gamma[:, None] * np.asarray(centroids32, dtype=np.float64)[codes]
+    o = lay.key_packed_size
+    vc = unpack_lsb(slots[:, o : o + lay.value_data_bytes], lay.value_bits, D)
+    o += lay.value_data_bytes
+    s = _from_u16_le(slots[:, o : o + 2]).view(np.float16).astype(np.float64)
+    z = _from_u16_le(slots[:, o + 2 : o + 4]).view(np.float16).astype(np.float64)
+    return K, z[:, None] + s[:, None] * vc.astype(np.float64)
+
+
 def gather_sequence(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: int, centroids32):
     """Dequantize tokens [0, seq_len) of one sequence and KV head.  Token t is
     in block block_table_row[t // bs] at offset t % bs; entries past
     ceil(seq_len / bs) are never read ([TRACK]: decode index-out-of-bounds
     fix)."""
     bs = kv_cache.shape[1]
-    K = np.zeros((seq_len, lay.head_dim))
-    V = np.zeros((seq_len, lay.head_dim))
-    for t in range(seq_len):
-        blk = int(block_table_row[t // bs])
-        K[t], V[t] = decode_slot(lay, kv_cache[blk, t % bs, hk], centroids32)
-    return K, V
+    t = np.arange(seq_len)
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // bs]
+    if seq_len == 0:
+        return np.zeros((0, lay.head_dim)), np.zeros((0, lay.head_dim))
+    return decode_slots(lay, kv_cache[blk, t % bs, hk], centroids32)
 
 
 def attend(q, K, V, scale: float):

@@ -1,0 +1,120 @@
+// Probe kernels for the tests only (not part of libtq): each runs a single
+// compiler builtin or bit helper so that a test can compare the GPU's lane
+// layout / rounding with a host model.  All launches are one small block on
+// the current device, synchronous, with every index inside the buffers the
+// caller sized: n items, fixed per-item strides.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_bits.h"
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kBitsIn = 12, kBitsOut = 8;
+
+// One helper call: inputs in[0..11], outputs out[0..7].
+TQ_HD void run_bits_op(int op, const uint32_t* in, uint32_t* out) {
+  for (int i = 0; i < kBitsOut; ++i) out[i] = 0;
+  switch (op) {
+    case 0: out[0] = tq::perm32(in[0], in[1], in[2]); break;
+    case 1: out[0] = tq::alignbyte(in[0], in[1], in[2]); break;
+    case 2: tq::key3_selectors(in[0], in[1], in[2], out); break;
+    case 3: tq::lut8(in[0], tq::Lut8{in[1], in[2], in[3], in[4]}, out[0], out[1]); break;
+    case 4: tq::lut16(in[0], tq::Lut8{in[1], in[2], in[3], in[4]}, tq::Lut8{in[5], in[6], in[7], in[8]}, out[0], out[1]); break;
+    case 5: tq::val4_pairs(in[0], in[1], out); break;
+    case 6: tq::val3_pairs(in[0], in[1], out); break;
+    case 7: {
+      float f;
+      uint32_t u = in[0];
+      __builtin_memcpy(&f, &u, 4);
+      out[0] = tq::f32_to_e4m3(f);
+      break;
+    }
+    default: break;
+  }
+}
+
+__global__ void bits_kernel(int op, const uint32_t* in, uint32_t* out, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    run_bits_op(op, in + static_cast<int64_t>(i) * kBitsIn, out + static_cast<int64_t>(i) * kBitsOut);
+}
+
+// a, b: per lane 4 dwords (8 halves); d: per lane 4 floats
+__global__ void mfma32_kernel(const uint32_t* a, const uint32_t* b, float* d) {
+  const int l = threadIdx.x;
+  u32x4 av = {a[4 * l], a[4 * l + 1], a[4 * l + 2], a[4 * l + 3]};
+  u32x4 bv = {b[4 * l], b[4 * l + 1], b[4 * l + 2], b[4 * l + 3]};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), __builtin_bit_cast(half8, bv), acc, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) d[4 * l + i] = acc[i];
+}
+
+// a, b: per lane 2 dwords (4 halves); d: per lane 4 floats
+__global__ void mfma16_kernel(const uint32_t* a, const uint32_t* b, float* d) {
+  const int l = threadIdx.x;
+  u32x2 av = {a[2 * l], a[2 * l + 1]};
+  u32x2 bv = {b[2 * l], b[2 * l + 1]};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4, av), __builtin_bit_cast(half4, bv), acc, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) d[4 * l + i] = acc[i];
+}
+
+// FP8 (E4M3) -> fp16 pairs: out[2i] = bytes 0,1 of in[i]; out[2i+1] = bytes 2,3
+__global__ void cvt_fp8_kernel(const uint32_t* in, uint32_t* out, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(in[i], 1.0f, false));
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(in[i], 1.0f, true));
+  }
+}
+
+int finish() {
+  if (hipGetLastError() != hipSuccess) return -8;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -8;
+}
+
+}  // namespace
+
+extern "C" {
+
+// host model of the bit helpers (emulated byte permutes)
+int tq_probe_bits_host(int op, const uint32_t* in, uint32_t* out, int n) {
+  for (int i = 0; i < n; ++i) run_bits_op(op, in + static_cast<int64_t>(i) * kBitsIn, out + static_cast<int64_t>(i) * kBitsOut);
+  return 0;
+}
+
+// same helpers on the GPU; in: device [n][12], out: device [n][8]
+int tq_probe_bits_device(int op, const uint32_t* in, uint32_t* out, int n) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(bits_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, 0, op, in, out, n);
+  return finish();
+}
+
+// one wave64: a, b device [64][4] dwords, d device [64][4] floats
+int tq_probe_mfma_16x16x32_f16(const uint32_t* a, const uint32_t* b, float* d) {
+  hipLaunchKernelGGL(mfma32_kernel, dim3(1), dim3(64), 0, 0, a, b, d);
+  return finish();
+}
+
+// one wave64: a, b device [64][2] dwords, d device [64][4] floats
+int tq_probe_mfma_16x16x16_f16(const uint32_t* a, const uint32_t* b, float* d) {
+  hipLaunchKernelGGL(mfma16_kernel, dim3(1), dim3(64), 0, 0, a, b, d);
+  return finish();
+}
+
+// in: device [n] dwords of 4 FP8 bytes; out: device [2n] fp16 pairs
+int tq_probe_cvt_fp8_f16(const uint32_t* in, uint32_t* out, int n) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(cvt_fp8_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, 0, in, out, n);
+  return finish();
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+// Bit-level helpers of the kernels: FP8 E4M3 encoding, byte permutes and the
+// unpacking of packed key/value codes into MFMA operand registers.
+//
+// Everything here is plain integer/float code that also compiles for the
+// host, where the two AMDGPU byte-permute instructions are emulated, so the
+// unpacking logic is unit-tested on the CPU (csrc/tests/test_bits.cpp).
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#if defined(__HIPCC__)
+#define TQ_HD __host__ __device__ __forceinline__
+#else
+#define TQ_HD inline
+#endif
+
+namespace tq {
+
+TQ_HD uint32_t f32_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  return u;
+}
+
+// v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value
+// {s0 (bytes 4..7), s1 (bytes 0..3)}; selector 12 gives 0x00, >= 13 gives 0xFF.
+TQ_HD uint32_t perm32(uint32_t s0, uint32_t s1, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_perm(s0, s1, sel);
+#else
+  uint64_t v = (static_cast<uint64_t>(s0) << 32) | s1;
+  uint32_t r = 0;
+  for (int k = 0; k < 4; ++k) {
+    uint32_t b = (sel >> (8 * k)) & 0xFF, byte;
+    if (b < 8)
+      byte = static_cast<uint32_t>(v >> (8 * b)) & 0xFF;
+    else if (b == 12)
+      byte = 0;
+    else if (b >= 13)
+      byte = 0xFF;
+    else
+      byte = ((v >> (16 * (b - 8) + 15)) & 1) ? 0xFF : 0;
+    r |= byte << (8 * k);
+  }
+  return r;
+#endif
+}
+
+// v_alignbyte_b32: low dword of {hi, lo} >> (8 * (shift & 3)).
+TQ_HD uint32_t alignbyte(uint32_t hi, uint32_t lo, uint32_t shift) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_alignbyte(hi, lo, shift);
+#else
+  return static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (8 * (shift & 3)));
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3 (OCP "fn": bias 7, no infinities, S.1111.111 = NaN) from fp32,
+// round to nearest even, saturating at +-448; NaN -> 0x7F.
+// ---------------------------------------------------------------------------
+TQ_HD uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = f32_bits(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;           // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;   // |x| >= 448 (and inf): saturate
+  if (a >= 0x3C800000u) {                      // |x| >= 2^-6: normal E4M3
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+    return sign | (r - (120u << 3));           // rebias exponent 127 -> 7
+  }
+  // subnormal range: value = m * 2^-9, m = rne(|x| * 512) in 0..8 (8 = 2^-6)
+  float ax = std::fabs(x) * 512.0f;
+  return sign | static_cast<uint32_t>(rintf(ax));
+}
+
+// ---------------------------------------------------------------------------
+// Key codebook lookup: codes -> fp16 centroids, two per dword, via v_perm.
+// The fp16 centroid table is split into its low and high bytes; an 8-entry
+// byte table fits the two source dwords of one permute.
+// ---------------------------------------------------------------------------
+struct Lut8 {
+  uint32_t lo0, lo1, hi0, hi1;  // low/high bytes of fp16 centroid 0..3 / 4..7
+};
+
+// S: four 3-bit codes, one per byte (values 0..7).  out0 = fp16 pair
+// (c[S.b0], c[S.b1]), out1 = (c[S.b2], c[S.b3]).
+TQ_HD void lut8(uint32_t S, const Lut8& t, uint32_t& out0, uint32_t& out1) {
+  uint32_t lo = perm32(t.lo1, t.lo0, S);
+  uint32_t hi = perm32(t.hi1, t.hi0, S);
+  out0 = perm32(hi, lo, 0x05010400u);
+  out1 = perm32(hi, lo, 0x07030602u);
+}
+
+// 16 entries: two 8-entry tables, picked per byte by bit 3 of the code.
+TQ_HD void lut16(uint32_t S, const Lut8& a, const Lut8& b, uint32_t& out0, uint32_t& out1) {
+  uint32_t s7 = S & 0x07070707u;
+  uint32_t m = ((S >> 3) & 0x01010101u) * 0xFFu;
+  uint32_t lo = (m & perm32(b.lo1, b.lo0, s7)) | (~m & perm32(a.lo1, a.lo0, s7));
+  uint32_t hi = (m & perm32(b.hi1, b.hi0, s7)) | (~m & perm32(a.hi1, a.hi0, s7));
+  out0 = perm32(hi, lo, 0x05010400u);
+  out1 = perm32(hi, lo, 0x07030602u);
+}
+
+// 32 packed 3-bit key codes (12 bytes, LSB-first bit stream: code j at bits
+// 3j..3j+2; bytes 3g..3g+2 hold codes 8g..8g+7) -> eight selector dwords.
+// sel[m] holds, in byte g, code 8g + m.  The codes of one byte column are
+// gathered first (X = byte 0 of every 3-byte group, Y = byte 1, Z = byte 2),
+// then each code is one shift and mask (two for the codes that straddle).
+TQ_HD void key3_selectors(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t sel[8]) {
+  uint32_t X = perm32(w2, perm32(w1, w0, 0x00060300u), 0x05020100u);
+  uint32_t Y = perm32(w2, perm32(w1, w0, 0x00070401u), 0x06020100u);
+  uint32_t Z = perm32(w2, perm32(w1, w0, 0x00000502u), 0x07040100u);
+  sel[0] = X & 0x07070707u;
+  sel[1] = (X >> 3) & 0x07070707u;
+  sel[2] = ((X >> 6) & 0x03030303u) | ((Y << 2) & 0x04040404u);
+  sel[3] = (Y >> 1) & 0x07070707u;
+  sel[4] = (Y >> 4) & 0x07070707u;
+  sel[5] = ((Y >> 7) & 0x01010101u) | ((Z << 1) & 0x06060606u);
+  sel[6] = (Z >> 2) & 0x07070707u;
+  sel[7] = (Z >> 5) & 0x07070707u;
+}
+
+// Order of the 32 key dims of a 3-bit lane chunk in the MFMA operand: chunk c
+// (0..3) element e (0..7) holds dim 8*(e & 3) + 2c + (e >> 2).
+TQ_HD int key3_dim(int c, int e) { return 8 * (e & 3) + 2 * c + (e >> 2); }
+
+// 4-bit keys: dword k of a lane chunk holds dims 8k..8k+7 (low nibble =
+// even dim).  lo = w & 0x0F0F0F0F selects the even dims, hi the odd ones.
+// Chunk c element e holds dim 8c + (e < 4 ? 2e : 2(e - 4) + 1).
+TQ_HD int key4_dim(int c, int e) { return 8 * c + (e < 4 ? 2 * e : 2 * (e - 4) + 1); }
+
+// ---------------------------------------------------------------------------
+// Value codes -> fp16 MFMA operand pairs, as fp16 subnormals.
+//
+// A 16-bit half whose exponent field is zero is the subnormal mantissa *
+// 2^-24, i.e. linear in its bits: a code sitting at bit position p (p + width
+// <= 10) of an otherwise zero half is exactly code * 2^(p-24).  Masking the
+// code in place therefore yields an MFMA operand with no conversion; the
+// power-of-two factor is undone after the accumulation.  Each output dword
+// holds the same dim of two tokens (token a in the low half).
+// ---------------------------------------------------------------------------
+
+// 4-bit: wa, wb = the dword of dims 8r..8r+7 of tokens a and b.  out[n]
+// (n = 0..7) = dim 8r+n of (a, b); code at bit position (n & 1) * 4.
+TQ_HD void val4_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
+  uint32_t p0 = perm32(wb, wa, 0x05040100u);  // bits 0..15 of a | bits 0..15 of b
+  uint32_t p1 = perm32(wb, wa, 0x07060302u);  // bits 16..31
+  uint32_t q0 = p0 >> 8, q1 = p1 >> 8;
+  out[0] = p0 & 0x000F000Fu;
+  out[1] = p0 & 0x00F000F0u;
+  out[2] = q0 & 0x000F000Fu;
+  out[3] = q0 & 0x00F000F0u;
+  out[4] = p1 & 0x000F000Fu;
+  out[5] = p1 & 0x00F000F0u;
+  out[6] = q1 & 0x000F000Fu;
+  out[7] = q1 & 0x00F000F0u;
+}
+TQ_HD int val4_pos(int n) { return (n & 1) * 4; }
+
+// 3-bit: wa, wb = 24 bits (bytes 0..2) = dims 8r..8r+7, code m at bits 3m.
+// out[m] = dim 8r+m of (a, b); code at bit position val3_pos(m).
+TQ_HD void val3_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
+  uint32_t p0 = perm32(wb, wa, 0x05040100u);  // word bits 0..15
+  uint32_t p1 = perm32(wb, wa, 0x06050201u);  // word bits 8..23
+  uint32_t p2 = perm32(wb, wa, 0x0C060C02u);  // word bits 16..23
+  out[0] = p0 & 0x00070007u;
+  out[1] = p0 & 0x00380038u;
+  out[2] = p0 & 0x01C001C0u;
+  out[3] = p1 & 0x000E000Eu;
+  out[4] = p1 & 0x00700070u;
+  out[5] = p1 & 0x03800380u;
+  out[6] = p2 & 0x001C001Cu;
+  out[7] = p2 & 0x00E000E0u;
+}
+// code m starts at bit 3m of the word and its window starts at bit 8*floor(3m/8)
+TQ_HD int val3_pos(int m) { return (3 * m) & 7; }
+
+}  // namespace tq

@@ -1,0 +1,556 @@
+// tq_decode_attention: split-KV decode attention over the compressed paged
+// cache ([PR] "实现拆解" item 4: stage 1 scores and accumulates values per
+// split, stage 2 merges the splits with a log-sum-exp reduction; [API]
+// _decode_attention).
+//
+// Stage 1 work unit: one workgroup per (sequence b, KV head hk, group of up
+// to 16 query heads, split s); its 4 wave64s take the split's 16-token tiles
+// round-robin and merge in LDS at the end.  Per tile a wave:
+//   - builds the key tile (16 tokens x 128 dims) as fp16 MFMA operands: FP8
+//     keys by the hardware FP8->fp16 convert, Lloyd-Max codes through a
+//     v_perm byte lookup of the fp16 codebook;
+//   - scores S^T = K . Q^T with 4 MFMA 16x16x32 f16 (tokens on rows, query
+//     heads on columns), the query rotated by the same transform and
+//     pre-scaled by scale*log2(e) (MSE presets, [API] _decode_attention);
+//   - applies the per-token key norm, an online softmax in base 2, and
+//   - accumulates O^T = V^T . P^T with 8 MFMA 16x16x16 f16, the value codes
+//     entering as fp16 subnormals (no conversion) and the per-token value
+//     scale folded into P; the per-token zero point is accumulated on the
+//     VALU as sum(p * zero).
+// The GQA group rides on the MFMA's 16 columns, so the key/value bytes of a
+// (token, KV head) are read and decoded once for all its query heads.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+
+#include "tq.h"
+#include "tq_bits.h"
+#include "tq_internal.h"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Slot geometry per preset at head_dim 128 (see tq_layout_init).
+template <int P>
+struct Preset;
+template <>
+struct Preset<TQ_K8V4> {
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 4, kKdata = 128, kKps = 128, kVdata = 64, kSlot = 196;
+};
+template <>
+struct Preset<TQ_4BIT_NC> {
+  static constexpr int kFp8 = 0, kKb = 4, kVb = 4, kKdata = 64, kKps = 66, kVdata = 64, kSlot = 134;
+};
+template <>
+struct Preset<TQ_K3V4_NC> {
+  static constexpr int kFp8 = 0, kKb = 3, kVb = 4, kKdata = 48, kKps = 50, kVdata = 64, kSlot = 118;
+};
+template <>
+struct Preset<TQ_3BIT_NC> {
+  static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102;
+};
+
+struct DecodeArgs {
+  const uint16_t* query;
+  const uint8_t* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* signs;
+  const float* centroids;
+  float* partials;  // [B][Hq][S][D+1]
+  float qscale;     // softmax scale * log2(e)
+  int32_t q_bf16;
+  int32_t num_q_heads, num_kv_heads, group, head_groups;
+  int32_t block_size, bt_stride, num_splits;
+};
+
+__device__ __forceinline__ float widen16(uint32_t bits, bool bf16) {
+  if (bf16) return __uint_as_float(bits << 16);
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t bits) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
+}
+
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; remap
+// so that consecutive *logical* ids (the KV heads of one sequence/split,
+// which share cache lines) run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks / 8, rem = nblocks % 8;
+  const int x = bid % 8, loc = bid / 8;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
+}
+
+// dword from a 2-byte aligned address: two aligned dwords, realigned.
+__device__ __forceinline__ uint32_t ld32_u(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(a & ~static_cast<uintptr_t>(3));
+  return tq::alignbyte(w.y, w.x, static_cast<uint32_t>(a & 3));
+}
+
+__device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+
+// Query head dim held by MFMA key-operand chunk c, element e, lane quarter q.
+template <int P>
+__device__ __forceinline__ int key_dim(int c, int q, int e) {
+  using T = Preset<P>;
+  if (T::kFp8) return (c >> 1) * 64 + 16 * q + (c & 1) * 8 + e;
+  if (T::kKb == 4) return 32 * q + tq::key4_dim(c, e);
+  return 32 * q + tq::key3_dim(c, e);
+}
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4a4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+__device__ __forceinline__ half4 as_half4(uint32_t a, uint32_t b) {
+  u32x2a4 v = {a, b};
+  return __builtin_bit_cast(half4, v);
+}
+__device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Key tile operand for one lane: token = lane % 16, its 32 dims of quarter q.
+template <int P>
+__device__ __forceinline__ void key_operand(const uint8_t* kslot, int q, const tq::Lut8& la, const tq::Lut8& lb,
+                                            half8 A[4]) {
+  using T = Preset<P>;
+  if constexpr (T::kFp8 != 0) {
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kslot + 16 * q);
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(kslot + 64 + 16 * q);
+    uint32_t w[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    uint32_t hv[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hv[2 * i] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+      hv[2 * i + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) A[c] = as_half8(hv[4 * c], hv[4 * c + 1], hv[4 * c + 2], hv[4 * c + 3]);
+  } else if constexpr (T::kKb == 4) {
+    const uint8_t* p = kslot + 16 * q;
+    const uintptr_t ad = reinterpret_cast<uintptr_t>(p);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(ad & ~static_cast<uintptr_t>(3));
+    const u32x4a4 r0 = *reinterpret_cast<const u32x4a4*>(base);
+    const uint32_t r4 = *reinterpret_cast<const uint32_t*>(base + 16);
+    const uint32_t sh = static_cast<uint32_t>(ad & 3);
+    uint32_t w[4] = {tq::alignbyte(r0.y, r0.x, sh), tq::alignbyte(r0.z, r0.y, sh), tq::alignbyte(r0.w, r0.z, sh),
+                     tq::alignbyte(r4, r0.w, sh)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t e0, e1, o0, o1;
+      tq::lut16(w[c] & 0x0F0F0F0Fu, la, lb, e0, e1);
+      tq::lut16((w[c] >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
+      A[c] = as_half8(e0, e1, o0, o1);
+    }
+  } else {
+    const uint8_t* p = kslot + 12 * q;
+    const uintptr_t ad = reinterpret_cast<uintptr_t>(p);
+    const u32x4a4 r = *reinterpret_cast<const u32x4a4*>(ad & ~static_cast<uintptr_t>(3));
+    const uint32_t sh = static_cast<uint32_t>(ad & 3);
+    uint32_t sel[8];
+    tq::key3_selectors(tq::alignbyte(r.y, r.x, sh), tq::alignbyte(r.z, r.y, sh), tq::alignbyte(r.w, r.z, sh), sel);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t a0, a1, b0, b1;
+      tq::lut8(sel[2 * c], la, a0, a1);
+      tq::lut8(sel[2 * c + 1], la, b0, b1);
+      A[c] = as_half8(a0, a1, b0, b1);
+    }
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void tq_decode_stage1_kernel(DecodeArgs a) {
+  using T = Preset<P>;
+  // LDS: fp32 rotation scratch (later reused for the cross-wave merge) and the
+  // fp16 query operand source.
+  __shared__ float smem[3 * 16 * kD + 2 * 4 * 16];
+  __shared__ _Float16 qh[16][kD + 8];
+  float(*qf)[kD] = reinterpret_cast<float(*)[kD]>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.num_splits, Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
+  int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int hk = lg % Hk;
+  lg /= Hk;
+  const int hg = lg % a.head_groups;
+  lg /= a.head_groups;
+  const int s = lg % S;
+  const int b = lg / S;
+
+  const int seqlen = a.seq_lens[b];
+  const int ntiles = (seqlen + 15) >> 4;
+  const int tps = (ntiles + S - 1) / S;
+  const int t_begin = s * tps;
+  const int t_end = min(t_begin + tps, ntiles);
+  const int h0 = hg * 16;
+  const int geff = min(16, g - h0);
+  const int hq0 = hk * g + h0;
+  const int64_t head_stride = static_cast<int64_t>(S) * (kD + 1);
+  float* part = a.partials + ((static_cast<int64_t>(b) * Hq + hq0) * S + s) * (kD + 1);
+
+  if (t_begin >= t_end) {  // empty split: zero partial, lse = -inf
+    for (int idx = tid; idx < geff * (kD + 1); idx += kThreads) {
+      const int j = idx / (kD + 1), d = idx % (kD + 1);
+      part[j * head_stride + d] = d == kD ? -INFINITY : 0.f;
+    }
+    return;
+  }
+
+  // ---- query: load, sign flip + Walsh-Hadamard (MSE keys), scale, fp16 ----
+  const bool qbf16 = a.q_bf16 != 0;
+  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+    const int j = idx >> 7, d = idx & (kD - 1);
+    float v = 0.f;
+    if (j < geff) v = widen16(a.query[(static_cast<int64_t>(b) * Hq + hq0 + j) * kD + d], qbf16);
+    if (!T::kFp8) v *= a.signs[d];
+    qf[j][d] = v;
+  }
+  __syncthreads();
+  if (!T::kFp8) {
+    for (int hs = 1; hs < kD; hs <<= 1) {
+      for (int pi = tid; pi < 16 * (kD / 2); pi += kThreads) {
+        const int j = pi / (kD / 2), k = pi % (kD / 2);
+        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
+        const float x0 = qf[j][i0], x1 = qf[j][i1];
+        qf[j][i0] = x0 + x1;
+        qf[j][i1] = x0 - x1;
+      }
+      __syncthreads();
+    }
+  }
+  const float qs = T::kFp8 ? a.qscale : a.qscale * 0.08838834764831845f;  // 1/sqrt(128) of the rotation
+  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+    const int j = idx >> 7, d = idx & (kD - 1);
+    qh[j][d] = static_cast<_Float16>(qf[j][d] * qs);
+  }
+
+  // codebook byte tables (fp16 centroids split into low / high bytes)
+  tq::Lut8 la{}, lb{};
+  if (!T::kFp8) {
+    uint32_t hb[16];
+#pragma unroll
+    for (int i = 0; i < (1 << (T::kFp8 ? 0 : T::kKb)); ++i)
+      hb[i] = __half_as_ushort(__float2half_rn(a.centroids[i]));
+    auto pack = [&](int base, int shift) {
+      return ((hb[base] >> shift) & 0xFF) | (((hb[base + 1] >> shift) & 0xFF) << 8) |
+             (((hb[base + 2] >> shift) & 0xFF) << 16) | (((hb[base + 3] >> shift) & 0xFF) << 24);
+    };
+    la = {pack(0, 0), pack(4, 0), pack(0, 8), pack(4, 8)};
+    if (T::kKb == 4) lb = {pack(8, 0), pack(12, 0), pack(8, 8), pack(12, 8)};
+  }
+  __syncthreads();
+
+  const int hl = lane & 15, q4 = lane >> 4;
+  half8 bq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bq[c][e] = qh[hl][key_dim<P>(c, q4, e)];
+
+  // ---- main loop over this wave's tiles ----
+  const int bs = a.block_size;
+  const int64_t blk_bytes = static_cast<int64_t>(bs) * Hk * T::kSlot;
+  const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  float m_run = -INFINITY, l_run = 0.f, z_run = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = t_begin + wave; t < t_end; t += kWaves) {
+    const int tok0 = t * 16;
+    const int blk = btab[tok0 / bs];
+    const uint8_t* blkbase = a.cache + static_cast<int64_t>(blk) * blk_bytes;
+    const int inblk = tok0 % bs;
+    const uint8_t* kslot = blkbase + (static_cast<int64_t>(inblk + hl) * Hk + hk) * T::kSlot;
+    const uint8_t* vs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vs[i] = blkbase + (static_cast<int64_t>(inblk + 4 * q4 + i) * Hk + hk) * T::kSlot;
+
+    // scores
+    half8 A[4];
+    key_operand<P>(kslot, q4, la, lb, A);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], bq[c], sc, 0, 0, 0);
+
+    float sv[4], zv[4], sco[4];
+    uint32_t vw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float gm = 1.f;
+      if (!T::kFp8) gm = half_bits_to_f32(ld16(vs[i] + T::kKdata));
+      sco[i] = sc[i] * gm;
+      sv[i] = half_bits_to_f32(ld16(vs[i] + T::kKps + T::kVdata));
+      zv[i] = half_bits_to_f32(ld16(vs[i] + T::kKps + T::kVdata + 2));
+      if (T::kVb == 4) {
+        if (T::kKps % 4 == 0 && T::kSlot % 4 == 0)
+          vw[i] = *reinterpret_cast<const uint32_t*>(vs[i] + T::kKps + 4 * hl);
+        else
+          vw[i] = ld32_u(vs[i] + T::kKps + 4 * hl);
+      } else {
+        vw[i] = ld32_u(vs[i] + T::kKps + 3 * hl);
+      }
+    }
+    const bool tail = tok0 + 16 > seqlen;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tok0 + 4 * q4 + i >= seqlen) {
+          sco[i] = -INFINITY;
+          sv[i] = 0.f;
+          zv[i] = 0.f;
+        }
+      }
+    }
+
+    // online softmax (base 2); the 4 lane quarters hold different tokens of
+    // the same query head and share one running maximum
+    float tmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+      l_run *= alpha;
+      z_run *= alpha;
+      m_run = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sco[i] - m_run);
+      l_run += p[i];
+      z_run = fmaf(p[i], zv[i], z_run);
+    }
+    half2v ps01 = {static_cast<_Float16>(p[0] * sv[0]), static_cast<_Float16>(p[1] * sv[1])};
+    half2v ps23 = {static_cast<_Float16>(p[2] * sv[2]), static_cast<_Float16>(p[3] * sv[3])};
+    const half4 pv = as_half4(h2_bits(ps01), h2_bits(ps23));
+
+    // values: V^T tile (dims on rows, tokens on k) as fp16 subnormal codes
+    uint32_t v01[8], v23[8];
+    if (T::kVb == 4) {
+      tq::val4_pairs(vw[0], vw[1], v01);
+      tq::val4_pairs(vw[2], vw[3], v23);
+    } else {
+      tq::val3_pairs(vw[0], vw[1], v01);
+      tq::val3_pairs(vw[2], vw[3], v23);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
+  }
+
+  // ---- per-wave totals: lane quarters hold disjoint tokens ----
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  z_run += __shfl_xor(z_run, 16, 64);
+  z_run += __shfl_xor(z_run, 32, 64);
+  // unnormalized output of head hl, dims 32*q4 + 8*i + n
+  float o[4][8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int pos = T::kVb == 4 ? tq::val4_pos(n) : tq::val3_pos(n);
+    const float unscale = static_cast<float>(1u << (24 - pos));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i][n] = fmaf(acc[n][i], unscale, z_run);
+  }
+
+  // ---- merge the 4 waves in LDS (reusing the rotation scratch) ----
+  __syncthreads();
+  float* mo = smem;                        // [3 waves][16 heads][128]
+  float* mm = smem + 3 * 16 * kD;          // [4][16]
+  float* ml = mm + 4 * 16;                 // [4][16]
+  if (q4 == 0) {
+    mm[wave * 16 + hl] = m_run;
+    ml[wave * 16 + hl] = l_run;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) mo[((wave - 1) * 16 + hl) * kD + 32 * q4 + 8 * i + n] = o[i][n];
+  }
+  __syncthreads();
+  if (wave == 0 && hl < geff) {
+    float M = mm[hl];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + hl]);
+    float fw[kWaves];
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = mm[w * 16 + hl];
+      fw[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      lsum = fmaf(fw[w], ml[w * 16 + hl], lsum);
+    }
+    const float inv = 1.0f / lsum;
+    float* dst = part + hl * head_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int d = 32 * q4 + 8 * i + n;
+        float v = fw[0] * o[i][n];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) v = fmaf(fw[w], mo[((w - 1) * 16 + hl) * kD + d], v);
+        dst[d] = v * inv;
+      }
+    }
+    if (q4 == 0) dst[kD] = (M + log2f(lsum)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------- stage 2
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __restrict__ partials, int rows, int S,
+                                                               void* out, int out_dtype, float* lse_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* base = partials + static_cast<int64_t>(row) * S * (kD + 1);
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, base[static_cast<int64_t>(s) * (kD + 1) + kD]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  float o0 = 0.f, o1 = 0.f, den = 0.f, lse = -INFINITY;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float* ps = base + static_cast<int64_t>(s) * (kD + 1);
+      const float ls = ps[kD];
+      const float w = ls == -INFINITY ? 0.f : expf(ls - M);
+      den += w;
+      o0 = fmaf(w, ps[lane], o0);
+      o1 = fmaf(w, ps[lane + 64], o1);
+    }
+    o0 /= den;
+    o1 /= den;
+    lse = M + logf(den);
+  }
+  const int64_t ob = static_cast<int64_t>(row) * kD;
+  if (out_dtype == TQ_F32) {
+    static_cast<float*>(out)[ob + lane] = o0;
+    static_cast<float*>(out)[ob + lane + 64] = o1;
+  } else if (out_dtype == TQ_F16) {
+    static_cast<__half*>(out)[ob + lane] = __float2half_rn(o0);
+    static_cast<__half*>(out)[ob + lane + 64] = __float2half_rn(o1);
+  } else {
+    static_cast<uint16_t*>(out)[ob + lane] = f32_to_bf16_rne(o0);
+    static_cast<uint16_t*>(out)[ob + lane + 64] = f32_to_bf16_rne(o1);
+  }
+  if (lse_out && lane == 0) lse_out[row] = lse;
+}
+
+template <int P>
+int launch_stage1(const DecodeArgs& a, int64_t nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL(tq_decode_stage1_kernel<P>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+           int32_t num_kv_heads, const void* kv_cache, int32_t block_size, const int32_t* block_table,
+           int32_t block_table_stride, const int32_t* seq_lens, const float* signs, const float* centroids,
+           float scale, int32_t num_kv_splits, void* workspace, hipStream_t stream) {
+  DecodeArgs a;
+  a.query = static_cast<const uint16_t*>(query);
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.signs = signs;
+  a.centroids = centroids;
+  a.partials = static_cast<float*>(workspace);
+  a.qscale = scale * kLog2e;
+  a.q_bf16 = q_dtype == TQ_BF16;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.head_groups = (a.group + 15) / 16;
+  a.block_size = block_size;
+  a.bt_stride = block_table_stride;
+  a.num_splits = num_kv_splits;
+  const int64_t nblocks = static_cast<int64_t>(batch) * num_kv_heads * a.head_groups * num_kv_splits;
+  if (nblocks > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
+  switch (layout->preset) {
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, nblocks, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, nblocks, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, nblocks, stream);
+  }
+  return TQ_EPRESET;
+}
+
+int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const void* workspace, void* out,
+           int32_t out_dtype, float* lse_out, hipStream_t stream) {
+  const int rows = batch * num_q_heads;
+  hipLaunchKernelGGL(tq_decode_stage2_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
+                     static_cast<const float*>(workspace), rows, num_kv_splits, out, out_dtype, lse_out);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+}  // namespace
+
+extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
+                                int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
+                                const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
+                                int32_t num_kv_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = tq::validate_decode(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
+                               block_size, block_table, block_table_stride, seq_lens, signs, centroids,
+                               num_kv_splits, workspace, workspace_bytes);
+  if (st != TQ_OK || batch == 0) return st;
+  return stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
+                block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace,
+                static_cast<hipStream_t>(stream));
+}
+
+extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
+                                const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                                float* lse_out, void* stream) {
+  int st = tq::validate_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace, workspace_bytes, out,
+                               out_dtype);
+  if (st != TQ_OK || batch == 0) return st;
+  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out,
+                static_cast<hipStream_t>(stream));
+}
+
+extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache,
+                                   int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                   int32_t block_table_stride, const int32_t* seq_lens, const float* signs,
+                                   const float* centroids, float scale, int32_t num_kv_splits, void* workspace,
+                                   size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
+                                   void* stream) {
+  int st = tq_decode_validate(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
+                              block_size, block_table, block_table_stride, seq_lens, signs, centroids, num_kv_splits,
+                              workspace, workspace_bytes, out, out_dtype);
+  if (st != TQ_OK || batch == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
+              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace, s);
+  if (st != TQ_OK) return st;
+  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out, s);
+}

@@ -1,0 +1,173 @@
+"""Shared set-up of the GPU parity tests: seeded inputs from workloads.py,
+the oracle's result on them, and the HIP library's result on the same
+bytes, plus the comparison rules (spec tolerances)."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle as O
+import workloads as W
+
+D = 128
+DECODE_RTOL = 5e-3  # max_i |o - o_ref| / max_i |o_ref| per (sequence, query head)
+LSE_ATOL = 5e-3
+GAMMA_RTOL = 1e-3
+BOUNDARY_EPS = 1e-6
+MISMATCH_FRAC = 1e-5
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as t
+
+    return t
+
+
+def dev16(bits: np.ndarray, dtype: str):
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return x.view(t.bfloat16 if dtype == "bf16" else t.float16)
+
+
+def oracle_tables(lay):
+    if lay.key_fp8:
+        return None, None
+    return O.codebook_tables(D, lay.key_bits)
+
+
+def gpu_tables(lay_c, signs):
+    import quantized_decode_attention_tq_amd as tq
+
+    return tq.Tables(lay_c, signs)
+
+
+# ------------------------------------------------------------------ store
+
+
+def compare_slots(lay, got: np.ndarray, want: np.ndarray, U: np.ndarray, b32):
+    """got/want: (rows, slot) bytes of the same rows; U: (rows, D) oracle key
+    units (MSE presets) used to excuse code mismatches next to a boundary.
+    Returns the number of key-code mismatches (all near a boundary)."""
+    assert got.shape == want.shape
+    if lay.key_fp8:
+        np.testing.assert_array_equal(got, want)
+        return 0
+    kd = lay.key_data_bytes
+    # value region and padding: bit-exact
+    np.testing.assert_array_equal(got[:, kd + 2 :], want[:, kd + 2 :])
+    cg = O.unpack_lsb(got[:, :kd], lay.key_bits, D)
+    cw = O.unpack_lsb(want[:, :kd], lay.key_bits, D)
+    bad = np.argwhere(cg != cw)
+    if len(bad):
+        u = U[bad[:, 0], bad[:, 1]]
+        dist = np.min(np.abs(u[:, None] - np.asarray(b32, np.float64)[None, :]), axis=1)
+        assert np.all(dist < BOUNDARY_EPS), f"code mismatch away from a boundary: {dist.max()}"
+        assert np.all(np.abs(cg[bad[:, 0], bad[:, 1]] - cw[bad[:, 0], bad[:, 1]]) == 1)
+    assert len(bad) <= MISMATCH_FRAC * cg.size, f"{len(bad)} code mismatches of {cg.size}"
+    gg = got[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+    gw = want[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+    np.testing.assert_allclose(gg, gw, rtol=GAMMA_RTOL, atol=0)
+    return len(bad)
+
+
+# ------------------------------------------------------------------ decode
+
+
+class DecodeCase:
+    """Inputs of one decode workload, the oracle cache, and device copies."""
+
+    def __init__(self, w: W.Workload, need_oracle_cache: bool = True):
+        t = torch()
+        import quantized_decode_attention_tq_amd as tq
+
+        self.w = w
+        self.lay = O.layout(w.preset, D)
+        self.lay_c = tq.layout_init(w.preset, D)
+        self.lens = W.seq_lens(w)
+        self.table = W.block_table(w)
+        self.nb = W.num_blocks(w)
+        self.signs = W.signs(w)
+        self.K, self.V = W.kv_all(w)
+        self.qbits = W.queries(w)
+        self.c32, self.b32 = oracle_tables(self.lay)
+        self.tab = gpu_tables(self.lay_c, self.signs)
+        self.shape = (self.nb, w.block_size, w.num_kv_heads, self.lay.slot_size_aligned)
+        self.cache_o = None
+        if need_oracle_cache:
+            self.cache_o = np.zeros(self.shape, np.uint8)
+            for b in range(w.batch):
+                O.store_rows(self.lay, O.widen(self.K[b], w.dtype), O.widen(self.V[b], w.dtype),
+                             W.slot_mapping_for_sequence(w, b, self.table, self.lens), self.cache_o, self.signs,
+                             self.c32, self.b32)
+        self.q = dev16(self.qbits, w.dtype)
+        self.bt = t.from_numpy(self.table).cuda()
+        self.sl = t.from_numpy(self.lens).cuda()
+        self.scale = 1.0 / math.sqrt(D)
+
+    def gpu_store_all(self):
+        """Fresh device cache filled by tq_store, one call per sequence."""
+        t = torch()
+        import quantized_decode_attention_tq_amd as tq
+
+        cache = t.zeros(self.shape, dtype=t.uint8, device="cuda")
+        for b in range(self.w.batch):
+            if self.lens[b] == 0:
+                continue
+            slots = t.from_numpy(W.slot_mapping_for_sequence(self.w, b, self.table, self.lens)).cuda()
+            tq.store(self.lay_c, dev16(self.K[b], self.w.dtype), dev16(self.V[b], self.w.dtype), slots, cache,
+                     self.tab.signs, self.tab.centroids, self.tab.boundaries)
+        return cache
+
+    def gpu_decode(self, cache, num_kv_splits, out_dtype=None):
+        import quantized_decode_attention_tq_amd as tq
+
+        t = torch()
+        out, lse = tq.decode(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids,
+                             self.scale, num_kv_splits, out_dtype=out_dtype or t.float32)
+        t.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+    def oracle_decode(self, rows=None, cache=None):
+        q = O.widen(self.qbits, self.w.dtype)
+        return O.decode(self.lay, q, self.cache_o if cache is None else cache, self.table, self.lens, self.signs,
+                        self.c32, self.scale, rows=rows)
+
+    def oracle_decode_rows_from_inputs(self, rows):
+        """Oracle result for (b, hq) rows, storing only the needed sequence /
+        KV head from the raw inputs (full-size workloads)."""
+        w = self.w
+        g = w.num_q_heads // w.num_kv_heads
+        q = O.widen(self.qbits, w.dtype)
+        R = None if self.lay.key_fp8 else O.rotation(self.signs.astype(np.float64))
+        res = {}
+        for b, hq in rows:
+            hk = hq // g
+            L = int(self.lens[b])
+            slots = O.encode_slots(self.lay, O.widen(self.K[b][:, hk], w.dtype), O.widen(self.V[b][:, hk], w.dtype),
+                                   R, self.c32, self.b32)
+            Kd, Vd = O.decode_slots(self.lay, slots, self.c32)
+            qq = q[b, hq] if self.lay.key_fp8 else R @ q[b, hq]
+            res[(b, hq)] = O.attend(qq, Kd[:L], Vd[:L], self.scale)
+        return res
+
+
+def check_decode(out, lse, ref_out, ref_lse, rows):
+    worst = 0.0
+    for b, hq in rows:
+        ro, rl = ref_out[b, hq], ref_lse[b, hq]
+        if rl == -math.inf:
+            assert np.all(out[b, hq] == 0) and lse[b, hq] == -math.inf, (b, hq)
+            continue
+        err = np.max(np.abs(out[b, hq] - ro)) / max(np.max(np.abs(ro)), 1e-30)
+        worst = max(worst, err)
+        assert err <= DECODE_RTOL, (b, hq, err)
+        assert abs(lse[b, hq] - rl) <= LSE_ATOL * max(1.0, abs(rl)), (b, hq, lse[b, hq], rl)
+    return worst

@@ -1,0 +1,149 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and its host-side functions (layout, codebook solvers, signs,
+workspace size, argument validation) agree with the oracle.  No GPU work is
+launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import quantized_decode_attention_tq_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tq_\w+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _header_symbols()
+    assert declared == set(tq.ABI_SYMBOLS), declared ^ set(tq.ABI_SYMBOLS)
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in tq.version()
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_layout_matches_oracle(preset, D):
+    got = tq.layout_init(preset, D).as_dict()
+    want = O.layout(preset, D)
+    for k in ("key_data_bytes", "key_packed_size", "value_data_bytes", "value_packed_size", "slot_size",
+              "slot_size_aligned", "key_bits", "value_bits"):
+        assert got[k] == getattr(want, k), k
+    assert got["key_fp8"] == int(want.key_fp8) and got["norm_correction"] == int(want.norm_correction)
+    assert got["n_centroids"] == want.n_centroids
+    assert got["preset"] == list(O.PRESETS).index(preset)
+
+
+def test_kv_cache_shape_and_presets():
+    for p in O.PRESETS:
+        L = tq.layout_init(p)
+        for bs in O.BLOCK_SIZES:
+            assert tq.kv_cache_shape(L, 37, bs, 8) == O.kv_cache_shape(O.layout(p, 128), 37, bs, 8)
+        with pytest.raises(tq.TQError) as e:
+            tq.kv_cache_shape(L, 37, 24, 8)
+        assert e.value.status == tq.TQ_EBLOCK
+    with pytest.raises(tq.TQError) as e:
+        tq.preset_from_name("turboquant_5bit")
+    assert e.value.status == tq.TQ_EPRESET
+    with pytest.raises(tq.TQError) as e:
+        tq.layout_init(7)
+    assert e.value.status == tq.TQ_EPRESET
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_lloyd_max_exact_matches_oracle(bits, d):
+    c, b = tq.lloyd_max(d, bits, 0)
+    oc, ob = O.codebook_tables(d, bits, "exact")
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(b, ob)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_pages_trapz_matches_oracle(bits):
+    c, b = tq.lloyd_max(128, bits, 1)
+    oc, ob = O.codebook_tables(128, bits, "pages-trapz")
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(b, ob)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 42, 1337, 2 ** 63 + 5])
+def test_wht_signs_match_oracle_splitmix64(seed):
+    np.testing.assert_array_equal(tq.wht_signs(256, seed), O.wht_signs(256, seed).astype(np.float32))
+
+
+def test_workspace_bytes():
+    for B, Hq, S in ((1, 2, 1), (32, 32, 16), (4, 40, 32), (64, 64, 8)):
+        n = tq.decode_workspace_bytes(B, Hq, 128, S)
+        assert n >= O.workspace_bytes(B, Hq, 128, S) and n % 256 == 0 and n - O.workspace_bytes(B, Hq, 128, S) < 256
+
+
+# ------------------------------------------------------------ validation
+# The *_validate entry points check arguments on the host and touch no
+# memory, so fake (aligned, non-null) addresses are fine here.
+
+A = 0x10000  # a 16-byte aligned fake address
+
+
+def _store_validate(L, **kw):
+    args = dict(key=A, value=A, in_dtype=tq.TQ_BF16, N=4, Hk=8, ks=1024, vs=1024, slots=A, cache=A, nb=10, bs=16,
+                signs=A, cent=A, bnd=A)
+    args.update(kw)
+    return tq._lib.tq_store_validate(ctypes.byref(L), args["key"], args["value"], args["in_dtype"], args["N"],
+                                     args["Hk"], args["ks"], args["vs"], args["slots"], args["cache"], args["nb"],
+                                     args["bs"], args["signs"], args["cent"], args["bnd"])
+
+
+def test_store_validation_codes():
+    L = tq.layout_init("turboquant_3bit_nc")
+    assert _store_validate(L) == tq.TQ_OK
+    assert _store_validate(L, N=0, key=None, value=None, slots=None, cache=None) == tq.TQ_OK  # N = 0: no-op
+    assert _store_validate(L, bs=24) == tq.TQ_EBLOCK
+    assert _store_validate(L, in_dtype=tq.TQ_F32) == tq.TQ_EDTYPE
+    assert _store_validate(L, key=None) == tq.TQ_EINVAL
+    assert _store_validate(L, key=A + 2) == tq.TQ_EINVAL  # misaligned
+    assert _store_validate(L, ks=1020) == tq.TQ_EINVAL  # stride below Hk*D
+    assert _store_validate(L, signs=None) == tq.TQ_EINVAL
+    assert _store_validate(L, N=-1) == tq.TQ_EINVAL
+    assert _store_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None, bnd=None) == tq.TQ_OK
+    assert _store_validate(tq.layout_init("turboquant_3bit_nc", 64)) == tq.TQ_EHEADDIM
+    bad = tq.layout_init("turboquant_3bit_nc")
+    bad.slot_size_aligned = 104  # layout not produced by tq_layout_init
+    assert _store_validate(bad) == tq.TQ_EINVAL
+
+
+def _decode_validate(L, **kw):
+    args = dict(q=A, qd=tq.TQ_BF16, B=4, Hq=32, Hk=8, cache=A, nb=100, bs=16, bt=A, bts=64, sl=A, signs=A, cent=A,
+                S=8, ws=A, wsb=tq.decode_workspace_bytes(4, 32, 128, 8), out=A, od=tq.TQ_F32)
+    args.update(kw)
+    return tq._lib.tq_decode_validate(ctypes.byref(L), args["q"], args["qd"], args["B"], args["Hq"], args["Hk"],
+                                      args["cache"], args["nb"], args["bs"], args["bt"], args["bts"], args["sl"],
+                                      args["signs"], args["cent"], args["S"], args["ws"], args["wsb"], args["out"],
+                                      args["od"])
+
+
+def test_decode_validation_codes():
+    L = tq.layout_init("turboquant_k3v4_nc")
+    assert _decode_validate(L) == tq.TQ_OK
+    assert _decode_validate(L, Hq=33) == tq.TQ_EGQA
+    assert _decode_validate(L, Hk=0) == tq.TQ_EGQA
+    assert _decode_validate(L, bs=8) == tq.TQ_EBLOCK
+    assert _decode_validate(L, wsb=1024) == tq.TQ_EWORKSPACE
+    assert _decode_validate(L, qd=tq.TQ_F32) == tq.TQ_EDTYPE
+    assert _decode_validate(L, od=7) == tq.TQ_EDTYPE
+    assert _decode_validate(L, S=0) == tq.TQ_EINVAL
+    assert _decode_validate(L, sl=None) == tq.TQ_EINVAL
+    assert _decode_validate(L, ws=A + 8) == tq.TQ_EINVAL
+    assert _decode_validate(L, signs=None) == tq.TQ_EINVAL
+    assert _decode_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None) == tq.TQ_OK
+    assert _decode_validate(L, B=0, q=None, sl=None, bt=None, ws=None, out=None) == tq.TQ_OK

@@ -1,0 +1,129 @@
+"""tq_decode_attention on the GPU against the oracle's exact softmax attention
+over the dequantized cache: per (sequence, query head) max |o - o_ref| /
+max |o_ref| <= 5e-3 (fp32 output), LSE within 5e-3.  Checked on identical
+cache bytes (written by the oracle) and end to end (GPU store + GPU decode).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import gpu_case as G
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ALL_ROWS = None
+
+
+def _rows(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
+
+
+def _small(preset, lens, Hq, Hk, bs, dtype="bf16", dist="normal_chscale", seed=31):
+    return W.Workload("t", preset, len(lens), Hq, Hk, bs, dtype, dist, seed=seed, lens=tuple(lens), pool_factor=1.5,
+                      chscale_range=(0.5, 4.0), outliers=4, outlier_scale=8.0)
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_decode_parity_identical_bytes(preset, S):
+    w = _small(preset, [1, 37, 300, 16], Hq=8, Hk=2, bs=16)
+    G.log(f"decode {preset} S={S} lens={w.lens}")
+    c = G.DecodeCase(w)
+    import torch
+
+    cache = torch.from_numpy(c.cache_o).cuda()
+    out, lse = c.gpu_decode(cache, S)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_decode_end_to_end_block_sizes(preset, bs):
+    w = _small(preset, [bs - 1, bs, bs + 1, 3 * bs + 5, 0], Hq=4, Hk=2, bs=bs, seed=40 + bs)
+    G.log(f"decode e2e {preset} bs={bs} lens={w.lens}")
+    c = G.DecodeCase(w)
+    cache = c.gpu_store_all()
+    out, lse = c.gpu_decode(cache, 4)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 5, 8, 16, 20])
+def test_decode_gqa_groups(g):
+    w = _small("turboquant_k3v4_nc", [70, 129], Hq=2 * g, Hk=2, bs=32, seed=60 + g)
+    G.log(f"decode gqa g={g}")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 2)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+def test_decode_tiny_workload_and_out_dtypes():
+    """The tiny workload (4bit_nc, 256 tokens, GQA 2, fp16, sequential
+    blocks): store all 256 tokens, decode one query."""
+    import torch
+
+    w = W.WORKLOADS["tiny"]
+    G.log("decode tiny")
+    c = G.DecodeCase(w)
+    cache = c.gpu_store_all()
+    ref, rlse = c.oracle_decode()
+    for S in (1, 4, 16, 40):
+        out, lse = c.gpu_decode(cache, S)
+        G.check_decode(out, lse, ref, rlse, _rows(w))
+    for dt in (torch.float16, torch.bfloat16):
+        out, lse = c.gpu_decode(cache, 4, out_dtype=dt)
+        tol = 2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11
+        for b, h in _rows(w):
+            err = np.max(np.abs(out[b, h] - ref[b, h])) / np.max(np.abs(ref[b, h]))
+            assert err <= G.DECODE_RTOL + tol, (dt, err)
+
+
+def test_decode_special_inputs():
+    """Zero query: uniform attention -> mean of the values.  Peaked query:
+    output follows the one matching token."""
+    import torch
+
+    w = _small("turboquant_4bit_nc", [50, 77], Hq=4, Hk=2, bs=16, seed=5)
+    c = G.DecodeCase(w)
+    c.qbits[0] = 0
+    G.log("decode special inputs")
+    c.q = G.dev16(c.qbits, w.dtype)
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 2)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+    _, Vd = O.gather_sequence(c.lay, c.cache_o, c.table[0], 50, 0, c.c32)
+    np.testing.assert_allclose(out[0, 0], Vd.mean(axis=0), rtol=2e-3, atol=2e-3 * np.abs(Vd).max())
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,S,rows", [
+    ("llama8b", 8, [(0, 0), (7, 13), (31, 31)]),
+    ("longctx", 32, [(0, 0), (3, 39), (2, 17)]),
+    ("qwen32b", 8, [(0, 0), (40, 63), (63, 9)]),
+])
+def test_decode_full_size_sampled(name, S, rows):
+    """Full-size workloads in the benchmark's launch configuration: the GPU
+    stores and decodes everything; the oracle recomputes sampled rows from
+    the raw inputs."""
+    w = W.WORKLOADS[name]
+    G.log(f"decode full-size {name} S={S}: generating inputs")
+    c = G.DecodeCase(w, need_oracle_cache=False)
+    G.log(f"decode full-size {name}: store")
+    cache = c.gpu_store_all()
+    G.log(f"decode full-size {name}: decode")
+    out, lse = c.gpu_decode(cache, S)
+    assert np.all(np.isfinite(out))
+    G.log(f"decode full-size {name}: oracle rows {rows}")
+    res = c.oracle_decode_rows_from_inputs(rows)
+    for (b, hq), (ro, rl) in res.items():
+        err = np.max(np.abs(out[b, hq] - ro)) / np.max(np.abs(ro))
+        assert err <= G.DECODE_RTOL, (b, hq, err)
+        assert abs(lse[b, hq] - rl) <= G.LSE_ATOL * max(1.0, abs(rl))

@@ -1,0 +1,94 @@
+"""GPU checks of the hardware behaviour the kernels rely on, each with small,
+in-bounds, single-wave probe launches: MFMA lane layouts, fp16 subnormal
+operands through MFMA, the FP8 -> fp16 convert, and the device byte-permute
+helpers against their host model."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import probe
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(7)
+
+
+def _run_mfma(kind, a_lanes, b_lanes):
+    import torch
+
+    L = probe.lib()
+    a = torch.from_numpy(np.ascontiguousarray(a_lanes).view(np.int32)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(b_lanes).view(np.int32)).cuda()
+    d = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    f = L.tq_probe_mfma_16x16x32_f16 if kind == 32 else L.tq_probe_mfma_16x16x16_f16
+    print(f"probe mfma 16x16x{kind}", flush=True)
+    assert f(a.data_ptr(), b.data_ptr(), d.data_ptr()) == 0
+    return d.cpu().numpy()
+
+
+def _lanes(M, per):  # M: [16 rows/cols][K]; lane l holds row l%16, k = per*(l//16) + e
+    out = np.zeros((64, per), np.float16)
+    for l in range(64):
+        out[l] = M[l % 16, per * (l // 16) : per * (l // 16) + per]
+    return out.view(np.uint32)
+
+
+@pytest.mark.parametrize("K", [32, 16])
+def test_mfma_layout(K):
+    per = K // 4
+    A = RNG.integers(-8, 9, (16, K)).astype(np.float16)  # rows = M
+    B = RNG.integers(-8, 9, (K, 16)).astype(np.float16)  # cols = N
+    d = _run_mfma(K, _lanes(A, per), _lanes(B.T, per))
+    C = A.astype(np.float64) @ B.astype(np.float64)
+    for l in range(64):
+        for r in range(4):
+            assert d[l, r] == C[4 * (l // 16) + r, l % 16], (l, r)
+
+
+def test_mfma_f16_subnormal_operands_are_exact():
+    """Value codes enter the PV product as fp16 subnormals code * 2^(p-24)."""
+    codes = RNG.integers(0, 16, (16, 16))
+    pos = RNG.integers(0, 7, (16, 16))
+    A = (codes * 2.0 ** (pos - 24)).astype(np.float16)
+    assert np.all(A.astype(np.float64) == codes * 2.0 ** (pos - 24))
+    B = RNG.integers(-60, 61, (16, 16)).astype(np.float16)  # sums stay exact in fp32
+    d = _run_mfma(16, _lanes(A, 4), _lanes(B.T, 4))
+    C = A.astype(np.float64) @ B.astype(np.float64)
+    for l in range(64):
+        for r in range(4):
+            assert d[l, r] == np.float32(C[4 * (l // 16) + r, l % 16]), (l, r, d[l, r], C[4 * (l // 16) + r, l % 16])
+
+
+def test_fp8_to_f16_convert_all_codes():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    words = codes.view(np.uint32)  # 64 dwords, bytes 4i..4i+3
+    din = torch.from_numpy(words.view(np.int32)).cuda()
+    dout = torch.zeros(128, dtype=torch.int32, device="cuda")
+    print("probe cvt fp8->f16", flush=True)
+    assert probe.lib().tq_probe_cvt_fp8_f16(din.data_ptr(), dout.data_ptr(), 64) == 0
+    halves = dout.cpu().numpy().view(np.uint16)  # order: bytes 0,1 then 2,3 of each dword
+    got = halves.view(np.float16).astype(np.float64)
+    want = O.fp8_e4m3fn_decode(codes)
+    finite = np.isfinite(want)
+    np.testing.assert_array_equal(got[finite], want[finite])
+    assert np.all(np.isnan(got[~finite]))
+
+
+@pytest.mark.parametrize("op", ["perm", "alignbyte", "key3_selectors", "lut8", "lut16", "val4_pairs", "val3_pairs",
+                                "f32_to_e4m3"])
+def test_device_bits_match_host_model(op):
+    n = 4096
+    inp = RNG.integers(0, 2 ** 32, (n, probe.N_IN), dtype=np.uint64).astype(np.uint32)
+    if op == "perm":
+        inp[:, 2] = RNG.integers(0, 16, (n, 4)).astype(np.uint32) @ np.array([1, 256, 65536, 2 ** 24], np.uint32)
+    if op in ("lut8", "lut16"):
+        inp[:, 0] &= 0x0F0F0F0F if op == "lut16" else 0x07070707
+    if op == "f32_to_e4m3":
+        x = np.concatenate([RNG.standard_normal(n // 2) * 100, RNG.standard_normal(n // 2) * 1e-3]).astype(np.float32)
+        x[:4] = [np.inf, -np.inf, np.nan, -0.0]
+        inp[:, 0] = x.view(np.uint32)
+    print(f"probe bits {op}", flush=True)
+    np.testing.assert_array_equal(probe.bits_device(op, inp), probe.bits_host(op, inp))

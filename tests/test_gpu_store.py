@@ -1,0 +1,112 @@
+"""tq_store on the GPU against the oracle: FP8 keys, value codes, value scale
+and zero bit-exact; Lloyd-Max key codes bit-exact except next to a bucket
+boundary (|u - b| < 1e-6, at most 1e-5 of the coordinates); stored key
+norms within 1e-3 relative; bytes outside the addressed slots untouched."""
+
+import numpy as np
+import pytest
+
+import gpu_case as G
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_store(preset, N, Hk, bs, dtype, seed, skip_every=0, sentinel=0xA5):
+    import torch
+    import quantized_decode_attention_tq_amd as tq
+
+    G.log(f"store preset={preset} N={N} Hk={Hk} bs={bs} dtype={dtype} seed={seed}")
+    K, V, slots, nb = W.store_inputs(num_tokens=N, num_kv_heads=Hk, block_size=bs, seed=seed, dtype=dtype)
+    nb += 2  # spare blocks stay untouched
+    if skip_every:
+        slots[::skip_every] = -1
+    lay = O.layout(preset, G.D)
+    lay_c = tq.layout_init(preset)
+    signs = W.signs(seed)
+    c32, b32 = G.oracle_tables(lay)
+    tab = G.gpu_tables(lay_c, signs)
+    shape = (nb, bs, Hk, lay.slot_size_aligned)
+    cache = torch.full(shape, sentinel, dtype=torch.uint8, device="cuda")
+    tq.store(lay_c, G.dev16(K, dtype), G.dev16(V, dtype), torch.from_numpy(slots).cuda(), cache, tab.signs,
+             tab.centroids, tab.boundaries)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    return lay, K, V, slots, got, signs, c32, b32, shape, sentinel
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_store_parity_small(preset, dtype):
+    lay, K, V, slots, got, signs, c32, b32, shape, sentinel = _run_store(preset, 1237, 3, 16, dtype, 11,
+                                                                         skip_every=13)
+    want = np.full(shape, sentinel, np.uint8)
+    O.store_rows(lay, O.widen(K, dtype), O.widen(V, dtype), slots, want, signs, c32, b32)
+    # untouched slots: identical sentinel bytes
+    written = np.zeros(shape[:3], bool)
+    keep = slots >= 0
+    written[slots[keep] // shape[1], slots[keep] % shape[1]] = True
+    np.testing.assert_array_equal(got[~written], want[~written])
+    # written slots
+    N, Hk = K.shape[:2]
+    rows_got = got[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
+    rows_want = want[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
+    U = None
+    if not lay.key_fp8:
+        U = O.key_units(lay, O.widen(K[keep], dtype).reshape(-1, G.D), O.rotation(signs.astype(np.float64)))
+    G.compare_slots(lay, rows_got, rows_want, U, b32)
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+def test_store_parity_full_sweep_sampled(preset):
+    """The store sweep at full size (65536 tokens x 8 KV heads, bs 32), as
+    the benchmark launches it; the oracle checks 4096 sampled rows."""
+    s = W.STORE_WORKLOAD
+    lay, K, V, slots, got, signs, c32, b32, shape, _ = _run_store(preset, s["num_tokens"], s["num_kv_heads"],
+                                                                 s["block_size"], s["dtype"], s["seed"])
+    rng = np.random.default_rng(99)
+    tok = rng.choice(s["num_tokens"], 512, replace=False)
+    Kr = O.widen(K[tok], s["dtype"]).reshape(-1, G.D)
+    Vr = O.widen(V[tok], s["dtype"]).reshape(-1, G.D)
+    R = None if lay.key_fp8 else O.rotation(signs.astype(np.float64))
+    want = O.encode_slots(lay, Kr, Vr, R, c32, b32)
+    rows = got[slots[tok] // shape[1], slots[tok] % shape[1]].reshape(-1, lay.slot_size_aligned)
+    G.compare_slots(lay, rows, want, None if lay.key_fp8 else O.key_units(lay, Kr, R), b32)
+
+
+def test_store_edge_cases():
+    import torch
+    import quantized_decode_attention_tq_amd as tq
+
+    lay_c = tq.layout_init("turboquant_3bit_nc")
+    tab = G.gpu_tables(lay_c, W.signs(3))
+    cache = torch.full((4, 16, 2, 102), 7, dtype=torch.uint8, device="cuda")
+    k = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    G.log("store N=0")
+    tq.store(lay_c, k, k, torch.zeros(0, dtype=torch.int64, device="cuda"), cache, tab.signs, tab.centroids,
+             tab.boundaries)  # no-op
+    G.log("store all slots negative")
+    k = torch.randn((5, 2, 128), device="cuda").to(torch.bfloat16)
+    tq.store(lay_c, k, k, torch.full((5,), -1, dtype=torch.int64, device="cuda"), cache, tab.signs, tab.centroids,
+             tab.boundaries)
+    torch.cuda.synchronize()
+    assert torch.all(cache == 7)
+    # zero key and constant value rows, fused-QKV style token stride
+    qkv = torch.zeros((6, 8 * 128), dtype=torch.bfloat16, device="cuda")
+    qkv[:, 2 * 128 : 4 * 128] = torch.randn((6, 256), device="cuda").to(torch.bfloat16)
+    qkv[1, 2 * 128 : 3 * 128] = 0.0
+    qkv[:, 4 * 128 : 6 * 128] = 2.5
+    keys = qkv[:, 2 * 128 : 4 * 128]
+    vals = qkv[:, 4 * 128 : 6 * 128]
+    slots = torch.tensor([0, 5, 17, 33, 40, 63], dtype=torch.int64, device="cuda")
+    G.log("store strided rows")
+    tq.store(lay_c, keys, vals, slots, cache, tab.signs, tab.centroids, tab.boundaries)
+    torch.cuda.synchronize()
+    lay = O.layout("turboquant_3bit_nc", 128)
+    c32, b32 = G.oracle_tables(lay)
+    want = np.full((4, 16, 2, 102), 7, np.uint8)
+    kb = keys.float().cpu().numpy().reshape(6, 2, 128).astype(np.float64)
+    vb = vals.float().cpu().numpy().reshape(6, 2, 128).astype(np.float64)
+    O.store_rows(lay, kb, vb, slots.cpu().numpy(), want, W.signs(3), c32, b32)
+    np.testing.assert_array_equal(cache.cpu().numpy(), want)

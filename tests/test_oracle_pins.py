@@ -501,3 +501,39 @@ def test_block_table_indirection():
         O.store(lay, k, v, table[np.arange(L) // bs] * bs + np.arange(L) % bs, cache, np.ones(D), c32, b32)
         outs.append(O.decode(lay, q, cache, table[None], np.array([L]), np.ones(D), c32, 0.1)[0])
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("preset", list(O.PRESETS))
+def test_row_vectorized_store_equals_per_row_store(preset):
+    lay = O.layout(preset, D)
+    rng = np.random.default_rng(21)
+    c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(D, lay.key_bits)
+    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    N, Hk, bs = 40, 3, 16
+    k = O.widen(W.to_bits(rng.standard_normal((N, Hk, D)) * rng.uniform(0.1, 8, (1, Hk, D)), "bf16"), "bf16")
+    v = O.widen(W.to_bits(rng.standard_normal((N, Hk, D)) * 3, "bf16"), "bf16")
+    k[3, 1] = 0.0  # zero key
+    v[5, 2] = 1.5  # constant value row
+    slots = rng.permutation(4 * bs)[:N]
+    slots[7] = -1
+    c1 = np.zeros((4, bs, Hk, lay.slot_size_aligned), np.uint8)
+    c2 = c1.copy()
+    O.store(lay, k, v, slots, c1, s, c32, b32)
+    O.store_rows(lay, k, v, slots, c2, s, c32, b32)
+    np.testing.assert_array_equal(c1, c2)
+
+
+@pytest.mark.parametrize("preset", list(O.PRESETS))
+def test_row_vectorized_decode_equals_per_slot_decode(preset):
+    lay = O.layout(preset, D)
+    rng = np.random.default_rng(22)
+    c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(D, lay.key_bits)
+    R = O.rotation(np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0))
+    k = O.widen(W.to_bits(rng.standard_normal((30, D)) * 2, "bf16"), "bf16")
+    v = O.widen(W.to_bits(rng.standard_normal((30, D)), "bf16"), "bf16")
+    slots = O.encode_slots(lay, k, v, R, c32, b32)
+    K, V = O.decode_slots(lay, slots, c32)
+    for i in range(30):
+        ki, vi = O.decode_slot(lay, slots[i], c32)
+        np.testing.assert_array_equal(K[i], ki)
+        np.testing.assert_array_equal(V[i], vi)

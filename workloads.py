@@ -53,6 +53,7 @@ class Workload:
     dist: str  # "normal_outliers" | "normal_chscale" | "student_t"
     seed: int
     seq_len: int = 0  # fixed context length (0 -> drawn, see len_range)
+    lens: tuple = ()  # explicit per-sequence lengths (overrides seq_len / len_range)
     len_range: tuple = (0, 0)
     num_kv_splits: int = 0  # 0 -> caller's choice
     pool_factor: float = 1.0  # pool blocks = factor * needed
@@ -96,9 +97,9 @@ def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
-        rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-        return rounded.astype(np.uint16)
+        # round to nearest even in uint32 (finite inputs: no carry out of 32 bits)
+        u = x.view(np.uint32)
+        return ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     raise ValueError(dtype)
 
 
@@ -112,6 +113,8 @@ def _rng(*key) -> np.random.Generator:
 
 
 def seq_lens(w: Workload) -> np.ndarray:
+    if w.lens:
+        return np.array(w.lens, dtype=np.int32)
     if w.seq_len:
         return np.full(w.batch, w.seq_len, dtype=np.int32)
     lo, hi = w.len_range
@@ -133,11 +136,11 @@ def block_table(w: Workload) -> np.ndarray:
     (those entries are never read)."""
     need = blocks_needed(w)
     nb = num_blocks(w)
+    width = max(1, int(need.max()))
     if w.sequential_table:
         ids = np.arange(nb, dtype=np.int64)
     else:
         ids = _rng(w.seed, 12).permutation(nb)
-    width = int(need.max())
     tab = np.full((w.batch, width), -1, dtype=np.int32)
     pos = 0
     for b in range(w.batch):
@@ -162,13 +165,16 @@ def _outlier_channels(w: Workload) -> np.ndarray:
     return _rng(w.seed, 15).choice(w.head_dim, size=w.outliers, replace=False)
 
 
-def kv_sequence(w: Workload, b: int, lens=None):
-    """(K, V) of sequence b: uint16 bits of shape (L_b, Hk, D) each."""
-    L = int((seq_lens(w) if lens is None else lens)[b])
-    shape = (L, w.num_kv_heads, w.head_dim)
+CHUNK = 8192  # tokens per independently seeded piece of a sequence
+
+
+def _kv_chunk(w: Workload, b: int, c: int, L: int):
+    """Tokens [c*CHUNK, min(L, (c+1)*CHUNK)) of sequence b: (K, V) uint16 bits."""
+    n = min(L, (c + 1) * CHUNK) - c * CHUNK
+    shape = (n, w.num_kv_heads, w.head_dim)
     out = []
     for which in (0, 1):
-        r = _rng(w.seed, 16, b, which)
+        r = _rng(w.seed, 16, b, which, c)
         if w.dist == "student_t":
             z = r.standard_normal(shape, dtype=np.float32)
             g = r.standard_gamma(2.5, shape, dtype=np.float32) * np.float32(2.0 / 5.0)
@@ -183,12 +189,43 @@ def kv_sequence(w: Workload, b: int, lens=None):
     return out[0], out[1]
 
 
+def kv_sequence(w: Workload, b: int, lens=None, threads: int = 1):
+    """(K, V) of sequence b: uint16 bits of shape (L_b, Hk, D) each."""
+    L = int((seq_lens(w) if lens is None else lens)[b])
+    K = np.empty((L, w.num_kv_heads, w.head_dim), np.uint16)
+    V = np.empty_like(K)
+
+    def fill(c):
+        k, v = _kv_chunk(w, b, c, L)
+        K[c * CHUNK : c * CHUNK + k.shape[0]] = k
+        V[c * CHUNK : c * CHUNK + v.shape[0]] = v
+
+    nchunks = -(-L // CHUNK)
+    if threads > 1 and nchunks > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(fill, range(nchunks)))
+    else:
+        for c in range(nchunks):
+            fill(c)
+    return K, V
+
+
 def kv_all(w: Workload, threads: int = 8):
-    """K, V for every sequence (lists), generated on a thread pool."""
+    """K, V for every sequence (lists), generated chunk-parallel."""
     lens = seq_lens(w)
+    Ks = [np.empty((int(L), w.num_kv_heads, w.head_dim), np.uint16) for L in lens]
+    Vs = [np.empty_like(k) for k in Ks]
+    jobs = [(b, c) for b in range(w.batch) for c in range(-(-int(lens[b]) // CHUNK))]
+
+    def fill(job):
+        b, c = job
+        k, v = _kv_chunk(w, b, c, int(lens[b]))
+        Ks[b][c * CHUNK : c * CHUNK + k.shape[0]] = k
+        Vs[b][c * CHUNK : c * CHUNK + v.shape[0]] = v
+
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        res = list(ex.map(lambda b: kv_sequence(w, b, lens), range(w.batch)))
-    return [k for k, _ in res], [v for _, v in res]
+        list(ex.map(fill, jobs))
+    return Ks, Vs
 
 
 def slot_mapping_for_sequence(w: Workload, b: int, table=None, lens=None) -> np.ndarray:
