@@ -540,8 +540,10 @@ def store_rows(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids
     N, Hk, D = key.shape
     bs = kv_cache.shape[1]
     R = None if lay.key_fp8 else rotation(np.asarray(signs, dtype=np.float64))
+    if N == 0:
+        return kv_cache
     slots = encode_slots(lay, key.reshape(N * Hk, D), value.reshape(N * Hk, D), R, centroids32,
-                         boundaries32).reshape(N, Hk, -1)
+                         boundaries32).reshape(N, Hk, lay.slot_size_aligned)
     m = np.asarray(slot_mapping, dtype=np.int64)
     keep = m >= 0
     kv_cache[m[keep] // bs, m[keep] % bs] = slots[keep]

@@ -52,9 +52,11 @@ def gpu_tables(lay_c, signs):
 # ------------------------------------------------------------------ store
 
 
-def compare_slots(lay, got: np.ndarray, want: np.ndarray, U: np.ndarray, b32):
-    """got/want: (rows, slot) bytes of the same rows; U: (rows, D) oracle key
-    units (MSE presets) used to excuse code mismatches next to a boundary.
+def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32):
+    """got/want: (rows, slot) bytes of the same rows; keys: (rows, D) float64
+    inputs of those rows (MSE presets) so that a key code may differ only
+    next to a bucket boundary.  Where codes differ the stored norm is checked
+    against nu / ||c[GPU codes]||, the norm those codes call for.
     Returns the number of key-code mismatches (all near a boundary)."""
     assert got.shape == want.shape
     if lay.key_fp8:
@@ -67,13 +69,19 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, U: np.ndarray, b32):
     cw = O.unpack_lsb(want[:, :kd], lay.key_bits, D)
     bad = np.argwhere(cg != cw)
     if len(bad):
-        u = U[bad[:, 0], bad[:, 1]]
+        U = O.key_units(lay, keys[np.unique(bad[:, 0])], O.rotation(np.asarray(signs, np.float64)))
+        row_idx = {r: i for i, r in enumerate(np.unique(bad[:, 0]))}
+        u = np.array([U[row_idx[r], j] for r, j in bad])
         dist = np.min(np.abs(u[:, None] - np.asarray(b32, np.float64)[None, :]), axis=1)
         assert np.all(dist < BOUNDARY_EPS), f"code mismatch away from a boundary: {dist.max()}"
         assert np.all(np.abs(cg[bad[:, 0], bad[:, 1]] - cw[bad[:, 0], bad[:, 1]]) == 1)
     assert len(bad) <= MISMATCH_FRAC * cg.size, f"{len(bad)} code mismatches of {cg.size}"
     gg = got[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     gw = want[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+    for r in np.unique(bad[:, 0]) if len(bad) else []:
+        nu = np.sqrt(np.sum(keys[r] ** 2))
+        chat = np.asarray(c32, np.float64)[cg[r]]
+        gw[r] = float(np.float16(nu / np.sqrt(np.sum(chat ** 2)))) if lay.norm_correction else nu
     np.testing.assert_allclose(gg, gw, rtol=GAMMA_RTOL, atol=0)
     return len(bad)
 

@@ -52,10 +52,7 @@ def test_store_parity_small(preset, dtype):
     N, Hk = K.shape[:2]
     rows_got = got[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
     rows_want = want[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    U = None
-    if not lay.key_fp8:
-        U = O.key_units(lay, O.widen(K[keep], dtype).reshape(-1, G.D), O.rotation(signs.astype(np.float64)))
-    G.compare_slots(lay, rows_got, rows_want, U, b32)
+    G.compare_slots(lay, rows_got, rows_want, O.widen(K[keep], dtype).reshape(-1, G.D), signs, c32, b32)
 
 
 @pytest.mark.parametrize("preset", O.PRESETS)
@@ -72,7 +69,7 @@ def test_store_parity_full_sweep_sampled(preset):
     R = None if lay.key_fp8 else O.rotation(signs.astype(np.float64))
     want = O.encode_slots(lay, Kr, Vr, R, c32, b32)
     rows = got[slots[tok] // shape[1], slots[tok] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rows, want, None if lay.key_fp8 else O.key_units(lay, Kr, R), b32)
+    G.compare_slots(lay, rows, want, Kr, signs, c32, b32)
 
 
 def test_store_edge_cases():
