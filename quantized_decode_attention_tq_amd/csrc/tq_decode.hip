@@ -124,46 +124,103 @@ __device__ __forceinline__ half4 as_half4(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
-// Key tile operand for one lane: token = lane % 16, its 32 dims of quarter q.
+// Byte offsets (lane constants) of what one lane loads for a 16-token tile,
+// relative to the tile's first slot row.  Block bases and the tile's first
+// row are multiples of 32 bytes, so the alignment of every address is a lane
+// constant too: unaligned fields are read as aligned dwords and realigned.
 template <int P>
-__device__ __forceinline__ void key_operand(const uint8_t* kslot, int q, const tq::Lut8& la, const tq::Lut8& lb,
-                                            half8 A[4]) {
+struct LaneOff {
+  uint32_t k, ksh;  // aligned-down key chunk start, its misalignment
+  uint32_t meta0;   // slot start of token 4q (token 4q+i is i rows further)
+  uint32_t vcol;    // byte offset of the lane's value-code column inside a slot
+};
+
+// Registers one tile's loads land in.
+template <int P>
+struct TileRegs {
+  uint32_t k[8];
+  uint32_t v[4][2];
+  uint32_t sz[4];  // fp16 scale | fp16 zero << 16
+  uint32_t gm[4];  // fp16 key norm (MSE keys)
+};
+
+template <int P>
+__device__ __forceinline__ LaneOff<P> lane_offsets(int hl, int q4, int hk, int Hk) {
+  using T = Preset<P>;
+  LaneOff<P> o;
+  const uint32_t kraw = static_cast<uint32_t>((hl * Hk + hk) * T::kSlot) +
+                        static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
+  o.k = kraw & ~3u;
+  o.ksh = kraw & 3u;
+  o.meta0 = static_cast<uint32_t>((4 * q4 * Hk + hk) * T::kSlot);
+  o.vcol = static_cast<uint32_t>(T::kKps + (T::kVb == 4 ? 4 * hl : 3 * hl));
+  return o;
+}
+
+// Issue every load of one tile.  tb: the tile's first slot row (uniform);
+// row: bytes per token row (Hk * slot, uniform).
+template <int P>
+__device__ __forceinline__ void load_tile(const uint8_t* tb, uint32_t row, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
   if constexpr (T::kFp8 != 0) {
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kslot + 16 * q);
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(kslot + 64 + 16 * q);
-    uint32_t w[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
+    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
+  } else {
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+    if (T::kKb == 4) r.k[4] = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // value codes of token 4q+i; the row stride may be 2 mod 4, so the
+    // whole in-tile offset is aligned down (tile bases are 32-byte aligned)
+    const uint32_t vo = i * row + o.meta0 + o.vcol;
+    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
+      r.v[i][0] = *reinterpret_cast<const uint32_t*>(tb + vo);
+    } else {
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
+      r.v[i][0] = w.x;
+      r.v[i][1] = w.y;
+    }
+    const uint8_t* m = tb + i * row + o.meta0;
+    if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
+      r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
+    } else {
+      r.sz[i] = ld16(m + T::kKps + T::kVdata) | (ld16(m + T::kKps + T::kVdata + 2) << 16);
+    }
+    if constexpr (T::kFp8 == 0) r.gm[i] = ld16(m + T::kKdata);
+  }
+}
+
+// Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q).
+template <int P>
+__device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, const tq::Lut8& la,
+                                            const tq::Lut8& lb, half8 A[4]) {
+  using T = Preset<P>;
+  if constexpr (T::kFp8 != 0) {
     uint32_t hv[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      hv[2 * i] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
-      hv[2 * i + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+      hv[2 * i] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.k[i], 1.0f, false));
+      hv[2 * i + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.k[i], 1.0f, true));
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) A[c] = as_half8(hv[4 * c], hv[4 * c + 1], hv[4 * c + 2], hv[4 * c + 3]);
   } else if constexpr (T::kKb == 4) {
-    const uint8_t* p = kslot + 16 * q;
-    const uintptr_t ad = reinterpret_cast<uintptr_t>(p);
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(ad & ~static_cast<uintptr_t>(3));
-    const u32x4a4 r0 = *reinterpret_cast<const u32x4a4*>(base);
-    const uint32_t r4 = *reinterpret_cast<const uint32_t*>(base + 16);
-    const uint32_t sh = static_cast<uint32_t>(ad & 3);
-    uint32_t w[4] = {tq::alignbyte(r0.y, r0.x, sh), tq::alignbyte(r0.z, r0.y, sh), tq::alignbyte(r0.w, r0.z, sh),
-                     tq::alignbyte(r4, r0.w, sh)};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      const uint32_t w = tq::alignbyte(r.k[c + 1], r.k[c], sh);
       uint32_t e0, e1, o0, o1;
-      tq::lut16(w[c] & 0x0F0F0F0Fu, la, lb, e0, e1);
-      tq::lut16((w[c] >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
+      tq::lut16(w & 0x0F0F0F0Fu, la, lb, e0, e1);
+      tq::lut16((w >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
       A[c] = as_half8(e0, e1, o0, o1);
     }
   } else {
-    const uint8_t* p = kslot + 12 * q;
-    const uintptr_t ad = reinterpret_cast<uintptr_t>(p);
-    const u32x4a4 r = *reinterpret_cast<const u32x4a4*>(ad & ~static_cast<uintptr_t>(3));
-    const uint32_t sh = static_cast<uint32_t>(ad & 3);
     uint32_t sel[8];
-    tq::key3_selectors(tq::alignbyte(r.y, r.x, sh), tq::alignbyte(r.z, r.y, sh), tq::alignbyte(r.w, r.z, sh), sel);
+    tq::key3_selectors(tq::alignbyte(r.k[1], r.k[0], sh), tq::alignbyte(r.k[2], r.k[1], sh),
+                       tq::alignbyte(r.k[3], r.k[2], sh), sel);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t a0, a1, b0, b1;
@@ -174,8 +231,106 @@ __device__ __forceinline__ void key_operand(const uint8_t* kslot, int q, const t
   }
 }
 
+// Online-softmax state of one lane: query head lane % 16; the 4 lane quarters
+// hold disjoint tokens and share the reference maximum m.
+struct Softmax {
+  float m, l, z;  // reference max (log2 domain), sum of p, sum of p * zero
+};
+
+// Largest growth of p = 2^(s - m) tolerated before the accumulators are
+// rescaled; p * value_scale must also stay inside fp16.
+constexpr float kLazyRescaleLog2 = 8.0f;
+
 template <int P>
-__global__ __launch_bounds__(kThreads) void tq_decode_stage1_kernel(DecodeArgs a) {
+__device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>& o, uint32_t row,
+                                          const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4], int valid,
+                                          Softmax& sm, f32x4 acc[8]) {
+  using T = Preset<P>;
+  half8 A[4];
+  key_operand<P>(r, o.ksh, la, lb, A);
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], bq[c], sc, 0, 0, 0);
+
+  float sco[4], sv[4], zv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sco[i] = T::kFp8 ? sc[i] : sc[i] * half_bits_to_f32(r.gm[i]);
+    sv[i] = half_bits_to_f32(r.sz[i] & 0xFFFFu);
+    zv[i] = half_bits_to_f32(r.sz[i] >> 16);
+  }
+  const int lane = threadIdx.x & 63;
+  if (valid < 16) {  // tail tile: tokens at or past the sequence end drop out
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * (lane >> 4) + i >= valid) {
+        sco[i] = -INFINITY;
+        sv[i] = 0.f;
+        zv[i] = 0.f;
+      }
+    }
+  }
+  float tmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float m_cand = fmaxf(sm.m, tmax);
+  float p[4], ps[4];
+  bool redo = __any(tmax > sm.m + kLazyRescaleLog2);
+  if (!redo) {
+    float pmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      ps[i] = p[i] * sv[i];
+      pmax = fmaxf(pmax, ps[i]);
+    }
+    redo = __any(pmax > 65504.f);
+  }
+  if (redo) {  // rescale the accumulators to the new maximum
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    sm.l *= alpha;
+    sm.z *= alpha;
+    sm.m = m_cand;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      ps[i] = p[i] * sv[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sm.l += p[i];
+    sm.z = fmaf(p[i], zv[i], sm.z);
+  }
+  half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
+  half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
+  const half4 pv = as_half4(h2_bits(ps01), h2_bits(ps23));
+
+  uint32_t vw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4)
+      vw[i] = r.v[i][0];
+    else
+      vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (i * row + o.meta0 + o.vcol) & 3u);
+  }
+  uint32_t v01[8], v23[8];
+  if (T::kVb == 4) {
+    tq::val4_pairs(vw[0], vw[1], v01);
+    tq::val4_pairs(vw[2], vw[3], v23);
+  } else {
+    tq::val3_pairs(vw[0], vw[1], v01);
+    tq::val3_pairs(vw[2], vw[3], v23);
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   // LDS: fp32 rotation scratch (later reused for the cross-wave merge) and the
   // fp16 query operand source.
@@ -263,100 +418,36 @@ __global__ __launch_bounds__(kThreads) void tq_decode_stage1_kernel(DecodeArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) bq[c][e] = qh[hl][key_dim<P>(c, q4, e)];
 
-  // ---- main loop over this wave's tiles ----
-  const int bs = a.block_size;
-  const int64_t blk_bytes = static_cast<int64_t>(bs) * Hk * T::kSlot;
+  // ---- main loop over this wave's tiles, next tile's loads in flight ----
+  const int bs_log2 = 31 - __clz(a.block_size);
+  const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * Hk * T::kSlot;
+  const uint32_t row = static_cast<uint32_t>(Hk * T::kSlot);
   const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  float m_run = -INFINITY, l_run = 0.f, z_run = 0.f;
+  const LaneOff<P> off = lane_offsets<P>(hl, q4, hk, Hk);
+  Softmax sm{-INFINITY, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = t_begin + wave; t < t_end; t += kWaves) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto tile_base = [&](int t) -> const uint8_t* {
     const int tok0 = t * 16;
-    const int blk = btab[tok0 / bs];
-    const uint8_t* blkbase = a.cache + static_cast<int64_t>(blk) * blk_bytes;
-    const int inblk = tok0 % bs;
-    const uint8_t* kslot = blkbase + (static_cast<int64_t>(inblk + hl) * Hk + hk) * T::kSlot;
-    const uint8_t* vs[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vs[i] = blkbase + (static_cast<int64_t>(inblk + 4 * q4 + i) * Hk + hk) * T::kSlot;
-
-    // scores
-    half8 A[4];
-    key_operand<P>(kslot, q4, la, lb, A);
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], bq[c], sc, 0, 0, 0);
-
-    float sv[4], zv[4], sco[4];
-    uint32_t vw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float gm = 1.f;
-      if (!T::kFp8) gm = half_bits_to_f32(ld16(vs[i] + T::kKdata));
-      sco[i] = sc[i] * gm;
-      sv[i] = half_bits_to_f32(ld16(vs[i] + T::kKps + T::kVdata));
-      zv[i] = half_bits_to_f32(ld16(vs[i] + T::kKps + T::kVdata + 2));
-      if (T::kVb == 4) {
-        if (T::kKps % 4 == 0 && T::kSlot % 4 == 0)
-          vw[i] = *reinterpret_cast<const uint32_t*>(vs[i] + T::kKps + 4 * hl);
-        else
-          vw[i] = ld32_u(vs[i] + T::kKps + 4 * hl);
-      } else {
-        vw[i] = ld32_u(vs[i] + T::kKps + 3 * hl);
-      }
-    }
-    const bool tail = tok0 + 16 > seqlen;
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tok0 + 4 * q4 + i >= seqlen) {
-          sco[i] = -INFINITY;
-          sv[i] = 0.f;
-          zv[i] = 0.f;
-        }
-      }
-    }
-
-    // online softmax (base 2); the 4 lane quarters hold different tokens of
-    // the same query head and share one running maximum
-    float tmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-      l_run *= alpha;
-      z_run *= alpha;
-      m_run = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sco[i] - m_run);
-      l_run += p[i];
-      z_run = fmaf(p[i], zv[i], z_run);
-    }
-    half2v ps01 = {static_cast<_Float16>(p[0] * sv[0]), static_cast<_Float16>(p[1] * sv[1])};
-    half2v ps23 = {static_cast<_Float16>(p[2] * sv[2]), static_cast<_Float16>(p[3] * sv[3])};
-    const half4 pv = as_half4(h2_bits(ps01), h2_bits(ps23));
-
-    // values: V^T tile (dims on rows, tokens on k) as fp16 subnormal codes
-    uint32_t v01[8], v23[8];
-    if (T::kVb == 4) {
-      tq::val4_pairs(vw[0], vw[1], v01);
-      tq::val4_pairs(vw[2], vw[3], v23);
-    } else {
-      tq::val3_pairs(vw[0], vw[1], v01);
-      tq::val3_pairs(vw[2], vw[3], v23);
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
+    const int blk = __builtin_amdgcn_readfirstlane(btab[tok0 >> bs_log2]);
+    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>(tok0 & (a.block_size - 1)) * row;
+  };
+  TileRegs<P> ra, rb;
+  int t = t_begin + wv;
+  if (t < t_end) load_tile<P>(tile_base(t), row, off, ra);
+  while (t < t_end) {
+    if (t + kWaves < t_end) load_tile<P>(tile_base(t + kWaves), row, off, rb);
+    tile_step<P>(ra, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+    t += kWaves;
+    if (t >= t_end) break;
+    if (t + kWaves < t_end) load_tile<P>(tile_base(t + kWaves), row, off, ra);
+    tile_step<P>(rb, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+    t += kWaves;
   }
+  float m_run = sm.m, l_run = sm.l, z_run = sm.z;
 
   // ---- per-wave totals: lane quarters hold disjoint tokens ----
   l_run += __shfl_xor(l_run, 16, 64);
