@@ -76,6 +76,28 @@ __global__ void cvt_fp8_kernel(const uint32_t* in, uint32_t* out, int n) {
   }
 }
 
+// Streaming read: grid-stride 16-byte loads over n16 chunks; the xor of
+// everything read goes to out[blockIdx] so no load is dead.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ in, int64_t n16,
+                                                          uint32_t* __restrict__ out) {
+  uint32_t x = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const u32x4 v = __builtin_nontemporal_load(in + i);
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(out + blockIdx.x, x);
+}
+
+// Plain copy of n16 16-byte chunks.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out,
+                                                   int64_t n16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    out[i] = in[i];
+}
+
 int finish() {
   if (hipGetLastError() != hipSuccess) return -8;
   return hipDeviceSynchronize() == hipSuccess ? 0 : -8;
@@ -115,6 +137,21 @@ int tq_probe_cvt_fp8_f16(const uint32_t* in, uint32_t* out, int n) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(cvt_fp8_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, 0, in, out, n);
   return finish();
+}
+
+// Streaming read of bytes (multiple of 16) from a device buffer; out: device
+// uint32 [blocks]; asynchronous on `stream` (timed by the caller).
+int tq_probe_stream_read(const void* in, int64_t bytes, uint32_t* out, int blocks, void* stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(in), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+// Copy bytes (multiple of 16), asynchronous on `stream`.
+int tq_probe_copy(const void* in, void* out, int64_t bytes, int blocks, void* stream) {
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(in), static_cast<u32x4*>(out), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 
 }  // extern "C"

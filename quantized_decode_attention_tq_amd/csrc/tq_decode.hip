@@ -64,6 +64,17 @@ struct Preset<TQ_3BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102;
 };
 
+// The constants above follow the slot layout of tq_layout_init at head_dim 128.
+template <int P>
+constexpr bool preset_geometry_ok() {
+  using T = Preset<P>;
+  return T::kKdata == (T::kFp8 ? kD : kD * T::kKb / 8) && T::kKps == (T::kFp8 ? kD : T::kKdata + 2) &&
+         T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + 4 + 1) / 2) * 2;
+}
+static_assert(preset_geometry_ok<TQ_K8V4>() && preset_geometry_ok<TQ_4BIT_NC>() &&
+                  preset_geometry_ok<TQ_K3V4_NC>() && preset_geometry_ok<TQ_3BIT_NC>(),
+              "slot geometry");
+
 struct DecodeArgs {
   const uint16_t* query;
   const uint8_t* cache;
@@ -74,7 +85,7 @@ struct DecodeArgs {
   float* partials;  // [B][Hq][S][D+1]
   float qscale;     // softmax scale * log2(e)
   int32_t q_bf16;
-  int32_t num_q_heads, num_kv_heads, group, head_groups;
+  int32_t num_q_heads, num_kv_heads, group, head_groups, heads_per_wg;
   int32_t block_size, bt_stride, num_splits;
 };
 
@@ -105,13 +116,24 @@ __device__ __forceinline__ uint32_t ld32_u(const uint8_t* p) {
 
 __device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
 
-// Query head dim held by MFMA key-operand chunk c, element e, lane quarter q.
+// Position of query dim d in the fp16 query operand image: lane quarter q,
+// MFMA chunk c, element e -> q*32 + c*8 + e, matching the order in which the
+// key operand holds dims (FP8 keys: quarter q loads dims 16q..16q+15 and
+// 64+16q..64+16q+15; 4-bit keys: even dims then odd dims of each byte group;
+// 3-bit keys: the selector order of tq::key3_selectors).
 template <int P>
-__device__ __forceinline__ int key_dim(int c, int q, int e) {
+__device__ __forceinline__ int qh_pos(int d) {
   using T = Preset<P>;
-  if (T::kFp8) return (c >> 1) * 64 + 16 * q + (c & 1) * 8 + e;
-  if (T::kKb == 4) return 32 * q + tq::key4_dim(c, e);
-  return 32 * q + tq::key3_dim(c, e);
+  if (T::kFp8) {
+    const int r = d & 63;
+    return (r >> 4) * 32 + ((d >> 6) * 2 + ((r & 15) >> 3)) * 8 + (d & 7);
+  }
+  const int q = d >> 5, dd = d & 31;
+  if (T::kKb == 4) {
+    const int r = dd & 7;
+    return q * 32 + (dd >> 3) * 8 + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
+  }
+  return q * 32 + ((dd & 7) >> 1) * 8 + (dd & 1) * 4 + (dd >> 3);
 }
 
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -329,24 +351,36 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
     acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
 }
 
+// Stage 1.  A workgroup owns (sequence b, group of heads_per_wg consecutive
+// KV heads, group of <= 16 query heads, split s).  Its 4 waves are spread
+// over the KV heads: with 4 heads per workgroup each wave takes one head and
+// all of the split's tiles (the 4 waves read adjacent slots of the same token
+// rows, so cache lines are shared inside the CU); with fewer heads per
+// workgroup the waves of one head take its tiles round-robin and merge their
+// partial softmax states in LDS at the end.
 template <int P>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
-  // LDS: fp32 rotation scratch (later reused for the cross-wave merge) and the
-  // fp16 query operand source.
-  __shared__ float smem[3 * 16 * kD + 2 * 4 * 16];
-  __shared__ _Float16 qh[16][kD + 8];
+  constexpr int kMergeStride = kD + 4;  // merge rows: 16-byte aligned, banks rotate per head
+  // fp32 query scratch (up to 64 rows), later reused as the merge area
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * 16 * kMergeStride + 2 * kWaves * 16];
+  __shared__ __attribute__((aligned(16))) _Float16 qh[kWaves * 16][kD + 8];
   float(*qf)[kD] = reinterpret_cast<float(*)[kD]>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.num_splits, Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
+  const int HW = a.heads_per_wg;  // 1, 2 or 4
+  const int wph = kWaves / HW;    // waves per KV head
   int lg = xcd_remap(blockIdx.x, gridDim.x);
-  const int hk = lg % Hk;
-  lg /= Hk;
+  const int hgrp = lg % (Hk / HW);  // fastest: neighbouring heads share cache lines
+  lg /= Hk / HW;
   const int hg = lg % a.head_groups;
   lg /= a.head_groups;
   const int s = lg % S;
   const int b = lg / S;
+  const int hs = wave / wph;  // this wave's head slot in the workgroup
+  const int phase = wave % wph;
+  const int hk = hgrp * HW + hs;
 
   const int seqlen = a.seq_lens[b];
   const int ntiles = (seqlen + 15) >> 4;
@@ -355,44 +389,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int t_end = min(t_begin + tps, ntiles);
   const int h0 = hg * 16;
   const int geff = min(16, g - h0);
-  const int hq0 = hk * g + h0;
-  const int64_t head_stride = static_cast<int64_t>(S) * (kD + 1);
-  float* part = a.partials + ((static_cast<int64_t>(b) * Hq + hq0) * S + s) * (kD + 1);
+  // partial row of query head h0 + j of KV head hgrp*HW + k
+  auto part_row = [&](int k, int j) {
+    return a.partials + ((static_cast<int64_t>(b) * Hq + (hgrp * HW + k) * g + h0 + j) * S + s) * (kD + 1);
+  };
 
   if (t_begin >= t_end) {  // empty split: zero partial, lse = -inf
-    for (int idx = tid; idx < geff * (kD + 1); idx += kThreads) {
-      const int j = idx / (kD + 1), d = idx % (kD + 1);
-      part[j * head_stride + d] = d == kD ? -INFINITY : 0.f;
+    for (int idx = tid; idx < HW * geff * (kD + 1); idx += kThreads) {
+      const int k = idx / (geff * (kD + 1)), r = idx % (geff * (kD + 1));
+      const int j = r / (kD + 1), d = r % (kD + 1);
+      part_row(k, j)[d] = d == kD ? -INFINITY : 0.f;
     }
     return;
   }
 
-  // ---- query: load, sign flip + Walsh-Hadamard (MSE keys), scale, fp16 ----
+  // ---- first tile's loads go out before the query prologue ----
+  const int hl = lane & 15, q4 = lane >> 4;
+  const int bs_log2 = 31 - __clz(a.block_size);
+  const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * Hk * T::kSlot;
+  const uint32_t row = static_cast<uint32_t>(Hk * T::kSlot);
+  const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const LaneOff<P> off = lane_offsets<P>(hl, q4, hk, Hk);
+  const int t_first = t_begin + __builtin_amdgcn_readfirstlane(phase);
+  auto tile_base = [&](int t) -> const uint8_t* {
+    const int tok0 = t * 16;
+    const int blk = __builtin_amdgcn_readfirstlane(btab[tok0 >> bs_log2]);
+    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>(tok0 & (a.block_size - 1)) * row;
+  };
+  TileRegs<P> ra, rb;
+  if (t_first < t_end) load_tile<P>(tile_base(t_first), row, off, ra);
+
+  // ---- query rows of the workgroup's heads: sign flip + Walsh-Hadamard
+  // (MSE keys), scale by softmax scale * log2(e), fp16 in MFMA operand order
+  const int nrows = HW * 16;
   const bool qbf16 = a.q_bf16 != 0;
-  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
-    const int j = idx >> 7, d = idx & (kD - 1);
+  for (int idx = tid; idx < nrows * kD; idx += kThreads) {
+    const int r = idx >> 7, d = idx & (kD - 1);
+    const int k = r >> 4, j = r & 15;
     float v = 0.f;
-    if (j < geff) v = widen16(a.query[(static_cast<int64_t>(b) * Hq + hq0 + j) * kD + d], qbf16);
+    if (j < geff) v = widen16(a.query[(static_cast<int64_t>(b) * Hq + (hgrp * HW + k) * g + h0 + j) * kD + d], qbf16);
     if (!T::kFp8) v *= a.signs[d];
-    qf[j][d] = v;
+    qf[r][d] = v;
   }
   __syncthreads();
   if (!T::kFp8) {
-    for (int hs = 1; hs < kD; hs <<= 1) {
-      for (int pi = tid; pi < 16 * (kD / 2); pi += kThreads) {
-        const int j = pi / (kD / 2), k = pi % (kD / 2);
-        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
-        const float x0 = qf[j][i0], x1 = qf[j][i1];
-        qf[j][i0] = x0 + x1;
-        qf[j][i1] = x0 - x1;
+    for (int hsz = 1; hsz < kD; hsz <<= 1) {
+      for (int pi = tid; pi < nrows * (kD / 2); pi += kThreads) {
+        const int r = pi / (kD / 2), k = pi % (kD / 2);
+        const int i0 = (k / hsz) * 2 * hsz + (k % hsz), i1 = i0 + hsz;
+        const float x0 = qf[r][i0], x1 = qf[r][i1];
+        qf[r][i0] = x0 + x1;
+        qf[r][i1] = x0 - x1;
       }
       __syncthreads();
     }
   }
   const float qs = T::kFp8 ? a.qscale : a.qscale * 0.08838834764831845f;  // 1/sqrt(128) of the rotation
-  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
-    const int j = idx >> 7, d = idx & (kD - 1);
-    qh[j][d] = static_cast<_Float16>(qf[j][d] * qs);
+  for (int idx = tid; idx < nrows * kD; idx += kThreads) {
+    const int r = idx >> 7, d = idx & (kD - 1);
+    qh[r][qh_pos<P>(d)] = static_cast<_Float16>(qf[r][d] * qs);
   }
 
   // codebook byte tables (fp16 centroids split into low / high bytes)
@@ -411,41 +466,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   __syncthreads();
 
-  const int hl = lane & 15, q4 = lane >> 4;
   half8 bq[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bq[c][e] = qh[hl][key_dim<P>(c, q4, e)];
+  for (int c = 0; c < 4; ++c) bq[c] = *reinterpret_cast<const half8*>(&qh[hs * 16 + hl][q4 * 32 + c * 8]);
 
   // ---- main loop over this wave's tiles, next tile's loads in flight ----
-  const int bs_log2 = 31 - __clz(a.block_size);
-  const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * Hk * T::kSlot;
-  const uint32_t row = static_cast<uint32_t>(Hk * T::kSlot);
-  const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const LaneOff<P> off = lane_offsets<P>(hl, q4, hk, Hk);
   Softmax sm{-INFINITY, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto tile_base = [&](int t) -> const uint8_t* {
-    const int tok0 = t * 16;
-    const int blk = __builtin_amdgcn_readfirstlane(btab[tok0 >> bs_log2]);
-    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>(tok0 & (a.block_size - 1)) * row;
-  };
-  TileRegs<P> ra, rb;
-  int t = t_begin + wv;
-  if (t < t_end) load_tile<P>(tile_base(t), row, off, ra);
+  // The prefetch is unconditional (past the wave's last tile it re-reads
+  // that tile, an L2 hit) so that every path into the loop has the same loads
+  // in flight and the waits stay exact; the scheduling barriers keep each
+  // prefetch issued before the compute of the current tile.
+  const int stride = __builtin_amdgcn_readfirstlane(wph);
+  int t = t_first;
   while (t < t_end) {
-    if (t + kWaves < t_end) load_tile<P>(tile_base(t + kWaves), row, off, rb);
+    load_tile<P>(tile_base(min(t + stride, t_end - 1)), row, off, rb);
+    __builtin_amdgcn_sched_barrier(0);
     tile_step<P>(ra, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
-    t += kWaves;
+    t += stride;
     if (t >= t_end) break;
-    if (t + kWaves < t_end) load_tile<P>(tile_base(t + kWaves), row, off, ra);
+    load_tile<P>(tile_base(min(t + stride, t_end - 1)), row, off, ra);
+    __builtin_amdgcn_sched_barrier(0);
     tile_step<P>(rb, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
-    t += kWaves;
+    t += stride;
   }
   float m_run = sm.m, l_run = sm.l, z_run = sm.z;
 
@@ -454,7 +500,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   l_run += __shfl_xor(l_run, 32, 64);
   z_run += __shfl_xor(z_run, 16, 64);
   z_run += __shfl_xor(z_run, 32, 64);
-  // unnormalized output of head hl, dims 32*q4 + 8*i + n
+  // unnormalized output of query head hl, dims 32*q4 + 8*i + n
   float o[4][8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -464,48 +510,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     for (int i = 0; i < 4; ++i) o[i][n] = fmaf(acc[n][i], unscale, z_run);
   }
 
-  // ---- merge the 4 waves in LDS (reusing the rotation scratch) ----
+  // ---- merge the waves of each head in LDS (reusing the query scratch) ----
+  // Each wave scales its unnormalized output by 2^(m_w - M) / l (M: max over
+  // the head's waves, l: merged softmax sum) and writes it as
+  // [wave][query head][dim]; the workgroup sums the waves of each head and
+  // writes every partial row with consecutive lanes on consecutive dims.
   __syncthreads();
-  float* mo = smem;                        // [3 waves][16 heads][128]
-  float* mm = smem + 3 * 16 * kD;          // [4][16]
-  float* ml = mm + 4 * 16;                 // [4][16]
+  float* mo = smem;                               // [wave][16][kMergeStride]
+  float* mm = smem + kWaves * 16 * kMergeStride;  // [wave][16] maxima
+  float* ml = mm + kWaves * 16;                   // [wave][16] sums
   if (q4 == 0) {
     mm[wave * 16 + hl] = m_run;
     ml[wave * 16 + hl] = l_run;
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int n = 0; n < 8; ++n) mo[((wave - 1) * 16 + hl) * kD + 32 * q4 + 8 * i + n] = o[i][n];
-  }
   __syncthreads();
-  if (wave == 0 && hl < geff) {
-    float M = mm[hl];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + hl]);
-    float fw[kWaves];
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = mm[w * 16 + hl];
-      fw[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lsum = fmaf(fw[w], ml[w * 16 + hl], lsum);
+  auto head_stats = [&](int hslot, int j, float& M, float& lsum) {
+    M = -INFINITY;
+    for (int k = 0; k < wph; ++k) M = fmaxf(M, mm[(hslot * wph + k) * 16 + j]);
+    lsum = 0.f;
+    for (int k = 0; k < wph; ++k) {
+      const float mw = mm[(hslot * wph + k) * 16 + j];
+      lsum = fmaf(mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M), ml[(hslot * wph + k) * 16 + j], lsum);
     }
-    const float inv = 1.0f / lsum;
-    float* dst = part + hl * head_stride;
+  };
+  {
+    float M, lsum;
+    head_stats(hs, hl, M, lsum);
+    const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    const float sc = lsum > 0.f ? f / lsum : 0.f;
+    float* rowp = mo + (wave * 16 + hl) * kMergeStride + 32 * q4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int d = 32 * q4 + 8 * i + n;
-        float v = fw[0] * o[i][n];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) v = fmaf(fw[w], mo[((w - 1) * 16 + hl) * kD + d], v);
-        dst[d] = v * inv;
-      }
+      f32x4 lo = {o[i][0] * sc, o[i][1] * sc, o[i][2] * sc, o[i][3] * sc};
+      f32x4 hi = {o[i][4] * sc, o[i][5] * sc, o[i][6] * sc, o[i][7] * sc};
+      *reinterpret_cast<f32x4*>(rowp + 8 * i) = lo;
+      *reinterpret_cast<f32x4*>(rowp + 8 * i + 4) = hi;
     }
-    if (q4 == 0) dst[kD] = (M + log2f(lsum)) * kLn2;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < HW * geff * kD; idx += kThreads) {
+    const int k = idx / (geff * kD), r = idx % (geff * kD);
+    const int j = r >> 7, d = r & (kD - 1);
+    float v = 0.f;
+    for (int w = 0; w < wph; ++w) v += mo[((k * wph + w) * 16 + j) * kMergeStride + d];
+    part_row(k, j)[d] = v;
+  }
+  if (tid < HW * geff) {
+    const int k = tid / geff, j = tid % geff;
+    float M, lsum;
+    head_stats(k, j, M, lsum);
+    part_row(k, j)[kD] = (M + log2f(lsum)) * kLn2;
   }
 }
 
@@ -583,7 +637,18 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.block_size = block_size;
   a.bt_stride = block_table_stride;
   a.num_splits = num_kv_splits;
-  const int64_t nblocks = static_cast<int64_t>(batch) * num_kv_heads * a.head_groups * num_kv_splits;
+  // Heads per workgroup: 4 when there are enough (sequence, split, head
+  // group) units to keep ~3 workgroups on each of the 256 CUs, else fewer
+  // (the waves of one head then share its tiles).
+  const int64_t units = static_cast<int64_t>(batch) * a.head_groups * num_kv_splits;
+  a.heads_per_wg = 1;
+  for (int hw : {4, 2}) {
+    if (num_kv_heads % hw == 0 && units * (num_kv_heads / hw) >= 768) {
+      a.heads_per_wg = hw;
+      break;
+    }
+  }
+  const int64_t nblocks = units * (num_kv_heads / a.heads_per_wg);
   if (nblocks > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
   switch (layout->preset) {
     case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, stream);

@@ -23,7 +23,9 @@ def lib():
                        ("tq_probe_bits_device", [ctypes.c_int, vp, vp, ctypes.c_int]),
                        ("tq_probe_mfma_16x16x32_f16", [vp, vp, vp]),
                        ("tq_probe_mfma_16x16x16_f16", [vp, vp, vp]),
-                       ("tq_probe_cvt_fp8_f16", [vp, vp, ctypes.c_int])):
+                       ("tq_probe_cvt_fp8_f16", [vp, vp, ctypes.c_int]),
+                       ("tq_probe_stream_read", [vp, ctypes.c_int64, vp, ctypes.c_int, vp]),
+                       ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp])):
         f = getattr(L, name)
         f.restype = ctypes.c_int
         f.argtypes = args

@@ -53,6 +53,24 @@ def test_decode_end_to_end_block_sizes(preset, bs):
     G.check_decode(out, lse, ref, rlse, _rows(w))
 
 
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("batch", [24, 48])
+def test_decode_heads_per_workgroup_modes(preset, batch):
+    """Enough (sequence, split) units select 2 (24 sequences) or 4 (48
+    sequences) KV heads per workgroup with 8 KV heads and 8 splits."""
+    rng = np.random.default_rng(batch)
+    lens = [int(x) for x in rng.integers(1, 160, batch)]
+    lens[0], lens[1] = 0, 16
+    w = _small(preset, lens, Hq=16, Hk=8, bs=16, seed=70 + batch)
+    G.log(f"decode modes {preset} B={batch}")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 8)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 5, 8, 16, 20])
 def test_decode_gqa_groups(g):
     w = _small("turboquant_k3v4_nc", [70, 129], Hq=2 * g, Hk=2, bs=32, seed=60 + g)
