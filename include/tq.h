@@ -95,6 +95,10 @@ const char* tq_version(void);
 /* Human-readable text for a tq_status (static storage). */
 const char* tq_status_str(int status);
 
+/* Text of the HIP error behind the most recent TQ_EHIP returned on this
+ * thread ("no error" if there was none); static storage. */
+const char* tq_last_hip_error(void);
+
 /* "turboquant_k8v4" | "turboquant_4bit_nc" | "turboquant_k3v4_nc" |
  * "turboquant_3bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
 int tq_preset_from_name(const char* name, int32_t* preset);

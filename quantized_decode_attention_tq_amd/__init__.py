@@ -27,14 +27,17 @@ TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
 PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc")
 
 #: every symbol include/tq.h declares
-ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_preset_from_name", "tq_layout_init", "tq_kv_cache_shape",
+ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init", "tq_kv_cache_shape",
                "tq_lloyd_max", "tq_wht_signs", "tq_decode_workspace_bytes", "tq_store", "tq_store_validate",
                "tq_decode_attention", "tq_decode_validate", "tq_decode_stage1", "tq_decode_stage2")
 
 
 class TQError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {_lib.tq_status_str(status).decode()} (status {status})")
+        msg = f"{where}: {_lib.tq_status_str(status).decode()} (status {status})"
+        if status == TQ_EHIP:
+            msg += f": {_lib.tq_last_hip_error().decode()}"
+        super().__init__(msg)
         self.status = status
 
 
@@ -51,6 +54,13 @@ class Layout(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with: python quantized_decode_attention_tq_amd/build.py")
+    # PyTorch ships its own HIP runtime under the same soname as ROCm's
+    # (libamdhip64.so.7).  Importing torch first makes libtq.so bind to that
+    # already-loaded runtime, so the process has one HIP runtime: torch's
+    # streams, events and graph capture then see libtq's launches.  Loaded
+    # the other way round, the process would hold two runtimes.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, u64, sz, vp, fp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p,
                                  ctypes.c_float)
@@ -58,6 +68,7 @@ def _load():
     sig = {
         "tq_version": (ctypes.c_char_p, []),
         "tq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "tq_last_hip_error": (ctypes.c_char_p, []),
         "tq_preset_from_name": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(i32)]),
         "tq_layout_init": (ctypes.c_int, [i32, i32, L]),
         "tq_kv_cache_shape": (ctypes.c_int, [L, i64, i32, i32, ctypes.POINTER(i64)]),

@@ -23,7 +23,9 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "tq.h"
 #include "tq_bits.h"
@@ -32,8 +34,6 @@
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -82,10 +82,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const float* signs;
   const float* centroids;
-  float* partials;  // [B][Hq][S][D+1]
+  float* part_o;    // [B][Hq][S][D] normalized partial outputs
+  float* part_lse;  // [B][Hq][S] natural-log LSE of each split
   float qscale;     // softmax scale * log2(e)
   int32_t q_bf16;
-  int32_t num_q_heads, num_kv_heads, group, head_groups, heads_per_wg;
+  int32_t num_q_heads, num_kv_heads, group, head_groups;
+  int32_t heads_per_wg;  // KV heads (= waves) per workgroup
+  int32_t ring_depth;    // tiles in the LDS ring
   int32_t block_size, bt_stride, num_splits;
 };
 
@@ -351,36 +354,168 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
     acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
 }
 
-// Stage 1.  A workgroup owns (sequence b, group of heads_per_wg consecutive
-// KV heads, group of <= 16 query heads, split s).  Its 4 waves are spread
-// over the KV heads: with 4 heads per workgroup each wave takes one head and
-// all of the split's tiles (the 4 waves read adjacent slots of the same token
-// rows, so cache lines are shared inside the CU); with fewer heads per
-// workgroup the waves of one head take its tiles round-robin and merge their
-// partial softmax states in LDS at the end.
-template <int P>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void tq_decode_stage1_kernel(DecodeArgs a) {
-  using T = Preset<P>;
-  constexpr int kMergeStride = kD + 4;  // merge rows: 16-byte aligned, banks rotate per head
-  // fp32 query scratch (up to 64 rows), later reused as the merge area
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * 16 * kMergeStride + 2 * kWaves * 16];
-  __shared__ __attribute__((aligned(16))) _Float16 qh[kWaves * 16][kD + 8];
-  float(*qf)[kD] = reinterpret_cast<float(*)[kD]>(smem);
+// ---- tile staging: block rows -> LDS ring by direct-to-LDS loads ----
+//
+// A tile is 16 consecutive token rows of the cache restricted to the
+// workgroup's G KV heads: 16 row pieces of G * slot bytes, each at
+// row_piece(i) = i * row + h0 * slot from the tile base (row = Hk * slot).
+// Either G == Hk (the 16 pieces are one contiguous run) or row is a
+// multiple of 16 (Hk % 8 == 0), so the whole tile is TC = G * slot 16-byte
+// chunks whose chunk c (piece c / (G*slot/16)) lies at a 16-byte aligned
+// global address.  The LDS image of a tile is the byte-exact concatenation
+// of the pieces: slot (token i, head h0 + hh) sits at i*G*slot + hh*slot,
+// with the same alignment mod 16 as in the cache.  Chunks are spread over
+// the workgroup's waves as "instruction slots" of 64 chunks: slot k =
+// n * G + wave is the wave's n-th load; lanes past TC repeat the last chunk
+// into the padding at the end of the ring entry.
+struct Ring {
+  uint32_t lds_base;    // LDS byte address of ring entry 0 (uniform)
+  uint32_t entry;       // bytes per ring entry (multiple of 1024)
+  int my_loads;         // loads per tile issued by this wave
+  uint32_t off[5];      // per load: chunk byte offset from the tile base
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One direct-to-LDS load of 16 bytes per lane, non-temporal: the data is
+// read once.  LDS destination = m0 + 16 * lane.  Written as inline assembly
+// so that the compiler does not guard every later LDS read with a full
+// vmcnt(0) wait; the ring's own waits (vm_wait + barrier) order the reads.
+// m0 is a reserved register the compiler cannot be told about: the stage-1
+// kernels use m0 for nothing else (checked in their ISA), so setting it here
+// disturbs no compiler-managed state.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(m0) : "memory");
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (n uniform).  Loads retire in order, so every older load has completed.
+__device__ __forceinline__ void vm_wait(int n) {
+  switch (n) {
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Workgroup barrier that first drains this wave's LDS reads, so a ring entry
+// released at the barrier has no read of it still in flight.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Query operand of one lane (query head h0 + hl of KV head hk, dims of lane
+// quarter q4): MSE keys rotate the query like the keys (sign flip, then the
+// Walsh-Hadamard butterflies: strides 1..16 inside the lane, 32 and 64
+// across lane quarters), everything scaled by softmax scale * log2(e); the
+// values land in fp16 in the order key_operand produces dims.
+template <int P>
+__device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk, int h0, int geff, int hl, int q4,
+                                              half8 bq[4]) {
+  using T = Preset<P>;
+  const bool live = hl < geff;
+  const uint16_t* qrow =
+      a.query + (static_cast<int64_t>(b) * a.num_q_heads + hk * a.group + h0 + (live ? hl : 0)) * kD;
+  const bool bf = a.q_bf16 != 0;
+  float v[32];
+  if constexpr (T::kFp8 != 0) {
+    // dims 16*q4 + j (v[j]) and 64 + 16*q4 + j (v[16 + j]); bq[c][e] = v[8c + e]
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4a4 w0 = *reinterpret_cast<const u32x4a4*>(qrow + 64 * h + 16 * q4);
+      const u32x4a4 w1 = *reinterpret_cast<const u32x4a4*>(qrow + 64 * h + 16 * q4 + 8);
+      const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[16 * h + 2 * j] = widen16(w[j] & 0xFFFFu, bf);
+        v[16 * h + 2 * j + 1] = widen16(w[j] >> 16, bf);
+      }
+    }
+    const float qs = live ? a.qscale : 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      half8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[8 * c + e] * qs);
+      bq[c] = h;
+    }
+  } else {
+    // dims 32*q4 + j (v[j])
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4a4 w = *reinterpret_cast<const u32x4a4*>(qrow + 32 * q4 + 8 * k);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.signs + 32 * q4 + 8 * k);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.signs + 32 * q4 + 8 * k + 4);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * k + 2 * j] = widen16(ww[j] & 0xFFFFu, bf) * (j < 2 ? s0[2 * j] : s1[2 * j - 4]);
+        v[8 * k + 2 * j + 1] = widen16(ww[j] >> 16, bf) * (j < 2 ? s0[2 * j + 1] : s1[2 * j - 3]);
+      }
+    }
+#pragma unroll
+    for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j & hs) == 0) {
+          const float x0 = v[j], x1 = v[j + hs];
+          v[j] = x0 + x1;
+          v[j + hs] = x0 - x1;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {  // strides 32 and 64: lane quarters q4 ^ 1, q4 ^ 2
+      const bool upper = (threadIdx.x & m) != 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float o = __shfl_xor(v[j], m, 64);
+        v[j] = upper ? o - v[j] : v[j] + o;
+      }
+    }
+    const float qs = live ? a.qscale * 0.08838834764831845f : 0.f;  // 1/sqrt(128) of the rotation
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      half8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // inverse of qh_pos inside the lane's 32 dims
+        const int dd = T::kKb == 4 ? 8 * c + (e < 4 ? 2 * e : 2 * (e - 4) + 1) : (e & 3) * 8 + 2 * c + (e >> 2);
+        h[e] = static_cast<_Float16>(v[dd] * qs);
+      }
+      bq[c] = h;
+    }
+  }
+}
+
+// Stage 1.  A workgroup owns (sequence b, split s, group of G KV heads,
+// group of <= 16 query heads) and has one wave per KV head.  Each tile of
+// the split is staged into an LDS ring by the whole workgroup (contiguous
+// 16-byte chunks, R-1 tiles ahead), then every wave scores and accumulates
+// its own head's 16 slots from LDS.  Each wave writes its partial rows.
+template <int P>
+__global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
+  using T = Preset<P>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.heads_per_wg;
   const int S = a.num_splits, Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
-  const int HW = a.heads_per_wg;  // 1, 2 or 4
-  const int wph = kWaves / HW;    // waves per KV head
   int lg = xcd_remap(blockIdx.x, gridDim.x);
-  const int hgrp = lg % (Hk / HW);  // fastest: neighbouring heads share cache lines
-  lg /= Hk / HW;
+  const int hgp = lg % (Hk / G);
+  lg /= Hk / G;
   const int hg = lg % a.head_groups;
   lg /= a.head_groups;
   const int s = lg % S;
   const int b = lg / S;
-  const int hs = wave / wph;  // this wave's head slot in the workgroup
-  const int phase = wave % wph;
-  const int hk = hgrp * HW + hs;
+  const int hk = hgp * G + wave;
 
   const int seqlen = a.seq_lens[b];
   const int ntiles = (seqlen + 15) >> 4;
@@ -389,68 +524,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int t_end = min(t_begin + tps, ntiles);
   const int h0 = hg * 16;
   const int geff = min(16, g - h0);
-  // partial row of query head h0 + j of KV head hgrp*HW + k
-  auto part_row = [&](int k, int j) {
-    return a.partials + ((static_cast<int64_t>(b) * Hq + (hgrp * HW + k) * g + h0 + j) * S + s) * (kD + 1);
-  };
+  const int hl = lane & 15, q4 = lane >> 4;
+  const int64_t prow0 = (static_cast<int64_t>(b) * Hq + hk * g + h0) * S + s;  // partial row of query head h0
+  auto prow = [&](int j) { return prow0 + static_cast<int64_t>(j) * S; };
 
   if (t_begin >= t_end) {  // empty split: zero partial, lse = -inf
-    for (int idx = tid; idx < HW * geff * (kD + 1); idx += kThreads) {
-      const int k = idx / (geff * (kD + 1)), r = idx % (geff * (kD + 1));
-      const int j = r / (kD + 1), d = r % (kD + 1);
-      part_row(k, j)[d] = d == kD ? -INFINITY : 0.f;
-    }
+    for (int idx = lane; idx < geff * kD; idx += 64) a.part_o[prow(idx >> 7) * kD + (idx & (kD - 1))] = 0.f;
+    if (lane < geff) a.part_lse[prow(lane)] = -INFINITY;
     return;
   }
 
-  // ---- first tile's loads go out before the query prologue ----
-  const int hl = lane & 15, q4 = lane >> 4;
+  // ---- ring set-up and the first R-1 tiles ----
   const int bs_log2 = 31 - __clz(a.block_size);
   const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * Hk * T::kSlot;
   const uint32_t row = static_cast<uint32_t>(Hk * T::kSlot);
+  const uint32_t piece = static_cast<uint32_t>(G * T::kSlot);  // bytes of one token row piece
+  const uint32_t tc = piece;                                   // 16-byte chunks per tile (16 pieces)
+  const int ns = static_cast<int>((tc + 63) / 64);             // instruction slots per tile
+  Ring ring;
+  ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
+  ring.entry = static_cast<uint32_t>(ns) * 1024u;
+  ring.my_loads = (ns - wave + G - 1) / G;
+#pragma unroll
+  for (int n = 0; n < 5; ++n) {
+    uint32_t c = static_cast<uint32_t>(64 * (n * G + wave) + lane);
+    c = min(c, tc - 1);
+    const uint32_t cpp = piece / 16;  // chunks per piece (piece is a multiple of 16 unless G == Hk)
+    ring.off[n] = G == Hk ? 16 * c : (c / cpp) * row + hgp * piece + 16 * (c % cpp);
+  }
+  const int R = a.ring_depth;
   const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const LaneOff<P> off = lane_offsets<P>(hl, q4, hk, Hk);
-  const int t_first = t_begin + __builtin_amdgcn_readfirstlane(phase);
-  auto tile_base = [&](int t) -> const uint8_t* {
-    const int tok0 = t * 16;
-    const int blk = __builtin_amdgcn_readfirstlane(btab[tok0 >> bs_log2]);
-    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>(tok0 & (a.block_size - 1)) * row;
-  };
-  TileRegs<P> ra, rb;
-  if (t_first < t_end) load_tile<P>(tile_base(t_first), row, off, ra);
-
-  // ---- query rows of the workgroup's heads: sign flip + Walsh-Hadamard
-  // (MSE keys), scale by softmax scale * log2(e), fp16 in MFMA operand order
-  const int nrows = HW * 16;
-  const bool qbf16 = a.q_bf16 != 0;
-  for (int idx = tid; idx < nrows * kD; idx += kThreads) {
-    const int r = idx >> 7, d = idx & (kD - 1);
-    const int k = r >> 4, j = r & 15;
-    float v = 0.f;
-    if (j < geff) v = widen16(a.query[(static_cast<int64_t>(b) * Hq + (hgrp * HW + k) * g + h0 + j) * kD + d], qbf16);
-    if (!T::kFp8) v *= a.signs[d];
-    qf[r][d] = v;
-  }
-  __syncthreads();
-  if (!T::kFp8) {
-    for (int hsz = 1; hsz < kD; hsz <<= 1) {
-      for (int pi = tid; pi < nrows * (kD / 2); pi += kThreads) {
-        const int r = pi / (kD / 2), k = pi % (kD / 2);
-        const int i0 = (k / hsz) * 2 * hsz + (k % hsz), i1 = i0 + hsz;
-        const float x0 = qf[r][i0], x1 = qf[r][i1];
-        qf[r][i0] = x0 + x1;
-        qf[r][i1] = x0 - x1;
-      }
-      __syncthreads();
+  // block ids of the split's tiles, one per lane (window of 64 blocks)
+  const int blk_first = (t_begin * 16) >> bs_log2;
+  const int nblk_seq = (seqlen + a.block_size - 1) >> bs_log2;
+  int win0 = blk_first;
+  int bt_v = (win0 + lane < nblk_seq) ? btab[win0 + lane] : 0;
+  auto tile_src = [&](int t) -> const uint8_t* {
+    const int bi = (t * 16) >> bs_log2;
+    if (bi - win0 >= 64) {  // slide the window (rare: > 64 blocks in a split)
+      win0 = bi;
+      bt_v = (win0 + lane < nblk_seq) ? btab[win0 + lane] : 0;
     }
-  }
-  const float qs = T::kFp8 ? a.qscale : a.qscale * 0.08838834764831845f;  // 1/sqrt(128) of the rotation
-  for (int idx = tid; idx < nrows * kD; idx += kThreads) {
-    const int r = idx >> 7, d = idx & (kD - 1);
-    qh[r][qh_pos<P>(d)] = static_cast<_Float16>(qf[r][d] * qs);
-  }
+    const int blk = __builtin_amdgcn_readlane(bt_v, bi - win0);
+    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>((t * 16) & (a.block_size - 1)) * row;
+  };
+  auto issue = [&](int t, int entry) {
+    const uint8_t* src = tile_src(t);
+    const uint32_t m0 = ring.lds_base + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(wave) * 1024u;
+#pragma unroll
+    for (int n = 0; n < 5; ++n)
+      if (n < ring.my_loads) dma16(src + ring.off[n], m0 + static_cast<uint32_t>(n * G) * 1024u);
+  };
+  const int pre = min(R - 1, t_end - t_begin);
+  for (int d = 0; d < pre; ++d) issue(t_begin + d, d);
 
-  // codebook byte tables (fp16 centroids split into low / high bytes)
+  // ---- query operand and codebook tables (registers) ----
+  half8 bq[4];
+  query_operand<P>(a, b, hk, h0, geff, hl, q4, bq);
   tq::Lut8 la{}, lb{};
   if (!T::kFp8) {
     uint32_t hb[16];
@@ -464,102 +594,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     la = {pack(0, 0), pack(4, 0), pack(0, 8), pack(4, 8)};
     if (T::kKb == 4) lb = {pack(8, 0), pack(12, 0), pack(8, 8), pack(12, 8)};
   }
-  __syncthreads();
+  const LaneOff<P> off = lane_offsets<P>(hl, q4, wave, G);
 
-  half8 bq[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) bq[c] = *reinterpret_cast<const half8*>(&qh[hs * 16 + hl][q4 * 32 + c * 8]);
-
-  // ---- main loop over this wave's tiles, next tile's loads in flight ----
   Softmax sm{-INFINITY, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The prefetch is unconditional (past the wave's last tile it re-reads
-  // that tile, an L2 hit) so that every path into the loop has the same loads
-  // in flight and the waits stay exact; the scheduling barriers keep each
-  // prefetch issued before the compute of the current tile.
-  const int stride = __builtin_amdgcn_readfirstlane(wph);
-  int t = t_first;
-  while (t < t_end) {
-    load_tile<P>(tile_base(min(t + stride, t_end - 1)), row, off, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_step<P>(ra, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
-    t += stride;
-    if (t >= t_end) break;
-    load_tile<P>(tile_base(min(t + stride, t_end - 1)), row, off, ra);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_step<P>(rb, off, row, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
-    t += stride;
+  // ---- main loop: wait for tile t, release the entry of tile t-1, refill
+  // it with tile t+R-1, compute tile t from LDS ----
+  int entry = 0;
+  for (int t = t_begin; t < t_end; ++t) {
+    vm_wait(ring.my_loads * min(R - 2, t_end - 1 - t));
+    wg_barrier();
+    if (t + R - 1 < t_end) issue(t + R - 1, entry == 0 ? R - 1 : entry - 1);
+    TileRegs<P> r;
+    const uint8_t* img = tq_ring + static_cast<uint32_t>(entry) * ring.entry;
+    load_tile<P>(img, piece, off, r);
+    tile_step<P>(r, off, piece, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+    entry = entry + 1 == R ? 0 : entry + 1;
   }
-  float m_run = sm.m, l_run = sm.l, z_run = sm.z;
 
-  // ---- per-wave totals: lane quarters hold disjoint tokens ----
+  // ---- this wave's partial rows: output / l and the natural-log LSE ----
+  float l_run = sm.l, z_run = sm.z;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   z_run += __shfl_xor(z_run, 16, 64);
   z_run += __shfl_xor(z_run, 32, 64);
-  // unnormalized output of query head hl, dims 32*q4 + 8*i + n
-  float o[4][8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int pos = T::kVb == 4 ? tq::val4_pos(n) : tq::val3_pos(n);
-    const float unscale = static_cast<float>(1u << (24 - pos));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i][n] = fmaf(acc[n][i], unscale, z_run);
-  }
-
-  // ---- merge the waves of each head in LDS (reusing the query scratch) ----
-  // Each wave scales its unnormalized output by 2^(m_w - M) / l (M: max over
-  // the head's waves, l: merged softmax sum) and writes it as
-  // [wave][query head][dim]; the workgroup sums the waves of each head and
-  // writes every partial row with consecutive lanes on consecutive dims.
-  __syncthreads();
-  float* mo = smem;                               // [wave][16][kMergeStride]
-  float* mm = smem + kWaves * 16 * kMergeStride;  // [wave][16] maxima
-  float* ml = mm + kWaves * 16;                   // [wave][16] sums
-  if (q4 == 0) {
-    mm[wave * 16 + hl] = m_run;
-    ml[wave * 16 + hl] = l_run;
-  }
-  __syncthreads();
-  auto head_stats = [&](int hslot, int j, float& M, float& lsum) {
-    M = -INFINITY;
-    for (int k = 0; k < wph; ++k) M = fmaxf(M, mm[(hslot * wph + k) * 16 + j]);
-    lsum = 0.f;
-    for (int k = 0; k < wph; ++k) {
-      const float mw = mm[(hslot * wph + k) * 16 + j];
-      lsum = fmaf(mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M), ml[(hslot * wph + k) * 16 + j], lsum);
-    }
-  };
-  {
-    float M, lsum;
-    head_stats(hs, hl, M, lsum);
-    const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-    const float sc = lsum > 0.f ? f / lsum : 0.f;
-    float* rowp = mo + (wave * 16 + hl) * kMergeStride + 32 * q4;
+  if (hl < geff) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* orow = a.part_o + prow(hl) * kD + 32 * q4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x4 lo = {o[i][0] * sc, o[i][1] * sc, o[i][2] * sc, o[i][3] * sc};
-      f32x4 hi = {o[i][4] * sc, o[i][5] * sc, o[i][6] * sc, o[i][7] * sc};
-      *reinterpret_cast<f32x4*>(rowp + 8 * i) = lo;
-      *reinterpret_cast<f32x4*>(rowp + 8 * i + 4) = hi;
+      float o[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int pos = T::kVb == 4 ? tq::val4_pos(n) : tq::val3_pos(n);
+        o[n] = fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
+      }
+      *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(orow + 8 * i + 4) = f32x4{o[4], o[5], o[6], o[7]};
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < HW * geff * kD; idx += kThreads) {
-    const int k = idx / (geff * kD), r = idx % (geff * kD);
-    const int j = r >> 7, d = r & (kD - 1);
-    float v = 0.f;
-    for (int w = 0; w < wph; ++w) v += mo[((k * wph + w) * 16 + j) * kMergeStride + d];
-    part_row(k, j)[d] = v;
-  }
-  if (tid < HW * geff) {
-    const int k = tid / geff, j = tid % geff;
-    float M, lsum;
-    head_stats(k, j, M, lsum);
-    part_row(k, j)[kD] = (M + log2f(lsum)) * kLn2;
+    if (q4 == 0) a.part_lse[prow(hl)] = l_run > 0.f ? (sm.m + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }
 
@@ -572,48 +648,62 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __restrict__ partials, int rows, int S,
+// One wave per (sequence, query head): weights exp(lse_s - max), output =
+// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s).
+__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_lse, int rows, int S,
                                                                void* out, int out_dtype, float* lse_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const float* base = partials + static_cast<int64_t>(row) * S * (kD + 1);
+  const float* ob_in = part_o + static_cast<int64_t>(row) * S * kD;
+  const float* lb_in = part_lse + static_cast<int64_t>(row) * S;
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, base[static_cast<int64_t>(s) * (kD + 1) + kD]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lb_in[s]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float o0 = 0.f, o1 = 0.f, den = 0.f, lse = -INFINITY;
   if (M != -INFINITY) {
     for (int s = 0; s < S; ++s) {
-      const float* ps = base + static_cast<int64_t>(s) * (kD + 1);
-      const float ls = ps[kD];
+      const float ls = lb_in[s];
       const float w = ls == -INFINITY ? 0.f : expf(ls - M);
       den += w;
-      o0 = fmaf(w, ps[lane], o0);
-      o1 = fmaf(w, ps[lane + 64], o1);
+      const float2 v = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s) * kD + 2 * lane);
+      o0 = fmaf(w, v.x, o0);
+      o1 = fmaf(w, v.y, o1);
     }
     o0 /= den;
     o1 /= den;
     lse = M + logf(den);
   }
-  const int64_t ob = static_cast<int64_t>(row) * kD;
+  const int64_t ob = static_cast<int64_t>(row) * kD + 2 * lane;
   if (out_dtype == TQ_F32) {
-    static_cast<float*>(out)[ob + lane] = o0;
-    static_cast<float*>(out)[ob + lane + 64] = o1;
+    *reinterpret_cast<float2*>(static_cast<float*>(out) + ob) = make_float2(o0, o1);
   } else if (out_dtype == TQ_F16) {
-    static_cast<__half*>(out)[ob + lane] = __float2half_rn(o0);
-    static_cast<__half*>(out)[ob + lane + 64] = __float2half_rn(o1);
+    *reinterpret_cast<__half2*>(static_cast<__half*>(out) + ob) = __halves2half2(__float2half_rn(o0), __float2half_rn(o1));
   } else {
-    static_cast<uint16_t*>(out)[ob + lane] = f32_to_bf16_rne(o0);
-    static_cast<uint16_t*>(out)[ob + lane + 64] = f32_to_bf16_rne(o1);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + ob) =
+        static_cast<uint32_t>(f32_to_bf16_rne(o0)) | (static_cast<uint32_t>(f32_to_bf16_rne(o1)) << 16);
   }
   if (lse_out && lane == 0) lse_out[row] = lse;
 }
 
+constexpr int kMaxLds = 160 * 1024;
+
 template <int P>
-int launch_stage1(const DecodeArgs& a, int64_t nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL(tq_decode_stage1_kernel<P>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+int launch_stage1(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  });
+  if (attr != hipSuccess) return tq::hip_status(attr);
+  DecodeArgs arg = a;
+  void* args[] = {&arg};
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P>),
+                                        dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.heads_per_wg), args, lds,
+                                        stream));
 }
 
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
@@ -627,7 +717,9 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.seq_lens = seq_lens;
   a.signs = signs;
   a.centroids = centroids;
-  a.partials = static_cast<float*>(workspace);
+  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * num_kv_splits;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + rows * kD;
   a.qscale = scale * kLog2e;
   a.q_bf16 = q_dtype == TQ_BF16;
   a.num_q_heads = num_q_heads;
@@ -637,24 +729,22 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.block_size = block_size;
   a.bt_stride = block_table_stride;
   a.num_splits = num_kv_splits;
-  // Heads per workgroup: 4 when there are enough (sequence, split, head
-  // group) units to keep ~3 workgroups on each of the 256 CUs, else fewer
-  // (the waves of one head then share its tiles).
-  const int64_t units = static_cast<int64_t>(batch) * a.head_groups * num_kv_splits;
-  a.heads_per_wg = 1;
-  for (int hw : {4, 2}) {
-    if (num_kv_heads % hw == 0 && units * (num_kv_heads / hw) >= 768) {
-      a.heads_per_wg = hw;
-      break;
-    }
-  }
-  const int64_t nblocks = units * (num_kv_heads / a.heads_per_wg);
+  a.heads_per_wg = tq::decode_heads_per_wg(layout, num_kv_heads);
+  if (a.heads_per_wg <= 0) return TQ_EUNSUPPORTED;
+  // Ring depth: as many tiles as fit in 10 KB of LDS per wave (two
+  // 8-wave workgroups per CU), between 2 and 4.
+  const int G = a.heads_per_wg;
+  const size_t entry = static_cast<size_t>((G * layout->slot_size_aligned + 63) / 64) * 1024;
+  a.ring_depth = static_cast<int>(std::min<size_t>(4, std::max<size_t>(2, (10240u * G) / entry)));
+  const size_t lds = entry * a.ring_depth;
+  if (lds > static_cast<size_t>(kMaxLds)) return TQ_EUNSUPPORTED;
+  const int64_t nblocks = static_cast<int64_t>(batch) * num_kv_splits * (num_kv_heads / G) * a.head_groups;
   if (nblocks > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
   switch (layout->preset) {
-    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, stream);
-    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, nblocks, stream);
-    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, nblocks, stream);
-    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, nblocks, stream);
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, lds, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, nblocks, lds, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, nblocks, lds, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }
@@ -662,12 +752,28 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
 int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const void* workspace, void* out,
            int32_t out_dtype, float* lse_out, hipStream_t stream) {
   const int rows = batch * num_q_heads;
-  hipLaunchKernelGGL(tq_decode_stage2_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
-                     static_cast<const float*>(workspace), rows, num_kv_splits, out, out_dtype, lse_out);
-  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+  const float* part_o = static_cast<const float*>(workspace);
+  const float* part_lse = part_o + static_cast<int64_t>(rows) * num_kv_splits * kD;
+  int S = num_kv_splits;
+  void* args[] = {&part_o, &part_lse, const_cast<int*>(&rows), &S, &out, &out_dtype, &lse_out};
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel),
+                                        dim3((rows + 3) / 4), dim3(256), args, 0, stream));
 }
 
 }  // namespace
+
+namespace tq {
+namespace {
+thread_local hipError_t g_last_hip_error = hipSuccess;
+}
+int hip_status(int e) {
+  if (e == hipSuccess) return TQ_OK;
+  g_last_hip_error = static_cast<hipError_t>(e);
+  return TQ_EHIP;
+}
+}  // namespace tq
+
+extern "C" const char* tq_last_hip_error(void) { return hipGetErrorString(tq::g_last_hip_error); }
 
 extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,

@@ -226,9 +226,10 @@ template <int KEY_FP8, int KB, int VB, int NC>
 int launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
-  hipLaunchKernelGGL((tq_store_kernel<KEY_FP8, KB, VB, NC>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, a);
-  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+  StoreArgs arg = a;
+  void* args[] = {&arg};
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC>),
+                                        dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
 }
 
 }  // namespace

@@ -147,3 +147,13 @@ def test_decode_validation_codes():
     assert _decode_validate(L, signs=None) == tq.TQ_EINVAL
     assert _decode_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None) == tq.TQ_OK
     assert _decode_validate(L, B=0, q=None, sl=None, bt=None, ws=None, out=None) == tq.TQ_OK
+
+
+def test_one_hip_runtime_in_the_process():
+    """libtq.so binds to the HIP runtime torch already loaded: a second copy
+    would not see torch's streams or graph captures."""
+    import torch  # noqa: F401
+
+    maps = open("/proc/self/maps").read().split("\n")
+    paths = {l.split()[-1] for l in maps if "libamdhip64" in l and "/" in l}
+    assert len({os.path.realpath(p) for p in paths}) == 1, paths
