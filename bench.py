@@ -145,18 +145,20 @@ class DecodeBench:
         return e0.elapsed_time(e1) / steps  # ms per step
 
     def time_stage1(self, launches):
-        """Average stage-1 kernel duration (ms) from events around each launch."""
+        """Average stage-1 kernel duration (ms): events on the launch stream
+        around `launches` back-to-back stage-1 launches (rotating caches), so
+        per-launch host overhead is hidden behind the queued kernels."""
         torch = self.torch
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
         for i in range(N_COPIES):
             self.stage1(i)
         torch.cuda.synchronize()
-        for i, (a, b) in enumerate(evs):
-            a.record()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(launches):
             self.stage1(i % N_COPIES)
-            b.record()
+        b.record()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return a.elapsed_time(b) / launches
 
 
 def store_sweep(torch, tq, steps):
@@ -226,6 +228,52 @@ def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
                       f"threads up to the {cores} cores in the affinity mask"}
 
 
+KERNEL_SOURCES = ("quantized_decode_attention_tq_amd/csrc/tq_decode.hip", "quantized_decode_attention_tq_amd/csrc/tq_bits.h",
+                  "quantized_decode_attention_tq_amd/csrc/tq_internal.h", "include/tq.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tq_decode_stage1_k8v4_llama8b_traffic.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per stage-1 launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(torch, mib: int = 512, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +282,8 @@ def main():
     ap.add_argument("--splits", type=int, default=8)
     ap.add_argument("--only", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain copy of 512 MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -241,6 +291,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     import quantized_decode_attention_tq_amd as tq
 
     w = W.WORKLOADS["llama8b"]
@@ -289,7 +343,7 @@ def main():
                    "global_batch": w.batch, "seq_len": int(w.seq_len), "num_kv_splits": args.splits,
                    "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head_bytes},
         "roofline": {"bound": "hbm", "achieved": st1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": st1_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "tq_decode_stage1_kernel<k8v4>",
+                     "frac": st1_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(), "kernel": "tq_decode_stage1_kernel<k8v4>",
                      "stage1_us": st1_ms * 1e3},
         "cpu_baseline": cpu,
         "extra": extra,
