@@ -26,8 +26,8 @@ Sources (cited by page title and section; the pages are the only authority):
 * [TQ+]    Atlas docs "TurboQuant+ — KV-cache compression beyond the Google
            baseline": sections "Background", "What landed (file-by-file)".
 
-Readings of points the pages leave open are listed in DESIGN.md ("Readings");
-each function below names the reading it takes.
+Where the pages leave a point open, the function that depends on it
+states the reading it takes.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (and guarded by the planted-mistake tests in
