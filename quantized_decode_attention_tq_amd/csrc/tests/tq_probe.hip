@@ -98,6 +98,19 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in,
     out[i] = in[i];
 }
 
+// one wave64: out[0..63], out[64..127] = the two results of permlane16_swap
+// (v, v); out[128..191], out[192..255] = those of permlane32_swap (v, v)
+__global__ void permlane_kernel(const uint32_t* in, uint32_t* out) {
+  const int l = threadIdx.x;
+  const uint32_t v = in[l];
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  out[l] = a[0];
+  out[64 + l] = a[1];
+  out[128 + l] = c[0];
+  out[192 + l] = c[1];
+}
+
 int finish() {
   if (hipGetLastError() != hipSuccess) return -8;
   return hipDeviceSynchronize() == hipSuccess ? 0 : -8;
@@ -129,6 +142,12 @@ int tq_probe_mfma_16x16x32_f16(const uint32_t* a, const uint32_t* b, float* d) {
 // one wave64: a, b device [64][2] dwords, d device [64][4] floats
 int tq_probe_mfma_16x16x16_f16(const uint32_t* a, const uint32_t* b, float* d) {
   hipLaunchKernelGGL(mfma16_kernel, dim3(1), dim3(64), 0, 0, a, b, d);
+  return finish();
+}
+
+// one wave64: in device [64] dwords, out device [256] dwords
+int tq_probe_permlane_swap(const uint32_t* in, uint32_t* out) {
+  hipLaunchKernelGGL(permlane_kernel, dim3(1), dim3(64), 0, 0, in, out);
   return finish();
 }
 

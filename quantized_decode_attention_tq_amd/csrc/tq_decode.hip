@@ -24,6 +24,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -43,6 +44,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef const __attribute__((address_space(4))) int32_t cint32;  // constant (scalar-loadable) memory
 
 // Slot geometry per preset at head_dim 128 (see tq_layout_init).
 template <int P>
@@ -87,8 +89,11 @@ struct DecodeArgs {
   float qscale;     // softmax scale * log2(e)
   int32_t q_bf16;
   int32_t num_q_heads, num_kv_heads, group, head_groups;
-  int32_t heads_per_wg;  // KV heads (= waves) per workgroup
-  int32_t ring_depth;    // tiles in the LDS ring
+  int32_t G;           // KV heads per workgroup
+  int32_t P;           // waves per KV head (tile phases)
+  int32_t ring_depth;  // super-tiles (P tiles each) in the LDS ring
+  int32_t spt;         // 1 KB direct-to-LDS slots per tile image
+  int32_t contiguous;  // G == Hk: a tile of the group is one run of 16 token rows
   int32_t block_size, bt_stride, num_splits;
 };
 
@@ -149,14 +154,32 @@ __device__ __forceinline__ half4 as_half4(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
-// Byte offsets (lane constants) of what one lane loads for a 16-token tile,
-// relative to the tile's first slot row.  Block bases and the tile's first
-// row are multiples of 32 bytes, so the alignment of every address is a lane
-// constant too: unaligned fields are read as aligned dwords and realigned.
+// Reductions over the four lane quarters (lanes l, l^16, l^32, l^48) with
+// the row-swap permutes: permlane16_swap leaves each lane holding its own
+// value and that of lane l^16 (one in each result), permlane32_swap the same
+// for l^32.  No LDS round trip.
+__device__ __forceinline__ float quarter_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float quarter_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Byte offsets (lane constants) of what one lane reads from a tile image in
+// LDS.  The image keeps every slot at the same alignment mod 16 as in the
+// cache, and that alignment depends only on the token row and the head, so
+// each address's alignment is a lane constant: unaligned fields are read as
+// aligned dwords and realigned.
 template <int P>
 struct LaneOff {
   uint32_t k, ksh;  // aligned-down key chunk start, its misalignment
-  uint32_t meta0;   // slot start of token 4q (token 4q+i is i rows further)
+  uint32_t mo[4];   // slot start of token 4q + i
   uint32_t vcol;    // byte offset of the lane's value-code column inside a slot
 };
 
@@ -169,23 +192,17 @@ struct TileRegs {
   uint32_t gm[4];  // fp16 key norm (MSE keys)
 };
 
-template <int P>
-__device__ __forceinline__ LaneOff<P> lane_offsets(int hl, int q4, int hk, int Hk) {
-  using T = Preset<P>;
-  LaneOff<P> o;
-  const uint32_t kraw = static_cast<uint32_t>((hl * Hk + hk) * T::kSlot) +
-                        static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
-  o.k = kraw & ~3u;
-  o.ksh = kraw & 3u;
-  o.meta0 = static_cast<uint32_t>((4 * q4 * Hk + hk) * T::kSlot);
-  o.vcol = static_cast<uint32_t>(T::kKps + (T::kVb == 4 ? 4 * hl : 3 * hl));
-  return o;
-}
+// Where the workgroup's rows sit in the cache and how its tile image is
+// laid out (see the staging notes below).
+struct ImageGeom {
+  uint32_t base;  // hgp * G * slot: byte offset of the group's piece in a cache row
+  uint32_t row;   // Hk * slot: bytes of a cache row
+  bool contiguous;
+};
 
-// Issue every load of one tile.  tb: the tile's first slot row (uniform);
-// row: bytes per token row (Hk * slot, uniform).
+// Read one tile's fields of this lane from the tile image at tb.
 template <int P>
-__device__ __forceinline__ void load_tile(const uint8_t* tb, uint32_t row, const LaneOff<P>& o, TileRegs<P>& r) {
+__device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
   if constexpr (T::kFp8 != 0) {
     const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
@@ -201,7 +218,7 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, uint32_t row, const
   for (int i = 0; i < 4; ++i) {
     // value codes of token 4q+i; the row stride may be 2 mod 4, so the
     // whole in-tile offset is aligned down (tile bases are 32-byte aligned)
-    const uint32_t vo = i * row + o.meta0 + o.vcol;
+    const uint32_t vo = o.mo[i] + o.vcol;
     if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
       r.v[i][0] = *reinterpret_cast<const uint32_t*>(tb + vo);
     } else {
@@ -209,7 +226,7 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, uint32_t row, const
       r.v[i][0] = w.x;
       r.v[i][1] = w.y;
     }
-    const uint8_t* m = tb + i * row + o.meta0;
+    const uint8_t* m = tb + o.mo[i];
     if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
       r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
     } else {
@@ -266,10 +283,11 @@ struct Softmax {
 // rescaled; p * value_scale must also stay inside fp16.
 constexpr float kLazyRescaleLog2 = 8.0f;
 
+// valid: tokens of the tile before the sequence end (1..16).
 template <int P>
-__device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>& o, uint32_t row,
-                                          const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4], int valid,
-                                          Softmax& sm, f32x4 acc[8]) {
+__device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
+                                          const tq::Lut8& lb, const half8 bq[4], int valid, Softmax& sm,
+                                          f32x4 acc[8]) {
   using T = Preset<P>;
   half8 A[4];
   key_operand<P>(r, o.ksh, la, lb, A);
@@ -295,9 +313,7 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
       }
     }
   }
-  float tmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float tmax = quarter_max(fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3])));
   const float m_cand = fmaxf(sm.m, tmax);
   float p[4], ps[4];
   bool redo = __any(tmax > sm.m + kLazyRescaleLog2);
@@ -339,7 +355,7 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
     if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4)
       vw[i] = r.v[i][0];
     else
-      vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (i * row + o.meta0 + o.vcol) & 3u);
+      vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (o.mo[i] + o.vcol) & 3u);
   }
   uint32_t v01[8], v23[8];
   if (T::kVb == 4) {
@@ -354,25 +370,27 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
     acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
 }
 
-// ---- tile staging: block rows -> LDS ring by direct-to-LDS loads ----
+// ---- tile staging: cache rows -> LDS ring by direct-to-LDS loads ----
 //
 // A tile is 16 consecutive token rows of the cache restricted to the
-// workgroup's G KV heads: 16 row pieces of G * slot bytes, each at
-// row_piece(i) = i * row + h0 * slot from the tile base (row = Hk * slot).
-// Either G == Hk (the 16 pieces are one contiguous run) or row is a
-// multiple of 16 (Hk % 8 == 0), so the whole tile is TC = G * slot 16-byte
-// chunks whose chunk c (piece c / (G*slot/16)) lies at a 16-byte aligned
-// global address.  The LDS image of a tile is the byte-exact concatenation
-// of the pieces: slot (token i, head h0 + hh) sits at i*G*slot + hh*slot,
-// with the same alignment mod 16 as in the cache.  Chunks are spread over
-// the workgroup's waves as "instruction slots" of 64 chunks: slot k =
-// n * G + wave is the wave's n-th load; lanes past TC repeat the last chunk
-// into the padding at the end of the ring entry.
+// workgroup's G KV heads: 16 row pieces of G * slot bytes at a row stride of
+// row = Hk * slot.  With G == Hk the pieces form one contiguous run of 16 *
+// row bytes (tile bases are 32-byte aligned).  Otherwise each piece is
+// fetched as the 16-byte chunks that cover it, from its start aligned down
+// to 16 bytes (cpp chunks per piece), so the image keeps every byte at its
+// cache alignment mod 16 and a few neighbouring bytes ride along.  Chunks go
+// out in 1 KB "DMA slots" of 64 lanes x 16 bytes; a tile image takes spt
+// slots (lanes past the last chunk repeat it into the image's padding).  A
+// super-tile is P consecutive tiles; one ring entry holds one super-tile.
+// Tile p of a super-tile is staged by the G waves of phase p (the waves
+// that will compute it): wave (hh, p) issues slots hh, hh + G, ... of it,
+// so a wave needs one block id and one base address per super-tile.
 struct Ring {
-  uint32_t lds_base;    // LDS byte address of ring entry 0 (uniform)
-  uint32_t entry;       // bytes per ring entry (multiple of 1024)
-  int my_loads;         // loads per tile issued by this wave
-  uint32_t off[5];      // per load: chunk byte offset from the tile base
+  uint32_t lds_base;  // LDS byte address of ring entry 0 (uniform)
+  uint32_t entry;     // bytes per ring entry (P * spt KB)
+  int my_loads;       // DMA slots per super-tile issued by this wave
+  uint32_t dst[5];    // per load: LDS offset inside the entry (uniform)
+  uint32_t off[5];    // per load: this lane's chunk offset from the tile base
 };
 
 // One direct-to-LDS load of 16 bytes per lane, non-temporal: the data is
@@ -494,19 +512,23 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
   }
 }
 
-// Stage 1.  A workgroup owns (sequence b, split s, group of G KV heads,
-// group of <= 16 query heads) and has one wave per KV head.  Each tile of
-// the split is staged into an LDS ring by the whole workgroup (contiguous
-// 16-byte chunks, R-1 tiles ahead), then every wave scores and accumulates
-// its own head's 16 slots from LDS.  Each wave writes its partial rows.
+// Stage 1.  A workgroup owns (sequence b, split s, group of G KV heads, up
+// to 16 query heads per KV head) and runs W = G * P waves: wave w serves KV
+// head w % G of the group in tile phase w / G.  The split's tiles are staged
+// into an LDS ring one super-tile (P consecutive tiles) at a time by the
+// whole workgroup, R-1 super-tiles ahead; the phase-p wave of a head scores
+// and accumulates tile p of every super-tile from LDS.  At the end the P
+// phase waves of a head merge their partial softmax states through LDS and
+// the phase-0 wave writes the split's partial rows.
 template <int P>
 __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = a.heads_per_wg;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.G, NP = a.P;
+  const int hh = w % G, ph = w / G;
   const int S = a.num_splits, Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
   int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int hgp = lg % (Hk / G);
@@ -515,7 +537,7 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   lg /= a.head_groups;
   const int s = lg % S;
   const int b = lg / S;
-  const int hk = hgp * G + wave;
+  const int hk = hgp * G + hh;
 
   const int seqlen = a.seq_lens[b];
   const int ntiles = (seqlen + 15) >> 4;
@@ -529,54 +551,90 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   auto prow = [&](int j) { return prow0 + static_cast<int64_t>(j) * S; };
 
   if (t_begin >= t_end) {  // empty split: zero partial, lse = -inf
-    for (int idx = lane; idx < geff * kD; idx += 64) a.part_o[prow(idx >> 7) * kD + (idx & (kD - 1))] = 0.f;
-    if (lane < geff) a.part_lse[prow(lane)] = -INFINITY;
+    if (ph == 0) {
+      for (int idx = lane; idx < geff * kD; idx += 64) a.part_o[prow(idx >> 7) * kD + (idx & (kD - 1))] = 0.f;
+      if (lane < geff) a.part_lse[prow(lane)] = -INFINITY;
+    }
     return;
   }
 
-  // ---- ring set-up and the first R-1 tiles ----
-  const int bs_log2 = 31 - __clz(a.block_size);
-  const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * Hk * T::kSlot;
-  const uint32_t row = static_cast<uint32_t>(Hk * T::kSlot);
-  const uint32_t piece = static_cast<uint32_t>(G * T::kSlot);  // bytes of one token row piece
-  const uint32_t tc = piece;                                   // 16-byte chunks per tile (16 pieces)
-  const int ns = static_cast<int>((tc + 63) / 64);             // instruction slots per tile
+  // ---- tile image geometry ----
+  ImageGeom geo;
+  geo.row = static_cast<uint32_t>(Hk * T::kSlot);
+  geo.base = static_cast<uint32_t>(hgp * G * T::kSlot);
+  geo.contiguous = a.contiguous != 0;
+  const uint32_t piece = static_cast<uint32_t>(G * T::kSlot);
+  // chunks covering row piece r: from its start aligned down to 16 bytes up
+  // to its end aligned up, so no chunk crosses the end of its cache block
+  auto piece_chunks = [&](int r) { return (((geo.base + r * geo.row) & 15u) + piece + 15u) >> 4; };
+  uint32_t tc;  // 16-byte chunks of one tile image
+  if (geo.contiguous) {
+    tc = geo.row;  // 16 rows of `row` bytes
+  } else {
+    tc = 0;
+    for (int r = 0; r < 16; ++r) tc += piece_chunks(r);
+  }
+  // LDS start of token row r: chunk prefix of the rows before it plus the
+  // row piece's misalignment
+  auto row_start = [&](int r) -> uint32_t {
+    if (geo.contiguous) return r * geo.row;
+    uint32_t c = 0;
+    for (int i = 0; i < r; ++i) c += piece_chunks(i);
+    return 16 * c + ((geo.base + r * geo.row) & 15u);
+  };
+
+  // ---- ring: this wave's DMA slots of each super-tile ----
+  const int spt = a.spt;
   Ring ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
-  ring.entry = static_cast<uint32_t>(ns) * 1024u;
-  ring.my_loads = (ns - wave + G - 1) / G;
+  ring.entry = static_cast<uint32_t>(NP * spt) * 1024u;
+  ring.my_loads = (spt - hh + G - 1) / G;
 #pragma unroll
-  for (int n = 0; n < 5; ++n) {
-    uint32_t c = static_cast<uint32_t>(64 * (n * G + wave) + lane);
-    c = min(c, tc - 1);
-    const uint32_t cpp = piece / 16;  // chunks per piece (piece is a multiple of 16 unless G == Hk)
-    ring.off[n] = G == Hk ? 16 * c : (c / cpp) * row + hgp * piece + 16 * (c % cpp);
+  for (int k = 0; k < 5; ++k) {
+    const int n = hh + k * G;  // slot of tile ph (n < spt for k < my_loads)
+    ring.dst[k] = static_cast<uint32_t>(ph * spt + n) * 1024u;
+    uint32_t c = min(static_cast<uint32_t>(64 * n + lane), tc - 1);
+    if (geo.contiguous) {
+      ring.off[k] = 16 * c;
+    } else {
+      int r = 0;
+      uint32_t first = 0;  // first chunk of row r
+      for (int i = 0; i < 15; ++i) {
+        const uint32_t nc = piece_chunks(r);
+        if (c >= first + nc) {
+          first += nc;
+          ++r;
+        }
+      }
+      ring.off[k] = ((geo.base + r * geo.row) & ~15u) + 16 * (c - first);
+    }
   }
   const int R = a.ring_depth;
-  const int32_t* btab = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  // block ids of the split's tiles, one per lane (window of 64 blocks)
-  const int blk_first = (t_begin * 16) >> bs_log2;
-  const int nblk_seq = (seqlen + a.block_size - 1) >> bs_log2;
-  int win0 = blk_first;
-  int bt_v = (win0 + lane < nblk_seq) ? btab[win0 + lane] : 0;
-  auto tile_src = [&](int t) -> const uint8_t* {
-    const int bi = (t * 16) >> bs_log2;
-    if (bi - win0 >= 64) {  // slide the window (rare: > 64 blocks in a split)
-      win0 = bi;
-      bt_v = (win0 + lane < nblk_seq) ? btab[win0 + lane] : 0;
-    }
-    const int blk = __builtin_amdgcn_readlane(bt_v, bi - win0);
-    return a.cache + static_cast<int64_t>(blk) * blk_bytes + static_cast<int64_t>((t * 16) & (a.block_size - 1)) * row;
-  };
-  auto issue = [&](int t, int entry) {
-    const uint8_t* src = tile_src(t);
-    const uint32_t m0 = ring.lds_base + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(wave) * 1024u;
+  const int bs_log2 = 31 - __clz(a.block_size);
+  const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * geo.row;
+  // Block ids are read with scalar loads (the table is constant while the
+  // kernel runs): a vector load here would make the compiler drain every
+  // outstanding ring load before its result could be used.
+  const cint32* btab = (const cint32*)(a.block_table) + static_cast<int64_t>(b) * a.bt_stride;
+  const uint32_t blk_bytes32 = static_cast<uint32_t>(blk_bytes);
+  // block id of this wave's tile of super-tile u; tiles past the split's end
+  // stand in for its last tile (in bounds; loaded, never computed), so every
+  // wave issues the same number of loads per super-tile
+  auto my_tile = [&](int u) { return min(t_begin + u * NP + ph, t_end - 1); };
+  auto block_of = [&](int t) { return btab[(t * 16) >> bs_log2]; };
+  auto issue = [&](int u, int entry, int blk) {
+    const int t = my_tile(u);
+    const uint8_t* base = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk)) * blk_bytes32 +
+                          static_cast<uint32_t>((t * 16) & (a.block_size - 1)) * geo.row;
+    const uint32_t e0 = ring.lds_base + static_cast<uint32_t>(entry) * ring.entry;
 #pragma unroll
-    for (int n = 0; n < 5; ++n)
-      if (n < ring.my_loads) dma16(src + ring.off[n], m0 + static_cast<uint32_t>(n * G) * 1024u);
+    for (int k = 0; k < 5; ++k)
+      if (k < ring.my_loads) dma16(base + ring.off[k], e0 + ring.dst[k]);
   };
-  const int pre = min(R - 1, t_end - t_begin);
-  for (int d = 0; d < pre; ++d) issue(t_begin + d, d);
+  const int nst = (t_end - t_begin + NP - 1) / NP;
+  const int pre = min(R - 1, nst);
+  for (int d = 0; d < pre; ++d) issue(d, d, block_of(my_tile(d)));
+  int blk_next = block_of(my_tile(R - 1));  // next refill's block id, fetched a step ahead
 
   // ---- query operand and codebook tables (registers) ----
   half8 bq[4];
@@ -594,48 +652,100 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
     la = {pack(0, 0), pack(4, 0), pack(0, 8), pack(4, 8)};
     if (T::kKb == 4) lb = {pack(8, 0), pack(12, 0), pack(8, 8), pack(12, 8)};
   }
-  const LaneOff<P> off = lane_offsets<P>(hl, q4, wave, G);
+  LaneOff<P> off;
+  {
+    const uint32_t kraw = row_start(hl) + static_cast<uint32_t>(hh * T::kSlot) +
+                          static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
+    off.k = kraw & ~3u;
+    off.ksh = kraw & 3u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) off.mo[i] = row_start(4 * q4 + i) + static_cast<uint32_t>(hh * T::kSlot);
+    off.vcol = static_cast<uint32_t>(T::kKps + (T::kVb == 4 ? 4 * hl : 3 * hl));
+  }
 
   Softmax sm{-INFINITY, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- main loop: wait for tile t, release the entry of tile t-1, refill
-  // it with tile t+R-1, compute tile t from LDS ----
+  // ---- main loop: wait for super-tile u, release the entry of u-1, refill
+  // it with u+R-1, compute this wave's tile of u from LDS ----
   int entry = 0;
-  for (int t = t_begin; t < t_end; ++t) {
-    vm_wait(ring.my_loads * min(R - 2, t_end - 1 - t));
+  for (int u = 0; u < nst; ++u) {
+    vm_wait(ring.my_loads * min(R - 2, nst - 1 - u));
     wg_barrier();
-    if (t + R - 1 < t_end) issue(t + R - 1, entry == 0 ? R - 1 : entry - 1);
-    TileRegs<P> r;
-    const uint8_t* img = tq_ring + static_cast<uint32_t>(entry) * ring.entry;
-    load_tile<P>(img, piece, off, r);
-    tile_step<P>(r, off, piece, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+    if (u + R - 1 < nst) {
+      issue(u + R - 1, entry == 0 ? R - 1 : entry - 1, blk_next);
+      blk_next = block_of(my_tile(u + R));
+    }
+    const int t = t_begin + u * NP + ph;
+    if (t < t_end) {
+      TileRegs<P> r;
+      const uint8_t* img = tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * spt) * 1024u;
+      load_tile<P>(img, off, r);
+      tile_step<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+    }
     entry = entry + 1 == R ? 0 : entry + 1;
   }
 
-  // ---- this wave's partial rows: output / l and the natural-log LSE ----
-  float l_run = sm.l, z_run = sm.z;
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  z_run += __shfl_xor(z_run, 16, 64);
-  z_run += __shfl_xor(z_run, 32, 64);
-  if (hl < geff) {
+  // ---- this wave's normalized partial (output / l, base-2 LSE) ----
+  const float l_run = quarter_sum(sm.l), z_run = quarter_sum(sm.z);
+  float o[32];  // o[8 * i + n]: acc[n][i] as output
+  {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* orow = a.part_o + prow(hl) * kD + 32 * q4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float o[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const int pos = T::kVb == 4 ? tq::val4_pos(n) : tq::val3_pos(n);
-        o[n] = fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
+        o[8 * i + n] = fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
       }
-      *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<f32x4*>(orow + 8 * i + 4) = f32x4{o[4], o[5], o[6], o[7]};
     }
-    if (q4 == 0) a.part_lse[prow(hl)] = l_run > 0.f ? (sm.m + log2f(l_run)) * kLn2 : -INFINITY;
+  }
+  float lse2 = l_run > 0.f ? sm.m + log2f(l_run) : -INFINITY;
+
+  // ---- merge the P phase waves of each head (through LDS) ----
+  if (NP > 1) {
+    wg_barrier();  // every wave is done with the ring
+    float* mrg = reinterpret_cast<float*>(tq_ring);
+    if (ph > 0) {
+      float* reg = mrg + ((ph - 1) * G + hh) * (33 * 64);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) reg[k * 64 + lane] = o[k];
+      reg[32 * 64 + lane] = lse2;
+    }
+    wg_barrier();
+    if (ph == 0) {
+      float M = lse2;
+      for (int p = 1; p < NP; ++p) M = fmaxf(M, mrg[((p - 1) * G + hh) * (33 * 64) + 32 * 64 + lane]);
+      float wsum = __builtin_amdgcn_exp2f(lse2 - M);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) o[k] *= wsum;
+      for (int p = 1; p < NP; ++p) {
+        const float* reg = mrg + ((p - 1) * G + hh) * (33 * 64);
+        const float lp = reg[32 * 64 + lane];
+        if (lp == -INFINITY) continue;
+        const float wp = __builtin_amdgcn_exp2f(lp - M);
+        wsum += wp;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) o[k] = fmaf(wp, reg[k * 64 + lane], o[k]);
+      }
+      const float inv = 1.f / wsum;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) o[k] *= inv;
+      lse2 = M + log2f(wsum);
+    }
+  }
+
+  // ---- the split's partial rows: output and natural-log LSE ----
+  if (ph == 0 && hl < geff) {
+    float* orow = a.part_o + prow(hl) * kD + 32 * q4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{o[8 * i], o[8 * i + 1], o[8 * i + 2], o[8 * i + 3]};
+      *reinterpret_cast<f32x4*>(orow + 8 * i + 4) = f32x4{o[8 * i + 4], o[8 * i + 5], o[8 * i + 6], o[8 * i + 7]};
+    }
+    if (q4 == 0) a.part_lse[prow(hl)] = lse2 * kLn2;
   }
 }
 
@@ -649,14 +759,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // One wave per (sequence, query head): weights exp(lse_s - max), output =
-// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s).
+// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s).  Lane s holds the
+// weight of split s (64 splits per pass); the partial rows are read eight
+// splits at a time so their loads overlap.
 __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __restrict__ part_o,
                                                                const float* __restrict__ part_lse, int rows, int S,
                                                                void* out, int out_dtype, float* lse_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const float* ob_in = part_o + static_cast<int64_t>(row) * S * kD;
+  const float* ob_in = part_o + static_cast<int64_t>(row) * S * kD + 2 * lane;
   const float* lb_in = part_lse + static_cast<int64_t>(row) * S;
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, lb_in[s]);
@@ -664,14 +776,35 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __re
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float o0 = 0.f, o1 = 0.f, den = 0.f, lse = -INFINITY;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lb_in[s];
-      const float w = ls == -INFINITY ? 0.f : expf(ls - M);
-      den += w;
-      const float2 v = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s) * kD + 2 * lane);
-      o0 = fmaf(w, v.x, o0);
-      o1 = fmaf(w, v.y, o1);
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int ns = min(64, S - s0);
+      float wl = 0.f;
+      if (lane < ns) {
+        const float ls = lb_in[s0 + lane];
+        wl = ls == -INFINITY ? 0.f : expf(ls - M);
+      }
+      den += wl;
+      int j = 0;
+      for (; j + 8 <= ns; j += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s0 + j + u) * kD);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
+          o0 = fmaf(wu, v[u].x, o0);
+          o1 = fmaf(wu, v[u].y, o1);
+        }
+      }
+      for (; j < ns; ++j) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+        const float2 v = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s0 + j) * kD);
+        o0 = fmaf(wu, v.x, o0);
+        o1 = fmaf(wu, v.y, o1);
+      }
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
     o0 /= den;
     o1 /= den;
     lse = M + logf(den);
@@ -690,6 +823,18 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __re
 
 constexpr int kMaxLds = 160 * 1024;
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int P>
 int launch_stage1(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
   static std::once_flag once;
@@ -702,7 +847,7 @@ int launch_stage1(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t 
   DecodeArgs arg = a;
   void* args[] = {&arg};
   return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P>),
-                                        dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.heads_per_wg), args, lds,
+                                        dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
                                         stream));
 }
 
@@ -729,17 +874,16 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.block_size = block_size;
   a.bt_stride = block_table_stride;
   a.num_splits = num_kv_splits;
-  a.heads_per_wg = tq::decode_heads_per_wg(layout, num_kv_heads);
-  if (a.heads_per_wg <= 0) return TQ_EUNSUPPORTED;
-  // Ring depth: as many tiles as fit in 10 KB of LDS per wave (two
-  // 8-wave workgroups per CU), between 2 and 4.
-  const int G = a.heads_per_wg;
-  const size_t entry = static_cast<size_t>((G * layout->slot_size_aligned + 63) / 64) * 1024;
-  a.ring_depth = static_cast<int>(std::min<size_t>(4, std::max<size_t>(2, (10240u * G) / entry)));
-  const size_t lds = entry * a.ring_depth;
-  if (lds > static_cast<size_t>(kMaxLds)) return TQ_EUNSUPPORTED;
-  const int64_t nblocks = static_cast<int64_t>(batch) * num_kv_splits * (num_kv_heads / G) * a.head_groups;
-  if (nblocks > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
+  tq::DecodePlan plan;
+  const int st = tq::decode_plan(layout, batch, num_q_heads, num_kv_heads, num_kv_splits, num_cus(), &plan);
+  if (st != TQ_OK) return st;
+  a.G = plan.G;
+  a.P = plan.P;
+  a.ring_depth = plan.R;
+  a.spt = plan.spt;
+  a.contiguous = plan.contiguous;
+  const int64_t nblocks = plan.grid;
+  const size_t lds = plan.lds;
   switch (layout->preset) {
     case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, lds, stream);
     case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, nblocks, lds, stream);

@@ -34,18 +34,51 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
 int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                     const void* workspace, size_t ws_bytes, const void* out, int32_t out_dtype);
 
-// KV heads per stage-1 workgroup (one wave each) for this layout, or 0 when
-// no grouping keeps every staged 16-byte chunk aligned.  A workgroup stages
-// the 16 token rows of a tile restricted to its G heads: with G == Hk that
-// is one contiguous run; otherwise every row piece (G * slot bytes at a row
-// stride of Hk * slot) must start on a 16-byte boundary.
-inline int decode_heads_per_wg(const tq_layout* L, int32_t num_kv_heads) {
-  const int slot = L->slot_size_aligned;
-  if (num_kv_heads <= 8) return num_kv_heads;
-  if ((num_kv_heads * slot) % 16 != 0) return 0;
-  for (int g = 8; g >= 1; g >>= 1)
-    if (num_kv_heads % g == 0 && (g * slot) % 16 == 0) return g;
-  return 0;
+// Launch plan of decode stage 1 (host).  A workgroup serves G KV heads with
+// P waves each (G * P <= 8 waves).  G is the largest divisor of Hk (<= 8)
+// that still gives at least two workgroups per compute unit, else 1; the P
+// waves of a head split its tiles.  A tile image (16 token rows of the
+// group) takes spt 1 KB slots of LDS; the ring holds R super-tiles of P
+// tiles, sized for two workgroups per compute unit.
+struct DecodePlan {
+  int G, P, R, spt, contiguous;
+  size_t lds;    // dynamic LDS bytes per workgroup
+  int64_t grid;  // workgroups
+};
+
+inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t num_splits, int num_cus, DecodePlan* p) {
+  constexpr size_t kLdsBudget = 80 * 1024, kLdsMax = 160 * 1024;
+  const int64_t slot = L->slot_size_aligned;
+  const int64_t row = num_kv_heads * slot;
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t units = static_cast<int64_t>(batch) * num_splits * ((group + 15) / 16);
+  int G = 1;
+  for (int d = num_kv_heads < 8 ? num_kv_heads : 8; d >= 1; --d) {
+    if (num_kv_heads % d != 0) continue;
+    G = d;
+    if (units * (num_kv_heads / d) >= 2LL * num_cus) break;
+  }
+  const int P = G >= 8 ? 1 : 8 / G;
+  const bool contiguous = G == num_kv_heads;
+  const int64_t piece = G * slot;
+  const int64_t tc_max = contiguous ? row : 16 * ((piece + 30) / 16);  // chunks per tile image
+  const int spt = static_cast<int>((tc_max + 63) / 64);
+  const size_t entry = static_cast<size_t>(P) * spt * 1024;
+  size_t R = kLdsBudget / entry;
+  R = R < 2 ? 2 : (R > 4 ? 4 : R);
+  const size_t merge = P > 1 ? static_cast<size_t>(P - 1) * G * 33 * 64 * 4 : 0;
+  p->G = G;
+  p->P = P;
+  p->R = static_cast<int>(R);
+  p->spt = spt;
+  p->contiguous = contiguous;
+  p->lds = R * entry > merge ? R * entry : merge;
+  p->grid = units * (num_kv_heads / G);
+  const int loads = (spt + G - 1) / G;  // DMA slots per wave per super-tile (its phase's tile)
+  const int64_t blk_bytes = 128 * row;   // largest block (block_size 128)
+  if (p->lds > kLdsMax || loads > 5 || p->grid > 0x7FFFFFFF || blk_bytes > 0xFFFFFFFFLL) return TQ_EUNSUPPORTED;
+  return TQ_OK;
 }
 
 }  // namespace tq

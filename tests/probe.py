@@ -17,6 +17,8 @@ OPS = {"perm": 0, "alignbyte": 1, "key3_selectors": 2, "lut8": 3, "lut16": 4, "v
 def lib():
     if not os.path.exists(PATH):
         raise ImportError(f"{PATH} missing; build with python quantized_decode_attention_tq_amd/build.py")
+    import torch  # noqa: F401  (load torch's HIP runtime first, so the probe library shares it)
+
     L = ctypes.CDLL(PATH)
     vp = ctypes.c_void_p
     for name, args in (("tq_probe_bits_host", [ctypes.c_int, vp, vp, ctypes.c_int]),
@@ -24,6 +26,7 @@ def lib():
                        ("tq_probe_mfma_16x16x32_f16", [vp, vp, vp]),
                        ("tq_probe_mfma_16x16x16_f16", [vp, vp, vp]),
                        ("tq_probe_cvt_fp8_f16", [vp, vp, ctypes.c_int]),
+                       ("tq_probe_permlane_swap", [vp, vp]),
                        ("tq_probe_stream_read", [vp, ctypes.c_int64, vp, ctypes.c_int, vp]),
                        ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp])):
         f = getattr(L, name)

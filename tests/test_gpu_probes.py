@@ -92,3 +92,20 @@ def test_device_bits_match_host_model(op):
         inp[:, 0] = x.view(np.uint32)
     print(f"probe bits {op}", flush=True)
     np.testing.assert_array_equal(probe.bits_device(op, inp), probe.bits_host(op, inp))
+
+
+def test_permlane_swaps_pair_each_lane_with_its_partner():
+    """The decode kernel's quarter reductions rely on permlane16_swap(v, v)
+    leaving lane l holding {v[l], v[l ^ 16]} across its two results, and
+    permlane32_swap(v, v) holding {v[l], v[l ^ 32]}."""
+    import torch
+
+    v = np.arange(64, dtype=np.uint32) * 7 + 1000
+    din = torch.from_numpy(v.view(np.int32)).cuda()
+    dout = torch.zeros(256, dtype=torch.int32, device="cuda")
+    print("probe permlane swaps", flush=True)
+    assert probe.lib().tq_probe_permlane_swap(din.data_ptr(), dout.data_ptr()) == 0
+    out = dout.cpu().numpy().view(np.uint32).reshape(4, 64)
+    for l in range(64):
+        assert {int(out[0, l]), int(out[1, l])} == {int(v[l]), int(v[l ^ 16])}, l
+        assert {int(out[2, l]), int(out[3, l])} == {int(v[l]), int(v[l ^ 32])}, l
