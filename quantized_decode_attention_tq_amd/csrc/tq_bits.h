@@ -3,7 +3,8 @@
 //
 // Everything here is plain integer/float code that also compiles for the
 // host, where the two AMDGPU byte-permute instructions are emulated, so the
-// unpacking logic is unit-tested on the CPU (csrc/tests/test_bits.cpp).
+// unpacking logic is unit-tested on the CPU against the oracle's packing
+// (through the host build of the probe library, csrc/tests/tq_probe.hip).
 #pragma once
 
 #include <cmath>
@@ -145,35 +146,50 @@ TQ_HD int key4_dim(int c, int e) { return 8 * c + (e < 4 ? 2 * e : 2 * (e - 4) +
 
 // 4-bit: wa, wb = the dword of dims 8r..8r+7 of tokens a and b.  out[n]
 // (n = 0..7) = dim 8r+n of (a, b); code at bit position (n & 1) * 4.
+// The unpack is split into a per-pair step (interleave the two tokens'
+// bytes: val4_pre / val3_pre) and a one-mask step per output
+// (val4_get / val3_get), so a caller can keep only the interleaved words
+// and produce each output when it is consumed.
+struct Val4Pre {
+  uint32_t w[4];  // p0, q0 = p0 >> 8, p1, q1 = p1 >> 8
+};
+TQ_HD Val4Pre val4_pre(uint32_t wa, uint32_t wb) {
+  Val4Pre r;
+  r.w[0] = perm32(wb, wa, 0x05040100u);  // bits 0..15 of a | bits 0..15 of b
+  r.w[2] = perm32(wb, wa, 0x07060302u);  // bits 16..31
+  r.w[1] = r.w[0] >> 8;
+  r.w[3] = r.w[2] >> 8;
+  return r;
+}
+TQ_HD uint32_t val4_get(const Val4Pre& r, int n) { return r.w[n >> 1] & ((n & 1) ? 0x00F000F0u : 0x000F000Fu); }
+
 TQ_HD void val4_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
-  uint32_t p0 = perm32(wb, wa, 0x05040100u);  // bits 0..15 of a | bits 0..15 of b
-  uint32_t p1 = perm32(wb, wa, 0x07060302u);  // bits 16..31
-  uint32_t q0 = p0 >> 8, q1 = p1 >> 8;
-  out[0] = p0 & 0x000F000Fu;
-  out[1] = p0 & 0x00F000F0u;
-  out[2] = q0 & 0x000F000Fu;
-  out[3] = q0 & 0x00F000F0u;
-  out[4] = p1 & 0x000F000Fu;
-  out[5] = p1 & 0x00F000F0u;
-  out[6] = q1 & 0x000F000Fu;
-  out[7] = q1 & 0x00F000F0u;
+  const Val4Pre r = val4_pre(wa, wb);
+  for (int n = 0; n < 8; ++n) out[n] = val4_get(r, n);
 }
 TQ_HD int val4_pos(int n) { return (n & 1) * 4; }
 
 // 3-bit: wa, wb = 24 bits (bytes 0..2) = dims 8r..8r+7, code m at bits 3m.
 // out[m] = dim 8r+m of (a, b); code at bit position val3_pos(m).
+struct Val3Pre {
+  uint32_t w[3];  // word bits 0..15, 8..23, 16..23 of a | the same of b
+};
+TQ_HD Val3Pre val3_pre(uint32_t wa, uint32_t wb) {
+  Val3Pre r;
+  r.w[0] = perm32(wb, wa, 0x05040100u);
+  r.w[1] = perm32(wb, wa, 0x06050201u);
+  r.w[2] = perm32(wb, wa, 0x0C060C02u);
+  return r;
+}
+TQ_HD uint32_t val3_get(const Val3Pre& r, int m) {
+  constexpr uint32_t kMask[8] = {0x00070007u, 0x00380038u, 0x01C001C0u, 0x000E000Eu,
+                                 0x00700070u, 0x03800380u, 0x001C001Cu, 0x00E000E0u};
+  return r.w[m < 3 ? 0 : (m < 6 ? 1 : 2)] & kMask[m];
+}
+
 TQ_HD void val3_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
-  uint32_t p0 = perm32(wb, wa, 0x05040100u);  // word bits 0..15
-  uint32_t p1 = perm32(wb, wa, 0x06050201u);  // word bits 8..23
-  uint32_t p2 = perm32(wb, wa, 0x0C060C02u);  // word bits 16..23
-  out[0] = p0 & 0x00070007u;
-  out[1] = p0 & 0x00380038u;
-  out[2] = p0 & 0x01C001C0u;
-  out[3] = p1 & 0x000E000Eu;
-  out[4] = p1 & 0x00700070u;
-  out[5] = p1 & 0x03800380u;
-  out[6] = p2 & 0x001C001Cu;
-  out[7] = p2 & 0x00E000E0u;
+  const Val3Pre r = val3_pre(wa, wb);
+  for (int m = 0; m < 8; ++m) out[m] = val3_get(r, m);
 }
 // code m starts at bit 3m of the word and its window starts at bit 8*floor(3m/8)
 TQ_HD int val3_pos(int m) { return (3 * m) & 7; }

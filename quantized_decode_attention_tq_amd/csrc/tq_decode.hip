@@ -24,7 +24,6 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -37,6 +36,7 @@ namespace {
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kRow = kD + static_cast<int>(tq::kPartPad);  // floats per partial row
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -84,8 +84,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const float* signs;
   const float* centroids;
-  float* part_o;    // [B][Hq][S][D] normalized partial outputs
-  float* part_lse;  // [B][Hq][S] natural-log LSE of each split
+  int32_t* table;   // [B][2]: first unit, number of units of each sequence
+  float* part;      // [U][Hq][kRow]: normalized partial output, then natural-log LSE
   float qscale;     // softmax scale * log2(e)
   int32_t q_bf16;
   int32_t num_q_heads, num_kv_heads, group, head_groups;
@@ -94,7 +94,8 @@ struct DecodeArgs {
   int32_t ring_depth;  // super-tiles (P tiles each) in the LDS ring
   int32_t spt;         // 1 KB direct-to-LDS slots per tile image
   int32_t contiguous;  // G == Hk: a tile of the group is one run of 16 token rows
-  int32_t block_size, bt_stride, num_splits;
+  int32_t block_size, bt_stride;
+  int32_t batch, num_units;  // B, U
 };
 
 __device__ __forceinline__ float widen16(uint32_t bits, bool bf16) {
@@ -283,22 +284,38 @@ struct Softmax {
 // rescaled; p * value_scale must also stay inside fp16.
 constexpr float kLazyRescaleLog2 = 8.0f;
 
-// valid: tokens of the tile before the sequence end (1..16).
+// A scored tile waiting for its value accumulation: value accumulation runs
+// on 16x16x32 MFMAs over two tiles at once (32 tokens on the reduction
+// axis), so the first tile of a pair is held here until the second is
+// scored.
+struct PendingTile {
+  uint32_t vw[4];  // value-code words of tokens 4q .. 4q+3 (dims of lane row)
+  half4 pv;        // p * value_scale of those tokens, fp16
+};
+
+// Score one tile and update the online softmax.  valid: tokens of the tile
+// before the sequence end (1..16).  On return `cur` holds the tile's value
+// words and weights; if the running maximum moved, the accumulators and the
+// pending tile (when `have_pend`) are rescaled to it.
 template <int P>
-__device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
-                                          const tq::Lut8& lb, const half8 bq[4], int valid, Softmax& sm,
-                                          f32x4 acc[8]) {
+__device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
+                                           const tq::Lut8& lb, const half8 bq[4], int valid, Softmax& sm,
+                                           f32x4 acc[8], PendingTile& pend, bool have_pend, PendingTile& cur) {
   using T = Preset<P>;
   half8 A[4];
   key_operand<P>(r, o.ksh, la, lb, A);
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], bq[c], sc, 0, 0, 0);
+  // two independent accumulation chains halve the dependent-MFMA latency
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], s1, 0, 0, 0);
 
   float sco[4], sv[4], zv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sco[i] = T::kFp8 ? sc[i] : sc[i] * half_bits_to_f32(r.gm[i]);
+    const float sc = s0[i] + s1[i];
+    sco[i] = T::kFp8 ? sc : sc * half_bits_to_f32(r.gm[i]);
     sv[i] = half_bits_to_f32(r.sz[i] & 0xFFFFu);
     zv[i] = half_bits_to_f32(r.sz[i] >> 16);
   }
@@ -327,13 +344,17 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
     }
     redo = __any(pmax > 65504.f);
   }
-  if (redo) {  // rescale the accumulators to the new maximum
+  if (redo) {  // rescale the accumulators (and the pending tile) to the new maximum
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] *= alpha;
     sm.l *= alpha;
     sm.z *= alpha;
     sm.m = m_cand;
+    if (have_pend) {
+      const _Float16 ah = static_cast<_Float16>(alpha);
+      pend.pv = pend.pv * ah;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
@@ -347,27 +368,41 @@ __device__ __forceinline__ void tile_step(const TileRegs<P>& r, const LaneOff<P>
   }
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
-  const half4 pv = as_half4(h2_bits(ps01), h2_bits(ps23));
-
-  uint32_t vw[4];
+  cur.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4)
-      vw[i] = r.v[i][0];
+      cur.vw[i] = r.v[i][0];
     else
-      vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (o.mo[i] + o.vcol) & 3u);
+      cur.vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (o.mo[i] + o.vcol) & 3u);
   }
-  uint32_t v01[8], v23[8];
-  if (T::kVb == 4) {
-    tq::val4_pairs(vw[0], vw[1], v01);
-    tq::val4_pairs(vw[2], vw[3], v23);
-  } else {
-    tq::val3_pairs(vw[0], vw[1], v01);
-    tq::val3_pairs(vw[2], vw[3], v23);
-  }
+}
+
+// O^T += V^T P^T over two scored tiles: 8 MFMA 16x16x32 f16, one per block
+// of 16 dims; reduction index k = 8q + j holds token 4q + j of tile `a`
+// (j < 4) or token 4q + j - 4 of tile `b`.
+template <int P>
+__device__ __forceinline__ void accumulate_pair(const PendingTile& a, const PendingTile& b, f32x4 acc[8]) {
+  using T = Preset<P>;
+  u32x2a4 pa = __builtin_bit_cast(u32x2a4, a.pv), pb = __builtin_bit_cast(u32x2a4, b.pv);
+  const half8 bp = as_half8(pa.x, pa.y, pb.x, pb.y);
+  if constexpr (T::kVb == 4) {
+    const tq::Val4Pre a01 = tq::val4_pre(a.vw[0], a.vw[1]), a23 = tq::val4_pre(a.vw[2], a.vw[3]);
+    const tq::Val4Pre b01 = tq::val4_pre(b.vw[0], b.vw[1]), b23 = tq::val4_pre(b.vw[2], b.vw[3]);
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
-    acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(v01[n], v23[n]), pv, acc[n], 0, 0, 0);
+    for (int n = 0; n < 8; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          as_half8(tq::val4_get(a01, n), tq::val4_get(a23, n), tq::val4_get(b01, n), tq::val4_get(b23, n)), bp,
+          acc[n], 0, 0, 0);
+  } else {
+    const tq::Val3Pre a01 = tq::val3_pre(a.vw[0], a.vw[1]), a23 = tq::val3_pre(a.vw[2], a.vw[3]);
+    const tq::Val3Pre b01 = tq::val3_pre(b.vw[0], b.vw[1]), b23 = tq::val3_pre(b.vw[2], b.vw[3]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          as_half8(tq::val3_get(a01, n), tq::val3_get(a23, n), tq::val3_get(b01, n), tq::val3_get(b23, n)), bp,
+          acc[n], 0, 0, 0);
+  }
 }
 
 // ---- tile staging: cache rows -> LDS ring by direct-to-LDS loads ----
@@ -400,8 +435,9 @@ struct Ring {
 // m0 is a reserved register the compiler cannot be told about: the stage-1
 // kernels use m0 for nothing else (checked in their ISA), so setting it here
 // disturbs no compiler-managed state.
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(m0) : "memory");
+// Addressing: uniform 64-bit base in SGPRs + this lane's 32-bit byte offset.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(m0) : "memory");
 }
 
 // Wait until at most n vector-memory loads of this wave are outstanding
@@ -512,9 +548,100 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
   }
 }
 
-// Stage 1.  A workgroup owns (sequence b, split s, group of G KV heads, up
-// to 16 query heads per KV head) and runs W = G * P waves: wave w serves KV
-// head w % G of the group in tile phase w / G.  The split's tiles are staged
+// ---- length-balanced units ----
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+struct UnitRange {
+  int b;                 // sequence of the unit, -1 if the unit is idle
+  int t_begin, t_end;    // its tiles [t_begin, t_end) of sequence b
+  int first_u, count_u;  // units of sequence u (the table entry unit u writes; 0, 0 if u >= batch)
+};
+
+// Every sequence b with tiles_b = ceil(L_b / 16) > 0 gets S_b = ceil(tiles_b
+// / tau) units, tau the smallest tile budget with sum_b S_b <= U; its units
+// are consecutive and split its tiles evenly (ceil(tiles_b / S_b) each).
+// Deterministic, so every workgroup derives the same assignment from
+// seq_lens alone; uniform lengths give each sequence U / batch equal units.
+__device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_lens, int B, int U, int u) {
+  const int lane = threadIdx.x & 63;
+  auto tiles = [&](int bb) { return bb < B ? (seq_lens[bb] + 15) >> 4 : 0; };
+  int T = 0, tmx = 0;
+  for (int bb = lane; bb < B; bb += 64) {
+    const int t = tiles(bb);
+    T += t;
+    tmx = max(tmx, t);
+  }
+  T = wave_sum_i(T);
+  tmx = wave_max_i(tmx);
+  int tau = 1;
+  if (T > 0) {
+    auto units_for = [&](int tt) {
+      int c = 0;
+      for (int bb = lane; bb < B; bb += 64) c += (tiles(bb) + tt - 1) / tt;
+      return wave_sum_i(c);
+    };
+    int lo = max(1, (T + U - 1) / U), hi = max(lo, tmx);  // units_for(tmx) <= B <= U
+    if (units_for(lo) > U) {
+      ++lo;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (units_for(mid) <= U)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+    }
+    tau = lo;
+  }
+  UnitRange r{-1, 0, 0, 0, 0};
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int t = tiles(b0 + lane);
+    const int sb = (t + tau - 1) / tau;
+    const int incl = wave_incl_scan_i(sb);
+    const int total = __shfl(incl, 63, 64);
+    if (u >= b0 && u < b0 + 64) {  // table entry of sequence u
+      r.first_u = base + __shfl(incl - sb, u - b0, 64);
+      r.count_u = __shfl(sb, u - b0, 64);
+    }
+    if (r.b < 0 && u < base + total) {
+      const uint64_t m = __ballot(base + incl > u);
+      const int L = __builtin_ctzll(m);
+      const int first = base + __shfl(incl - sb, L, 64);
+      const int nsb = __shfl(sb, L, 64);
+      const int tb = __shfl(t, L, 64);
+      const int chunk = (tb + nsb - 1) / nsb;
+      r.b = b0 + L;
+      r.t_begin = min((u - first) * chunk, tb);
+      r.t_end = min(r.t_begin + chunk, tb);
+    }
+    base += total;
+  }
+  return r;
+}
+
+// Stage 1.  A workgroup owns (unit u: a tile range of one sequence, group of
+// G KV heads, up to 16 query heads per KV head) and runs W = G * P waves:
+// wave w serves KV head w % G of the group in tile phase w / G.  The range's tiles are staged
 // into an LDS ring one super-tile (P consecutive tiles) at a time by the
 // whole workgroup, R-1 super-tiles ahead; the phase-p wave of a head scores
 // and accumulates tile p of every super-tile from LDS.  At the end the P
@@ -529,31 +656,41 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.G, NP = a.P;
   const int hh = w % G, ph = w / G;
-  const int S = a.num_splits, Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
+  const int Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
   int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int hgp = lg % (Hk / G);
   lg /= Hk / G;
   const int hg = lg % a.head_groups;
-  lg /= a.head_groups;
-  const int s = lg % S;
-  const int b = lg / S;
+  const int u = lg / a.head_groups;  // unit
   const int hk = hgp * G + hh;
+  const int hl = lane & 15, q4 = lane >> 4;
 
+  // ---- unit -> (sequence, tile range): length-balanced split ----
+  UnitRange ur = find_unit(a.seq_lens, a.batch, a.num_units, u);
+  // uniform by construction (cross-lane results): tell the compiler
+  ur.b = __builtin_amdgcn_readfirstlane(ur.b);
+  ur.t_begin = __builtin_amdgcn_readfirstlane(ur.t_begin);
+  ur.t_end = __builtin_amdgcn_readfirstlane(ur.t_end);
+  ur.first_u = __builtin_amdgcn_readfirstlane(ur.first_u);
+  ur.count_u = __builtin_amdgcn_readfirstlane(ur.count_u);
+  if (u < a.batch && hgp == 0 && hg == 0 && w == 0 && lane == 0) {  // table entry of sequence u
+    a.table[2 * u] = ur.first_u;
+    a.table[2 * u + 1] = ur.count_u;
+  }
+  if (ur.b < 0) return;  // idle unit (uniform over the workgroup)
+  const int b = ur.b;
   const int seqlen = a.seq_lens[b];
-  const int ntiles = (seqlen + 15) >> 4;
-  const int tps = (ntiles + S - 1) / S;
-  const int t_begin = s * tps;
-  const int t_end = min(t_begin + tps, ntiles);
+  const int t_begin = ur.t_begin;
+  const int t_end = ur.t_end;
   const int h0 = hg * 16;
   const int geff = min(16, g - h0);
-  const int hl = lane & 15, q4 = lane >> 4;
-  const int64_t prow0 = (static_cast<int64_t>(b) * Hq + hk * g + h0) * S + s;  // partial row of query head h0
-  auto prow = [&](int j) { return prow0 + static_cast<int64_t>(j) * S; };
+  const int64_t prow0 = static_cast<int64_t>(u) * Hq + hk * g + h0;  // partial row of query head h0
+  auto prow = [&](int j) { return prow0 + j; };
 
-  if (t_begin >= t_end) {  // empty split: zero partial, lse = -inf
+  if (t_begin >= t_end) {  // empty range: zero partial, lse = -inf
     if (ph == 0) {
-      for (int idx = lane; idx < geff * kD; idx += 64) a.part_o[prow(idx >> 7) * kD + (idx & (kD - 1))] = 0.f;
-      if (lane < geff) a.part_lse[prow(lane)] = -INFINITY;
+      for (int idx = lane; idx < geff * kD; idx += 64) a.part[prow(idx >> 7) * kRow + (idx & (kD - 1))] = 0.f;
+      if (lane < geff) a.part[prow(lane) * kRow + kD] = -INFINITY;
     }
     return;
   }
@@ -629,7 +766,7 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
     const uint32_t e0 = ring.lds_base + static_cast<uint32_t>(entry) * ring.entry;
 #pragma unroll
     for (int k = 0; k < 5; ++k)
-      if (k < ring.my_loads) dma16(base + ring.off[k], e0 + ring.dst[k]);
+      if (k < ring.my_loads) dma16(base, ring.off[k], e0 + ring.dst[k]);
   };
   const int nst = (t_end - t_begin + NP - 1) / NP;
   const int pre = min(R - 1, nst);
@@ -667,6 +804,8 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   f32x4 acc[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  PendingTile pend;
+  bool have_pend = false;
 
   // ---- main loop: wait for super-tile u, release the entry of u-1, refill
   // it with u+R-1, compute this wave's tile of u from LDS ----
@@ -683,9 +822,25 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
       TileRegs<P> r;
       const uint8_t* img = tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * spt) * 1024u;
       load_tile<P>(img, off, r);
-      tile_step<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc);
+      PendingTile cur;
+      score_tile<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
+      if (have_pend) {
+        accumulate_pair<P>(pend, cur, acc);
+        have_pend = false;
+      } else {
+        pend = cur;
+        have_pend = true;
+      }
     }
     entry = entry + 1 == R ? 0 : entry + 1;
+  }
+
+  if (have_pend) {  // an odd tile out: pair it with an empty one
+    PendingTile none;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) none.vw[i] = 0u;
+    none.pv = half4{0, 0, 0, 0};
+    accumulate_pair<P>(pend, none, acc);
   }
 
   // ---- this wave's normalized partial (output / l, base-2 LSE) ----
@@ -739,13 +894,13 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
 
   // ---- the split's partial rows: output and natural-log LSE ----
   if (ph == 0 && hl < geff) {
-    float* orow = a.part_o + prow(hl) * kD + 32 * q4;
+    float* orow = a.part + prow(hl) * kRow + 32 * q4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{o[8 * i], o[8 * i + 1], o[8 * i + 2], o[8 * i + 3]};
       *reinterpret_cast<f32x4*>(orow + 8 * i + 4) = f32x4{o[8 * i + 4], o[8 * i + 5], o[8 * i + 6], o[8 * i + 7]};
     }
-    if (q4 == 0) a.part_lse[prow(hl)] = lse2 * kLn2;
+    if (q4 == 0) a.part[prow(hl) * kRow + kD] = lse2 * kLn2;
   }
 }
 
@@ -759,28 +914,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // One wave per (sequence, query head): weights exp(lse_s - max), output =
-// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s).  Lane s holds the
-// weight of split s (64 splits per pass); the partial rows are read eight
-// splits at a time so their loads overlap.
-__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __restrict__ part_o,
-                                                               const float* __restrict__ part_lse, int rows, int S,
+// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s), over the sequence's
+// units (the table stage 1 writes).  Lane s holds the weight of unit s (64
+// per pass); the partial rows are read eight at a time so their loads
+// overlap.
+__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
+                                                               const float* __restrict__ part, int Hq, int rows,
                                                                void* out, int out_dtype, float* lse_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const float* ob_in = part_o + static_cast<int64_t>(row) * S * kD + 2 * lane;
-  const float* lb_in = part_lse + static_cast<int64_t>(row) * S;
+  const int b = row / Hq, hq = row - b * Hq;
+  const int first = table[2 * b], n = table[2 * b + 1];
+  const float* base = part + (static_cast<int64_t>(first) * Hq + hq) * kRow;
+  const int64_t stride = static_cast<int64_t>(Hq) * kRow;  // between consecutive units
+  auto lse_of = [&](int s) { return base[s * stride + kD]; };
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lb_in[s]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse_of(s));
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float o0 = 0.f, o1 = 0.f, den = 0.f, lse = -INFINITY;
   if (M != -INFINITY) {
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const int ns = min(64, S - s0);
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int ns = min(64, n - s0);
       float wl = 0.f;
       if (lane < ns) {
-        const float ls = lb_in[s0 + lane];
+        const float ls = lse_of(s0 + lane);
         wl = ls == -INFINITY ? 0.f : expf(ls - M);
       }
       den += wl;
@@ -788,17 +947,17 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __re
       for (; j + 8 <= ns; j += 8) {
         float2 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s0 + j + u) * kD);
+        for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const float2*>(base + (s0 + j + q) * stride + 2 * lane);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
-          o0 = fmaf(wu, v[u].x, o0);
-          o1 = fmaf(wu, v[u].y, o1);
+        for (int q = 0; q < 8; ++q) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + q));
+          o0 = fmaf(wu, v[q].x, o0);
+          o1 = fmaf(wu, v[q].y, o1);
         }
       }
       for (; j < ns; ++j) {
         const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
-        const float2 v = *reinterpret_cast<const float2*>(ob_in + static_cast<int64_t>(s0 + j) * kD);
+        const float2 v = *reinterpret_cast<const float2*>(base + (s0 + j) * stride + 2 * lane);
         o0 = fmaf(wu, v.x, o0);
         o1 = fmaf(wu, v.y, o1);
       }
@@ -822,18 +981,6 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const float* __re
 }
 
 constexpr int kMaxLds = 160 * 1024;
-
-// Compute units of the current device (cached per device; 256 on MI355X).
-int num_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 template <int P>
 int launch_stage1(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
@@ -862,9 +1009,8 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.seq_lens = seq_lens;
   a.signs = signs;
   a.centroids = centroids;
-  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * num_kv_splits;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + rows * kD;
+  a.table = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tq::table_bytes(batch));
   a.qscale = scale * kLog2e;
   a.q_bf16 = q_dtype == TQ_BF16;
   a.num_q_heads = num_q_heads;
@@ -873,10 +1019,12 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.head_groups = (a.group + 15) / 16;
   a.block_size = block_size;
   a.bt_stride = block_table_stride;
-  a.num_splits = num_kv_splits;
+  a.batch = batch;
   tq::DecodePlan plan;
-  const int st = tq::decode_plan(layout, batch, num_q_heads, num_kv_heads, num_kv_splits, num_cus(), &plan);
+  const int64_t max_tiles = (static_cast<int64_t>(block_table_stride) * block_size + 15) / 16;
+  const int st = tq::decode_plan(layout, batch, num_q_heads, num_kv_heads, num_kv_splits, max_tiles, &plan);
   if (st != TQ_OK) return st;
+  a.num_units = static_cast<int32_t>(plan.units);
   a.G = plan.G;
   a.P = plan.P;
   a.ring_depth = plan.R;
@@ -893,13 +1041,13 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   return TQ_EPRESET;
 }
 
-int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const void* workspace, void* out,
-           int32_t out_dtype, float* lse_out, hipStream_t stream) {
-  const int rows = batch * num_q_heads;
-  const float* part_o = static_cast<const float*>(workspace);
-  const float* part_lse = part_o + static_cast<int64_t>(rows) * num_kv_splits * kD;
-  int S = num_kv_splits;
-  void* args[] = {&part_o, &part_lse, const_cast<int*>(&rows), &S, &out, &out_dtype, &lse_out};
+int stage2(int32_t batch, int32_t num_q_heads, const void* workspace, void* out, int32_t out_dtype, float* lse_out,
+           hipStream_t stream) {
+  int rows = batch * num_q_heads;
+  int Hq = num_q_heads;
+  const int32_t* table = static_cast<const int32_t*>(workspace);
+  const float* part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + tq::table_bytes(batch));
+  void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out};
   return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel),
                                         dim3((rows + 3) / 4), dim3(256), args, 0, stream));
 }
@@ -939,8 +1087,7 @@ extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head
   int st = tq::validate_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace, workspace_bytes, out,
                                out_dtype);
   if (st != TQ_OK || batch == 0) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out,
-                static_cast<hipStream_t>(stream));
+  return stage2(batch, num_q_heads, workspace, out, out_dtype, lse_out, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
@@ -958,5 +1105,5 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
   st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
               block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace, s);
   if (st != TQ_OK) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out, s);
+  return stage2(batch, num_q_heads, workspace, out, out_dtype, lse_out, s);
 }

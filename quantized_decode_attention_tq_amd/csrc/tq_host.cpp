@@ -267,7 +267,8 @@ extern "C" int tq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int
 namespace tq {
 
 size_t workspace_bytes(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t num_kv_splits) {
-  size_t b = static_cast<size_t>(batch) * num_q_heads * num_kv_splits * (head_dim + 1) * sizeof(float);
+  const size_t rows = static_cast<size_t>(batch) * num_q_heads * max_splits(batch, num_kv_splits);
+  const size_t b = static_cast<size_t>(table_bytes(batch)) + rows * (head_dim + kPartPad) * sizeof(float);
   return (b + 255) / 256 * 256;
 }
 

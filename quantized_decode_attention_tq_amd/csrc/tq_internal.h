@@ -17,7 +17,7 @@ inline bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 
 // true when *L equals what tq_layout_init produces for (L->preset, L->head_dim)
 bool layout_consistent(const tq_layout* L);
 
-// stage-1 partials (B, Hq, S, D+1) fp32, rounded up to 256 bytes
+// decode workspace: sequence table + partial rows (layout below), rounded up to 256 bytes
 size_t workspace_bytes(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t num_kv_splits);
 
 int validate_store(const tq_layout* L, const void* key, const void* value, int32_t in_dtype, int64_t num_tokens,
@@ -34,33 +34,70 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
 int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                     const void* workspace, size_t ws_bytes, const void* out, int32_t out_dtype);
 
+// ---- decode workspace and stage-1 launch plan ----
+//
+// Stage 1 cuts the batch into U "units" of work: the tiles (16 tokens) of
+// each sequence are split into S_b ranges so that every unit holds about the
+// same number of tiles (sum_b S_b <= U), whatever the mix of lengths.  U =
+// batch * S_int, where S_int >= the caller's num_kv_splits S is raised until
+// the grid has about kTargetWorkgroups workgroups (two per compute unit of an
+// MI355X).  The workspace holds
+//   [table]  int32 [batch][2] = (first unit, number of units) of each sequence
+//   [rows]   fp32 [U][Hq][kPartPad + head_dim]: the normalized partial output
+//            of a (unit, query head) followed by its natural-log LSE (padded
+//            to 16-byte rows).
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kPartPad = 4;  // LSE + 3 pad floats after the head_dim outputs
+
+inline int64_t table_bytes(int64_t batch) { return (8 * batch + 255) / 256 * 256; }
+
+// Largest S_int any launch with this (batch, S) uses (the plan's raise
+// assumes at least one workgroup per unit).
+inline int64_t max_splits(int64_t batch, int64_t num_splits) {
+  if (batch <= 0) return num_splits;
+  const int64_t per = batch * num_splits;
+  const int64_t m = (kTargetWorkgroups + per - 1) / per;
+  return num_splits * (m > 1 ? m : 1);
+}
+
 // Launch plan of decode stage 1 (host).  A workgroup serves G KV heads with
-// P waves each (G * P <= 8 waves).  G is the largest divisor of Hk (<= 8)
-// that still gives at least two workgroups per compute unit, else 1; the P
-// waves of a head split its tiles.  A tile image (16 token rows of the
-// group) takes spt 1 KB slots of LDS; the ring holds R super-tiles of P
-// tiles, sized for two workgroups per compute unit.
+// P waves each (G * P <= 8 waves).  G = Hk when Hk <= 8, so a tile of the
+// group is one contiguous run of cache rows; otherwise the largest divisor
+// of Hk (<= 8) whose row pieces stay 16-byte aligned.  The P waves of a head
+// split its tiles.  A tile image (16 token rows of the group) takes spt 1 KB
+// slots of LDS; the ring holds R super-tiles of P tiles, sized for two
+// workgroups per compute unit.  max_tiles: tiles of the longest possible
+// sequence (block-table width), which caps S_int.
 struct DecodePlan {
   int G, P, R, spt, contiguous;
-  size_t lds;    // dynamic LDS bytes per workgroup
-  int64_t grid;  // workgroups
+  size_t lds;      // dynamic LDS bytes per workgroup
+  int64_t units;   // U
+  int64_t grid;    // workgroups = U * (Hk / G) * head groups
 };
 
 inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t num_splits, int num_cus, DecodePlan* p) {
+                       int32_t num_splits, int64_t max_tiles, DecodePlan* p) {
   constexpr size_t kLdsBudget = 80 * 1024, kLdsMax = 160 * 1024;
   const int64_t slot = L->slot_size_aligned;
   const int64_t row = num_kv_heads * slot;
   const int group = num_q_heads / num_kv_heads;
-  const int64_t units = static_cast<int64_t>(batch) * num_splits * ((group + 15) / 16);
-  int G = 1;
-  for (int d = num_kv_heads < 8 ? num_kv_heads : 8; d >= 1; --d) {
-    if (num_kv_heads % d != 0) continue;
-    G = d;
-    if (units * (num_kv_heads / d) >= 2LL * num_cus) break;
+  const int64_t hgroups = (group + 15) / 16;
+  int G = 0;
+  if (num_kv_heads <= 8) {
+    G = num_kv_heads;
+  } else {
+    for (int d = 8; d >= 1 && G == 0; --d)
+      if (num_kv_heads % d == 0 && (d * slot) % 16 == 0 && row % 16 == 0) G = d;
+    for (int d = 8; d >= 1 && G == 0; --d)
+      if (num_kv_heads % d == 0) G = d;
   }
   const int P = G >= 8 ? 1 : 8 / G;
   const bool contiguous = G == num_kv_heads;
+  const int64_t wg_per_unit = (num_kv_heads / G) * hgroups;
+  const int64_t per = static_cast<int64_t>(batch) * num_splits * wg_per_unit;
+  int64_t s_int = num_splits * (per > 0 && per < kTargetWorkgroups ? (kTargetWorkgroups + per - 1) / per : 1);
+  const int64_t cap = (max_tiles + P - 1) / P;  // more units than P-tile steps per sequence are idle
+  if (s_int > num_splits && s_int > cap) s_int = cap > num_splits ? cap : num_splits;
   const int64_t piece = G * slot;
   const int64_t tc_max = contiguous ? row : 16 * ((piece + 30) / 16);  // chunks per tile image
   const int spt = static_cast<int>((tc_max + 63) / 64);
@@ -74,10 +111,13 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   p->spt = spt;
   p->contiguous = contiguous;
   p->lds = R * entry > merge ? R * entry : merge;
-  p->grid = units * (num_kv_heads / G);
+  p->units = static_cast<int64_t>(batch) * s_int;
+  p->grid = p->units * wg_per_unit;
   const int loads = (spt + G - 1) / G;  // DMA slots per wave per super-tile (its phase's tile)
-  const int64_t blk_bytes = 128 * row;   // largest block (block_size 128)
-  if (p->lds > kLdsMax || loads > 5 || p->grid > 0x7FFFFFFF || blk_bytes > 0xFFFFFFFFLL) return TQ_EUNSUPPORTED;
+  const int64_t blk_bytes = 128 * row;  // largest block (block_size 128)
+  if (p->lds > kLdsMax || loads > 5 || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
+      blk_bytes > 0xFFFFFFFFLL || s_int > max_splits(batch, num_splits))
+    return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
 

@@ -83,9 +83,16 @@ def test_wht_signs_match_oracle_splitmix64(seed):
 
 
 def test_workspace_bytes():
-    for B, Hq, S in ((1, 2, 1), (32, 32, 16), (4, 40, 32), (64, 64, 8)):
+    """At least the pages' (B, Hq, S, D+1) partial buffer; the library's own
+    layout is a (first unit, unit count) table per sequence, then 16-byte
+    partial rows (D outputs + LSE + pad) for up to S_max = S * max(1,
+    ceil(512 / (B * S))) units per sequence."""
+    for B, Hq, S in ((1, 2, 1), (32, 32, 16), (4, 40, 32), (64, 64, 8), (32, 32, 8), (3, 6, 5)):
         n = tq.decode_workspace_bytes(B, Hq, 128, S)
-        assert n >= O.workspace_bytes(B, Hq, 128, S) and n % 256 == 0 and n - O.workspace_bytes(B, Hq, 128, S) < 256
+        assert n >= O.workspace_bytes(B, Hq, 128, S) and n % 256 == 0
+        s_max = S * max(1, -(-512 // (B * S)))
+        want = -(-8 * B // 256) * 256 + B * Hq * s_max * (128 + 4) * 4
+        assert n == -(-want // 256) * 256, (B, Hq, S)
 
 
 # ------------------------------------------------------------ validation
