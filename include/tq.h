@@ -129,9 +129,17 @@ int tq_lloyd_max(int32_t d, int32_t bits, int32_t mode, float* centroids, float*
  * that policy. */
 int tq_wht_signs(int32_t d, uint64_t seed, float* signs);
 
-/* Bytes of device workspace tq_decode_attention needs: the stage-1 partials
- * (batch, num_q_heads, num_kv_splits, head_dim + 1) fp32 ([PR] attention.py
- * excerpt, the mid_o buffer; [API] _decode_attention), rounded up to 256. */
+/* Bytes of device workspace tq_decode_attention needs ([PR] attention.py
+ * excerpt, the mid_o buffer of stage-1 partials; [API] _decode_attention).
+ * Layout (library-private; callers treat it as scratch):
+ *   int32 [batch][2] table = (first work unit, number of work units) of each
+ *   sequence, padded to 256 bytes; then fp32 rows [U][num_q_heads][head_dim
+ *   + 4] = the normalized partial output of (unit, query head), its
+ *   natural-log LSE and 3 pad floats.  U = batch * S_max, S_max =
+ *   num_kv_splits * max(1, ceil(512 / (batch * num_kv_splits))).
+ * At least the pages' (batch, num_q_heads, num_kv_splits, head_dim + 1)
+ * fp32 buffer.  Rounded up to 256.  One workspace can serve every layer
+ * (calls on one stream run in order). */
 int tq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                               size_t* bytes);
 
@@ -185,9 +193,13 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *   seq_lens     device int32 [batch], each in [0, block_table_stride*block_size].
  *   signs, centroids  as for tq_store (MSE presets).
  *   scale        softmax scale (1/sqrt(head_dim) for standard attention).
- *   num_kv_splits S >= 1: each sequence's tokens are cut into S contiguous
- *                ranges (16-token granularity); fixed per call so the launch
- *                shape never depends on device data.
+ *   num_kv_splits S >= 1: the split-KV parallelism requested.  The library
+ *                launches batch * S_int work units (S <= S_int <= S_max,
+ *                raised so the grid has about 512 workgroups, capped by
+ *                block_table_stride) and gives each sequence a number of
+ *                units in proportion to its length, each a contiguous range
+ *                of 16-token tiles; the launch shape depends only on the
+ *                arguments, never on device data.
  *   workspace    device, >= tq_decode_workspace_bytes(batch, num_q_heads,
  *                head_dim, S) bytes, 16-byte aligned; contents are scratch.
  *   out          device [batch, num_q_heads, head_dim], dtype out_dtype
@@ -210,10 +222,11 @@ int tq_decode_validate(const tq_layout* layout, const void* query, int32_t q_dty
                        const void* workspace, size_t workspace_bytes, const void* out, int32_t out_dtype);
 
 /* The two launches of tq_decode_attention, exposed separately so that each
- * can be timed on its own.  Stage 1 writes the workspace partials
- * [b][hq][split] = (normalized partial output[head_dim], natural-log LSE);
- * stage 2 merges them into out / lse_out.  Same arguments and checks as
- * tq_decode_attention. */
+ * can be timed on its own.  Stage 1 writes the workspace table and the
+ * partial rows of every work unit; stage 2 merges each sequence's units into
+ * out / lse_out.  Same arguments and checks as tq_decode_attention; stage 2
+ * must run on a workspace written by stage 1 with the same batch and
+ * num_q_heads. */
 int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                      int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                      const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,

@@ -98,6 +98,20 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in,
     out[i] = in[i];
 }
 
+// FP8 E4M3 encodes of fp32 inputs: out[3i] = the software encoder
+// (tq::f32_to_e4m3), out[3i+1] = v_cvt_pk_fp8_f32, out[3i+2] =
+// v_cvt_scalef32_pk_fp8_f32 with scale 1 (low byte of each).
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+__global__ void fp8enc_kernel(const uint32_t* in, uint32_t* out, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float x = __uint_as_float(in[i]);
+    out[3 * i] = tq::f32_to_e4m3(x);
+    out[3 * i + 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFFu;
+    const v2i16 old = {0, 0};
+    out[3 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, x, x, 1.0f, false)) & 0xFFu;
+  }
+}
+
 // one wave64: out[0..63], out[64..127] = the two results of permlane16_swap
 // (v, v); out[128..191], out[192..255] = those of permlane32_swap (v, v)
 __global__ void permlane_kernel(const uint32_t* in, uint32_t* out) {
@@ -148,6 +162,13 @@ int tq_probe_mfma_16x16x16_f16(const uint32_t* a, const uint32_t* b, float* d) {
 // one wave64: in device [64] dwords, out device [256] dwords
 int tq_probe_permlane_swap(const uint32_t* in, uint32_t* out) {
   hipLaunchKernelGGL(permlane_kernel, dim3(1), dim3(64), 0, 0, in, out);
+  return finish();
+}
+
+// in: device [n] fp32 bits; out: device [3n] (software, cvt_pk, cvt_scalef32)
+int tq_probe_fp8_encode(const uint32_t* in, uint32_t* out, int n) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(fp8enc_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, 0, in, out, n);
   return finish();
 }
 

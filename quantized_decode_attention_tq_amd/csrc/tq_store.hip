@@ -25,6 +25,7 @@ constexpr int kRowsPerWave = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
+constexpr int kMaxSlot = 208;  // >= every preset's slot at head_dim 128, 16-byte multiple
 
 struct StoreArgs {
   const uint16_t* key;
@@ -47,7 +48,21 @@ __device__ __forceinline__ float widen16(uint32_t bits, bool bf16) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
 }
 
-__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
+// Value of lane (l ^ m) for m = 1, 2, 4 (within each 8-lane row group), by
+// DPP lane moves: no LDS round trip.  xor 1 / xor 2 are quad permutes; xor 4
+// is the quad reversal (l ^ 3) followed by the half-row mirror (l ^ 7).
+__device__ __forceinline__ float xor_shfl(float v, int m) {
+  int x = __float_as_int(v);
+  if (m == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if (m == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else {
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);   // quad_perm [3, 2, 1, 0]
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  }
+  return __int_as_float(x);
+}
 
 __device__ __forceinline__ void load_row16(const uint16_t* p, bool bf16, float x[kDpl]) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -105,8 +120,25 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   uint32_t kbytes[kDpl / 2] = {};  // lane's key bytes, little-endian, packed 4 per dword
   uint32_t gamma_bits = 0;
   if (KEY_FP8) {
+    // Hardware convert (round to nearest even) after clamping to the E4M3
+    // range, which gives the saturating encoder's bytes for every non-NaN
+    // input; a wave holding a NaN key takes the software encoder.
+    bool has_nan = false;
 #pragma unroll
-    for (int i = 0; i < kDpl; ++i) kbytes[i / 4] |= tq::f32_to_e4m3(x[i]) << (8 * (i % 4));
+    for (int i = 0; i < kDpl; ++i) has_nan |= __builtin_isnan(x[i]);
+    if (__any(has_nan)) {
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) kbytes[i / 4] |= tq::f32_to_e4m3(x[i]) << (8 * (i % 4));
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDpl / 4; ++j) {
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x[4 * j], -448.f, 448.f),
+                                                     __builtin_amdgcn_fmed3f(x[4 * j + 1], -448.f, 448.f), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x[4 * j + 2], -448.f, 448.f),
+                                            __builtin_amdgcn_fmed3f(x[4 * j + 3], -448.f, 448.f), w, true);
+        kbytes[j] = w;
+      }
+    }
   } else {
     float ss = 0.f;
 #pragma unroll
@@ -204,13 +236,38 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   constexpr int kValBytesPerLane = (kDpl * VB) / 8;
 
   // ---------------- stores ----------------
-  if (write) {
+  const int kdata = KEY_FP8 ? kD : (kD * KB) / 8;
+  const int kps = KEY_FP8 ? kD : kdata + 2;
+  const int vdata = (kD * VB) / 8;
+  if (a.num_kv_heads % kRowsPerWave == 0) {
+    // The wave's 8 rows are 8 consecutive heads of one token: 8 adjacent
+    // slots, 16-byte aligned.  Assemble them in LDS, then write them with
+    // 16-byte stores.
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][kRowsPerWave * kMaxSlot];
+    uint8_t* sl = stage[wave] + (lane >> 3) * a.slot_bytes;
+    uint8_t* kp = sl + sub * kKeyBytesPerLane;
+#pragma unroll
+    for (int i = 0; i < kKeyBytesPerLane / 2; ++i) st16(kp + 2 * i, kbytes[i / 2] >> (16 * (i % 2)));
+    if (!KEY_FP8 && sub == 0) st16(sl + kdata, gamma_bits);
+    uint8_t* vp = sl + kps + sub * kValBytesPerLane;
+#pragma unroll
+    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, static_cast<uint32_t>(vacc >> (16 * i)));
+    if (sub == 0) {
+      st16(sl + kps + vdata, __half_as_ushort(s16));
+      st16(sl + kps + vdata + 2, __half_as_ushort(z16));
+    }
+    __syncthreads();
+    // every row of the wave has the same token, activity and slot mapping
+    if (write) {
+      uint8_t* dst = slot - (lane >> 3) * static_cast<int64_t>(a.slot_bytes);  // slot of the wave's first head
+      const int nchunk = (kRowsPerWave * a.slot_bytes) >> 4;
+      for (int c = lane; c < nchunk; c += 64)
+        *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+    }
+  } else if (write) {
     uint8_t* kp = slot + sub * kKeyBytesPerLane;
 #pragma unroll
     for (int i = 0; i < kKeyBytesPerLane / 2; ++i) st16(kp + 2 * i, kbytes[i / 2] >> (16 * (i % 2)));
-    const int kdata = KEY_FP8 ? kD : (kD * KB) / 8;
-    const int kps = KEY_FP8 ? kD : kdata + 2;
-    const int vdata = (kD * VB) / 8;
     if (!KEY_FP8 && sub == 0) st16(slot + kdata, gamma_bits);
     uint8_t* vp = slot + kps + sub * kValBytesPerLane;
 #pragma unroll

@@ -109,3 +109,27 @@ def test_permlane_swaps_pair_each_lane_with_its_partner():
     for l in range(64):
         assert {int(out[0, l]), int(out[1, l])} == {int(v[l]), int(v[l ^ 16])}, l
         assert {int(out[2, l]), int(out[3, l])} == {int(v[l]), int(v[l ^ 32])}, l
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_hardware_fp8_encode_matches_software_encoder(kind):
+    """The store kernel encodes FP8 keys with the hardware convert after
+    clamping to [-448, 448] (NaN inputs take the software encoder): this pins
+    that the hardware gives the software encoder's bytes (RNE) for every
+    finite fp16 / bf16 input with |x| <= 448 -- above that it returns NaN
+    where the encoder saturates, which the clamp covers."""
+    import torch
+
+    bits = np.arange(65536, dtype=np.uint32)
+    x = O.widen(bits.astype(np.uint16), kind)
+    f32 = x.astype(np.float32).view(np.uint32)
+    din = torch.from_numpy(f32.view(np.int32)).cuda()
+    dout = torch.zeros(3 * 65536, dtype=torch.int32, device="cuda")
+    print(f"probe fp8 encode {kind}", flush=True)
+    assert probe.lib().tq_probe_fp8_encode(din.data_ptr(), dout.data_ptr(), 65536) == 0
+    out = dout.cpu().numpy().view(np.uint32).reshape(-1, 3)
+    sw = out[:, 0]
+    np.testing.assert_array_equal(sw, O.fp8_e4m3fn_encode(x))
+    inr = np.isfinite(x) & (np.abs(x) <= 448)
+    for col in (1, 2):
+        np.testing.assert_array_equal(out[inr, col], sw[inr])
