@@ -10,10 +10,11 @@ sequences x 4096 tokens, 32/8 heads, block 16).  ``value`` is the effective
 decode-attention bandwidth: compressed-cache bytes the step reads
 (sum_b L_b * Hk * slot_size) over the step's wall time, inputs resident in HBM.
 
-Timing: HIP graphs of the step are replayed on torch's current stream,
-rotating over 3 copies of the cache (3 x 411 MB for the headline) so that the
-256 MB Infinity Cache cannot serve the next step's reads; K steps are
-bracketed by events after a synchronize.  The roofline figure times stage-1
+Timing: the step is captured in a HIP graph three times in a row, once per
+copy of the cache (3 x 411 MB for the headline, so the 256 MB Infinity Cache
+cannot serve a step's reads from the previous one), the way a multi-layer
+decode graph strings layers together; the graph is replayed on torch's
+current stream and K steps are bracketed by events after a synchronize.  The roofline figure times stage-1
 launches alone with events on the same stream.  The CPU baseline is the
 oracle (NumPy) decoding a bounded sample of the same workload.
 
@@ -113,6 +114,9 @@ class DecodeBench:
         self.stage2()
 
     def graphs(self):
+        """One graph holding N_COPIES consecutive steps (one per cache copy),
+        like a stretch of a multi-layer decode graph, plus one-step graphs for
+        a remainder."""
         torch = self.torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -121,25 +125,32 @@ class DecodeBench:
                 self.step(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        gs = []
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for i in range(N_COPIES):
+                self.step(i)
+        singles = []
         for i in range(N_COPIES):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 self.step(i)
-            gs.append(g)
+            singles.append(g)
         torch.cuda.synchronize()
-        return gs
+        return g_all, singles
 
     def time_steps(self, steps, warmup):
+        """ms per step over exactly `steps` steps (graph replays)."""
         torch = self.torch
-        gs = self.graphs()
-        for i in range(warmup):
-            gs[i % N_COPIES].replay()
+        g_all, singles = self.graphs()
+        for _ in range(max(1, warmup // N_COPIES)):
+            g_all.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(steps):
-            gs[i % N_COPIES].replay()
+        for _ in range(steps // N_COPIES):
+            g_all.replay()
+        for i in range(steps % N_COPIES):
+            singles[i].replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps  # ms per step

@@ -320,7 +320,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
     zv[i] = half_bits_to_f32(r.sz[i] >> 16);
   }
   const int lane = threadIdx.x & 63;
-  if (valid < 16) {  // tail tile: tokens at or past the sequence end drop out
+  if (__builtin_expect(valid < 16, 0)) {  // tail tile: tokens at or past the sequence end drop out
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (4 * (lane >> 4) + i >= valid) {
@@ -330,10 +330,11 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
       }
     }
   }
-  const float tmax = quarter_max(fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3])));
-  const float m_cand = fmaxf(sm.m, tmax);
+  // The rescale test needs no cross-lane maximum: a head's maximum over its
+  // four lane quarters exceeds the threshold iff one of the lanes' does.
+  const float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
   float p[4], ps[4];
-  bool redo = __any(tmax > sm.m + kLazyRescaleLog2);
+  bool redo = __any(lmax > sm.m + kLazyRescaleLog2);
   if (!redo) {
     float pmax = 0.f;
 #pragma unroll
@@ -345,6 +346,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
     redo = __any(pmax > 65504.f);
   }
   if (redo) {  // rescale the accumulators (and the pending tile) to the new maximum
+    const float m_cand = fmaxf(sm.m, quarter_max(lmax));
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] *= alpha;
@@ -913,60 +915,87 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// One wave per (sequence, query head): weights exp(lse_s - max), output =
-// sum_s w_s o_s / sum_s w_s, lse = max + log(sum_s w_s), over the sequence's
-// units (the table stage 1 writes).  Lane s holds the weight of unit s (64
-// per pass); the partial rows are read eight at a time so their loads
-// overlap.
+// One workgroup (4 waves) per (sequence, query head): output = sum_s w_s o_s
+// / sum_s w_s with w_s = exp(lse_s - max), lse = max + log(sum_s w_s), over
+// the sequence's units (the table stage 1 writes).  Latency-bound, so the
+// loads are issued together: wave w takes units w, w + 4, ...; after the
+// table read each lane fetches its 2 output dims of 16 of the wave's units
+// and lane j the LSE of the wave's j-th unit, all at once.  The 4 waves'
+// running (max, sum, output) are combined through LDS.
 __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
                                                                const float* __restrict__ part, int Hq, int rows,
                                                                void* out, int out_dtype, float* lse_out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  constexpr int kBatch = 16, kW = 4;
+  __shared__ float comb[kW - 1][2 * 64 + 2];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = row / Hq, hq = row - b * Hq;
   const int first = table[2 * b], n = table[2 * b + 1];
   const float* base = part + (static_cast<int64_t>(first) * Hq + hq) * kRow;
-  const int64_t stride = static_cast<int64_t>(Hq) * kRow;  // between consecutive units
-  auto lse_of = [&](int s) { return base[s * stride + kD]; };
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse_of(s));
+  const int64_t stride = static_cast<int64_t>(Hq) * kRow * kW;  // between this wave's consecutive units
+  base += static_cast<int64_t>(w) * Hq * kRow;
+  const int nw = n > w ? (n - w + kW - 1) / kW : 0;  // units of this wave
+  float M = -INFINITY, o0 = 0.f, o1 = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < nw; s0 += kBatch) {
+    const int ns = min(kBatch, nw - s0);
+    float2 v[kBatch];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  float o0 = 0.f, o1 = 0.f, den = 0.f, lse = -INFINITY;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n; s0 += 64) {
-      const int ns = min(64, n - s0);
-      float wl = 0.f;
-      if (lane < ns) {
-        const float ls = lse_of(s0 + lane);
-        wl = ls == -INFINITY ? 0.f : expf(ls - M);
-      }
-      den += wl;
-      int j = 0;
-      for (; j + 8 <= ns; j += 8) {
-        float2 v[8];
+    for (int q = 0; q < kBatch; ++q)
+      v[q] = q < ns ? *reinterpret_cast<const float2*>(base + (s0 + q) * stride + 2 * lane) : make_float2(0.f, 0.f);
+    const float ls = lane < ns ? base[(s0 + lane) * stride + kD] : -INFINITY;
+    float Mb = ls;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const float2*>(base + (s0 + j + q) * stride + 2 * lane);
+    for (int m = 8; m >= 1; m >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, m, 64));  // lanes 0..15 hold the batch
+    Mb = __shfl(Mb, 0, 64);
+    const float Mn = fmaxf(M, Mb);
+    if (Mn == -INFINITY) continue;  // nothing live yet
+    const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
+    o0 *= alpha;
+    o1 *= alpha;
+    den *= alpha;
+    M = Mn;
+    const float wl = ls == -INFINITY ? 0.f : expf(ls - M);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + q));
-          o0 = fmaf(wu, v[q].x, o0);
-          o1 = fmaf(wu, v[q].y, o1);
-        }
-      }
-      for (; j < ns; ++j) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
-        const float2 v = *reinterpret_cast<const float2*>(base + (s0 + j) * stride + 2 * lane);
-        o0 = fmaf(wu, v.x, o0);
-        o1 = fmaf(wu, v.y, o1);
-      }
+    for (int q = 0; q < kBatch; ++q) {
+      const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), q));
+      den += wq;
+      o0 = fmaf(wq, v[q].x, o0);
+      o1 = fmaf(wq, v[q].y, o1);
     }
+  }
+  if (w > 0) {
+    comb[w - 1][2 * lane] = o0;
+    comb[w - 1][2 * lane + 1] = o1;
+    if (lane == 0) {
+      comb[w - 1][128] = M;
+      comb[w - 1][129] = den;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float Mt = M;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
+  for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][128]);
+  float lse = -INFINITY;
+  if (Mt != -INFINITY) {
+    float a0 = M == -INFINITY ? 0.f : expf(M - Mt);
+    o0 *= a0;
+    o1 *= a0;
+    den *= a0;
+#pragma unroll
+    for (int k = 0; k < kW - 1; ++k) {
+      const float mk = comb[k][128];
+      if (mk == -INFINITY) continue;
+      const float ak = expf(mk - Mt);
+      den = fmaf(ak, comb[k][129], den);
+      o0 = fmaf(ak, comb[k][2 * lane], o0);
+      o1 = fmaf(ak, comb[k][2 * lane + 1], o1);
+    }
     o0 /= den;
     o1 /= den;
-    lse = M + logf(den);
+    lse = Mt + logf(den);
+  } else {
+    o0 = o1 = 0.f;
   }
   const int64_t ob = static_cast<int64_t>(row) * kD + 2 * lane;
   if (out_dtype == TQ_F32) {
@@ -1049,7 +1078,7 @@ int stage2(int32_t batch, int32_t num_q_heads, const void* workspace, void* out,
   const float* part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + tq::table_bytes(batch));
   void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out};
   return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel),
-                                        dim3((rows + 3) / 4), dim3(256), args, 0, stream));
+                                        dim3(rows), dim3(256), args, 0, stream));
 }
 
 }  // namespace

@@ -65,7 +65,8 @@ inline int64_t max_splits(int64_t batch, int64_t num_splits) {
 // group is one contiguous run of cache rows; otherwise the largest divisor
 // of Hk (<= 8) whose row pieces stay 16-byte aligned.  The P waves of a head
 // split its tiles.  A tile image (16 token rows of the group) takes spt 1 KB
-// slots of LDS; the ring holds R super-tiles of P tiles, sized for two
+// slots of LDS; the ring holds R super-tiles of P tiles (two-deep unless a
+// super-tile is small), sized for two
 // workgroups per compute unit.  max_tiles: tiles of the longest possible
 // sequence (block-table width), which caps S_int.
 struct DecodePlan {
@@ -77,7 +78,7 @@ struct DecodePlan {
 
 inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t num_splits, int64_t max_tiles, DecodePlan* p) {
-  constexpr size_t kLdsBudget = 80 * 1024, kLdsMax = 160 * 1024;
+  constexpr size_t kLdsBudget = 52 * 1024, kLdsMax = 160 * 1024;  // two-deep rings measured best
   const int64_t slot = L->slot_size_aligned;
   const int64_t row = num_kv_heads * slot;
   const int group = num_q_heads / num_kv_heads;
