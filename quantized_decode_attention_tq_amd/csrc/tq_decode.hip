@@ -649,7 +649,7 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // and accumulates tile p of every super-tile from LDS.  At the end the P
 // phase waves of a head merge their partial softmax states through LDS and
 // the phase-0 wave writes the split's partial rows.
-template <int P>
+template <int P, int TPW>
 __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
@@ -657,6 +657,7 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.G, NP = a.P;
+  const int Q = NP * TPW;  // tiles per super-tile
   const int hh = w % G, ph = w / G;
   const int Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
   int lg = xcd_remap(blockIdx.x, gridDim.x);
@@ -726,12 +727,12 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   const int spt = a.spt;
   Ring ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
-  ring.entry = static_cast<uint32_t>(NP * spt) * 1024u;
-  ring.my_loads = (spt - hh + G - 1) / G;
+  ring.entry = static_cast<uint32_t>(Q * spt) * 1024u;
+  ring.my_loads = (spt - hh + G - 1) / G;  // per tile
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     const int n = hh + k * G;  // slot of tile ph (n < spt for k < my_loads)
-    ring.dst[k] = static_cast<uint32_t>(ph * spt + n) * 1024u;
+    ring.dst[k] = static_cast<uint32_t>(ph * TPW * spt + n) * 1024u;  // in tile 0 of this wave's TPW
     uint32_t c = min(static_cast<uint32_t>(64 * n + lane), tc - 1);
     if (geo.contiguous) {
       ring.off[k] = 16 * c;
@@ -759,21 +760,33 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   // block id of this wave's tile of super-tile u; tiles past the split's end
   // stand in for its last tile (in bounds; loaded, never computed), so every
   // wave issues the same number of loads per super-tile
-  auto my_tile = [&](int u) { return min(t_begin + u * NP + ph, t_end - 1); };
+  auto my_tile = [&](int u, int j) { return min(t_begin + u * Q + ph * TPW + j, t_end - 1); };
   auto block_of = [&](int t) { return btab[(t * 16) >> bs_log2]; };
-  auto issue = [&](int u, int entry, int blk) {
-    const int t = my_tile(u);
-    const uint8_t* base = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk)) * blk_bytes32 +
-                          static_cast<uint32_t>((t * 16) & (a.block_size - 1)) * geo.row;
+  struct Blk {
+    int id[TPW];
+  };
+  auto blocks_of = [&](int u) {
+    Blk r;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) r.id[j] = block_of(my_tile(u, j));
+    return r;
+  };
+  auto issue = [&](int u, int entry, const Blk& blk) {
     const uint32_t e0 = ring.lds_base + static_cast<uint32_t>(entry) * ring.entry;
 #pragma unroll
-    for (int k = 0; k < 5; ++k)
-      if (k < ring.my_loads) dma16(base, ring.off[k], e0 + ring.dst[k]);
+    for (int j = 0; j < TPW; ++j) {
+      const int t = my_tile(u, j);
+      const uint8_t* base = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk.id[j])) * blk_bytes32 +
+                            static_cast<uint32_t>((t * 16) & (a.block_size - 1)) * geo.row;
+#pragma unroll
+      for (int k = 0; k < 5; ++k)
+        if (k < ring.my_loads) dma16(base, ring.off[k], e0 + ring.dst[k] + static_cast<uint32_t>(j * spt) * 1024u);
+    }
   };
-  const int nst = (t_end - t_begin + NP - 1) / NP;
+  const int nst = (t_end - t_begin + Q - 1) / Q;
   const int pre = min(R - 1, nst);
-  for (int d = 0; d < pre; ++d) issue(d, d, block_of(my_tile(d)));
-  int blk_next = block_of(my_tile(R - 1));  // next refill's block id, fetched a step ahead
+  for (int d = 0; d < pre; ++d) issue(d, d, blocks_of(d));
+  Blk blk_next = blocks_of(R - 1);  // next refill's block ids, fetched a step ahead
 
   // ---- query operand and codebook tables (registers) ----
   half8 bq[4];
@@ -813,25 +826,29 @@ __global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
   // it with u+R-1, compute this wave's tile of u from LDS ----
   int entry = 0;
   for (int u = 0; u < nst; ++u) {
-    vm_wait(ring.my_loads * min(R - 2, nst - 1 - u));
+    vm_wait(TPW * ring.my_loads * min(R - 2, nst - 1 - u));
     wg_barrier();
     if (u + R - 1 < nst) {
       issue(u + R - 1, entry == 0 ? R - 1 : entry - 1, blk_next);
-      blk_next = block_of(my_tile(u + R));
+      blk_next = blocks_of(u + R);
     }
-    const int t = t_begin + u * NP + ph;
-    if (t < t_end) {
-      TileRegs<P> r;
-      const uint8_t* img = tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * spt) * 1024u;
-      load_tile<P>(img, off, r);
-      PendingTile cur;
-      score_tile<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
-      if (have_pend) {
-        accumulate_pair<P>(pend, cur, acc);
-        have_pend = false;
-      } else {
-        pend = cur;
-        have_pend = true;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t_begin + u * Q + ph * TPW + j;
+      if (t < t_end) {
+        TileRegs<P> r;
+        const uint8_t* img =
+            tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
+        load_tile<P>(img, off, r);
+        PendingTile cur;
+        score_tile<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
+        if (have_pend) {
+          accumulate_pair<P>(pend, cur, acc);
+          have_pend = false;
+        } else {
+          pend = cur;
+          have_pend = true;
+        }
       }
     }
     entry = entry + 1 == R ? 0 : entry + 1;
@@ -1011,20 +1028,25 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int P>
-int launch_stage1(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
+template <int P, int TPW>
+int launch_stage1_t(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   });
   if (attr != hipSuccess) return tq::hip_status(attr);
   DecodeArgs arg = a;
   void* args[] = {&arg};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P>),
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW>),
                                         dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
                                         stream));
+}
+
+template <int P>
+int launch_stage1(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
+  return tpw == 2 ? launch_stage1_t<P, 2>(a, nblocks, lds, stream) : launch_stage1_t<P, 1>(a, nblocks, lds, stream);
 }
 
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
@@ -1062,10 +1084,10 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   const int64_t nblocks = plan.grid;
   const size_t lds = plan.lds;
   switch (layout->preset) {
-    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, nblocks, lds, stream);
-    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, nblocks, lds, stream);
-    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, nblocks, lds, stream);
-    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, nblocks, lds, stream);
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, nblocks, lds, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, nblocks, lds, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, nblocks, lds, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }

@@ -71,6 +71,7 @@ inline int64_t max_splits(int64_t batch, int64_t num_splits) {
 // sequence (block-table width), which caps S_int.
 struct DecodePlan {
   int G, P, R, spt, contiguous;
+  int tpw;         // tiles each wave computes per super-tile (between barriers)
   size_t lds;      // dynamic LDS bytes per workgroup
   int64_t units;   // U
   int64_t grid;    // workgroups = U * (Hk / G) * head groups
@@ -102,19 +103,23 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   const int64_t piece = G * slot;
   const int64_t tc_max = contiguous ? row : 16 * ((piece + 30) / 16);  // chunks per tile image
   const int spt = static_cast<int>((tc_max + 63) / 64);
-  const size_t entry = static_cast<size_t>(P) * spt * 1024;
+  // MSE keys: two tiles per wave between barriers (two independent chains
+  // to interleave), when the ring still fits two workgroups per CU
+  const int tpw = (!L->key_fp8 && 2 * static_cast<size_t>(P) * spt * 1024 * 2 <= 80 * 1024) ? 2 : 1;
+  const size_t entry = static_cast<size_t>(P) * tpw * spt * 1024;
   size_t R = kLdsBudget / entry;
   R = R < 2 ? 2 : (R > 4 ? 4 : R);
   const size_t merge = P > 1 ? static_cast<size_t>(P - 1) * G * 33 * 64 * 4 : 0;
   p->G = G;
   p->P = P;
   p->R = static_cast<int>(R);
+  p->tpw = tpw;
   p->spt = spt;
   p->contiguous = contiguous;
   p->lds = R * entry > merge ? R * entry : merge;
   p->units = static_cast<int64_t>(batch) * s_int;
   p->grid = p->units * wg_per_unit;
-  const int loads = (spt + G - 1) / G;  // DMA slots per wave per super-tile (its phase's tile)
+  const int loads = (spt + G - 1) / G;  // DMA slots per wave per tile of its phase
   const int64_t blk_bytes = 128 * row;  // largest block (block_size 128)
   if (p->lds > kLdsMax || loads > 5 || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
       blk_bytes > 0xFFFFFFFFLL || s_int > max_splits(batch, num_splits))
