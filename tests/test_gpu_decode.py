@@ -145,3 +145,51 @@ def test_decode_full_size_sampled(name, S, rows):
         err = np.max(np.abs(out[b, hq] - ro)) / np.max(np.abs(ro))
         assert err <= G.DECODE_RTOL, (b, hq, err)
         assert abs(lse[b, hq] - rl) <= G.LSE_ATOL * max(1.0, abs(rl))
+
+
+@pytest.mark.parametrize("preset", ["turboquant_k8v4", "turboquant_3bit_nc"])
+@pytest.mark.parametrize("S", [1, 4, 32])
+def test_decode_ragged_lengths_balanced_units(preset, S):
+    """Very uneven lengths: the work units are spread in proportion to
+    length, empty sequences get none (o = 0, lse = -inf)."""
+    w = _small(preset, [1, 2000, 17, 0, 700, 40], Hq=4, Hk=2, bs=16, seed=90 + S)
+    G.log(f"decode ragged {preset} S={S}")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), S)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+def test_decode_many_sequences():
+    """More than 64 sequences: the unit search scans the lengths in several
+    64-wide passes."""
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(0, 90, 150)]
+    w = _small("turboquant_k3v4_nc", lens, Hq=2, Hk=1, bs=32, seed=12)
+    G.log("decode 150 sequences")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 3)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+@pytest.mark.parametrize("preset,Hk,g", [
+    ("turboquant_4bit_nc", 1, 4),     # one head: 8 phase waves
+    ("turboquant_k8v4", 3, 2),        # contiguous group of 3 heads, 2 phases
+    ("turboquant_k3v4_nc", 16, 2),    # groups of 8 heads, 16-byte aligned row pieces
+    ("turboquant_4bit_nc", 12, 1),    # groups of 6 heads, misaligned row pieces
+    ("turboquant_k8v4", 12, 3),       # groups of 4 heads, aligned (196-byte slots), 2 phases
+])
+def test_decode_head_groupings(preset, Hk, g):
+    w = _small(preset, [45, 130, 16], Hq=Hk * g, Hk=Hk, bs=32, seed=100 + Hk)
+    G.log(f"decode groupings {preset} Hk={Hk} g={g}")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 2)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
