@@ -9,6 +9,8 @@ cache.  The headline workload is the Llama-3-8B-shaped layer (k8v4, 32
 sequences x 4096 tokens, 32/8 heads, block 16).  ``value`` is the effective
 decode-attention bandwidth: compressed-cache bytes the step reads
 (sum_b L_b * Hk * slot_size) over the step's wall time, inputs resident in HBM.
+The same bytes over one tq_decode_attention call alone (no store) are
+reported as ``config.decode_call_gbs``.
 
 Timing: the step is captured in a HIP graph three times in a row, once per
 copy of the cache (3 x 411 MB for the headline, so the 256 MB Infinity Cache
@@ -154,6 +156,26 @@ class DecodeBench:
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps  # ms per step
+
+    def time_decode(self, calls):
+        """ms per tq_decode_attention call (stage 1 + stage 2, no store),
+        from a graph of one call per cache copy replayed back to back."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(N_COPIES):
+                self.stage1(i)
+                self.stage2()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, calls // N_COPIES)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * N_COPIES)
 
     def time_stage1(self, launches):
         """Average stage-1 kernel duration (ms): events on the launch stream
@@ -312,9 +334,12 @@ def main():
     hb = DecodeBench(torch, tq, w, args.splits)
     ms = hb.time_steps(args.steps, args.warmup)
     st1_ms = hb.time_stage1(max(30, args.steps // 4))
+    dec_ms = hb.time_decode(max(30, args.steps // 2))
     gbs = hb.bytes_read / (ms * 1e-3) / 1e9
     st1_gbs = hb.bytes_read / (st1_ms * 1e-3) / 1e9
-    log(f"[llama8b] step {ms * 1e3:.1f} us  -> {gbs:.0f} GB/s; stage1 {st1_ms * 1e3:.1f} us -> {st1_gbs:.0f} GB/s")
+    dec_gbs = hb.bytes_read / (dec_ms * 1e-3) / 1e9
+    log(f"[llama8b] step {ms * 1e3:.1f} us  -> {gbs:.0f} GB/s; decode call {dec_ms * 1e3:.1f} us -> {dec_gbs:.0f} GB/s; "
+        f"stage1 {st1_ms * 1e3:.1f} us -> {st1_gbs:.0f} GB/s")
     head_bytes = hb.bytes_read
     del hb
     torch.cuda.empty_cache()
@@ -324,13 +349,16 @@ def main():
         for name, S in (("longctx", 32), ("qwen32b", args.splits)):
             wk = W.WORKLOADS[name]
             b = DecodeBench(torch, tq, wk, S)
-            m = b.time_steps(max(20, args.steps // 4), max(5, args.warmup // 4))
+            m = b.time_steps(max(21, args.steps // 4), max(6, args.warmup // 4))
             s1 = b.time_stage1(20)
-            extra[name] = {"preset": wk.preset, "ms_per_step": m, "decode_gbs": b.bytes_read / (m * 1e-3) / 1e9,
-                           "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9,
-                           "frac_hbm": b.bytes_read / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, "num_kv_splits": S,
+            d = b.time_decode(30)
+            extra[name] = {"preset": wk.preset, "ms_per_step": m, "step_gbs": b.bytes_read / (m * 1e-3) / 1e9,
+                           "ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
+                           "decode_frac_hbm": b.bytes_read / (d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "num_kv_splits": S,
                            "bytes_read": b.bytes_read}
-            log(f"[{name}] step {m * 1e3:.1f} us -> {extra[name]['decode_gbs']:.0f} GB/s")
+            log(f"[{name}] step {m * 1e3:.1f} us -> {extra[name]['step_gbs']:.0f} GB/s; decode call {d * 1e3:.1f} us "
+                f"-> {extra[name]['decode_gbs']:.0f} GB/s")
             del b
             torch.cuda.empty_cache()
         extra["store_sweep"] = store_sweep(torch, tq, 50)
@@ -352,7 +380,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama8b: k8v4 decode step, 32 seqs x 4096 tokens, 32/8 heads, head_dim 128, block 16",
                    "global_batch": w.batch, "seq_len": int(w.seq_len), "num_kv_splits": args.splits,
-                   "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head_bytes},
+                   "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head_bytes,
+                   "decode_call_us": dec_ms * 1e3, "decode_call_gbs": dec_gbs,
+                   "decode_call_frac_hbm_peak": dec_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": st1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": st1_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(), "kernel": "tq_decode_stage1_kernel<k8v4>",
                      "stage1_us": st1_ms * 1e3},
