@@ -932,20 +932,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// One workgroup (4 waves) per (sequence, query head): output = sum_s w_s o_s
-// / sum_s w_s with w_s = exp(lse_s - max), lse = max + log(sum_s w_s), over
-// the sequence's units (the table stage 1 writes).  Latency-bound, so the
-// loads are issued together: wave w takes units w, w + 4, ...; after the
-// table read each lane fetches its 2 output dims of 16 of the wave's units
-// and lane j the LSE of the wave's j-th unit, all at once.  The 4 waves'
-// running (max, sum, output) are combined through LDS.
+// Output = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max), lse = max
+// + log(sum_s w_s), over the units of a (sequence, query head) row (the table
+// stage 1 writes).  Latency-bound, so the loads are issued together: after
+// the table read each lane fetches its 2 output dims of up to 16 units and
+// lane j the LSE of unit j, all at once.  kW waves share a row (wave w takes
+// units w, w + kW, ...; their running (max, sum, output) combine through
+// LDS) when rows have many units; otherwise each wave of the workgroup
+// takes its own row (kW = 1).
+template <int kW>
 __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
                                                                const float* __restrict__ part, int Hq, int rows,
                                                                void* out, int out_dtype, float* lse_out) {
-  constexpr int kBatch = 16, kW = 4;
-  __shared__ float comb[kW - 1][2 * 64 + 2];
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kBatch = 16;
+  __shared__ float comb[kW > 1 ? kW - 1 : 1][2 * 64 + 2];
+  const int lane = threadIdx.x & 63;
+  const int w = kW > 1 ? (threadIdx.x >> 6) : 0;
+  const int row = kW > 1 ? blockIdx.x : blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (kW == 1 && row >= rows) return;
   const int b = row / Hq, hq = row - b * Hq;
   const int first = table[2 * b], n = table[2 * b + 1];
   const float* base = part + (static_cast<int64_t>(first) * Hq + hq) * kRow;
@@ -980,19 +984,21 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
       o1 = fmaf(wq, v[q].y, o1);
     }
   }
-  if (w > 0) {
-    comb[w - 1][2 * lane] = o0;
-    comb[w - 1][2 * lane + 1] = o1;
-    if (lane == 0) {
-      comb[w - 1][128] = M;
-      comb[w - 1][129] = den;
+  if (kW > 1) {
+    if (w > 0) {
+      comb[w - 1][2 * lane] = o0;
+      comb[w - 1][2 * lane + 1] = o1;
+      if (lane == 0) {
+        comb[w - 1][128] = M;
+        comb[w - 1][129] = den;
+      }
     }
+    __syncthreads();
+    if (w != 0) return;
   }
-  __syncthreads();
-  if (w != 0) return;
   float Mt = M;
 #pragma unroll
-  for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][128]);
+  for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][128]);  // no-op for kW == 1
   float lse = -INFINITY;
   if (Mt != -INFINITY) {
     float a0 = M == -INFINITY ? 0.f : expf(M - Mt);
@@ -1092,15 +1098,21 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   return TQ_EPRESET;
 }
 
-int stage2(int32_t batch, int32_t num_q_heads, const void* workspace, void* out, int32_t out_dtype, float* lse_out,
-           hipStream_t stream) {
+int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const void* workspace, void* out,
+           int32_t out_dtype, float* lse_out, hipStream_t stream) {
   int rows = batch * num_q_heads;
   int Hq = num_q_heads;
   const int32_t* table = static_cast<const int32_t*>(workspace);
   const float* part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + tq::table_bytes(batch));
   void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel),
-                                        dim3(rows), dim3(256), args, 0, stream));
+  // rows of many units share 4 waves; otherwise one wave per row.  The bound
+  // on units per sequence is S_max (balanced units give long sequences more,
+  // so the threshold leaves room).
+  if (tq::max_splits(batch, num_kv_splits) > 24)
+    return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<4>), dim3(rows),
+                                          dim3(256), args, 0, stream));
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<1>),
+                                        dim3((rows + 3) / 4), dim3(256), args, 0, stream));
 }
 
 }  // namespace
@@ -1138,7 +1150,8 @@ extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head
   int st = tq::validate_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace, workspace_bytes, out,
                                out_dtype);
   if (st != TQ_OK || batch == 0) return st;
-  return stage2(batch, num_q_heads, workspace, out, out_dtype, lse_out, static_cast<hipStream_t>(stream));
+  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out,
+                static_cast<hipStream_t>(stream));
 }
 
 extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
@@ -1156,5 +1169,5 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
   st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
               block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace, s);
   if (st != TQ_OK) return st;
-  return stage2(batch, num_q_heads, workspace, out, out_dtype, lse_out, s);
+  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out, s);
 }
