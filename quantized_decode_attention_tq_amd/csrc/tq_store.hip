@@ -30,7 +30,7 @@ constexpr int kMaxSlot = 208;  // >= every preset's slot at head_dim 128, 16-byt
 struct StoreArgs {
   const uint16_t* key;
   const uint16_t* value;
-  int64_t num_rows;  // N * Hk
+  int32_t num_rows;  // tokens of this launch * Hk, below 2^31
   int64_t key_tok_stride;
   int64_t val_tok_stride;
   const int64_t* slot_mapping;
@@ -40,13 +40,7 @@ struct StoreArgs {
   const float* boundaries;
   int32_t num_kv_heads;
   int32_t slot_bytes;  // slot_size_aligned
-  int32_t is_bf16;
 };
-
-__device__ __forceinline__ float widen16(uint32_t bits, bool bf16) {
-  if (bf16) return __uint_as_float(bits << 16);
-  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
-}
 
 // Value of lane (l ^ m) for m = 1, 2, 4 (within each 8-lane row group), by
 // DPP lane moves: no LDS round trip.  xor 1 / xor 2 are quad permutes; xor 4
@@ -64,52 +58,105 @@ __device__ __forceinline__ float xor_shfl(float v, int m) {
   return __int_as_float(x);
 }
 
-__device__ __forceinline__ void load_row16(const uint16_t* p, bool bf16, float x[kDpl]) {
+// 16 consecutive bf16 / fp16 elements -> fp32
+template <int BF16>
+__device__ __forceinline__ void load_row16(const uint16_t* p, float x[kDpl]) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
   uint4 a = q[0], b = q[1];
   uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    x[2 * i] = widen16(w[i] & 0xFFFFu, bf16);
-    x[2 * i + 1] = widen16(w[i] >> 16, bf16);
+    if (BF16) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    } else {
+      x[2 * i] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xFFFFu)));
+      x[2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+    }
   }
 }
 
 __device__ __forceinline__ void st16(uint8_t* p, uint32_t v) { *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v); }
 
-// count of boundaries strictly below u, binary search over the sorted table
+// Bucket search over the sorted boundaries, kept in LDS in breadth-first
+// (Eytzinger) order: node n (1 .. 2^KB - 1) holds the boundary the plain
+// binary search probes after taking the branches spelled by the bits of n
+// below its leading one.  The walk n <- 2n + (u > tree[n]) ends on node
+// 2^KB + #{boundaries < u}.  The walk carries 4n, the node's byte offset.
 template <int KB>
-__device__ __forceinline__ int bucketize(float u, const float* __restrict__ b_lds) {
-  constexpr int L = 1 << KB;
-  int i = 0;
+__device__ __forceinline__ uint32_t tree_search(float u, const float* __restrict__ tree) {
+  uint32_t m = 4;
 #pragma unroll
-  for (int step = L / 2; step >= 1; step >>= 1) i += (u > b_lds[i + step - 1]) ? step : 0;
-  return i;
+  for (int d = 0; d < KB; ++d) {
+    const float t = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(tree) + m);
+    m = 2 * m + (u > t ? 4u : 0u);
+  }
+  return m;
 }
 
-template <int KEY_FP8, int KB, int VB, int NC>
+// Sum, mod 2^32, of the 2^KB terms that the search's end nodes carry into
+// word k of a lane's packed key bits (codes that straddle into the next word
+// carry none).
+template <int KB>
+__host__ __device__ constexpr uint32_t key_bias(int k) {
+  uint32_t r = 0;
+  for (int i = 0; i < kDpl; ++i) {
+    const int p = KB * i;
+    if ((p >> 5) == k && (p & 31) + KB < 32) r += 1u << ((p & 31) + KB);
+  }
+  return r;
+}
+
+// Packs B-bit fields LSB-first into 32-bit words: field i at bit B*i.
+template <int B>
+struct Pack32 {
+  uint32_t w[2] = {0u, 0u};
+  // m = 4 * the search's end node 2^B + code: added whole, the 2^B terms
+  // are removed once per word by finish_nodes()
+  __device__ __forceinline__ void add_node(int i, uint32_t m) {
+    const int p = B * i, k = p >> 5, s = p & 31;
+    w[k] += s >= 2 ? m << (s - 2) : m >> (2 - s);
+    if (s + B > 32) w[k + 1] += __builtin_amdgcn_ubfe(m, 34 - s, s + B - 32);
+  }
+  __device__ __forceinline__ void finish_nodes() {
+    w[0] -= key_bias<B>(0);
+    w[1] -= key_bias<B>(1);
+  }
+  __device__ __forceinline__ void or_code(int i, uint32_t c) {
+    const int p = B * i, k = p >> 5, s = p & 31;
+    w[k] |= c << s;
+    if (s + B > 32) w[k + 1] |= c >> (32 - s);
+  }
+};
+
+template <int KEY_FP8, int KB, int VB, int NC, int BF16>
 __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
-  __shared__ float c_lds[16];
-  __shared__ float b_lds[16];
+  constexpr int kL = 1 << KB;
+  __shared__ float tree[kL];        // node 1 .. kL - 1: boundaries in search order
+  __shared__ float cent[2 * kL];    // kL + code: centroid of the search's end node
   if (!KEY_FP8) {
-    if (threadIdx.x < (1 << KB)) c_lds[threadIdx.x] = a.centroids[threadIdx.x];
-    if (threadIdx.x < (1 << KB) - 1) b_lds[threadIdx.x] = a.boundaries[threadIdx.x];
+    const int t = threadIdx.x;
+    if (t >= 1 && t < kL) {
+      const int d = 31 - __builtin_clz(t);  // depth of node t
+      const int p = t - (1 << d);           // branches taken to reach it
+      tree[t] = a.boundaries[(p << (KB - d)) + (1 << (KB - d - 1)) - 1];
+    }
+    if (t < kL) cent[kL + t] = a.centroids[t];
     __syncthreads();
   }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane & 7;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kRowsPerWave + (lane >> 3);
-  const bool active = row0 < a.num_rows;
-  const int64_t row = active ? row0 : a.num_rows - 1;  // inactive rows compute on a valid row, store nothing
-  const int64_t n = row / a.num_kv_heads;
+  const uint32_t row0 = (blockIdx.x * kWaves + wave) * kRowsPerWave + (lane >> 3);
+  const bool active = row0 < static_cast<uint32_t>(a.num_rows);
+  const uint32_t row = active ? row0 : a.num_rows - 1;  // inactive rows compute on a valid row, store nothing
+  const uint32_t n = row / static_cast<uint32_t>(a.num_kv_heads);
   const int h = static_cast<int>(row - n * a.num_kv_heads);
-  const bool bf16 = a.is_bf16 != 0;
 
   float x[kDpl], v[kDpl];
-  load_row16(a.key + n * a.key_tok_stride + h * kD + sub * kDpl, bf16, x);
-  load_row16(a.value + n * a.val_tok_stride + h * kD + sub * kDpl, bf16, v);
+  load_row16<BF16>(a.key + n * a.key_tok_stride + h * kD + sub * kDpl, x);
+  load_row16<BF16>(a.value + n * a.val_tok_stride + h * kD + sub * kDpl, v);
 
   const int64_t m = a.slot_mapping[n];
   uint8_t* slot = a.cache + (m * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes);
@@ -117,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
 
   // ---------------- key ----------------
   constexpr int kKeyBytesPerLane = KEY_FP8 ? kDpl : (kDpl * KB) / 8;
-  uint32_t kbytes[kDpl / 2] = {};  // lane's key bytes, little-endian, packed 4 per dword
+  uint32_t kbytes[kDpl / 4] = {};  // lane's key bytes, little-endian, packed 4 per dword
   uint32_t gamma_bits = 0;
   if (KEY_FP8) {
     // Hardware convert (round to nearest even) after clamping to the E4M3
@@ -148,19 +195,22 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     ss += xor_shfl(ss, 4);
     const float nu = sqrtf(ss);
 
+    // Walsh-Hadamard butterflies, natural (Sylvester) order.  Stride 1 takes
+    // the signs in: with s = +-1, s_i x_i is exact, so fma(x_i, s_i, +-s_j x_j)
+    // rounds exactly as the sum of the signed pair does.
     float y[kDpl];
     const float4* sg = reinterpret_cast<const float4*>(a.signs + sub * kDpl);
 #pragma unroll
     for (int i = 0; i < kDpl / 4; ++i) {
-      float4 s4 = sg[i];
-      y[4 * i + 0] = x[4 * i + 0] * s4.x;
-      y[4 * i + 1] = x[4 * i + 1] * s4.y;
-      y[4 * i + 2] = x[4 * i + 2] * s4.z;
-      y[4 * i + 3] = x[4 * i + 3] * s4.w;
+      const float4 s4 = sg[i];
+      const float q0 = x[4 * i + 1] * s4.y, q1 = x[4 * i + 3] * s4.w;
+      y[4 * i + 0] = fmaf(x[4 * i], s4.x, q0);
+      y[4 * i + 1] = fmaf(x[4 * i], s4.x, -q0);
+      y[4 * i + 2] = fmaf(x[4 * i + 2], s4.z, q1);
+      y[4 * i + 3] = fmaf(x[4 * i + 2], s4.z, -q1);
     }
-    // Walsh-Hadamard butterflies, natural (Sylvester) order
 #pragma unroll
-    for (int hs = 1; hs < kDpl; hs <<= 1) {
+    for (int hs = 2; hs < kDpl; hs <<= 1) {
 #pragma unroll
       for (int i = 0; i < kDpl; ++i) {
         if ((i & hs) == 0) {
@@ -170,39 +220,41 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
         }
       }
     }
+    // Strides 16, 32, 64 pair lane l with lane l ^ msk of the row's 8 lanes:
+    // the lower lane of a pair takes p + q, the upper one p - q.  Each lane
+    // keeps its coordinates times a lane sign sigma (equal on both lanes of a
+    // pair before the stride): w <- w + e * w_partner with e = -1 on the upper
+    // lane and +1 on the lower one gives sigma*(p+q) on the lower lane and
+    // -sigma*(p-q) on the upper one, so each stride is one fma per value and
+    // flips sigma on the upper lanes.  After the three strides
+    // sigma = (-1)^popcount(sub); it is folded into the scale below.
 #pragma unroll
     for (int msk = 1; msk < 8; msk <<= 1) {
-      const bool upper = (sub & msk) != 0;
+      const float e = (sub & msk) ? -1.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < kDpl; ++i) {
-        float o = xor_shfl(y[i], msk);
-        y[i] = upper ? (o - y[i]) : (y[i] + o);
-      }
+      for (int i = 0; i < kDpl; ++i) y[i] = fmaf(xor_shfl(y[i], msk), e, y[i]);
     }
     // u = (H s.*x) / (sqrt(D) * nu); nu == 0 gives u = 0 and a zero norm field
-    const float inv = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
+    const float inv0 = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
+    const float inv = (__builtin_popcount(sub) & 1) ? -inv0 : inv0;
     float cs = 0.f;
-    int code[kDpl];
+    Pack32<KB> kp;
 #pragma unroll
     for (int i = 0; i < kDpl; ++i) {
-      code[i] = bucketize<KB>(y[i] * inv, b_lds);
-      const float c = c_lds[code[i]];
+      const uint32_t m4 = tree_search<KB>(y[i] * inv, tree);
+      const float c = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(cent) + m4);
       cs = fmaf(c, c, cs);
+      kp.add_node(i, m4);
     }
+    kp.finish_nodes();
+    kbytes[0] = kp.w[0];
+    kbytes[1] = kp.w[1];
     cs += xor_shfl(cs, 1);
     cs += xor_shfl(cs, 2);
     cs += xor_shfl(cs, 4);
     float gamma = nu;
     if (NC) gamma = nu > 0.f ? nu / sqrtf(cs) : 0.f;
     gamma_bits = __half_as_ushort(__float2half_rn(gamma));
-    // LSB-first bit stream: code i of the lane at bit KB*i of the lane's chunk
-    uint64_t bitsacc = 0;
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) bitsacc |= static_cast<uint64_t>(code[i]) << (KB * i);
-#pragma unroll
-    for (int i = 0; i < kDpl / 2; ++i) kbytes[i] = 0;
-    kbytes[0] = static_cast<uint32_t>(bitsacc);
-    kbytes[1] = static_cast<uint32_t>(bitsacc >> 32);
   }
 
   // ---------------- value ----------------
@@ -223,14 +275,19 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   const __half s16 = __float2half_rn(s32);
   const float zf = __half2float(z16);
   const float sf = __half2float(s16);
-  uint64_t vacc = 0;
+  Pack32<VB> vp32;
   if (sf != 0.f) {
     const float inv = __fdiv_rn(1.0f, sf);
 #pragma unroll
     for (int i = 0; i < kDpl; ++i) {
-      float r = __fadd_rn(__fmul_rn(__fsub_rn(v[i], zf), inv), 0.5f);
-      r = fminf(fmaxf(floorf(r), 0.f), static_cast<float>(kLevels));  // NaN -> 0
-      vacc |= static_cast<uint64_t>(static_cast<uint32_t>(r)) << (VB * i);
+      // three fp32 roundings, as defined: no fused multiply-add here
+#pragma clang fp contract(off)
+      const float q = (v[i] - zf) * inv;
+      float r = q + 0.5f;
+      // clamp to [0, levels] (NaN -> 0), then truncate: floor of a
+      // non-negative number
+      r = fminf(fmaxf(r, 0.f), static_cast<float>(kLevels));
+      vp32.or_code(i, static_cast<uint32_t>(r));
     }
   }
   constexpr int kValBytesPerLane = (kDpl * VB) / 8;
@@ -251,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     if (!KEY_FP8 && sub == 0) st16(sl + kdata, gamma_bits);
     uint8_t* vp = sl + kps + sub * kValBytesPerLane;
 #pragma unroll
-    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, static_cast<uint32_t>(vacc >> (16 * i)));
+    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, vp32.w[i / 2] >> (16 * (i % 2)));
     if (sub == 0) {
       st16(sl + kps + vdata, __half_as_ushort(s16));
       st16(sl + kps + vdata + 2, __half_as_ushort(z16));
@@ -271,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     if (!KEY_FP8 && sub == 0) st16(slot + kdata, gamma_bits);
     uint8_t* vp = slot + kps + sub * kValBytesPerLane;
 #pragma unroll
-    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, static_cast<uint32_t>(vacc >> (16 * i)));
+    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, vp32.w[i / 2] >> (16 * (i % 2)));
     if (sub == 0) {
       st16(slot + kps + vdata, __half_as_ushort(s16));
       st16(slot + kps + vdata + 2, __half_as_ushort(z16));
@@ -280,13 +337,23 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
 }
 
 template <int KEY_FP8, int KB, int VB, int NC>
-int launch_store(const StoreArgs& a, hipStream_t stream) {
-  const int64_t blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
+int launch_store(const StoreArgs& a, bool bf16, hipStream_t stream) {
+  const int blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   StoreArgs arg = a;
   void* args[] = {&arg};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC>),
-                                        dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
+  const void* fn = bf16 ? reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, 1>)
+                        : reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, 0>);
+  return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
+}
+
+int launch_preset(int32_t preset, const StoreArgs& a, bool bf16, hipStream_t s) {
+  switch (preset) {
+    case TQ_K8V4: return launch_store<1, 8, 4, 0>(a, bf16, s);
+    case TQ_4BIT_NC: return launch_store<0, 4, 4, 1>(a, bf16, s);
+    case TQ_K3V4_NC: return launch_store<0, 3, 4, 1>(a, bf16, s);
+    case TQ_3BIT_NC: return launch_store<0, 3, 3, 1>(a, bf16, s);
+  }
+  return TQ_EPRESET;
 }
 
 }  // namespace
@@ -299,25 +366,26 @@ extern "C" int tq_store(const tq_layout* layout, const void* key, const void* va
                               slot_mapping, kv_cache, num_blocks, block_size, signs, centroids, boundaries);
   if (st != TQ_OK || num_tokens == 0) return st;
   StoreArgs a;
-  a.key = static_cast<const uint16_t*>(key);
-  a.value = static_cast<const uint16_t*>(value);
-  a.num_rows = num_tokens * num_kv_heads;
+  a.num_kv_heads = num_kv_heads;
   a.key_tok_stride = key_tok_stride;
   a.val_tok_stride = val_tok_stride;
-  a.slot_mapping = slot_mapping;
   a.cache = static_cast<uint8_t*>(kv_cache);
   a.signs = signs;
   a.centroids = centroids;
   a.boundaries = boundaries;
-  a.num_kv_heads = num_kv_heads;
   a.slot_bytes = layout->slot_size_aligned;
-  a.is_bf16 = in_dtype == TQ_BF16;
+  const bool bf16 = in_dtype == TQ_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (layout->preset) {
-    case TQ_K8V4: return launch_store<1, 8, 4, 0>(a, s);
-    case TQ_4BIT_NC: return launch_store<0, 4, 4, 1>(a, s);
-    case TQ_K3V4_NC: return launch_store<0, 3, 4, 1>(a, s);
-    case TQ_3BIT_NC: return launch_store<0, 3, 3, 1>(a, s);
+  // the kernel indexes rows in 32 bits: launches of at most 2^30 rows
+  const int64_t chunk = (int64_t{1} << 30) / num_kv_heads > 0 ? (int64_t{1} << 30) / num_kv_heads : 1;
+  for (int64_t t0 = 0; t0 < num_tokens; t0 += chunk) {
+    const int64_t nt = num_tokens - t0 < chunk ? num_tokens - t0 : chunk;
+    a.key = static_cast<const uint16_t*>(key) + t0 * key_tok_stride;
+    a.value = static_cast<const uint16_t*>(value) + t0 * val_tok_stride;
+    a.slot_mapping = slot_mapping + t0;
+    a.num_rows = static_cast<int32_t>(nt * num_kv_heads);
+    st = launch_preset(layout->preset, a, bf16, s);
+    if (st != TQ_OK) return st;
   }
-  return TQ_EPRESET;
+  return TQ_OK;
 }
