@@ -231,7 +231,11 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
     if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
       r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
     } else {
-      r.sz[i] = ld16(m + T::kKps + T::kVdata) | (ld16(m + T::kKps + T::kVdata + 2) << 16);
+      // 2 mod 4 for half the heads: an aligned pair of dwords, realigned
+      // (an unaligned LDS dword read stalls)
+      const uint32_t so = o.mo[i] + static_cast<uint32_t>(T::kKps + T::kVdata);
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (so & ~3u));
+      r.sz[i] = tq::alignbyte(w.y, w.x, so & 3u);
     }
     if constexpr (T::kFp8 == 0) r.gm[i] = ld16(m + T::kKdata);
   }
@@ -650,7 +654,7 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // phase waves of a head merge their partial softmax states through LDS and
 // the phase-0 wave writes the split's partial rows.
 template <int P, int TPW>
-__global__ __launch_bounds__(512) void tq_decode_stage1_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
 
