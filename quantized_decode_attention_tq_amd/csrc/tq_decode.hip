@@ -426,12 +426,14 @@ __device__ __forceinline__ void accumulate_pair(const PendingTile& a, const Pend
 // Tile p of a super-tile is staged by the G waves of phase p (the waves
 // that will compute it): wave (hh, p) issues slots hh, hh + G, ... of it,
 // so a wave needs one block id and one base address per super-tile.
+template <int P>
 struct Ring {
-  uint32_t lds_base;  // LDS byte address of ring entry 0 (uniform)
-  uint32_t entry;     // bytes per ring entry (P * spt KB)
-  int my_loads;       // DMA slots per super-tile issued by this wave
-  uint32_t dst[5];    // per load: LDS offset inside the entry (uniform)
-  uint32_t off[5];    // per load: this lane's chunk offset from the tile base
+  static constexpr int kLoads = tq::max_dma_loads(P);
+  uint32_t lds_base;       // LDS byte address of ring entry 0 (uniform)
+  uint32_t entry;          // bytes per ring entry (P * spt KB)
+  int my_loads;            // DMA slots per super-tile issued by this wave
+  uint32_t dst[kLoads];    // per load: LDS offset inside the entry (uniform)
+  uint32_t off[kLoads];    // per load: this lane's chunk offset from the tile base
 };
 
 // One direct-to-LDS load of 16 bytes per lane, non-temporal: the data is
@@ -729,12 +731,12 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 
   // ---- ring: this wave's DMA slots of each super-tile ----
   const int spt = a.spt;
-  Ring ring;
+  Ring<P> ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
   ring.entry = static_cast<uint32_t>(Q * spt) * 1024u;
   ring.my_loads = (spt - hh + G - 1) / G;  // per tile
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < Ring<P>::kLoads; ++k) {
     const int n = hh + k * G;  // slot of tile ph (n < spt for k < my_loads)
     ring.dst[k] = static_cast<uint32_t>(ph * TPW * spt + n) * 1024u;  // in tile 0 of this wave's TPW
     uint32_t c = min(static_cast<uint32_t>(64 * n + lane), tc - 1);
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
       const uint8_t* base = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk.id[j])) * blk_bytes32 +
                             static_cast<uint32_t>((t * 16) & (a.block_size - 1)) * geo.row;
 #pragma unroll
-      for (int k = 0; k < 5; ++k)
+      for (int k = 0; k < Ring<P>::kLoads; ++k)
         if (k < ring.my_loads) dma16(base, ring.off[k], e0 + ring.dst[k] + static_cast<uint32_t>(j * spt) * 1024u);
     }
   };

@@ -77,6 +77,12 @@ struct DecodePlan {
   int64_t grid;    // workgroups = U * (Hk / G) * head groups
 };
 
+// Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
+// this many for any head count at head_dim 128 (slots of 196 / 134 / 118 /
+// 102 bytes; a wave of G waves per tile takes ceil(spt / G) of the tile's
+// spt loads).
+constexpr int max_dma_loads(int preset) { return preset == TQ_K8V4 ? 4 : (preset == TQ_3BIT_NC ? 2 : 3); }
+
 inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t num_splits, int64_t max_tiles, DecodePlan* p) {
   constexpr size_t kLdsBudget = 52 * 1024, kLdsMax = 160 * 1024;  // two-deep rings measured best
@@ -121,7 +127,7 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   p->grid = p->units * wg_per_unit;
   const int loads = (spt + G - 1) / G;  // DMA slots per wave per tile of its phase
   const int64_t blk_bytes = 128 * row;  // largest block (block_size 128)
-  if (p->lds > kLdsMax || loads > 5 || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
+  if (p->lds > kLdsMax || loads > max_dma_loads(L->preset) || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
       blk_bytes > 0xFFFFFFFFLL || s_int > max_splits(batch, num_splits))
     return TQ_EUNSUPPORTED;
   return TQ_OK;

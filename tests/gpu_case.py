@@ -143,6 +143,23 @@ class DecodeCase:
         t.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
+    def gpu_decode_two_stage(self, cache, num_kv_splits, workspace_fill=None):
+        """tq_decode_stage1 then tq_decode_stage2 (the split entry points)."""
+        import quantized_decode_attention_tq_amd as tq
+
+        t = torch()
+        B, Hq = self.q.shape[:2]
+        ws = t.empty(tq.decode_workspace_bytes(B, Hq, 128, num_kv_splits), dtype=t.uint8, device="cuda")
+        if workspace_fill is not None:
+            ws.fill_(workspace_fill)
+        tq.decode_stage1(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids, self.scale,
+                         num_kv_splits, ws)
+        out = t.empty((B, Hq, 128), dtype=t.float32, device="cuda")
+        lse = t.empty((B, Hq), dtype=t.float32, device="cuda")
+        tq.decode_stage2(B, Hq, 128, num_kv_splits, ws, out, lse)
+        t.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
     def oracle_decode(self, rows=None, cache=None):
         q = O.widen(self.qbits, self.w.dtype)
         return O.decode(self.lay, q, self.cache_o if cache is None else cache, self.table, self.lens, self.signs,

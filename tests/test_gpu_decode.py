@@ -193,3 +193,24 @@ def test_decode_head_groupings(preset, Hk, g):
     out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 2)
     ref, rlse = c.oracle_decode()
     G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("S", [1, 8])
+def test_split_entry_points_match_single_call(preset, S):
+    """tq_decode_stage1 + tq_decode_stage2 on a workspace holding garbage give
+    what tq_decode_attention gives (the same two launches), within the oracle
+    bar, including sequences of length 0."""
+    w = _small(preset, [0, 1, 37, 300, 16, 1000, 0, 129], Hq=8, Hk=2, bs=16, seed=90 + S)
+    G.log(f"split entry points {preset} S={S} lens={w.lens}")
+    c = G.DecodeCase(w)
+    import torch
+
+    cache = torch.from_numpy(c.cache_o).cuda()
+    out2, lse2 = c.gpu_decode_two_stage(cache, S, workspace_fill=0x7F)
+    out1, lse1 = c.gpu_decode(cache, S)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out2, lse2, ref, rlse, _rows(w))
+    np.testing.assert_array_equal(out1, out2)
+    np.testing.assert_array_equal(lse1, lse2)
