@@ -307,6 +307,51 @@ def calibrate_copy(torch, mib: int = 512, reps: int = 5):
     print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}))
 
 
+DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS = 131072, 8, 128
+
+
+def dequant_sweep(torch, tq, reps):
+    """Cached prefix back to dense fp16 K/V (tq_dequant_kv): one sequence of
+    131072 tokens x 8 KV heads in 128-token blocks (the long-context shape),
+    per preset.  Bytes = slots read + 2 x 128 fp16 written per (token, head);
+    3 cache copies rotate so no launch finds its input in the 256 MB MALL."""
+    n, Hk, bs = DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS
+    nb = n // bs
+    g = torch.Generator(device="cuda").manual_seed(21)
+    K = torch.randn((n, Hk, 128), device="cuda", generator=g).to(torch.bfloat16)
+    V = torch.randn((n, Hk, 128), device="cuda", generator=g).to(torch.bfloat16)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(22)).to(torch.int32)
+    table = perm.cuda()
+    slots = (perm.to(torch.int64).repeat_interleave(bs) * bs + torch.arange(bs).repeat(nb)).cuda()
+    ko = torch.empty((n, Hk, 128), dtype=torch.float16, device="cuda")
+    vo = torch.empty_like(ko)
+    res = {}
+    for preset in ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
+        lay = tq.layout_init(preset)
+        tab = tq.Tables(lay, W.signs(21))
+        caches = [torch.zeros(tq.kv_cache_shape(lay, nb, bs, Hk), dtype=torch.uint8, device="cuda")
+                  for _ in range(N_COPIES)]
+        for c in caches:
+            tq.store(lay, K, V, slots, c, tab.signs, tab.centroids, tab.boundaries)
+        for i in range(N_COPIES):
+            tq.dequant_kv(lay, caches[i], table, n, tab.signs, tab.centroids, key_out=ko, value_out=vo)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            tq.dequant_kv(lay, caches[i % N_COPIES], table, n, tab.signs, tab.centroids, key_out=ko, value_out=vo)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n * Hk * (lay.slot_size_aligned + 2 * 128 * 2)
+        res[preset] = {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                       "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+                       "mtok_s": n / (ms * 1e-3) / 1e6}
+        del caches
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +408,8 @@ def main():
             torch.cuda.empty_cache()
         extra["store_sweep"] = store_sweep(torch, tq, 50)
         log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items()})}")
+        extra["dequant"] = dequant_sweep(torch, tq, 20)
+        log(f"[dequant] {json.dumps({k: round(v['gbs']) for k, v in extra['dequant'].items()})} GB/s")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     line = {

@@ -237,6 +237,39 @@ int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32
                      const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
                      void* stream);
 
+/* Dequantize the cached prefix of one sequence back to dense K and V in the
+ * original space, the first step of a continuation prefill ([API]
+ * _continuation_prefill: the cached K/V are dequantized, MSE keys rotated
+ * back, then attention runs over cached + new tokens).  For tokens
+ * t < num_tokens (token t in block block_table[t / block_size] at offset
+ * t % block_size) and KV heads h:
+ *   MSE keys: k = s .* (H (gamma c[code])) / sqrt(D), the transpose of the
+ *             store's rotation applied to the dequantized rotated key;
+ *   FP8 keys: the E4M3 values;
+ *   values:   zero + scale * code (stored fp16 scale and zero).
+ * Computed in fp32 and rounded to nearest even in out_dtype.
+ * Arguments:
+ *   kv_cache      device bytes written by tq_store (same layout, block_size).
+ *   block_table   device int32 [ceil(num_tokens / block_size)], entries < num_blocks.
+ *   num_tokens    >= 0; 0 returns TQ_OK with no launch.
+ *   signs, centroids  as for tq_store (MSE presets; may be NULL for FP8 keys).
+ *   key_out, value_out  device, row (t, h) at element t*out_tok_stride + h*head_dim,
+ *                 dtype out_dtype (TQ_F16 | TQ_BF16 | TQ_F32), 16-byte aligned;
+ *                 out_tok_stride >= num_kv_heads * head_dim and a multiple of 8,
+ *                 so the rows can land in a larger [tokens, Hk, D] buffer.  Only
+ *                 the rows written are touched.
+ * Supported: head_dim 128, block_size 16/32/64/128, num_tokens * num_kv_heads < 2^31. */
+int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
+                  const float* centroids, void* key_out, void* value_out, int32_t out_dtype, int64_t out_tok_stride,
+                  void* stream);
+
+/* Host-only check of tq_dequant_kv's arguments. */
+int tq_dequant_validate(const tq_layout* layout, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
+                        const float* centroids, const void* key_out, const void* value_out, int32_t out_dtype,
+                        int64_t out_tok_stride);
+
 #ifdef __cplusplus
 }
 #endif

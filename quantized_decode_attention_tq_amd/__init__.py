@@ -29,7 +29,8 @@ PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turbo
 #: every symbol include/tq.h declares
 ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init", "tq_kv_cache_shape",
                "tq_lloyd_max", "tq_wht_signs", "tq_decode_workspace_bytes", "tq_store", "tq_store_validate",
-               "tq_decode_attention", "tq_decode_validate", "tq_decode_stage1", "tq_decode_stage2")
+               "tq_decode_attention", "tq_decode_validate", "tq_decode_stage1", "tq_decode_stage2",
+               "tq_dequant_kv", "tq_dequant_validate")
 
 
 class TQError(RuntimeError):
@@ -84,6 +85,8 @@ def _load():
         "tq_decode_stage1": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp, fp, i32, vp,
                                             sz, vp]),
         "tq_decode_stage2": (ctypes.c_int, [i32, i32, i32, i32, vp, sz, vp, i32, vp, vp]),
+        "tq_dequant_kv": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64, vp]),
+        "tq_dequant_validate": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -245,6 +248,33 @@ def decode_stage2(batch: int, num_q_heads: int, head_dim: int, num_kv_splits: in
     _check(_lib.tq_decode_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), out.data_ptr(), _dt(out), _ptr(lse),
                                  _stream(stream, out.device)), "tq_decode_stage2")
+
+
+def dequant_kv(layout: Layout, kv_cache, block_table, num_tokens: int, signs=None, centroids=None, key_out=None,
+               value_out=None, out_dtype=None, stream=None):
+    """Cached prefix of one sequence back to dense (num_tokens, Hk, D) K and V
+    in the original space; returns (key_out, value_out).  block_table: int32
+    (ceil(num_tokens / block_size),) block ids of the sequence.  The outputs
+    may be row slices of larger (tokens, Hk, D) buffers (same token stride,
+    last two dims contiguous); they are allocated with torch when not given."""
+    torch = _torch()
+    Hk = kv_cache.shape[2]
+    D = layout.head_dim
+    dt = out_dtype or torch.float16
+    if key_out is None:
+        key_out = torch.empty((num_tokens, Hk, D), dtype=dt, device=kv_cache.device)
+    if value_out is None:
+        value_out = torch.empty((num_tokens, Hk, D), dtype=dt, device=kv_cache.device)
+    for t in (key_out, value_out):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != D or t.shape[0] < num_tokens:
+            raise TQError(TQ_EINVAL, "dequant_kv: outputs must be (tokens, Hk, D) with contiguous heads")
+    if key_out.stride(0) != value_out.stride(0) or key_out.dtype != value_out.dtype:
+        raise TQError(TQ_EINVAL, "dequant_kv: key_out and value_out must share dtype and token stride")
+    _check(_lib.tq_dequant_kv(ctypes.byref(layout), kv_cache.data_ptr(), kv_cache.shape[0], kv_cache.shape[1], Hk,
+                              block_table.data_ptr(), int(num_tokens), _ptr(signs), _ptr(centroids),
+                              key_out.data_ptr(), value_out.data_ptr(), _dt(key_out), key_out.stride(0),
+                              _stream(stream, kv_cache.device)), "tq_dequant_kv")
+    return key_out, value_out
 
 
 class Tables:

@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 
-LIB_SOURCES = ["tq_host.cpp", "tq_store.hip", "tq_decode.hip"]
+LIB_SOURCES = ["tq_host.cpp", "tq_store.hip", "tq_decode.hip", "tq_dequant.hip"]
 PROBE_SOURCES = ["tests/tq_probe.hip"]
 ARCH = "gfx950"
 

@@ -1,0 +1,220 @@
+// tq_dequant_kv: the cached prefix of one sequence back to dense K/V in the
+// original space, the first step of a continuation prefill ([API]
+// _continuation_prefill: dequantize the cached K/V, inverse-rotate MSE keys,
+// then attend over cached + new tokens).
+//
+// Work mapping as in the store (gfx950, wave64): a "row" is one (token, KV
+// head) slot, 8 lanes per row, 16 consecutive coordinates per lane, 8 rows
+// per wave.  MSE keys: the lane looks up gamma * c[code] for its 16 rotated
+// coordinates and applies the rotation's transpose in registers, s .* (H y)
+// / sqrt(D) (H symmetric, H H = D I), with the store's butterflies.  FP8 keys
+// and the values decode lane-locally.  Each lane writes its 16 outputs of K
+// and of V as 16-byte vector stores, so a row's 8 lanes write one contiguous
+// run.  HBM-bound: slot bytes in, 2 * 128 elements out per slot.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "tq.h"
+#include "tq_internal.h"
+#include "tq_wht.h"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kDpl = tq::kWhtPerLane;  // coordinates per lane
+constexpr int kRowsPerWave = 8;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
+
+struct DequantArgs {
+  const uint8_t* cache;
+  const int32_t* block_table;
+  const float* signs;
+  const float* centroids;
+  void* key_out;
+  void* value_out;
+  int64_t out_tok_stride;  // elements between consecutive tokens of the outputs
+  int32_t num_rows;        // num_tokens * num_kv_heads (< 2^31)
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t slot_bytes;  // slot_size_aligned
+};
+
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+
+// n bytes (n even, <= 16) from a 2-byte aligned address, LSB-first into words.
+template <int N>
+__device__ __forceinline__ void ld_bytes(const uint8_t* p, uint32_t w[(N + 3) / 4]) {
+#pragma unroll
+  for (int i = 0; i < (N + 3) / 4; ++i) w[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) w[i / 2] |= ld_u16(p + 2 * i) << (16 * (i % 2));
+}
+
+// B-bit field i of an LSB-first bit stream held in words.
+template <int B>
+__device__ __forceinline__ uint32_t field(const uint32_t* w, int i) {
+  const int p = B * i, k = p >> 5, s = p & 31;
+  uint32_t v = w[k] >> s;
+  if (s + B > 32) v |= w[k + 1] << (32 - s);
+  return v & ((1u << B) - 1u);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// 16 consecutive outputs of one lane, rounded to the output type.
+template <int OUT>
+__device__ __forceinline__ void store16(void* base, int64_t elem, const float x[kDpl]) {
+  if constexpr (OUT == TQ_F32) {
+    float4* q = reinterpret_cast<float4*>(static_cast<float*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t lo, hi;
+      if constexpr (OUT == TQ_F16) {
+        lo = __half_as_ushort(__float2half_rn(x[2 * i]));
+        hi = __half_as_ushort(__float2half_rn(x[2 * i + 1]));
+      } else {
+        lo = f32_to_bf16_rne(x[2 * i]);
+        hi = f32_to_bf16_rne(x[2 * i + 1]);
+      }
+      h[i] = lo | (hi << 16);
+    }
+    uint4* q = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + elem);
+    q[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    q[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  }
+}
+
+template <int KEY_FP8, int KB, int VB, int OUT>
+__global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
+  constexpr int kL = 1 << KB;
+  __shared__ float cent[KEY_FP8 ? 1 : kL];
+  if (!KEY_FP8) {
+    if (threadIdx.x < kL) cent[threadIdx.x] = a.centroids[threadIdx.x];
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 7;
+  const uint32_t row0 = (blockIdx.x * kWaves + wave) * kRowsPerWave + (lane >> 3);
+  const bool active = row0 < static_cast<uint32_t>(a.num_rows);
+  const uint32_t row = active ? row0 : a.num_rows - 1;  // inactive rows decode a valid row, write nothing
+  const uint32_t t = row / static_cast<uint32_t>(a.num_kv_heads);
+  const int h = static_cast<int>(row - t * a.num_kv_heads);
+  const int64_t blk = a.block_table[t / static_cast<uint32_t>(a.block_size)];
+  const int64_t pos = blk * a.block_size + t % static_cast<uint32_t>(a.block_size);
+  const uint8_t* slot = a.cache + (pos * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes);
+
+  // ---------------- key ----------------
+  float k[kDpl];
+  if (KEY_FP8) {
+    uint32_t w[4];
+    ld_bytes<16>(slot + kDpl * sub, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // bytes 2, 3
+      k[4 * i] = lo[0];
+      k[4 * i + 1] = lo[1];
+      k[4 * i + 2] = hi[0];
+      k[4 * i + 3] = hi[1];
+    }
+  } else {
+    constexpr int kKeyBytes = kDpl * KB / 8;  // 8 (4-bit) or 6 (3-bit) per lane
+    constexpr int kKdata = kD * KB / 8;
+    uint32_t w[(kKeyBytes + 3) / 4 + 1];
+    w[(kKeyBytes + 3) / 4] = 0u;
+    ld_bytes<kKeyBytes>(slot + kKeyBytes * sub, w);
+    const float gamma = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKdata))));
+    // rotated coordinates, then H y with the store's butterflies
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) k[i] = gamma * cent[field<KB>(w, i)];
+    tq::wht_inlane(k, 1);
+    tq::wht_crosslane(k, sub);
+    // s .* (H y) / sqrt(D), undoing the lane sign the cross-lane strides leave
+    const float c = tq::wht_lane_negated(sub) ? -0.08838834764831845f : 0.08838834764831845f;
+    const float4* sg = reinterpret_cast<const float4*>(a.signs + kDpl * sub);
+#pragma unroll
+    for (int i = 0; i < kDpl / 4; ++i) {
+      const float4 s4 = sg[i];
+      k[4 * i] *= s4.x * c;
+      k[4 * i + 1] *= s4.y * c;
+      k[4 * i + 2] *= s4.z * c;
+      k[4 * i + 3] *= s4.w * c;
+    }
+  }
+
+  // ---------------- value ----------------
+  constexpr int kKps = KEY_FP8 ? kD : kD * KB / 8 + 2;
+  constexpr int kValBytes = kDpl * VB / 8;
+  constexpr int kVdata = kD * VB / 8;
+  float v[kDpl];
+  {
+    uint32_t w[(kValBytes + 3) / 4 + 1];
+    w[(kValBytes + 3) / 4] = 0u;
+    ld_bytes<kValBytes>(slot + kKps + kValBytes * sub, w);
+    const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKps + kVdata))));
+    const float z = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKps + kVdata + 2))));
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) v[i] = fmaf(sc, static_cast<float>(field<VB>(w, i)), z);  // exact product
+  }
+
+  if (active) {
+    const int64_t e = static_cast<int64_t>(t) * a.out_tok_stride + h * kD + kDpl * sub;
+    store16<OUT>(a.key_out, e, k);
+    store16<OUT>(a.value_out, e, v);
+  }
+}
+
+template <int KEY_FP8, int KB, int VB>
+int launch_dequant(const DequantArgs& a, int32_t out_dtype, hipStream_t stream) {
+  const int blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  DequantArgs arg = a;
+  void* args[] = {&arg};
+  const void* fn = out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_F32>)
+                   : out_dtype == TQ_F16 ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_F16>)
+                                         : reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_BF16>);
+  return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
+}
+
+}  // namespace
+
+extern "C" int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                             int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
+                             const float* centroids, void* key_out, void* value_out, int32_t out_dtype,
+                             int64_t out_tok_stride, void* stream) {
+  int st = tq::validate_dequant(layout, kv_cache, num_blocks, block_size, num_kv_heads, block_table, num_tokens, signs,
+                                centroids, key_out, value_out, out_dtype, out_tok_stride);
+  if (st != TQ_OK || num_tokens == 0) return st;
+  DequantArgs a;
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.signs = signs;
+  a.centroids = centroids;
+  a.key_out = key_out;
+  a.value_out = value_out;
+  a.out_tok_stride = out_tok_stride;
+  a.num_rows = num_tokens * num_kv_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.slot_bytes = layout->slot_size_aligned;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (layout->preset) {
+    case TQ_K8V4: return launch_dequant<1, 8, 4>(a, out_dtype, s);
+    case TQ_4BIT_NC: return launch_dequant<0, 4, 4>(a, out_dtype, s);
+    case TQ_K3V4_NC: return launch_dequant<0, 3, 4>(a, out_dtype, s);
+    case TQ_3BIT_NC: return launch_dequant<0, 3, 3>(a, out_dtype, s);
+  }
+  return TQ_EPRESET;
+}

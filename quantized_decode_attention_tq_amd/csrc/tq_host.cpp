@@ -326,7 +326,35 @@ int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_
   return TQ_OK;
 }
 
+int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                     int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
+                     const float* centroids, const void* key_out, const void* value_out, int32_t out_dtype,
+                     int64_t out_tok_stride) {
+  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset > 3) ? TQ_EPRESET : TQ_EINVAL;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return TQ_EINVAL;
+  if (!block_size_ok(block_size)) return TQ_EBLOCK;
+  if (out_dtype != TQ_F16 && out_dtype != TQ_BF16 && out_dtype != TQ_F32) return TQ_EDTYPE;
+  if (L->head_dim != 128) return TQ_EHEADDIM;
+  if (num_tokens == 0) return TQ_OK;
+  if (!kv_cache || !block_table || !key_out || !value_out) return TQ_EINVAL;
+  if (!aligned16(kv_cache) || !aligned16(key_out) || !aligned16(value_out) || out_tok_stride % 8 != 0 ||
+      out_tok_stride < static_cast<int64_t>(num_kv_heads) * L->head_dim)
+    return TQ_EINVAL;
+  if (static_cast<int64_t>(num_tokens) * num_kv_heads >= (int64_t{1} << 31)) return TQ_EINVAL;
+  if (static_cast<int64_t>(num_tokens + block_size - 1) / block_size > num_blocks) return TQ_EINVAL;
+  if (!L->key_fp8 && (!signs || !centroids || !aligned16(signs))) return TQ_EINVAL;
+  return TQ_OK;
+}
+
 }  // namespace tq
+
+extern "C" int tq_dequant_validate(const tq_layout* layout, const void* kv_cache, int64_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads, const int32_t* block_table,
+                                   int32_t num_tokens, const float* signs, const float* centroids, const void* key_out,
+                                   const void* value_out, int32_t out_dtype, int64_t out_tok_stride) {
+  return tq::validate_dequant(layout, kv_cache, num_blocks, block_size, num_kv_heads, block_table, num_tokens, signs,
+                              centroids, key_out, value_out, out_dtype, out_tok_stride);
+}
 
 extern "C" int tq_store_validate(const tq_layout* layout, const void* key, const void* value, int32_t in_dtype,
                                  int64_t num_tokens, int32_t num_kv_heads, int64_t key_tok_stride,

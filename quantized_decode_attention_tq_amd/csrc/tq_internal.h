@@ -34,6 +34,11 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
 int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                     const void* workspace, size_t ws_bytes, const void* out, int32_t out_dtype);
 
+int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                     int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
+                     const float* centroids, const void* key_out, const void* value_out, int32_t out_dtype,
+                     int64_t out_tok_stride);
+
 // ---- decode workspace and stage-1 launch plan ----
 //
 // Stage 1 cuts the batch into U "units" of work: the tiles (16 tokens) of

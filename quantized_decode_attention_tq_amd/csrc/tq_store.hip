@@ -16,8 +16,11 @@
 #include "tq.h"
 #include "tq_bits.h"
 #include "tq_internal.h"
+#include "tq_wht.h"
 
 namespace {
+
+using tq::xor_shfl;
 
 constexpr int kD = 128;
 constexpr int kDpl = 16;           // dims per lane
@@ -41,22 +44,6 @@ struct StoreArgs {
   int32_t num_kv_heads;
   int32_t slot_bytes;  // slot_size_aligned
 };
-
-// Value of lane (l ^ m) for m = 1, 2, 4 (within each 8-lane row group), by
-// DPP lane moves: no LDS round trip.  xor 1 / xor 2 are quad permutes; xor 4
-// is the quad reversal (l ^ 3) followed by the half-row mirror (l ^ 7).
-__device__ __forceinline__ float xor_shfl(float v, int m) {
-  int x = __float_as_int(v);
-  if (m == 1) {
-    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
-  } else if (m == 2) {
-    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
-  } else {
-    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);   // quad_perm [3, 2, 1, 0]
-    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror
-  }
-  return __int_as_float(x);
-}
 
 // 16 consecutive bf16 / fp16 elements -> fp32
 template <int BF16>
@@ -209,34 +196,13 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
       y[4 * i + 2] = fmaf(x[4 * i + 2], s4.z, q1);
       y[4 * i + 3] = fmaf(x[4 * i + 2], s4.z, -q1);
     }
-#pragma unroll
-    for (int hs = 2; hs < kDpl; hs <<= 1) {
-#pragma unroll
-      for (int i = 0; i < kDpl; ++i) {
-        if ((i & hs) == 0) {
-          float p = y[i], q = y[i + hs];
-          y[i] = p + q;
-          y[i + hs] = p - q;
-        }
-      }
-    }
-    // Strides 16, 32, 64 pair lane l with lane l ^ msk of the row's 8 lanes:
-    // the lower lane of a pair takes p + q, the upper one p - q.  Each lane
-    // keeps its coordinates times a lane sign sigma (equal on both lanes of a
-    // pair before the stride): w <- w + e * w_partner with e = -1 on the upper
-    // lane and +1 on the lower one gives sigma*(p+q) on the lower lane and
-    // -sigma*(p-q) on the upper one, so each stride is one fma per value and
-    // flips sigma on the upper lanes.  After the three strides
-    // sigma = (-1)^popcount(sub); it is folded into the scale below.
-#pragma unroll
-    for (int msk = 1; msk < 8; msk <<= 1) {
-      const float e = (sub & msk) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < kDpl; ++i) y[i] = fmaf(xor_shfl(y[i], msk), e, y[i]);
-    }
+    tq::wht_inlane(y, 2);
+    // strides 16, 32, 64 across the row's lanes; the lane sign they leave is
+    // folded into the scale below
+    tq::wht_crosslane(y, sub);
     // u = (H s.*x) / (sqrt(D) * nu); nu == 0 gives u = 0 and a zero norm field
     const float inv0 = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
-    const float inv = (__builtin_popcount(sub) & 1) ? -inv0 : inv0;
+    const float inv = tq::wht_lane_negated(sub) ? -inv0 : inv0;
     float cs = 0.f;
     Pack32<KB> kp;
 #pragma unroll

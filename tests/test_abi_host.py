@@ -164,3 +164,31 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read().split("\n")
     paths = {l.split()[-1] for l in maps if "libamdhip64" in l and "/" in l}
     assert len({os.path.realpath(p) for p in paths}) == 1, paths
+
+
+def _dequant_validate(L, **kw):
+    args = dict(cache=A, nb=10, bs=16, Hk=8, bt=A, n=100, signs=A, cent=A, ko=A, vo=A, od=tq.TQ_F16, stride=1024)
+    args.update(kw)
+    return tq._lib.tq_dequant_validate(ctypes.byref(L), args["cache"], args["nb"], args["bs"], args["Hk"], args["bt"],
+                                       args["n"], args["signs"], args["cent"], args["ko"], args["vo"], args["od"],
+                                       args["stride"])
+
+
+def test_dequant_validation_codes():
+    L = tq.layout_init("turboquant_k3v4_nc")
+    assert _dequant_validate(L) == tq.TQ_OK
+    assert _dequant_validate(L, n=0, cache=None, bt=None, ko=None, vo=None) == tq.TQ_OK  # empty prefix: no-op
+    assert _dequant_validate(L, bs=8) == tq.TQ_EBLOCK
+    assert _dequant_validate(L, od=7) == tq.TQ_EDTYPE
+    assert _dequant_validate(L, od=tq.TQ_F32) == tq.TQ_OK
+    assert _dequant_validate(L, n=-1) == tq.TQ_EINVAL
+    assert _dequant_validate(L, Hk=0) == tq.TQ_EINVAL
+    assert _dequant_validate(L, ko=A + 8) == tq.TQ_EINVAL  # misaligned output
+    assert _dequant_validate(L, stride=1020) == tq.TQ_EINVAL  # token stride below Hk * D
+    assert _dequant_validate(L, stride=1028) == tq.TQ_EINVAL  # not a multiple of 8 elements
+    assert _dequant_validate(L, stride=2048) == tq.TQ_OK  # rows inside a larger buffer
+    assert _dequant_validate(L, n=161) == tq.TQ_EINVAL  # needs 11 blocks, 10 exist
+    assert _dequant_validate(L, signs=None) == tq.TQ_EINVAL
+    assert _dequant_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None) == tq.TQ_OK
+    assert _dequant_validate(tq.layout_init("turboquant_k3v4_nc", 64)) == tq.TQ_EHEADDIM
+    assert _dequant_validate(L, n=1 << 28, nb=1 << 30) == tq.TQ_EINVAL  # rows beyond 2^31

@@ -537,3 +537,49 @@ def test_row_vectorized_decode_equals_per_slot_decode(preset):
         ki, vi = O.decode_slot(lay, slots[i], c32)
         np.testing.assert_array_equal(K[i], ki)
         np.testing.assert_array_equal(V[i], vi)
+
+
+# ------------------------------------------------------- dequant (original space)
+# Mean squared error of the Lloyd-Max quantizer for a unit Gaussian, from
+# J. Max, "Quantizing for minimum distortion" (1960), table of optimum
+# quantizers: N = 8 and N = 16 levels.
+MAX_GAUSSIAN_DISTORTION = {3: 0.03454, 4: 0.009497}
+
+
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
+def test_dequant_original_space_error_matches_lloyd_max_distortion(preset):
+    """Store then dequantize back to the original space: after the randomized
+    Hadamard rotation the coordinates are near-Gaussian ([TQ+] "Background":
+    why the sign vector matters), so the relative key error averages out at
+    the Gaussian Lloyd-Max distortion of the key bit width.  Applying the
+    rotation instead of its transpose, or dropping the signs, gives about 2.
+    Values: the uniform quantizer's error bound (half a step plus the zero
+    point's fp16 rounding)."""
+    rng = np.random.default_rng(5)
+    lay = O.layout(preset, D)
+    c32, b32 = O.codebook_tables(D, lay.key_bits)
+    s = O.wht_signs(D, 3)
+    N, bs = 400, 16
+    K = O.widen(W.to_bits(rng.standard_normal((N, 1, D)) * np.exp(0.3 * rng.standard_normal((1, 1, D))), "bf16"),
+                "bf16")
+    V = O.widen(W.to_bits(rng.standard_normal((N, 1, D)), "bf16"), "bf16")
+    cache = np.zeros((N // bs, bs, 1, lay.slot_size_aligned), np.uint8)
+    O.store_rows(lay, K, V, np.arange(N), cache, s, c32, b32)
+    Kd, Vd = O.dequant_original_space(lay, cache, np.arange(N // bs), N, 0, s, c32)
+    k, v = K[:, 0], V[:, 0]
+    rel = np.sum((k - Kd) ** 2, axis=1) / np.sum(k ** 2, axis=1)
+    ratio = rel.mean() / MAX_GAUSSIAN_DISTORTION[lay.key_bits]
+    assert 0.85 < ratio < 1.1, ratio
+    levels = (1 << lay.value_bits) - 1
+    step = np.float16((v.max(1) - v.min(1)).astype(np.float32) / np.float32(levels)).astype(np.float64)
+    zerr = np.abs(np.float16(v.min(1)).astype(np.float64) - v.min(1))
+    assert np.all(np.abs(v - Vd) <= (0.5 * step + zerr)[:, None] * (1 + 1e-6) + 1e-12)
+
+
+def test_dequant_original_space_fp8_keys_are_the_e4m3_values():
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache("turboquant_k8v4", lens=(37, 5))
+    for b, L in enumerate(lens):
+        for h in range(cache.shape[2]):
+            Kd, _ = O.dequant_original_space(lay, cache, table[b], int(L), h, s, c32)
+            want = O.fp8_e4m3fn_decode(O.fp8_e4m3fn_encode(K[b][:, h]))
+            np.testing.assert_array_equal(Kd, want)
