@@ -62,14 +62,13 @@ __device__ __forceinline__ uint32_t field(const uint32_t* w, int i) {
   return v & ((1u << B) - 1u);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// 16 consecutive outputs of one lane, rounded to the output type.
+// 16 consecutive outputs of one lane, rounded to nearest even in the output
+// type (pairs through the packed converts, v_cvt_pk_f16_f32 /
+// v_cvt_pk_bf16_f32).
 template <int OUT>
 __device__ __forceinline__ void store16(void* base, int64_t elem, const float x[kDpl]) {
   if constexpr (OUT == TQ_F32) {
@@ -80,15 +79,11 @@ __device__ __forceinline__ void store16(void* base, int64_t elem, const float x[
     uint32_t h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t lo, hi;
-      if constexpr (OUT == TQ_F16) {
-        lo = __half_as_ushort(__float2half_rn(x[2 * i]));
-        hi = __half_as_ushort(__float2half_rn(x[2 * i + 1]));
-      } else {
-        lo = f32_to_bf16_rne(x[2 * i]);
-        hi = f32_to_bf16_rne(x[2 * i + 1]);
-      }
-      h[i] = lo | (hi << 16);
+      const f32x2 p = {x[2 * i], x[2 * i + 1]};
+      if constexpr (OUT == TQ_F16)
+        h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+      else
+        h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
     }
     uint4* q = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + elem);
     q[0] = make_uint4(h[0], h[1], h[2], h[3]);
@@ -96,8 +91,41 @@ __device__ __forceinline__ void store16(void* base, int64_t elem, const float x[
   }
 }
 
+// Raw fields of one slot for this lane: its key bytes (or FP8 key bytes),
+// the key norm, its value-code bytes, the value scale and zero.
+template <int KEY_FP8, int KB, int VB>
+struct SlotFields {
+  static constexpr int kKeyBytes = KEY_FP8 ? kDpl : kDpl * KB / 8;
+  static constexpr int kValBytes = kDpl * VB / 8;
+  uint32_t kw[(kKeyBytes + 3) / 4 + 1];
+  uint32_t vw[(kValBytes + 3) / 4 + 1];
+  uint32_t gamma, scale_zero;
+};
+
+template <int KEY_FP8, int KB, int VB>
+__device__ __forceinline__ void load_fields(const uint8_t* slot, int sub, SlotFields<KEY_FP8, KB, VB>& f) {
+  using F = SlotFields<KEY_FP8, KB, VB>;
+  constexpr int kKdata = KEY_FP8 ? kD : kD * KB / 8;
+  constexpr int kKps = KEY_FP8 ? kD : kKdata + 2;
+  constexpr int kVdata = kD * VB / 8;
+  f.kw[(F::kKeyBytes + 3) / 4] = 0u;
+  f.vw[(F::kValBytes + 3) / 4] = 0u;
+  ld_bytes<F::kKeyBytes>(slot + F::kKeyBytes * sub, f.kw);
+  ld_bytes<F::kValBytes>(slot + kKps + F::kValBytes * sub, f.vw);
+  f.gamma = KEY_FP8 ? 0u : ld_u16(slot + kKdata);
+  f.scale_zero = ld_u16(slot + kKps + kVdata) | (ld_u16(slot + kKps + kVdata + 2) << 16);
+}
+
+// Each wave takes kGroups groups of 8 consecutive rows (a group: 8 lanes per
+// row); the loads of all its groups are issued before any is decoded, so a
+// wave keeps several slots' worth of reads in flight.  The MSE presets, with
+// more arithmetic per slot, take 4; FP8 keys keep 1 and more waves resident.
+template <int KEY_FP8>
+constexpr int groups_per_wave() { return KEY_FP8 ? 1 : 4; }
+
 template <int KEY_FP8, int KB, int VB, int OUT>
 __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
+  constexpr int kGroups = groups_per_wave<KEY_FP8>();
   constexpr int kL = 1 << KB;
   __shared__ float cent[KEY_FP8 ? 1 : kL];
   if (!KEY_FP8) {
@@ -107,79 +135,83 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane & 7;
-  const uint32_t row0 = (blockIdx.x * kWaves + wave) * kRowsPerWave + (lane >> 3);
-  const bool active = row0 < static_cast<uint32_t>(a.num_rows);
-  const uint32_t row = active ? row0 : a.num_rows - 1;  // inactive rows decode a valid row, write nothing
-  const uint32_t t = row / static_cast<uint32_t>(a.num_kv_heads);
-  const int h = static_cast<int>(row - t * a.num_kv_heads);
-  const int64_t blk = a.block_table[t / static_cast<uint32_t>(a.block_size)];
-  const int64_t pos = blk * a.block_size + t % static_cast<uint32_t>(a.block_size);
-  const uint8_t* slot = a.cache + (pos * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes);
+  const uint32_t base = (blockIdx.x * kWaves + wave) * (kRowsPerWave * kGroups) + (lane >> 3);
 
-  // ---------------- key ----------------
-  float k[kDpl];
-  if (KEY_FP8) {
-    uint32_t w[4];
-    ld_bytes<16>(slot + kDpl * sub, w);
+  SlotFields<KEY_FP8, KB, VB> f[kGroups];
+  uint32_t rows[kGroups];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // bytes 0, 1
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // bytes 2, 3
-      k[4 * i] = lo[0];
-      k[4 * i + 1] = lo[1];
-      k[4 * i + 2] = hi[0];
-      k[4 * i + 3] = hi[1];
-    }
-  } else {
-    constexpr int kKeyBytes = kDpl * KB / 8;  // 8 (4-bit) or 6 (3-bit) per lane
-    constexpr int kKdata = kD * KB / 8;
-    uint32_t w[(kKeyBytes + 3) / 4 + 1];
-    w[(kKeyBytes + 3) / 4] = 0u;
-    ld_bytes<kKeyBytes>(slot + kKeyBytes * sub, w);
-    const float gamma = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKdata))));
-    // rotated coordinates, then H y with the store's butterflies
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) k[i] = gamma * cent[field<KB>(w, i)];
-    tq::wht_inlane(k, 1);
-    tq::wht_crosslane(k, sub);
-    // s .* (H y) / sqrt(D), undoing the lane sign the cross-lane strides leave
+  for (int g = 0; g < kGroups; ++g) {
+    const uint32_t row0 = base + g * kRowsPerWave;
+    const uint32_t row = row0 < static_cast<uint32_t>(a.num_rows) ? row0 : a.num_rows - 1;  // in bounds
+    rows[g] = row0;
+    const uint32_t t = row / static_cast<uint32_t>(a.num_kv_heads);
+    const int h = static_cast<int>(row - t * a.num_kv_heads);
+    const int64_t blk = a.block_table[t / static_cast<uint32_t>(a.block_size)];
+    const int64_t pos = blk * a.block_size + t % static_cast<uint32_t>(a.block_size);
+    load_fields<KEY_FP8, KB, VB>(a.cache + (pos * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes), sub,
+                                 f[g]);
+  }
+
+  float sg[kDpl];  // signs * (+-1/sqrt(D)), the lane sign of the butterflies undone
+  if (!KEY_FP8) {
     const float c = tq::wht_lane_negated(sub) ? -0.08838834764831845f : 0.08838834764831845f;
-    const float4* sg = reinterpret_cast<const float4*>(a.signs + kDpl * sub);
+    const float4* sp = reinterpret_cast<const float4*>(a.signs + kDpl * sub);
 #pragma unroll
     for (int i = 0; i < kDpl / 4; ++i) {
-      const float4 s4 = sg[i];
-      k[4 * i] *= s4.x * c;
-      k[4 * i + 1] *= s4.y * c;
-      k[4 * i + 2] *= s4.z * c;
-      k[4 * i + 3] *= s4.w * c;
+      const float4 s4 = sp[i];
+      sg[4 * i] = s4.x * c;
+      sg[4 * i + 1] = s4.y * c;
+      sg[4 * i + 2] = s4.z * c;
+      sg[4 * i + 3] = s4.w * c;
     }
   }
 
-  // ---------------- value ----------------
-  constexpr int kKps = KEY_FP8 ? kD : kD * KB / 8 + 2;
-  constexpr int kValBytes = kDpl * VB / 8;
-  constexpr int kVdata = kD * VB / 8;
-  float v[kDpl];
-  {
-    uint32_t w[(kValBytes + 3) / 4 + 1];
-    w[(kValBytes + 3) / 4] = 0u;
-    ld_bytes<kValBytes>(slot + kKps + kValBytes * sub, w);
-    const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKps + kVdata))));
-    const float z = __half2float(__ushort_as_half(static_cast<unsigned short>(ld_u16(slot + kKps + kVdata + 2))));
 #pragma unroll
-    for (int i = 0; i < kDpl; ++i) v[i] = fmaf(sc, static_cast<float>(field<VB>(w, i)), z);  // exact product
-  }
+  for (int g = 0; g < kGroups; ++g) {
+    // ---------------- key ----------------
+    float k[kDpl];
+    if (KEY_FP8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(f[g].kw[i], false);  // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(f[g].kw[i], true);   // bytes 2, 3
+        k[4 * i] = lo[0];
+        k[4 * i + 1] = lo[1];
+        k[4 * i + 2] = hi[0];
+        k[4 * i + 3] = hi[1];
+      }
+    } else {
+      // rotated coordinates gamma * c[code], then s .* (H y) / sqrt(D) with the
+      // store's butterflies
+      const float gamma = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].gamma)));
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) k[i] = gamma * cent[field<KB>(f[g].kw, i)];
+      tq::wht_inlane(k, 1);
+      tq::wht_crosslane(k, sub);
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) k[i] *= sg[i];
+    }
+    // ---------------- value ----------------
+    float v[kDpl];
+    const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero & 0xFFFFu)));
+    const float z = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero >> 16)));
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) v[i] = fmaf(sc, static_cast<float>(field<VB>(f[g].vw, i)), z);  // exact product
 
-  if (active) {
-    const int64_t e = static_cast<int64_t>(t) * a.out_tok_stride + h * kD + kDpl * sub;
-    store16<OUT>(a.key_out, e, k);
-    store16<OUT>(a.value_out, e, v);
+    if (rows[g] < static_cast<uint32_t>(a.num_rows)) {
+      const uint32_t t = rows[g] / static_cast<uint32_t>(a.num_kv_heads);
+      const int h = static_cast<int>(rows[g] - t * a.num_kv_heads);
+      const int64_t e = static_cast<int64_t>(t) * a.out_tok_stride + h * kD + kDpl * sub;
+      store16<OUT>(a.key_out, e, k);
+      store16<OUT>(a.value_out, e, v);
+    }
   }
 }
 
 template <int KEY_FP8, int KB, int VB>
 int launch_dequant(const DequantArgs& a, int32_t out_dtype, hipStream_t stream) {
-  const int blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t per_block = static_cast<int64_t>(kRowsPerBlock) * groups_per_wave<KEY_FP8>();
+  const int blocks = static_cast<int>((a.num_rows + per_block - 1) / per_block);
   DequantArgs arg = a;
   void* args[] = {&arg};
   const void* fn = out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_F32>)
