@@ -241,6 +241,59 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
   }
 }
 
+// The key words of the lane (token lane % 16, dims of its quarter).
+template <int P>
+__device__ __forceinline__ void load_keys(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
+  using T = Preset<P>;
+  if constexpr (T::kFp8 != 0) {
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
+    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
+  } else {
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+    if (T::kKb == 4) r.k[4] = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
+  }
+}
+
+// The per-token fields of the lane's 4 tokens (4q .. 4q+3): value scale and
+// zero, and the key norm (MSE keys).
+template <int P>
+__device__ __forceinline__ void load_token_fields(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
+  using T = Preset<P>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* m = tb + o.mo[i];
+    if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
+      r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
+    } else {
+      // 2 mod 4 for half the heads: an aligned pair of dwords, realigned
+      const uint32_t so = o.mo[i] + static_cast<uint32_t>(T::kKps + T::kVdata);
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (so & ~3u));
+      r.sz[i] = tq::alignbyte(w.y, w.x, so & 3u);
+    }
+    if constexpr (T::kFp8 == 0) r.gm[i] = ld16(m + T::kKdata);
+  }
+}
+
+// The value-code words of the lane's 4 tokens (tokens 4q .. 4q+3, dims of
+// lane row), realigned, straight from the tile image.
+template <int P>
+__device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]) {
+  using T = Preset<P>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t vo = o.mo[i] + o.vcol;
+    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
+      vw[i] = *reinterpret_cast<const uint32_t*>(tb + vo);
+    } else {
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
+      vw[i] = tq::alignbyte(w.y, w.x, vo & 3u);
+    }
+  }
+}
+
 // Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q).
 template <int P>
 __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, const tq::Lut8& la,
@@ -409,6 +462,118 @@ __device__ __forceinline__ void accumulate_pair(const PendingTile& a, const Pend
           as_half8(tq::val3_get(a01, n), tq::val3_get(a23, n), tq::val3_get(b01, n), tq::val3_get(b23, n)), bp,
           acc[n], 0, 0, 0);
   }
+}
+
+// Value of lane l ^ 8 (the other half of the lane's row of 16): DPP row_ror:8.
+__device__ __forceinline__ float swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t swap8(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false));
+}
+
+// Two tiles of a super-tile scored as one, for GQA groups of at most 8
+// query heads.  The score MFMA gives each tile a 16 x 16 block whose
+// columns 8..15 carry no query head; tile B's columns 0..7 move into them
+// (lanes 8..15 of each row of 16 take lane l - 8's value, one masked DPP move
+// per value), so one softmax pass over 4 values per lane covers both tiles:
+// lane (row r, column c) holds token 4(l/16)+i of tile A (c < 8) or of tile
+// B (c >= 8) for query head c % 8.  Lanes c and c ^ 8 hold the same head and
+// keep the same running maximum (their maxima are combined); each keeps the
+// sums of its own tile's tokens, added together at the end.  The per-token
+// key norm and value scale/zero come from the lane's own tile: one set of
+// reads for both tiles.  The value MFMA then takes tile A's weights from the
+// lane itself and tile B's from lane c + 8.  Columns 8..15 of the output
+// accumulators hold nothing used.
+template <int P>
+__device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
+                                                  const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4],
+                                                  int validA, int validB, Softmax& sm, f32x4 acc[8]) {
+  using T = Preset<P>;
+  const int lane = threadIdx.x & 63;
+  const bool tileB = (lane & 8) != 0;
+  TileRegs<P> rA, rB, own;
+  load_keys<P>(imgA, o, rA);
+  load_keys<P>(imgB, o, rB);
+  load_token_fields<P>(tileB ? imgB : imgA, o, own);
+  half8 A[4];
+  key_operand<P>(rA, o.ksh, la, lb, A);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], a1, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], a1, 0, 0, 0);
+  key_operand<P>(rB, o.ksh, la, lb, A);
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+  b0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], b0, 0, 0, 0);
+  b1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], b1, 0, 0, 0);
+  b0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], b0, 0, 0, 0);
+  b1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], b1, 0, 0, 0);
+
+  float sco[4], sv[4], zv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sa = a0[i] + a1[i], sb = b0[i] + b1[i];
+    // lanes 8..15 of each row of 16 take tile B's value of lane l - 8
+    const float sc = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(sa), __float_as_int(sb), 0x118, 0xF, 0xC, false));
+    sco[i] = T::kFp8 ? sc : sc * half_bits_to_f32(own.gm[i]);
+    sv[i] = half_bits_to_f32(own.sz[i] & 0xFFFFu);
+    zv[i] = half_bits_to_f32(own.sz[i] >> 16);
+  }
+  const int valid = tileB ? validB : validA;
+  if (__builtin_expect(validA < 16 || validB < 16, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * (lane >> 4) + i >= valid) {
+        sco[i] = -INFINITY;
+        sv[i] = 0.f;
+        zv[i] = 0.f;
+      }
+    }
+  }
+  float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
+  lmax = fmaxf(lmax, swap8(lmax));  // the head's maximum over both tiles
+  float p[4], ps[4];
+  bool redo = __any(lmax > sm.m + kLazyRescaleLog2);
+  if (!redo) {
+    float pmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      ps[i] = p[i] * sv[i];
+      pmax = fmaxf(pmax, ps[i]);
+    }
+    redo = __any(pmax > 65504.f);
+  }
+  if (redo) {  // rescale the accumulators to the new maximum (same on lanes c and c ^ 8)
+    const float m_cand = fmaxf(sm.m, quarter_max(lmax));
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    sm.l *= alpha;
+    sm.z *= alpha;
+    sm.m = m_cand;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      ps[i] = p[i] * sv[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sm.l += p[i];
+    sm.z = fmaf(p[i], zv[i], sm.z);
+  }
+  // value weights: tile A's from this lane, tile B's from lane c + 8
+  half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
+  half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
+  PendingTile ta, tb;
+  ta.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
+  tb.pv = as_half4(swap8(h2_bits(ps01)), swap8(h2_bits(ps23)));
+  load_value_words<P>(imgA, o, ta.vw);
+  load_value_words<P>(imgB, o, tb.vw);
+  accumulate_pair<P>(ta, tb, acc);
 }
 
 // ---- tile staging: cache rows -> LDS ring by direct-to-LDS loads ----
@@ -655,7 +820,7 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // and accumulates tile p of every super-tile from LDS.  At the end the P
 // phase waves of a head merge their partial softmax states through LDS and
 // the phase-0 wave writes the split's partial rows.
-template <int P, int TPW>
+template <int P, int TPW, int PACK>
 __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
@@ -838,6 +1003,17 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
       issue(u + R - 1, entry == 0 ? R - 1 : entry - 1, blk_next);
       blk_next = blocks_of(u + R);
     }
+    if constexpr (PACK != 0) {
+      // the wave's two tiles of the super-tile, scored together
+      const int t = t_begin + u * Q + ph * TPW;
+      if (t < t_end) {
+        const uint8_t* img =
+            tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
+        score_pair_packed<P>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, bq,
+                             min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0, sm,
+                             acc);
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = t_begin + u * Q + ph * TPW + j;
@@ -857,6 +1033,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
         }
       }
     }
+    }
     entry = entry + 1 == R ? 0 : entry + 1;
   }
 
@@ -869,6 +1046,10 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   }
 
   // ---- this wave's normalized partial (output / l, base-2 LSE) ----
+  if (PACK != 0) {  // lanes c and c ^ 8 summed the two tiles of each pair: add them
+    sm.l += swap8(sm.l);
+    sm.z += swap8(sm.z);
+  }
   const float l_run = quarter_sum(sm.l), z_run = quarter_sum(sm.z);
   float o[32];  // o[8 * i + n]: acc[n][i] as output
   {
@@ -1040,25 +1221,30 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int P, int TPW>
+template <int P, int TPW, int PACK>
 int launch_stage1_t(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   });
   if (attr != hipSuccess) return tq::hip_status(attr);
   DecodeArgs arg = a;
   void* args[] = {&arg};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW>),
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK>),
                                         dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
                                         stream));
 }
 
+// Two tiles per wave: GQA groups of at most 8 query heads score them packed
+// into one MFMA block layout; wider groups one at a time.
 template <int P>
 int launch_stage1(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
-  return tpw == 2 ? launch_stage1_t<P, 2>(a, nblocks, lds, stream) : launch_stage1_t<P, 1>(a, nblocks, lds, stream);
+  if (tpw == 2)
+    return a.group <= 8 ? launch_stage1_t<P, 2, 1>(a, nblocks, lds, stream)
+                        : launch_stage1_t<P, 2, 0>(a, nblocks, lds, stream);
+  return launch_stage1_t<P, 1, 0>(a, nblocks, lds, stream);
 }
 
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
