@@ -107,6 +107,21 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t bits) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
 }
 
+// x * (fp16 in the low / high half of w), rounded once to fp32.  Written as an
+// fma with a +0 addend (equal to the product but for the sign of a zero
+// product) so that it becomes one v_fma_mix_f32 reading the half in place
+// instead of a conversion and a multiply.
+__device__ __forceinline__ float mul_lo16(float x, uint32_t w) {
+  return fmaf(x, static_cast<float>(__builtin_bit_cast(half2v, w)[0]), 0.0f);
+}
+__device__ __forceinline__ float mul_hi16(float x, uint32_t w) {
+  return fmaf(x, static_cast<float>(__builtin_bit_cast(half2v, w)[1]), 0.0f);
+}
+// x * (high half of w) + y, rounded once.
+__device__ __forceinline__ float fma_hi16(float x, uint32_t w, float y) {
+  return fmaf(x, static_cast<float>(__builtin_bit_cast(half2v, w)[1]), y);
+}
+
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; remap
 // so that consecutive *logical* ids (the KV heads of one sequence/split,
 // which share cache lines) run on the same XCD and share its L2.
@@ -368,13 +383,14 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
   s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], s0, 0, 0, 0);
   s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], s1, 0, 0, 0);
 
-  float sco[4], sv[4], zv[4];
+  // per token: fp16 value scale (low half) and zero (high half)
+  float sco[4];
+  uint32_t sz[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float sc = s0[i] + s1[i];
-    sco[i] = T::kFp8 ? sc : sc * half_bits_to_f32(r.gm[i]);
-    sv[i] = half_bits_to_f32(r.sz[i] & 0xFFFFu);
-    zv[i] = half_bits_to_f32(r.sz[i] >> 16);
+    sco[i] = T::kFp8 ? sc : mul_lo16(sc, r.gm[i]);
+    sz[i] = r.sz[i];
   }
   const int lane = threadIdx.x & 63;
   if (__builtin_expect(valid < 16, 0)) {  // tail tile: tokens at or past the sequence end drop out
@@ -382,8 +398,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
     for (int i = 0; i < 4; ++i) {
       if (4 * (lane >> 4) + i >= valid) {
         sco[i] = -INFINITY;
-        sv[i] = 0.f;
-        zv[i] = 0.f;
+        sz[i] = 0u;  // the bytes past the end may hold anything (a NaN scale)
       }
     }
   }
@@ -397,7 +412,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
-      ps[i] = p[i] * sv[i];
+      ps[i] = mul_lo16(p[i], sz[i]);
       pmax = fmaxf(pmax, ps[i]);
     }
     redo = __any(pmax > 65504.f);
@@ -417,13 +432,13 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
-      ps[i] = p[i] * sv[i];
+      ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    sm.z = fmaf(p[i], zv[i], sm.z);
+    sm.z = fma_hi16(p[i], sz[i], sm.z);
   }
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
@@ -496,30 +511,31 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   load_keys<P>(imgA, o, rA);
   load_keys<P>(imgB, o, rB);
   load_token_fields<P>(tileB ? imgB : imgA, o, own);
+  // one accumulation chain per tile: the two tiles' chains interleave
   half8 A[4];
   key_operand<P>(rA, o.ksh, la, lb, A);
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], a0, 0, 0, 0);
-  a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], a1, 0, 0, 0);
-  a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], a0, 0, 0, 0);
-  a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], a1, 0, 0, 0);
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+  sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sa, 0, 0, 0);
+  sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sa, 0, 0, 0);
+  sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], sa, 0, 0, 0);
+  sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], sa, 0, 0, 0);
   key_operand<P>(rB, o.ksh, la, lb, A);
-  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
-  b0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], b0, 0, 0, 0);
-  b1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], b1, 0, 0, 0);
-  b0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], b0, 0, 0, 0);
-  b1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], b1, 0, 0, 0);
+  f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+  sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sb, 0, 0, 0);
+  sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sb, 0, 0, 0);
+  sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], sb, 0, 0, 0);
+  sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], sb, 0, 0, 0);
 
-  float sco[4], sv[4], zv[4];
+  // per token: fp16 value scale (low half) and zero (high half)
+  float sco[4];
+  uint32_t sz[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float sa = a0[i] + a1[i], sb = b0[i] + b1[i];
     // lanes 8..15 of each row of 16 take tile B's value of lane l - 8
     const float sc = __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(sa), __float_as_int(sb), 0x118, 0xF, 0xC, false));
-    sco[i] = T::kFp8 ? sc : sc * half_bits_to_f32(own.gm[i]);
-    sv[i] = half_bits_to_f32(own.sz[i] & 0xFFFFu);
-    zv[i] = half_bits_to_f32(own.sz[i] >> 16);
+        __builtin_amdgcn_update_dpp(__float_as_int(sa[i]), __float_as_int(sb[i]), 0x118, 0xF, 0xC, false));
+    sco[i] = T::kFp8 ? sc : mul_lo16(sc, own.gm[i]);
+    sz[i] = own.sz[i];
   }
   const int valid = tileB ? validB : validA;
   if (__builtin_expect(validA < 16 || validB < 16, 0)) {
@@ -527,8 +543,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
     for (int i = 0; i < 4; ++i) {
       if (4 * (lane >> 4) + i >= valid) {
         sco[i] = -INFINITY;
-        sv[i] = 0.f;
-        zv[i] = 0.f;
+        sz[i] = 0u;  // the bytes past the end may hold anything (a NaN scale)
       }
     }
   }
@@ -541,7 +556,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
-      ps[i] = p[i] * sv[i];
+      ps[i] = mul_lo16(p[i], sz[i]);
       pmax = fmaxf(pmax, ps[i]);
     }
     redo = __any(pmax > 65504.f);
@@ -557,13 +572,13 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
-      ps[i] = p[i] * sv[i];
+      ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    sm.z = fmaf(p[i], zv[i], sm.z);
+    sm.z = fma_hi16(p[i], sz[i], sm.z);
   }
   // value weights: tile A's from this lane, tile B's from lane c + 8
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
