@@ -574,6 +574,84 @@ def store(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, b
 
 
 # --------------------------------------------------------------------------
+# SoA block layout
+# --------------------------------------------------------------------------
+#
+# The pages' gfx950 path writes the cache in a second byte convention with
+# the same tensor shape ([API] _store_kv: data region and metadata region
+# separated per block, shape identical to the combined-slot store; [API]
+# forward: a cache written that way must be read by the matching decode, the
+# combined-slot reader takes norm, scale and zero from the wrong offsets;
+# [API] _continuation_prefill: the reader's constants -- data bytes per slot
+# = key data + value data, metadata region offset = block_size * Hk * data
+# bytes per slot, 3 fields for MSE keys (norm 0, scale 1, zero 2) and 2 for
+# FP8 keys (scale 0, zero 1)).
+#
+# Readings (the pages give only those constants): rows inside each region
+# keep the combined cache's token-major order, row r = t * Hk + h; data row r
+# is [key data | value data] at r * data_bytes; field f of row r is the
+# little-endian u16 at meta_offset + 2 * (r * fields + f).
+
+
+def soa_geometry(lay: Layout, block_size: int, num_kv_heads: int):
+    """(data bytes per row, metadata region offset, u16 fields per row)."""
+    data = lay.key_data_bytes + lay.value_data_bytes
+    fields = 2 if lay.key_fp8 else 3
+    return data, block_size * num_kv_heads * data, fields
+
+
+def _slot_fields(lay: Layout):
+    """Byte offsets, inside a combined slot, of the u16 metadata fields in
+    SoA field order."""
+    vfields = lay.key_packed_size + lay.value_data_bytes
+    keyn = [] if lay.key_fp8 else [lay.key_data_bytes]
+    return keyn + [vfields, vfields + 2]
+
+
+def soa_from_aos(lay: Layout, kv_cache):
+    """Combined-slot cache (num_blocks, bs, Hk, slot) -> the same cache in
+    the SoA convention (new array of the same shape and dtype uint8)."""
+    c = np.asarray(kv_cache, dtype=np.uint8)
+    nb, bs, Hk, slot = c.shape
+    data, meta, nf = soa_geometry(lay, bs, Hk)
+    rows = c.reshape(nb, bs * Hk, slot)  # row r = t * Hk + h
+    out = np.zeros((nb, bs * Hk * slot), np.uint8)
+    kd, vd, kps = lay.key_data_bytes, lay.value_data_bytes, lay.key_packed_size
+    for r in range(bs * Hk):
+        out[:, r * data : r * data + kd] = rows[:, r, :kd]
+        out[:, r * data + kd : (r + 1) * data] = rows[:, r, kps : kps + vd]
+        for f, o in enumerate(_slot_fields(lay)):
+            a = meta + 2 * (r * nf + f)
+            out[:, a : a + 2] = rows[:, r, o : o + 2]
+    return out.reshape(nb, bs, Hk, slot)
+
+
+def aos_from_soa(lay: Layout, kv_cache):
+    """Inverse of ``soa_from_aos`` (slot padding bytes, if any, read 0)."""
+    c = np.asarray(kv_cache, dtype=np.uint8)
+    nb, bs, Hk, slot = c.shape
+    data, meta, nf = soa_geometry(lay, bs, Hk)
+    flat = c.reshape(nb, bs * Hk * slot)
+    out = np.zeros((nb, bs * Hk, slot), np.uint8)
+    kd, vd, kps = lay.key_data_bytes, lay.value_data_bytes, lay.key_packed_size
+    for r in range(bs * Hk):
+        out[:, r, :kd] = flat[:, r * data : r * data + kd]
+        out[:, r, kps : kps + vd] = flat[:, r * data + kd : (r + 1) * data]
+        for f, o in enumerate(_slot_fields(lay)):
+            a = meta + 2 * (r * nf + f)
+            out[:, r, o : o + 2] = flat[:, a : a + 2]
+    return out.reshape(nb, bs, Hk, slot)
+
+
+def store_soa(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, boundaries32):
+    """``store`` into a cache held in the SoA convention (in place)."""
+    aos = aos_from_soa(lay, kv_cache)
+    store_rows(lay, key, value, slot_mapping, aos, signs, centroids32, boundaries32)
+    kv_cache[...] = soa_from_aos(lay, aos)
+    return kv_cache
+
+
+# --------------------------------------------------------------------------
 # Dequantization and decode attention
 # --------------------------------------------------------------------------
 

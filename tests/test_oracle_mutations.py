@@ -109,3 +109,31 @@ def test_wrong_gqa_mapping_is_caught(monkeypatch):
 
     _patch(monkeypatch, "decode", bad)
     _fails(P.test_decode_close_to_unquantized_attention)
+
+
+def test_head_major_soa_rows_are_caught(monkeypatch):
+    real = T.soa_from_aos
+
+    def bad(lay, c):
+        c = np.asarray(c, np.uint8)
+        return real(lay, c.transpose(0, 2, 1, 3).copy().reshape(c.shape))  # rows h * bs + t
+
+    _patch(monkeypatch, "soa_from_aos", bad)
+    _fails(P.test_soa_field_positions_of_one_slot, "turboquant_k3v4_nc")
+
+
+def test_swapped_soa_scale_and_zero_are_caught(monkeypatch):
+    real = T._slot_fields
+    monkeypatch.setattr(T, "_slot_fields", lambda lay: real(lay)[:-2] + real(lay)[-2:][::-1])
+    _fails(P.test_soa_field_positions_of_one_slot, "turboquant_k8v4")
+
+
+def test_soa_meta_offset_counting_the_norm_is_caught(monkeypatch):
+    real = T.soa_geometry
+
+    def bad(lay, bs, Hk):  # the key norm counted as data
+        data, meta, nf = real(lay, bs, Hk)
+        return data, bs * Hk * (lay.key_packed_size + lay.value_data_bytes), nf
+
+    _patch(monkeypatch, "soa_geometry", bad)
+    _fails(P.test_soa_geometry_matches_the_pages_constants, "turboquant_k3v4_nc", 16, 8)

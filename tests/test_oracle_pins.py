@@ -583,3 +583,94 @@ def test_dequant_original_space_fp8_keys_are_the_e4m3_values():
             Kd, _ = O.dequant_original_space(lay, cache, table[b], int(L), h, s, c32)
             want = O.fp8_e4m3fn_decode(O.fp8_e4m3fn_encode(K[b][:, h]))
             np.testing.assert_array_equal(Kd, want)
+
+
+# ---------------------------------------------------------------- SoA layout
+
+# Per preset at head_dim 128: (data bytes per row = key data + value data,
+# u16 metadata fields per row), the constants of the pages' SoA reader ([API]
+# _continuation_prefill: data bytes per slot, NUM_SOA_FIELDS 2 for FP8 keys
+# and 3 otherwise).
+SOA_CONSTANTS = {
+    "turboquant_k8v4": (128 + 64, 2),
+    "turboquant_4bit_nc": (64 + 64, 3),
+    "turboquant_k3v4_nc": (48 + 64, 3),
+    "turboquant_3bit_nc": (48 + 48, 3),
+}
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("bs,Hk", [(16, 1), (16, 8), (64, 3), (128, 2)])
+def test_soa_geometry_matches_the_pages_constants(preset, bs, Hk):
+    """Metadata region offset = block_size * Hk * data bytes per slot, and the
+    two regions fill exactly the combined cache's block (same tensor shape,
+    [API] _store_kv)."""
+    lay = O.layout(preset, D)
+    data, meta, nf = O.soa_geometry(lay, bs, Hk)
+    assert (data, nf) == SOA_CONSTANTS[preset]
+    assert meta == bs * Hk * data
+    assert meta + bs * Hk * 2 * nf == bs * Hk * lay.slot_size_aligned
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+def test_soa_conversion_is_a_byte_permutation(preset):
+    """Every byte of a block lands in exactly one place and comes back: with
+    all slot bytes distinct (as 16-bit tags carried in two byte planes) the
+    SoA block holds each tag once, and the inverse restores the cache."""
+    lay = O.layout(preset, D)
+    bs, Hk, slot = 16, 3, lay.slot_size_aligned
+    n = bs * Hk * slot
+    tags = np.arange(n, dtype=np.int64).reshape(1, bs, Hk, slot)
+    lo = O.soa_from_aos(lay, (tags & 0xFF).astype(np.uint8)).astype(np.int64)
+    hi = O.soa_from_aos(lay, (tags >> 8).astype(np.uint8)).astype(np.int64)
+    assert sorted((lo | (hi << 8)).ravel().tolist()) == list(range(n))
+    rng = np.random.default_rng(1)
+    c = rng.integers(0, 256, (4, bs, Hk, slot), dtype=np.uint8)
+    np.testing.assert_array_equal(O.aos_from_soa(lay, O.soa_from_aos(lay, c)), c)
+
+
+@pytest.mark.parametrize("preset", ["turboquant_k8v4", "turboquant_k3v4_nc"])
+def test_soa_field_positions_of_one_slot(preset):
+    """Hand-placed example: the slot of token 3, KV head 1 in a block of 16
+    tokens x 2 heads is row r = 3 * 2 + 1 = 7.  Its key data and value data
+    follow each other at 7 * data; its norm (MSE keys), scale and zero are the
+    u16 fields 0..2 (FP8: scale, zero = 0, 1) of row 7 in the metadata
+    region."""
+    lay = O.layout(preset, D)
+    bs, Hk = 16, 2
+    data, meta, nf = O.soa_geometry(lay, bs, Hk)
+    cache = np.zeros((1, bs, Hk, lay.slot_size_aligned), np.uint8)
+    s = cache[0, 3, 1]
+    kd, vd, kps = lay.key_data_bytes, lay.value_data_bytes, lay.key_packed_size
+    s[:kd] = 0x11
+    s[kps : kps + vd] = 0x33
+    if not lay.key_fp8:
+        s[kd : kd + 2] = [0xA1, 0xA2]
+    s[kps + vd : kps + vd + 4] = [0xB1, 0xB2, 0xC1, 0xC2]
+    flat = O.soa_from_aos(lay, cache).reshape(-1)
+    want = np.zeros_like(flat)
+    want[7 * data : 7 * data + kd] = 0x11
+    want[7 * data + kd : 8 * data] = 0x33
+    fields = ([[0xA1, 0xA2]] if not lay.key_fp8 else []) + [[0xB1, 0xB2], [0xC1, 0xC2]]
+    for f, v in enumerate(fields):
+        want[meta + 2 * (7 * nf + f) : meta + 2 * (7 * nf + f) + 2] = v
+    np.testing.assert_array_equal(flat, want)
+
+
+def test_soa_store_equals_converted_combined_store():
+    """Storing into an SoA cache that already holds rows leaves the other
+    rows untouched and writes the new ones as the combined store would."""
+    rng = np.random.default_rng(2)
+    lay = O.layout("turboquant_3bit_nc", D)
+    c32, b32 = O.codebook_tables(D, 3)
+    s = O.wht_signs(D, 1)
+    bs, Hk, nb = 32, 2, 3
+    K = rng.standard_normal((40, Hk, D))
+    V = rng.standard_normal((40, Hk, D))
+    slots = rng.permutation(nb * bs)[:40]
+    aos = np.zeros((nb, bs, Hk, lay.slot_size_aligned), np.uint8)
+    O.store_rows(lay, K[:25], V[:25], slots[:25], aos, s, c32, b32)
+    soa = O.soa_from_aos(lay, aos)
+    O.store_rows(lay, K[25:], V[25:], slots[25:], aos, s, c32, b32)
+    O.store_soa(lay, K[25:], V[25:], slots[25:], soa, s, c32, b32)
+    np.testing.assert_array_equal(soa, O.soa_from_aos(lay, aos))
