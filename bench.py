@@ -52,14 +52,29 @@ def dev16(torch, bits, dtype):
     return x.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
 
 
+def warm_gpu(torch, fn, ms=150.0):
+    """Launch fn() until `ms` of GPU time has passed: after seconds of host
+    work the GPU has idled and its clock is back down, and the first few ms of
+    VALU-bound kernels run 20-30% slow."""
+    spent = 0.0
+    while spent < ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        spent += a.elapsed_time(b)
+
+
 class DecodeBench:
     """Device state of one decode workload: N_COPIES caches, the step's new
     tokens, queries, tables, workspace."""
 
-    def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int):
+    def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos"):
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
-        self.lay = tq.layout_init(w.preset)
+        self.lay = tq.layout_init(w.preset, 128, block_layout)
         self.lens = W.seq_lens(w)
         table = W.block_table(w)
         self.table_np = table
@@ -98,6 +113,8 @@ class DecodeBench:
         self.scale = 1.0 / math.sqrt(128)
         self.bytes_read = int(self.lens.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
         torch.cuda.synchronize()
+        it = iter(range(1 << 30))
+        warm_gpu(torch, lambda: self.step(next(it) % N_COPIES))
 
     def store(self, i):
         self.tq.store(self.lay, self.knew, self.vnew, self.snew, self.caches[i], self.tab.signs, self.tab.centroids,
@@ -194,7 +211,7 @@ class DecodeBench:
         return a.elapsed_time(b) / launches
 
 
-def store_sweep(torch, tq, steps):
+def store_sweep(torch, tq, steps, block_layout="aos"):
     """Store sweep: 65536 tokens x 8 KV heads, bs 32, per preset (Mtok/s)."""
     s = W.STORE_WORKLOAD
     K, V, slots, nb = W.store_inputs()
@@ -202,13 +219,13 @@ def store_sweep(torch, tq, steps):
     sd = torch.from_numpy(slots).cuda()
     res = {}
     for preset in s["presets"]:
-        lay = tq.layout_init(preset)
+        lay = tq.layout_init(preset, 128, block_layout)
         tab = tq.Tables(lay, W.signs(s["seed"]))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, s["block_size"], s["num_kv_heads"]), dtype=torch.uint8,
                               device="cuda") for _ in range(N_COPIES)]
         for c in caches:
             tq.store(lay, kd, vd, sd, c, tab.signs, tab.centroids, tab.boundaries)
-        torch.cuda.synchronize()
+        warm_gpu(torch, lambda: tq.store(lay, kd, vd, sd, caches[0], tab.signs, tab.centroids, tab.boundaries), 50.0)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i, (a, b) in enumerate(evs):
             a.record()
@@ -310,7 +327,7 @@ def calibrate_copy(torch, mib: int = 512, reps: int = 5):
 DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS = 131072, 8, 128
 
 
-def dequant_sweep(torch, tq, reps):
+def dequant_sweep(torch, tq, reps, block_layout="aos"):
     """Cached prefix back to dense fp16 K/V (tq_dequant_kv): one sequence of
     131072 tokens x 8 KV heads in 128-token blocks (the long-context shape),
     per preset.  Bytes = slots read + 2 x 128 fp16 written per (token, head);
@@ -327,7 +344,7 @@ def dequant_sweep(torch, tq, reps):
     vo = torch.empty_like(ko)
     res = {}
     for preset in ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
-        lay = tq.layout_init(preset)
+        lay = tq.layout_init(preset, 128, block_layout)
         tab = tq.Tables(lay, W.signs(21))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, bs, Hk), dtype=torch.uint8, device="cuda")
                   for _ in range(N_COPIES)]
@@ -335,7 +352,8 @@ def dequant_sweep(torch, tq, reps):
             tq.store(lay, K, V, slots, c, tab.signs, tab.centroids, tab.boundaries)
         for i in range(N_COPIES):
             tq.dequant_kv(lay, caches[i], table, n, tab.signs, tab.centroids, key_out=ko, value_out=vo)
-        torch.cuda.synchronize()
+        warm_gpu(torch, lambda: tq.dequant_kv(lay, caches[0], table, n, tab.signs, tab.centroids, key_out=ko,
+                                              value_out=vo), 50.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
@@ -410,6 +428,23 @@ def main():
         log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items()})}")
         extra["dequant"] = dequant_sweep(torch, tq, 20)
         log(f"[dequant] {json.dumps({k: round(v['gbs']) for k, v in extra['dequant'].items()})} GB/s")
+        # the same workloads with the cache in the SoA block convention
+        soa = {}
+        for name, S in (("llama8b", args.splits), ("longctx", 32), ("qwen32b", args.splits)):
+            b = DecodeBench(torch, tq, W.WORKLOADS[name], S, block_layout="soa")
+            s1 = b.time_stage1(30)
+            d = b.time_decode(30)
+            soa[name] = {"ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
+                         "stage1_ms": s1, "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9}
+            log(f"[soa {name}] decode call {d * 1e3:.1f} us -> {soa[name]['decode_gbs']:.0f} GB/s; "
+                f"stage1 {s1 * 1e3:.1f} us")
+            del b
+            torch.cuda.empty_cache()
+        soa["store_sweep"] = store_sweep(torch, tq, 50, "soa")
+        soa["dequant"] = dequant_sweep(torch, tq, 20, "soa")
+        log(f"[soa store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in soa['store_sweep'].items()})}; "
+            f"[soa dequant] {json.dumps({k: round(v['gbs']) for k, v in soa['dequant'].items()})} GB/s")
+        extra["soa"] = soa
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     line = {

@@ -73,6 +73,25 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
  * _continuation_prefill; [PR] get_kv_cache_shape).  Codes are packed as one
  * little-endian bit stream, code j in bits [b*j, b*j+b) (3-bit: 8 codes per
  * 3 bytes, [TQ+] "Background"). */
+/* Block byte conventions of the cache; both give the same tensor shape.
+ *   TQ_LAYOUT_AOS: the combined slots above, slot m of KV head h at byte
+ *     (m*num_kv_heads + h)*slot_size_aligned.
+ *   TQ_LAYOUT_SOA: per cache block of block_size tokens, a data region of
+ *     block_size*num_kv_heads rows (row r = t*num_kv_heads + h, token t of
+ *     the block) of soa_data_bytes = key_data_bytes + value_data_bytes each,
+ *     [key data | value codes]; then, at byte block_size*num_kv_heads*
+ *     soa_data_bytes of the block, soa_meta_fields little-endian 16-bit
+ *     fields per row, field f of row r at 2*(r*soa_meta_fields + f): MSE keys
+ *     (norm, scale, zero), FP8 keys (scale, zero).  ([API] _store_kv: data
+ *     and metadata regions separated per block, same tensor shape; forward:
+ *     such a cache must be read by the matching reader; _continuation_prefill:
+ *     data bytes per slot, metadata region offset, field counts and indices.
+ *     Row order and field interleave are this library's reading: the pages
+ *     give only those constants.)
+ * A cache is written and read with one convention: every call takes it from
+ * the layout, so the store, decode and dequant of one layout agree. */
+typedef enum { TQ_LAYOUT_AOS = 0, TQ_LAYOUT_SOA = 1 } tq_block_layout;
+
 typedef struct tq_layout {
   int32_t preset;
   int32_t head_dim;
@@ -87,6 +106,9 @@ typedef struct tq_layout {
   int32_t value_packed_size;
   int32_t slot_size;
   int32_t slot_size_aligned;
+  int32_t block_layout;    /* tq_block_layout */
+  int32_t soa_data_bytes;  /* SoA: key_data_bytes + value_data_bytes; 0 for AoS */
+  int32_t soa_meta_fields; /* SoA: 3 (MSE keys) or 2 (FP8 keys); 0 for AoS */
 } tq_layout;
 
 /* Library version string (static storage). */
@@ -103,14 +125,21 @@ const char* tq_last_hip_error(void);
  * "turboquant_3bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
 int tq_preset_from_name(const char* name, int32_t* preset);
 
-/* Fill *out for (preset, head_dim) (host).  head_dim must be a positive
- * multiple of 8; the kernels additionally need head_dim == 128. */
+/* Fill *out for (preset, head_dim) (host), block_layout TQ_LAYOUT_AOS.
+ * head_dim must be a positive multiple of 8; the kernels additionally need
+ * head_dim == 128. */
 int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out);
 
+/* tq_layout_init with a block convention (tq_block_layout) (host).  TQ_EINVAL
+ * for an unknown convention.  Decode attention over an SoA cache needs
+ * num_kv_heads <= 8 or a multiple of 8 (TQ_EUNSUPPORTED otherwise); store
+ * and dequant take any head count. */
+int tq_layout_init_ex(int32_t preset, int32_t head_dim, int32_t block_layout, tq_layout* out);
+
 /* Cache tensor shape (num_blocks, block_size, num_kv_heads,
- * slot_size_aligned), no leading K/V dimension ([PR] get_kv_cache_shape).
- * The cache is a byte tensor of that shape; slot m of KV head h is at byte
- * (m*num_kv_heads + h)*slot_size_aligned (host). */
+ * slot_size_aligned), no leading K/V dimension ([PR] get_kv_cache_shape),
+ * for either block convention.  The cache is a byte tensor of that shape
+ * (host). */
 int tq_kv_cache_shape(const tq_layout* layout, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                       int64_t shape_out[4]);
 

@@ -27,7 +27,8 @@ TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
 PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc")
 
 #: every symbol include/tq.h declares
-ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init", "tq_kv_cache_shape",
+ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init",
+               "tq_layout_init_ex", "tq_kv_cache_shape",
                "tq_lloyd_max", "tq_wht_signs", "tq_decode_workspace_bytes", "tq_store", "tq_store_validate",
                "tq_decode_attention", "tq_decode_validate", "tq_decode_stage1", "tq_decode_stage2",
                "tq_dequant_kv", "tq_dequant_validate")
@@ -46,7 +47,7 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "preset", "head_dim", "key_fp8", "key_bits", "value_bits", "norm_correction", "n_centroids",
         "key_data_bytes", "key_packed_size", "value_data_bytes", "value_packed_size", "slot_size",
-        "slot_size_aligned")]
+        "slot_size_aligned", "block_layout", "soa_data_bytes", "soa_meta_fields")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -72,6 +73,7 @@ def _load():
         "tq_last_hip_error": (ctypes.c_char_p, []),
         "tq_preset_from_name": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(i32)]),
         "tq_layout_init": (ctypes.c_int, [i32, i32, L]),
+        "tq_layout_init_ex": (ctypes.c_int, [i32, i32, i32, L]),
         "tq_kv_cache_shape": (ctypes.c_int, [L, i64, i32, i32, ctypes.POINTER(i64)]),
         "tq_lloyd_max": (ctypes.c_int, [i32, i32, i32, vp, vp]),
         "tq_wht_signs": (ctypes.c_int, [i32, u64, vp]),
@@ -120,11 +122,18 @@ def preset_from_name(name: str) -> int:
     return p.value
 
 
-def layout_init(preset, head_dim: int = 128) -> Layout:
+LAYOUT_AOS, LAYOUT_SOA = 0, 1
+
+
+def layout_init(preset, head_dim: int = 128, block_layout="aos") -> Layout:
+    """tq_layout_init_ex; block_layout "aos" (combined slots) or "soa" (data
+    region + metadata region per block), or the tq_block_layout id."""
     if isinstance(preset, str):
         preset = preset_from_name(preset)
+    if isinstance(block_layout, str):
+        block_layout = {"aos": LAYOUT_AOS, "soa": LAYOUT_SOA}[block_layout]
     lay = Layout()
-    _check(_lib.tq_layout_init(preset, head_dim, ctypes.byref(lay)), "tq_layout_init")
+    _check(_lib.tq_layout_init_ex(preset, head_dim, block_layout, ctypes.byref(lay)), "tq_layout_init_ex")
     return lay
 
 

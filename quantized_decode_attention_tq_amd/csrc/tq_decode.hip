@@ -3,9 +3,10 @@
 // split, stage 2 merges the splits with a log-sum-exp reduction; [API]
 // _decode_attention).
 //
-// Stage 1 work unit: one workgroup per (sequence b, KV head hk, group of up
-// to 16 query heads, split s); its 4 wave64s take the split's 16-token tiles
-// round-robin and merge in LDS at the end.  Per tile a wave:
+// Stage 1 work unit: one workgroup per (length-balanced tile range of one
+// sequence, group of G KV heads, up to 16 query heads per KV head); its
+// G * P wave64s take the range's 16-token tiles (P phases per head) and merge
+// in LDS at the end.  Per tile a wave:
 //   - builds the key tile (16 tokens x 128 dims) as fp16 MFMA operands: FP8
 //     keys by the hardware FP8->fp16 convert, Lloyd-Max codes through a
 //     v_perm byte lookup of the fp16 codebook;
@@ -13,12 +14,14 @@
 //     heads on columns), the query rotated by the same transform and
 //     pre-scaled by scale*log2(e) (MSE presets, [API] _decode_attention);
 //   - applies the per-token key norm, an online softmax in base 2, and
-//   - accumulates O^T = V^T . P^T with 8 MFMA 16x16x16 f16, the value codes
+//   - accumulates O^T = V^T . P^T with 8 MFMA 16x16x32 f16 per pair of tiles, the value codes
 //     entering as fp16 subnormals (no conversion) and the per-token value
 //     scale folded into P; the per-token zero point is accumulated on the
 //     VALU as sum(p * zero).
 // The GQA group rides on the MFMA's 16 columns, so the key/value bytes of a
 // (token, KV head) are read and decoded once for all its query heads.
+// Both block conventions of the cache (combined slots, SoA data + metadata
+// regions) are read; the convention is a template parameter.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -66,6 +69,16 @@ struct Preset<TQ_3BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102;
 };
 
+// SoA convention: data row = key data + value data; metadata record = kNf
+// 16-bit fields (norm, scale, zero; FP8 keys: scale, zero).
+template <int P>
+struct Soa {
+  static constexpr int kDb = Preset<P>::kKdata + Preset<P>::kVdata;
+  static constexpr int kNf = Preset<P>::kFp8 ? 2 : 3;
+  static constexpr int kMb = 2 * kNf;
+  static_assert(kDb % 16 == 0, "SoA data rows are 16-byte multiples");
+};
+
 // The constants above follow the slot layout of tq_layout_init at head_dim 128.
 template <int P>
 constexpr bool preset_geometry_ok() {
@@ -94,6 +107,8 @@ struct DecodeArgs {
   int32_t ring_depth;  // super-tiles (P tiles each) in the LDS ring
   int32_t spt;         // 1 KB direct-to-LDS slots per tile image
   int32_t contiguous;  // G == Hk: a tile of the group is one run of 16 token rows
+  int32_t dslots;      // SoA: slots of the data part of a tile image (the metadata part follows)
+  int32_t soa_pad;     // SoA: pad bytes after each image row of data (a multiple of 16)
   int32_t block_size, bt_stride;
   int32_t batch, num_units;  // B, U
 };
@@ -194,10 +209,21 @@ __device__ __forceinline__ float quarter_sum(float v) {
 // aligned dwords and realigned.
 template <int P>
 struct LaneOff {
-  uint32_t k, ksh;  // aligned-down key chunk start, its misalignment
-  uint32_t mo[4];   // slot start of token 4q + i
-  uint32_t vcol;    // byte offset of the lane's value-code column inside a slot
+  uint32_t k, ksh;  // aligned-down key chunk start, its misalignment (0 for SoA)
+  uint32_t mo[4];   // slot start of token 4q + i (SoA: mo[0] = data row of token 4q)
+  uint32_t vcol;    // byte offset of the lane's value-code column inside a slot / data row
+  uint32_t mm0;     // SoA: metadata record of token 4q
+  uint32_t sd, sm;  // SoA: image bytes between consecutive tokens' data rows / records (uniform)
 };
+
+template <int P, int SOA>
+__device__ __forceinline__ uint32_t data_row(const LaneOff<P>& o, int i) {
+  return SOA ? o.mo[0] + static_cast<uint32_t>(i) * o.sd : o.mo[i];
+}
+template <int P>
+__device__ __forceinline__ uint32_t meta_rec(const LaneOff<P>& o, int i) {
+  return o.mm0 + static_cast<uint32_t>(i) * o.sm;
+}
 
 // Registers one tile's loads land in.
 template <int P>
@@ -216,10 +242,27 @@ struct ImageGeom {
   bool contiguous;
 };
 
-// Read one tile's fields of this lane from the tile image at tb.
 template <int P>
+__device__ __forceinline__ void load_keys_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r);
+template <int P>
+__device__ __forceinline__ void load_token_fields_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r);
+template <int P>
+__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]);
+
+// Read one tile's fields of this lane from the tile image at tb.  SoA: the
+// value words arrive realigned in v[i][0].
+template <int P, int SOA>
 __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
+  if constexpr (SOA != 0) {
+    load_keys_soa<P>(tb, o, r);
+    load_token_fields_soa<P>(tb, o, r);
+    uint32_t vw[4];
+    load_value_words_soa<P>(tb, o, vw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i][0] = vw[i];
+    return;
+  }
   if constexpr (T::kFp8 != 0) {
     const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
     const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
@@ -309,8 +352,55 @@ __device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOf
   }
 }
 
-// Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q).
+// SoA image: data rows are 16-byte multiples, so the key chunk and (4-bit)
+// value words of a lane are 4-byte aligned; 3-bit value words and the MSE
+// scale/zero pair (after the 16-bit norm) are realigned.
 template <int P>
+__device__ __forceinline__ void load_keys_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
+  using T = Preset<P>;
+  const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+  r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+  if constexpr (T::kFp8 != 0) {
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
+    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void load_token_fields_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
+  using T = Preset<P>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t rec = meta_rec(o, i);
+    if constexpr (T::kFp8 != 0) {
+      r.sz[i] = *reinterpret_cast<const uint32_t*>(tb + rec);  // records of 4 bytes: aligned
+    } else {
+      r.gm[i] = ld16(tb + rec);
+      const uint32_t so = rec + 2u;
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (so & ~3u));
+      r.sz[i] = tq::alignbyte(w.y, w.x, so & 3u);
+    }
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]) {
+  using T = Preset<P>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t vo = data_row<P, 1>(o, i) + o.vcol;
+    if constexpr (T::kVb == 4) {
+      vw[i] = *reinterpret_cast<const uint32_t*>(tb + vo);
+    } else {
+      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
+      vw[i] = tq::alignbyte(w.y, w.x, vo & 3u);
+    }
+  }
+}
+
+// Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q).
+// SOA: the key words are aligned (sh unused).
+template <int P, int SOA>
 __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, const tq::Lut8& la,
                                             const tq::Lut8& lb, half8 A[4]) {
   using T = Preset<P>;
@@ -326,7 +416,7 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, c
   } else if constexpr (T::kKb == 4) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w = tq::alignbyte(r.k[c + 1], r.k[c], sh);
+      const uint32_t w = SOA ? r.k[c] : tq::alignbyte(r.k[c + 1], r.k[c], sh);
       uint32_t e0, e1, o0, o1;
       tq::lut16(w & 0x0F0F0F0Fu, la, lb, e0, e1);
       tq::lut16((w >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
@@ -334,8 +424,11 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, c
     }
   } else {
     uint32_t sel[8];
-    tq::key3_selectors(tq::alignbyte(r.k[1], r.k[0], sh), tq::alignbyte(r.k[2], r.k[1], sh),
-                       tq::alignbyte(r.k[3], r.k[2], sh), sel);
+    if (SOA)
+      tq::key3_selectors(r.k[0], r.k[1], r.k[2], sel);
+    else
+      tq::key3_selectors(tq::alignbyte(r.k[1], r.k[0], sh), tq::alignbyte(r.k[2], r.k[1], sh),
+                         tq::alignbyte(r.k[3], r.k[2], sh), sel);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t a0, a1, b0, b1;
@@ -369,13 +462,13 @@ struct PendingTile {
 // before the sequence end (1..16).  On return `cur` holds the tile's value
 // words and weights; if the running maximum moved, the accumulators and the
 // pending tile (when `have_pend`) are rescaled to it.
-template <int P>
+template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
                                            const tq::Lut8& lb, const half8 bq[4], int valid, Softmax& sm,
                                            f32x4 acc[8], PendingTile& pend, bool have_pend, PendingTile& cur) {
   using T = Preset<P>;
   half8 A[4];
-  key_operand<P>(r, o.ksh, la, lb, A);
+  key_operand<P, SOA>(r, o.ksh, la, lb, A);
   // two independent accumulation chains halve the dependent-MFMA latency
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], s0, 0, 0, 0);
@@ -445,7 +538,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
   cur.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4)
+    if constexpr (SOA != 0 || (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4))
       cur.vw[i] = r.v[i][0];
     else
       cur.vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (o.mo[i] + o.vcol) & 3u);
@@ -500,7 +593,7 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 // reads for both tiles.  The value MFMA then takes tile A's weights from the
 // lane itself and tile B's from lane c + 8.  Columns 8..15 of the output
 // accumulators hold nothing used.
-template <int P>
+template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4],
                                                   int validA, int validB, Softmax& sm, f32x4 acc[8]) {
@@ -508,18 +601,24 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   const int lane = threadIdx.x & 63;
   const bool tileB = (lane & 8) != 0;
   TileRegs<P> rA, rB, own;
-  load_keys<P>(imgA, o, rA);
-  load_keys<P>(imgB, o, rB);
-  load_token_fields<P>(tileB ? imgB : imgA, o, own);
+  if constexpr (SOA != 0) {
+    load_keys_soa<P>(imgA, o, rA);
+    load_keys_soa<P>(imgB, o, rB);
+    load_token_fields_soa<P>(tileB ? imgB : imgA, o, own);
+  } else {
+    load_keys<P>(imgA, o, rA);
+    load_keys<P>(imgB, o, rB);
+    load_token_fields<P>(tileB ? imgB : imgA, o, own);
+  }
   // one accumulation chain per tile: the two tiles' chains interleave
   half8 A[4];
-  key_operand<P>(rA, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rA, o.ksh, la, lb, A);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f};
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], sa, 0, 0, 0);
-  key_operand<P>(rB, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rB, o.ksh, la, lb, A);
   f32x4 sb = {0.f, 0.f, 0.f, 0.f};
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sb, 0, 0, 0);
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sb, 0, 0, 0);
@@ -586,8 +685,13 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   PendingTile ta, tb;
   ta.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
   tb.pv = as_half4(swap8(h2_bits(ps01)), swap8(h2_bits(ps23)));
-  load_value_words<P>(imgA, o, ta.vw);
-  load_value_words<P>(imgB, o, tb.vw);
+  if constexpr (SOA != 0) {
+    load_value_words_soa<P>(imgA, o, ta.vw);
+    load_value_words_soa<P>(imgB, o, tb.vw);
+  } else {
+    load_value_words<P>(imgA, o, ta.vw);
+    load_value_words<P>(imgB, o, tb.vw);
+  }
   accumulate_pair<P>(ta, tb, acc);
 }
 
@@ -606,14 +710,15 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
 // Tile p of a super-tile is staged by the G waves of phase p (the waves
 // that will compute it): wave (hh, p) issues slots hh, hh + G, ... of it,
 // so a wave needs one block id and one base address per super-tile.
-template <int P>
+template <int P, int SOA>
 struct Ring {
-  static constexpr int kLoads = tq::max_dma_loads(P);
+  static constexpr int kLoads = tq::max_dma_loads(P, SOA != 0);
   uint32_t lds_base;       // LDS byte address of ring entry 0 (uniform)
   uint32_t entry;          // bytes per ring entry (P * spt KB)
   int my_loads;            // DMA slots per super-tile issued by this wave
   uint32_t dst[kLoads];    // per load: LDS offset inside the entry (uniform)
   uint32_t off[kLoads];    // per load: this lane's chunk offset from the tile base
+  uint32_t meta_loads;     // SoA: bit k set when load k reads the metadata part (uniform)
 };
 
 // One direct-to-LDS load of 16 bytes per lane, non-temporal: the data is
@@ -835,7 +940,7 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // and accumulates tile p of every super-tile from LDS.  At the end the P
 // phase waves of a head merge their partial softmax states through LDS and
 // the phase-0 wave writes the split's partial rows.
-template <int P, int TPW, int PACK>
+template <int P, int TPW, int PACK, int SOA>
 __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
@@ -911,14 +1016,46 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 
   // ---- ring: this wave's DMA slots of each super-tile ----
   const int spt = a.spt;
-  Ring<P> ring;
+  Ring<P, SOA> ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
   ring.entry = static_cast<uint32_t>(Q * spt) * 1024u;
   ring.my_loads = (spt - hh + G - 1) / G;  // per tile
+  ring.meta_loads = 0u;
 #pragma unroll
-  for (int k = 0; k < Ring<P>::kLoads; ++k) {
+  for (int k = 0; k < Ring<P, SOA>::kLoads; ++k) {
     const int n = hh + k * G;  // slot of tile ph (n < spt for k < my_loads)
     ring.dst[k] = static_cast<uint32_t>(ph * TPW * spt + n) * 1024u;  // in tile 0 of this wave's TPW
+    if constexpr (SOA != 0) {
+      // SoA image: the tile's 16 token rows of data (G rows of kDb bytes
+      // each, from one run when G == Hk, else from 16 pieces at the cache's
+      // row stride) in the first dslots slots, each image row followed by
+      // soa_pad bytes; then its metadata records (16 x G x kMb bytes).  The
+      // pad moves the image row stride off multiples of 256 bytes (G * kDb
+      // here), where the 16 lanes reading one column of 16 rows would all
+      // hit one LDS bank.  A pad chunk repeats the row's last chunk (an L2
+      // hit).
+      using S = Soa<P>;
+      const int ds = a.dslots;
+      if (n < ds) {
+        const uint32_t pc = static_cast<uint32_t>(G * S::kDb) / 16u;  // chunks of a token row
+        const uint32_t pr = pc + static_cast<uint32_t>(a.soa_pad) / 16u;  // chunks of an image row
+        const uint32_t p = min(static_cast<uint32_t>(64 * n + lane), 16u * pr - 1u);
+        const uint32_t r = p / pr, j = min(p % pr, pc - 1u);
+        ring.off[k] = geo.contiguous ? 16u * (r * pc + j)
+                                     : r * static_cast<uint32_t>(Hk * S::kDb) +
+                                           static_cast<uint32_t>(hgp * G * S::kDb) + 16u * j;
+      } else {
+        ring.meta_loads |= 1u << k;
+        const uint32_t meta_off = static_cast<uint32_t>(a.block_size * Hk * S::kDb);  // region start in a block
+        const uint32_t pc = static_cast<uint32_t>(G * S::kMb) / 16u;
+        const uint32_t tot = static_cast<uint32_t>(G * S::kMb);  // 16 records of G*kMb bytes = G*kMb chunks
+        const uint32_t c = min(static_cast<uint32_t>(64 * (n - ds) + lane), tot - 1u);
+        ring.off[k] = meta_off + (geo.contiguous ? 16u * c
+                                                 : (c / pc) * static_cast<uint32_t>(Hk * S::kMb) +
+                                                       static_cast<uint32_t>(hgp * G * S::kMb) + 16u * (c % pc));
+      }
+      continue;
+    }
     uint32_t c = min(static_cast<uint32_t>(64 * n + lane), tc - 1);
     if (geo.contiguous) {
       ring.off[k] = 16 * c;
@@ -962,11 +1099,23 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = my_tile(u, j);
-      const uint8_t* base = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk.id[j])) * blk_bytes32 +
-                            static_cast<uint32_t>((t * 16) & (a.block_size - 1)) * geo.row;
+      const uint8_t* blkp = a.cache + static_cast<uint64_t>(static_cast<uint32_t>(blk.id[j])) * blk_bytes32;
+      const uint32_t t16 = static_cast<uint32_t>((t * 16) & (a.block_size - 1));  // tile's first row in the block
+      if constexpr (SOA != 0) {
+        const uint8_t* bd = blkp + t16 * static_cast<uint32_t>(Hk * Soa<P>::kDb);
+        const uint8_t* bm = blkp + t16 * static_cast<uint32_t>(Hk * Soa<P>::kMb);
 #pragma unroll
-      for (int k = 0; k < Ring<P>::kLoads; ++k)
-        if (k < ring.my_loads) dma16(base, ring.off[k], e0 + ring.dst[k] + static_cast<uint32_t>(j * spt) * 1024u);
+        for (int k = 0; k < Ring<P, SOA>::kLoads; ++k)
+          if (k < ring.my_loads)
+            dma16(((ring.meta_loads >> k) & 1u) ? bm : bd, ring.off[k],
+                  e0 + ring.dst[k] + static_cast<uint32_t>(j * spt) * 1024u);
+      } else {
+        const uint8_t* base = blkp + t16 * geo.row;
+#pragma unroll
+        for (int k = 0; k < Ring<P, SOA>::kLoads; ++k)
+          if (k < ring.my_loads)
+            dma16(base, ring.off[k], e0 + ring.dst[k] + static_cast<uint32_t>(j * spt) * 1024u);
+      }
     }
   };
   const int nst = (t_end - t_begin + Q - 1) / Q;
@@ -991,7 +1140,19 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
     if (T::kKb == 4) lb = {pack(8, 0), pack(12, 0), pack(8, 8), pack(12, 8)};
   }
   LaneOff<P> off;
-  {
+  if constexpr (SOA != 0) {
+    using S = Soa<P>;
+    off.sd = static_cast<uint32_t>(G * S::kDb + a.soa_pad);  // image row: G data rows + the pad
+    off.sm = static_cast<uint32_t>(G * S::kMb);
+    off.k = hl * off.sd + static_cast<uint32_t>(hh * S::kDb) +
+            static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
+    off.ksh = 0u;
+    off.mo[0] = static_cast<uint32_t>(4 * q4) * off.sd + static_cast<uint32_t>(hh * S::kDb);
+    off.mo[1] = off.mo[2] = off.mo[3] = 0u;
+    off.vcol = static_cast<uint32_t>(T::kKdata + (T::kVb == 4 ? 4 * hl : 3 * hl));
+    off.mm0 = static_cast<uint32_t>(a.dslots) * 1024u + static_cast<uint32_t>(4 * q4) * off.sm +
+              static_cast<uint32_t>(hh * S::kMb);
+  } else {
     const uint32_t kraw = row_start(hl) + static_cast<uint32_t>(hh * T::kSlot) +
                           static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
     off.k = kraw & ~3u;
@@ -999,6 +1160,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) off.mo[i] = row_start(4 * q4 + i) + static_cast<uint32_t>(hh * T::kSlot);
     off.vcol = static_cast<uint32_t>(T::kKps + (T::kVb == 4 ? 4 * hl : 3 * hl));
+    off.mm0 = off.sd = off.sm = 0u;
   }
 
   Softmax sm{-INFINITY, 0.f, 0.f};
@@ -1024,7 +1186,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
       if (t < t_end) {
         const uint8_t* img =
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
-        score_pair_packed<P>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, bq,
+        score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, bq,
                              min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0, sm,
                              acc);
       }
@@ -1036,9 +1198,9 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
         TileRegs<P> r;
         const uint8_t* img =
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
-        load_tile<P>(img, off, r);
+        load_tile<P, SOA>(img, off, r);
         PendingTile cur;
-        score_tile<P>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
+        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
         if (have_pend) {
           accumulate_pair<P>(pend, cur, acc);
           have_pend = false;
@@ -1236,30 +1398,36 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int P, int TPW, int PACK>
+template <int P, int TPW, int PACK, int SOA>
 int launch_stage1_t(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   });
   if (attr != hipSuccess) return tq::hip_status(attr);
   DecodeArgs arg = a;
   void* args[] = {&arg};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK>),
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>),
                                         dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
                                         stream));
 }
 
 // Two tiles per wave: GQA groups of at most 8 query heads score them packed
 // into one MFMA block layout; wider groups one at a time.
-template <int P>
-int launch_stage1(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
+template <int P, int SOA>
+int launch_stage1_l(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
   if (tpw == 2)
-    return a.group <= 8 ? launch_stage1_t<P, 2, 1>(a, nblocks, lds, stream)
-                        : launch_stage1_t<P, 2, 0>(a, nblocks, lds, stream);
-  return launch_stage1_t<P, 1, 0>(a, nblocks, lds, stream);
+    return a.group <= 8 ? launch_stage1_t<P, 2, 1, SOA>(a, nblocks, lds, stream)
+                        : launch_stage1_t<P, 2, 0, SOA>(a, nblocks, lds, stream);
+  return launch_stage1_t<P, 1, 0, SOA>(a, nblocks, lds, stream);
+}
+
+template <int P>
+int launch_stage1(const DecodeArgs& a, int tpw, bool soa, int64_t nblocks, size_t lds, hipStream_t stream) {
+  return soa ? launch_stage1_l<P, 1>(a, tpw, nblocks, lds, stream)
+             : launch_stage1_l<P, 0>(a, tpw, nblocks, lds, stream);
 }
 
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
@@ -1294,13 +1462,16 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.ring_depth = plan.R;
   a.spt = plan.spt;
   a.contiguous = plan.contiguous;
+  a.dslots = plan.dslots;
+  a.soa_pad = plan.soa_pad;
   const int64_t nblocks = plan.grid;
   const size_t lds = plan.lds;
+  const bool soa = layout->block_layout == TQ_LAYOUT_SOA;
   switch (layout->preset) {
-    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, nblocks, lds, stream);
-    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, nblocks, lds, stream);
-    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, nblocks, lds, stream);
-    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, nblocks, lds, stream);
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }

@@ -40,6 +40,7 @@ struct DequantArgs {
   int32_t num_kv_heads;
   int32_t block_size;
   int32_t slot_bytes;  // slot_size_aligned
+  int32_t soa;         // SoA block convention: data rows, then 16-bit metadata records
 };
 
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
@@ -102,18 +103,18 @@ struct SlotFields {
   uint32_t gamma, scale_zero;
 };
 
+// kp / vp: the row's key data and value codes; gp: its key norm (MSE keys);
+// sp: its value scale, the zero 2 bytes on.
 template <int KEY_FP8, int KB, int VB>
-__device__ __forceinline__ void load_fields(const uint8_t* slot, int sub, SlotFields<KEY_FP8, KB, VB>& f) {
+__device__ __forceinline__ void load_fields(const uint8_t* kp, const uint8_t* vp, const uint8_t* gp,
+                                            const uint8_t* sp, int sub, SlotFields<KEY_FP8, KB, VB>& f) {
   using F = SlotFields<KEY_FP8, KB, VB>;
-  constexpr int kKdata = KEY_FP8 ? kD : kD * KB / 8;
-  constexpr int kKps = KEY_FP8 ? kD : kKdata + 2;
-  constexpr int kVdata = kD * VB / 8;
   f.kw[(F::kKeyBytes + 3) / 4] = 0u;
   f.vw[(F::kValBytes + 3) / 4] = 0u;
-  ld_bytes<F::kKeyBytes>(slot + F::kKeyBytes * sub, f.kw);
-  ld_bytes<F::kValBytes>(slot + kKps + F::kValBytes * sub, f.vw);
-  f.gamma = KEY_FP8 ? 0u : ld_u16(slot + kKdata);
-  f.scale_zero = ld_u16(slot + kKps + kVdata) | (ld_u16(slot + kKps + kVdata + 2) << 16);
+  ld_bytes<F::kKeyBytes>(kp + F::kKeyBytes * sub, f.kw);
+  ld_bytes<F::kValBytes>(vp + F::kValBytes * sub, f.vw);
+  f.gamma = KEY_FP8 ? 0u : ld_u16(gp);
+  f.scale_zero = ld_u16(sp) | (ld_u16(sp + 2) << 16);
 }
 
 // Each wave takes kGroups groups of 8 consecutive rows (a group: 8 lanes per
@@ -147,9 +148,25 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
     const uint32_t t = row / static_cast<uint32_t>(a.num_kv_heads);
     const int h = static_cast<int>(row - t * a.num_kv_heads);
     const int64_t blk = a.block_table[t / static_cast<uint32_t>(a.block_size)];
-    const int64_t pos = blk * a.block_size + t % static_cast<uint32_t>(a.block_size);
-    load_fields<KEY_FP8, KB, VB>(a.cache + (pos * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes), sub,
-                                 f[g]);
+    const uint32_t tb = t % static_cast<uint32_t>(a.block_size);
+    constexpr int kKdata = KEY_FP8 ? kD : kD * KB / 8;
+    constexpr int kKps = KEY_FP8 ? kD : kKdata + 2;
+    constexpr int kVdata = kD * VB / 8;
+    if (a.soa) {
+      // SoA: row r = t * Hk + h of the block: [key data | value codes] at
+      // r * kDb, then the fields (norm, scale, zero / scale, zero) at
+      // 2 * (r * kNf + f) after the data region
+      constexpr int kDb = kKdata + kVdata, kNf = KEY_FP8 ? 2 : 3;
+      const int64_t rows = static_cast<int64_t>(a.block_size) * a.num_kv_heads;
+      const uint8_t* blkp = a.cache + blk * rows * a.slot_bytes;
+      const int64_t r = static_cast<int64_t>(tb) * a.num_kv_heads + h;
+      const uint8_t* drow = blkp + r * kDb;
+      const uint8_t* rec = blkp + rows * kDb + r * (2 * kNf);
+      load_fields<KEY_FP8, KB, VB>(drow, drow + kKdata, rec, rec + (KEY_FP8 ? 0 : 2), sub, f[g]);
+    } else {
+      const uint8_t* slot = a.cache + ((blk * a.block_size + tb) * a.num_kv_heads + h) * a.slot_bytes;
+      load_fields<KEY_FP8, KB, VB>(slot, slot + kKps, slot + kKdata, slot + kKps + kVdata, sub, f[g]);
+    }
   }
 
   float sg[kDpl];  // signs * (+-1/sqrt(D)), the lane sign of the butterflies undone
@@ -241,6 +258,7 @@ extern "C" int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int6
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
   a.slot_bytes = layout->slot_size_aligned;
+  a.soa = layout->block_layout == TQ_LAYOUT_SOA;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (layout->preset) {
     case TQ_K8V4: return launch_dequant<1, 8, 4>(a, out_dtype, s);

@@ -69,7 +69,11 @@ extern "C" int tq_preset_from_name(const char* name, int32_t* preset) {
 // value region ends with two 16-bit fields (scale, zero).  [PR]
 // get_kv_cache_shape: slot rounded up to an even byte count.
 extern "C" int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out) {
-  if (!out) return TQ_EINVAL;
+  return tq_layout_init_ex(preset, head_dim, TQ_LAYOUT_AOS, out);
+}
+
+extern "C" int tq_layout_init_ex(int32_t preset, int32_t head_dim, int32_t block_layout, tq_layout* out) {
+  if (!out || (block_layout != TQ_LAYOUT_AOS && block_layout != TQ_LAYOUT_SOA)) return TQ_EINVAL;
   if (preset < 0 || preset > 3) return TQ_EPRESET;
   if (head_dim <= 0 || head_dim % 8 != 0) return TQ_EHEADDIM;
   const PresetDef& p = kPresets[preset];
@@ -87,6 +91,14 @@ extern "C" int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out) 
   L.value_packed_size = L.value_data_bytes + 4;
   L.slot_size = L.key_packed_size + L.value_packed_size;
   L.slot_size_aligned = (L.slot_size + 1) / 2 * 2;
+  L.block_layout = block_layout;
+  // SoA ([API] _continuation_prefill constants): the rows' data, then 16-bit
+  // fields; the two regions fill the same block bytes as the slots (slot
+  // sizes are even, so there is no padding to account for)
+  L.soa_data_bytes = block_layout == TQ_LAYOUT_SOA ? L.key_data_bytes + L.value_data_bytes : 0;
+  L.soa_meta_fields = block_layout == TQ_LAYOUT_SOA ? (p.key_fp8 ? 2 : 3) : 0;
+  if (block_layout == TQ_LAYOUT_SOA && L.soa_data_bytes + 2 * L.soa_meta_fields != L.slot_size_aligned)
+    return TQ_EHEADDIM;
   *out = L;
   return TQ_OK;
 }
@@ -96,7 +108,7 @@ namespace tq {
 bool layout_consistent(const tq_layout* L) {
   if (!L) return false;
   tq_layout ref;
-  if (tq_layout_init(L->preset, L->head_dim, &ref) != TQ_OK) return false;
+  if (tq_layout_init_ex(L->preset, L->head_dim, L->block_layout, &ref) != TQ_OK) return false;
   return std::memcmp(&ref, L, sizeof(tq_layout)) == 0;
 }
 
@@ -307,6 +319,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
   if (q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EDTYPE;
   if (L->head_dim != 128) return TQ_EHEADDIM;
   if (num_kv_splits <= 0 || num_kv_splits > 4096) return TQ_EINVAL;
+  if (L->block_layout == TQ_LAYOUT_SOA && num_kv_heads > 8 && num_kv_heads % 8 != 0) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!query || !kv_cache || !block_table || !seq_lens || !workspace) return TQ_EINVAL;
   if (!aligned16(query) || !aligned16(workspace) || !aligned16(kv_cache)) return TQ_EINVAL;

@@ -52,6 +52,8 @@ int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_block
 //            of a (unit, query head) followed by its natural-log LSE (padded
 //            to 16-byte rows).
 constexpr int64_t kTargetWorkgroups = 512;
+// SoA tile images: bytes of padding after each image row of data (G data rows)
+constexpr int kSoaRowPad = 16;
 constexpr int64_t kPartPad = 4;  // LSE + 3 pad floats after the head_dim outputs
 
 inline int64_t table_bytes(int64_t batch) { return (8 * batch + 255) / 256 * 256; }
@@ -76,6 +78,8 @@ inline int64_t max_splits(int64_t batch, int64_t num_splits) {
 // sequence (block-table width), which caps S_int.
 struct DecodePlan {
   int G, P, R, spt, contiguous;
+  int dslots;      // SoA: slots of a tile image's data part (0 for combined slots)
+  int soa_pad;     // SoA: pad bytes after each 16-token image row of data (a multiple of 16)
   int tpw;         // tiles each wave computes per super-tile (between barriers)
   size_t lds;      // dynamic LDS bytes per workgroup
   int64_t units;   // U
@@ -85,8 +89,13 @@ struct DecodePlan {
 // Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
 // this many for any head count at head_dim 128 (slots of 196 / 134 / 118 /
 // 102 bytes; a wave of G waves per tile takes ceil(spt / G) of the tile's
-// spt loads).
-constexpr int max_dma_loads(int preset) { return preset == TQ_K8V4 ? 4 : (preset == TQ_3BIT_NC ? 2 : 3); }
+// spt loads).  SoA images pad each image row by 16 bytes and round the data
+// part and the metadata part up to whole slots separately: with one KV head
+// that takes one load more for k8v4, 4bit_nc and 3bit_nc.
+constexpr int max_dma_loads(int preset, bool soa = false) {
+  if (soa) return preset == TQ_K8V4 ? 5 : (preset == TQ_4BIT_NC ? 4 : 3);
+  return preset == TQ_K8V4 ? 4 : (preset == TQ_3BIT_NC ? 2 : 3);
+}
 
 inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t num_splits, int64_t max_tiles, DecodePlan* p) {
@@ -95,8 +104,13 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   const int64_t row = num_kv_heads * slot;
   const int group = num_q_heads / num_kv_heads;
   const int64_t hgroups = (group + 15) / 16;
+  const bool soa = L->block_layout == TQ_LAYOUT_SOA;
   int G = 0;
-  if (num_kv_heads <= 8) {
+  if (soa) {
+    // SoA pieces must stay 16-byte multiples: all KV heads, or 8 of them
+    if (num_kv_heads > 8 && num_kv_heads % 8 != 0) return TQ_EUNSUPPORTED;
+    G = num_kv_heads <= 8 ? num_kv_heads : 8;
+  } else if (num_kv_heads <= 8) {
     G = num_kv_heads;
   } else {
     for (int d = 8; d >= 1 && G == 0; --d)
@@ -113,7 +127,12 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   if (s_int > num_splits && s_int > cap) s_int = cap > num_splits ? cap : num_splits;
   const int64_t piece = G * slot;
   const int64_t tc_max = contiguous ? row : 16 * ((piece + 30) / 16);  // chunks per tile image
-  const int spt = static_cast<int>((tc_max + 63) / 64);
+  // SoA: 16 image rows of G * (key data + value data) bytes plus a 16-byte
+  // pad, then 16 x G records of 2 * fields bytes, each part in whole 1 KB
+  // slots
+  const int64_t soa_data = L->soa_data_bytes, soa_meta = 2 * static_cast<int64_t>(L->soa_meta_fields);
+  const int dslots = soa ? static_cast<int>((G * soa_data + kSoaRowPad + 63) / 64) : 0;
+  const int spt = soa ? dslots + static_cast<int>((G * soa_meta + 63) / 64) : static_cast<int>((tc_max + 63) / 64);
   // MSE keys: two tiles per wave between barriers (two independent chains
   // to interleave), when the ring still fits two workgroups per CU
   const int tpw = (!L->key_fp8 && 2 * static_cast<size_t>(P) * spt * 1024 * 2 <= 80 * 1024) ? 2 : 1;
@@ -127,12 +146,14 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   p->tpw = tpw;
   p->spt = spt;
   p->contiguous = contiguous;
+  p->dslots = dslots;
+  p->soa_pad = soa ? kSoaRowPad : 0;
   p->lds = R * entry > merge ? R * entry : merge;
   p->units = static_cast<int64_t>(batch) * s_int;
   p->grid = p->units * wg_per_unit;
   const int loads = (spt + G - 1) / G;  // DMA slots per wave per tile of its phase
   const int64_t blk_bytes = 128 * row;  // largest block (block_size 128)
-  if (p->lds > kLdsMax || loads > max_dma_loads(L->preset) || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
+  if (p->lds > kLdsMax || loads > max_dma_loads(L->preset, soa) || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
       blk_bytes > 0xFFFFFFFFLL || s_int > max_splits(batch, num_splits))
     return TQ_EUNSUPPORTED;
   return TQ_OK;

@@ -43,6 +43,8 @@ struct StoreArgs {
   const float* boundaries;
   int32_t num_kv_heads;
   int32_t slot_bytes;  // slot_size_aligned
+  int32_t soa;         // SoA block convention: data rows, then 16-bit metadata records
+  int32_t bs_log2;     // log2(block_size) (SoA addressing)
 };
 
 // 16 consecutive bf16 / fp16 elements -> fp32
@@ -148,6 +150,17 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   const int64_t m = a.slot_mapping[n];
   uint8_t* slot = a.cache + (m * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes);
   const bool write = active && m >= 0;
+  // SoA ([API] _store_kv): row r = t * Hk + h of the block holds [key data |
+  // value data] at r * kDb; its fields (norm, scale, zero / scale, zero)
+  // follow the data region as 16-bit values at 2 * (r * kNf + f)
+  constexpr int kDb = (KEY_FP8 ? kD : kD * KB / 8) + kD * VB / 8;
+  constexpr int kNf = KEY_FP8 ? 2 : 3;
+  const int64_t mm = m >= 0 ? m : 0;
+  const int64_t blk_rows = static_cast<int64_t>(a.num_kv_heads) << a.bs_log2;  // rows of a block
+  uint8_t* blkp = a.cache + (mm >> a.bs_log2) * blk_rows * a.slot_bytes;
+  const int64_t r = (mm & ((int64_t{1} << a.bs_log2) - 1)) * a.num_kv_heads + h;
+  uint8_t* drow = blkp + r * kDb;
+  uint8_t* mrec = blkp + blk_rows * kDb + r * (2 * kNf);
 
   // ---------------- key ----------------
   constexpr int kKeyBytesPerLane = KEY_FP8 ? kDpl : (kDpl * KB) / 8;
@@ -262,43 +275,58 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   const int kdata = KEY_FP8 ? kD : (kD * KB) / 8;
   const int kps = KEY_FP8 ? kD : kdata + 2;
   const int vdata = (kD * VB) / 8;
-  if (a.num_kv_heads % kRowsPerWave == 0) {
-    // The wave's 8 rows are 8 consecutive heads of one token: 8 adjacent
-    // slots, 16-byte aligned.  Assemble them in LDS, then write them with
-    // 16-byte stores.
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][kRowsPerWave * kMaxSlot];
-    uint8_t* sl = stage[wave] + (lane >> 3) * a.slot_bytes;
-    uint8_t* kp = sl + sub * kKeyBytesPerLane;
+  // the row's fields: key bytes, value bytes, norm, scale (zero 2 bytes on)
+  auto put = [&](uint8_t* kp0, uint8_t* vp0, uint8_t* gp, uint8_t* sp) {
+    uint8_t* kp = kp0 + sub * kKeyBytesPerLane;
 #pragma unroll
     for (int i = 0; i < kKeyBytesPerLane / 2; ++i) st16(kp + 2 * i, kbytes[i / 2] >> (16 * (i % 2)));
-    if (!KEY_FP8 && sub == 0) st16(sl + kdata, gamma_bits);
-    uint8_t* vp = sl + kps + sub * kValBytesPerLane;
+    if (!KEY_FP8 && sub == 0) st16(gp, gamma_bits);
+    uint8_t* vp = vp0 + sub * kValBytesPerLane;
 #pragma unroll
     for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, vp32.w[i / 2] >> (16 * (i % 2)));
     if (sub == 0) {
-      st16(sl + kps + vdata, __half_as_ushort(s16));
-      st16(sl + kps + vdata + 2, __half_as_ushort(z16));
+      st16(sp, __half_as_ushort(s16));
+      st16(sp + 2, __half_as_ushort(z16));
+    }
+  };
+  const int fs = KEY_FP8 ? 0 : 2;  // SoA: byte of the scale inside a record
+  if (a.num_kv_heads % kRowsPerWave == 0) {
+    // The wave's 8 rows are 8 consecutive heads of one token: 8 adjacent
+    // slots (SoA: 8 adjacent data rows and 8 adjacent records), 16-byte
+    // aligned.  Assemble them in LDS, then write them with 16-byte stores.
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][kRowsPerWave * kMaxSlot];
+    const int q = lane >> 3;  // row of the wave
+    if (a.soa) {
+      uint8_t* sd = stage[wave] + q * kDb;
+      uint8_t* sm = stage[wave] + kRowsPerWave * kDb + q * (2 * kNf);
+      put(sd, sd + kdata, sm, sm + fs);
+    } else {
+      uint8_t* sl = stage[wave] + q * a.slot_bytes;
+      put(sl, sl + kps, sl + kdata, sl + kps + vdata);
     }
     __syncthreads();
     // every row of the wave has the same token, activity and slot mapping
     if (write) {
-      uint8_t* dst = slot - (lane >> 3) * static_cast<int64_t>(a.slot_bytes);  // slot of the wave's first head
-      const int nchunk = (kRowsPerWave * a.slot_bytes) >> 4;
-      for (int c = lane; c < nchunk; c += 64)
-        *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+      if (a.soa) {
+        uint8_t* dd = drow - q * kDb;            // data row of the wave's first head
+        uint8_t* dm = mrec - q * (2 * kNf);      // its record
+        constexpr int kDc = kRowsPerWave * kDb / 16, kMc = kRowsPerWave * 2 * kNf / 16;
+        for (int c = lane; c < kDc + kMc; c += 64) {
+          uint8_t* dst = c < kDc ? dd + 16 * c : dm + 16 * (c - kDc);
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+        }
+      } else {
+        uint8_t* dst = slot - q * static_cast<int64_t>(a.slot_bytes);  // slot of the wave's first head
+        const int nchunk = (kRowsPerWave * a.slot_bytes) >> 4;
+        for (int c = lane; c < nchunk; c += 64)
+          *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+      }
     }
   } else if (write) {
-    uint8_t* kp = slot + sub * kKeyBytesPerLane;
-#pragma unroll
-    for (int i = 0; i < kKeyBytesPerLane / 2; ++i) st16(kp + 2 * i, kbytes[i / 2] >> (16 * (i % 2)));
-    if (!KEY_FP8 && sub == 0) st16(slot + kdata, gamma_bits);
-    uint8_t* vp = slot + kps + sub * kValBytesPerLane;
-#pragma unroll
-    for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, vp32.w[i / 2] >> (16 * (i % 2)));
-    if (sub == 0) {
-      st16(slot + kps + vdata, __half_as_ushort(s16));
-      st16(slot + kps + vdata + 2, __half_as_ushort(z16));
-    }
+    if (a.soa)
+      put(drow, drow + kdata, mrec, mrec + fs);
+    else
+      put(slot, slot + kps, slot + kdata, slot + kps + vdata);
   }
 }
 
@@ -340,6 +368,8 @@ extern "C" int tq_store(const tq_layout* layout, const void* key, const void* va
   a.centroids = centroids;
   a.boundaries = boundaries;
   a.slot_bytes = layout->slot_size_aligned;
+  a.soa = layout->block_layout == TQ_LAYOUT_SOA;
+  a.bs_log2 = 31 - __builtin_clz(static_cast<unsigned>(block_size));
   const bool bf16 = in_dtype == TQ_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the kernel indexes rows in 32 bits: launches of at most 2^30 rows

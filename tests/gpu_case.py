@@ -90,15 +90,18 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32)
 
 
 class DecodeCase:
-    """Inputs of one decode workload, the oracle cache, and device copies."""
+    """Inputs of one decode workload, the oracle cache, and device copies.
+    block_layout "soa": the library calls use the SoA convention; the oracle
+    cache stays in combined slots (``oracle_cache_bytes`` converts it)."""
 
-    def __init__(self, w: W.Workload, need_oracle_cache: bool = True):
+    def __init__(self, w: W.Workload, need_oracle_cache: bool = True, block_layout: str = "aos"):
         t = torch()
         import quantized_decode_attention_tq_amd as tq
 
         self.w = w
+        self.soa = block_layout == "soa"
         self.lay = O.layout(w.preset, D)
-        self.lay_c = tq.layout_init(w.preset, D)
+        self.lay_c = tq.layout_init(w.preset, D, block_layout)
         self.lens = W.seq_lens(w)
         self.table = W.block_table(w)
         self.nb = W.num_blocks(w)
@@ -119,6 +122,14 @@ class DecodeCase:
         self.bt = t.from_numpy(self.table).cuda()
         self.sl = t.from_numpy(self.lens).cuda()
         self.scale = 1.0 / math.sqrt(D)
+
+    def oracle_cache_bytes(self):
+        """The oracle's cache in this case's block convention."""
+        return O.soa_from_aos(self.lay, self.cache_o) if self.soa else self.cache_o
+
+    def as_oracle_cache(self, cache_np):
+        """Cache bytes of this case's convention -> combined slots."""
+        return O.aos_from_soa(self.lay, cache_np) if self.soa else cache_np
 
     def gpu_store_all(self):
         """Fresh device cache filled by tq_store, one call per sequence."""

@@ -44,6 +44,43 @@ def test_layout_matches_oracle(preset, D):
     assert got["preset"] == list(O.PRESETS).index(preset)
 
 
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("D", [64, 128])
+def test_soa_layout_matches_oracle(preset, D):
+    """The SoA layout keeps every slot field of the combined one and adds the
+    oracle's SoA geometry (data bytes per row, metadata fields per row)."""
+    aos = tq.layout_init(preset, D).as_dict()
+    soa = tq.layout_init(preset, D, "soa").as_dict()
+    data, meta, nf = O.soa_geometry(O.layout(preset, D), 16, 1)
+    assert aos["block_layout"] == tq.LAYOUT_AOS and aos["soa_data_bytes"] == 0 and aos["soa_meta_fields"] == 0
+    assert soa["block_layout"] == tq.LAYOUT_SOA and soa["soa_data_bytes"] == data and soa["soa_meta_fields"] == nf
+    for k, v in aos.items():
+        if k not in ("block_layout", "soa_data_bytes", "soa_meta_fields"):
+            assert soa[k] == v, k
+    for bs in O.BLOCK_SIZES:
+        assert tq.kv_cache_shape(tq.layout_init(preset, D, "soa"), 5, bs, 3) == tq.kv_cache_shape(
+            tq.layout_init(preset, D), 5, bs, 3)
+
+
+def test_soa_layout_codes():
+    L = tq.Layout()
+    assert tq._lib.tq_layout_init_ex(0, 128, 2, ctypes.byref(L)) == tq.TQ_EINVAL
+    assert tq._lib.tq_layout_init_ex(0, 128, -1, ctypes.byref(L)) == tq.TQ_EINVAL
+    bad = tq.layout_init("turboquant_k3v4_nc", 128, "soa")
+    bad.soa_meta_fields = 2  # not what tq_layout_init_ex produces
+    assert _store_validate(bad) == tq.TQ_EINVAL
+    mixed = tq.layout_init("turboquant_k3v4_nc")
+    mixed.block_layout = tq.LAYOUT_SOA  # AoS sizes with the SoA flag
+    assert _store_validate(mixed) == tq.TQ_EINVAL
+    S = tq.layout_init("turboquant_k3v4_nc", 128, "soa")
+    # decode over SoA: all heads in one workgroup (<= 8) or groups of 8
+    for Hk, want in ((1, tq.TQ_OK), (3, tq.TQ_OK), (8, tq.TQ_OK), (16, tq.TQ_OK), (12, tq.TQ_EUNSUPPORTED),
+                     (10, tq.TQ_EUNSUPPORTED)):
+        assert _decode_validate(S, Hk=Hk, Hq=Hk * 4, wsb=tq.decode_workspace_bytes(4, Hk * 4, 128, 8)) == want, Hk
+    assert _dequant_validate(S) == tq.TQ_OK
+    assert _store_validate(S) == tq.TQ_OK
+
+
 def test_kv_cache_shape_and_presets():
     for p in O.PRESETS:
         L = tq.layout_init(p)
