@@ -9,7 +9,7 @@
  *          attention.py::_init_turboquant_buffers).
  *   [API]  vLLM API docs "vllm.v1.attention.backends.turboquant_attn":
  *          TurboQuantAttentionBackend, TurboQuantAttentionImpl.__init__,
- *          _ensure_on_device, do_kv_cache_update, _store_kv,
+ *          _ensure_on_device, do_kv_cache_update, forward, _store_kv,
  *          _continuation_prefill, _decode_attention.
  *   [TQ+]  Atlas docs "TurboQuant+ -- KV-cache compression beyond the Google
  *          baseline", sections "Background" and "What landed".
@@ -58,8 +58,21 @@ typedef enum {
  * supported_kv_cache_dtypes.  k8v4 = FP8 (E4M3) keys + 4-bit values;
  * 4bit_nc = 4-bit Lloyd-Max keys + 4-bit values; k3v4_nc = 3-bit keys +
  * 4-bit values; 3bit_nc = 3-bit keys + 3-bit values; "nc" = norm
- * correction (stored key norm is ||x|| / ||c[code]||, [TQ+] "Background"). */
-typedef enum { TQ_K8V4 = 0, TQ_4BIT_NC = 1, TQ_K3V4_NC = 2, TQ_3BIT_NC = 3 } tq_preset;
+ * correction (stored key norm is ||x|| / ||c[code]||, [TQ+] "Background").
+ * More codecs ([TQ+] "What landed": the 2-bit Lloyd-Max codebook, 4 codes
+ * per byte, and asymmetric K/V pairs): k8v3 = FP8 keys + 3-bit values;
+ * k4v3_nc = 4-bit keys + 3-bit values; 2bit_nc = 2-bit keys + 2-bit values.
+ * Names "turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc". */
+typedef enum {
+  TQ_K8V4 = 0,
+  TQ_4BIT_NC = 1,
+  TQ_K3V4_NC = 2,
+  TQ_3BIT_NC = 3,
+  TQ_K8V3 = 4,
+  TQ_K4V3_NC = 5,
+  TQ_2BIT_NC = 6,
+  TQ_NUM_PRESETS = 7
+} tq_preset;
 
 typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
 
@@ -122,7 +135,8 @@ const char* tq_status_str(int status);
 const char* tq_last_hip_error(void);
 
 /* "turboquant_k8v4" | "turboquant_4bit_nc" | "turboquant_k3v4_nc" |
- * "turboquant_3bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
+ * "turboquant_3bit_nc" | "turboquant_k8v3" | "turboquant_k4v3_nc" |
+ * "turboquant_2bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
 int tq_preset_from_name(const char* name, int32_t* preset);
 
 /* Fill *out for (preset, head_dim) (host), block_layout TQ_LAYOUT_AOS.

@@ -57,6 +57,16 @@ PRESETS = {
     "turboquant_4bit_nc": (False, 4, 4, True),
     "turboquant_k3v4_nc": (False, 3, 4, True),
     "turboquant_3bit_nc": (False, 3, 3, True),
+    # More codecs, from the Atlas page ([TQ+] "What landed": the 2-bit
+    # Lloyd-Max codebook "Turbo2", 4 codes per byte; asymmetric K/V pairs
+    # with FP8 keys or 4-bit keys over 3-bit values).  Reading: the pairs
+    # take this module's key codecs and its uniform value codec at the
+    # stated bit widths (the Atlas value codebook is not modelled); the
+    # 2-bit preset quantizes keys with the 2-bit Lloyd-Max codebook and
+    # values with the 2-bit uniform codec, norm-corrected like the others.
+    "turboquant_k8v3": (True, 8, 3, False),
+    "turboquant_k4v3_nc": (False, 4, 3, True),
+    "turboquant_2bit_nc": (False, 2, 2, True),
 }
 
 #: kernel block sizes the backend accepts ([PR] turboquant_attn.py excerpt,

@@ -25,11 +25,17 @@ struct PresetDef {
 
 // [PR] "实现拆解" item 1 (four named presets with key bits, value bits and
 // norm correction); "评论区精华" (k8v4 means FP8 keys and 4-bit values).
-constexpr PresetDef kPresets[4] = {
+// The last three follow [TQ+] "What landed": asymmetric pairs (FP8 or 4-bit
+// keys over 3-bit values) and the 2-bit codebook, with this library's key
+// and value codecs at those widths.
+constexpr PresetDef kPresets[TQ_NUM_PRESETS] = {
     {"turboquant_k8v4", 1, 8, 4, 0},
     {"turboquant_4bit_nc", 0, 4, 4, 1},
     {"turboquant_k3v4_nc", 0, 3, 4, 1},
     {"turboquant_3bit_nc", 0, 3, 3, 1},
+    {"turboquant_k8v3", 1, 8, 3, 0},
+    {"turboquant_k4v3_nc", 0, 4, 3, 1},
+    {"turboquant_2bit_nc", 0, 2, 2, 1},
 };
 
 }  // namespace
@@ -54,7 +60,7 @@ extern "C" const char* tq_status_str(int status) {
 
 extern "C" int tq_preset_from_name(const char* name, int32_t* preset) {
   if (!name || !preset) return TQ_EINVAL;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TQ_NUM_PRESETS; ++i) {
     if (std::strcmp(name, kPresets[i].name) == 0) {
       *preset = i;
       return TQ_OK;
@@ -74,7 +80,7 @@ extern "C" int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out) 
 
 extern "C" int tq_layout_init_ex(int32_t preset, int32_t head_dim, int32_t block_layout, tq_layout* out) {
   if (!out || (block_layout != TQ_LAYOUT_AOS && block_layout != TQ_LAYOUT_SOA)) return TQ_EINVAL;
-  if (preset < 0 || preset > 3) return TQ_EPRESET;
+  if (preset < 0 || preset >= TQ_NUM_PRESETS) return TQ_EPRESET;
   if (head_dim <= 0 || head_dim % 8 != 0) return TQ_EHEADDIM;
   const PresetDef& p = kPresets[preset];
   tq_layout L{};
@@ -290,7 +296,7 @@ int validate_store(const tq_layout* L, const void* key, const void* value, int32
                    int32_t num_kv_heads, int64_t key_tok_stride, int64_t val_tok_stride, const int64_t* slot_mapping,
                    const void* kv_cache, int64_t num_blocks, int32_t block_size, const float* signs,
                    const float* centroids, const float* boundaries) {
-  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset > 3) ? TQ_EPRESET : TQ_EINVAL;
+  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset >= TQ_NUM_PRESETS) ? TQ_EPRESET : TQ_EINVAL;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (in_dtype != TQ_F16 && in_dtype != TQ_BF16) return TQ_EDTYPE;
@@ -312,7 +318,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
                     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                     const float* signs, const float* centroids, int32_t num_kv_splits, const void* workspace,
                     size_t ws_bytes) {
-  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset > 3) ? TQ_EPRESET : TQ_EINVAL;
+  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset >= TQ_NUM_PRESETS) ? TQ_EPRESET : TQ_EINVAL;
   if (batch < 0 || num_blocks < 0 || block_table_stride < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return TQ_EGQA;
@@ -343,7 +349,7 @@ int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_block
                      int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
                      const float* centroids, const void* key_out, const void* value_out, int32_t out_dtype,
                      int64_t out_tok_stride) {
-  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset > 3) ? TQ_EPRESET : TQ_EINVAL;
+  if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset >= TQ_NUM_PRESETS) ? TQ_EPRESET : TQ_EINVAL;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (out_dtype != TQ_F16 && out_dtype != TQ_BF16 && out_dtype != TQ_F32) return TQ_EDTYPE;
