@@ -67,6 +67,9 @@ def warm_gpu(torch, fn, ms=150.0):
         spent += a.elapsed_time(b)
 
 
+MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc")
+
+
 class DecodeBench:
     """Device state of one decode workload: N_COPIES caches, the step's new
     tokens, queries, tables, workspace."""
@@ -211,14 +214,14 @@ class DecodeBench:
         return a.elapsed_time(b) / launches
 
 
-def store_sweep(torch, tq, steps, block_layout="aos"):
+def store_sweep(torch, tq, steps, block_layout="aos", presets=None):
     """Store sweep: 65536 tokens x 8 KV heads, bs 32, per preset (Mtok/s)."""
     s = W.STORE_WORKLOAD
     K, V, slots, nb = W.store_inputs()
     kd, vd = dev16(torch, K, s["dtype"]), dev16(torch, V, s["dtype"])
     sd = torch.from_numpy(slots).cuda()
     res = {}
-    for preset in s["presets"]:
+    for preset in presets or s["presets"]:
         lay = tq.layout_init(preset, 128, block_layout)
         tab = tq.Tables(lay, W.signs(s["seed"]))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, s["block_size"], s["num_kv_heads"]), dtype=torch.uint8,
@@ -327,7 +330,7 @@ def calibrate_copy(torch, mib: int = 512, reps: int = 5):
 DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS = 131072, 8, 128
 
 
-def dequant_sweep(torch, tq, reps, block_layout="aos"):
+def dequant_sweep(torch, tq, reps, block_layout="aos", presets=None):
     """Cached prefix back to dense fp16 K/V (tq_dequant_kv): one sequence of
     131072 tokens x 8 KV heads in 128-token blocks (the long-context shape),
     per preset.  Bytes = slots read + 2 x 128 fp16 written per (token, head);
@@ -343,7 +346,7 @@ def dequant_sweep(torch, tq, reps, block_layout="aos"):
     ko = torch.empty((n, Hk, 128), dtype=torch.float16, device="cuda")
     vo = torch.empty_like(ko)
     res = {}
-    for preset in ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
+    for preset in presets or ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
         lay = tq.layout_init(preset, 128, block_layout)
         tab = tq.Tables(lay, W.signs(21))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, bs, Hk), dtype=torch.uint8, device="cuda")
@@ -445,6 +448,25 @@ def main():
         log(f"[soa store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in soa['store_sweep'].items()})}; "
             f"[soa dequant] {json.dumps({k: round(v['gbs']) for k, v in soa['dequant'].items()})} GB/s")
         extra["soa"] = soa
+        # the further presets (asymmetric pairs, 2-bit) on the llama8b shape
+        more = {}
+        for preset in MORE_PRESETS:
+            wk = W.scaled(W.WORKLOADS["llama8b"], name=f"llama8b/{preset}", preset=preset)
+            b = DecodeBench(torch, tq, wk, args.splits)
+            s1 = b.time_stage1(30)
+            d = b.time_decode(30)
+            more[preset] = {"workload": "llama8b shape", "ms_per_decode_call": d,
+                            "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
+                            "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
+            log(f"[{preset}] llama8b shape: decode call {d * 1e3:.1f} us -> {more[preset]['decode_gbs']:.0f} GB/s; "
+                f"stage1 {s1 * 1e3:.1f} us")
+            del b
+            torch.cuda.empty_cache()
+        more["store_sweep"] = store_sweep(torch, tq, 50, presets=MORE_PRESETS)
+        more["dequant"] = dequant_sweep(torch, tq, 20, presets=MORE_PRESETS)
+        log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items()})}; "
+            f"[more dequant] {json.dumps({k: round(v['gbs']) for k, v in more['dequant'].items()})} GB/s")
+        extra["more_presets"] = more
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     line = {

@@ -32,6 +32,10 @@ TQ_HD void run_bits_op(int op, const uint32_t* in, uint32_t* out) {
     case 4: tq::lut16(in[0], tq::Lut8{in[1], in[2], in[3], in[4]}, tq::Lut8{in[5], in[6], in[7], in[8]}, out[0], out[1]); break;
     case 5: tq::val4_pairs(in[0], in[1], out); break;
     case 6: tq::val3_pairs(in[0], in[1], out); break;
+    case 8: tq::val2_pairs(in[0], in[1], out); break;
+    case 9:
+      for (int k = 0; k < 4; ++k) out[k] = tq::key2_selector(in[0], k);
+      break;
     case 7: {
       float f;
       uint32_t u = in[0];

@@ -133,6 +133,14 @@ TQ_HD int key3_dim(int c, int e) { return 8 * (e & 3) + 2 * c + (e >> 2); }
 // Chunk c element e holds dim 8c + (e < 4 ? 2e : 2(e - 4) + 1).
 TQ_HD int key4_dim(int c, int e) { return 8 * c + (e < 4 ? 2 * e : 2 * (e - 4) + 1); }
 
+// 2-bit keys: a lane chunk is 2 dwords, byte b of dword w holding dims
+// 16w + 4b .. 16w + 4b + 3 (code k of the byte at bits 2k).  Selector
+// (w >> 2k) & 0x03030303 holds dim 16w + 4b + k in byte b; chunk c takes
+// selectors k = 2(c & 1) and k + 1 of dword c >> 1, so element e holds dim
+// 16(c >> 1) + 4(e & 3) + 2(c & 1) + (e >> 2).
+TQ_HD uint32_t key2_selector(uint32_t w, int k) { return (w >> (2 * k)) & 0x03030303u; }
+TQ_HD int key2_dim(int c, int e) { return 16 * (c >> 1) + 4 * (e & 3) + 2 * (c & 1) + (e >> 2); }
+
 // ---------------------------------------------------------------------------
 // Value codes -> fp16 MFMA operand pairs, as fp16 subnormals.
 //
@@ -193,5 +201,25 @@ TQ_HD void val3_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
 }
 // code m starts at bit 3m of the word and its window starts at bit 8*floor(3m/8)
 TQ_HD int val3_pos(int m) { return (3 * m) & 7; }
+
+// 2-bit: wa, wb = 16 bits (bytes 0..1) = dims 8r..8r+7, code m at bits 2m.
+// out[m] = dim 8r+m of (a, b); code at bit position val2_pos(m) (codes 4..7
+// come from the word shifted down a byte, so no code reaches the exponent).
+struct Val2Pre {
+  uint32_t w[2];  // word bits 0..15 of a | of b; the same shifted right by 8
+};
+TQ_HD Val2Pre val2_pre(uint32_t wa, uint32_t wb) {
+  Val2Pre r;
+  r.w[0] = perm32(wb, wa, 0x05040100u);
+  r.w[1] = r.w[0] >> 8;
+  return r;
+}
+TQ_HD uint32_t val2_get(const Val2Pre& r, int m) { return r.w[m >> 2] & (0x00030003u << (2 * (m & 3))); }
+
+TQ_HD void val2_pairs(uint32_t wa, uint32_t wb, uint32_t out[8]) {
+  const Val2Pre r = val2_pre(wa, wb);
+  for (int m = 0; m < 8; ++m) out[m] = val2_get(r, m);
+}
+TQ_HD int val2_pos(int m) { return 2 * (m & 3); }
 
 }  // namespace tq

@@ -68,6 +68,18 @@ template <>
 struct Preset<TQ_3BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102;
 };
+template <>
+struct Preset<TQ_K8V3> {
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 180;
+};
+template <>
+struct Preset<TQ_K4V3_NC> {
+  static constexpr int kFp8 = 0, kKb = 4, kVb = 3, kKdata = 64, kKps = 66, kVdata = 48, kSlot = 118;
+};
+template <>
+struct Preset<TQ_2BIT_NC> {
+  static constexpr int kFp8 = 0, kKb = 2, kVb = 2, kKdata = 32, kKps = 34, kVdata = 32, kSlot = 70;
+};
 
 // SoA convention: data row = key data + value data; metadata record = kNf
 // 16-bit fields (norm, scale, zero; FP8 keys: scale, zero).
@@ -87,7 +99,9 @@ constexpr bool preset_geometry_ok() {
          T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + 4 + 1) / 2) * 2;
 }
 static_assert(preset_geometry_ok<TQ_K8V4>() && preset_geometry_ok<TQ_4BIT_NC>() &&
-                  preset_geometry_ok<TQ_K3V4_NC>() && preset_geometry_ok<TQ_3BIT_NC>(),
+                  preset_geometry_ok<TQ_K3V4_NC>() && preset_geometry_ok<TQ_3BIT_NC>() &&
+                  preset_geometry_ok<TQ_K8V3>() && preset_geometry_ok<TQ_K4V3_NC>() &&
+                  preset_geometry_ok<TQ_2BIT_NC>(),
               "slot geometry");
 
 struct DecodeArgs {
@@ -159,7 +173,8 @@ __device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return *reinterpret
 // MFMA chunk c, element e -> q*32 + c*8 + e, matching the order in which the
 // key operand holds dims (FP8 keys: quarter q loads dims 16q..16q+15 and
 // 64+16q..64+16q+15; 4-bit keys: even dims then odd dims of each byte group;
-// 3-bit keys: the selector order of tq::key3_selectors).
+// 3-bit keys: the selector order of tq::key3_selectors; 2-bit keys:
+// tq::key2_dim).
 template <int P>
 __device__ __forceinline__ int qh_pos(int d) {
   using T = Preset<P>;
@@ -172,6 +187,7 @@ __device__ __forceinline__ int qh_pos(int d) {
     const int r = dd & 7;
     return q * 32 + (dd >> 3) * 8 + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
   }
+  if (T::kKb == 2) return q * 32 + (2 * (dd >> 4) + ((dd & 3) >> 1)) * 8 + ((dd >> 2) & 3) + 4 * (dd & 1);
   return q * 32 + ((dd & 7) >> 1) * 8 + (dd & 1) * 4 + (dd >> 3);
 }
 
@@ -422,6 +438,17 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, c
       tq::lut16((w >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
       A[c] = as_half8(e0, e1, o0, o1);
     }
+  } else if constexpr (T::kKb == 2) {
+    const uint32_t w0 = SOA ? r.k[0] : tq::alignbyte(r.k[1], r.k[0], sh);
+    const uint32_t w1 = SOA ? r.k[1] : tq::alignbyte(r.k[2], r.k[1], sh);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = c < 2 ? w0 : w1;
+      uint32_t a0, a1, b0, b1;
+      tq::lut8(tq::key2_selector(w, 2 * (c & 1)), la, a0, a1);
+      tq::lut8(tq::key2_selector(w, 2 * (c & 1) + 1), la, b0, b1);
+      A[c] = as_half8(a0, a1, b0, b1);
+    }
   } else {
     uint32_t sel[8];
     if (SOA)
@@ -560,6 +587,14 @@ __device__ __forceinline__ void accumulate_pair(const PendingTile& a, const Pend
     for (int n = 0; n < 8; ++n)
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           as_half8(tq::val4_get(a01, n), tq::val4_get(a23, n), tq::val4_get(b01, n), tq::val4_get(b23, n)), bp,
+          acc[n], 0, 0, 0);
+  } else if constexpr (T::kVb == 2) {
+    const tq::Val2Pre a01 = tq::val2_pre(a.vw[0], a.vw[1]), a23 = tq::val2_pre(a.vw[2], a.vw[3]);
+    const tq::Val2Pre b01 = tq::val2_pre(b.vw[0], b.vw[1]), b23 = tq::val2_pre(b.vw[2], b.vw[3]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          as_half8(tq::val2_get(a01, n), tq::val2_get(a23, n), tq::val2_get(b01, n), tq::val2_get(b23, n)), bp,
           acc[n], 0, 0, 0);
   } else {
     const tq::Val3Pre a01 = tq::val3_pre(a.vw[0], a.vw[1]), a23 = tq::val3_pre(a.vw[2], a.vw[3]);
@@ -833,7 +868,7 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // inverse of qh_pos inside the lane's 32 dims
-        const int dd = T::kKb == 4 ? 8 * c + (e < 4 ? 2 * e : 2 * (e - 4) + 1) : (e & 3) * 8 + 2 * c + (e >> 2);
+        const int dd = T::kKb == 4 ? tq::key4_dim(c, e) : (T::kKb == 2 ? tq::key2_dim(c, e) : tq::key3_dim(c, e));
         h[e] = static_cast<_Float16>(v[dd] * qs);
       }
       bq[c] = h;
@@ -1128,7 +1163,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   query_operand<P>(a, b, hk, h0, geff, hl, q4, bq);
   tq::Lut8 la{}, lb{};
   if (!T::kFp8) {
-    uint32_t hb[16];
+    uint32_t hb[16] = {};
 #pragma unroll
     for (int i = 0; i < (1 << (T::kFp8 ? 0 : T::kKb)); ++i)
       hb[i] = __half_as_ushort(__float2half_rn(a.centroids[i]));
@@ -1145,21 +1180,21 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
     off.sd = static_cast<uint32_t>(G * S::kDb + a.soa_pad);  // image row: G data rows + the pad
     off.sm = static_cast<uint32_t>(G * S::kMb);
     off.k = hl * off.sd + static_cast<uint32_t>(hh * S::kDb) +
-            static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
+            static_cast<uint32_t>(T::kFp8 ? 16 * q4 : 4 * T::kKb * q4);
     off.ksh = 0u;
     off.mo[0] = static_cast<uint32_t>(4 * q4) * off.sd + static_cast<uint32_t>(hh * S::kDb);
     off.mo[1] = off.mo[2] = off.mo[3] = 0u;
-    off.vcol = static_cast<uint32_t>(T::kKdata + (T::kVb == 4 ? 4 * hl : 3 * hl));
+    off.vcol = static_cast<uint32_t>(T::kKdata + T::kVb * hl);
     off.mm0 = static_cast<uint32_t>(a.dslots) * 1024u + static_cast<uint32_t>(4 * q4) * off.sm +
               static_cast<uint32_t>(hh * S::kMb);
   } else {
     const uint32_t kraw = row_start(hl) + static_cast<uint32_t>(hh * T::kSlot) +
-                          static_cast<uint32_t>(T::kFp8 ? 16 * q4 : (T::kKb == 4 ? 16 * q4 : 12 * q4));
+                          static_cast<uint32_t>(T::kFp8 ? 16 * q4 : 4 * T::kKb * q4);
     off.k = kraw & ~3u;
     off.ksh = kraw & 3u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) off.mo[i] = row_start(4 * q4 + i) + static_cast<uint32_t>(hh * T::kSlot);
-    off.vcol = static_cast<uint32_t>(T::kKps + (T::kVb == 4 ? 4 * hl : 3 * hl));
+    off.vcol = static_cast<uint32_t>(T::kKps + T::kVb * hl);
     off.mm0 = off.sd = off.sm = 0u;
   }
 
@@ -1235,7 +1270,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int pos = T::kVb == 4 ? tq::val4_pos(n) : tq::val3_pos(n);
+        const int pos = T::kVb == 4 ? tq::val4_pos(n) : (T::kVb == 3 ? tq::val3_pos(n) : tq::val2_pos(n));
         o[8 * i + n] = fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
       }
     }
@@ -1472,6 +1507,9 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
     case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
     case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, soa, nblocks, lds, stream);
     case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }

@@ -265,6 +265,9 @@ extern "C" int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int6
     case TQ_4BIT_NC: return launch_dequant<0, 4, 4>(a, out_dtype, s);
     case TQ_K3V4_NC: return launch_dequant<0, 3, 4>(a, out_dtype, s);
     case TQ_3BIT_NC: return launch_dequant<0, 3, 3>(a, out_dtype, s);
+    case TQ_K8V3: return launch_dequant<1, 8, 3>(a, out_dtype, s);
+    case TQ_K4V3_NC: return launch_dequant<0, 4, 3>(a, out_dtype, s);
+    case TQ_2BIT_NC: return launch_dequant<0, 2, 2>(a, out_dtype, s);
   }
   return TQ_EPRESET;
 }

@@ -88,13 +88,22 @@ struct DecodePlan {
 
 // Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
 // this many for any head count at head_dim 128 (slots of 196 / 134 / 118 /
-// 102 bytes; a wave of G waves per tile takes ceil(spt / G) of the tile's
-// spt loads).  SoA images pad each image row by 16 bytes and round the data
-// part and the metadata part up to whole slots separately: with one KV head
-// that takes one load more for k8v4, 4bit_nc and 3bit_nc.
+// 102 / 180 / 118 / 70 bytes in preset order; a wave of G waves per tile
+// takes ceil(spt / G) of the tile's spt loads).  SoA images pad each image
+// row by 16 bytes and round the data part and the metadata part up to whole
+// slots separately, which takes one load more with one KV head for k8v4,
+// 4bit_nc, 3bit_nc and 2bit_nc.
 constexpr int max_dma_loads(int preset, bool soa = false) {
-  if (soa) return preset == TQ_K8V4 ? 5 : (preset == TQ_4BIT_NC ? 4 : 3);
-  return preset == TQ_K8V4 ? 4 : (preset == TQ_3BIT_NC ? 2 : 3);
+  switch (preset) {
+    case TQ_K8V4: return soa ? 5 : 4;
+    case TQ_4BIT_NC: return soa ? 4 : 3;
+    case TQ_K3V4_NC: return 3;
+    case TQ_3BIT_NC: return soa ? 3 : 2;
+    case TQ_K8V3: return 4;
+    case TQ_K4V3_NC: return 3;
+    case TQ_2BIT_NC: return soa ? 3 : 2;
+  }
+  return 0;
 }
 
 inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -346,6 +346,9 @@ int launch_preset(int32_t preset, const StoreArgs& a, bool bf16, hipStream_t s) 
     case TQ_4BIT_NC: return launch_store<0, 4, 4, 1>(a, bf16, s);
     case TQ_K3V4_NC: return launch_store<0, 3, 4, 1>(a, bf16, s);
     case TQ_3BIT_NC: return launch_store<0, 3, 3, 1>(a, bf16, s);
+    case TQ_K8V3: return launch_store<1, 8, 3, 0>(a, bf16, s);
+    case TQ_K4V3_NC: return launch_store<0, 4, 3, 1>(a, bf16, s);
+    case TQ_2BIT_NC: return launch_store<0, 2, 2, 1>(a, bf16, s);
   }
   return TQ_EPRESET;
 }

@@ -80,7 +80,7 @@ def test_lut8_and_lut16():
     np.testing.assert_array_equal(halves, h4[codes])
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_value_pairs_are_subnormal_codes(bits):
     """Each output half is code << pos, i.e. the fp16 subnormal code * 2^(pos-24)."""
     n = 3000
@@ -88,8 +88,9 @@ def test_value_pairs_are_subnormal_codes(bits):
     cb = RNG.integers(0, 1 << bits, (n, 8))
     wa = _bytes_to_words(O.pack_lsb(ca, bits))[:, 0]
     wb = _bytes_to_words(O.pack_lsb(cb, bits))[:, 0]
-    out = probe.bits_host("val4_pairs" if bits == 4 else "val3_pairs", np.column_stack([wa, wb]))
-    pos = [(m & 1) * 4 for m in range(8)] if bits == 4 else [(3 * m) & 7 for m in range(8)]
+    out = probe.bits_host({2: "val2_pairs", 3: "val3_pairs", 4: "val4_pairs"}[bits], np.column_stack([wa, wb]))
+    pos = {2: [2 * (m & 3) for m in range(8)], 3: [(3 * m) & 7 for m in range(8)],
+           4: [(m & 1) * 4 for m in range(8)]}[bits]
     for m in range(8):
         lo = out[:, m] & 0xFFFF
         hi = out[:, m] >> 16
@@ -98,3 +99,14 @@ def test_value_pairs_are_subnormal_codes(bits):
         assert np.all(lo < 0x400) and np.all(hi < 0x400)  # exponent field zero: subnormal or zero
         vals = lo.astype(np.uint16).view(np.float16).astype(np.float64)
         np.testing.assert_array_equal(vals, ca[:, m] * 2.0 ** (pos[m] - 24))
+
+
+def test_key2_selectors_put_one_code_per_byte():
+    """Selector k of a dword of 16 packed 2-bit codes holds, in byte b, the
+    code of dim 4b + k (the order the decode's 2-bit key operand takes)."""
+    codes = RNG.integers(0, 4, (3000, 16))
+    w = _bytes_to_words(O.pack_lsb(codes, 2))[:, 0]
+    out = probe.bits_host("key2_selectors", w[:, None])
+    for k in range(4):
+        for b in range(4):
+            np.testing.assert_array_equal((out[:, k] >> (8 * b)) & 0xFF, codes[:, 4 * b + k])
