@@ -719,19 +719,37 @@ def gather_sequence(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: in
     return decode_slots(lay, kv_cache[blk, t % bs, hk], centroids32)
 
 
-def attend(q, K, V, scale: float):
+def attend(q, K, V, scale: float, sink: float = -math.inf):
     """Textbook softmax attention of one query over (K, V), float64.
-    Returns (o, lse) with lse = log sum exp(scores); empty K gives (0, -inf)."""
-    if K.shape[0] == 0:
+    Returns (o, lse) with lse = log sum exp(scores); empty K gives (0, -inf).
+
+    sink: an attention-sink logit ([API] TurboQuantAttentionImpl.__init__
+    and _decode_attention pass per-head ``sinks`` to the decode kernel).
+    Reading: the sink is one more logit in the softmax denominator, in the
+    units of the scaled scores, with no value: o = sum_t e^{s_t} v_t /
+    (sum_t e^{s_t} + e^{sink}), lse = log(sum_t e^{s_t} + e^{sink});
+    -inf is no sink."""
+    s = scale * (K @ q) if K.shape[0] else np.zeros(0)
+    m = max(s.max() if len(s) else -math.inf, sink)
+    if m == -math.inf:
         return np.zeros(V.shape[1]), -math.inf
-    s = scale * (K @ q)
-    m = s.max()
     p = np.exp(s - m)
-    l = p.sum()
-    return (p @ V) / l, m + math.log(l)
+    l = p.sum() + math.exp(sink - m)
+    return (p @ V) / l if len(s) else np.zeros(V.shape[1]), m + math.log(l)
 
 
-def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids32, scale: float, rows=None):
+def window_start(seq_len: int, sliding_window: int) -> int:
+    """First token a decode query attends to ([API] TurboQuantAttentionImpl.__init__
+    takes ``sliding_window``; _decode_attention passes it to the decode
+    kernel).  Reading: the query (the sequence's last token) sees the last
+    ``sliding_window`` tokens, itself included; 0 or None means no window."""
+    if not sliding_window or sliding_window <= 0:
+        return 0
+    return max(0, seq_len - sliding_window)
+
+
+def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids32, scale: float, rows=None,
+           sliding_window: int = 0, sinks=None):
     """Decode attention of one query per sequence over the compressed cache.
 
     query: (B, Hq, D) float64.  GQA: query head hq reads KV head hq // g with
@@ -743,6 +761,8 @@ def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids
     = exact softmax attention over the dequantized cache (the split-KV +
     log-sum-exp merge of the kernels is a faster route to the same value).
     ``rows``: optional iterable of (b, hq) to compute; others stay NaN.
+    ``sliding_window`` / ``sinks`` (Hq logits): see ``window_start`` and
+    ``attend``.
     Returns (out (B,Hq,D), lse (B,Hq)).
     """
     query = np.asarray(query, dtype=np.float64)
@@ -759,8 +779,10 @@ def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids
         if (b, hk) not in cache:
             cache = {(b, hk): gather_sequence(lay, kv_cache, block_table[b], int(seq_lens[b]), hk, centroids32)}
         K, V = cache[(b, hk)]
+        f = window_start(int(seq_lens[b]), sliding_window)
         q = query[b, hq] if lay.key_fp8 else R @ query[b, hq]
-        out[b, hq], lse[b, hq] = attend(q, K, V, scale)
+        sink = -math.inf if sinks is None else float(sinks[hq])
+        out[b, hq], lse[b, hq] = attend(q, K[f:], V[f:], scale, sink)
     return out, lse
 
 
@@ -772,12 +794,15 @@ def split_ranges(seq_len: int, num_splits: int, block_size: int):
     return [(min(s * chunk, seq_len), min((s + 1) * chunk, seq_len)) for s in range(num_splits)]
 
 
-def merge_partials(parts):
+def merge_partials(parts, sink: float = -math.inf):
     """Log-sum-exp merge of (o_s, lse_s) partials, o_s normalized within its
     split: M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
     lse = M + log sum w_s; empty partials (lse = -inf) drop out ([PR]
-    "实现拆解" item 4: stage 2 performs the log-sum-exp reduction)."""
+    "实现拆解" item 4: stage 2 performs the log-sum-exp reduction).  A sink
+    logit joins the merge as one more weight with a zero output."""
     live = [(o, l) for o, l in parts if l != -math.inf]
+    if sink != -math.inf:
+        live.append((np.zeros_like(parts[0][0]), sink))
     if not live:
         return np.zeros_like(parts[0][0]), -math.inf
     M = max(l for _, l in live)
@@ -786,10 +811,10 @@ def merge_partials(parts):
     return o, M + math.log(w.sum())
 
 
-def decode_split(q_rot, K, V, scale: float, num_splits: int, block_size: int):
+def decode_split(q_rot, K, V, scale: float, num_splits: int, block_size: int, sink: float = -math.inf):
     """Stage 1 per split then stage 2, for one query over one sequence/head."""
     parts = [attend(q_rot, K[a:b], V[a:b], scale) for a, b in split_ranges(K.shape[0], num_splits, block_size)]
-    return merge_partials(parts)
+    return merge_partials(parts, sink)
 
 
 def dequant_original_space(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: int, signs, centroids32):

@@ -137,3 +137,33 @@ def test_soa_meta_offset_counting_the_norm_is_caught(monkeypatch):
 
     _patch(monkeypatch, "soa_geometry", bad)
     _fails(P.test_soa_geometry_matches_the_pages_constants, "turboquant_k3v4_nc", 16, 8)
+
+
+def test_sink_left_out_of_the_lse_is_caught(monkeypatch):
+    real = T.attend
+
+    def bad(q, K, V, scale, sink=-math.inf):
+        o, l = real(q, K, V, scale, sink)
+        return o, real(q, K, V, scale)[1]
+
+    _patch(monkeypatch, "attend", bad)
+    _fails(P.test_sink_closed_form_against_no_sink)
+
+
+def test_sink_in_the_numerator_is_caught(monkeypatch):
+    real = T.attend
+
+    def bad(q, K, V, scale, sink=-math.inf):  # the sink weight spread over the values
+        o, l = real(q, K, V, scale)
+        if sink == -math.inf or K.shape[0] == 0:
+            return real(q, K, V, scale, sink)
+        return o, np.logaddexp(l, sink)
+
+    _patch(monkeypatch, "attend", bad)
+    _fails(P.test_sink_closed_form_against_no_sink)
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    real = T.window_start
+    _patch(monkeypatch, "window_start", lambda L, W: max(0, real(L, W) - 1) if W else 0)
+    _fails(P.test_sliding_window_closed_forms)

@@ -680,3 +680,77 @@ def test_soa_store_equals_converted_combined_store():
     O.store_rows(lay, K[25:], V[25:], slots[25:], aos, s, c32, b32)
     O.store_soa(lay, K[25:], V[25:], slots[25:], soa, s, c32, b32)
     np.testing.assert_array_equal(soa, O.soa_from_aos(lay, aos))
+
+
+# ---------------------------------------------------------------- sinks and sliding window
+
+
+def _qkv(n, seed=0, D=16):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(D), rng.standard_normal((n, D)), rng.standard_normal((n, D))
+
+
+def test_sink_closed_form_against_no_sink():
+    """A sink logit only adds e^sink to the denominator: o_sink = o * e^lse /
+    (e^lse + e^sink) and lse_sink = logaddexp(lse, sink), for sinks below,
+    near and above the scores."""
+    q, K, V = _qkv(23, 1)
+    o0, l0 = O.attend(q, K, V, 0.3)
+    for sink in (-30.0, -1.0, 0.0, l0, 2.5, 40.0):
+        o, l = O.attend(q, K, V, 0.3, sink)
+        np.testing.assert_allclose(l, np.logaddexp(l0, sink), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(o, o0 * math.exp(l0 - np.logaddexp(l0, sink)), rtol=1e-11, atol=1e-14)
+    o, l = O.attend(q, K, V, 0.3, -math.inf)
+    np.testing.assert_array_equal(o, o0)
+    assert l == l0
+
+
+def test_sink_is_a_zero_valued_extra_logit():
+    """Brute force with a library softmax: scores plus the sink, values plus a
+    zero row."""
+    import scipy.special
+
+    q, K, V = _qkv(9, 2)
+    sink = 0.7
+    w = scipy.special.softmax(np.append(0.5 * (K @ q), sink))
+    o, l = O.attend(q, K, V, 0.5, sink)
+    np.testing.assert_allclose(o, w[:-1] @ V, rtol=1e-12)
+    np.testing.assert_allclose(l, scipy.special.logsumexp(np.append(0.5 * (K @ q), sink)), rtol=1e-13)
+    # no tokens: the output is 0 and the LSE is the sink alone
+    o, l = O.attend(q, K[:0], V[:0], 0.5, sink)
+    assert np.all(o == 0) and l == sink
+
+
+def test_sink_survives_the_split_merge():
+    q, K, V = _qkv(100, 3)
+    want = O.attend(q, K, V, 0.2, 1.3)
+    for S in (1, 3, 8):
+        o, l = O.decode_split(q, K, V, 0.2, S, 16, 1.3)
+        np.testing.assert_allclose(o, want[0], rtol=1e-11)
+        np.testing.assert_allclose(l, want[1], rtol=1e-12)
+
+
+def test_sliding_window_closed_forms():
+    """Window 1: the softmax over one token is that token's value exactly;
+    a window at least the length changes nothing; otherwise the attention of
+    the last W rows (scipy softmax)."""
+    import scipy.special
+
+    lay, s, c32, table, lens, cache, q, K, V = _tiny_cache("turboquant_k3v4_nc", lens=(37, 5))
+    qd = q
+    full = O.decode(lay, qd, cache, table, lens, s, c32, 0.25)
+    np.testing.assert_array_equal(O.decode(lay, qd, cache, table, lens, s, c32, 0.25, sliding_window=37)[0], full[0])
+    np.testing.assert_array_equal(O.decode(lay, qd, cache, table, lens, s, c32, 0.25, sliding_window=1000)[0], full[0])
+    one, lse1 = O.decode(lay, qd, cache, table, lens, s, c32, 0.25, sliding_window=1)
+    R = O.rotation(np.asarray(s, np.float64))
+    g = qd.shape[1] // cache.shape[2]
+    for b, L in enumerate(lens):
+        for hq in range(qd.shape[1]):
+            Kd, Vd = O.gather_sequence(lay, cache, table[b], int(L), hq // g, c32)
+            np.testing.assert_array_equal(one[b, hq], Vd[L - 1])
+            np.testing.assert_allclose(lse1[b, hq], 0.25 * Kd[L - 1] @ (R @ qd[b, hq]), rtol=1e-12)
+            for W in (3, 16, 17):
+                o, l = O.decode(lay, qd, cache, table, lens, s, c32, 0.25, rows=[(b, hq)], sliding_window=W)
+                sc = 0.25 * (Kd[max(0, L - W):] @ (R @ qd[b, hq]))
+                np.testing.assert_allclose(o[b, hq], scipy.special.softmax(sc) @ Vd[max(0, L - W):], rtol=1e-11)
+                np.testing.assert_allclose(l[b, hq], scipy.special.logsumexp(sc), rtol=1e-12)
