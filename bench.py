@@ -74,9 +74,11 @@ class DecodeBench:
     """Device state of one decode workload: N_COPIES caches, the step's new
     tokens, queries, tables, workspace."""
 
-    def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos"):
+    def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos",
+                 sliding_window: int = 0, sinks=None):
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
+        self.window = sliding_window
         self.lay = tq.layout_init(w.preset, 128, block_layout)
         self.lens = W.seq_lens(w)
         table = W.block_table(w)
@@ -114,7 +116,9 @@ class DecodeBench:
         self.out = torch.empty((w.batch, w.num_q_heads, 128), dtype=self.q.dtype, device="cuda")
         self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
         self.scale = 1.0 / math.sqrt(128)
-        self.bytes_read = int(self.lens.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
+        seen = np.minimum(self.lens, sliding_window) if sliding_window > 0 else self.lens
+        self.bytes_read = int(seen.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
+        self.sinks = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
         torch.cuda.synchronize()
         it = iter(range(1 << 30))
         warm_gpu(torch, lambda: self.step(next(it) % N_COPIES))
@@ -125,10 +129,11 @@ class DecodeBench:
 
     def stage1(self, i):
         self.tq.decode_stage1(self.lay, self.q, self.caches[i], self.bt, self.sl, self.tab.signs, self.tab.centroids,
-                              self.scale, self.S, self.ws)
+                              self.scale, self.S, self.ws, sliding_window=self.window)
 
     def stage2(self):
-        self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, 128, self.S, self.ws, self.out, self.lse)
+        self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, 128, self.S, self.ws, self.out, self.lse,
+                              sinks=self.sinks)
 
     def step(self, i):
         self.store(i)
@@ -467,6 +472,19 @@ def main():
         log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items()})}; "
             f"[more dequant] {json.dumps({k: round(v['gbs']) for k, v in more['dequant'].items()})} GB/s")
         extra["more_presets"] = more
+        # sliding window + attention sinks: long context with an 8192-token window
+        wk = W.WORKLOADS["longctx"]
+        b = DecodeBench(torch, tq, wk, 32, sliding_window=8192,
+                        sinks=np.random.default_rng(0).uniform(-2, 6, wk.num_q_heads))
+        s1 = b.time_stage1(30)
+        d = b.time_decode(30)
+        extra["window_sinks"] = {"workload": "longctx, sliding_window 8192, per-head sinks", "ms_per_decode_call": d,
+                                 "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
+                                 "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
+        log(f"[window+sinks] longctx W=8192: decode call {d * 1e3:.1f} us -> "
+            f"{extra['window_sinks']['decode_gbs']:.0f} GB/s; stage1 {s1 * 1e3:.1f} us")
+        del b
+        torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     line = {

@@ -225,8 +225,8 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  * log-sum-exp reduction).  Query head hq reads KV head hq / (Hq/Hk).  MSE
  * keys are scored against the query rotated by the same transform;
  * FP8 keys against the raw query.  Result = softmax(scale * q.k) v over
- * tokens [0, seq_lens[b]) of each sequence; seq_lens[b] == 0 gives o = 0
- * and lse = -inf.
+ * tokens [w_b, seq_lens[b]) of each sequence, w_b the window start; an empty
+ * range gives o = 0 and lse = -inf (lse = the sink with sinks).
  * Arguments:
  *   query        device [batch, num_q_heads, head_dim], dtype q_dtype
  *                (TQ_F16 | TQ_BF16), contiguous.
@@ -243,42 +243,56 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *                units in proportion to its length, each a contiguous range
  *                of 16-token tiles; the launch shape depends only on the
  *                arguments, never on device data.
+ *   sliding_window  > 0: each query sees the last sliding_window tokens of
+ *                its sequence, itself included (w_b = max(0, seq_len -
+ *                sliding_window)); 0: the whole sequence.  ([API]
+ *                TurboQuantAttentionImpl.__init__ keeps sliding_window and
+ *                _decode_attention hands it to the decode kernel; the window
+ *                reading is this library's.)  Tiles before the window are
+ *                neither read nor counted in the work split.
+ *   sinks        device fp32 [num_q_heads] attention-sink logits, or NULL
+ *                ([API] TurboQuantAttentionImpl.__init__ / _decode_attention
+ *                pass per-head sinks).  Reading: one more logit in each
+ *                head's softmax denominator, in the units of scale * q.k,
+ *                with no value: o = sum_t e^{s_t} v_t / (sum_t e^{s_t} +
+ *                e^{sink}); the lse includes it.  Applied in stage 2.
  *   workspace    device, >= tq_decode_workspace_bytes(batch, num_q_heads,
  *                head_dim, S) bytes, 16-byte aligned; contents are scratch.
  *   out          device [batch, num_q_heads, head_dim], dtype out_dtype
  *                (TQ_F16 | TQ_BF16 | TQ_F32), contiguous.
  *   lse_out      device fp32 [batch, num_q_heads] natural-log LSE, or NULL.
  * Supported: head_dim 128, block_size 16/32/64/128, num_q_heads a multiple
- * of num_kv_heads. */
+ * of num_kv_heads, sliding_window >= 0 (TQ_EINVAL otherwise). */
 int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                         int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                         int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                         const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
-                        int32_t num_kv_splits, void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
-                        float* lse_out, void* stream);
+                        int32_t num_kv_splits, int32_t sliding_window, const float* sinks, void* workspace,
+                        size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out, void* stream);
 
 /* Host-only check of tq_decode_attention's arguments. */
 int tq_decode_validate(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                        int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                        int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                        const int32_t* seq_lens, const float* signs, const float* centroids, int32_t num_kv_splits,
-                       const void* workspace, size_t workspace_bytes, const void* out, int32_t out_dtype);
+                       int32_t sliding_window, const void* workspace, size_t workspace_bytes, const void* out,
+                       int32_t out_dtype);
 
 /* The two launches of tq_decode_attention, exposed separately so that each
  * can be timed on its own.  Stage 1 writes the workspace table and the
  * partial rows of every work unit; stage 2 merges each sequence's units into
- * out / lse_out.  Same arguments and checks as tq_decode_attention; stage 2
- * must run on a workspace written by stage 1 with the same batch and
- * num_q_heads. */
+ * out / lse_out.  Same arguments and checks as tq_decode_attention (stage 1
+ * takes the window, stage 2 the sinks); stage 2 must run on a workspace
+ * written by stage 1 with the same batch and num_q_heads. */
 int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                      int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                      const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
-                     const float* signs, const float* centroids, float scale, int32_t num_kv_splits, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     const float* signs, const float* centroids, float scale, int32_t num_kv_splits,
+                     int32_t sliding_window, void* workspace, size_t workspace_bytes, void* stream);
 
 int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
-                     const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
-                     void* stream);
+                     const float* sinks, const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                     float* lse_out, void* stream);
 
 /* Dequantize the cached prefix of one sequence back to dense K and V in the
  * original space, the first step of a continuation prefill ([API]

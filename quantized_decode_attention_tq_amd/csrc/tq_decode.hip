@@ -125,6 +125,7 @@ struct DecodeArgs {
   int32_t soa_pad;     // SoA: pad bytes after each image row of data (a multiple of 16)
   int32_t block_size, bt_stride;
   int32_t batch, num_units;  // B, U
+  int32_t window;            // sliding window in tokens, 0 = the whole sequence
 };
 
 __device__ __forceinline__ float widen16(uint32_t bits, bool bf16) {
@@ -491,7 +492,7 @@ struct PendingTile {
 // pending tile (when `have_pend`) are rescaled to it.
 template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
-                                           const tq::Lut8& lb, const half8 bq[4], int valid, Softmax& sm,
+                                           const tq::Lut8& lb, const half8 bq[4], int valid, int skip, Softmax& sm,
                                            f32x4 acc[8], PendingTile& pend, bool have_pend, PendingTile& cur) {
   using T = Preset<P>;
   half8 A[4];
@@ -513,10 +514,11 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
     sz[i] = r.sz[i];
   }
   const int lane = threadIdx.x & 63;
-  if (__builtin_expect(valid < 16, 0)) {  // tail tile: tokens at or past the sequence end drop out
+  if (__builtin_expect(valid < 16 || skip > 0, 0)) {  // tokens past the end or before the window drop out
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (4 * (lane >> 4) + i >= valid) {
+      const int j = 4 * (lane >> 4) + i;
+      if (j >= valid || j < skip) {
         sco[i] = -INFINITY;
         sz[i] = 0u;  // the bytes past the end may hold anything (a NaN scale)
       }
@@ -631,7 +633,8 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4],
-                                                  int validA, int validB, Softmax& sm, f32x4 acc[8]) {
+                                                  int validA, int validB, int skipA, int skipB, Softmax& sm,
+                                                  f32x4 acc[8]) {
   using T = Preset<P>;
   const int lane = threadIdx.x & 63;
   const bool tileB = (lane & 8) != 0;
@@ -672,10 +675,12 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
     sz[i] = own.sz[i];
   }
   const int valid = tileB ? validB : validA;
-  if (__builtin_expect(validA < 16 || validB < 16, 0)) {
+  const int skip = tileB ? skipB : skipA;
+  if (__builtin_expect(validA < 16 || validB < 16 || skipA > 0, 0)) {  // (a window start falls in tile A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (4 * (lane >> 4) + i >= valid) {
+      const int j = 4 * (lane >> 4) + i;
+      if (j >= valid || j < skip) {
         sco[i] = -INFINITY;
         sz[i] = 0u;  // the bytes past the end may hold anything (a NaN scale)
       }
@@ -909,9 +914,21 @@ struct UnitRange {
 // are consecutive and split its tiles evenly (ceil(tiles_b / S_b) each).
 // Deterministic, so every workgroup derives the same assignment from
 // seq_lens alone; uniform lengths give each sequence U / batch equal units.
-__device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_lens, int B, int U, int u) {
+// First token a sequence's query attends to: the last `window` tokens
+// (itself included), or all of them with no window.
+__device__ __forceinline__ int window_start(int seq_len, int window) {
+  return window > 0 ? max(0, seq_len - window) : 0;
+}
+
+__device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_lens, int B, int U, int u,
+                                               int window) {
   const int lane = threadIdx.x & 63;
-  auto tiles = [&](int bb) { return bb < B ? (seq_lens[bb] + 15) >> 4 : 0; };
+  // tiles of sequence bb inside its window (tile indices from the window's first tile)
+  auto tiles = [&](int bb) {
+    if (bb >= B) return 0;
+    const int L = seq_lens[bb];
+    return L > 0 ? ((L + 15) >> 4) - (window_start(L, window) >> 4) : 0;
+  };
   int T = 0, tmx = 0;
   for (int bb = lane; bb < B; bb += 64) {
     const int t = tiles(bb);
@@ -995,7 +1012,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   const int hl = lane & 15, q4 = lane >> 4;
 
   // ---- unit -> (sequence, tile range): length-balanced split ----
-  UnitRange ur = find_unit(a.seq_lens, a.batch, a.num_units, u);
+  UnitRange ur = find_unit(a.seq_lens, a.batch, a.num_units, u, a.window);
   // uniform by construction (cross-lane results): tell the compiler
   ur.b = __builtin_amdgcn_readfirstlane(ur.b);
   ur.t_begin = __builtin_amdgcn_readfirstlane(ur.t_begin);
@@ -1009,8 +1026,9 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   if (ur.b < 0) return;  // idle unit (uniform over the workgroup)
   const int b = ur.b;
   const int seqlen = a.seq_lens[b];
-  const int t_begin = ur.t_begin;
-  const int t_end = ur.t_end;
+  const int wstart = window_start(seqlen, a.window);  // tokens before it are masked out of their tile
+  const int t_begin = ur.t_begin + (wstart >> 4);     // absolute tile indices of the sequence
+  const int t_end = ur.t_end + (wstart >> 4);
   const int h0 = hg * 16;
   const int geff = min(16, g - h0);
   const int64_t prow0 = static_cast<int64_t>(u) * Hq + hk * g + h0;  // partial row of query head h0
@@ -1222,8 +1240,8 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
         const uint8_t* img =
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
         score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, bq,
-                             min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0, sm,
-                             acc);
+                                  min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
+                                  max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), sm, acc);
       }
     } else {
 #pragma unroll
@@ -1235,7 +1253,8 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
         load_tile<P, SOA>(img, off, r);
         PendingTile cur;
-        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), sm, acc, pend, have_pend, cur);
+        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), sm, acc, pend,
+                           have_pend, cur);
         if (have_pend) {
           accumulate_pair<P>(pend, cur, acc);
           have_pend = false;
@@ -1342,7 +1361,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 template <int kW>
 __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
                                                                const float* __restrict__ part, int Hq, int rows,
-                                                               void* out, int out_dtype, float* lse_out) {
+                                                               void* out, int out_dtype, float* lse_out,
+                                                               const float* __restrict__ sinks) {
   constexpr int kBatch = 16;
   __shared__ float comb[kW > 1 ? kW - 1 : 1][2 * 64 + 2];
   const int lane = threadIdx.x & 63;
@@ -1398,6 +1418,9 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
   float Mt = M;
 #pragma unroll
   for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][128]);  // no-op for kW == 1
+  // an attention sink: one more term of the denominator, with no value
+  const float sink = sinks ? sinks[hq] : -INFINITY;
+  Mt = fmaxf(Mt, sink);
   float lse = -INFINITY;
   if (Mt != -INFINITY) {
     float a0 = M == -INFINITY ? 0.f : expf(M - Mt);
@@ -1413,6 +1436,7 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
       o0 = fmaf(ak, comb[k][2 * lane], o0);
       o1 = fmaf(ak, comb[k][2 * lane + 1], o1);
     }
+    if (sink != -INFINITY) den += expf(sink - Mt);
     o0 /= den;
     o1 /= den;
     lse = Mt + logf(den);
@@ -1468,8 +1492,9 @@ int launch_stage1(const DecodeArgs& a, int tpw, bool soa, int64_t nblocks, size_
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
            int32_t num_kv_heads, const void* kv_cache, int32_t block_size, const int32_t* block_table,
            int32_t block_table_stride, const int32_t* seq_lens, const float* signs, const float* centroids,
-           float scale, int32_t num_kv_splits, void* workspace, hipStream_t stream) {
+           float scale, int32_t num_kv_splits, int32_t sliding_window, void* workspace, hipStream_t stream) {
   DecodeArgs a;
+  a.window = sliding_window;
   a.query = static_cast<const uint16_t*>(query);
   a.cache = static_cast<const uint8_t*>(kv_cache);
   a.block_table = block_table;
@@ -1514,13 +1539,13 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   return TQ_EPRESET;
 }
 
-int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const void* workspace, void* out,
-           int32_t out_dtype, float* lse_out, hipStream_t stream) {
+int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const float* sinks, const void* workspace,
+           void* out, int32_t out_dtype, float* lse_out, hipStream_t stream) {
   int rows = batch * num_q_heads;
   int Hq = num_q_heads;
   const int32_t* table = static_cast<const int32_t*>(workspace);
   const float* part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + tq::table_bytes(batch));
-  void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out};
+  void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out, &sinks};
   // rows of many units share 4 waves; otherwise one wave per row.  The bound
   // on units per sequence is S_max (balanced units give long sequences more,
   // so the threshold leaves room).
@@ -1550,23 +1575,24 @@ extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int3
                                 int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                                 int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                                 const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
-                                int32_t num_kv_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                                int32_t num_kv_splits, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   int st = tq::validate_decode(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                                block_size, block_table, block_table_stride, seq_lens, signs, centroids,
-                               num_kv_splits, workspace, workspace_bytes);
+                               num_kv_splits, sliding_window, workspace, workspace_bytes);
   if (st != TQ_OK || batch == 0) return st;
   return stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
-                block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace,
+                block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, workspace,
                 static_cast<hipStream_t>(stream));
 }
 
 extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
-                                const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
-                                float* lse_out, void* stream) {
+                                const float* sinks, const void* workspace, size_t workspace_bytes, void* out,
+                                int32_t out_dtype, float* lse_out, void* stream) {
   int st = tq::validate_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace, workspace_bytes, out,
                                out_dtype);
   if (st != TQ_OK || batch == 0) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out,
+  return stage2(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -1574,16 +1600,17 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
                                    int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache,
                                    int64_t num_blocks, int32_t block_size, const int32_t* block_table,
                                    int32_t block_table_stride, const int32_t* seq_lens, const float* signs,
-                                   const float* centroids, float scale, int32_t num_kv_splits, void* workspace,
+                                   const float* centroids, float scale, int32_t num_kv_splits,
+                                   int32_t sliding_window, const float* sinks, void* workspace,
                                    size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
                                    void* stream) {
   int st = tq_decode_validate(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                               block_size, block_table, block_table_stride, seq_lens, signs, centroids, num_kv_splits,
-                              workspace, workspace_bytes, out, out_dtype);
+                              sliding_window, workspace, workspace_bytes, out, out_dtype);
   if (st != TQ_OK || batch == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
-              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, workspace, s);
+              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, workspace, s);
   if (st != TQ_OK) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, workspace, out, out_dtype, lse_out, s);
+  return stage2(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, s);
 }

@@ -145,16 +145,18 @@ class DecodeCase:
                      self.tab.signs, self.tab.centroids, self.tab.boundaries)
         return cache
 
-    def gpu_decode(self, cache, num_kv_splits, out_dtype=None):
+    def gpu_decode(self, cache, num_kv_splits, out_dtype=None, sliding_window=0, sinks=None):
         import quantized_decode_attention_tq_amd as tq
 
         t = torch()
+        sk = None if sinks is None else t.from_numpy(np.asarray(sinks, np.float32)).cuda()
         out, lse = tq.decode(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids,
-                             self.scale, num_kv_splits, out_dtype=out_dtype or t.float32)
+                             self.scale, num_kv_splits, out_dtype=out_dtype or t.float32,
+                             sliding_window=sliding_window, sinks=sk)
         t.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
-    def gpu_decode_two_stage(self, cache, num_kv_splits, workspace_fill=None):
+    def gpu_decode_two_stage(self, cache, num_kv_splits, workspace_fill=None, sliding_window=0, sinks=None):
         """tq_decode_stage1 then tq_decode_stage2 (the split entry points)."""
         import quantized_decode_attention_tq_amd as tq
 
@@ -164,19 +166,21 @@ class DecodeCase:
         if workspace_fill is not None:
             ws.fill_(workspace_fill)
         tq.decode_stage1(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids, self.scale,
-                         num_kv_splits, ws)
+                         num_kv_splits, ws, sliding_window=sliding_window)
         out = t.empty((B, Hq, 128), dtype=t.float32, device="cuda")
         lse = t.empty((B, Hq), dtype=t.float32, device="cuda")
-        tq.decode_stage2(B, Hq, 128, num_kv_splits, ws, out, lse)
+        sk = None if sinks is None else t.from_numpy(np.asarray(sinks, np.float32)).cuda()
+        tq.decode_stage2(B, Hq, 128, num_kv_splits, ws, out, lse, sinks=sk)
         t.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
-    def oracle_decode(self, rows=None, cache=None):
+    def oracle_decode(self, rows=None, cache=None, sliding_window=0, sinks=None):
         q = O.widen(self.qbits, self.w.dtype)
+        sk = None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64)
         return O.decode(self.lay, q, self.cache_o if cache is None else cache, self.table, self.lens, self.signs,
-                        self.c32, self.scale, rows=rows)
+                        self.c32, self.scale, rows=rows, sliding_window=sliding_window, sinks=sk)
 
-    def oracle_decode_rows_from_inputs(self, rows):
+    def oracle_decode_rows_from_inputs(self, rows, sliding_window=0, sinks=None):
         """Oracle result for (b, hq) rows, storing only the needed sequence /
         KV head from the raw inputs (full-size workloads)."""
         w = self.w
@@ -191,7 +195,9 @@ class DecodeCase:
                                    R, self.c32, self.b32)
             Kd, Vd = O.decode_slots(self.lay, slots, self.c32)
             qq = q[b, hq] if self.lay.key_fp8 else R @ q[b, hq]
-            res[(b, hq)] = O.attend(qq, Kd[:L], Vd[:L], self.scale)
+            f = O.window_start(L, sliding_window)
+            sink = -math.inf if sinks is None else float(np.float32(sinks[hq]))
+            res[(b, hq)] = O.attend(qq, Kd[f:L], Vd[f:L], self.scale, sink)
         return res
 
 

@@ -168,12 +168,12 @@ def test_store_validation_codes():
 
 def _decode_validate(L, **kw):
     args = dict(q=A, qd=tq.TQ_BF16, B=4, Hq=32, Hk=8, cache=A, nb=100, bs=16, bt=A, bts=64, sl=A, signs=A, cent=A,
-                S=8, ws=A, wsb=tq.decode_workspace_bytes(4, 32, 128, 8), out=A, od=tq.TQ_F32)
+                S=8, win=0, ws=A, wsb=tq.decode_workspace_bytes(4, 32, 128, 8), out=A, od=tq.TQ_F32)
     args.update(kw)
     return tq._lib.tq_decode_validate(ctypes.byref(L), args["q"], args["qd"], args["B"], args["Hq"], args["Hk"],
                                       args["cache"], args["nb"], args["bs"], args["bt"], args["bts"], args["sl"],
-                                      args["signs"], args["cent"], args["S"], args["ws"], args["wsb"], args["out"],
-                                      args["od"])
+                                      args["signs"], args["cent"], args["S"], args["win"], args["ws"], args["wsb"],
+                                      args["out"], args["od"])
 
 
 def test_decode_validation_codes():
@@ -186,6 +186,8 @@ def test_decode_validation_codes():
     assert _decode_validate(L, qd=tq.TQ_F32) == tq.TQ_EDTYPE
     assert _decode_validate(L, od=7) == tq.TQ_EDTYPE
     assert _decode_validate(L, S=0) == tq.TQ_EINVAL
+    assert _decode_validate(L, win=-1) == tq.TQ_EINVAL
+    assert _decode_validate(L, win=4096) == tq.TQ_OK
     assert _decode_validate(L, sl=None) == tq.TQ_EINVAL
     assert _decode_validate(L, ws=A + 8) == tq.TQ_EINVAL
     assert _decode_validate(L, signs=None) == tq.TQ_EINVAL
