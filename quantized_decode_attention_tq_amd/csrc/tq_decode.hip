@@ -1513,7 +1513,9 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   a.bt_stride = block_table_stride;
   a.batch = batch;
   tq::DecodePlan plan;
-  const int64_t max_tiles = (static_cast<int64_t>(block_table_stride) * block_size + 15) / 16;
+  // tiles of the longest possible sequence (block-table width), or of a window
+  int64_t max_tiles = (static_cast<int64_t>(block_table_stride) * block_size + 15) / 16;
+  if (sliding_window > 0) max_tiles = std::min<int64_t>(max_tiles, (sliding_window + 15) / 16 + 1);
   const int st = tq::decode_plan(layout, batch, num_q_heads, num_kv_heads, num_kv_splits, max_tiles, &plan);
   if (st != TQ_OK) return st;
   a.num_units = static_cast<int32_t>(plan.units);

@@ -54,6 +54,10 @@ int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_block
 constexpr int64_t kTargetWorkgroups = 512;
 // SoA tile images: bytes of padding after each image row of data (G data rows)
 constexpr int kSoaRowPad = 16;
+// The raise of S_int stops where a unit of the longest possible sequence
+// would hold fewer tiles than this: a unit's fixed cost (work search, query
+// rotation, ring fill) needs a few tiles to amortize.
+constexpr int64_t kMinTilesPerUnit = 16;
 constexpr int64_t kPartPad = 4;  // LSE + 3 pad floats after the head_dim outputs
 
 inline int64_t table_bytes(int64_t batch) { return (8 * batch + 255) / 256 * 256; }
@@ -132,7 +136,9 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   const int64_t wg_per_unit = (num_kv_heads / G) * hgroups;
   const int64_t per = static_cast<int64_t>(batch) * num_splits * wg_per_unit;
   int64_t s_int = num_splits * (per > 0 && per < kTargetWorkgroups ? (kTargetWorkgroups + per - 1) / per : 1);
-  const int64_t cap = (max_tiles + P - 1) / P;  // more units than P-tile steps per sequence are idle
+  const int64_t cap_p = (max_tiles + P - 1) / P;  // more units than P-tile steps per sequence are idle
+  const int64_t cap_t = (max_tiles + kMinTilesPerUnit - 1) / kMinTilesPerUnit;
+  const int64_t cap = cap_p < cap_t ? cap_p : cap_t;
   if (s_int > num_splits && s_int > cap) s_int = cap > num_splits ? cap : num_splits;
   const int64_t piece = G * slot;
   const int64_t tc_max = contiguous ? row : 16 * ((piece + 30) / 16);  // chunks per tile image
