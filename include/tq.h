@@ -62,7 +62,11 @@ typedef enum {
  * More codecs ([TQ+] "What landed": the 2-bit Lloyd-Max codebook, 4 codes
  * per byte, and asymmetric K/V pairs): k8v3 = FP8 keys + 3-bit values;
  * k4v3_nc = 4-bit keys + 3-bit values; 2bit_nc = 2-bit keys + 2-bit values.
- * Names "turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc". */
+ * Names "turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc".
+ * Lloyd-Max values ([TQ+] "What landed": values take the keys' rotation and
+ * Lloyd-Max codebook with the matched-norm correction): k8v3lm = FP8 keys +
+ * 3-bit Lloyd-Max values; 3bit_lm = 3-bit keys + 3-bit Lloyd-Max values.
+ * Names "turboquant_k8v3lm", "turboquant_3bit_lm". */
 typedef enum {
   TQ_K8V4 = 0,
   TQ_4BIT_NC = 1,
@@ -71,7 +75,9 @@ typedef enum {
   TQ_K8V3 = 4,
   TQ_K4V3_NC = 5,
   TQ_2BIT_NC = 6,
-  TQ_NUM_PRESETS = 7
+  TQ_K8V3LM = 7,
+  TQ_3BIT_LM = 8,
+  TQ_NUM_PRESETS = 9
 } tq_preset;
 
 typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
@@ -121,7 +127,9 @@ typedef struct tq_layout {
   int32_t slot_size_aligned;
   int32_t block_layout;    /* tq_block_layout */
   int32_t soa_data_bytes;  /* SoA: key_data_bytes + value_data_bytes; 0 for AoS */
-  int32_t soa_meta_fields; /* SoA: 3 (MSE keys) or 2 (FP8 keys); 0 for AoS */
+  int32_t soa_meta_fields; /* SoA: 3 (MSE keys) or 2 (FP8 keys); one fewer with Lloyd-Max values; 0 for AoS */
+  int32_t value_lloyd_max; /* 1: values are rotated Lloyd-Max codes + fp16 norm (value region [codes |
+                              norm]); 0: uniform codes + fp16 scale + fp16 zero */
 } tq_layout;
 
 /* Library version string (static storage). */
@@ -136,7 +144,8 @@ const char* tq_last_hip_error(void);
 
 /* "turboquant_k8v4" | "turboquant_4bit_nc" | "turboquant_k3v4_nc" |
  * "turboquant_3bit_nc" | "turboquant_k8v3" | "turboquant_k4v3_nc" |
- * "turboquant_2bit_nc" -> preset id (host).  TQ_EPRESET for other names. */
+ * "turboquant_2bit_nc" | "turboquant_k8v3lm" | "turboquant_3bit_lm" ->
+ * preset id (host).  TQ_EPRESET for other names. */
 int tq_preset_from_name(const char* name, int32_t* preset);
 
 /* Fill *out for (preset, head_dim) (host), block_layout TQ_LAYOUT_AOS.
@@ -204,9 +213,14 @@ int tq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_d
  *   kv_cache         device bytes, shape tq_kv_cache_shape(...).  Only the
  *                    addressed slots are written.  Slots must be distinct
  *                    (two tokens mapped to one slot race).
- *   signs            device fp32 [head_dim] (MSE presets; may be NULL for FP8).
+ *   signs            device fp32 [head_dim] (MSE keys or Lloyd-Max values;
+ *                    may be NULL otherwise).
  *   centroids        device fp32 [n_centroids]; boundaries device fp32
  *                    [n_centroids - 1] (MSE presets; NULL for FP8 keys).
+ *                    Lloyd-Max value layouts append the value codebook:
+ *                    centroids [key codebook (MSE keys) | 2^value_bits],
+ *                    boundaries [key boundaries | 2^value_bits - 1]; the
+ *                    decode and dequant read centroids the same way.
  * Supported: head_dim 128, block_size 16/32/64/128, num_kv_heads >= 1. */
 int tq_store(const tq_layout* layout, const void* key, const void* value, int32_t in_dtype, int64_t num_tokens,
              int32_t num_kv_heads, int64_t key_tok_stride, int64_t val_tok_stride, const int64_t* slot_mapping,

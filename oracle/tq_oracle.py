@@ -48,15 +48,15 @@ import numpy as np
 # Presets and slot layout
 # --------------------------------------------------------------------------
 
-#: preset name -> (key_fp8, key_bits, value_bits, norm_correction)
+#: preset name -> (key_fp8, key_bits, value_bits, norm_correction, value_lloyd_max)
 #: [PR] "实现拆解" item 1 (four named presets, each fixing key bits, value bits
 #: and norm correction); [PR] "评论区精华" (k8v4 = FP8 keys + 4-bit values);
 #: [API] TurboQuantAttentionBackend.supported_kv_cache_dtypes.
 PRESETS = {
-    "turboquant_k8v4": (True, 8, 4, False),
-    "turboquant_4bit_nc": (False, 4, 4, True),
-    "turboquant_k3v4_nc": (False, 3, 4, True),
-    "turboquant_3bit_nc": (False, 3, 3, True),
+    "turboquant_k8v4": (True, 8, 4, False, False),
+    "turboquant_4bit_nc": (False, 4, 4, True, False),
+    "turboquant_k3v4_nc": (False, 3, 4, True, False),
+    "turboquant_3bit_nc": (False, 3, 3, True, False),
     # More codecs, from the Atlas page ([TQ+] "What landed": the 2-bit
     # Lloyd-Max codebook "Turbo2", 4 codes per byte; asymmetric K/V pairs
     # with FP8 keys or 4-bit keys over 3-bit values).  Reading: the pairs
@@ -64,9 +64,17 @@ PRESETS = {
     # stated bit widths (the Atlas value codebook is not modelled); the
     # 2-bit preset quantizes keys with the 2-bit Lloyd-Max codebook and
     # values with the 2-bit uniform codec, norm-corrected like the others.
-    "turboquant_k8v3": (True, 8, 3, False),
-    "turboquant_k4v3_nc": (False, 4, 3, True),
-    "turboquant_2bit_nc": (False, 2, 2, True),
+    "turboquant_k8v3": (True, 8, 3, False, False),
+    "turboquant_k4v3_nc": (False, 4, 3, True, False),
+    "turboquant_2bit_nc": (False, 2, 2, True, False),
+    # The Atlas value codec ([TQ+] "What landed": values take the same
+    # rotation ("WHT bookend") and Lloyd-Max codebook as keys, with the
+    # matched-norm correction; [TQ+] asymmetric pairs such as FP8 K + 3-bit
+    # V, and the symmetric 3-bit codec).  The value region is [codes | fp16
+    # norm]; the value codebook is the Lloyd-Max codebook of the value bit
+    # width for N(0, 1/D), as for keys.
+    "turboquant_k8v3lm": (True, 8, 3, False, True),
+    "turboquant_3bit_lm": (False, 3, 3, True, True),
 }
 
 #: kernel block sizes the backend accepts ([PR] turboquant_attn.py excerpt,
@@ -94,9 +102,10 @@ class Layout:
     key_data_bytes: int  # packed key codes, or D fp8 bytes
     key_packed_size: int  # key region: codes + fp16 norm (MSE), or D (fp8)
     value_data_bytes: int  # packed value codes
-    value_packed_size: int  # value region: codes + fp16 scale + fp16 zero
+    value_packed_size: int  # value region: codes + fp16 scale + fp16 zero (Lloyd-Max values: + fp16 norm)
     slot_size: int
     slot_size_aligned: int
+    value_lm: bool = False  # values: rotated Lloyd-Max codes with a norm (else uniform min/max codes)
 
     @property
     def n_centroids(self) -> int:
@@ -104,7 +113,7 @@ class Layout:
 
 
 def layout(preset: str, head_dim: int) -> Layout:
-    key_fp8, kb, vb, nc = PRESETS[preset]
+    key_fp8, kb, vb, nc, vlm = PRESETS[preset]
     D = head_dim
     if key_fp8:
         kdata = D
@@ -113,10 +122,21 @@ def layout(preset: str, head_dim: int) -> Layout:
         kdata = math.ceil(D * kb / 8)
         kps = kdata + 2  # fp16 norm after the codes
     vdata = math.ceil(D * vb / 8)
-    vps = vdata + 4  # fp16 scale, fp16 zero
+    vps = vdata + (2 if vlm else 4)  # fp16 norm, or fp16 scale + fp16 zero
     slot = kps + vps
     aligned = ((slot + 1) // 2) * 2
-    return Layout(preset, D, key_fp8, kb, vb, nc, kdata, kps, vdata, vps, slot, aligned)
+    return Layout(preset, D, key_fp8, kb, vb, nc, kdata, kps, vdata, vps, slot, aligned, vlm)
+
+
+def needs_rotation(lay: Layout) -> bool:
+    """Whether the slots of this layout hold rotated coordinates (MSE keys
+    or Lloyd-Max values)."""
+    return (not lay.key_fp8) or lay.value_lm
+
+
+def value_tables(lay: Layout):
+    """The value codebook and boundaries (fp32) of a Lloyd-Max value layout."""
+    return codebook_tables(lay.head_dim, lay.value_bits)
 
 
 def kv_cache_shape(lay: Layout, num_blocks: int, block_size: int, num_kv_heads: int):
@@ -481,8 +501,15 @@ def encode_slot(lay: Layout, k, v, R, centroids32, boundaries32) -> np.ndarray:
         codes, gamma = quantize_key_mse(k, R, centroids32, boundaries32, lay.norm_correction)
         out[: lay.key_data_bytes] = pack_lsb(codes, lay.key_bits)
         out[lay.key_data_bytes : lay.key_data_bytes + 2] = _u16_le(fp16_bits(gamma))
-    vc, s16, z16 = quantize_values(v, lay.value_bits)
     o = lay.key_packed_size
+    if lay.value_lm:
+        vcent, vbound = value_tables(lay)
+        vc, gv = quantize_key_mse(v, R, vcent, vbound, True)
+        out[o : o + lay.value_data_bytes] = pack_lsb(vc, lay.value_bits)
+        o += lay.value_data_bytes
+        out[o : o + 2] = _u16_le(fp16_bits(gv))
+        return out
+    vc, s16, z16 = quantize_values(v, lay.value_bits)
     out[o : o + lay.value_data_bytes] = pack_lsb(vc, lay.value_bits)
     o += lay.value_data_bytes
     out[o : o + 2] = _u16_le(s16)
@@ -510,6 +537,20 @@ def encode_slots(lay: Layout, K, V, R, centroids32, boundaries32) -> np.ndarray:
             gamma = np.where(nu > 0, nu / r if lay.norm_correction else nu, 0.0)
         out[:, : lay.key_data_bytes] = pack_lsb(codes, lay.key_bits)
         out[:, lay.key_data_bytes : lay.key_data_bytes + 2] = _u16_le(fp16_bits(gamma))
+    if lay.value_lm:  # the steps of quantize_key_mse on the value rows
+        vcent, vbound = value_tables(lay)
+        nu = np.sqrt(np.sum(V * V, axis=1))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            U = np.where(nu[:, None] > 0, (V @ R.T) / nu[:, None], 0.0)
+        vc = (np.asarray(vbound, np.float64)[None, None, :] < U[:, :, None]).sum(axis=2)
+        chat = np.asarray(vcent, dtype=np.float64)[vc]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            gv = np.where(nu > 0, nu / np.sqrt(np.sum(chat * chat, axis=1)), 0.0)
+        o = lay.key_packed_size
+        out[:, o : o + lay.value_data_bytes] = pack_lsb(vc, lay.value_bits)
+        o += lay.value_data_bytes
+        out[:, o : o + 2] = _u16_le(fp16_bits(gv))
+        return out
     # values: the fp32 steps of quantize_values, per row
     v32 = V.astype(np.float32)
     levels = (1 << lay.value_bits) - 1
@@ -549,7 +590,7 @@ def store_rows(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids
     value = np.asarray(value, dtype=np.float64)
     N, Hk, D = key.shape
     bs = kv_cache.shape[1]
-    R = None if lay.key_fp8 else rotation(np.asarray(signs, dtype=np.float64))
+    R = rotation(np.asarray(signs, dtype=np.float64)) if needs_rotation(lay) else None
     if N == 0:
         return kv_cache
     slots = encode_slots(lay, key.reshape(N * Hk, D), value.reshape(N * Hk, D), R, centroids32,
@@ -573,7 +614,7 @@ def store(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, b
     value = np.asarray(value, dtype=np.float64)
     N, Hk, D = key.shape
     bs = kv_cache.shape[1]
-    R = None if lay.key_fp8 else rotation(np.asarray(signs, dtype=np.float64))
+    R = rotation(np.asarray(signs, dtype=np.float64)) if needs_rotation(lay) else None
     for n in range(N):
         m = int(slot_mapping[n])
         if m < 0:
@@ -604,9 +645,11 @@ def store(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids32, b
 
 
 def soa_geometry(lay: Layout, block_size: int, num_kv_heads: int):
-    """(data bytes per row, metadata region offset, u16 fields per row)."""
+    """(data bytes per row, metadata region offset, u16 fields per row).
+    Lloyd-Max values carry one field (their norm) where uniform values carry
+    two (scale, zero); this extends the pages' field list to that codec."""
     data = lay.key_data_bytes + lay.value_data_bytes
-    fields = 2 if lay.key_fp8 else 3
+    fields = (0 if lay.key_fp8 else 1) + (1 if lay.value_lm else 2)
     return data, block_size * num_kv_heads * data, fields
 
 
@@ -615,7 +658,7 @@ def _slot_fields(lay: Layout):
     SoA field order."""
     vfields = lay.key_packed_size + lay.value_data_bytes
     keyn = [] if lay.key_fp8 else [lay.key_data_bytes]
-    return keyn + [vfields, vfields + 2]
+    return keyn + ([vfields] if lay.value_lm else [vfields, vfields + 2])
 
 
 def soa_from_aos(lay: Layout, kv_cache):
@@ -666,11 +709,13 @@ def store_soa(lay: Layout, key, value, slot_mapping, kv_cache, signs, centroids3
 # --------------------------------------------------------------------------
 
 
-def decode_slot(lay: Layout, slot, centroids32):
+def decode_slot(lay: Layout, slot, centroids32, R=None):
     """Slot bytes -> (key, value) in float64.
 
     MSE keys are returned in the rotated domain, k' = γ·c[code]; FP8 keys as
-    decoded.  Values are v = zero + scale·code from the stored fp16 fields.
+    decoded.  Values are v = zero + scale·code from the stored fp16 fields;
+    Lloyd-Max values are v = R^T (γ_v c_v[code]) in the original space (R
+    is then required).
     """
     slot = np.asarray(slot, dtype=np.uint8)
     D = lay.head_dim
@@ -683,12 +728,15 @@ def decode_slot(lay: Layout, slot, centroids32):
     o = lay.key_packed_size
     vc = unpack_lsb(slot[o : o + lay.value_data_bytes], lay.value_bits, D)
     o += lay.value_data_bytes
+    if lay.value_lm:
+        gv = float(np.uint16(_from_u16_le(slot[o : o + 2])).view(np.float16))
+        return k, (gv * np.asarray(value_tables(lay)[0], dtype=np.float64)[vc]) @ R
     s = float(np.uint16(_from_u16_le(slot[o : o + 2])).view(np.float16))
     z = float(np.uint16(_from_u16_le(slot[o + 2 : o + 4])).view(np.float16))
     return k, z + s * vc.astype(np.float64)
 
 
-def decode_slots(lay: Layout, slots, centroids32):
+def decode_slots(lay: Layout, slots, centroids32, R=None):
     """``decode_slot`` applied to every row of slots (rows, slot bytes)."""
     slots = np.asarray(slots, dtype=np.uint8)
     D = lay.head_dim
@@ -701,12 +749,15 @@ def decode_slots(lay: Layout, slots, centroids32):
     o = lay.key_packed_size
     vc = unpack_lsb(slots[:, o : o + lay.value_data_bytes], lay.value_bits, D)
     o += lay.value_data_bytes
+    if lay.value_lm:
+        gv = _from_u16_le(slots[:, o : o + 2]).view(np.float16).astype(np.float64)
+        return K, (gv[:, None] * np.asarray(value_tables(lay)[0], dtype=np.float64)[vc]) @ R
     s = _from_u16_le(slots[:, o : o + 2]).view(np.float16).astype(np.float64)
     z = _from_u16_le(slots[:, o + 2 : o + 4]).view(np.float16).astype(np.float64)
     return K, z[:, None] + s[:, None] * vc.astype(np.float64)
 
 
-def gather_sequence(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: int, centroids32):
+def gather_sequence(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: int, centroids32, R=None):
     """Dequantize tokens [0, seq_len) of one sequence and KV head.  Token t is
     in block block_table_row[t // bs] at offset t % bs; entries past
     ceil(seq_len / bs) are never read ([TRACK]: decode index-out-of-bounds
@@ -716,7 +767,7 @@ def gather_sequence(lay: Layout, kv_cache, block_table_row, seq_len: int, hk: in
     blk = np.asarray(block_table_row, dtype=np.int64)[t // bs]
     if seq_len == 0:
         return np.zeros((0, lay.head_dim)), np.zeros((0, lay.head_dim))
-    return decode_slots(lay, kv_cache[blk, t % bs, hk], centroids32)
+    return decode_slots(lay, kv_cache[blk, t % bs, hk], centroids32, R)
 
 
 def attend(q, K, V, scale: float, sink: float = -math.inf):
@@ -769,7 +820,7 @@ def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids
     B, Hq, D = query.shape
     Hk = kv_cache.shape[2]
     g = Hq // Hk
-    R = None if lay.key_fp8 else rotation(np.asarray(signs, dtype=np.float64))
+    R = rotation(np.asarray(signs, dtype=np.float64)) if needs_rotation(lay) else None
     out = np.full((B, Hq, D), np.nan)
     lse = np.full((B, Hq), np.nan)
     want = {(b, h) for b in range(B) for h in range(Hq)} if rows is None else set(rows)
@@ -777,7 +828,7 @@ def decode(lay: Layout, query, kv_cache, block_table, seq_lens, signs, centroids
     for b, hq in sorted(want):
         hk = hq // g
         if (b, hk) not in cache:
-            cache = {(b, hk): gather_sequence(lay, kv_cache, block_table[b], int(seq_lens[b]), hk, centroids32)}
+            cache = {(b, hk): gather_sequence(lay, kv_cache, block_table[b], int(seq_lens[b]), hk, centroids32, R)}
         K, V = cache[(b, hk)]
         f = window_start(int(seq_lens[b]), sliding_window)
         q = query[b, hq] if lay.key_fp8 else R @ query[b, hq]
@@ -822,9 +873,10 @@ def dequant_original_space(lay: Layout, kv_cache, block_table_row, seq_len: int,
     keys, FP8 keys as decoded; V = zero + scale·code ([API]
     _continuation_prefill: dequantize the prefix, inverse-rotate MSE keys
     only)."""
-    K, V = gather_sequence(lay, kv_cache, block_table_row, seq_len, hk, centroids32)
+    R = rotation(np.asarray(signs, dtype=np.float64)) if needs_rotation(lay) else None
+    K, V = gather_sequence(lay, kv_cache, block_table_row, seq_len, hk, centroids32, R)
     if not lay.key_fp8:
-        K = K @ rotation(np.asarray(signs, dtype=np.float64))
+        K = K @ R
     return K, V
 
 

@@ -47,7 +47,7 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "preset", "head_dim", "key_fp8", "key_bits", "value_bits", "norm_correction", "n_centroids",
         "key_data_bytes", "key_packed_size", "value_data_bytes", "value_packed_size", "slot_size",
-        "slot_size_aligned", "block_layout", "soa_data_bytes", "soa_meta_fields")]
+        "slot_size_aligned", "block_layout", "soa_data_bytes", "soa_meta_fields", "value_lloyd_max")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -297,10 +297,12 @@ class Tables:
     def __init__(self, layout: Layout, signs: np.ndarray, device="cuda", mode: int = 0):
         torch = _torch()
         self.layout = layout
-        if layout.key_fp8:
+        # the key codebook (MSE keys), then the value codebook (Lloyd-Max values)
+        books = ([layout.key_bits] if not layout.key_fp8 else []) + ([layout.value_bits] if layout.value_lloyd_max else [])
+        if not books:
             self.signs = self.centroids = self.boundaries = None
             return
-        c, b = lloyd_max(layout.head_dim, layout.key_bits, mode)
+        cb = [lloyd_max(layout.head_dim, bits, mode) for bits in books]
         self.signs = torch.from_numpy(np.ascontiguousarray(signs, dtype=np.float32)).to(device)
-        self.centroids = torch.from_numpy(c).to(device)
-        self.boundaries = torch.from_numpy(b).to(device)
+        self.centroids = torch.from_numpy(np.concatenate([c for c, _ in cb])).to(device)
+        self.boundaries = torch.from_numpy(np.concatenate([b for _, b in cb])).to(device)

@@ -20,7 +20,7 @@ namespace {
 
 struct PresetDef {
   const char* name;
-  int key_fp8, key_bits, value_bits, norm_correction;
+  int key_fp8, key_bits, value_bits, norm_correction, value_lloyd_max;
 };
 
 // [PR] "实现拆解" item 1 (four named presets with key bits, value bits and
@@ -29,13 +29,15 @@ struct PresetDef {
 // keys over 3-bit values) and the 2-bit codebook, with this library's key
 // and value codecs at those widths.
 constexpr PresetDef kPresets[TQ_NUM_PRESETS] = {
-    {"turboquant_k8v4", 1, 8, 4, 0},
-    {"turboquant_4bit_nc", 0, 4, 4, 1},
-    {"turboquant_k3v4_nc", 0, 3, 4, 1},
-    {"turboquant_3bit_nc", 0, 3, 3, 1},
-    {"turboquant_k8v3", 1, 8, 3, 0},
-    {"turboquant_k4v3_nc", 0, 4, 3, 1},
-    {"turboquant_2bit_nc", 0, 2, 2, 1},
+    {"turboquant_k8v4", 1, 8, 4, 0, 0},
+    {"turboquant_4bit_nc", 0, 4, 4, 1, 0},
+    {"turboquant_k3v4_nc", 0, 3, 4, 1, 0},
+    {"turboquant_3bit_nc", 0, 3, 3, 1, 0},
+    {"turboquant_k8v3", 1, 8, 3, 0, 0},
+    {"turboquant_k4v3_nc", 0, 4, 3, 1, 0},
+    {"turboquant_2bit_nc", 0, 2, 2, 1, 0},
+    {"turboquant_k8v3lm", 1, 8, 3, 0, 1},
+    {"turboquant_3bit_lm", 0, 3, 3, 1, 1},
 };
 
 }  // namespace
@@ -94,7 +96,8 @@ extern "C" int tq_layout_init_ex(int32_t preset, int32_t head_dim, int32_t block
   L.key_data_bytes = p.key_fp8 ? head_dim : (head_dim * p.key_bits + 7) / 8;
   L.key_packed_size = p.key_fp8 ? head_dim : L.key_data_bytes + 2;
   L.value_data_bytes = (head_dim * p.value_bits + 7) / 8;
-  L.value_packed_size = L.value_data_bytes + 4;
+  L.value_lloyd_max = p.value_lloyd_max;
+  L.value_packed_size = L.value_data_bytes + (p.value_lloyd_max ? 2 : 4);  // norm, or scale + zero
   L.slot_size = L.key_packed_size + L.value_packed_size;
   L.slot_size_aligned = (L.slot_size + 1) / 2 * 2;
   L.block_layout = block_layout;
@@ -102,7 +105,7 @@ extern "C" int tq_layout_init_ex(int32_t preset, int32_t head_dim, int32_t block
   // fields; the two regions fill the same block bytes as the slots (slot
   // sizes are even, so there is no padding to account for)
   L.soa_data_bytes = block_layout == TQ_LAYOUT_SOA ? L.key_data_bytes + L.value_data_bytes : 0;
-  L.soa_meta_fields = block_layout == TQ_LAYOUT_SOA ? (p.key_fp8 ? 2 : 3) : 0;
+  L.soa_meta_fields = block_layout == TQ_LAYOUT_SOA ? (p.key_fp8 ? 0 : 1) + (p.value_lloyd_max ? 1 : 2) : 0;
   if (block_layout == TQ_LAYOUT_SOA && L.soa_data_bytes + 2 * L.soa_meta_fields != L.slot_size_aligned)
     return TQ_EHEADDIM;
   *out = L;
@@ -309,7 +312,8 @@ int validate_store(const tq_layout* L, const void* key, const void* value, int32
   if (key_tok_stride < static_cast<int64_t>(num_kv_heads) * L->head_dim ||
       val_tok_stride < static_cast<int64_t>(num_kv_heads) * L->head_dim)
     return TQ_EINVAL;
-  if (!L->key_fp8 && (!signs || !centroids || !boundaries || !aligned16(signs))) return TQ_EINVAL;
+  if ((!L->key_fp8 || L->value_lloyd_max) && (!signs || !centroids || !boundaries || !aligned16(signs)))
+    return TQ_EINVAL;
   return TQ_OK;
 }
 
@@ -329,7 +333,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
   if (batch == 0) return TQ_OK;
   if (!query || !kv_cache || !block_table || !seq_lens || !workspace) return TQ_EINVAL;
   if (!aligned16(query) || !aligned16(workspace) || !aligned16(kv_cache)) return TQ_EINVAL;
-  if (!L->key_fp8 && (!signs || !centroids)) return TQ_EINVAL;
+  if ((!L->key_fp8 || L->value_lloyd_max) && (!signs || !centroids)) return TQ_EINVAL;
   if (ws_bytes < workspace_bytes(batch, num_q_heads, L->head_dim, num_kv_splits)) return TQ_EWORKSPACE;
   return TQ_OK;
 }
@@ -361,7 +365,7 @@ int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_block
     return TQ_EINVAL;
   if (static_cast<int64_t>(num_tokens) * num_kv_heads >= (int64_t{1} << 31)) return TQ_EINVAL;
   if (static_cast<int64_t>(num_tokens + block_size - 1) / block_size > num_blocks) return TQ_EINVAL;
-  if (!L->key_fp8 && (!signs || !centroids || !aligned16(signs))) return TQ_EINVAL;
+  if ((!L->key_fp8 || L->value_lloyd_max) && (!signs || !centroids || !aligned16(signs))) return TQ_EINVAL;
   return TQ_OK;
 }
 

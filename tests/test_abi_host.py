@@ -93,7 +93,7 @@ def test_kv_cache_shape_and_presets():
         tq.preset_from_name("turboquant_5bit")
     assert e.value.status == tq.TQ_EPRESET
     with pytest.raises(tq.TQError) as e:
-        tq.layout_init(7)
+        tq.layout_init(len(O.PRESETS))
     assert e.value.status == tq.TQ_EPRESET
 
 

@@ -86,8 +86,8 @@ def test_swapped_scale_zero_is_caught(monkeypatch):
 def test_off_by_one_gather_is_caught(monkeypatch):
     real = T.gather_sequence
 
-    def bad(lay, cache, row, L, hk, c):
-        K, V = real(lay, cache, row, L + 1 if L > 0 else L, hk, c)
+    def bad(lay, cache, row, L, hk, c, R=None):
+        K, V = real(lay, cache, row, L + 1 if L > 0 else L, hk, c, R)
         return K[1:], V[1:]
 
     _patch(monkeypatch, "gather_sequence", bad)
@@ -167,3 +167,17 @@ def test_window_off_by_one_is_caught(monkeypatch):
     real = T.window_start
     _patch(monkeypatch, "window_start", lambda L, W: max(0, real(L, W) - 1) if W else 0)
     _fails(P.test_sliding_window_closed_forms)
+
+
+def test_lloyd_max_values_left_rotated_are_caught(monkeypatch):
+    """Decoding Lloyd-Max values without the inverse rotation leaves them in
+    the rotated space: their error is about 2x the signal, not the codebook
+    distortion."""
+    real = T.decode_slots
+
+    def bad(lay, slots, c32, R=None):
+        K, V = real(lay, slots, c32, R)
+        return K, (V @ R.T) if lay.value_lm else V
+
+    _patch(monkeypatch, "decode_slots", bad)
+    _fails(P.test_dequant_original_space_error_matches_lloyd_max_distortion, "turboquant_3bit_lm")
