@@ -258,7 +258,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
     lens = W.seq_lens(w)
     signs = W.signs(w).astype(np.float64)
     c32, b32 = (None, None) if lay.key_fp8 else O.codebook_tables(128, lay.key_bits)
-    R = None if lay.key_fp8 else O.rotation(signs)
+    R = O.rotation(signs) if O.needs_rotation(lay) else None
     q = O.widen(W.queries(w), w.dtype)
     g = w.num_q_heads // w.num_kv_heads
     scale = 1.0 / math.sqrt(128)
@@ -268,7 +268,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
         for hk in range(w.num_kv_heads):
             slots = O.encode_slots(lay, O.widen(K[:, hk], w.dtype), O.widen(V[:, hk], w.dtype), R, c32, b32)
             t0 = time.perf_counter()
-            Kd, Vd = O.decode_slots(lay, slots, c32)
+            Kd, Vd = O.decode_slots(lay, slots, c32, R)
             for j in range(g):
                 qq = q[b, hk * g + j] if lay.key_fp8 else R @ q[b, hk * g + j]
                 O.attend(qq, Kd, Vd, scale)

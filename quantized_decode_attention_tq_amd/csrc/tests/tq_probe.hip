@@ -36,6 +36,7 @@ TQ_HD void run_bits_op(int op, const uint32_t* in, uint32_t* out) {
     case 9:
       for (int k = 0; k < 4; ++k) out[k] = tq::key2_selector(in[0], k);
       break;
+    case 10: tq::lm_value_selectors(in, out); break;
     case 7: {
       float f;
       uint32_t u = in[0];

@@ -124,6 +124,18 @@ TQ_HD void key3_selectors(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t sel[8]
   sel[7] = (Z >> 5) & 0x07070707u;
 }
 
+// 3-bit Lloyd-Max value codes of 4 tokens -> eight selector dwords for the
+// codebook lookup: w[g] holds token g's 8 codes in bits 0..23 (its lane
+// column of dims); sel[m] holds, in byte g, token g's code m.  The four
+// 24-bit words joined end to end are a 32-code stream whose code 8g + m is
+// token g's code m, which key3_selectors lays out exactly so.
+TQ_HD void lm_value_selectors(const uint32_t w[4], uint32_t sel[8]) {
+  const uint32_t s0 = perm32(w[1], w[0], 0x04020100u);  // t0 bytes 0..2, t1 byte 0
+  const uint32_t s1 = perm32(w[2], w[1], 0x05040201u);  // t1 bytes 1..2, t2 bytes 0..1
+  const uint32_t s2 = perm32(w[3], w[2], 0x06050402u);  // t2 byte 2, t3 bytes 0..2
+  key3_selectors(s0, s1, s2, sel);
+}
+
 // Order of the 32 key dims of a 3-bit lane chunk in the MFMA operand: chunk c
 // (0..3) element e (0..7) holds dim 8*(e & 3) + 2c + (e >> 2).
 TQ_HD int key3_dim(int c, int e) { return 8 * (e & 3) + 2 * c + (e >> 2); }

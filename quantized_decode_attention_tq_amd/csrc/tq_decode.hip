@@ -54,31 +54,40 @@ template <int P>
 struct Preset;
 template <>
 struct Preset<TQ_K8V4> {
-  static constexpr int kFp8 = 1, kKb = 8, kVb = 4, kKdata = 128, kKps = 128, kVdata = 64, kSlot = 196;
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 4, kKdata = 128, kKps = 128, kVdata = 64, kSlot = 196, kVlm = 0;
 };
 template <>
 struct Preset<TQ_4BIT_NC> {
-  static constexpr int kFp8 = 0, kKb = 4, kVb = 4, kKdata = 64, kKps = 66, kVdata = 64, kSlot = 134;
+  static constexpr int kFp8 = 0, kKb = 4, kVb = 4, kKdata = 64, kKps = 66, kVdata = 64, kSlot = 134, kVlm = 0;
 };
 template <>
 struct Preset<TQ_K3V4_NC> {
-  static constexpr int kFp8 = 0, kKb = 3, kVb = 4, kKdata = 48, kKps = 50, kVdata = 64, kSlot = 118;
+  static constexpr int kFp8 = 0, kKb = 3, kVb = 4, kKdata = 48, kKps = 50, kVdata = 64, kSlot = 118, kVlm = 0;
 };
 template <>
 struct Preset<TQ_3BIT_NC> {
-  static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102;
+  static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102, kVlm = 0;
 };
 template <>
 struct Preset<TQ_K8V3> {
-  static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 180;
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 180, kVlm = 0;
 };
 template <>
 struct Preset<TQ_K4V3_NC> {
-  static constexpr int kFp8 = 0, kKb = 4, kVb = 3, kKdata = 64, kKps = 66, kVdata = 48, kSlot = 118;
+  static constexpr int kFp8 = 0, kKb = 4, kVb = 3, kKdata = 64, kKps = 66, kVdata = 48, kSlot = 118, kVlm = 0;
 };
 template <>
 struct Preset<TQ_2BIT_NC> {
-  static constexpr int kFp8 = 0, kKb = 2, kVb = 2, kKdata = 32, kKps = 34, kVdata = 32, kSlot = 70;
+  static constexpr int kFp8 = 0, kKb = 2, kVb = 2, kKdata = 32, kKps = 34, kVdata = 32, kSlot = 70, kVlm = 0;
+};
+// Lloyd-Max values: value region [codes | fp16 norm]
+template <>
+struct Preset<TQ_K8V3LM> {
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 178, kVlm = 1;
+};
+template <>
+struct Preset<TQ_3BIT_LM> {
+  static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 100, kVlm = 1;
 };
 
 // SoA convention: data row = key data + value data; metadata record = kNf
@@ -86,7 +95,7 @@ struct Preset<TQ_2BIT_NC> {
 template <int P>
 struct Soa {
   static constexpr int kDb = Preset<P>::kKdata + Preset<P>::kVdata;
-  static constexpr int kNf = Preset<P>::kFp8 ? 2 : 3;
+  static constexpr int kNf = (Preset<P>::kFp8 ? 0 : 1) + (Preset<P>::kVlm ? 1 : 2);
   static constexpr int kMb = 2 * kNf;
   static_assert(kDb % 16 == 0, "SoA data rows are 16-byte multiples");
 };
@@ -96,12 +105,14 @@ template <int P>
 constexpr bool preset_geometry_ok() {
   using T = Preset<P>;
   return T::kKdata == (T::kFp8 ? kD : kD * T::kKb / 8) && T::kKps == (T::kFp8 ? kD : T::kKdata + 2) &&
-         T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + 4 + 1) / 2) * 2;
+         T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + (T::kVlm ? 2 : 4) + 1) / 2) * 2 &&
+         (!T::kVlm || T::kVb == 3);
 }
 static_assert(preset_geometry_ok<TQ_K8V4>() && preset_geometry_ok<TQ_4BIT_NC>() &&
                   preset_geometry_ok<TQ_K3V4_NC>() && preset_geometry_ok<TQ_3BIT_NC>() &&
                   preset_geometry_ok<TQ_K8V3>() && preset_geometry_ok<TQ_K4V3_NC>() &&
-                  preset_geometry_ok<TQ_2BIT_NC>(),
+                  preset_geometry_ok<TQ_2BIT_NC>() && preset_geometry_ok<TQ_K8V3LM>() &&
+                  preset_geometry_ok<TQ_3BIT_LM>(),
               "slot geometry");
 
 struct DecodeArgs {
@@ -280,7 +291,18 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
     for (int i = 0; i < 4; ++i) r.v[i][0] = vw[i];
     return;
   }
-  if constexpr (T::kFp8 != 0) {
+  if constexpr (T::kFp8 != 0 && T::kSlot % 4 != 0) {
+    // FP8 keys in slots of 2 mod 4 bytes: half the heads start 2 bytes off
+    // a dword; read the aligned words around each 16-byte run and realign
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
+    const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tb + o.k + 80);
+    r.k[0] = tq::alignbyte(k0.y, k0.x, o.ksh); r.k[1] = tq::alignbyte(k0.z, k0.y, o.ksh);
+    r.k[2] = tq::alignbyte(k0.w, k0.z, o.ksh); r.k[3] = tq::alignbyte(e0, k0.w, o.ksh);
+    r.k[4] = tq::alignbyte(k1.y, k1.x, o.ksh); r.k[5] = tq::alignbyte(k1.z, k1.y, o.ksh);
+    r.k[6] = tq::alignbyte(k1.w, k1.z, o.ksh); r.k[7] = tq::alignbyte(e1, k1.w, o.ksh);
+  } else if constexpr (T::kFp8 != 0) {
     const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
     const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
     r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
@@ -320,7 +342,18 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
 template <int P>
 __device__ __forceinline__ void load_keys(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
-  if constexpr (T::kFp8 != 0) {
+  if constexpr (T::kFp8 != 0 && T::kSlot % 4 != 0) {
+    // FP8 keys in slots of 2 mod 4 bytes: half the heads start 2 bytes off
+    // a dword; read the aligned words around each 16-byte run and realign
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
+    const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
+    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
+    const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tb + o.k + 80);
+    r.k[0] = tq::alignbyte(k0.y, k0.x, o.ksh); r.k[1] = tq::alignbyte(k0.z, k0.y, o.ksh);
+    r.k[2] = tq::alignbyte(k0.w, k0.z, o.ksh); r.k[3] = tq::alignbyte(e0, k0.w, o.ksh);
+    r.k[4] = tq::alignbyte(k1.y, k1.x, o.ksh); r.k[5] = tq::alignbyte(k1.z, k1.y, o.ksh);
+    r.k[6] = tq::alignbyte(k1.w, k1.z, o.ksh); r.k[7] = tq::alignbyte(e1, k1.w, o.ksh);
+  } else if constexpr (T::kFp8 != 0) {
     const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
     const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
     r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
@@ -389,7 +422,13 @@ __device__ __forceinline__ void load_token_fields_soa(const uint8_t* tb, const L
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t rec = meta_rec(o, i);
-    if constexpr (T::kFp8 != 0) {
+    if constexpr (T::kVlm != 0 && T::kFp8 != 0) {
+      r.sz[i] = ld16(tb + rec);  // records of one 16-bit field: the value norm
+    } else if constexpr (T::kVlm != 0) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(tb + rec);  // key norm | value norm: aligned
+      r.gm[i] = w;
+      r.sz[i] = w >> 16;
+    } else if constexpr (T::kFp8 != 0) {
       r.sz[i] = *reinterpret_cast<const uint32_t*>(tb + rec);  // records of 4 bytes: aligned
     } else {
       r.gm[i] = ld16(tb + rec);
@@ -560,7 +599,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    sm.z = fma_hi16(p[i], sz[i], sm.z);
+    if (!T::kVlm) sm.z = fma_hi16(p[i], sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
@@ -577,12 +616,27 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 // O^T += V^T P^T over two scored tiles: 8 MFMA 16x16x32 f16, one per block
 // of 16 dims; reduction index k = 8q + j holds token 4q + j of tile `a`
 // (j < 4) or token 4q + j - 4 of tile `b`.
+// Lloyd-Max values (lv: their fp16 codebook) go through the byte-permute
+// lookup instead: selector n holds code n (dim 8 * row + n) of the tile's 4
+// tokens, so one lookup yields two tokens' fp16 centroids for that dim.
 template <int P>
-__device__ __forceinline__ void accumulate_pair(const PendingTile& a, const PendingTile& b, f32x4 acc[8]) {
+__device__ __forceinline__ void accumulate_pair(const PendingTile& a, const PendingTile& b, const tq::Lut8& lv,
+                                                f32x4 acc[8]) {
   using T = Preset<P>;
   u32x2a4 pa = __builtin_bit_cast(u32x2a4, a.pv), pb = __builtin_bit_cast(u32x2a4, b.pv);
   const half8 bp = as_half8(pa.x, pa.y, pb.x, pb.y);
-  if constexpr (T::kVb == 4) {
+  if constexpr (T::kVlm != 0) {
+    uint32_t sa[8], sb[8];
+    tq::lm_value_selectors(a.vw, sa);
+    tq::lm_value_selectors(b.vw, sb);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      uint32_t a0, a1, b0, b1;
+      tq::lut8(sa[n], lv, a0, a1);
+      tq::lut8(sb[n], lv, b0, b1);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0, a1, b0, b1), bp, acc[n], 0, 0, 0);
+    }
+  } else if constexpr (T::kVb == 4) {
     const tq::Val4Pre a01 = tq::val4_pre(a.vw[0], a.vw[1]), a23 = tq::val4_pre(a.vw[2], a.vw[3]);
     const tq::Val4Pre b01 = tq::val4_pre(b.vw[0], b.vw[1]), b23 = tq::val4_pre(b.vw[2], b.vw[3]);
 #pragma unroll
@@ -632,9 +686,9 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 // accumulators hold nothing used.
 template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
-                                                  const tq::Lut8& la, const tq::Lut8& lb, const half8 bq[4],
-                                                  int validA, int validB, int skipA, int skipB, Softmax& sm,
-                                                  f32x4 acc[8]) {
+                                                  const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
+                                                  const half8 bq[4], int validA, int validB, int skipA, int skipB,
+                                                  Softmax& sm, f32x4 acc[8]) {
   using T = Preset<P>;
   const int lane = threadIdx.x & 63;
   const bool tileB = (lane & 8) != 0;
@@ -717,7 +771,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    sm.z = fma_hi16(p[i], sz[i], sm.z);
+    if (!T::kVlm) sm.z = fma_hi16(p[i], sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   // value weights: tile A's from this lane, tile B's from lane c + 8
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
@@ -732,7 +786,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
     load_value_words<P>(imgA, o, ta.vw);
     load_value_words<P>(imgB, o, tb.vw);
   }
-  accumulate_pair<P>(ta, tb, acc);
+  accumulate_pair<P>(ta, tb, lv, acc);
 }
 
 // ---- tile staging: cache rows -> LDS ring by direct-to-LDS loads ----
@@ -797,6 +851,32 @@ __device__ __forceinline__ void vm_wait(int n) {
 // released at the barrier has no read of it still in flight.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Walsh-Hadamard transform (unnormalized, natural order) of 128 values held
+// as 32 per lane, lane quarter q holding values 32q .. 32q + 31: strides 1..16
+// inside the lane, 32 and 64 across lane quarters (lanes l ^ 16, l ^ 32).
+__device__ __forceinline__ void wht128_quarters(float v[32]) {
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((j & hs) == 0) {
+        const float x0 = v[j], x1 = v[j + hs];
+        v[j] = x0 + x1;
+        v[j + hs] = x0 - x1;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {  // strides 32 and 64: lane quarters q4 ^ 1, q4 ^ 2
+    const bool upper = (threadIdx.x & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float o = __shfl_xor(v[j], m, 64);
+      v[j] = upper ? o - v[j] : v[j] + o;
+    }
+  }
+}
+
 // Query operand of one lane (query head h0 + hl of KV head hk, dims of lane
 // quarter q4): MSE keys rotate the query like the keys (sign flip, then the
 // Walsh-Hadamard butterflies: strides 1..16 inside the lane, 32 and 64
@@ -846,26 +926,7 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
         v[8 * k + 2 * j + 1] = widen16(ww[j] >> 16, bf) * (j < 2 ? s0[2 * j + 1] : s1[2 * j - 3]);
       }
     }
-#pragma unroll
-    for (int hs = 1; hs < 32; hs <<= 1) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if ((j & hs) == 0) {
-          const float x0 = v[j], x1 = v[j + hs];
-          v[j] = x0 + x1;
-          v[j + hs] = x0 - x1;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {  // strides 32 and 64: lane quarters q4 ^ 1, q4 ^ 2
-      const bool upper = (threadIdx.x & m) != 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float o = __shfl_xor(v[j], m, 64);
-        v[j] = upper ? o - v[j] : v[j] + o;
-      }
-    }
+    wht128_quarters(v);
     const float qs = live ? a.qscale * 0.08838834764831845f : 0.f;  // 1/sqrt(128) of the rotation
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -1179,18 +1240,27 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   // ---- query operand and codebook tables (registers) ----
   half8 bq[4];
   query_operand<P>(a, b, hk, h0, geff, hl, q4, bq);
-  tq::Lut8 la{}, lb{};
+  // fp16 codebooks for the byte-permute lookups: keys (la, lb), Lloyd-Max
+  // values (lv, the value codebook after the key codebook in the table)
+  auto lut_bytes = [](const uint32_t* hb, int base, int shift) {
+    return ((hb[base] >> shift) & 0xFF) | (((hb[base + 1] >> shift) & 0xFF) << 8) |
+           (((hb[base + 2] >> shift) & 0xFF) << 16) | (((hb[base + 3] >> shift) & 0xFF) << 24);
+  };
+  tq::Lut8 la{}, lb{}, lv{};
   if (!T::kFp8) {
     uint32_t hb[16] = {};
 #pragma unroll
     for (int i = 0; i < (1 << (T::kFp8 ? 0 : T::kKb)); ++i)
       hb[i] = __half_as_ushort(__float2half_rn(a.centroids[i]));
-    auto pack = [&](int base, int shift) {
-      return ((hb[base] >> shift) & 0xFF) | (((hb[base + 1] >> shift) & 0xFF) << 8) |
-             (((hb[base + 2] >> shift) & 0xFF) << 16) | (((hb[base + 3] >> shift) & 0xFF) << 24);
-    };
-    la = {pack(0, 0), pack(4, 0), pack(0, 8), pack(4, 8)};
-    if (T::kKb == 4) lb = {pack(8, 0), pack(12, 0), pack(8, 8), pack(12, 8)};
+    la = {lut_bytes(hb, 0, 0), lut_bytes(hb, 4, 0), lut_bytes(hb, 0, 8), lut_bytes(hb, 4, 8)};
+    if (T::kKb == 4) lb = {lut_bytes(hb, 8, 0), lut_bytes(hb, 12, 0), lut_bytes(hb, 8, 8), lut_bytes(hb, 12, 8)};
+  }
+  if (T::kVlm) {
+    uint32_t hv[8];
+    const float* vc = a.centroids + (T::kFp8 ? 0 : (1 << T::kKb));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[i] = __half_as_ushort(__float2half_rn(vc[i]));
+    lv = {lut_bytes(hv, 0, 0), lut_bytes(hv, 4, 0), lut_bytes(hv, 0, 8), lut_bytes(hv, 4, 8)};
   }
   LaneOff<P> off;
   if constexpr (SOA != 0) {
@@ -1239,7 +1309,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
       if (t < t_end) {
         const uint8_t* img =
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
-        score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, bq,
+        score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, bq,
                                   min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
                                   max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), sm, acc);
       }
@@ -1256,7 +1326,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
         score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), sm, acc, pend,
                            have_pend, cur);
         if (have_pend) {
-          accumulate_pair<P>(pend, cur, acc);
+          accumulate_pair<P>(pend, cur, lv, acc);
           have_pend = false;
         } else {
           pend = cur;
@@ -1273,7 +1343,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) none.vw[i] = 0u;
     none.pv = half4{0, 0, 0, 0};
-    accumulate_pair<P>(pend, none, acc);
+    accumulate_pair<P>(pend, none, lv, acc);
   }
 
   // ---- this wave's normalized partial (output / l, base-2 LSE) ----
@@ -1290,7 +1360,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const int pos = T::kVb == 4 ? tq::val4_pos(n) : (T::kVb == 3 ? tq::val3_pos(n) : tq::val2_pos(n));
-        o[8 * i + n] = fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
+        o[8 * i + n] = T::kVlm ? acc[n][i] * inv : fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
       }
     }
   }
@@ -1326,6 +1396,18 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 #pragma unroll
       for (int k = 0; k < 32; ++k) o[k] *= inv;
       lse2 = M + log2f(wsum);
+    }
+  }
+
+  // ---- Lloyd-Max values were accumulated in the rotated space: rotate the
+  // head's output back, o <- s .* (H o) / sqrt(D) (lane quarter q4 holds dims
+  // 32 q4 .. 32 q4 + 31, as in the query operand) ----
+  if constexpr (T::kVlm != 0) {
+    if (ph == 0) {
+      wht128_quarters(o);
+      const float* sp = a.signs + 32 * q4;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) o[j] *= sp[j] * 0.08838834764831845f;
     }
   }
 
@@ -1537,6 +1619,8 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
     case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, plan.tpw, soa, nblocks, lds, stream);
     case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, plan.tpw, soa, nblocks, lds, stream);
     case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, plan.tpw, soa, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }

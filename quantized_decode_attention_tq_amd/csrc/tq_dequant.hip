@@ -105,7 +105,7 @@ struct SlotFields {
 
 // kp / vp: the row's key data and value codes; gp: its key norm (MSE keys);
 // sp: its value scale, the zero 2 bytes on.
-template <int KEY_FP8, int KB, int VB>
+template <int KEY_FP8, int KB, int VB, int VLM>
 __device__ __forceinline__ void load_fields(const uint8_t* kp, const uint8_t* vp, const uint8_t* gp,
                                             const uint8_t* sp, int sub, SlotFields<KEY_FP8, KB, VB>& f) {
   using F = SlotFields<KEY_FP8, KB, VB>;
@@ -114,7 +114,8 @@ __device__ __forceinline__ void load_fields(const uint8_t* kp, const uint8_t* vp
   ld_bytes<F::kKeyBytes>(kp + F::kKeyBytes * sub, f.kw);
   ld_bytes<F::kValBytes>(vp + F::kValBytes * sub, f.vw);
   f.gamma = KEY_FP8 ? 0u : ld_u16(gp);
-  f.scale_zero = ld_u16(sp) | (ld_u16(sp + 2) << 16);
+  // Lloyd-Max values: sp is their norm, the only field
+  f.scale_zero = VLM ? ld_u16(sp) : (ld_u16(sp) | (ld_u16(sp + 2) << 16));
 }
 
 // Each wave takes kGroups groups of 8 consecutive rows (a group: 8 lanes per
@@ -124,13 +125,17 @@ __device__ __forceinline__ void load_fields(const uint8_t* kp, const uint8_t* vp
 template <int KEY_FP8>
 constexpr int groups_per_wave() { return KEY_FP8 ? 1 : 4; }
 
-template <int KEY_FP8, int KB, int VB, int OUT>
+// VLM: Lloyd-Max values, decoded like MSE keys with the value codebook (which
+// follows the key codebook in the table).
+template <int KEY_FP8, int KB, int VB, int VLM, int OUT>
 __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
-  constexpr int kGroups = groups_per_wave<KEY_FP8>();
-  constexpr int kL = 1 << KB;
+  constexpr int kGroups = groups_per_wave<KEY_FP8 && !VLM>();
+  constexpr int kL = 1 << KB, kLv = 1 << VB;
   __shared__ float cent[KEY_FP8 ? 1 : kL];
-  if (!KEY_FP8) {
-    if (threadIdx.x < kL) cent[threadIdx.x] = a.centroids[threadIdx.x];
+  __shared__ float vcent[VLM ? kLv : 1];
+  if (!KEY_FP8 || VLM) {
+    if (!KEY_FP8 && threadIdx.x < kL) cent[threadIdx.x] = a.centroids[threadIdx.x];
+    if (VLM && threadIdx.x < kLv) vcent[threadIdx.x] = a.centroids[(KEY_FP8 ? 0 : kL) + threadIdx.x];
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
@@ -156,21 +161,21 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
       // SoA: row r = t * Hk + h of the block: [key data | value codes] at
       // r * kDb, then the fields (norm, scale, zero / scale, zero) at
       // 2 * (r * kNf + f) after the data region
-      constexpr int kDb = kKdata + kVdata, kNf = KEY_FP8 ? 2 : 3;
+      constexpr int kDb = kKdata + kVdata, kNf = (KEY_FP8 ? 0 : 1) + (VLM ? 1 : 2);
       const int64_t rows = static_cast<int64_t>(a.block_size) * a.num_kv_heads;
       const uint8_t* blkp = a.cache + blk * rows * a.slot_bytes;
       const int64_t r = static_cast<int64_t>(tb) * a.num_kv_heads + h;
       const uint8_t* drow = blkp + r * kDb;
       const uint8_t* rec = blkp + rows * kDb + r * (2 * kNf);
-      load_fields<KEY_FP8, KB, VB>(drow, drow + kKdata, rec, rec + (KEY_FP8 ? 0 : 2), sub, f[g]);
+      load_fields<KEY_FP8, KB, VB, VLM>(drow, drow + kKdata, rec, rec + (KEY_FP8 ? 0 : 2), sub, f[g]);
     } else {
       const uint8_t* slot = a.cache + ((blk * a.block_size + tb) * a.num_kv_heads + h) * a.slot_bytes;
-      load_fields<KEY_FP8, KB, VB>(slot, slot + kKps, slot + kKdata, slot + kKps + kVdata, sub, f[g]);
+      load_fields<KEY_FP8, KB, VB, VLM>(slot, slot + kKps, slot + kKdata, slot + kKps + kVdata, sub, f[g]);
     }
   }
 
   float sg[kDpl];  // signs * (+-1/sqrt(D)), the lane sign of the butterflies undone
-  if (!KEY_FP8) {
+  if (!KEY_FP8 || VLM) {
     const float c = tq::wht_lane_negated(sub) ? -0.08838834764831845f : 0.08838834764831845f;
     const float4* sp = reinterpret_cast<const float4*>(a.signs + kDpl * sub);
 #pragma unroll
@@ -210,10 +215,20 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
     }
     // ---------------- value ----------------
     float v[kDpl];
-    const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero & 0xFFFFu)));
-    const float z = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero >> 16)));
+    if (VLM) {  // as the keys: gamma_v * c_v[code], rotated back
+      const float gv = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero)));
 #pragma unroll
-    for (int i = 0; i < kDpl; ++i) v[i] = fmaf(sc, static_cast<float>(field<VB>(f[g].vw, i)), z);  // exact product
+      for (int i = 0; i < kDpl; ++i) v[i] = gv * vcent[field<VB>(f[g].vw, i)];
+      tq::wht_inlane(v, 1);
+      tq::wht_crosslane(v, sub);
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) v[i] *= sg[i];
+    } else {
+      const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero & 0xFFFFu)));
+      const float z = __half2float(__ushort_as_half(static_cast<unsigned short>(f[g].scale_zero >> 16)));
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) v[i] = fmaf(sc, static_cast<float>(field<VB>(f[g].vw, i)), z);  // exact product
+    }
 
     if (rows[g] < static_cast<uint32_t>(a.num_rows)) {
       const uint32_t t = rows[g] / static_cast<uint32_t>(a.num_kv_heads);
@@ -225,15 +240,15 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
   }
 }
 
-template <int KEY_FP8, int KB, int VB>
+template <int KEY_FP8, int KB, int VB, int VLM = 0>
 int launch_dequant(const DequantArgs& a, int32_t out_dtype, hipStream_t stream) {
-  const int64_t per_block = static_cast<int64_t>(kRowsPerBlock) * groups_per_wave<KEY_FP8>();
+  const int64_t per_block = static_cast<int64_t>(kRowsPerBlock) * groups_per_wave<KEY_FP8 && !VLM>();
   const int blocks = static_cast<int>((a.num_rows + per_block - 1) / per_block);
   DequantArgs arg = a;
   void* args[] = {&arg};
-  const void* fn = out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_F32>)
-                   : out_dtype == TQ_F16 ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_F16>)
-                                         : reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, TQ_BF16>);
+  const void* fn = out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_F32>)
+                   : out_dtype == TQ_F16 ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_F16>)
+                                         : reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_BF16>);
   return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
 }
 
@@ -268,6 +283,8 @@ extern "C" int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int6
     case TQ_K8V3: return launch_dequant<1, 8, 3>(a, out_dtype, s);
     case TQ_K4V3_NC: return launch_dequant<0, 4, 3>(a, out_dtype, s);
     case TQ_2BIT_NC: return launch_dequant<0, 2, 2>(a, out_dtype, s);
+    case TQ_K8V3LM: return launch_dequant<1, 8, 3, 1>(a, out_dtype, s);
+    case TQ_3BIT_LM: return launch_dequant<0, 3, 3, 1>(a, out_dtype, s);
   }
   return TQ_EPRESET;
 }

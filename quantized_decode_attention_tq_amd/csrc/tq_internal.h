@@ -92,7 +92,7 @@ struct DecodePlan {
 
 // Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
 // this many for any head count at head_dim 128 (slots of 196 / 134 / 118 /
-// 102 / 180 / 118 / 70 bytes in preset order; a wave of G waves per tile
+// 102 / 180 / 118 / 70 / 178 / 100 bytes in preset order; a wave of G waves per tile
 // takes ceil(spt / G) of the tile's spt loads).  SoA images pad each image
 // row by 16 bytes and round the data part and the metadata part up to whole
 // slots separately, which takes one load more with one KV head for k8v4,
@@ -106,6 +106,8 @@ constexpr int max_dma_loads(int preset, bool soa = false) {
     case TQ_K8V3: return 4;
     case TQ_K4V3_NC: return 3;
     case TQ_2BIT_NC: return soa ? 3 : 2;
+    case TQ_K8V3LM: return 4;
+    case TQ_3BIT_LM: return soa ? 3 : 2;
   }
   return 0;
 }

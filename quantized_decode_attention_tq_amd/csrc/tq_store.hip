@@ -118,19 +118,95 @@ struct Pack32 {
   }
 };
 
-template <int KEY_FP8, int KB, int VB, int NC, int BF16>
+// Lloyd-Max quantization of one row held by 8 lanes (16 coordinates each):
+// norm, randomized Hadamard rotation in registers, bucket search over the
+// LDS boundary tree, packed codes and the fp16 norm field (norm-corrected
+// when NC_).  Used for MSE keys and for Lloyd-Max values alike ([TQ+]
+// "What landed": values take the keys' rotation and codebook).
+template <int B, int NC_>
+__device__ __forceinline__ void mse_quantize(const float x[kDpl], const float* __restrict__ signs, int sub,
+                                             const float* tree, const float* cent, uint32_t out[2],
+                                             uint32_t& gamma_bits) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDpl; ++i) ss = fmaf(x[i], x[i], ss);
+  ss += xor_shfl(ss, 1);
+  ss += xor_shfl(ss, 2);
+  ss += xor_shfl(ss, 4);
+  const float nu = sqrtf(ss);
+
+  // Walsh-Hadamard butterflies, natural (Sylvester) order.  Stride 1 takes
+  // the signs in: with s = +-1, s_i x_i is exact, so fma(x_i, s_i, +-s_j x_j)
+  // rounds exactly as the sum of the signed pair does.
+  float y[kDpl];
+  const float4* sg = reinterpret_cast<const float4*>(signs + sub * kDpl);
+#pragma unroll
+  for (int i = 0; i < kDpl / 4; ++i) {
+    const float4 s4 = sg[i];
+    const float q0 = x[4 * i + 1] * s4.y, q1 = x[4 * i + 3] * s4.w;
+    y[4 * i + 0] = fmaf(x[4 * i], s4.x, q0);
+    y[4 * i + 1] = fmaf(x[4 * i], s4.x, -q0);
+    y[4 * i + 2] = fmaf(x[4 * i + 2], s4.z, q1);
+    y[4 * i + 3] = fmaf(x[4 * i + 2], s4.z, -q1);
+  }
+  tq::wht_inlane(y, 2);
+  // strides 16, 32, 64 across the row's lanes; the lane sign they leave is
+  // folded into the scale below
+  tq::wht_crosslane(y, sub);
+  // u = (H s.*x) / (sqrt(D) * nu); nu == 0 gives u = 0 and a zero norm field
+  const float inv0 = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
+  const float inv = tq::wht_lane_negated(sub) ? -inv0 : inv0;
+  float cs = 0.f;
+  Pack32<B> kp;
+#pragma unroll
+  for (int i = 0; i < kDpl; ++i) {
+    const uint32_t m4 = tree_search<B>(y[i] * inv, tree);
+    const float c = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(cent) + m4);
+    cs = fmaf(c, c, cs);
+    kp.add_node(i, m4);
+  }
+  kp.finish_nodes();
+  out[0] = kp.w[0];
+  out[1] = kp.w[1];
+  cs += xor_shfl(cs, 1);
+  cs += xor_shfl(cs, 2);
+  cs += xor_shfl(cs, 4);
+  float gamma = nu;
+  if (NC_) gamma = nu > 0.f ? nu / sqrtf(cs) : 0.f;
+  gamma_bits = __half_as_ushort(__float2half_rn(gamma));
+}
+
+// The codebook of B bits at (centroids, boundaries) into LDS: the search tree
+// of the boundaries in breadth-first order (node n = 1 .. 2^B - 1) and the
+// centroids at 2^B + code (the end node of each search).
+template <int B>
+__device__ __forceinline__ void load_tables(const float* centroids, const float* boundaries, float* tree,
+                                            float* cent) {
+  constexpr int kL = 1 << B;
+  const int t = threadIdx.x;
+  if (t >= 1 && t < kL) {
+    const int d = 31 - __builtin_clz(t);  // depth of node t
+    const int p = t - (1 << d);           // branches taken to reach it
+    tree[t] = boundaries[(p << (B - d)) + (1 << (B - d - 1)) - 1];
+  }
+  if (t < kL) cent[kL + t] = centroids[t];
+}
+
+// VLM: Lloyd-Max values (rotated, codebook after the key codebook in the
+// tables, norm-corrected), else uniform min/max values.
+template <int KEY_FP8, int KB, int VB, int NC, int VLM, int BF16>
 __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
-  constexpr int kL = 1 << KB;
-  __shared__ float tree[kL];        // node 1 .. kL - 1: boundaries in search order
-  __shared__ float cent[2 * kL];    // kL + code: centroid of the search's end node
-  if (!KEY_FP8) {
-    const int t = threadIdx.x;
-    if (t >= 1 && t < kL) {
-      const int d = 31 - __builtin_clz(t);  // depth of node t
-      const int p = t - (1 << d);           // branches taken to reach it
-      tree[t] = a.boundaries[(p << (KB - d)) + (1 << (KB - d - 1)) - 1];
+  constexpr int kL = 1 << KB, kLv = 1 << VB;
+  __shared__ float tree[KEY_FP8 ? 4 : kL];      // node 1 .. kL - 1: boundaries in search order
+  __shared__ float cent[KEY_FP8 ? 8 : 2 * kL];  // kL + code: centroid of the search's end node
+  __shared__ float vtree[VLM ? kLv : 1];
+  __shared__ float vcent[VLM ? 2 * kLv : 1];
+  if (!KEY_FP8 || VLM) {
+    if (!KEY_FP8) load_tables<KB>(a.centroids, a.boundaries, tree, cent);
+    if (VLM) {
+      const int ko = KEY_FP8 ? 0 : kL;  // the value codebook follows the key codebook
+      load_tables<VB>(a.centroids + ko, a.boundaries + (KEY_FP8 ? 0 : kL - 1), vtree, vcent);
     }
-    if (t < kL) cent[kL + t] = a.centroids[t];
     __syncthreads();
   }
 
@@ -154,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   // value data] at r * kDb; its fields (norm, scale, zero / scale, zero)
   // follow the data region as 16-bit values at 2 * (r * kNf + f)
   constexpr int kDb = (KEY_FP8 ? kD : kD * KB / 8) + kD * VB / 8;
-  constexpr int kNf = KEY_FP8 ? 2 : 3;
+  constexpr int kNf = (KEY_FP8 ? 0 : 1) + (VLM ? 1 : 2);
   const int64_t mm = m >= 0 ? m : 0;
   const int64_t blk_rows = static_cast<int64_t>(a.num_kv_heads) << a.bs_log2;  // rows of a block
   uint8_t* blkp = a.cache + (mm >> a.bs_log2) * blk_rows * a.slot_bytes;
@@ -187,56 +263,17 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
       }
     }
   } else {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) ss = fmaf(x[i], x[i], ss);
-    ss += xor_shfl(ss, 1);
-    ss += xor_shfl(ss, 2);
-    ss += xor_shfl(ss, 4);
-    const float nu = sqrtf(ss);
-
-    // Walsh-Hadamard butterflies, natural (Sylvester) order.  Stride 1 takes
-    // the signs in: with s = +-1, s_i x_i is exact, so fma(x_i, s_i, +-s_j x_j)
-    // rounds exactly as the sum of the signed pair does.
-    float y[kDpl];
-    const float4* sg = reinterpret_cast<const float4*>(a.signs + sub * kDpl);
-#pragma unroll
-    for (int i = 0; i < kDpl / 4; ++i) {
-      const float4 s4 = sg[i];
-      const float q0 = x[4 * i + 1] * s4.y, q1 = x[4 * i + 3] * s4.w;
-      y[4 * i + 0] = fmaf(x[4 * i], s4.x, q0);
-      y[4 * i + 1] = fmaf(x[4 * i], s4.x, -q0);
-      y[4 * i + 2] = fmaf(x[4 * i + 2], s4.z, q1);
-      y[4 * i + 3] = fmaf(x[4 * i + 2], s4.z, -q1);
-    }
-    tq::wht_inlane(y, 2);
-    // strides 16, 32, 64 across the row's lanes; the lane sign they leave is
-    // folded into the scale below
-    tq::wht_crosslane(y, sub);
-    // u = (H s.*x) / (sqrt(D) * nu); nu == 0 gives u = 0 and a zero norm field
-    const float inv0 = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
-    const float inv = tq::wht_lane_negated(sub) ? -inv0 : inv0;
-    float cs = 0.f;
-    Pack32<KB> kp;
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) {
-      const uint32_t m4 = tree_search<KB>(y[i] * inv, tree);
-      const float c = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(cent) + m4);
-      cs = fmaf(c, c, cs);
-      kp.add_node(i, m4);
-    }
-    kp.finish_nodes();
-    kbytes[0] = kp.w[0];
-    kbytes[1] = kp.w[1];
-    cs += xor_shfl(cs, 1);
-    cs += xor_shfl(cs, 2);
-    cs += xor_shfl(cs, 4);
-    float gamma = nu;
-    if (NC) gamma = nu > 0.f ? nu / sqrtf(cs) : 0.f;
-    gamma_bits = __half_as_ushort(__float2half_rn(gamma));
+    mse_quantize<(KEY_FP8 ? 2 : KB), NC>(x, a.signs, sub, tree, cent, kbytes, gamma_bits);
   }
 
   // ---------------- value ----------------
+  constexpr int kLevels = (1 << VB) - 1;
+  Pack32<VB> vp32;
+  __half z16 = __ushort_as_half(0), s16 = __ushort_as_half(0);  // uniform codes: zero, scale
+  uint32_t vgamma_bits = 0;                                          // Lloyd-Max codes: norm
+  if constexpr (VLM != 0) {
+    mse_quantize<VB, 1>(v, a.signs, sub, vtree, vcent, vp32.w, vgamma_bits);
+  } else {
   float vmin = v[0], vmax = v[0];
 #pragma unroll
   for (int i = 1; i < kDpl; ++i) {
@@ -248,13 +285,11 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     vmin = fminf(vmin, xor_shfl(vmin, msk));
     vmax = fmaxf(vmax, xor_shfl(vmax, msk));
   }
-  constexpr int kLevels = (1 << VB) - 1;
-  const __half z16 = __float2half_rn(vmin);
+  z16 = __float2half_rn(vmin);
   const float s32 = __fdiv_rn(__fsub_rn(vmax, vmin), static_cast<float>(kLevels));
-  const __half s16 = __float2half_rn(s32);
+  s16 = __float2half_rn(s32);
   const float zf = __half2float(z16);
   const float sf = __half2float(s16);
-  Pack32<VB> vp32;
   if (sf != 0.f) {
     const float inv = __fdiv_rn(1.0f, sf);
 #pragma unroll
@@ -268,6 +303,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
       r = fminf(fmaxf(r, 0.f), static_cast<float>(kLevels));
       vp32.or_code(i, static_cast<uint32_t>(r));
     }
+  }
   }
   constexpr int kValBytesPerLane = (kDpl * VB) / 8;
 
@@ -285,8 +321,12 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
 #pragma unroll
     for (int i = 0; i < kValBytesPerLane / 2; ++i) st16(vp + 2 * i, vp32.w[i / 2] >> (16 * (i % 2)));
     if (sub == 0) {
-      st16(sp, __half_as_ushort(s16));
-      st16(sp + 2, __half_as_ushort(z16));
+      if (VLM) {
+        st16(sp, vgamma_bits);
+      } else {
+        st16(sp, __half_as_ushort(s16));
+        st16(sp + 2, __half_as_ushort(z16));
+      }
     }
   };
   const int fs = KEY_FP8 ? 0 : 2;  // SoA: byte of the scale inside a record
@@ -330,13 +370,13 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   }
 }
 
-template <int KEY_FP8, int KB, int VB, int NC>
+template <int KEY_FP8, int KB, int VB, int NC, int VLM = 0>
 int launch_store(const StoreArgs& a, bool bf16, hipStream_t stream) {
   const int blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   StoreArgs arg = a;
   void* args[] = {&arg};
-  const void* fn = bf16 ? reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, 1>)
-                        : reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, 0>);
+  const void* fn = bf16 ? reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, VLM, 1>)
+                        : reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, VLM, 0>);
   return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
 }
 
@@ -349,6 +389,8 @@ int launch_preset(int32_t preset, const StoreArgs& a, bool bf16, hipStream_t s) 
     case TQ_K8V3: return launch_store<1, 8, 3, 0>(a, bf16, s);
     case TQ_K4V3_NC: return launch_store<0, 4, 3, 1>(a, bf16, s);
     case TQ_2BIT_NC: return launch_store<0, 2, 2, 1>(a, bf16, s);
+    case TQ_K8V3LM: return launch_store<1, 8, 3, 0, 1>(a, bf16, s);
+    case TQ_3BIT_LM: return launch_store<0, 3, 3, 1, 1>(a, bf16, s);
   }
   return TQ_EPRESET;
 }

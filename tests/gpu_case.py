@@ -52,38 +52,57 @@ def gpu_tables(lay_c, signs):
 # ------------------------------------------------------------------ store
 
 
-def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32):
-    """got/want: (rows, slot) bytes of the same rows; keys: (rows, D) float64
-    inputs of those rows (MSE presets) so that a key code may differ only
-    next to a bucket boundary.  Where codes differ the stored norm is checked
-    against nu / ||c[GPU codes]||, the norm those codes call for.
-    Returns the number of key-code mismatches (all near a boundary)."""
-    assert got.shape == want.shape
-    if lay.key_fp8:
-        np.testing.assert_array_equal(got, want)
-        return 0
-    kd = lay.key_data_bytes
-    # value region and padding: bit-exact
-    np.testing.assert_array_equal(got[:, kd + 2 :], want[:, kd + 2 :])
-    cg = O.unpack_lsb(got[:, :kd], lay.key_bits, D)
-    cw = O.unpack_lsb(want[:, :kd], lay.key_bits, D)
+def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc):
+    """got/want: (rows, code bytes + 2) = packed Lloyd-Max codes then the
+    fp16 norm of the same rows; rows: (rows, D) float64 inputs.  A code may
+    differ only next to a bucket boundary (|u - b| < 1e-6, by one), at most
+    1e-5 of the codes; the norm within 1e-3, re-derived from the GPU's codes
+    where they differ.  Returns the number of differing codes."""
+    nb = got.shape[1] - 2
+    cg = O.unpack_lsb(got[:, :nb], bits, D)
+    cw = O.unpack_lsb(want[:, :nb], bits, D)
     bad = np.argwhere(cg != cw)
     if len(bad):
-        U = O.key_units(lay, keys[np.unique(bad[:, 0])], O.rotation(np.asarray(signs, np.float64)))
+        U = O.key_units(lay, rows[np.unique(bad[:, 0])], R)
         row_idx = {r: i for i, r in enumerate(np.unique(bad[:, 0]))}
         u = np.array([U[row_idx[r], j] for r, j in bad])
-        dist = np.min(np.abs(u[:, None] - np.asarray(b32, np.float64)[None, :]), axis=1)
+        dist = np.min(np.abs(u[:, None] - np.asarray(bound, np.float64)[None, :]), axis=1)
         assert np.all(dist < BOUNDARY_EPS), f"code mismatch away from a boundary: {dist.max()}"
         assert np.all(np.abs(cg[bad[:, 0], bad[:, 1]] - cw[bad[:, 0], bad[:, 1]]) == 1)
     assert len(bad) <= MISMATCH_FRAC * cg.size, f"{len(bad)} code mismatches of {cg.size}"
-    gg = got[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
-    gw = want[:, kd : kd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+    gg = got[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+    gw = want[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     for r in np.unique(bad[:, 0]) if len(bad) else []:
-        nu = np.sqrt(np.sum(keys[r] ** 2))
-        chat = np.asarray(c32, np.float64)[cg[r]]
-        gw[r] = float(np.float16(nu / np.sqrt(np.sum(chat ** 2)))) if lay.norm_correction else nu
+        nu = np.sqrt(np.sum(rows[r] ** 2))
+        chat = np.asarray(cent, np.float64)[cg[r]]
+        gw[r] = float(np.float16(nu / np.sqrt(np.sum(chat ** 2)))) if nc else nu
     np.testing.assert_allclose(gg, gw, rtol=GAMMA_RTOL, atol=0)
     return len(bad)
+
+
+def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32, values=None):
+    """got/want: (rows, slot) bytes of the same rows; keys / values: (rows, D)
+    float64 inputs of those rows.  Lloyd-Max codes (MSE keys, Lloyd-Max
+    values) follow _compare_codes; FP8 keys, uniform value codes, scale, zero
+    and padding are bit-exact.  Returns the number of code mismatches."""
+    assert got.shape == want.shape
+    R = O.rotation(np.asarray(signs, np.float64)) if O.needs_rotation(lay) else None
+    kd, vo, vd = lay.key_data_bytes, lay.key_packed_size, lay.value_data_bytes
+    n = 0
+    if lay.key_fp8:
+        np.testing.assert_array_equal(got[:, :kd], want[:, :kd])
+    else:
+        n += _compare_codes(lay, lay.key_bits, got[:, : kd + 2], want[:, : kd + 2], keys, R, c32, b32,
+                            lay.norm_correction)
+    if lay.value_lm:
+        assert values is not None, "Lloyd-Max values need the value inputs"
+        vc32, vb32 = O.value_tables(lay)
+        n += _compare_codes(lay, lay.value_bits, got[:, vo : vo + vd + 2], want[:, vo : vo + vd + 2], values, R,
+                            vc32, vb32, True)
+        np.testing.assert_array_equal(got[:, vo + vd + 2 :], want[:, vo + vd + 2 :])
+    else:
+        np.testing.assert_array_equal(got[:, vo:], want[:, vo:])
+    return n
 
 
 # ------------------------------------------------------------------ decode
@@ -186,14 +205,14 @@ class DecodeCase:
         w = self.w
         g = w.num_q_heads // w.num_kv_heads
         q = O.widen(self.qbits, w.dtype)
-        R = None if self.lay.key_fp8 else O.rotation(self.signs.astype(np.float64))
+        R = O.rotation(self.signs.astype(np.float64)) if O.needs_rotation(self.lay) else None
         res = {}
         for b, hq in rows:
             hk = hq // g
             L = int(self.lens[b])
             slots = O.encode_slots(self.lay, O.widen(self.K[b][:, hk], w.dtype), O.widen(self.V[b][:, hk], w.dtype),
                                    R, self.c32, self.b32)
-            Kd, Vd = O.decode_slots(self.lay, slots, self.c32)
+            Kd, Vd = O.decode_slots(self.lay, slots, self.c32, R)
             qq = q[b, hq] if self.lay.key_fp8 else R @ q[b, hq]
             f = O.window_start(L, sliding_window)
             sink = -math.inf if sinks is None else float(np.float32(sinks[hq]))

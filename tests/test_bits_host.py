@@ -110,3 +110,16 @@ def test_key2_selectors_put_one_code_per_byte():
     for k in range(4):
         for b in range(4):
             np.testing.assert_array_equal((out[:, k] >> (8 * b)) & 0xFF, codes[:, 4 * b + k])
+
+
+def test_lm_value_selectors_transpose_four_tokens():
+    """Four tokens' 3-bit code words (8 codes each, bits 0..23, garbage in
+    bits 24..31) -> selector m holds token g's code m in byte g."""
+    codes = RNG.integers(0, 8, (3000, 4, 8))
+    w = np.stack([_bytes_to_words(np.concatenate([O.pack_lsb(codes[:, g], 3),
+                                                  RNG.integers(0, 256, (3000, 1)).astype(np.uint8)], axis=1))[:, 0]
+                  for g in range(4)], axis=1)
+    out = probe.bits_host("lm_value_selectors", w)
+    for m in range(8):
+        for g in range(4):
+            np.testing.assert_array_equal((out[:, m] >> (8 * g)) & 0xFF, codes[:, g, m])

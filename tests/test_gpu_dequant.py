@@ -162,10 +162,10 @@ def test_dequant_long_prefix_sampled(preset):
     v_np = vo[idx].cpu().numpy().astype(np.float64)
     blk = torch.from_numpy(table[pick // bs].astype(np.int64)).cuda()
     c_np = cache[blk, torch.from_numpy(pick % bs).cuda()].cpu().numpy()  # (samples, Hk, slot)
-    R = None if lay.key_fp8 else O.rotation(np.asarray(s, np.float64))
+    R = O.rotation(np.asarray(s, np.float64)) if O.needs_rotation(lay) else None
     for i in range(len(pick)):
-        Kd, Vd = O.decode_slots(lay, c_np[i], c32)
-        if R is not None:
+        Kd, Vd = O.decode_slots(lay, c_np[i], c32, R)
+        if not lay.key_fp8:
             Kd = Kd @ R
         _check(k_np[i][None], Kd[None], "f32", exact=lay.key_fp8)
         _check(v_np[i][None], Vd[None], "f32")

@@ -81,7 +81,8 @@ def test_soa_store_parity(preset, Hk, bs):
     np.testing.assert_array_equal(got[~written], want[~written])
     rg = got[slots[keep] // bs, slots[keep] % bs].reshape(-1, lay.slot_size_aligned)
     rw = want[slots[keep] // bs, slots[keep] % bs].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rg, rw, O.widen(K[keep], "bf16").reshape(-1, G.D), signs, c32, b32)
+    G.compare_slots(lay, rg, rw, O.widen(K[keep], "bf16").reshape(-1, G.D), signs, c32, b32,
+                    O.widen(V[keep], "bf16").reshape(-1, G.D))
 
 
 @pytest.mark.parametrize("preset", O.PRESETS)

@@ -52,7 +52,8 @@ def test_store_parity_small(preset, dtype):
     N, Hk = K.shape[:2]
     rows_got = got[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
     rows_want = want[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rows_got, rows_want, O.widen(K[keep], dtype).reshape(-1, G.D), signs, c32, b32)
+    G.compare_slots(lay, rows_got, rows_want, O.widen(K[keep], dtype).reshape(-1, G.D), signs, c32, b32,
+                    O.widen(V[keep], dtype).reshape(-1, G.D))
 
 
 @pytest.mark.parametrize("preset", O.PRESETS)
@@ -66,10 +67,10 @@ def test_store_parity_full_sweep_sampled(preset):
     tok = rng.choice(s["num_tokens"], 512, replace=False)
     Kr = O.widen(K[tok], s["dtype"]).reshape(-1, G.D)
     Vr = O.widen(V[tok], s["dtype"]).reshape(-1, G.D)
-    R = None if lay.key_fp8 else O.rotation(signs.astype(np.float64))
+    R = O.rotation(signs.astype(np.float64)) if O.needs_rotation(lay) else None
     want = O.encode_slots(lay, Kr, Vr, R, c32, b32)
     rows = got[slots[tok] // shape[1], slots[tok] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rows, want, Kr, signs, c32, b32)
+    G.compare_slots(lay, rows, want, Kr, signs, c32, b32, Vr)
 
 
 def test_store_edge_cases():
