@@ -67,7 +67,7 @@ def warm_gpu(torch, fn, ms=150.0):
         spent += a.elapsed_time(b)
 
 
-MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc")
+MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
 
 
 class DecodeBench:
