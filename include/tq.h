@@ -45,7 +45,7 @@ typedef enum {
   TQ_OK = 0,
   TQ_EINVAL = -1,       /* null pointer, negative size, misaligned tensor   */
   TQ_EPRESET = -2,      /* unknown preset id or name                        */
-  TQ_EHEADDIM = -3,     /* head_dim unsupported (kernels: 128)              */
+  TQ_EHEADDIM = -3,     /* head_dim unsupported (kernels: 128, 256)         */
   TQ_EBLOCK = -4,       /* block_size not one of 16, 32, 64, 128            */
   TQ_EGQA = -5,         /* num_q_heads not a multiple of num_kv_heads       */
   TQ_EWORKSPACE = -6,   /* workspace smaller than tq_decode_workspace_bytes */
@@ -150,7 +150,12 @@ int tq_preset_from_name(const char* name, int32_t* preset);
 
 /* Fill *out for (preset, head_dim) (host), block_layout TQ_LAYOUT_AOS.
  * head_dim must be a positive multiple of 8; the kernels additionally need
- * head_dim == 128. */
+ * head_dim 128 or 256.  A 256-dim slot keeps the same field order: its key
+ * bits and value codes are positional (dim i at bits B*i), so their first
+ * half is what a 128-dim slot of the first 128 dims would hold; the rotation
+ * is the 256-point transform and the codebook the one for d = 256 (the
+ * marginal N(0, 1/d) of tq_lloyd_max; [TQ+] "What landed" ships sign arrays
+ * for 256-dim heads). */
 int tq_layout_init(int32_t preset, int32_t head_dim, tq_layout* out);
 
 /* tq_layout_init with a block convention (tq_block_layout) (host).  TQ_EINVAL
@@ -221,7 +226,7 @@ int tq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_d
  *                    centroids [key codebook (MSE keys) | 2^value_bits],
  *                    boundaries [key boundaries | 2^value_bits - 1]; the
  *                    decode and dequant read centroids the same way.
- * Supported: head_dim 128, block_size 16/32/64/128, num_kv_heads >= 1. */
+ * Supported: head_dim 128 or 256, block_size 16/32/64/128, num_kv_heads >= 1. */
 int tq_store(const tq_layout* layout, const void* key, const void* value, int32_t in_dtype, int64_t num_tokens,
              int32_t num_kv_heads, int64_t key_tok_stride, int64_t val_tok_stride, const int64_t* slot_mapping,
              void* kv_cache, int64_t num_blocks, int32_t block_size, const float* signs, const float* centroids,
@@ -275,8 +280,8 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *   out          device [batch, num_q_heads, head_dim], dtype out_dtype
  *                (TQ_F16 | TQ_BF16 | TQ_F32), contiguous.
  *   lse_out      device fp32 [batch, num_q_heads] natural-log LSE, or NULL.
- * Supported: head_dim 128, block_size 16/32/64/128, num_q_heads a multiple
- * of num_kv_heads, sliding_window >= 0 (TQ_EINVAL otherwise). */
+ * Supported: head_dim 128 or 256, block_size 16/32/64/128, num_q_heads a
+ * multiple of num_kv_heads, sliding_window >= 0 (TQ_EINVAL otherwise). */
 int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                         int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                         int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
@@ -329,7 +334,7 @@ int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32
  *                 out_tok_stride >= num_kv_heads * head_dim and a multiple of 8,
  *                 so the rows can land in a larger [tokens, Hk, D] buffer.  Only
  *                 the rows written are touched.
- * Supported: head_dim 128, block_size 16/32/64/128, num_tokens * num_kv_heads < 2^31. */
+ * Supported: head_dim 128 or 256, block_size 16/32/64/128, num_tokens * num_kv_heads < 2^31. */
 int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                   int32_t num_kv_heads, const int32_t* block_table, int32_t num_tokens, const float* signs,
                   const float* centroids, void* key_out, void* value_out, int32_t out_dtype, int64_t out_tok_stride,

@@ -36,10 +36,14 @@
 
 namespace {
 
-constexpr int kD = 128;
+constexpr int kD = 128;  // dims of one head half: the kernels' lane layouts cover 128 dims
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kRow = kD + static_cast<int>(tq::kPartPad);  // floats per partial row
+// Preset code flag: head_dim 256, held as two 128-dim halves.  The packed
+// key bits and value codes of a row are positional (dim i at bits B*i), so
+// half h of a 256-dim slot's key data and value data is the bytes a 128-dim
+// slot would hold for those 128 dims, at offset h * (bytes of a half).
+constexpr int kHead256 = 256;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -51,43 +55,59 @@ typedef const __attribute__((address_space(4))) int32_t cint32;  // constant (sc
 
 // Slot geometry per preset at head_dim 128 (see tq_layout_init).
 template <int P>
-struct Preset;
+struct Base;
 template <>
-struct Preset<TQ_K8V4> {
+struct Base<TQ_K8V4> {
   static constexpr int kFp8 = 1, kKb = 8, kVb = 4, kKdata = 128, kKps = 128, kVdata = 64, kSlot = 196, kVlm = 0;
 };
 template <>
-struct Preset<TQ_4BIT_NC> {
+struct Base<TQ_4BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 4, kVb = 4, kKdata = 64, kKps = 66, kVdata = 64, kSlot = 134, kVlm = 0;
 };
 template <>
-struct Preset<TQ_K3V4_NC> {
+struct Base<TQ_K3V4_NC> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 4, kKdata = 48, kKps = 50, kVdata = 64, kSlot = 118, kVlm = 0;
 };
 template <>
-struct Preset<TQ_3BIT_NC> {
+struct Base<TQ_3BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 102, kVlm = 0;
 };
 template <>
-struct Preset<TQ_K8V3> {
+struct Base<TQ_K8V3> {
   static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 180, kVlm = 0;
 };
 template <>
-struct Preset<TQ_K4V3_NC> {
+struct Base<TQ_K4V3_NC> {
   static constexpr int kFp8 = 0, kKb = 4, kVb = 3, kKdata = 64, kKps = 66, kVdata = 48, kSlot = 118, kVlm = 0;
 };
 template <>
-struct Preset<TQ_2BIT_NC> {
+struct Base<TQ_2BIT_NC> {
   static constexpr int kFp8 = 0, kKb = 2, kVb = 2, kKdata = 32, kKps = 34, kVdata = 32, kSlot = 70, kVlm = 0;
 };
 // Lloyd-Max values: value region [codes | fp16 norm]
 template <>
-struct Preset<TQ_K8V3LM> {
+struct Base<TQ_K8V3LM> {
   static constexpr int kFp8 = 1, kKb = 8, kVb = 3, kKdata = 128, kKps = 128, kVdata = 48, kSlot = 178, kVlm = 1;
 };
 template <>
-struct Preset<TQ_3BIT_LM> {
+struct Base<TQ_3BIT_LM> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 100, kVlm = 1;
+};
+
+// The geometry at the head_dim of preset code PD (a preset, plus kHead256
+// for two halves): fields of the whole slot; kHk / kHv are the key / value
+// data bytes of one 128-dim half.
+template <int PD>
+struct Preset : Base<PD & 0xFF> {
+  using B = Base<PD & 0xFF>;
+  static constexpr int kNh = (PD & kHead256) ? 2 : 1;  // 128-dim halves
+  static constexpr int kDim = 128 * kNh;
+  static constexpr int kHk = B::kKdata, kHv = B::kVdata;
+  static constexpr int kKdata = kNh * B::kKdata;
+  static constexpr int kKps = B::kFp8 ? kKdata : kKdata + 2;
+  static constexpr int kVdata = kNh * B::kVdata;
+  static constexpr int kSlot = ((kKps + kVdata + (B::kVlm ? 2 : 4) + 1) / 2) * 2;
+  static constexpr int kRow = kDim + static_cast<int>(tq::kPartPad);  // floats per partial row
 };
 
 // SoA convention: data row = key data + value data; metadata record = kNf
@@ -103,7 +123,7 @@ struct Soa {
 // The constants above follow the slot layout of tq_layout_init at head_dim 128.
 template <int P>
 constexpr bool preset_geometry_ok() {
-  using T = Preset<P>;
+  using T = Base<P>;
   return T::kKdata == (T::kFp8 ? kD : kD * T::kKb / 8) && T::kKps == (T::kFp8 ? kD : T::kKdata + 2) &&
          T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + (T::kVlm ? 2 : 4) + 1) / 2) * 2 &&
          (!T::kVlm || T::kVb == 3);
@@ -256,8 +276,8 @@ __device__ __forceinline__ uint32_t meta_rec(const LaneOff<P>& o, int i) {
 // Registers one tile's loads land in.
 template <int P>
 struct TileRegs {
-  uint32_t k[8];
-  uint32_t v[4][2];
+  uint32_t k[Preset<P>::kNh][8];     // per head half
+  uint32_t v[Preset<P>::kNh][4][2];  // per head half
   uint32_t sz[4];  // fp16 scale | fp16 zero << 16
   uint32_t gm[4];  // fp16 key norm (MSE keys)
 };
@@ -271,11 +291,14 @@ struct ImageGeom {
 };
 
 template <int P>
+__device__ __forceinline__ void load_keys(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r);
+template <int P>
 __device__ __forceinline__ void load_keys_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r);
 template <int P>
 __device__ __forceinline__ void load_token_fields_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r);
 template <int P>
-__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]);
+__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o,
+                                                     uint32_t (&vw)[Preset<P>::kNh][4]);
 
 // Read one tile's fields of this lane from the tile image at tb.  SoA: the
 // value words arrive realigned in v[i][0].
@@ -285,44 +308,30 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
   if constexpr (SOA != 0) {
     load_keys_soa<P>(tb, o, r);
     load_token_fields_soa<P>(tb, o, r);
-    uint32_t vw[4];
+    uint32_t vw[T::kNh][4];
     load_value_words_soa<P>(tb, o, vw);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i][0] = vw[i];
+    for (int h = 0; h < T::kNh; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.v[h][i][0] = vw[h][i];
     return;
   }
-  if constexpr (T::kFp8 != 0 && T::kSlot % 4 != 0) {
-    // FP8 keys in slots of 2 mod 4 bytes: half the heads start 2 bytes off
-    // a dword; read the aligned words around each 16-byte run and realign
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
-    const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tb + o.k + 80);
-    r.k[0] = tq::alignbyte(k0.y, k0.x, o.ksh); r.k[1] = tq::alignbyte(k0.z, k0.y, o.ksh);
-    r.k[2] = tq::alignbyte(k0.w, k0.z, o.ksh); r.k[3] = tq::alignbyte(e0, k0.w, o.ksh);
-    r.k[4] = tq::alignbyte(k1.y, k1.x, o.ksh); r.k[5] = tq::alignbyte(k1.z, k1.y, o.ksh);
-    r.k[6] = tq::alignbyte(k1.w, k1.z, o.ksh); r.k[7] = tq::alignbyte(e1, k1.w, o.ksh);
-  } else if constexpr (T::kFp8 != 0) {
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
-    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
-    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
-  } else {
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
-    if (T::kKb == 4) r.k[4] = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
-  }
+  load_keys<P>(tb, o, r);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // value codes of token 4q+i; the row stride may be 2 mod 4, so the
-    // whole in-tile offset is aligned down (tile bases are 32-byte aligned)
-    const uint32_t vo = o.mo[i] + o.vcol;
-    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
-      r.v[i][0] = *reinterpret_cast<const uint32_t*>(tb + vo);
-    } else {
-      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
-      r.v[i][0] = w.x;
-      r.v[i][1] = w.y;
+    // whole in-tile offset is aligned down (tile bases are 32-byte aligned).
+    // Both halves' words share the alignment (half sizes are 4-byte multiples).
+#pragma unroll
+    for (int h = 0; h < T::kNh; ++h) {
+      const uint32_t vo = o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv);
+      if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
+        r.v[h][i][0] = *reinterpret_cast<const uint32_t*>(tb + vo);
+      } else {
+        const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
+        r.v[h][i][0] = w.x;
+        r.v[h][i][1] = w.y;
+      }
     }
     const uint8_t* m = tb + o.mo[i];
     if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
@@ -338,30 +347,37 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
   }
 }
 
-// The key words of the lane (token lane % 16, dims of its quarter).
+// The key words of the lane (token lane % 16, dims of its quarter), per head
+// half (half h's key data starts h * kHk bytes on, a multiple of 4: both
+// halves share the alignment).
 template <int P>
 __device__ __forceinline__ void load_keys(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
-  if constexpr (T::kFp8 != 0 && T::kSlot % 4 != 0) {
-    // FP8 keys in slots of 2 mod 4 bytes: half the heads start 2 bytes off
-    // a dword; read the aligned words around each 16-byte run and realign
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
-    const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tb + o.k + 80);
-    r.k[0] = tq::alignbyte(k0.y, k0.x, o.ksh); r.k[1] = tq::alignbyte(k0.z, k0.y, o.ksh);
-    r.k[2] = tq::alignbyte(k0.w, k0.z, o.ksh); r.k[3] = tq::alignbyte(e0, k0.w, o.ksh);
-    r.k[4] = tq::alignbyte(k1.y, k1.x, o.ksh); r.k[5] = tq::alignbyte(k1.z, k1.y, o.ksh);
-    r.k[6] = tq::alignbyte(k1.w, k1.z, o.ksh); r.k[7] = tq::alignbyte(e1, k1.w, o.ksh);
-  } else if constexpr (T::kFp8 != 0) {
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
-    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
-    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
-  } else {
-    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
-    if (T::kKb == 4) r.k[4] = *reinterpret_cast<const uint32_t*>(tb + o.k + 16);
+#pragma unroll
+  for (int h = 0; h < T::kNh; ++h) {
+    const uint8_t* kb = tb + o.k + h * T::kHk;
+    uint32_t* rk = r.k[h];
+    if constexpr (T::kFp8 != 0 && T::kSlot % 4 != 0) {
+      // FP8 keys in slots of 2 mod 4 bytes: half the heads start 2 bytes off
+      // a dword; read the aligned words around each 16-byte run and realign
+      const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kb);
+      const uint32_t e0 = *reinterpret_cast<const uint32_t*>(kb + 16);
+      const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(kb + 64);
+      const uint32_t e1 = *reinterpret_cast<const uint32_t*>(kb + 80);
+      rk[0] = tq::alignbyte(k0.y, k0.x, o.ksh); rk[1] = tq::alignbyte(k0.z, k0.y, o.ksh);
+      rk[2] = tq::alignbyte(k0.w, k0.z, o.ksh); rk[3] = tq::alignbyte(e0, k0.w, o.ksh);
+      rk[4] = tq::alignbyte(k1.y, k1.x, o.ksh); rk[5] = tq::alignbyte(k1.z, k1.y, o.ksh);
+      rk[6] = tq::alignbyte(k1.w, k1.z, o.ksh); rk[7] = tq::alignbyte(e1, k1.w, o.ksh);
+    } else if constexpr (T::kFp8 != 0) {
+      const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kb);
+      const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(kb + 64);
+      rk[0] = k0.x; rk[1] = k0.y; rk[2] = k0.z; rk[3] = k0.w;
+      rk[4] = k1.x; rk[5] = k1.y; rk[6] = k1.z; rk[7] = k1.w;
+    } else {
+      const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kb);
+      rk[0] = k0.x; rk[1] = k0.y; rk[2] = k0.z; rk[3] = k0.w;
+      if (T::kKb == 4) rk[4] = *reinterpret_cast<const uint32_t*>(kb + 16);
+    }
   }
 }
 
@@ -388,16 +404,19 @@ __device__ __forceinline__ void load_token_fields(const uint8_t* tb, const LaneO
 // The value-code words of the lane's 4 tokens (tokens 4q .. 4q+3, dims of
 // lane row), realigned, straight from the tile image.
 template <int P>
-__device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]) {
+__device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOff<P>& o,
+                                                 uint32_t (&vw)[Preset<P>::kNh][4]) {
   using T = Preset<P>;
 #pragma unroll
+  for (int h = 0; h < T::kNh; ++h)
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t vo = o.mo[i] + o.vcol;
+    const uint32_t vo = o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv);
     if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
-      vw[i] = *reinterpret_cast<const uint32_t*>(tb + vo);
+      vw[h][i] = *reinterpret_cast<const uint32_t*>(tb + vo);
     } else {
       const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
-      vw[i] = tq::alignbyte(w.y, w.x, vo & 3u);
+      vw[h][i] = tq::alignbyte(w.y, w.x, vo & 3u);
     }
   }
 }
@@ -408,11 +427,15 @@ __device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOf
 template <int P>
 __device__ __forceinline__ void load_keys_soa(const uint8_t* tb, const LaneOff<P>& o, TileRegs<P>& r) {
   using T = Preset<P>;
-  const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(tb + o.k);
-  r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
-  if constexpr (T::kFp8 != 0) {
-    const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(tb + o.k + 64);
-    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
+#pragma unroll
+  for (int h = 0; h < T::kNh; ++h) {
+    const uint8_t* kb = tb + o.k + h * T::kHk;
+    const u32x4a4 k0 = *reinterpret_cast<const u32x4a4*>(kb);
+    r.k[h][0] = k0.x; r.k[h][1] = k0.y; r.k[h][2] = k0.z; r.k[h][3] = k0.w;
+    if constexpr (T::kFp8 != 0) {
+      const u32x4a4 k1 = *reinterpret_cast<const u32x4a4*>(kb + 64);
+      r.k[h][4] = k1.x; r.k[h][5] = k1.y; r.k[h][6] = k1.z; r.k[h][7] = k1.w;
+    }
   }
 }
 
@@ -440,47 +463,51 @@ __device__ __forceinline__ void load_token_fields_soa(const uint8_t* tb, const L
 }
 
 template <int P>
-__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o, uint32_t vw[4]) {
+__device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const LaneOff<P>& o,
+                                                     uint32_t (&vw)[Preset<P>::kNh][4]) {
   using T = Preset<P>;
 #pragma unroll
+  for (int h = 0; h < T::kNh; ++h)
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t vo = data_row<P, 1>(o, i) + o.vcol;
+    const uint32_t vo = data_row<P, 1>(o, i) + o.vcol + static_cast<uint32_t>(h * T::kHv);
     if constexpr (T::kVb == 4) {
-      vw[i] = *reinterpret_cast<const uint32_t*>(tb + vo);
+      vw[h][i] = *reinterpret_cast<const uint32_t*>(tb + vo);
     } else {
       const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
-      vw[i] = tq::alignbyte(w.y, w.x, vo & 3u);
+      vw[h][i] = tq::alignbyte(w.y, w.x, vo & 3u);
     }
   }
 }
 
-// Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q).
-// SOA: the key words are aligned (sh unused).
+// Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q
+// in head half hh).  SOA: the key words are aligned (sh unused).
 template <int P, int SOA>
-__device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, const tq::Lut8& la,
+__device__ __forceinline__ void key_operand(const TileRegs<P>& rr, int hh, uint32_t sh, const tq::Lut8& la,
                                             const tq::Lut8& lb, half8 A[4]) {
   using T = Preset<P>;
+  const uint32_t* k = rr.k[hh];
   if constexpr (T::kFp8 != 0) {
     uint32_t hv[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      hv[2 * i] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.k[i], 1.0f, false));
-      hv[2 * i + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.k[i], 1.0f, true));
+      hv[2 * i] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[i], 1.0f, false));
+      hv[2 * i + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[i], 1.0f, true));
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) A[c] = as_half8(hv[4 * c], hv[4 * c + 1], hv[4 * c + 2], hv[4 * c + 3]);
   } else if constexpr (T::kKb == 4) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w = SOA ? r.k[c] : tq::alignbyte(r.k[c + 1], r.k[c], sh);
+      const uint32_t w = SOA ? k[c] : tq::alignbyte(k[c + 1], k[c], sh);
       uint32_t e0, e1, o0, o1;
       tq::lut16(w & 0x0F0F0F0Fu, la, lb, e0, e1);
       tq::lut16((w >> 4) & 0x0F0F0F0Fu, la, lb, o0, o1);
       A[c] = as_half8(e0, e1, o0, o1);
     }
   } else if constexpr (T::kKb == 2) {
-    const uint32_t w0 = SOA ? r.k[0] : tq::alignbyte(r.k[1], r.k[0], sh);
-    const uint32_t w1 = SOA ? r.k[1] : tq::alignbyte(r.k[2], r.k[1], sh);
+    const uint32_t w0 = SOA ? k[0] : tq::alignbyte(k[1], k[0], sh);
+    const uint32_t w1 = SOA ? k[1] : tq::alignbyte(k[2], k[1], sh);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w = c < 2 ? w0 : w1;
@@ -492,10 +519,10 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& r, uint32_t sh, c
   } else {
     uint32_t sel[8];
     if (SOA)
-      tq::key3_selectors(r.k[0], r.k[1], r.k[2], sel);
+      tq::key3_selectors(k[0], k[1], k[2], sel);
     else
-      tq::key3_selectors(tq::alignbyte(r.k[1], r.k[0], sh), tq::alignbyte(r.k[2], r.k[1], sh),
-                         tq::alignbyte(r.k[3], r.k[2], sh), sel);
+      tq::key3_selectors(tq::alignbyte(k[1], k[0], sh), tq::alignbyte(k[2], k[1], sh),
+                         tq::alignbyte(k[3], k[2], sh), sel);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t a0, a1, b0, b1;
@@ -520,28 +547,33 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 // on 16x16x32 MFMAs over two tiles at once (32 tokens on the reduction
 // axis), so the first tile of a pair is held here until the second is
 // scored.
+template <int P>
 struct PendingTile {
-  uint32_t vw[4];  // value-code words of tokens 4q .. 4q+3 (dims of lane row)
-  half4 pv;        // p * value_scale of those tokens, fp16
+  uint32_t vw[Preset<P>::kNh][4];  // per head half: value-code words of tokens 4q .. 4q+3 (dims of lane row)
+  half4 pv;                        // p * value_scale of those tokens, fp16
 };
 
 // Score one tile and update the online softmax.  valid: tokens of the tile
 // before the sequence end (1..16).  On return `cur` holds the tile's value
 // words and weights; if the running maximum moved, the accumulators and the
-// pending tile (when `have_pend`) are rescaled to it.
+// pending tile (when `have_pend`) are rescaled to it.  bq: 4 query operands
+// per head half; acc: 8 accumulators per head half.
 template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
-                                           const tq::Lut8& lb, const half8 bq[4], int valid, int skip, Softmax& sm,
-                                           f32x4 acc[8], PendingTile& pend, bool have_pend, PendingTile& cur) {
+                                           const tq::Lut8& lb, const half8* bq, int valid, int skip, Softmax& sm,
+                                           f32x4* acc, PendingTile<P>& pend, bool have_pend, PendingTile<P>& cur) {
   using T = Preset<P>;
-  half8 A[4];
-  key_operand<P, SOA>(r, o.ksh, la, lb, A);
   // two independent accumulation chains halve the dependent-MFMA latency
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], s1, 0, 0, 0);
+#pragma unroll
+  for (int h = 0; h < T::kNh; ++h) {
+    half8 A[4];
+    key_operand<P, SOA>(r, h, o.ksh, la, lb, A);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[4 * h], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[4 * h + 1], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[4 * h + 2], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[4 * h + 3], s1, 0, 0, 0);
+  }
 
   // per token: fp16 value scale (low half) and zero (high half)
   float sco[4];
@@ -582,7 +614,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
     const float m_cand = fmaxf(sm.m, quarter_max(lmax));
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    for (int n = 0; n < 8 * T::kNh; ++n) acc[n] *= alpha;
     sm.l *= alpha;
     sm.z *= alpha;
     sm.m = m_cand;
@@ -605,30 +637,31 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
   cur.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
 #pragma unroll
+  for (int h = 0; h < T::kNh; ++h)
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (SOA != 0 || (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4))
-      cur.vw[i] = r.v[i][0];
+      cur.vw[h][i] = r.v[h][i][0];
     else
-      cur.vw[i] = tq::alignbyte(r.v[i][1], r.v[i][0], (o.mo[i] + o.vcol) & 3u);
+      cur.vw[h][i] = tq::alignbyte(r.v[h][i][1], r.v[h][i][0], (o.mo[i] + o.vcol) & 3u);
   }
 }
 
-// O^T += V^T P^T over two scored tiles: 8 MFMA 16x16x32 f16, one per block
-// of 16 dims; reduction index k = 8q + j holds token 4q + j of tile `a`
+// O^T += V^T P^T over two scored tiles, one 128-dim head half (av / bv: the
+// tiles' value words of that half; bp: their weights): 8 MFMA 16x16x32 f16,
+// one per block of 16 dims; reduction index k = 8q + j holds token 4q + j of tile `a`
 // (j < 4) or token 4q + j - 4 of tile `b`.
 // Lloyd-Max values (lv: their fp16 codebook) go through the byte-permute
 // lookup instead: selector n holds code n (dim 8 * row + n) of the tile's 4
 // tokens, so one lookup yields two tokens' fp16 centroids for that dim.
 template <int P>
-__device__ __forceinline__ void accumulate_pair(const PendingTile& a, const PendingTile& b, const tq::Lut8& lv,
-                                                f32x4 acc[8]) {
+__device__ __forceinline__ void accumulate_half(const uint32_t (&av)[4], const uint32_t (&bv)[4], const half8& bp,
+                                                const tq::Lut8& lv, f32x4* acc) {
   using T = Preset<P>;
-  u32x2a4 pa = __builtin_bit_cast(u32x2a4, a.pv), pb = __builtin_bit_cast(u32x2a4, b.pv);
-  const half8 bp = as_half8(pa.x, pa.y, pb.x, pb.y);
   if constexpr (T::kVlm != 0) {
     uint32_t sa[8], sb[8];
-    tq::lm_value_selectors(a.vw, sa);
-    tq::lm_value_selectors(b.vw, sb);
+    tq::lm_value_selectors(av, sa);
+    tq::lm_value_selectors(bv, sb);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       uint32_t a0, a1, b0, b1;
@@ -637,30 +670,41 @@ __device__ __forceinline__ void accumulate_pair(const PendingTile& a, const Pend
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0, a1, b0, b1), bp, acc[n], 0, 0, 0);
     }
   } else if constexpr (T::kVb == 4) {
-    const tq::Val4Pre a01 = tq::val4_pre(a.vw[0], a.vw[1]), a23 = tq::val4_pre(a.vw[2], a.vw[3]);
-    const tq::Val4Pre b01 = tq::val4_pre(b.vw[0], b.vw[1]), b23 = tq::val4_pre(b.vw[2], b.vw[3]);
+    const tq::Val4Pre a01 = tq::val4_pre(av[0], av[1]), a23 = tq::val4_pre(av[2], av[3]);
+    const tq::Val4Pre b01 = tq::val4_pre(bv[0], bv[1]), b23 = tq::val4_pre(bv[2], bv[3]);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           as_half8(tq::val4_get(a01, n), tq::val4_get(a23, n), tq::val4_get(b01, n), tq::val4_get(b23, n)), bp,
           acc[n], 0, 0, 0);
   } else if constexpr (T::kVb == 2) {
-    const tq::Val2Pre a01 = tq::val2_pre(a.vw[0], a.vw[1]), a23 = tq::val2_pre(a.vw[2], a.vw[3]);
-    const tq::Val2Pre b01 = tq::val2_pre(b.vw[0], b.vw[1]), b23 = tq::val2_pre(b.vw[2], b.vw[3]);
+    const tq::Val2Pre a01 = tq::val2_pre(av[0], av[1]), a23 = tq::val2_pre(av[2], av[3]);
+    const tq::Val2Pre b01 = tq::val2_pre(bv[0], bv[1]), b23 = tq::val2_pre(bv[2], bv[3]);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           as_half8(tq::val2_get(a01, n), tq::val2_get(a23, n), tq::val2_get(b01, n), tq::val2_get(b23, n)), bp,
           acc[n], 0, 0, 0);
   } else {
-    const tq::Val3Pre a01 = tq::val3_pre(a.vw[0], a.vw[1]), a23 = tq::val3_pre(a.vw[2], a.vw[3]);
-    const tq::Val3Pre b01 = tq::val3_pre(b.vw[0], b.vw[1]), b23 = tq::val3_pre(b.vw[2], b.vw[3]);
+    const tq::Val3Pre a01 = tq::val3_pre(av[0], av[1]), a23 = tq::val3_pre(av[2], av[3]);
+    const tq::Val3Pre b01 = tq::val3_pre(bv[0], bv[1]), b23 = tq::val3_pre(bv[2], bv[3]);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           as_half8(tq::val3_get(a01, n), tq::val3_get(a23, n), tq::val3_get(b01, n), tq::val3_get(b23, n)), bp,
           acc[n], 0, 0, 0);
   }
+}
+
+// Both head halves of a pair of scored tiles (acc: 8 accumulators per half).
+template <int P>
+__device__ __forceinline__ void accumulate_pair(const PendingTile<P>& a, const PendingTile<P>& b,
+                                                const tq::Lut8& lv, f32x4* acc) {
+  using T = Preset<P>;
+  u32x2a4 pa = __builtin_bit_cast(u32x2a4, a.pv), pb = __builtin_bit_cast(u32x2a4, b.pv);
+  const half8 bp = as_half8(pa.x, pa.y, pb.x, pb.y);
+#pragma unroll
+  for (int h = 0; h < T::kNh; ++h) accumulate_half<P>(a.vw[h], b.vw[h], bp, lv, acc + 8 * h);
 }
 
 // Value of lane l ^ 8 (the other half of the lane's row of 16): DPP row_ror:8.
@@ -687,9 +731,10 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
-                                                  const half8 bq[4], int validA, int validB, int skipA, int skipB,
-                                                  Softmax& sm, f32x4 acc[8]) {
+                                                  const half8* bq, int validA, int validB, int skipA, int skipB,
+                                                  Softmax& sm, f32x4* acc) {
   using T = Preset<P>;
+  static_assert(T::kNh == 1, "packed pairs: head_dim 128");
   const int lane = threadIdx.x & 63;
   const bool tileB = (lane & 8) != 0;
   TileRegs<P> rA, rB, own;
@@ -704,13 +749,13 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   }
   // one accumulation chain per tile: the two tiles' chains interleave
   half8 A[4];
-  key_operand<P, SOA>(rA, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rA, 0, o.ksh, la, lb, A);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f};
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], sa, 0, 0, 0);
-  key_operand<P, SOA>(rB, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rB, 0, o.ksh, la, lb, A);
   f32x4 sb = {0.f, 0.f, 0.f, 0.f};
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sb, 0, 0, 0);
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sb, 0, 0, 0);
@@ -776,7 +821,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   // value weights: tile A's from this lane, tile B's from lane c + 8
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
-  PendingTile ta, tb;
+  PendingTile<P> ta, tb;
   ta.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
   tb.pv = as_half4(swap8(h2_bits(ps01)), swap8(h2_bits(ps23)));
   if constexpr (SOA != 0) {
@@ -806,7 +851,7 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
 // so a wave needs one block id and one base address per super-tile.
 template <int P, int SOA>
 struct Ring {
-  static constexpr int kLoads = tq::max_dma_loads(P, SOA != 0);
+  static constexpr int kLoads = tq::max_dma_loads(P & 0xFF, SOA != 0, Preset<P>::kDim);
   uint32_t lds_base;       // LDS byte address of ring entry 0 (uniform)
   uint32_t entry;          // bytes per ring entry (P * spt KB)
   int my_loads;            // DMA slots per super-tile issued by this wave
@@ -878,56 +923,78 @@ __device__ __forceinline__ void wht128_quarters(float v[32]) {
 }
 
 // Query operand of one lane (query head h0 + hl of KV head hk, dims of lane
-// quarter q4): MSE keys rotate the query like the keys (sign flip, then the
-// Walsh-Hadamard butterflies: strides 1..16 inside the lane, 32 and 64
-// across lane quarters), everything scaled by softmax scale * log2(e); the
-// values land in fp16 in the order key_operand produces dims.
+// quarter q4 in each 128-dim head half h, bq[4h .. 4h + 3]): MSE keys rotate
+// the query like the keys (sign flip, then the Walsh-Hadamard butterflies:
+// strides 1..16 inside the lane, 32 and 64 across lane quarters, and at
+// head_dim 256 the stride 128 between the lane's two halves), everything
+// scaled by softmax scale * log2(e); the values land in fp16 in the order
+// key_operand produces dims.
 template <int P>
 __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk, int h0, int geff, int hl, int q4,
-                                              half8 bq[4]) {
+                                              half8* bq) {
   using T = Preset<P>;
   const bool live = hl < geff;
   const uint16_t* qrow =
-      a.query + (static_cast<int64_t>(b) * a.num_q_heads + hk * a.group + h0 + (live ? hl : 0)) * kD;
+      a.query + (static_cast<int64_t>(b) * a.num_q_heads + hk * a.group + h0 + (live ? hl : 0)) * T::kDim;
   const bool bf = a.q_bf16 != 0;
-  float v[32];
+  float v[T::kNh][32];
   if constexpr (T::kFp8 != 0) {
-    // dims 16*q4 + j (v[j]) and 64 + 16*q4 + j (v[16 + j]); bq[c][e] = v[8c + e]
+    // dims 16*q4 + j (v[j]) and 64 + 16*q4 + j (v[16 + j]) of each half;
+    // bq[4h + c][e] = v[h][8c + e]
+#pragma unroll
+    for (int hh = 0; hh < T::kNh; ++hh)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4a4 w0 = *reinterpret_cast<const u32x4a4*>(qrow + 64 * h + 16 * q4);
-      const u32x4a4 w1 = *reinterpret_cast<const u32x4a4*>(qrow + 64 * h + 16 * q4 + 8);
+      const u32x4a4 w0 = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4);
+      const u32x4a4 w1 = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4 + 8);
       const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        v[16 * h + 2 * j] = widen16(w[j] & 0xFFFFu, bf);
-        v[16 * h + 2 * j + 1] = widen16(w[j] >> 16, bf);
+        v[hh][16 * h + 2 * j] = widen16(w[j] & 0xFFFFu, bf);
+        v[hh][16 * h + 2 * j + 1] = widen16(w[j] >> 16, bf);
       }
     }
     const float qs = live ? a.qscale : 0.f;
 #pragma unroll
+    for (int hh = 0; hh < T::kNh; ++hh)
+#pragma unroll
     for (int c = 0; c < 4; ++c) {
       half8 h;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[8 * c + e] * qs);
-      bq[c] = h;
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[hh][8 * c + e] * qs);
+      bq[4 * hh + c] = h;
     }
   } else {
-    // dims 32*q4 + j (v[j])
+    // dims 128*hh + 32*q4 + j (v[hh][j])
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4a4 w = *reinterpret_cast<const u32x4a4*>(qrow + 32 * q4 + 8 * k);
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.signs + 32 * q4 + 8 * k);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.signs + 32 * q4 + 8 * k + 4);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int hh = 0; hh < T::kNh; ++hh) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * k + 2 * j] = widen16(ww[j] & 0xFFFFu, bf) * (j < 2 ? s0[2 * j] : s1[2 * j - 4]);
-        v[8 * k + 2 * j + 1] = widen16(ww[j] >> 16, bf) * (j < 2 ? s0[2 * j + 1] : s1[2 * j - 3]);
+      for (int k = 0; k < 4; ++k) {
+        const int d0 = 128 * hh + 32 * q4 + 8 * k;
+        const u32x4a4 w = *reinterpret_cast<const u32x4a4*>(qrow + d0);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.signs + d0);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.signs + d0 + 4);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[hh][8 * k + 2 * j] = widen16(ww[j] & 0xFFFFu, bf) * (j < 2 ? s0[2 * j] : s1[2 * j - 4]);
+          v[hh][8 * k + 2 * j + 1] = widen16(ww[j] >> 16, bf) * (j < 2 ? s0[2 * j + 1] : s1[2 * j - 3]);
+        }
+      }
+      wht128_quarters(v[hh]);
+    }
+    if constexpr (T::kNh == 2) {  // stride 128: (lower + upper, lower - upper)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float x0 = v[0][j], x1 = v[1][j];
+        v[0][j] = x0 + x1;
+        v[1][j] = x0 - x1;
       }
     }
-    wht128_quarters(v);
-    const float qs = live ? a.qscale * 0.08838834764831845f : 0.f;  // 1/sqrt(128) of the rotation
+    // 1/sqrt(head_dim) of the rotation
+    const float qs = live ? a.qscale * (T::kNh == 2 ? 0.0625f : 0.08838834764831845f) : 0.f;
+#pragma unroll
+    for (int hh = 0; hh < T::kNh; ++hh)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       half8 h;
@@ -935,9 +1002,9 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
       for (int e = 0; e < 8; ++e) {
         // inverse of qh_pos inside the lane's 32 dims
         const int dd = T::kKb == 4 ? tq::key4_dim(c, e) : (T::kKb == 2 ? tq::key2_dim(c, e) : tq::key3_dim(c, e));
-        h[e] = static_cast<_Float16>(v[dd] * qs);
+        h[e] = static_cast<_Float16>(v[hh][dd] * qs);
       }
-      bq[c] = h;
+      bq[4 * hh + c] = h;
     }
   }
 }
@@ -1052,10 +1119,14 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // whole workgroup, R-1 super-tiles ahead; the phase-p wave of a head scores
 // and accumulates tile p of every super-tile from LDS.  At the end the P
 // phase waves of a head merge their partial softmax states through LDS and
-// the phase-0 wave writes the split's partial rows.
+// the phase-0 wave writes the split's partial rows.  head_dim 256 (two
+// halves: twice the accumulators and query operands) runs one tile per wave
+// and keeps 2 waves per SIMD's registers.
 template <int P, int TPW, int PACK, int SOA>
-__global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_kernel(DecodeArgs a) {
   using T = Preset<P>;
+  static_assert(T::kNh == 1 || (TPW == 1 && PACK == 0), "head_dim 256: one tile per wave");
+  constexpr int kOut = 32 * T::kNh;  // output dims per lane (32 of each half)
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
 
   const int lane = threadIdx.x & 63;
@@ -1097,8 +1168,10 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
 
   if (t_begin >= t_end) {  // empty range: zero partial, lse = -inf
     if (ph == 0) {
-      for (int idx = lane; idx < geff * kD; idx += 64) a.part[prow(idx >> 7) * kRow + (idx & (kD - 1))] = 0.f;
-      if (lane < geff) a.part[prow(lane) * kRow + kD] = -INFINITY;
+      constexpr int kDimLog2 = T::kNh == 2 ? 8 : 7;
+      for (int idx = lane; idx < geff * T::kDim; idx += 64)
+        a.part[prow(idx >> kDimLog2) * T::kRow + (idx & (T::kDim - 1))] = 0.f;
+      if (lane < geff) a.part[prow(lane) * T::kRow + T::kDim] = -INFINITY;
     }
     return;
   }
@@ -1238,7 +1311,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   Blk blk_next = blocks_of(R - 1);  // next refill's block ids, fetched a step ahead
 
   // ---- query operand and codebook tables (registers) ----
-  half8 bq[4];
+  half8 bq[4 * T::kNh];
   query_operand<P>(a, b, hk, h0, geff, hl, q4, bq);
   // fp16 codebooks for the byte-permute lookups: keys (la, lb), Lloyd-Max
   // values (lv, the value codebook after the key codebook in the table)
@@ -1287,10 +1360,10 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   }
 
   Softmax sm{-INFINITY, 0.f, 0.f};
-  f32x4 acc[8];
+  f32x4 acc[8 * T::kNh];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  PendingTile pend;
+  for (int n = 0; n < 8 * T::kNh; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  PendingTile<P> pend;
   bool have_pend = false;
 
   // ---- main loop: wait for super-tile u, release the entry of u-1, refill
@@ -1322,7 +1395,7 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
         const uint8_t* img =
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
         load_tile<P, SOA>(img, off, r);
-        PendingTile cur;
+        PendingTile<P> cur;
         score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), sm, acc, pend,
                            have_pend, cur);
         if (have_pend) {
@@ -1339,9 +1412,11 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
   }
 
   if (have_pend) {  // an odd tile out: pair it with an empty one
-    PendingTile none;
+    PendingTile<P> none;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) none.vw[i] = 0u;
+    for (int h = 0; h < T::kNh; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) none.vw[h][i] = 0u;
     none.pv = half4{0, 0, 0, 0};
     accumulate_pair<P>(pend, none, lv, acc);
   }
@@ -1352,15 +1427,18 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
     sm.z += swap8(sm.z);
   }
   const float l_run = quarter_sum(sm.l), z_run = quarter_sum(sm.z);
-  float o[32];  // o[8 * i + n]: acc[n][i] as output
+  float o[kOut];  // o[32 * h + 8 * i + n]: acc[8 * h + n][i] as output
   {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int h = 0; h < T::kNh; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const int pos = T::kVb == 4 ? tq::val4_pos(n) : (T::kVb == 3 ? tq::val3_pos(n) : tq::val2_pos(n));
-        o[8 * i + n] = T::kVlm ? acc[n][i] * inv : fmaf(acc[n][i], static_cast<float>(1u << (24 - pos)), z_run) * inv;
+        const float x = acc[8 * h + n][i];
+        o[32 * h + 8 * i + n] = T::kVlm ? x * inv : fmaf(x, static_cast<float>(1u << (24 - pos)), z_run) * inv;
       }
     }
   }
@@ -1371,55 +1449,74 @@ __global__ __launch_bounds__(512, 4) void tq_decode_stage1_kernel(DecodeArgs a) 
     wg_barrier();  // every wave is done with the ring
     float* mrg = reinterpret_cast<float*>(tq_ring);
     if (ph > 0) {
-      float* reg = mrg + ((ph - 1) * G + hh) * (33 * 64);
+      float* reg = mrg + ((ph - 1) * G + hh) * ((kOut + 1) * 64);
 #pragma unroll
-      for (int k = 0; k < 32; ++k) reg[k * 64 + lane] = o[k];
-      reg[32 * 64 + lane] = lse2;
+      for (int k = 0; k < kOut; ++k) reg[k * 64 + lane] = o[k];
+      reg[kOut * 64 + lane] = lse2;
     }
     wg_barrier();
     if (ph == 0) {
       float M = lse2;
-      for (int p = 1; p < NP; ++p) M = fmaxf(M, mrg[((p - 1) * G + hh) * (33 * 64) + 32 * 64 + lane]);
+      for (int p = 1; p < NP; ++p) M = fmaxf(M, mrg[((p - 1) * G + hh) * ((kOut + 1) * 64) + kOut * 64 + lane]);
       float wsum = __builtin_amdgcn_exp2f(lse2 - M);
 #pragma unroll
-      for (int k = 0; k < 32; ++k) o[k] *= wsum;
+      for (int k = 0; k < kOut; ++k) o[k] *= wsum;
       for (int p = 1; p < NP; ++p) {
-        const float* reg = mrg + ((p - 1) * G + hh) * (33 * 64);
-        const float lp = reg[32 * 64 + lane];
+        const float* reg = mrg + ((p - 1) * G + hh) * ((kOut + 1) * 64);
+        const float lp = reg[kOut * 64 + lane];
         if (lp == -INFINITY) continue;
         const float wp = __builtin_amdgcn_exp2f(lp - M);
         wsum += wp;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) o[k] = fmaf(wp, reg[k * 64 + lane], o[k]);
+        for (int k = 0; k < kOut; ++k) o[k] = fmaf(wp, reg[k * 64 + lane], o[k]);
       }
       const float inv = 1.f / wsum;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) o[k] *= inv;
+      for (int k = 0; k < kOut; ++k) o[k] *= inv;
       lse2 = M + log2f(wsum);
     }
   }
 
   // ---- Lloyd-Max values were accumulated in the rotated space: rotate the
   // head's output back, o <- s .* (H o) / sqrt(D) (lane quarter q4 holds dims
-  // 32 q4 .. 32 q4 + 31, as in the query operand) ----
+  // 128 h + 32 q4 .. 128 h + 32 q4 + 31 of each half h, as in the query
+  // operand; at head_dim 256 the stride-128 butterfly joins the halves) ----
   if constexpr (T::kVlm != 0) {
     if (ph == 0) {
-      wht128_quarters(o);
-      const float* sp = a.signs + 32 * q4;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) o[j] *= sp[j] * 0.08838834764831845f;
+      for (int h = 0; h < T::kNh; ++h) wht128_quarters(o + 32 * h);
+      if constexpr (T::kNh == 2) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float x0 = o[j], x1 = o[32 + j];
+          o[j] = x0 + x1;
+          o[32 + j] = x0 - x1;
+        }
+      }
+      constexpr float kInvSqrtD = T::kNh == 2 ? 0.0625f : 0.08838834764831845f;
+#pragma unroll
+      for (int h = 0; h < T::kNh; ++h) {
+        const float* sp = a.signs + 128 * h + 32 * q4;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) o[32 * h + j] *= sp[j] * kInvSqrtD;
+      }
     }
   }
 
   // ---- the split's partial rows: output and natural-log LSE ----
   if (ph == 0 && hl < geff) {
-    float* orow = a.part + prow(hl) * kRow + 32 * q4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{o[8 * i], o[8 * i + 1], o[8 * i + 2], o[8 * i + 3]};
-      *reinterpret_cast<f32x4*>(orow + 8 * i + 4) = f32x4{o[8 * i + 4], o[8 * i + 5], o[8 * i + 6], o[8 * i + 7]};
+    for (int h = 0; h < T::kNh; ++h) {
+      float* orow = a.part + prow(hl) * T::kRow + 128 * h + 32 * q4;
+      const float* oh = o + 32 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<f32x4*>(orow + 8 * i) = f32x4{oh[8 * i], oh[8 * i + 1], oh[8 * i + 2], oh[8 * i + 3]};
+        *reinterpret_cast<f32x4*>(orow + 8 * i + 4) =
+            f32x4{oh[8 * i + 4], oh[8 * i + 5], oh[8 * i + 6], oh[8 * i + 7]};
+      }
     }
-    if (q4 == 0) a.part[prow(hl) * kRow + kD] = lse2 * kLn2;
+    if (q4 == 0) a.part[prow(hl) * T::kRow + T::kDim] = lse2 * kLn2;
   }
 }
 
@@ -1435,36 +1532,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Output = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max), lse = max
 // + log(sum_s w_s), over the units of a (sequence, query head) row (the table
 // stage 1 writes).  Latency-bound, so the loads are issued together: after
-// the table read each lane fetches its 2 output dims of up to 16 units and
-// lane j the LSE of unit j, all at once.  kW waves share a row (wave w takes
-// units w, w + kW, ...; their running (max, sum, output) combine through
-// LDS) when rows have many units; otherwise each wave of the workgroup
-// takes its own row (kW = 1).
-template <int kW>
+// the table read each lane fetches its 2 output dims of each 128-dim head
+// half (NH halves) of up to 16 units and lane j the LSE of unit j, all at
+// once.  kW waves share a row (wave w takes units w, w + kW, ...; their
+// running (max, sum, output) combine through LDS) when rows have many
+// units; otherwise each wave of the workgroup takes its own row (kW = 1).
+template <int kW, int NH>
 __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
                                                                const float* __restrict__ part, int Hq, int rows,
                                                                void* out, int out_dtype, float* lse_out,
                                                                const float* __restrict__ sinks) {
   constexpr int kBatch = 16;
-  __shared__ float comb[kW > 1 ? kW - 1 : 1][2 * 64 + 2];
+  constexpr int kDim = 128 * NH, kRowN = kDim + static_cast<int>(tq::kPartPad), kO = 2 * NH;
+  __shared__ float comb[kW > 1 ? kW - 1 : 1][kO * 64 + 2];
   const int lane = threadIdx.x & 63;
   const int w = kW > 1 ? (threadIdx.x >> 6) : 0;
   const int row = kW > 1 ? blockIdx.x : blockIdx.x * 4 + (threadIdx.x >> 6);
   if (kW == 1 && row >= rows) return;
   const int b = row / Hq, hq = row - b * Hq;
   const int first = table[2 * b], n = table[2 * b + 1];
-  const float* base = part + (static_cast<int64_t>(first) * Hq + hq) * kRow;
-  const int64_t stride = static_cast<int64_t>(Hq) * kRow * kW;  // between this wave's consecutive units
-  base += static_cast<int64_t>(w) * Hq * kRow;
+  const float* base = part + (static_cast<int64_t>(first) * Hq + hq) * kRowN;
+  const int64_t stride = static_cast<int64_t>(Hq) * kRowN * kW;  // between this wave's consecutive units
+  base += static_cast<int64_t>(w) * Hq * kRowN;
   const int nw = n > w ? (n - w + kW - 1) / kW : 0;  // units of this wave
-  float M = -INFINITY, o0 = 0.f, o1 = 0.f, den = 0.f;
+  float M = -INFINITY, den = 0.f;
+  float o[kO];  // dims 128 h + 2 lane, 128 h + 2 lane + 1 at o[2 h], o[2 h + 1]
+#pragma unroll
+  for (int k = 0; k < kO; ++k) o[k] = 0.f;
   for (int s0 = 0; s0 < nw; s0 += kBatch) {
     const int ns = min(kBatch, nw - s0);
-    float2 v[kBatch];
+    float2 v[kBatch][NH];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q)
-      v[q] = q < ns ? *reinterpret_cast<const float2*>(base + (s0 + q) * stride + 2 * lane) : make_float2(0.f, 0.f);
-    const float ls = lane < ns ? base[(s0 + lane) * stride + kD] : -INFINITY;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        v[q][h] = q < ns ? *reinterpret_cast<const float2*>(base + (s0 + q) * stride + 128 * h + 2 * lane)
+                         : make_float2(0.f, 0.f);
+    const float ls = lane < ns ? base[(s0 + lane) * stride + kDim] : -INFINITY;
     float Mb = ls;
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, m, 64));  // lanes 0..15 hold the batch
@@ -1472,8 +1576,8 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
     const float Mn = fmaxf(M, Mb);
     if (Mn == -INFINITY) continue;  // nothing live yet
     const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
-    o0 *= alpha;
-    o1 *= alpha;
+#pragma unroll
+    for (int k = 0; k < kO; ++k) o[k] *= alpha;
     den *= alpha;
     M = Mn;
     const float wl = ls == -INFINITY ? 0.f : expf(ls - M);
@@ -1481,17 +1585,20 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
     for (int q = 0; q < kBatch; ++q) {
       const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), q));
       den += wq;
-      o0 = fmaf(wq, v[q].x, o0);
-      o1 = fmaf(wq, v[q].y, o1);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        o[2 * h] = fmaf(wq, v[q][h].x, o[2 * h]);
+        o[2 * h + 1] = fmaf(wq, v[q][h].y, o[2 * h + 1]);
+      }
     }
   }
   if (kW > 1) {
     if (w > 0) {
-      comb[w - 1][2 * lane] = o0;
-      comb[w - 1][2 * lane + 1] = o1;
+#pragma unroll
+      for (int k = 0; k < kO; ++k) comb[w - 1][kO * lane + k] = o[k];
       if (lane == 0) {
-        comb[w - 1][128] = M;
-        comb[w - 1][129] = den;
+        comb[w - 1][kO * 64] = M;
+        comb[w - 1][kO * 64 + 1] = den;
       }
     }
     __syncthreads();
@@ -1499,40 +1606,46 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
   }
   float Mt = M;
 #pragma unroll
-  for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][128]);  // no-op for kW == 1
+  for (int k = 0; k < kW - 1; ++k) Mt = fmaxf(Mt, comb[k][kO * 64]);  // no-op for kW == 1
   // an attention sink: one more term of the denominator, with no value
   const float sink = sinks ? sinks[hq] : -INFINITY;
   Mt = fmaxf(Mt, sink);
   float lse = -INFINITY;
   if (Mt != -INFINITY) {
-    float a0 = M == -INFINITY ? 0.f : expf(M - Mt);
-    o0 *= a0;
-    o1 *= a0;
+    const float a0 = M == -INFINITY ? 0.f : expf(M - Mt);
+#pragma unroll
+    for (int k = 0; k < kO; ++k) o[k] *= a0;
     den *= a0;
 #pragma unroll
     for (int k = 0; k < kW - 1; ++k) {
-      const float mk = comb[k][128];
+      const float mk = comb[k][kO * 64];
       if (mk == -INFINITY) continue;
       const float ak = expf(mk - Mt);
-      den = fmaf(ak, comb[k][129], den);
-      o0 = fmaf(ak, comb[k][2 * lane], o0);
-      o1 = fmaf(ak, comb[k][2 * lane + 1], o1);
+      den = fmaf(ak, comb[k][kO * 64 + 1], den);
+#pragma unroll
+      for (int j = 0; j < kO; ++j) o[j] = fmaf(ak, comb[k][kO * lane + j], o[j]);
     }
     if (sink != -INFINITY) den += expf(sink - Mt);
-    o0 /= den;
-    o1 /= den;
+#pragma unroll
+    for (int k = 0; k < kO; ++k) o[k] /= den;
     lse = Mt + logf(den);
   } else {
-    o0 = o1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kO; ++k) o[k] = 0.f;
   }
-  const int64_t ob = static_cast<int64_t>(row) * kD + 2 * lane;
-  if (out_dtype == TQ_F32) {
-    *reinterpret_cast<float2*>(static_cast<float*>(out) + ob) = make_float2(o0, o1);
-  } else if (out_dtype == TQ_F16) {
-    *reinterpret_cast<__half2*>(static_cast<__half*>(out) + ob) = __halves2half2(__float2half_rn(o0), __float2half_rn(o1));
-  } else {
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + ob) =
-        static_cast<uint32_t>(f32_to_bf16_rne(o0)) | (static_cast<uint32_t>(f32_to_bf16_rne(o1)) << 16);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int64_t ob = static_cast<int64_t>(row) * kDim + 128 * h + 2 * lane;
+    const float o0 = o[2 * h], o1 = o[2 * h + 1];
+    if (out_dtype == TQ_F32) {
+      *reinterpret_cast<float2*>(static_cast<float*>(out) + ob) = make_float2(o0, o1);
+    } else if (out_dtype == TQ_F16) {
+      *reinterpret_cast<__half2*>(static_cast<__half*>(out) + ob) =
+          __halves2half2(__float2half_rn(o0), __float2half_rn(o1));
+    } else {
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + ob) =
+          static_cast<uint32_t>(f32_to_bf16_rne(o0)) | (static_cast<uint32_t>(f32_to_bf16_rne(o1)) << 16);
+    }
   }
   if (lse_out && lane == 0) lse_out[row] = lse;
 }
@@ -1565,8 +1678,16 @@ int launch_stage1_l(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, h
   return launch_stage1_t<P, 1, 0, SOA>(a, nblocks, lds, stream);
 }
 
+// head_dim 256 (preset code P | kHead256): one tile per wave (the plan's
+// choice there: two tile images per wave do not fit the ring).
 template <int P>
-int launch_stage1(const DecodeArgs& a, int tpw, bool soa, int64_t nblocks, size_t lds, hipStream_t stream) {
+int launch_stage1(const DecodeArgs& a, int tpw, bool soa, bool d256, int64_t nblocks, size_t lds,
+                  hipStream_t stream) {
+  if (d256) {
+    if (tpw != 1) return TQ_EUNSUPPORTED;
+    return soa ? launch_stage1_t<P | kHead256, 1, 0, 1>(a, nblocks, lds, stream)
+               : launch_stage1_t<P | kHead256, 1, 0, 0>(a, nblocks, lds, stream);
+  }
   return soa ? launch_stage1_l<P, 1>(a, tpw, nblocks, lds, stream)
              : launch_stage1_l<P, 0>(a, tpw, nblocks, lds, stream);
 }
@@ -1611,22 +1732,24 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   const int64_t nblocks = plan.grid;
   const size_t lds = plan.lds;
   const bool soa = layout->block_layout == TQ_LAYOUT_SOA;
+  const bool d256 = layout->head_dim == 256;
   switch (layout->preset) {
-    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, plan.tpw, soa, nblocks, lds, stream);
-    case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, plan.tpw, soa, nblocks, lds, stream);
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, plan.tpw, soa, d256, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }
 
-int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const float* sinks, const void* workspace,
-           void* out, int32_t out_dtype, float* lse_out, hipStream_t stream) {
+template <int NH>
+int stage2_t(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const float* sinks, const void* workspace,
+             void* out, int32_t out_dtype, float* lse_out, hipStream_t stream) {
   int rows = batch * num_q_heads;
   int Hq = num_q_heads;
   const int32_t* table = static_cast<const int32_t*>(workspace);
@@ -1636,10 +1759,17 @@ int stage2(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const floa
   // on units per sequence is S_max (balanced units give long sequences more,
   // so the threshold leaves room).
   if (tq::max_splits(batch, num_kv_splits) > 24)
-    return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<4>), dim3(rows),
-                                          dim3(256), args, 0, stream));
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<1>),
+    return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<4, NH>),
+                                          dim3(rows), dim3(256), args, 0, stream));
+  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<1, NH>),
                                         dim3((rows + 3) / 4), dim3(256), args, 0, stream));
+}
+
+int stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits, const float* sinks,
+           const void* workspace, void* out, int32_t out_dtype, float* lse_out, hipStream_t stream) {
+  return head_dim == 256
+             ? stage2_t<2>(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, stream)
+             : stage2_t<1>(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, stream);
 }
 
 }  // namespace
@@ -1678,7 +1808,7 @@ extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head
   int st = tq::validate_stage2(batch, num_q_heads, head_dim, num_kv_splits, workspace, workspace_bytes, out,
                                out_dtype);
   if (st != TQ_OK || batch == 0) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out,
+  return stage2(batch, num_q_heads, head_dim, num_kv_splits, sinks, workspace, out, out_dtype, lse_out,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -1698,5 +1828,5 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
   st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
               block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, workspace, s);
   if (st != TQ_OK) return st;
-  return stage2(batch, num_q_heads, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, s);
+  return stage2(batch, num_q_heads, layout->head_dim, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, s);
 }

@@ -4,13 +4,13 @@
 // then attend over cached + new tokens).
 //
 // Work mapping as in the store (gfx950, wave64): a "row" is one (token, KV
-// head) slot, 8 lanes per row, 16 consecutive coordinates per lane, 8 rows
-// per wave.  MSE keys: the lane looks up gamma * c[code] for its 16 rotated
+// head) slot, D / 16 lanes per row (8 at head_dim 128, 16 at 256), 16
+// consecutive coordinates per lane.  MSE keys: the lane looks up gamma * c[code] for its 16 rotated
 // coordinates and applies the rotation's transpose in registers, s .* (H y)
 // / sqrt(D) (H symmetric, H H = D I), with the store's butterflies.  FP8 keys
 // and the values decode lane-locally.  Each lane writes its 16 outputs of K
-// and of V as 16-byte vector stores, so a row's 8 lanes write one contiguous
-// run.  HBM-bound: slot bytes in, 2 * 128 elements out per slot.
+// and of V as 16-byte vector stores, so a row's lanes write one contiguous
+// run.  HBM-bound: slot bytes in, 2 * D elements out per slot.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -21,12 +21,9 @@
 
 namespace {
 
-constexpr int kD = 128;
 constexpr int kDpl = tq::kWhtPerLane;  // coordinates per lane
-constexpr int kRowsPerWave = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 
 struct DequantArgs {
   const uint8_t* cache;
@@ -118,8 +115,8 @@ __device__ __forceinline__ void load_fields(const uint8_t* kp, const uint8_t* vp
   f.scale_zero = VLM ? ld_u16(sp) : (ld_u16(sp) | (ld_u16(sp + 2) << 16));
 }
 
-// Each wave takes kGroups groups of 8 consecutive rows (a group: 8 lanes per
-// row); the loads of all its groups are issued before any is decoded, so a
+// Each wave takes kGroups groups of 64 / (D / 16) consecutive rows (D / 16
+// lanes per row); the loads of all its groups are issued before any is decoded, so a
 // wave keeps several slots' worth of reads in flight.  The MSE presets, with
 // more arithmetic per slot, take 4; FP8 keys keep 1 and more waves resident.
 template <int KEY_FP8>
@@ -127,9 +124,11 @@ constexpr int groups_per_wave() { return KEY_FP8 ? 1 : 4; }
 
 // VLM: Lloyd-Max values, decoded like MSE keys with the value codebook (which
 // follows the key codebook in the table).
-template <int KEY_FP8, int KB, int VB, int VLM, int OUT>
+template <int D, int KEY_FP8, int KB, int VB, int VLM, int OUT>
 __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
   constexpr int kGroups = groups_per_wave<KEY_FP8 && !VLM>();
+  constexpr int kLpr = D / kDpl;  // lanes per row
+  constexpr int kRowsPerWave = 64 / kLpr;
   constexpr int kL = 1 << KB, kLv = 1 << VB;
   __shared__ float cent[KEY_FP8 ? 1 : kL];
   __shared__ float vcent[VLM ? kLv : 1];
@@ -140,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
   }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int sub = lane & 7;
-  const uint32_t base = (blockIdx.x * kWaves + wave) * (kRowsPerWave * kGroups) + (lane >> 3);
+  const int sub = lane & (kLpr - 1);
+  const uint32_t base = (blockIdx.x * kWaves + wave) * (kRowsPerWave * kGroups) + lane / kLpr;
 
   SlotFields<KEY_FP8, KB, VB> f[kGroups];
   uint32_t rows[kGroups];
@@ -154,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
     const int h = static_cast<int>(row - t * a.num_kv_heads);
     const int64_t blk = a.block_table[t / static_cast<uint32_t>(a.block_size)];
     const uint32_t tb = t % static_cast<uint32_t>(a.block_size);
-    constexpr int kKdata = KEY_FP8 ? kD : kD * KB / 8;
-    constexpr int kKps = KEY_FP8 ? kD : kKdata + 2;
-    constexpr int kVdata = kD * VB / 8;
+    constexpr int kKdata = KEY_FP8 ? D : D * KB / 8;
+    constexpr int kKps = KEY_FP8 ? D : kKdata + 2;
+    constexpr int kVdata = D * VB / 8;
     if (a.soa) {
       // SoA: row r = t * Hk + h of the block: [key data | value codes] at
       // r * kDb, then the fields (norm, scale, zero / scale, zero) at
@@ -176,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
 
   float sg[kDpl];  // signs * (+-1/sqrt(D)), the lane sign of the butterflies undone
   if (!KEY_FP8 || VLM) {
-    const float c = tq::wht_lane_negated(sub) ? -0.08838834764831845f : 0.08838834764831845f;
+    constexpr float kInvSqrtD = D == 128 ? 0.08838834764831845f : 0.0625f;
+    const float c = tq::wht_lane_negated(sub) ? -kInvSqrtD : kInvSqrtD;
     const float4* sp = reinterpret_cast<const float4*>(a.signs + kDpl * sub);
 #pragma unroll
     for (int i = 0; i < kDpl / 4; ++i) {
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
 #pragma unroll
       for (int i = 0; i < kDpl; ++i) k[i] = gamma * cent[field<KB>(f[g].kw, i)];
       tq::wht_inlane(k, 1);
-      tq::wht_crosslane(k, sub);
+      tq::wht_crosslane<kLpr>(k, sub);
 #pragma unroll
       for (int i = 0; i < kDpl; ++i) k[i] *= sg[i];
     }
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
 #pragma unroll
       for (int i = 0; i < kDpl; ++i) v[i] = gv * vcent[field<VB>(f[g].vw, i)];
       tq::wht_inlane(v, 1);
-      tq::wht_crosslane(v, sub);
+      tq::wht_crosslane<kLpr>(v, sub);
 #pragma unroll
       for (int i = 0; i < kDpl; ++i) v[i] *= sg[i];
     } else {
@@ -233,23 +233,40 @@ __global__ __launch_bounds__(kThreads) void tq_dequant_kernel(DequantArgs a) {
     if (rows[g] < static_cast<uint32_t>(a.num_rows)) {
       const uint32_t t = rows[g] / static_cast<uint32_t>(a.num_kv_heads);
       const int h = static_cast<int>(rows[g] - t * a.num_kv_heads);
-      const int64_t e = static_cast<int64_t>(t) * a.out_tok_stride + h * kD + kDpl * sub;
+      const int64_t e = static_cast<int64_t>(t) * a.out_tok_stride + h * D + kDpl * sub;
       store16<OUT>(a.key_out, e, k);
       store16<OUT>(a.value_out, e, v);
     }
   }
 }
 
-template <int KEY_FP8, int KB, int VB, int VLM = 0>
+template <int D, int KEY_FP8, int KB, int VB, int VLM = 0>
 int launch_dequant(const DequantArgs& a, int32_t out_dtype, hipStream_t stream) {
-  const int64_t per_block = static_cast<int64_t>(kRowsPerBlock) * groups_per_wave<KEY_FP8 && !VLM>();
+  const int64_t per_block = static_cast<int64_t>(kThreads / (D / kDpl)) * groups_per_wave<KEY_FP8 && !VLM>();
   const int blocks = static_cast<int>((a.num_rows + per_block - 1) / per_block);
   DequantArgs arg = a;
   void* args[] = {&arg};
-  const void* fn = out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_F32>)
-                   : out_dtype == TQ_F16 ? reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_F16>)
-                                         : reinterpret_cast<const void*>(&tq_dequant_kernel<KEY_FP8, KB, VB, VLM, TQ_BF16>);
+  const void* fn =
+      out_dtype == TQ_F32   ? reinterpret_cast<const void*>(&tq_dequant_kernel<D, KEY_FP8, KB, VB, VLM, TQ_F32>)
+      : out_dtype == TQ_F16 ? reinterpret_cast<const void*>(&tq_dequant_kernel<D, KEY_FP8, KB, VB, VLM, TQ_F16>)
+                            : reinterpret_cast<const void*>(&tq_dequant_kernel<D, KEY_FP8, KB, VB, VLM, TQ_BF16>);
   return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
+}
+
+template <int D>
+int launch_preset(int32_t preset, const DequantArgs& a, int32_t out_dtype, hipStream_t s) {
+  switch (preset) {
+    case TQ_K8V4: return launch_dequant<D, 1, 8, 4>(a, out_dtype, s);
+    case TQ_4BIT_NC: return launch_dequant<D, 0, 4, 4>(a, out_dtype, s);
+    case TQ_K3V4_NC: return launch_dequant<D, 0, 3, 4>(a, out_dtype, s);
+    case TQ_3BIT_NC: return launch_dequant<D, 0, 3, 3>(a, out_dtype, s);
+    case TQ_K8V3: return launch_dequant<D, 1, 8, 3>(a, out_dtype, s);
+    case TQ_K4V3_NC: return launch_dequant<D, 0, 4, 3>(a, out_dtype, s);
+    case TQ_2BIT_NC: return launch_dequant<D, 0, 2, 2>(a, out_dtype, s);
+    case TQ_K8V3LM: return launch_dequant<D, 1, 8, 3, 1>(a, out_dtype, s);
+    case TQ_3BIT_LM: return launch_dequant<D, 0, 3, 3, 1>(a, out_dtype, s);
+  }
+  return TQ_EPRESET;
 }
 
 }  // namespace
@@ -275,16 +292,6 @@ extern "C" int tq_dequant_kv(const tq_layout* layout, const void* kv_cache, int6
   a.slot_bytes = layout->slot_size_aligned;
   a.soa = layout->block_layout == TQ_LAYOUT_SOA;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (layout->preset) {
-    case TQ_K8V4: return launch_dequant<1, 8, 4>(a, out_dtype, s);
-    case TQ_4BIT_NC: return launch_dequant<0, 4, 4>(a, out_dtype, s);
-    case TQ_K3V4_NC: return launch_dequant<0, 3, 4>(a, out_dtype, s);
-    case TQ_3BIT_NC: return launch_dequant<0, 3, 3>(a, out_dtype, s);
-    case TQ_K8V3: return launch_dequant<1, 8, 3>(a, out_dtype, s);
-    case TQ_K4V3_NC: return launch_dequant<0, 4, 3>(a, out_dtype, s);
-    case TQ_2BIT_NC: return launch_dequant<0, 2, 2>(a, out_dtype, s);
-    case TQ_K8V3LM: return launch_dequant<1, 8, 3, 1>(a, out_dtype, s);
-    case TQ_3BIT_LM: return launch_dequant<0, 3, 3, 1>(a, out_dtype, s);
-  }
-  return TQ_EPRESET;
+  return layout->head_dim == 256 ? launch_preset<256>(layout->preset, a, out_dtype, s)
+                                 : launch_preset<128>(layout->preset, a, out_dtype, s);
 }

@@ -49,7 +49,7 @@ extern "C" const char* tq_status_str(int status) {
     case TQ_OK: return "ok";
     case TQ_EINVAL: return "invalid argument (null pointer, negative size or misaligned tensor)";
     case TQ_EPRESET: return "unknown preset";
-    case TQ_EHEADDIM: return "unsupported head_dim (kernels support 128)";
+    case TQ_EHEADDIM: return "unsupported head_dim (kernels support 128 and 256)";
     case TQ_EBLOCK: return "block_size must be 16, 32, 64 or 128";
     case TQ_EGQA: return "num_q_heads must be a positive multiple of num_kv_heads";
     case TQ_EWORKSPACE: return "workspace too small";
@@ -303,7 +303,7 @@ int validate_store(const tq_layout* L, const void* key, const void* value, int32
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (in_dtype != TQ_F16 && in_dtype != TQ_BF16) return TQ_EDTYPE;
-  if (L->head_dim != 128) return TQ_EHEADDIM;
+  if (L->head_dim != 128 && L->head_dim != 256) return TQ_EHEADDIM;
   if (num_tokens == 0) return TQ_OK;
   if (!key || !value || !slot_mapping || !kv_cache) return TQ_EINVAL;
   if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache) || key_tok_stride % 8 != 0 ||
@@ -327,7 +327,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return TQ_EGQA;
   if (q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EDTYPE;
-  if (L->head_dim != 128) return TQ_EHEADDIM;
+  if (L->head_dim != 128 && L->head_dim != 256) return TQ_EHEADDIM;
   if (num_kv_splits <= 0 || num_kv_splits > 4096 || sliding_window < 0) return TQ_EINVAL;
   if (L->block_layout == TQ_LAYOUT_SOA && num_kv_heads > 8 && num_kv_heads % 8 != 0) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
@@ -341,7 +341,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
 int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                     const void* workspace, size_t ws_bytes, const void* out, int32_t out_dtype) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_splits <= 0 || num_kv_splits > 4096) return TQ_EINVAL;
-  if (head_dim != 128) return TQ_EHEADDIM;
+  if (head_dim != 128 && head_dim != 256) return TQ_EHEADDIM;
   if (out_dtype != TQ_F16 && out_dtype != TQ_BF16 && out_dtype != TQ_F32) return TQ_EDTYPE;
   if (batch == 0) return TQ_OK;
   if (!workspace || !out || !aligned16(workspace)) return TQ_EINVAL;
@@ -357,7 +357,7 @@ int validate_dequant(const tq_layout* L, const void* kv_cache, int64_t num_block
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
   if (out_dtype != TQ_F16 && out_dtype != TQ_BF16 && out_dtype != TQ_F32) return TQ_EDTYPE;
-  if (L->head_dim != 128) return TQ_EHEADDIM;
+  if (L->head_dim != 128 && L->head_dim != 256) return TQ_EHEADDIM;
   if (num_tokens == 0) return TQ_OK;
   if (!kv_cache || !block_table || !key_out || !value_out) return TQ_EINVAL;
   if (!aligned16(kv_cache) || !aligned16(key_out) || !aligned16(value_out) || out_tok_stride % 8 != 0 ||

@@ -91,23 +91,25 @@ struct DecodePlan {
 };
 
 // Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
-// this many for any head count at head_dim 128 (slots of 196 / 134 / 118 /
-// 102 / 180 / 118 / 70 / 178 / 100 bytes in preset order; a wave of G waves per tile
-// takes ceil(spt / G) of the tile's spt loads).  SoA images pad each image
-// row by 16 bytes and round the data part and the metadata part up to whole
-// slots separately, which takes one load more with one KV head for k8v4,
-// 4bit_nc, 3bit_nc and 2bit_nc.
-constexpr int max_dma_loads(int preset, bool soa = false) {
+// this many for any head count (a wave of G waves per tile takes ceil(spt /
+// G) of the tile's spt loads).  head_dim 128: slots of 196 / 134 / 118 / 102
+// / 180 / 118 / 70 / 178 / 100 bytes in preset order; SoA images pad each
+// image row by 16 bytes and round the data part and the metadata part up to
+// whole slots separately, which takes one load more with one KV head for
+// k8v4, 4bit_nc, 3bit_nc and 2bit_nc.  head_dim 256: slots of 388 / 262 / 230
+// / 198 / 356 / 230 / 134 / 354 / 196 bytes.
+constexpr int max_dma_loads(int preset, bool soa = false, int head_dim = 128) {
+  const bool d256 = head_dim == 256;
   switch (preset) {
-    case TQ_K8V4: return soa ? 5 : 4;
-    case TQ_4BIT_NC: return soa ? 4 : 3;
-    case TQ_K3V4_NC: return 3;
-    case TQ_3BIT_NC: return soa ? 3 : 2;
-    case TQ_K8V3: return 4;
-    case TQ_K4V3_NC: return 3;
-    case TQ_2BIT_NC: return soa ? 3 : 2;
-    case TQ_K8V3LM: return 4;
-    case TQ_3BIT_LM: return soa ? 3 : 2;
+    case TQ_K8V4: return d256 ? (soa ? 8 : 7) : (soa ? 5 : 4);
+    case TQ_4BIT_NC: return d256 ? (soa ? 6 : 5) : (soa ? 4 : 3);
+    case TQ_K3V4_NC: return d256 ? (soa ? 5 : 4) : 3;
+    case TQ_3BIT_NC: return d256 ? (soa ? 5 : 4) : (soa ? 3 : 2);
+    case TQ_K8V3: return d256 ? (soa ? 7 : 6) : 4;
+    case TQ_K4V3_NC: return d256 ? (soa ? 5 : 4) : 3;
+    case TQ_2BIT_NC: return d256 ? (soa ? 4 : 3) : (soa ? 3 : 2);
+    case TQ_K8V3LM: return d256 ? (soa ? 7 : 6) : 4;
+    case TQ_3BIT_LM: return d256 ? (soa ? 5 : 4) : (soa ? 3 : 2);
   }
   return 0;
 }
@@ -151,12 +153,16 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   const int dslots = soa ? static_cast<int>((G * soa_data + kSoaRowPad + 63) / 64) : 0;
   const int spt = soa ? dslots + static_cast<int>((G * soa_meta + 63) / 64) : static_cast<int>((tc_max + 63) / 64);
   // MSE keys: two tiles per wave between barriers (two independent chains
-  // to interleave), when the ring still fits two workgroups per CU
-  const int tpw = (!L->key_fp8 && 2 * static_cast<size_t>(P) * spt * 1024 * 2 <= 80 * 1024) ? 2 : 1;
+  // to interleave), when the ring still fits two workgroups per CU (never
+  // at head_dim 256, whose tile images are twice as large)
+  const int tpw =
+      (!L->key_fp8 && L->head_dim == 128 && 2 * static_cast<size_t>(P) * spt * 1024 * 2 <= 80 * 1024) ? 2 : 1;
   const size_t entry = static_cast<size_t>(P) * tpw * spt * 1024;
   size_t R = kLdsBudget / entry;
   R = R < 2 ? 2 : (R > 4 ? 4 : R);
-  const size_t merge = P > 1 ? static_cast<size_t>(P - 1) * G * 33 * 64 * 4 : 0;
+  // phase merge: per (phase > 0, head) a lane's outputs (32 per 128-dim
+  // half) and its LSE
+  const size_t merge = P > 1 ? static_cast<size_t>(P - 1) * G * (32 * (L->head_dim / 128) + 1) * 64 * 4 : 0;
   p->G = G;
   p->P = P;
   p->R = static_cast<int>(R);
@@ -170,7 +176,7 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   p->grid = p->units * wg_per_unit;
   const int loads = (spt + G - 1) / G;  // DMA slots per wave per tile of its phase
   const int64_t blk_bytes = 128 * row;  // largest block (block_size 128)
-  if (p->lds > kLdsMax || loads > max_dma_loads(L->preset, soa) || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
+  if (p->lds > kLdsMax || loads > max_dma_loads(L->preset, soa, L->head_dim) || p->grid > 0x7FFFFFFF || p->units > 0x7FFFFFFF ||
       blk_bytes > 0xFFFFFFFFLL || s_int > max_splits(batch, num_splits))
     return TQ_EUNSUPPORTED;
   return TQ_OK;

@@ -2,13 +2,13 @@
 // paged cache, one fused launch ([PR] "实现拆解" item 4: bucketing, norm,
 // index packing and value quantization in one kernel; [API] _store_kv).
 //
-// Work mapping (gfx950, wave64): a "row" is one (token, KV head) pair.  Each
-// wave owns 8 rows, 8 lanes per row, 16 contiguous dims per lane (D = 128).
-// The randomized Hadamard rotation runs in registers: the butterfly strides
-// 1..8 are inside a lane, strides 16/32/64 are lane exchanges within the
-// row's 8-lane group ([TQ+] "Background": random signs, then the WHT).
-// Norms and min/max reduce over the same 8 lanes.  The codebook and its
-// boundaries sit in LDS.
+// Work mapping (gfx950, wave64): a "row" is one (token, KV head) pair, held
+// by D / 16 lanes (8 at head_dim 128, 16 at 256), 16 contiguous dims per
+// lane; a wave owns 64 / (D / 16) rows.  The randomized Hadamard rotation
+// runs in registers: the butterfly strides 1..8 are inside a lane, strides
+// 16 .. D / 2 are lane exchanges within the row's lane group ([TQ+]
+// "Background": random signs, then the WHT).  Norms and min/max reduce over
+// the same lanes.  The codebook and its boundaries sit in LDS.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -22,13 +22,16 @@ namespace {
 
 using tq::xor_shfl;
 
-constexpr int kD = 128;
 constexpr int kDpl = 16;           // dims per lane
-constexpr int kRowsPerWave = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
-constexpr int kMaxSlot = 208;  // >= every preset's slot at head_dim 128, 16-byte multiple
+constexpr int kStageRows = 8;  // rows assembled per 16-byte-store group
+// Rows of a workgroup at head_dim D (D / 16 lanes per row).
+template <int D>
+constexpr int rows_per_block() { return kThreads / (D / kDpl); }
+// >= every preset's slot at head_dim D, 16-byte multiple
+template <int D>
+constexpr int max_slot() { return D == 128 ? 208 : 400; }
 
 struct StoreArgs {
   const uint16_t* key;
@@ -118,21 +121,20 @@ struct Pack32 {
   }
 };
 
-// Lloyd-Max quantization of one row held by 8 lanes (16 coordinates each):
+// Lloyd-Max quantization of one row held by LPR = D / 16 lanes (16 coordinates each):
 // norm, randomized Hadamard rotation in registers, bucket search over the
 // LDS boundary tree, packed codes and the fp16 norm field (norm-corrected
 // when NC_).  Used for MSE keys and for Lloyd-Max values alike ([TQ+]
 // "What landed": values take the keys' rotation and codebook).
-template <int B, int NC_>
+template <int B, int NC_, int LPR>
 __device__ __forceinline__ void mse_quantize(const float x[kDpl], const float* __restrict__ signs, int sub,
                                              const float* tree, const float* cent, uint32_t out[2],
                                              uint32_t& gamma_bits) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kDpl; ++i) ss = fmaf(x[i], x[i], ss);
-  ss += xor_shfl(ss, 1);
-  ss += xor_shfl(ss, 2);
-  ss += xor_shfl(ss, 4);
+#pragma unroll
+  for (int msk = 1; msk < LPR; msk <<= 1) ss += xor_shfl(ss, msk);
   const float nu = sqrtf(ss);
 
   // Walsh-Hadamard butterflies, natural (Sylvester) order.  Stride 1 takes
@@ -150,11 +152,12 @@ __device__ __forceinline__ void mse_quantize(const float x[kDpl], const float* _
     y[4 * i + 3] = fmaf(x[4 * i + 2], s4.z, -q1);
   }
   tq::wht_inlane(y, 2);
-  // strides 16, 32, 64 across the row's lanes; the lane sign they leave is
+  // strides 16 .. D / 2 across the row's lanes; the lane sign they leave is
   // folded into the scale below
-  tq::wht_crosslane(y, sub);
+  tq::wht_crosslane<LPR>(y, sub);
   // u = (H s.*x) / (sqrt(D) * nu); nu == 0 gives u = 0 and a zero norm field
-  const float inv0 = nu > 0.f ? 1.0f / (nu * 11.313708498984761f) : 0.f;
+  constexpr float kSqrtD = LPR == 8 ? 11.313708498984761f : 16.f;
+  const float inv0 = nu > 0.f ? 1.0f / (nu * kSqrtD) : 0.f;
   const float inv = tq::wht_lane_negated(sub) ? -inv0 : inv0;
   float cs = 0.f;
   Pack32<B> kp;
@@ -168,9 +171,8 @@ __device__ __forceinline__ void mse_quantize(const float x[kDpl], const float* _
   kp.finish_nodes();
   out[0] = kp.w[0];
   out[1] = kp.w[1];
-  cs += xor_shfl(cs, 1);
-  cs += xor_shfl(cs, 2);
-  cs += xor_shfl(cs, 4);
+#pragma unroll
+  for (int msk = 1; msk < LPR; msk <<= 1) cs += xor_shfl(cs, msk);
   float gamma = nu;
   if (NC_) gamma = nu > 0.f ? nu / sqrtf(cs) : 0.f;
   gamma_bits = __half_as_ushort(__float2half_rn(gamma));
@@ -194,8 +196,10 @@ __device__ __forceinline__ void load_tables(const float* centroids, const float*
 
 // VLM: Lloyd-Max values (rotated, codebook after the key codebook in the
 // tables, norm-corrected), else uniform min/max values.
-template <int KEY_FP8, int KB, int VB, int NC, int VLM, int BF16>
+template <int D, int KEY_FP8, int KB, int VB, int NC, int VLM, int BF16>
 __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
+  constexpr int kLpr = D / kDpl;  // lanes per row
+  constexpr int kRowsPerWave = 64 / kLpr;
   constexpr int kL = 1 << KB, kLv = 1 << VB;
   __shared__ float tree[KEY_FP8 ? 4 : kL];      // node 1 .. kL - 1: boundaries in search order
   __shared__ float cent[KEY_FP8 ? 8 : 2 * kL];  // kL + code: centroid of the search's end node
@@ -212,16 +216,16 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int sub = lane & 7;
-  const uint32_t row0 = (blockIdx.x * kWaves + wave) * kRowsPerWave + (lane >> 3);
+  const int sub = lane & (kLpr - 1);
+  const uint32_t row0 = (blockIdx.x * kWaves + wave) * kRowsPerWave + lane / kLpr;
   const bool active = row0 < static_cast<uint32_t>(a.num_rows);
   const uint32_t row = active ? row0 : a.num_rows - 1;  // inactive rows compute on a valid row, store nothing
   const uint32_t n = row / static_cast<uint32_t>(a.num_kv_heads);
   const int h = static_cast<int>(row - n * a.num_kv_heads);
 
   float x[kDpl], v[kDpl];
-  load_row16<BF16>(a.key + n * a.key_tok_stride + h * kD + sub * kDpl, x);
-  load_row16<BF16>(a.value + n * a.val_tok_stride + h * kD + sub * kDpl, v);
+  load_row16<BF16>(a.key + n * a.key_tok_stride + h * D + sub * kDpl, x);
+  load_row16<BF16>(a.value + n * a.val_tok_stride + h * D + sub * kDpl, v);
 
   const int64_t m = a.slot_mapping[n];
   uint8_t* slot = a.cache + (m * a.num_kv_heads + h) * static_cast<int64_t>(a.slot_bytes);
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   // SoA ([API] _store_kv): row r = t * Hk + h of the block holds [key data |
   // value data] at r * kDb; its fields (norm, scale, zero / scale, zero)
   // follow the data region as 16-bit values at 2 * (r * kNf + f)
-  constexpr int kDb = (KEY_FP8 ? kD : kD * KB / 8) + kD * VB / 8;
+  constexpr int kDb = (KEY_FP8 ? D : D * KB / 8) + D * VB / 8;
   constexpr int kNf = (KEY_FP8 ? 0 : 1) + (VLM ? 1 : 2);
   const int64_t mm = m >= 0 ? m : 0;
   const int64_t blk_rows = static_cast<int64_t>(a.num_kv_heads) << a.bs_log2;  // rows of a block
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
       }
     }
   } else {
-    mse_quantize<(KEY_FP8 ? 2 : KB), NC>(x, a.signs, sub, tree, cent, kbytes, gamma_bits);
+    mse_quantize<(KEY_FP8 ? 2 : KB), NC, kLpr>(x, a.signs, sub, tree, cent, kbytes, gamma_bits);
   }
 
   // ---------------- value ----------------
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   __half z16 = __ushort_as_half(0), s16 = __ushort_as_half(0);  // uniform codes: zero, scale
   uint32_t vgamma_bits = 0;                                          // Lloyd-Max codes: norm
   if constexpr (VLM != 0) {
-    mse_quantize<VB, 1>(v, a.signs, sub, vtree, vcent, vp32.w, vgamma_bits);
+    mse_quantize<VB, 1, kLpr>(v, a.signs, sub, vtree, vcent, vp32.w, vgamma_bits);
   } else {
   float vmin = v[0], vmax = v[0];
 #pragma unroll
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     vmax = fmaxf(vmax, v[i]);
   }
 #pragma unroll
-  for (int msk = 1; msk < 8; msk <<= 1) {
+  for (int msk = 1; msk < kLpr; msk <<= 1) {
     vmin = fminf(vmin, xor_shfl(vmin, msk));
     vmax = fmaxf(vmax, xor_shfl(vmax, msk));
   }
@@ -308,9 +312,9 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   constexpr int kValBytesPerLane = (kDpl * VB) / 8;
 
   // ---------------- stores ----------------
-  const int kdata = KEY_FP8 ? kD : (kD * KB) / 8;
-  const int kps = KEY_FP8 ? kD : kdata + 2;
-  const int vdata = (kD * VB) / 8;
+  const int kdata = KEY_FP8 ? D : (D * KB) / 8;
+  const int kps = KEY_FP8 ? D : kdata + 2;
+  const int vdata = (D * VB) / 8;
   // the row's fields: key bytes, value bytes, norm, scale (zero 2 bytes on)
   auto put = [&](uint8_t* kp0, uint8_t* vp0, uint8_t* gp, uint8_t* sp) {
     uint8_t* kp = kp0 + sub * kKeyBytesPerLane;
@@ -330,36 +334,39 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
     }
   };
   const int fs = KEY_FP8 ? 0 : 2;  // SoA: byte of the scale inside a record
-  if (a.num_kv_heads % kRowsPerWave == 0) {
-    // The wave's 8 rows are 8 consecutive heads of one token: 8 adjacent
-    // slots (SoA: 8 adjacent data rows and 8 adjacent records), 16-byte
-    // aligned.  Assemble them in LDS, then write them with 16-byte stores.
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][kRowsPerWave * kMaxSlot];
-    const int q = lane >> 3;  // row of the wave
+  if (a.num_kv_heads % kStageRows == 0) {
+    // Each group of 8 consecutive rows (one wave at head_dim 128, two at
+    // 256) is 8 consecutive heads of one token: 8 adjacent slots (SoA: 8
+    // adjacent data rows and 8 adjacent records), 16-byte aligned.  Assemble
+    // them in LDS, then write them with 16-byte stores.
+    constexpr int kGt = kStageRows * kLpr;  // threads of a group
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads / kGt][kStageRows * max_slot<D>()];
+    const int gi = threadIdx.x / kGt, gt = threadIdx.x % kGt;
+    const int q = gt / kLpr;  // row of the group
     if (a.soa) {
-      uint8_t* sd = stage[wave] + q * kDb;
-      uint8_t* sm = stage[wave] + kRowsPerWave * kDb + q * (2 * kNf);
+      uint8_t* sd = stage[gi] + q * kDb;
+      uint8_t* sm = stage[gi] + kStageRows * kDb + q * (2 * kNf);
       put(sd, sd + kdata, sm, sm + fs);
     } else {
-      uint8_t* sl = stage[wave] + q * a.slot_bytes;
+      uint8_t* sl = stage[gi] + q * a.slot_bytes;
       put(sl, sl + kps, sl + kdata, sl + kps + vdata);
     }
     __syncthreads();
-    // every row of the wave has the same token, activity and slot mapping
+    // every row of the group has the same token, activity and slot mapping
     if (write) {
       if (a.soa) {
-        uint8_t* dd = drow - q * kDb;            // data row of the wave's first head
+        uint8_t* dd = drow - q * kDb;            // data row of the group's first head
         uint8_t* dm = mrec - q * (2 * kNf);      // its record
-        constexpr int kDc = kRowsPerWave * kDb / 16, kMc = kRowsPerWave * 2 * kNf / 16;
-        for (int c = lane; c < kDc + kMc; c += 64) {
+        constexpr int kDc = kStageRows * kDb / 16, kMc = kStageRows * 2 * kNf / 16;
+        for (int c = gt; c < kDc + kMc; c += kGt) {
           uint8_t* dst = c < kDc ? dd + 16 * c : dm + 16 * (c - kDc);
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stage[gi] + 16 * c);
         }
       } else {
-        uint8_t* dst = slot - q * static_cast<int64_t>(a.slot_bytes);  // slot of the wave's first head
-        const int nchunk = (kRowsPerWave * a.slot_bytes) >> 4;
-        for (int c = lane; c < nchunk; c += 64)
-          *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stage[wave] + 16 * c);
+        uint8_t* dst = slot - q * static_cast<int64_t>(a.slot_bytes);  // slot of the group's first head
+        const int nchunk = (kStageRows * a.slot_bytes) >> 4;
+        for (int c = gt; c < nchunk; c += kGt)
+          *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stage[gi] + 16 * c);
       }
     }
   } else if (write) {
@@ -370,27 +377,28 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   }
 }
 
-template <int KEY_FP8, int KB, int VB, int NC, int VLM = 0>
+template <int D, int KEY_FP8, int KB, int VB, int NC, int VLM = 0>
 int launch_store(const StoreArgs& a, bool bf16, hipStream_t stream) {
-  const int blocks = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int blocks = (a.num_rows + rows_per_block<D>() - 1) / rows_per_block<D>();
   StoreArgs arg = a;
   void* args[] = {&arg};
-  const void* fn = bf16 ? reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, VLM, 1>)
-                        : reinterpret_cast<const void*>(&tq_store_kernel<KEY_FP8, KB, VB, NC, VLM, 0>);
+  const void* fn = bf16 ? reinterpret_cast<const void*>(&tq_store_kernel<D, KEY_FP8, KB, VB, NC, VLM, 1>)
+                        : reinterpret_cast<const void*>(&tq_store_kernel<D, KEY_FP8, KB, VB, NC, VLM, 0>);
   return tq::hip_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0, stream));
 }
 
+template <int D>
 int launch_preset(int32_t preset, const StoreArgs& a, bool bf16, hipStream_t s) {
   switch (preset) {
-    case TQ_K8V4: return launch_store<1, 8, 4, 0>(a, bf16, s);
-    case TQ_4BIT_NC: return launch_store<0, 4, 4, 1>(a, bf16, s);
-    case TQ_K3V4_NC: return launch_store<0, 3, 4, 1>(a, bf16, s);
-    case TQ_3BIT_NC: return launch_store<0, 3, 3, 1>(a, bf16, s);
-    case TQ_K8V3: return launch_store<1, 8, 3, 0>(a, bf16, s);
-    case TQ_K4V3_NC: return launch_store<0, 4, 3, 1>(a, bf16, s);
-    case TQ_2BIT_NC: return launch_store<0, 2, 2, 1>(a, bf16, s);
-    case TQ_K8V3LM: return launch_store<1, 8, 3, 0, 1>(a, bf16, s);
-    case TQ_3BIT_LM: return launch_store<0, 3, 3, 1, 1>(a, bf16, s);
+    case TQ_K8V4: return launch_store<D, 1, 8, 4, 0>(a, bf16, s);
+    case TQ_4BIT_NC: return launch_store<D, 0, 4, 4, 1>(a, bf16, s);
+    case TQ_K3V4_NC: return launch_store<D, 0, 3, 4, 1>(a, bf16, s);
+    case TQ_3BIT_NC: return launch_store<D, 0, 3, 3, 1>(a, bf16, s);
+    case TQ_K8V3: return launch_store<D, 1, 8, 3, 0>(a, bf16, s);
+    case TQ_K4V3_NC: return launch_store<D, 0, 4, 3, 1>(a, bf16, s);
+    case TQ_2BIT_NC: return launch_store<D, 0, 2, 2, 1>(a, bf16, s);
+    case TQ_K8V3LM: return launch_store<D, 1, 8, 3, 0, 1>(a, bf16, s);
+    case TQ_3BIT_LM: return launch_store<D, 0, 3, 3, 1, 1>(a, bf16, s);
   }
   return TQ_EPRESET;
 }
@@ -425,7 +433,8 @@ extern "C" int tq_store(const tq_layout* layout, const void* key, const void* va
     a.value = static_cast<const uint16_t*>(value) + t0 * val_tok_stride;
     a.slot_mapping = slot_mapping + t0;
     a.num_rows = static_cast<int32_t>(nt * num_kv_heads);
-    st = launch_preset(layout->preset, a, bf16, s);
+    st = layout->head_dim == 256 ? launch_preset<256>(layout->preset, a, bf16, s)
+                                 : launch_preset<128>(layout->preset, a, bf16, s);
     if (st != TQ_OK) return st;
   }
   return TQ_OK;

@@ -40,7 +40,7 @@ def dev16(bits: np.ndarray, dtype: str):
 def oracle_tables(lay):
     if lay.key_fp8:
         return None, None
-    return O.codebook_tables(D, lay.key_bits)
+    return O.codebook_tables(lay.head_dim, lay.key_bits)
 
 
 def gpu_tables(lay_c, signs):
@@ -52,15 +52,16 @@ def gpu_tables(lay_c, signs):
 # ------------------------------------------------------------------ store
 
 
-def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc):
+def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0):
     """got/want: (rows, code bytes + 2) = packed Lloyd-Max codes then the
     fp16 norm of the same rows; rows: (rows, D) float64 inputs.  A code may
     differ only next to a bucket boundary (|u - b| < 1e-6, by one), at most
-    1e-5 of the codes; the norm within 1e-3, re-derived from the GPU's codes
-    where they differ.  Returns the number of differing codes."""
+    1e-5 of the codes (or min_allowed of them, for samples too small for that
+    rate); the norm within 1e-3, re-derived from the GPU's codes where they
+    differ.  Returns the number of differing codes."""
     nb = got.shape[1] - 2
-    cg = O.unpack_lsb(got[:, :nb], bits, D)
-    cw = O.unpack_lsb(want[:, :nb], bits, D)
+    cg = O.unpack_lsb(got[:, :nb], bits, lay.head_dim)
+    cw = O.unpack_lsb(want[:, :nb], bits, lay.head_dim)
     bad = np.argwhere(cg != cw)
     if len(bad):
         U = O.key_units(lay, rows[np.unique(bad[:, 0])], R)
@@ -69,7 +70,7 @@ def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc):
         dist = np.min(np.abs(u[:, None] - np.asarray(bound, np.float64)[None, :]), axis=1)
         assert np.all(dist < BOUNDARY_EPS), f"code mismatch away from a boundary: {dist.max()}"
         assert np.all(np.abs(cg[bad[:, 0], bad[:, 1]] - cw[bad[:, 0], bad[:, 1]]) == 1)
-    assert len(bad) <= MISMATCH_FRAC * cg.size, f"{len(bad)} code mismatches of {cg.size}"
+    assert len(bad) <= max(MISMATCH_FRAC * cg.size, min_allowed), f"{len(bad)} code mismatches of {cg.size}"
     gg = got[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     gw = want[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     for r in np.unique(bad[:, 0]) if len(bad) else []:
@@ -80,7 +81,7 @@ def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc):
     return len(bad)
 
 
-def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32, values=None):
+def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32, values=None, min_allowed=0):
     """got/want: (rows, slot) bytes of the same rows; keys / values: (rows, D)
     float64 inputs of those rows.  Lloyd-Max codes (MSE keys, Lloyd-Max
     values) follow _compare_codes; FP8 keys, uniform value codes, scale, zero
@@ -93,12 +94,12 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32,
         np.testing.assert_array_equal(got[:, :kd], want[:, :kd])
     else:
         n += _compare_codes(lay, lay.key_bits, got[:, : kd + 2], want[:, : kd + 2], keys, R, c32, b32,
-                            lay.norm_correction)
+                            lay.norm_correction, min_allowed)
     if lay.value_lm:
         assert values is not None, "Lloyd-Max values need the value inputs"
         vc32, vb32 = O.value_tables(lay)
         n += _compare_codes(lay, lay.value_bits, got[:, vo : vo + vd + 2], want[:, vo : vo + vd + 2], values, R,
-                            vc32, vb32, True)
+                            vc32, vb32, True, min_allowed)
         np.testing.assert_array_equal(got[:, vo + vd + 2 :], want[:, vo + vd + 2 :])
     else:
         np.testing.assert_array_equal(got[:, vo:], want[:, vo:])
@@ -118,9 +119,10 @@ class DecodeCase:
         import quantized_decode_attention_tq_amd as tq
 
         self.w = w
+        self.D = w.head_dim
         self.soa = block_layout == "soa"
-        self.lay = O.layout(w.preset, D)
-        self.lay_c = tq.layout_init(w.preset, D, block_layout)
+        self.lay = O.layout(w.preset, self.D)
+        self.lay_c = tq.layout_init(w.preset, self.D, block_layout)
         self.lens = W.seq_lens(w)
         self.table = W.block_table(w)
         self.nb = W.num_blocks(w)
@@ -140,7 +142,7 @@ class DecodeCase:
         self.q = dev16(self.qbits, w.dtype)
         self.bt = t.from_numpy(self.table).cuda()
         self.sl = t.from_numpy(self.lens).cuda()
-        self.scale = 1.0 / math.sqrt(D)
+        self.scale = 1.0 / math.sqrt(self.D)
 
     def oracle_cache_bytes(self):
         """The oracle's cache in this case's block convention."""
@@ -181,15 +183,15 @@ class DecodeCase:
 
         t = torch()
         B, Hq = self.q.shape[:2]
-        ws = t.empty(tq.decode_workspace_bytes(B, Hq, 128, num_kv_splits), dtype=t.uint8, device="cuda")
+        ws = t.empty(tq.decode_workspace_bytes(B, Hq, self.D, num_kv_splits), dtype=t.uint8, device="cuda")
         if workspace_fill is not None:
             ws.fill_(workspace_fill)
         tq.decode_stage1(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids, self.scale,
                          num_kv_splits, ws, sliding_window=sliding_window)
-        out = t.empty((B, Hq, 128), dtype=t.float32, device="cuda")
+        out = t.empty((B, Hq, self.D), dtype=t.float32, device="cuda")
         lse = t.empty((B, Hq), dtype=t.float32, device="cuda")
         sk = None if sinks is None else t.from_numpy(np.asarray(sinks, np.float32)).cuda()
-        tq.decode_stage2(B, Hq, 128, num_kv_splits, ws, out, lse, sinks=sk)
+        tq.decode_stage2(B, Hq, self.D, num_kv_splits, ws, out, lse, sinks=sk)
         t.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

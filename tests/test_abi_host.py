@@ -45,7 +45,7 @@ def test_layout_matches_oracle(preset, D):
 
 
 @pytest.mark.parametrize("preset", O.PRESETS)
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_soa_layout_matches_oracle(preset, D):
     """The SoA layout keeps every slot field of the combined one and adds the
     oracle's SoA geometry (data bytes per row, metadata fields per row)."""
@@ -161,6 +161,8 @@ def test_store_validation_codes():
     assert _store_validate(L, N=-1) == tq.TQ_EINVAL
     assert _store_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None, bnd=None) == tq.TQ_OK
     assert _store_validate(tq.layout_init("turboquant_3bit_nc", 64)) == tq.TQ_EHEADDIM
+    assert _store_validate(tq.layout_init("turboquant_3bit_nc", 256), ks=2048, vs=2048) == tq.TQ_OK
+    assert _store_validate(tq.layout_init("turboquant_3bit_nc", 256)) == tq.TQ_EINVAL  # stride below Hk * 256
     bad = tq.layout_init("turboquant_3bit_nc")
     bad.slot_size_aligned = 104  # layout not produced by tq_layout_init
     assert _store_validate(bad) == tq.TQ_EINVAL
@@ -230,4 +232,5 @@ def test_dequant_validation_codes():
     assert _dequant_validate(L, signs=None) == tq.TQ_EINVAL
     assert _dequant_validate(tq.layout_init("turboquant_k8v4"), signs=None, cent=None) == tq.TQ_OK
     assert _dequant_validate(tq.layout_init("turboquant_k3v4_nc", 64)) == tq.TQ_EHEADDIM
+    assert _dequant_validate(tq.layout_init("turboquant_k3v4_nc", 256), stride=2048) == tq.TQ_OK
     assert _dequant_validate(L, n=1 << 28, nb=1 << 30) == tq.TQ_EINVAL  # rows beyond 2^31

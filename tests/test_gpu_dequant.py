@@ -28,12 +28,12 @@ def _torch_dtype(name):
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[name]
 
 
-def _cache(preset, n, Hk, bs, seed, dtype="bf16"):
+def _cache(preset, n, Hk, bs, seed, dtype="bf16", D=D):
     """Oracle-written cache of one sequence of n tokens in a shuffled pool."""
     rng = np.random.default_rng(seed)
     lay = O.layout(preset, D)
     c32, b32 = G.oracle_tables(lay)
-    s = W.signs(seed)
+    s = W.signs(seed, D)
     nbl = -(-n // bs)
     nb = nbl + 3
     table = rng.permutation(nb)[:nbl].astype(np.int32)
@@ -47,11 +47,14 @@ def _cache(preset, n, Hk, bs, seed, dtype="bf16"):
     return lay, cache, table, s, c32
 
 
-def _gpu(preset, cache, table, n, s, out, stride_tokens=None, sentinel=None):
+def _gpu(preset, cache, table, n, s, out, stride_tokens=None, sentinel=None, D=D, block_layout="aos"):
+    """cache: combined slots (converted to the SoA convention for block_layout "soa")."""
     import torch
     import quantized_decode_attention_tq_amd as tq
 
-    lay_c = tq.layout_init(preset)
+    lay_c = tq.layout_init(preset, D, block_layout)
+    if block_layout == "soa":
+        cache = O.soa_from_aos(O.layout(preset, D), cache)
     Hk = cache.shape[2]
     tab = G.gpu_tables(lay_c, s)
     dt = _torch_dtype(out)

@@ -13,18 +13,19 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _run_store(preset, N, Hk, bs, dtype, seed, skip_every=0, sentinel=0xA5):
+def _run_store(preset, N, Hk, bs, dtype, seed, skip_every=0, sentinel=0xA5, head_dim=128, block_layout="aos"):
     import torch
     import quantized_decode_attention_tq_amd as tq
 
-    G.log(f"store preset={preset} N={N} Hk={Hk} bs={bs} dtype={dtype} seed={seed}")
-    K, V, slots, nb = W.store_inputs(num_tokens=N, num_kv_heads=Hk, block_size=bs, seed=seed, dtype=dtype)
+    G.log(f"store preset={preset} N={N} Hk={Hk} bs={bs} dtype={dtype} seed={seed} D={head_dim} {block_layout}")
+    K, V, slots, nb = W.store_inputs(num_tokens=N, num_kv_heads=Hk, block_size=bs, seed=seed, dtype=dtype,
+                                     head_dim=head_dim)
     nb += 2  # spare blocks stay untouched
     if skip_every:
         slots[::skip_every] = -1
-    lay = O.layout(preset, G.D)
-    lay_c = tq.layout_init(preset)
-    signs = W.signs(seed)
+    lay = O.layout(preset, head_dim)
+    lay_c = tq.layout_init(preset, head_dim, block_layout)
+    signs = W.signs(seed, head_dim)
     c32, b32 = G.oracle_tables(lay)
     tab = G.gpu_tables(lay_c, signs)
     shape = (nb, bs, Hk, lay.slot_size_aligned)
@@ -36,11 +37,10 @@ def _run_store(preset, N, Hk, bs, dtype, seed, skip_every=0, sentinel=0xA5):
     return lay, K, V, slots, got, signs, c32, b32, shape, sentinel
 
 
-@pytest.mark.parametrize("preset", O.PRESETS)
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_store_parity_small(preset, dtype):
-    lay, K, V, slots, got, signs, c32, b32, shape, sentinel = _run_store(preset, 1237, 3, 16, dtype, 11,
-                                                                         skip_every=13)
+def check_store_parity(preset, dtype, N, Hk, bs, seed, skip_every, head_dim=128):
+    """Store N tokens on the GPU and compare every slot with the oracle's."""
+    lay, K, V, slots, got, signs, c32, b32, shape, sentinel = _run_store(preset, N, Hk, bs, dtype, seed,
+                                                                         skip_every=skip_every, head_dim=head_dim)
     want = np.full(shape, sentinel, np.uint8)
     O.store_rows(lay, O.widen(K, dtype), O.widen(V, dtype), slots, want, signs, c32, b32)
     # untouched slots: identical sentinel bytes
@@ -52,8 +52,14 @@ def test_store_parity_small(preset, dtype):
     N, Hk = K.shape[:2]
     rows_got = got[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
     rows_want = want[slots[keep] // shape[1], slots[keep] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rows_got, rows_want, O.widen(K[keep], dtype).reshape(-1, G.D), signs, c32, b32,
-                    O.widen(V[keep], dtype).reshape(-1, G.D))
+    G.compare_slots(lay, rows_got, rows_want, O.widen(K[keep], dtype).reshape(-1, lay.head_dim), signs, c32, b32,
+                    O.widen(V[keep], dtype).reshape(-1, lay.head_dim))
+
+
+@pytest.mark.parametrize("preset", O.PRESETS)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_store_parity_small(preset, dtype):
+    check_store_parity(preset, dtype, 1237, 3, 16, 11, 13)
 
 
 @pytest.mark.parametrize("preset", O.PRESETS)

@@ -25,12 +25,12 @@ def _fails(pin, *args):
 def test_transposed_rotation_is_caught(monkeypatch):
     real = T.rotation
     _patch(monkeypatch, "rotation", lambda s: real(s).T)
-    _fails(P.test_rotation_properties)
+    _fails(P.test_rotation_properties, 128)
 
 
 def test_signs_on_wrong_side_are_caught(monkeypatch):
     _patch(monkeypatch, "rotation", lambda s: T.hadamard(s.shape[0]) * s[:, None] / math.sqrt(s.shape[0]))
-    _fails(P.test_rotation_properties)
+    _fails(P.test_rotation_properties, 128)
 
 
 def test_unrotated_query_is_caught(monkeypatch):
@@ -51,7 +51,7 @@ def test_unrotated_query_is_caught(monkeypatch):
 def test_dropped_norm_correction_is_caught(monkeypatch):
     real = T.quantize_key_mse
     _patch(monkeypatch, "quantize_key_mse", lambda x, R, c, b, nc: real(x, R, c, b, False))
-    _fails(P.test_mse_key_reconstruction_statistics, 3, 0.03455)
+    _fails(P.test_mse_key_reconstruction_statistics, 3, 0.03455, 128)
 
 
 def test_inclusive_bucketize_is_caught(monkeypatch):
@@ -180,4 +180,4 @@ def test_lloyd_max_values_left_rotated_are_caught(monkeypatch):
         return K, (V @ R.T) if lay.value_lm else V
 
     _patch(monkeypatch, "decode_slots", bad)
-    _fails(P.test_dequant_original_space_error_matches_lloyd_max_distortion, "turboquant_3bit_lm")
+    _fails(P.test_dequant_original_space_error_matches_lloyd_max_distortion, "turboquant_3bit_lm", 128)

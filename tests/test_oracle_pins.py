@@ -61,22 +61,23 @@ def _fwht(x):
     return y
 
 
-def test_rotation_properties():
+@pytest.mark.parametrize("d", [128, 256])
+def test_rotation_properties(d):
     rng = np.random.default_rng(1)
-    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    s = np.where(rng.integers(0, 2, d) == 1, -1.0, 1.0)
     R = O.rotation(s)
-    np.testing.assert_allclose(R @ R.T, np.eye(D), atol=1e-12)
-    x = rng.standard_normal(D)
+    np.testing.assert_allclose(R @ R.T, np.eye(d), atol=1e-12)
+    x = rng.standard_normal(d)
     np.testing.assert_allclose(R.T @ (R @ x), x, atol=1e-12)
-    # signs first, then the WHT: R x = FWHT(s * x) / sqrt(D)
-    np.testing.assert_allclose(R @ x, _fwht(s * x) / math.sqrt(D), atol=1e-12)
-    H = O.hadamard(D)
-    np.testing.assert_array_equal(H @ H, D * np.eye(D))
+    # signs first, then the WHT: R x = FWHT(s * x) / sqrt(d)
+    np.testing.assert_allclose(R @ x, _fwht(s * x) / math.sqrt(d), atol=1e-12)
+    H = O.hadamard(d)
+    np.testing.assert_array_equal(H @ H, d * np.eye(d))
     assert np.all(H[:, 0] == 1.0)
     # all-+1 signs reduce to the plain (unsigned, symmetric) Hadamard rotation
-    np.testing.assert_allclose(O.rotation(np.ones(D)), scipy.linalg.hadamard(D) / math.sqrt(D), atol=0)
+    np.testing.assert_allclose(O.rotation(np.ones(d)), scipy.linalg.hadamard(d) / math.sqrt(d), atol=0)
     # the signs act on the input side (columns), not the output side
-    assert not np.allclose(R, (H * s[:, None]) / math.sqrt(D))
+    assert not np.allclose(R, (H * s[:, None]) / math.sqrt(d))
 
 
 # ---------------------------------------------------------------- Lloyd-Max
@@ -290,16 +291,17 @@ def test_bucketize_ties_and_ends():
 
 
 @pytest.mark.parametrize("bits,distortion", [(2, 0.1175), (3, 0.03455), (4, 0.009497)])
-def test_mse_key_reconstruction_statistics(bits, distortion):
+@pytest.mark.parametrize("d", [128, 256])
+def test_mse_key_reconstruction_statistics(bits, distortion, d):
     """Gaussian keys: relative squared error of gamma R^T c[code] is close to
     the Lloyd-Max distortion, and the norm correction matches norms."""
     rng = np.random.default_rng(bits)
-    c32, b32 = O.codebook_tables(D, bits)
-    s = np.where(rng.integers(0, 2, D) == 1, -1.0, 1.0)
+    c32, b32 = O.codebook_tables(d, bits)
+    s = np.where(rng.integers(0, 2, d) == 1, -1.0, 1.0)
     R = O.rotation(s)
     errs = []
     for _ in range(300):
-        x = rng.standard_normal(D) * rng.uniform(0.1, 10)
+        x = rng.standard_normal(d) * rng.uniform(0.1, 10)
         codes, gamma = O.quantize_key_mse(x, R, c32, b32, True)
         chat = c32[codes].astype(np.float64)
         xr = gamma * (R.T @ chat)
@@ -310,7 +312,7 @@ def test_mse_key_reconstruction_statistics(bits, distortion):
     # E||c[code]||^2 ~ 1 - distortion for unit-norm inputs (no correction)
     norms = []
     for _ in range(300):
-        x = rng.standard_normal(D)
+        x = rng.standard_normal(d)
         codes, _ = O.quantize_key_mse(x, R, c32, b32, False)
         norms.append(np.sum(c32[codes].astype(np.float64) ** 2))
     assert abs(np.mean(norms) - (1 - distortion)) < 0.25 * distortion
@@ -559,7 +561,8 @@ MAX_GAUSSIAN_DISTORTION = {2: 0.1175, 3: 0.03454, 4: 0.009497}
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc",
                                     "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_3bit_lm",
                                     "turboquant_k8v3lm"])
-def test_dequant_original_space_error_matches_lloyd_max_distortion(preset):
+@pytest.mark.parametrize("d", [128, 256])
+def test_dequant_original_space_error_matches_lloyd_max_distortion(preset, d):
     """Store then dequantize back to the original space: after the randomized
     Hadamard rotation the coordinates are near-Gaussian ([TQ+] "Background":
     why the sign vector matters), so the relative key error averages out at
@@ -568,13 +571,13 @@ def test_dequant_original_space_error_matches_lloyd_max_distortion(preset):
     Values: the uniform quantizer's error bound (half a step plus the zero
     point's fp16 rounding)."""
     rng = np.random.default_rng(5)
-    lay = O.layout(preset, D)
-    c32, b32 = O.codebook_tables(D, lay.key_bits)
-    s = O.wht_signs(D, 3)
+    lay = O.layout(preset, d)
+    c32, b32 = O.codebook_tables(d, lay.key_bits)
+    s = O.wht_signs(d, 3)
     N, bs = 400, 16
-    K = O.widen(W.to_bits(rng.standard_normal((N, 1, D)) * np.exp(0.3 * rng.standard_normal((1, 1, D))), "bf16"),
+    K = O.widen(W.to_bits(rng.standard_normal((N, 1, d)) * np.exp(0.3 * rng.standard_normal((1, 1, d))), "bf16"),
                 "bf16")
-    V = O.widen(W.to_bits(rng.standard_normal((N, 1, D)), "bf16"), "bf16")
+    V = O.widen(W.to_bits(rng.standard_normal((N, 1, d)), "bf16"), "bf16")
     cache = np.zeros((N // bs, bs, 1, lay.slot_size_aligned), np.uint8)
     O.store_rows(lay, K, V, np.arange(N), cache, s, c32, b32)
     Kd, Vd = O.dequant_original_space(lay, cache, np.arange(N // bs), N, 0, s, c32)

@@ -150,8 +150,12 @@ def block_table(w: Workload) -> np.ndarray:
 
 
 def signs(w_or_seed, d: int = HEAD_DIM) -> np.ndarray:
-    """Rademacher +-1 signs for the rotation, float32 (D,)."""
-    seed = w_or_seed.seed if isinstance(w_or_seed, Workload) else int(w_or_seed)
+    """Rademacher +-1 signs for the rotation, float32 (D,): D = the workload's
+    head_dim, or d for a plain seed."""
+    if isinstance(w_or_seed, Workload):
+        seed, d = w_or_seed.seed, w_or_seed.head_dim
+    else:
+        seed = int(w_or_seed)
     return np.where(_rng(seed, 13).integers(0, 2, size=d) == 1, -1.0, 1.0).astype(np.float32)
 
 
