@@ -68,6 +68,8 @@ def warm_gpu(torch, fn, ms=150.0):
 
 
 MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
+# head_dim 256 leg: the headline preset, FP8 keys with Lloyd-Max values (the pages' fp8k_turbo3v), 3-bit MSE
+HEAD256_PRESETS = ("turboquant_k8v4", "turboquant_k8v3lm", "turboquant_3bit_nc")
 
 
 class DecodeBench:
@@ -79,7 +81,8 @@ class DecodeBench:
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
         self.window = sliding_window
-        self.lay = tq.layout_init(w.preset, 128, block_layout)
+        D = w.head_dim
+        self.lay = tq.layout_init(w.preset, D, block_layout)
         self.lens = W.seq_lens(w)
         table = W.block_table(w)
         self.table_np = table
@@ -111,11 +114,11 @@ class DecodeBench:
         self.q = dev16(torch, W.queries(w), w.dtype)
         self.bt = torch.from_numpy(table).cuda()
         self.sl = torch.from_numpy(self.lens).cuda()
-        self.ws = torch.empty(tq.decode_workspace_bytes(w.batch, w.num_q_heads, 128, self.S), dtype=torch.uint8,
+        self.ws = torch.empty(tq.decode_workspace_bytes(w.batch, w.num_q_heads, D, self.S), dtype=torch.uint8,
                               device="cuda")
-        self.out = torch.empty((w.batch, w.num_q_heads, 128), dtype=self.q.dtype, device="cuda")
+        self.out = torch.empty((w.batch, w.num_q_heads, D), dtype=self.q.dtype, device="cuda")
         self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
-        self.scale = 1.0 / math.sqrt(128)
+        self.scale = 1.0 / math.sqrt(D)
         seen = np.minimum(self.lens, sliding_window) if sliding_window > 0 else self.lens
         self.bytes_read = int(seen.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
         self.sinks = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
@@ -132,7 +135,7 @@ class DecodeBench:
                               self.scale, self.S, self.ws, sliding_window=self.window)
 
     def stage2(self):
-        self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, 128, self.S, self.ws, self.out, self.lse,
+        self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, self.w.head_dim, self.S, self.ws, self.out, self.lse,
                               sinks=self.sinks)
 
     def step(self, i):
@@ -219,16 +222,16 @@ class DecodeBench:
         return a.elapsed_time(b) / launches
 
 
-def store_sweep(torch, tq, steps, block_layout="aos", presets=None):
+def store_sweep(torch, tq, steps, block_layout="aos", presets=None, head_dim=128):
     """Store sweep: 65536 tokens x 8 KV heads, bs 32, per preset (Mtok/s)."""
     s = W.STORE_WORKLOAD
-    K, V, slots, nb = W.store_inputs()
+    K, V, slots, nb = W.store_inputs(head_dim=head_dim)
     kd, vd = dev16(torch, K, s["dtype"]), dev16(torch, V, s["dtype"])
     sd = torch.from_numpy(slots).cuda()
     res = {}
     for preset in presets or s["presets"]:
-        lay = tq.layout_init(preset, 128, block_layout)
-        tab = tq.Tables(lay, W.signs(s["seed"]))
+        lay = tq.layout_init(preset, head_dim, block_layout)
+        tab = tq.Tables(lay, W.signs(s["seed"], head_dim))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, s["block_size"], s["num_kv_heads"]), dtype=torch.uint8,
                               device="cuda") for _ in range(N_COPIES)]
         for c in caches:
@@ -242,7 +245,7 @@ def store_sweep(torch, tq, steps, block_layout="aos", presets=None):
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
         n = s["num_tokens"]
-        bytes_moved = n * s["num_kv_heads"] * (2 * 128 * 2 + lay.slot_size_aligned) + n * 8
+        bytes_moved = n * s["num_kv_heads"] * (2 * head_dim * 2 + lay.slot_size_aligned) + n * 8
         res[preset] = {"mtok_s": n / (ms * 1e-3) / 1e6, "ms": ms, "gbs": bytes_moved / (ms * 1e-3) / 1e9,
                        "frac_hbm": bytes_moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del caches
@@ -335,25 +338,26 @@ def calibrate_copy(torch, mib: int = 512, reps: int = 5):
 DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS = 131072, 8, 128
 
 
-def dequant_sweep(torch, tq, reps, block_layout="aos", presets=None):
+def dequant_sweep(torch, tq, reps, block_layout="aos", presets=None, head_dim=128):
     """Cached prefix back to dense fp16 K/V (tq_dequant_kv): one sequence of
     131072 tokens x 8 KV heads in 128-token blocks (the long-context shape),
-    per preset.  Bytes = slots read + 2 x 128 fp16 written per (token, head);
+    per preset.  Bytes = slots read + 2 x head_dim fp16 written per (token, head);
     3 cache copies rotate so no launch finds its input in the 256 MB MALL."""
     n, Hk, bs = DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS
     nb = n // bs
     g = torch.Generator(device="cuda").manual_seed(21)
-    K = torch.randn((n, Hk, 128), device="cuda", generator=g).to(torch.bfloat16)
-    V = torch.randn((n, Hk, 128), device="cuda", generator=g).to(torch.bfloat16)
+    D = head_dim
+    K = torch.randn((n, Hk, D), device="cuda", generator=g).to(torch.bfloat16)
+    V = torch.randn((n, Hk, D), device="cuda", generator=g).to(torch.bfloat16)
     perm = torch.randperm(nb, generator=torch.Generator().manual_seed(22)).to(torch.int32)
     table = perm.cuda()
     slots = (perm.to(torch.int64).repeat_interleave(bs) * bs + torch.arange(bs).repeat(nb)).cuda()
-    ko = torch.empty((n, Hk, 128), dtype=torch.float16, device="cuda")
+    ko = torch.empty((n, Hk, D), dtype=torch.float16, device="cuda")
     vo = torch.empty_like(ko)
     res = {}
     for preset in presets or ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
-        lay = tq.layout_init(preset, 128, block_layout)
-        tab = tq.Tables(lay, W.signs(21))
+        lay = tq.layout_init(preset, D, block_layout)
+        tab = tq.Tables(lay, W.signs(21, D))
         caches = [torch.zeros(tq.kv_cache_shape(lay, nb, bs, Hk), dtype=torch.uint8, device="cuda")
                   for _ in range(N_COPIES)]
         for c in caches:
@@ -369,7 +373,7 @@ def dequant_sweep(torch, tq, reps, block_layout="aos", presets=None):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        nbytes = n * Hk * (lay.slot_size_aligned + 2 * 128 * 2)
+        nbytes = n * Hk * (lay.slot_size_aligned + 2 * D * 2)
         res[preset] = {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
                        "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
                        "mtok_s": n / (ms * 1e-3) / 1e6}
@@ -472,6 +476,26 @@ def main():
         log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items()})}; "
             f"[more dequant] {json.dumps({k: round(v['gbs']) for k, v in more['dequant'].items()})} GB/s")
         extra["more_presets"] = more
+        # head_dim 256: decode on the hd256 shape, store and dequant sweeps
+        h256 = {}
+        for preset in HEAD256_PRESETS:
+            wk = W.scaled(W.WORKLOADS["hd256"], name=f"hd256/{preset}", preset=preset)
+            b = DecodeBench(torch, tq, wk, args.splits)
+            s1 = b.time_stage1(30)
+            d = b.time_decode(30)
+            h256[preset] = {"workload": "hd256: 64 seqs x 4096 tokens, 16/2 heads, head_dim 256, block 16",
+                            "ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
+                            "decode_frac_hbm": b.bytes_read / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, "stage1_ms": s1,
+                            "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
+            log(f"[hd256 {preset}] decode call {d * 1e3:.1f} us -> {h256[preset]['decode_gbs']:.0f} GB/s; "
+                f"stage1 {s1 * 1e3:.1f} us -> {h256[preset]['stage1_gbs']:.0f} GB/s")
+            del b
+            torch.cuda.empty_cache()
+        h256["store_sweep"] = store_sweep(torch, tq, 50, presets=HEAD256_PRESETS, head_dim=256)
+        h256["dequant"] = dequant_sweep(torch, tq, 20, presets=HEAD256_PRESETS, head_dim=256)
+        log(f"[hd256 store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in h256['store_sweep'].items()})}; "
+            f"[hd256 dequant] {json.dumps({k: round(v['gbs']) for k, v in h256['dequant'].items()})} GB/s")
+        extra["head256"] = h256
         # sliding window + attention sinks: long context with an 8192-token window
         wk = W.WORKLOADS["longctx"]
         b = DecodeBench(torch, tq, wk, 32, sliding_window=8192,

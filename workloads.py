@@ -9,7 +9,7 @@ here, so the two sides always see identical bytes.
 16-bit float inputs are returned as uint16 bit patterns plus a dtype tag
 ("bf16" or "f16").
 
-Workloads (head_dim 128 throughout; synthetic stand-ins for model
+Workloads (head_dim 128 except hd256; synthetic stand-ins for model
 activations, shaped like the models they are named after):
 
   tiny       4bit_nc, 1 seq x 256 tokens, Hq=2/Hk=1, bs=16, fp16 N(0,1) with
@@ -28,6 +28,10 @@ activations, shaped like the models they are named after):
   longctx    k3v4_nc, 4 seqs x 131072 tokens, Hq=40/Hk=8, bs=128, 32 KV
              splits, bf16 N(0,1)*sigma_c with sigma_c log-uniform in
              [0.25, 8]; 4096 blocks, random permutation.
+  hd256      k8v4 at head_dim 256 (the 256-dim heads of the pages' Bench F),
+             64 seqs x 4096 tokens, Hq=16/Hk=2, bs=16, bf16 N(0,1)*sigma_c
+             with sigma_c log-uniform in [0.5, 4]; pool = 2x the blocks
+             needed, random permutation (203 MB of k8v4 cache per step).
 """
 
 from __future__ import annotations
@@ -72,6 +76,8 @@ WORKLOADS = {
                         pool_factor=2.0, chscale_range=(0.5, 4.0)),
     "qwen32b": Workload("qwen32b", "turboquant_3bit_nc", 64, 64, 8, 64, "bf16", "student_t", seed=3,
                         len_range=(1024, 16384), pool_factor=2.0),
+    "hd256": Workload("hd256", "turboquant_k8v4", 64, 16, 2, 16, "bf16", "normal_chscale", seed=6, seq_len=4096,
+                      pool_factor=2.0, chscale_range=(0.5, 4.0), head_dim=256),
     "longctx": Workload("longctx", "turboquant_k3v4_nc", 4, 40, 8, 128, "bf16", "normal_chscale", seed=5,
                         seq_len=131072, num_kv_splits=32, pool_factor=1.0, chscale_range=(0.25, 8.0)),
 }
