@@ -139,3 +139,24 @@ def test_decode_window_sinks_and_split_entry_points_head256(preset):
     out, lse = c.gpu_decode_two_stage(cache, 3, workspace_fill=0x7F)
     ref, rlse = c.oracle_decode()
     G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
+@pytest.mark.parametrize("preset", ["turboquant_k8v4", "turboquant_k8v3lm", "turboquant_3bit_nc"])
+def test_decode_full_size_hd256_sampled(preset):
+    """The hd256 workload at full size (64 x 4096 tokens, 16/2 heads) in the
+    benchmark's launch configuration (8 splits): the GPU stores and decodes
+    everything; the oracle recomputes sampled rows from the raw inputs."""
+    w = W.scaled(W.WORKLOADS["hd256"], preset=preset)
+    rows = [(0, 0), (31, 9), (63, 15)]
+    G.log(f"decode full-size hd256 {preset}: generating inputs")
+    c = G.DecodeCase(w, need_oracle_cache=False)
+    G.log(f"decode full-size hd256 {preset}: store")
+    cache = c.gpu_store_all()
+    G.log(f"decode full-size hd256 {preset}: decode")
+    out, lse = c.gpu_decode(cache, 8)
+    assert np.all(np.isfinite(out))
+    G.log(f"decode full-size hd256 {preset}: oracle rows {rows}")
+    for (b, hq), (ro, rl) in c.oracle_decode_rows_from_inputs(rows).items():
+        err = np.max(np.abs(out[b, hq] - ro)) / np.max(np.abs(ro))
+        assert err <= G.DECODE_RTOL, (b, hq, err)
+        assert abs(lse[b, hq] - rl) <= G.LSE_ATOL * max(1.0, abs(rl))
