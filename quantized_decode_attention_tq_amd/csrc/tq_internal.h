@@ -72,7 +72,7 @@ inline int64_t max_splits(int64_t batch, int64_t num_splits) {
 }
 
 // Launch plan of decode stage 1 (host).  A workgroup serves G KV heads with
-// P waves each (G * P <= 8 waves).  G = Hk when Hk <= 8, so a tile of the
+// P waves each (P <= 2, G * P <= 8 waves).  G = Hk when Hk <= 8, so a tile of the
 // group is one contiguous run of cache rows; otherwise the largest divisor
 // of Hk (<= 8) whose row pieces stay 16-byte aligned.  The P waves of a head
 // split its tiles.  A tile image (16 token rows of the group) takes spt 1 KB
@@ -135,11 +135,12 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
     for (int d = 8; d >= 1 && G == 0; --d)
       if (num_kv_heads % d == 0) G = d;
   }
-  // head_dim 256: at most 2 phase waves per head.  Smaller workgroups and
-  // rings (the 256-dim tile images are twice as large) let more of them
-  // share a CU; on 2 KV heads this cut stage 1 by 22-30% against 4 phases
-  // (1 phase: no better than 4)
-  const int P = G >= 8 ? 1 : (L->head_dim == 256 ? (8 / G < 2 ? 8 / G : 2) : 8 / G);
+  // At most 2 phase waves per head: with few KV heads, smaller workgroups
+  // and rings let more of them share a CU.  Against 8 / G phases, stage 1
+  // on 205 MB of cache took 26-29% less time with 1 KV head (4-8 phases
+  // before), 9% less on 3bit_nc with 2 (k8v4 unchanged), and 22-30% less
+  // at head_dim 256 with 2 KV heads; 1 phase was no better than 4.
+  const int P = G >= 8 ? 1 : (8 / G < 2 ? 8 / G : 2);
   const bool contiguous = G == num_kv_heads;
   const int64_t wg_per_unit = (num_kv_heads / G) * hgroups;
   const int64_t per = static_cast<int64_t>(batch) * num_splits * wg_per_unit;

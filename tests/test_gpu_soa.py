@@ -29,11 +29,11 @@ def _same_plan(lay, Hk):
     rule: a tile image of spt 1 KB LDS slots (combined slots: ceil(G * slot
     / 64), plus a chunk of slack per row piece for groups of 8 of more heads;
     SoA: 16 image rows of G data rows plus a 16-byte pad, then the records,
-    each part rounded up to whole slots); P = 8 / G phase waves; MSE keys take
+    each part rounded up to whole slots); P = min(8 / G, 2) phase waves; MSE keys take
     two tiles per wave when P * spt <= 20; ring depth = 52 // (P * tpw * spt)
     clamped to 2..4."""
     G = min(Hk, 8)
-    P = 8 // G
+    P = 1 if G >= 8 else min(8 // G, 2)
     data, _, nf = O.soa_geometry(lay, 16, G)
     if Hk <= 8:
         spt_a = -(-G * lay.slot_size_aligned // 64)
