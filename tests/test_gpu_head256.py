@@ -10,6 +10,7 @@ import gpu_case as G
 import oracle as O
 import test_gpu_dequant as DQ
 import test_gpu_store as ST
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -54,8 +55,6 @@ def test_dequant_soa_head256_matches_combined_slots(preset):
 
 
 # ------------------------------------------------------------------ decode
-
-import workloads as W  # noqa: E402
 
 
 def _w(preset, lens, Hq, Hk, bs, seed=61):
