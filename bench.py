@@ -68,6 +68,7 @@ def warm_gpu(torch, fn, ms=150.0):
 
 
 MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
+SPARSE_V_GATE = 1e-3
 # head_dim 256 leg: the headline preset, FP8 keys with Lloyd-Max values (the pages' fp8k_turbo3v), 3-bit MSE
 HEAD256_PRESETS = ("turboquant_k8v4", "turboquant_k8v3lm", "turboquant_3bit_nc")
 
@@ -77,10 +78,11 @@ class DecodeBench:
     tokens, queries, tables, workspace."""
 
     def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos",
-                 sliding_window: int = 0, sinks=None):
+                 sliding_window: int = 0, sinks=None, value_gate: float = 0.0):
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
         self.window = sliding_window
+        self.gate = value_gate
         D = w.head_dim
         self.lay = tq.layout_init(w.preset, D, block_layout)
         self.lens = W.seq_lens(w)
@@ -132,7 +134,7 @@ class DecodeBench:
 
     def stage1(self, i):
         self.tq.decode_stage1(self.lay, self.q, self.caches[i], self.bt, self.sl, self.tab.signs, self.tab.centroids,
-                              self.scale, self.S, self.ws, sliding_window=self.window)
+                              self.scale, self.S, self.ws, sliding_window=self.window, value_gate=self.gate)
 
     def stage2(self):
         self.tq.decode_stage2(self.w.batch, self.w.num_q_heads, self.w.head_dim, self.S, self.ws, self.out, self.lse,
@@ -496,6 +498,19 @@ def main():
         log(f"[hd256 store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in h256['store_sweep'].items()})}; "
             f"[hd256 dequant] {json.dumps({k: round(v['gbs']) for k, v in h256['dequant'].items()})} GB/s")
         extra["head256"] = h256
+        # the opt-in sparse-V gate at 1e-3 (the pages' threshold) on the three decode workloads
+        sv = {"value_gate": SPARSE_V_GATE}
+        for name, S in (("llama8b", args.splits), ("longctx", 32), ("qwen32b", args.splits)):
+            b = DecodeBench(torch, tq, W.WORKLOADS[name], S, value_gate=SPARSE_V_GATE)
+            s1 = b.time_stage1(30)
+            d = b.time_decode(30)
+            sv[name] = {"ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
+                        "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9}
+            log(f"[sparse-V {name}] decode call {d * 1e3:.1f} us -> {sv[name]['decode_gbs']:.0f} GB/s; "
+                f"stage1 {s1 * 1e3:.1f} us")
+            del b
+            torch.cuda.empty_cache()
+        extra["sparse_v"] = sv
         # sliding window + attention sinks: long context with an 8192-token window
         wk = W.WORKLOADS["longctx"]
         b = DecodeBench(torch, tq, wk, 32, sliding_window=8192,

@@ -269,6 +269,18 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *                _decode_attention hands it to the decode kernel; the window
  *                reading is this library's.)  Tiles before the window are
  *                neither read nor counted in the work split.
+ *   value_gate   0: exact attention.  In (0, 1): the opt-in sparse-V gate
+ *                ([TQ+] "nvfp4 dec_after_8K cliff explained": rows whose
+ *                softmax factor exp(s - m) falls below the gate contribute
+ *                no value; 1e-3 there).  A token whose factor against the
+ *                work unit's running maximum is below value_gate keeps its
+ *                weight in the softmax denominator (and the lse) but adds no
+ *                value; a pair of 16-token tiles whose tokens are all gated
+ *                skips its value decode and value products.  The running
+ *                maximum never exceeds the final one, so every gated token
+ *                has exp(s - max) < value_gate and the output moves by at
+ *                most sum over such tokens of (normalized weight) * |v|.
+ *                TQ_EINVAL outside [0, 1) or NaN.
  *   sinks        device fp32 [num_q_heads] attention-sink logits, or NULL
  *                ([API] TurboQuantAttentionImpl.__init__ / _decode_attention
  *                pass per-head sinks).  Reading: one more logit in each
@@ -281,21 +293,23 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *                (TQ_F16 | TQ_BF16 | TQ_F32), contiguous.
  *   lse_out      device fp32 [batch, num_q_heads] natural-log LSE, or NULL.
  * Supported: head_dim 128 or 256, block_size 16/32/64/128, num_q_heads a
- * multiple of num_kv_heads, sliding_window >= 0 (TQ_EINVAL otherwise). */
+ * multiple of num_kv_heads, sliding_window >= 0, 0 <= value_gate < 1
+ * (TQ_EINVAL otherwise). */
 int tq_decode_attention(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                         int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                         int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                         const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
-                        int32_t num_kv_splits, int32_t sliding_window, const float* sinks, void* workspace,
-                        size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out, void* stream);
+                        int32_t num_kv_splits, int32_t sliding_window, float value_gate, const float* sinks,
+                        void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
+                        void* stream);
 
 /* Host-only check of tq_decode_attention's arguments. */
 int tq_decode_validate(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                        int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                        int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                        const int32_t* seq_lens, const float* signs, const float* centroids, int32_t num_kv_splits,
-                       int32_t sliding_window, const void* workspace, size_t workspace_bytes, const void* out,
-                       int32_t out_dtype);
+                       int32_t sliding_window, float value_gate, const void* workspace, size_t workspace_bytes,
+                       const void* out, int32_t out_dtype);
 
 /* The two launches of tq_decode_attention, exposed separately so that each
  * can be timed on its own.  Stage 1 writes the workspace table and the
@@ -307,7 +321,8 @@ int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype
                      int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                      const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                      const float* signs, const float* centroids, float scale, int32_t num_kv_splits,
-                     int32_t sliding_window, void* workspace, size_t workspace_bytes, void* stream);
+                     int32_t sliding_window, float value_gate, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                      const float* sinks, const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,

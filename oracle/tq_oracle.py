@@ -789,6 +789,31 @@ def attend(q, K, V, scale: float, sink: float = -math.inf):
     return (p @ V) / l if len(s) else np.zeros(V.shape[1]), m + math.log(l)
 
 
+def attend_sparse_v(q, K, V, scale: float, gate: float, sink: float = -math.inf):
+    """Attention with the sparse-V gate of [TQ+] "nvfp4 dec_after_8K cliff
+    explained": a token whose softmax factor exp(s_t - max) is below the gate
+    adds no value; its weight stays in the denominator (only the value side
+    is skipped), so the lse is the exact one.  Here max is the maximum over
+    all of the query's scores (the sink excluded, as it has no value row).
+    Returns (o, lse, bound): bound[d] = sum over gated tokens of
+    e^{s_t - max} |V[t, d]| / L, L the exact denominator, bounds how far any
+    result that drops only gated tokens' values can be from exact attention
+    in dim d -- in particular one gated against a running maximum, which
+    never exceeds this max, so it drops a subset of these tokens."""
+    o, lse = attend(q, K, V, scale, sink)
+    D = V.shape[1]
+    if K.shape[0] == 0 or lse == -math.inf:
+        return o, lse, np.zeros(D)
+    s = scale * (K @ q)
+    M = s.max()
+    f = np.exp(s - M)
+    L = math.exp(lse - M)  # the exact denominator in units of e^M, sink included
+    drop = f < gate
+    o_gated = (f[~drop] @ V[~drop]) / L
+    bound = (f[drop] @ np.abs(V[drop])) / L
+    return o_gated, lse, bound
+
+
 def window_start(seq_len: int, sliding_window: int) -> int:
     """First token a decode query attends to ([API] TurboQuantAttentionImpl.__init__
     takes ``sliding_window``; _decode_attention passes it to the decode

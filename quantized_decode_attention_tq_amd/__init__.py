@@ -81,11 +81,11 @@ def _load():
         "tq_store": (ctypes.c_int, [L, vp, vp, i32, i64, i32, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp]),
         "tq_store_validate": (ctypes.c_int, [L, vp, vp, i32, i64, i32, i64, i64, vp, vp, i64, i32, vp, vp, vp]),
         "tq_decode_attention": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp, fp, i32,
-                                               i32, vp, vp, sz, vp, i32, vp, vp]),
+                                               i32, fp, vp, vp, sz, vp, i32, vp, vp]),
         "tq_decode_validate": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp, i32, i32,
-                                              vp, sz, vp, i32]),
+                                              fp, vp, sz, vp, i32]),
         "tq_decode_stage1": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp, fp, i32, i32,
-                                            vp, sz, vp]),
+                                            fp, vp, sz, vp]),
         "tq_decode_stage2": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, sz, vp, i32, vp, vp]),
         "tq_dequant_kv": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64, vp]),
         "tq_dequant_validate": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64]),
@@ -220,11 +220,12 @@ def _decode_common(query, kv_cache, block_table):
 
 def decode(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centroids, scale: float,
            num_kv_splits: int, workspace=None, out=None, out_dtype=None, lse=None, stream=None,
-           sliding_window: int = 0, sinks=None):
+           sliding_window: int = 0, sinks=None, value_gate: float = 0.0):
     """Decode attention; returns (out, lse).  query (B, Hq, D) fp16/bf16;
     block_table int32 (B, max_blocks); seq_lens int32 (B,); sinks fp32 (Hq,)
-    or None.  Allocates the workspace, out and lse with torch when they are
-    not given."""
+    or None; value_gate 0 (exact) or the opt-in sparse-V gate in (0, 1).
+    Allocates the workspace, out and lse with torch when they are not
+    given."""
     torch = _torch()
     B, Hq, Hk, bt_stride = _decode_common(query, kv_cache, block_table)
     D = layout.head_dim
@@ -238,7 +239,8 @@ def decode(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centro
     _check(_lib.tq_decode_attention(ctypes.byref(layout), query.data_ptr(), _dt(query), B, Hq, Hk,
                                     kv_cache.data_ptr(), kv_cache.shape[0], kv_cache.shape[1], block_table.data_ptr(),
                                     bt_stride, seq_lens.data_ptr(), _ptr(signs), _ptr(centroids), float(scale),
-                                    num_kv_splits, int(sliding_window), _ptr(sinks), workspace.data_ptr(),
+                                    num_kv_splits, int(sliding_window), float(value_gate), _ptr(sinks),
+                                    workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), out.data_ptr(), _dt(out), _ptr(lse),
                                     _stream(stream, query.device)),
            "tq_decode_attention")
@@ -246,12 +248,13 @@ def decode(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centro
 
 
 def decode_stage1(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centroids, scale: float,
-                  num_kv_splits: int, workspace, stream=None, sliding_window: int = 0) -> None:
+                  num_kv_splits: int, workspace, stream=None, sliding_window: int = 0,
+                  value_gate: float = 0.0) -> None:
     B, Hq, Hk, bt_stride = _decode_common(query, kv_cache, block_table)
     _check(_lib.tq_decode_stage1(ctypes.byref(layout), query.data_ptr(), _dt(query), B, Hq, Hk, kv_cache.data_ptr(),
                                  kv_cache.shape[0], kv_cache.shape[1], block_table.data_ptr(), bt_stride,
                                  seq_lens.data_ptr(), _ptr(signs), _ptr(centroids), float(scale), num_kv_splits,
-                                 int(sliding_window), workspace.data_ptr(),
+                                 int(sliding_window), float(value_gate), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream(stream, query.device)),
            "tq_decode_stage1")
 

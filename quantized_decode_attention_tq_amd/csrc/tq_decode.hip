@@ -553,6 +553,28 @@ struct PendingTile {
   half4 pv;                        // p * value_scale of those tokens, fp16
 };
 
+// The opt-in sparse-V gate (gate > 0, uniform): a token whose factor p =
+// exp(s - m) against the running reference maximum is below the gate keeps
+// p in the softmax sum but adds no value (its value weight ps and its
+// zero-point term drop).  m never exceeds the final maximum, so every gated
+// token also has exp(s - max) < gate.  gated_p: p for the zero-point sum.
+__device__ __forceinline__ void sparse_v_gate(float gate, const float p[4], float ps[4]) {
+  if (gate > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p[i] < gate) ps[i] = 0.f;
+  }
+}
+__device__ __forceinline__ float gated_p(float gate, float p) { return gate > 0.f && p < gate ? 0.f : p; }
+
+// Whether either tile of a pair has a value weight left (false only when the
+// sparse-V gate dropped every token of both: the pair's value work is skipped).
+template <int P>
+__device__ __forceinline__ bool pair_has_values(const PendingTile<P>& x, const PendingTile<P>& y) {
+  const u32x2a4 a = __builtin_bit_cast(u32x2a4, x.pv), b = __builtin_bit_cast(u32x2a4, y.pv);
+  return __any(((a.x | a.y | b.x | b.y) & 0x7FFF7FFFu) != 0u);
+}
+
 // Score one tile and update the online softmax.  valid: tokens of the tile
 // before the sequence end (1..16).  On return `cur` holds the tile's value
 // words and weights; if the running maximum moved, the accumulators and the
@@ -560,8 +582,9 @@ struct PendingTile {
 // per head half; acc: 8 accumulators per head half.
 template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
-                                           const tq::Lut8& lb, const half8* bq, int valid, int skip, Softmax& sm,
-                                           f32x4* acc, PendingTile<P>& pend, bool have_pend, PendingTile<P>& cur) {
+                                           const tq::Lut8& lb, const half8* bq, int valid, int skip, float gate,
+                                           Softmax& sm, f32x4* acc, PendingTile<P>& pend, bool have_pend,
+                                           PendingTile<P>& cur) {
   using T = Preset<P>;
   // two independent accumulation chains halve the dependent-MFMA latency
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -628,10 +651,11 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
+  sparse_v_gate(gate, p, ps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    if (!T::kVlm) sm.z = fma_hi16(p[i], sz[i], sm.z);  // Lloyd-Max values have no zero point
+    if (!T::kVlm) sm.z = fma_hi16(gated_p(gate, p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
@@ -732,7 +756,7 @@ template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
                                                   const half8* bq, int validA, int validB, int skipA, int skipB,
-                                                  Softmax& sm, f32x4* acc) {
+                                                  float gate, Softmax& sm, f32x4* acc) {
   using T = Preset<P>;
   static_assert(T::kNh == 1, "packed pairs: head_dim 128");
   const int lane = threadIdx.x & 63;
@@ -813,10 +837,11 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
+  sparse_v_gate(gate, p, ps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    if (!T::kVlm) sm.z = fma_hi16(p[i], sz[i], sm.z);  // Lloyd-Max values have no zero point
+    if (!T::kVlm) sm.z = fma_hi16(gated_p(gate, p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   // value weights: tile A's from this lane, tile B's from lane c + 8
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
@@ -824,6 +849,8 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   PendingTile<P> ta, tb;
   ta.pv = as_half4(h2_bits(ps01), h2_bits(ps23));
   tb.pv = as_half4(swap8(h2_bits(ps01)), swap8(h2_bits(ps23)));
+  // every token of both tiles gated: no value reads, no value products
+  if (gate > 0.f && !__any(ps[0] != 0.f || ps[1] != 0.f || ps[2] != 0.f || ps[3] != 0.f)) return;
   if constexpr (SOA != 0) {
     load_value_words_soa<P>(imgA, o, ta.vw);
     load_value_words_soa<P>(imgB, o, tb.vw);
@@ -1122,8 +1149,11 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // the phase-0 wave writes the split's partial rows.  head_dim 256 (two
 // halves: twice the accumulators and query operands) runs one tile per wave
 // and keeps 2 waves per SIMD's registers.
-template <int P, int TPW, int PACK, int SOA>
-__global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_kernel(DecodeArgs a) {
+// GATE: the body honours the sparse-V gate vgate (> 0, on exp(s - running
+// max)); the default kernel is built without its code and keeps a single
+// argument, the gated one takes the gate as a second.
+template <int P, int TPW, int PACK, int SOA, int GATE>
+__device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   using T = Preset<P>;
   static_assert(T::kNh == 1 || (TPW == 1 && PACK == 0), "head_dim 256: one tile per wave");
   constexpr int kOut = 32 * T::kNh;  // output dims per lane (32 of each half)
@@ -1384,7 +1414,7 @@ __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_st
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
         score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, bq,
                                   min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
-                                  max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), sm, acc);
+                                  max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), vgate, sm, acc);
       }
     } else {
 #pragma unroll
@@ -1396,10 +1426,10 @@ __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_st
             tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
         load_tile<P, SOA>(img, off, r);
         PendingTile<P> cur;
-        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), sm, acc, pend,
-                           have_pend, cur);
+        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, sm,
+                           acc, pend, have_pend, cur);
         if (have_pend) {
-          accumulate_pair<P>(pend, cur, lv, acc);
+          if (!GATE || pair_has_values(pend, cur)) accumulate_pair<P>(pend, cur, lv, acc);
           have_pend = false;
         } else {
           pend = cur;
@@ -1418,7 +1448,7 @@ __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_st
 #pragma unroll
       for (int i = 0; i < 4; ++i) none.vw[h][i] = 0u;
     none.pv = half4{0, 0, 0, 0};
-    accumulate_pair<P>(pend, none, lv, acc);
+    if (!GATE || pair_has_values(pend, none)) accumulate_pair<P>(pend, none, lv, acc);
   }
 
   // ---- this wave's normalized partial (output / l, base-2 LSE) ----
@@ -1518,6 +1548,17 @@ __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_st
     }
     if (q4 == 0) a.part[prow(hl) * T::kRow + T::kDim] = lse2 * kLn2;
   }
+}
+
+template <int P, int TPW, int PACK, int SOA>
+__global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_kernel(DecodeArgs a) {
+  stage1_body<P, TPW, PACK, SOA, 0>(a, 0.f);
+}
+
+template <int P, int TPW, int PACK, int SOA>
+__global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_gated_kernel(DecodeArgs a,
+                                                                                                   float value_gate) {
+  stage1_body<P, TPW, PACK, SOA, 1>(a, value_gate);
 }
 
 // ---------------------------------------------------------------- stage 2
@@ -1652,50 +1693,58 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int P, int TPW, int PACK, int SOA>
-int launch_stage1_t(const DecodeArgs& a, int64_t nblocks, size_t lds, hipStream_t stream) {
+template <int P, int TPW, int PACK, int SOA, int GATE>
+int launch_stage1_g(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds, hipStream_t stream) {
+  const void* fn = GATE ? reinterpret_cast<const void*>(&tq_decode_stage1_gated_kernel<P, TPW, PACK, SOA>)
+                        : reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>);
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-  });
+  std::call_once(once, [fn] { attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
   if (attr != hipSuccess) return tq::hip_status(attr);
   DecodeArgs arg = a;
-  void* args[] = {&arg};
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>),
+  float g = gate;
+  void* args[] = {&arg, &g};  // the default kernel reads the first only
+  return tq::hip_status(hipLaunchKernel(fn,
                                         dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
                                         stream));
+}
+
+// The sparse-V gate takes its own kernels.
+template <int P, int TPW, int PACK, int SOA>
+int launch_stage1_t(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds, hipStream_t stream) {
+  return gate > 0.f ? launch_stage1_g<P, TPW, PACK, SOA, 1>(a, gate, nblocks, lds, stream)
+                    : launch_stage1_g<P, TPW, PACK, SOA, 0>(a, gate, nblocks, lds, stream);
 }
 
 // Two tiles per wave: GQA groups of at most 8 query heads score them packed
 // into one MFMA block layout; wider groups one at a time.
 template <int P, int SOA>
-int launch_stage1_l(const DecodeArgs& a, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
+int launch_stage1_l(const DecodeArgs& a, float gate, int tpw, int64_t nblocks, size_t lds, hipStream_t stream) {
   if (tpw == 2)
-    return a.group <= 8 ? launch_stage1_t<P, 2, 1, SOA>(a, nblocks, lds, stream)
-                        : launch_stage1_t<P, 2, 0, SOA>(a, nblocks, lds, stream);
-  return launch_stage1_t<P, 1, 0, SOA>(a, nblocks, lds, stream);
+    return a.group <= 8 ? launch_stage1_t<P, 2, 1, SOA>(a, gate, nblocks, lds, stream)
+                        : launch_stage1_t<P, 2, 0, SOA>(a, gate, nblocks, lds, stream);
+  return launch_stage1_t<P, 1, 0, SOA>(a, gate, nblocks, lds, stream);
 }
 
 // head_dim 256 (preset code P | kHead256): one tile per wave (the plan's
 // choice there: two tile images per wave do not fit the ring).
 template <int P>
-int launch_stage1(const DecodeArgs& a, int tpw, bool soa, bool d256, int64_t nblocks, size_t lds,
+int launch_stage1(const DecodeArgs& a, float gate, int tpw, bool soa, bool d256, int64_t nblocks, size_t lds,
                   hipStream_t stream) {
   if (d256) {
     if (tpw != 1) return TQ_EUNSUPPORTED;
-    return soa ? launch_stage1_t<P | kHead256, 1, 0, 1>(a, nblocks, lds, stream)
-               : launch_stage1_t<P | kHead256, 1, 0, 0>(a, nblocks, lds, stream);
+    return soa ? launch_stage1_t<P | kHead256, 1, 0, 1>(a, gate, nblocks, lds, stream)
+               : launch_stage1_t<P | kHead256, 1, 0, 0>(a, gate, nblocks, lds, stream);
   }
-  return soa ? launch_stage1_l<P, 1>(a, tpw, nblocks, lds, stream)
-             : launch_stage1_l<P, 0>(a, tpw, nblocks, lds, stream);
+  return soa ? launch_stage1_l<P, 1>(a, gate, tpw, nblocks, lds, stream)
+             : launch_stage1_l<P, 0>(a, gate, tpw, nblocks, lds, stream);
 }
 
 int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
            int32_t num_kv_heads, const void* kv_cache, int32_t block_size, const int32_t* block_table,
            int32_t block_table_stride, const int32_t* seq_lens, const float* signs, const float* centroids,
-           float scale, int32_t num_kv_splits, int32_t sliding_window, void* workspace, hipStream_t stream) {
+           float scale, int32_t num_kv_splits, int32_t sliding_window, float value_gate, void* workspace,
+           hipStream_t stream) {
   DecodeArgs a;
   a.window = sliding_window;
   a.query = static_cast<const uint16_t*>(query);
@@ -1734,15 +1783,15 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
   const bool soa = layout->block_layout == TQ_LAYOUT_SOA;
   const bool d256 = layout->head_dim == 256;
   switch (layout->preset) {
-    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, plan.tpw, soa, d256, nblocks, lds, stream);
-    case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V4: return launch_stage1<TQ_K8V4>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_4BIT_NC: return launch_stage1<TQ_4BIT_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K3V4_NC: return launch_stage1<TQ_K3V4_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_3BIT_NC: return launch_stage1<TQ_3BIT_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V3: return launch_stage1<TQ_K8V3>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K4V3_NC: return launch_stage1<TQ_K4V3_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }
@@ -1791,14 +1840,16 @@ extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int3
                                 int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                                 int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                                 const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
-                                int32_t num_kv_splits, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                int32_t num_kv_splits, int32_t sliding_window, float value_gate, void* workspace,
+                                size_t workspace_bytes,
                                 void* stream) {
   int st = tq::validate_decode(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                                block_size, block_table, block_table_stride, seq_lens, signs, centroids,
-                               num_kv_splits, sliding_window, workspace, workspace_bytes);
+                               num_kv_splits, sliding_window, value_gate, workspace, workspace_bytes);
   if (st != TQ_OK || batch == 0) return st;
   return stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
-                block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, workspace,
+                block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, value_gate,
+                workspace,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -1817,16 +1868,17 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
                                    int64_t num_blocks, int32_t block_size, const int32_t* block_table,
                                    int32_t block_table_stride, const int32_t* seq_lens, const float* signs,
                                    const float* centroids, float scale, int32_t num_kv_splits,
-                                   int32_t sliding_window, const float* sinks, void* workspace,
+                                   int32_t sliding_window, float value_gate, const float* sinks, void* workspace,
                                    size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
                                    void* stream) {
   int st = tq_decode_validate(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                               block_size, block_table, block_table_stride, seq_lens, signs, centroids, num_kv_splits,
-                              sliding_window, workspace, workspace_bytes, out, out_dtype);
+                              sliding_window, value_gate, workspace, workspace_bytes, out, out_dtype);
   if (st != TQ_OK || batch == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
-              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, workspace, s);
+              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, value_gate,
+              workspace, s);
   if (st != TQ_OK) return st;
   return stage2(batch, num_q_heads, layout->head_dim, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, s);
 }

@@ -321,7 +321,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
                     int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                     const float* signs, const float* centroids, int32_t num_kv_splits, int32_t sliding_window,
-                    const void* workspace, size_t ws_bytes) {
+                    float value_gate, const void* workspace, size_t ws_bytes) {
   if (!layout_consistent(L)) return L && (L->preset < 0 || L->preset >= TQ_NUM_PRESETS) ? TQ_EPRESET : TQ_EINVAL;
   if (batch < 0 || num_blocks < 0 || block_table_stride < 0) return TQ_EINVAL;
   if (!block_size_ok(block_size)) return TQ_EBLOCK;
@@ -329,6 +329,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
   if (q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EDTYPE;
   if (L->head_dim != 128 && L->head_dim != 256) return TQ_EHEADDIM;
   if (num_kv_splits <= 0 || num_kv_splits > 4096 || sliding_window < 0) return TQ_EINVAL;
+  if (!(value_gate >= 0.f && value_gate < 1.f)) return TQ_EINVAL;  // NaN fails too
   if (L->block_layout == TQ_LAYOUT_SOA && num_kv_heads > 8 && num_kv_heads % 8 != 0) return TQ_EUNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!query || !kv_cache || !block_table || !seq_lens || !workspace) return TQ_EINVAL;
@@ -393,11 +394,11 @@ extern "C" int tq_decode_validate(const tq_layout* layout, const void* query, in
                                   int64_t num_blocks, int32_t block_size, const int32_t* block_table,
                                   int32_t block_table_stride, const int32_t* seq_lens, const float* signs,
                                   const float* centroids, int32_t num_kv_splits, int32_t sliding_window,
-                                  const void* workspace, size_t workspace_bytes, const void* out,
+                                  float value_gate, const void* workspace, size_t workspace_bytes, const void* out,
                                   int32_t out_dtype) {
   int st = tq::validate_decode(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                                block_size, block_table, block_table_stride, seq_lens, signs, centroids,
-                               num_kv_splits, sliding_window, workspace, workspace_bytes);
+                               num_kv_splits, sliding_window, value_gate, workspace, workspace_bytes);
   if (st != TQ_OK) return st;
   return tq::validate_stage2(batch, num_q_heads, layout->head_dim, num_kv_splits, workspace, workspace_bytes, out,
                              out_dtype);

@@ -29,7 +29,7 @@ int validate_decode(const tq_layout* L, const void* query, int32_t q_dtype, int3
                     int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                     const float* signs, const float* centroids, int32_t num_kv_splits, int32_t sliding_window,
-                    const void* workspace, size_t ws_bytes);
+                    float value_gate, const void* workspace, size_t ws_bytes);
 
 int validate_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                     const void* workspace, size_t ws_bytes, const void* out, int32_t out_dtype);

@@ -166,14 +166,14 @@ class DecodeCase:
                      self.tab.signs, self.tab.centroids, self.tab.boundaries)
         return cache
 
-    def gpu_decode(self, cache, num_kv_splits, out_dtype=None, sliding_window=0, sinks=None):
+    def gpu_decode(self, cache, num_kv_splits, out_dtype=None, sliding_window=0, sinks=None, value_gate=0.0):
         import quantized_decode_attention_tq_amd as tq
 
         t = torch()
         sk = None if sinks is None else t.from_numpy(np.asarray(sinks, np.float32)).cuda()
         out, lse = tq.decode(self.lay_c, self.q, cache, self.bt, self.sl, self.tab.signs, self.tab.centroids,
                              self.scale, num_kv_splits, out_dtype=out_dtype or t.float32,
-                             sliding_window=sliding_window, sinks=sk)
+                             sliding_window=sliding_window, sinks=sk, value_gate=value_gate)
         t.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

@@ -170,11 +170,12 @@ def test_store_validation_codes():
 
 def _decode_validate(L, **kw):
     args = dict(q=A, qd=tq.TQ_BF16, B=4, Hq=32, Hk=8, cache=A, nb=100, bs=16, bt=A, bts=64, sl=A, signs=A, cent=A,
-                S=8, win=0, ws=A, wsb=tq.decode_workspace_bytes(4, 32, 128, 8), out=A, od=tq.TQ_F32)
+                S=8, win=0, gate=0.0, ws=A, wsb=tq.decode_workspace_bytes(4, 32, 128, 8), out=A, od=tq.TQ_F32)
     args.update(kw)
     return tq._lib.tq_decode_validate(ctypes.byref(L), args["q"], args["qd"], args["B"], args["Hq"], args["Hk"],
                                       args["cache"], args["nb"], args["bs"], args["bt"], args["bts"], args["sl"],
-                                      args["signs"], args["cent"], args["S"], args["win"], args["ws"], args["wsb"],
+                                      args["signs"], args["cent"], args["S"], args["win"], args["gate"], args["ws"],
+                                      args["wsb"],
                                       args["out"], args["od"])
 
 
@@ -190,6 +191,9 @@ def test_decode_validation_codes():
     assert _decode_validate(L, S=0) == tq.TQ_EINVAL
     assert _decode_validate(L, win=-1) == tq.TQ_EINVAL
     assert _decode_validate(L, win=4096) == tq.TQ_OK
+    assert _decode_validate(L, gate=1e-3) == tq.TQ_OK  # the opt-in sparse-V gate
+    for bad in (-1e-3, 1.0, float("nan"), float("inf")):
+        assert _decode_validate(L, gate=bad) == tq.TQ_EINVAL, bad
     assert _decode_validate(L, sl=None) == tq.TQ_EINVAL
     assert _decode_validate(L, ws=A + 8) == tq.TQ_EINVAL
     assert _decode_validate(L, signs=None) == tq.TQ_EINVAL

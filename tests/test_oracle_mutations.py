@@ -181,3 +181,17 @@ def test_lloyd_max_values_left_rotated_are_caught(monkeypatch):
 
     _patch(monkeypatch, "decode_slots", bad)
     _fails(P.test_dequant_original_space_error_matches_lloyd_max_distortion, "turboquant_3bit_lm", 128)
+
+
+def test_sparse_v_gate_renormalized_over_kept_tokens_is_caught(monkeypatch):
+    """The gate skips only the value side: dividing by the kept tokens'
+    weights alone (dropping the gated ones from the denominator) moves o."""
+    def bad(q, K, V, scale, gate, sink=-math.inf):
+        o, lse = T.attend(q, K, V, scale, sink)
+        s = scale * (K @ q)
+        f = np.exp(s - s.max())
+        keep = f >= gate
+        return (f[keep] @ V[keep]) / (f[keep].sum() + math.exp(sink - s.max())), lse, np.zeros(V.shape[1])
+
+    _patch(monkeypatch, "attend_sparse_v", bad)
+    _fails(P.test_sparse_v_gate_closed_form)

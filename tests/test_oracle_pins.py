@@ -774,3 +774,53 @@ def test_sliding_window_closed_forms():
                 sc = 0.25 * (Kd[max(0, L - W):] @ (R @ qd[b, hq]))
                 np.testing.assert_allclose(o[b, hq], scipy.special.softmax(sc) @ Vd[max(0, L - W):], rtol=1e-11)
                 np.testing.assert_allclose(l[b, hq], scipy.special.logsumexp(sc), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- sparse-V gate
+
+
+def test_sparse_v_gate_closed_form():
+    """Two tokens with scores 8 and 0 (factor e^-8 = 3.4e-4 < 1e-3): the gate
+    drops token 2's value but keeps its weight in the denominator, so
+    o = v1 / (1 + e^-8) while exact attention is (v1 + e^-8 v2) / (1 + e^-8);
+    the lse is exact; the bound is e^-8 |v2| / (1 + e^-8).  A gate below
+    every factor is exact attention with a zero bound."""
+    q = np.array([1.0, 0.0])
+    K = np.array([[8.0, 0.0], [0.0, 0.0]])
+    V = np.array([[1.0, 2.0], [-3.0, 5.0]])
+    e = math.exp(-8.0)
+    o, lse, b = O.attend_sparse_v(q, K, V, 1.0, 1e-3)
+    np.testing.assert_allclose(o, V[0] / (1 + e), rtol=1e-15)
+    assert lse == pytest.approx(8 + math.log1p(e), abs=1e-14)
+    np.testing.assert_allclose(b, e * np.abs(V[1]) / (1 + e), rtol=1e-14)
+    ox, lx = O.attend(q, K, V, 1.0)
+    np.testing.assert_allclose(np.abs(o - ox), b, rtol=1e-12)  # the bound is tight here
+    o0, lse0, b0 = O.attend_sparse_v(q, K, V, 1.0, e / 2)
+    np.testing.assert_allclose(o0, ox, rtol=1e-15)
+    assert lse0 == lx and np.all(b0 == 0)
+    # a sink joins the denominator only: o = v1 / (1 + e^-8 + e^{sink - 8})
+    o, lse, b = O.attend_sparse_v(q, K, V, 1.0, 1e-3, sink=7.0)
+    np.testing.assert_allclose(o, V[0] / (1 + e + math.exp(-1.0)), rtol=1e-15)
+
+
+def test_sparse_v_bound_covers_every_subset_of_gated_tokens():
+    """A kernel gates against a running maximum, which never exceeds the
+    final one, so it drops some subset of the tokens gated here: every such
+    result stays within the bound of exact attention."""
+    rng = np.random.default_rng(4)
+    for trial in range(20):
+        n, d = 200, 16
+        q, K, V = rng.standard_normal(d), rng.standard_normal((n, d)) * 2, rng.standard_normal((n, d))
+        scale, gate = 1.0, 10.0 ** rng.uniform(-4, -1)
+        ox, _ = O.attend(q, K, V, scale)
+        _, _, b = O.attend_sparse_v(q, K, V, scale, gate)
+        s = scale * (K @ q)
+        f = np.exp(s - s.max())
+        gated = np.flatnonzero(f < gate)
+        assert len(gated) > 0
+        for _ in range(5):
+            sub = gated[rng.random(len(gated)) < 0.5]
+            keep = np.ones(n, bool)
+            keep[sub] = False
+            o_sub = (f[keep] @ V[keep]) / f.sum()
+            assert np.all(np.abs(o_sub - ox) <= b * (1 + 1e-12) + 1e-15)
