@@ -1704,9 +1704,8 @@ int launch_stage1_g(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds
   DecodeArgs arg = a;
   float g = gate;
   void* args[] = {&arg, &g};  // the default kernel reads the first only
-  return tq::hip_status(hipLaunchKernel(fn,
-                                        dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds,
-                                        stream));
+  return tq::hip_status(
+      hipLaunchKernel(fn, dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds, stream));
 }
 
 // The sparse-V gate takes its own kernels.
@@ -1841,16 +1840,14 @@ extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int3
                                 int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
                                 const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
                                 int32_t num_kv_splits, int32_t sliding_window, float value_gate, void* workspace,
-                                size_t workspace_bytes,
-                                void* stream) {
+                                size_t workspace_bytes, void* stream) {
   int st = tq::validate_decode(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
                                block_size, block_table, block_table_stride, seq_lens, signs, centroids,
                                num_kv_splits, sliding_window, value_gate, workspace, workspace_bytes);
   if (st != TQ_OK || batch == 0) return st;
   return stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
                 block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, value_gate,
-                workspace,
-                static_cast<hipStream_t>(stream));
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
