@@ -78,7 +78,7 @@ class DecodeBench:
     tokens, queries, tables, workspace."""
 
     def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos",
-                 sliding_window: int = 0, sinks=None, value_gate: float = 0.0):
+                 sliding_window: int = 0, sinks=None, value_gate: float = 0.0, scale_mult: float = 1.0):
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
         self.window = sliding_window
@@ -120,7 +120,7 @@ class DecodeBench:
                               device="cuda")
         self.out = torch.empty((w.batch, w.num_q_heads, D), dtype=self.q.dtype, device="cuda")
         self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
-        self.scale = 1.0 / math.sqrt(D)
+        self.scale = scale_mult / math.sqrt(D)
         seen = np.minimum(self.lens, sliding_window) if sliding_window > 0 else self.lens
         self.bytes_read = int(seen.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
         self.sinks = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
@@ -510,6 +510,18 @@ def main():
                 f"stage1 {s1 * 1e3:.1f} us")
             del b
             torch.cuda.empty_cache()
+        # concentrated attention (softmax scale x4): most tile pairs fall below the gate
+        for name, S in (("llama8b", args.splits), ("qwen32b", args.splits)):
+            res = {}
+            for gate in (0.0, SPARSE_V_GATE):
+                b = DecodeBench(torch, tq, W.WORKLOADS[name], S, value_gate=gate, scale_mult=4.0)
+                res[gate] = (b.time_stage1(30), b.time_decode(30))
+                del b
+                torch.cuda.empty_cache()
+            sv[f"{name}_scale_x4"] = {"ungated_decode_ms": res[0.0][1], "gated_decode_ms": res[SPARSE_V_GATE][1],
+                                      "ungated_stage1_ms": res[0.0][0], "gated_stage1_ms": res[SPARSE_V_GATE][0]}
+            log(f"[sparse-V {name}, softmax scale x4] decode call {res[0.0][1] * 1e3:.1f} us ungated, "
+                f"{res[SPARSE_V_GATE][1] * 1e3:.1f} us gated")
         extra["sparse_v"] = sv
         # sliding window + attention sinks: long context with an 8192-token window
         wk = W.WORKLOADS["longctx"]
