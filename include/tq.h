@@ -315,8 +315,9 @@ int tq_decode_validate(const tq_layout* layout, const void* query, int32_t q_dty
  * can be timed on its own.  Stage 1 writes the workspace table and the
  * partial rows of every work unit; stage 2 merges each sequence's units into
  * out / lse_out.  Same arguments and checks as tq_decode_attention (stage 1
- * takes the window, stage 2 the sinks); stage 2 must run on a workspace
- * written by stage 1 with the same batch and num_q_heads. */
+ * takes the window and the value gate, stage 2 the sinks); stage 2 must run
+ * on a workspace written by stage 1 with the same batch, num_q_heads and
+ * head_dim. */
 int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                      int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks, int32_t block_size,
                      const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
