@@ -5,10 +5,12 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 (the HIP library and its Python binding) never imports, links or calls it, and
 this module imports nothing from the product path.
 
-Everything here is NumPy in float64, except where a floating-point step decides
-an integer that the kernel decides in fp32 (the value codes, see
-``quantize_values``): there both sides take the decision in fp32, with the same
-IEEE round-to-nearest-even operations.
+Everything here is NumPy in float64.  Where a floating-point comparison decides
+an integer (a Lloyd-Max bucket, a value code) the oracle takes the decision on
+the exact value of the defining expression; the kernels take it in fp32, so
+their codes may differ next to a decision boundary, which the parity tests
+allow for (at most one step, within 1e-6 of the boundary, on at most 1e-5 of
+the coordinates).
 
 Sources (cited by page title and section; the pages are the only authority):
 
@@ -214,8 +216,9 @@ def _trapz(f, a: float, b: float, n: int = 200) -> float:
     return s * h
 
 
-def lloyd_max_pages_trapz(d: int, bits: int, max_iter: int = 200, tol: float = 1e-10):
-    """The pages' own solver, run as described ([PR] "关键源码片段", centroids.py).
+def lloyd_max_pages_trapz(d: int, bits: int, max_iter: int = 200, tol: float = 1e-10, info=None):
+    """The pages' own solver ([PR] "关键源码片段", centroids.py), transcribed
+    step for step so that its output can be reproduced exactly (reading R3).
 
     Start from 2^bits centroids spread uniformly over +-3.5 sigma; each round
     takes boundaries at midpoints, closes the outer cells at +-10.5 sigma,
@@ -224,7 +227,8 @@ def lloyd_max_pages_trapz(d: int, bits: int, max_iter: int = 200, tol: float = 1
     stops after ``max_iter`` rounds or as soon as no centroid moves by
     ``tol`` -- and in that case keeps the centroids from before the last
     update.  Returns float64 (centroids, boundaries) before the fp32 cast the
-    pages apply.
+    pages apply.  ``info`` (a dict, optional) receives the number of rounds
+    run and whether the tolerance stopped it.
     """
     L = 1 << bits
     s2 = 1.0 / d
@@ -235,7 +239,9 @@ def lloyd_max_pages_trapz(d: int, bits: int, max_iter: int = 200, tol: float = 1
 
     lo, hi = -3.5 * sigma, 3.5 * sigma
     c = [lo + (hi - lo) * (i + 0.5) / L for i in range(L)]
+    rounds, converged = 0, False
     for _ in range(max_iter):
+        rounds += 1
         mids = [(c[i] + c[i + 1]) / 2.0 for i in range(L - 1)]
         edges = [3.0 * lo] + mids + [3.0 * hi]
         new = []
@@ -245,8 +251,11 @@ def lloyd_max_pages_trapz(d: int, bits: int, max_iter: int = 200, tol: float = 1
             den = _trapz(pdf, a, b)
             new.append(num / den if den > 1e-15 else c[i])
         if max(abs(new[i] - c[i]) for i in range(L)) < tol:
+            converged = True
             break
         c = new
+    if info is not None:
+        info.update(rounds=rounds, converged=converged)
     c = np.array(c, dtype=np.float64)
     return c, (c[:-1] + c[1:]) / 2.0
 
@@ -453,38 +462,62 @@ def quantize_key_mse(x, R, centroids32, boundaries32, norm_correction: bool):
     return codes, gamma
 
 
+def _value_scale_zero(vmin, vmax, bits: int):
+    """fp16 (scale, zero) of rows with extremes vmin, vmax (float64 arrays):
+    zero = fp16(min v), scale = fp16((max v - min v) / (2^b - 1)), each
+    rounded to nearest even once from the float64 value ([API]
+    _continuation_prefill: the value region ends with 16-bit scale and zero
+    fields).  For 16-bit inputs the difference is exact in float64 and the
+    quotient's one float64 rounding does not change its fp16 rounding."""
+    levels = (1 << bits) - 1
+    with np.errstate(all="ignore"):
+        s16 = ((vmax - vmin) / float(levels)).astype(np.float16)
+    z16 = np.asarray(vmin, dtype=np.float64).astype(np.float16)
+    return s16, z16
+
+
+def value_codes(v, z, s, bits: int) -> np.ndarray:
+    """code = clamp(floor((v - z) / s + 1/2), 0, 2^b - 1) against the stored
+    fp16 scale s and zero z (reading R12: round half up, clamp; scale 0
+    gives all-zero codes; a NaN quotient gives 0).  v: (rows, D) float64;
+    z, s: (rows,) float64.  The decision is exact: the float64 quotient
+    settles every code whose quotient is not within 1e-9 of a half-integer,
+    and those few are recomputed in rational arithmetic from the exact
+    binary values of v, z and s."""
+    from fractions import Fraction
+
+    levels = (1 << bits) - 1
+    v = np.asarray(v, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)[:, None]
+    s = np.asarray(s, dtype=np.float64)[:, None]
+    with np.errstate(all="ignore"):
+        x = (v - z) / s
+        fl = np.floor(x + 0.5)
+    fl = np.where(np.isnan(fl), 0.0, fl)
+    frac = x - np.floor(x)
+    near = np.isfinite(x) & np.isfinite(v) & np.isfinite(z) & np.isfinite(s) & (s != 0) & \
+        (np.abs(frac - 0.5) < 1e-9 * np.maximum(1.0, np.abs(x)))
+    for r, c in zip(*np.nonzero(near)):
+        q = (Fraction(float(v[r, c])) - Fraction(float(z[r, 0]))) / Fraction(float(s[r, 0])) + Fraction(1, 2)
+        fl[r, c] = float(q.numerator // q.denominator)
+    codes = np.clip(fl, 0, levels).astype(np.int64)
+    codes[np.broadcast_to(s == 0, codes.shape)] = 0
+    return codes
+
+
 def quantize_values(v, bits: int):
     """One value vector -> (codes, fp16 scale bits, fp16 zero bits).
 
     Uniform asymmetric codes in the unrotated space with a per-slot fp16
     scale and zero ([API] _continuation_prefill: the value region holds the
-    codes then two 16-bit fields, scale and zero; values are not rotated).
-    zero = fp16(min v); scale = fp16((max v - min v) / (2^b - 1)) with the
-    range and quotient formed in fp32; the codes are formed against the
-    stored fp16 scale and zero (reading R12):
-        inv = fl32(1 / scale); code = floor(fl32(fl32(v - zero) * inv) + 0.5)
-    clamped to [0, 2^b - 1] (NaN -> 0); scale == 0 gives all-zero codes.
-    These are fp32 operations on both sides because they decide integers.
+    codes then two 16-bit fields, scale and zero; values are not rotated),
+    the codes formed against the stored fp16 scale and zero (reading R12):
+    see ``_value_scale_zero`` and ``value_codes``.
     """
-    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)  # exact for bf16/fp16 inputs
-    levels = (1 << bits) - 1
-    vmin = v32.min()
-    vmax = v32.max()
-    rng = np.float32(vmax - vmin)
-    scale32 = np.float32(rng / np.float32(levels))
-    s16 = np.float16(scale32)
-    z16 = np.float16(vmin)
-    if float(s16) == 0.0:
-        codes = np.zeros(v32.shape, dtype=np.int64)
-    else:
-        with np.errstate(all="ignore"):
-            inv = np.float32(np.float32(1.0) / np.float32(s16))
-            t = (v32 - np.float32(z16)).astype(np.float32)
-            q = (t * inv).astype(np.float32)
-            r = (q + np.float32(0.5)).astype(np.float32)
-            r = np.where(np.isnan(r), np.float32(0.0), r)
-            codes = np.clip(np.floor(r), 0, levels).astype(np.int64)
-    return codes, np.array(s16).view(np.uint16), np.array(z16).view(np.uint16)
+    v = np.asarray(v, dtype=np.float64).reshape(1, -1)
+    s16, z16 = _value_scale_zero(v.min(axis=1), v.max(axis=1), bits)
+    codes = value_codes(v, z16.astype(np.float64), s16.astype(np.float64), bits)[0]
+    return codes, np.array(s16[0]).view(np.uint16), np.array(z16[0]).view(np.uint16)
 
 
 def encode_slot(lay: Layout, k, v, R, centroids32, boundaries32) -> np.ndarray:
@@ -551,22 +584,9 @@ def encode_slots(lay: Layout, K, V, R, centroids32, boundaries32) -> np.ndarray:
         o += lay.value_data_bytes
         out[:, o : o + 2] = _u16_le(fp16_bits(gv))
         return out
-    # values: the fp32 steps of quantize_values, per row
-    v32 = V.astype(np.float32)
-    levels = (1 << lay.value_bits) - 1
-    vmin = v32.min(axis=1)
-    vmax = v32.max(axis=1)
-    scale32 = ((vmax - vmin).astype(np.float32) / np.float32(levels)).astype(np.float32)
-    s16 = scale32.astype(np.float16)
-    z16 = vmin.astype(np.float16)
-    with np.errstate(all="ignore"):
-        inv = (np.float32(1.0) / s16.astype(np.float32)).astype(np.float32)
-        t = (v32 - z16.astype(np.float32)[:, None]).astype(np.float32)
-        q = (t * inv[:, None]).astype(np.float32)
-        rr = (q + np.float32(0.5)).astype(np.float32)
-        rr = np.where(np.isnan(rr), np.float32(0.0), rr)
-        vc = np.clip(np.floor(rr), 0, levels).astype(np.int64)
-    vc[s16.astype(np.float32) == 0.0] = 0
+    # values: the steps of quantize_values, per row
+    s16, z16 = _value_scale_zero(V.min(axis=1), V.max(axis=1), lay.value_bits)
+    vc = value_codes(V, z16.astype(np.float64), s16.astype(np.float64), lay.value_bits)
     o = lay.key_packed_size
     out[:, o : o + lay.value_data_bytes] = pack_lsb(vc, lay.value_bits)
     o += lay.value_data_bytes
@@ -906,6 +926,8 @@ def dequant_original_space(lay: Layout, kv_cache, block_table_row, seq_len: int,
 
 
 def workspace_bytes(batch: int, num_q_heads: int, head_dim: int, num_kv_splits: int) -> int:
-    """Stage-1 scratch (B, Hq, S, D+1) fp32 ([PR] attention.py excerpt,
-    the mid_o buffer; [API] _decode_attention)."""
+    """Bytes of the pages' stage-1 scratch: (B, Hq, S, D+1) fp32, the
+    split's partial output and its LSE ([PR] attention.py excerpt, the mid_o
+    buffer; [API] _decode_attention).  A decode workspace must hold at least
+    this much partial state."""
     return batch * num_q_heads * num_kv_splits * (head_dim + 1) * 4

@@ -81,11 +81,37 @@ def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0
     return len(bad)
 
 
-def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32, values=None, min_allowed=0):
+def _compare_value_codes(lay, got, want, values, min_allowed=0):
+    """got/want: (rows, value data + 4) = packed uniform value codes, fp16
+    scale, fp16 zero of the same rows; values: (rows, D) float64 inputs.
+    Scale and zero are bit-exact.  A code may differ from the oracle's exact
+    floor((v - z) / s + 1/2) only by one, where that quotient is within
+    1e-6 * (2^b - 1) of a half-integer (the kernel decides in fp32), at most
+    1e-5 of the codes (or min_allowed).  Returns the number of differing
+    codes."""
+    vd, vb = lay.value_data_bytes, lay.value_bits
+    np.testing.assert_array_equal(got[:, vd:], want[:, vd:])
+    cg = O.unpack_lsb(got[:, :vd], vb, lay.head_dim)
+    cw = O.unpack_lsb(want[:, :vd], vb, lay.head_dim)
+    bad = np.argwhere(cg != cw)
+    if len(bad):
+        s = want[:, vd : vd + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+        z = want[:, vd + 2 : vd + 4].copy().view(np.float16).astype(np.float64)[:, 0]
+        r, c = bad[:, 0], bad[:, 1]
+        x = (values[r, c] - z[r]) / s[r]
+        dist = np.abs(x - (np.floor(x) + 0.5))
+        assert np.all(dist < BOUNDARY_EPS * ((1 << vb) - 1)), f"value code mismatch away from a tie: {dist.max()}"
+        assert np.all(np.abs(cg[r, c] - cw[r, c]) == 1)
+    assert len(bad) <= max(MISMATCH_FRAC * cg.size, min_allowed), f"{len(bad)} value code mismatches of {cg.size}"
+    return len(bad)
+
+
+def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32, values, min_allowed=0):
     """got/want: (rows, slot) bytes of the same rows; keys / values: (rows, D)
     float64 inputs of those rows.  Lloyd-Max codes (MSE keys, Lloyd-Max
-    values) follow _compare_codes; FP8 keys, uniform value codes, scale, zero
-    and padding are bit-exact.  Returns the number of code mismatches."""
+    values) follow _compare_codes, uniform value codes _compare_value_codes;
+    FP8 keys, value scale and zero and padding are bit-exact.  Returns the
+    number of code mismatches."""
     assert got.shape == want.shape
     R = O.rotation(np.asarray(signs, np.float64)) if O.needs_rotation(lay) else None
     kd, vo, vd = lay.key_data_bytes, lay.key_packed_size, lay.value_data_bytes
@@ -96,13 +122,13 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32,
         n += _compare_codes(lay, lay.key_bits, got[:, : kd + 2], want[:, : kd + 2], keys, R, c32, b32,
                             lay.norm_correction, min_allowed)
     if lay.value_lm:
-        assert values is not None, "Lloyd-Max values need the value inputs"
         vc32, vb32 = O.value_tables(lay)
         n += _compare_codes(lay, lay.value_bits, got[:, vo : vo + vd + 2], want[:, vo : vo + vd + 2], values, R,
                             vc32, vb32, True, min_allowed)
         np.testing.assert_array_equal(got[:, vo + vd + 2 :], want[:, vo + vd + 2 :])
     else:
-        np.testing.assert_array_equal(got[:, vo:], want[:, vo:])
+        n += _compare_value_codes(lay, got[:, vo : vo + vd + 4], want[:, vo : vo + vd + 4], values, min_allowed)
+        np.testing.assert_array_equal(got[:, vo + vd + 4 :], want[:, vo + vd + 4 :])
     return n
 
 

@@ -1,6 +1,7 @@
-"""tq_store on the GPU against the oracle: FP8 keys, value codes, value scale
-and zero bit-exact; Lloyd-Max key codes bit-exact except next to a bucket
-boundary (|u - b| < 1e-6, at most 1e-5 of the coordinates); stored key
+"""tq_store on the GPU against the oracle: FP8 keys, value scale and zero
+bit-exact; Lloyd-Max key codes and uniform value codes bit-exact except next
+to a decision boundary (|u - b| < 1e-6 for keys, |(v - z)/s - (k + 1/2)| <
+1e-6 * (2^b - 1) for values; at most 1e-5 of the coordinates); stored key
 norms within 1e-3 relative; bytes outside the addressed slots untouched."""
 
 import numpy as np
@@ -112,5 +113,11 @@ def test_store_edge_cases():
     want = np.full((4, 16, 2, 102), 7, np.uint8)
     kb = keys.float().cpu().numpy().reshape(6, 2, 128).astype(np.float64)
     vb = vals.float().cpu().numpy().reshape(6, 2, 128).astype(np.float64)
-    O.store_rows(lay, kb, vb, slots.cpu().numpy(), want, W.signs(3), c32, b32)
-    np.testing.assert_array_equal(cache.cpu().numpy(), want)
+    sl = slots.cpu().numpy()
+    O.store_rows(lay, kb, vb, sl, want, W.signs(3), c32, b32)
+    got = cache.cpu().numpy()
+    written = np.zeros((4, 16, 2), bool)
+    written[sl // 16, sl % 16] = True
+    np.testing.assert_array_equal(got[~written], want[~written])
+    G.compare_slots(lay, got[sl // 16, sl % 16].reshape(-1, 102), want[sl // 16, sl % 16].reshape(-1, 102),
+                    kb.reshape(-1, 128), W.signs(3), c32, b32, vb.reshape(-1, 128))

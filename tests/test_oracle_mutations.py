@@ -195,3 +195,63 @@ def test_sparse_v_gate_renormalized_over_kept_tokens_is_caught(monkeypatch):
 
     _patch(monkeypatch, "attend_sparse_v", bad)
     _fails(P.test_sparse_v_gate_closed_form)
+
+
+def _pages_trapz_variant(intervals=200, start=3.5, keep_post=False):
+    """A copy of the pages' solver with one planted change."""
+
+    def solver(d, bits, max_iter=200, tol=1e-10, info=None):
+        L = 1 << bits
+        s2 = 1.0 / d
+        sigma = math.sqrt(s2)
+        pdf = lambda x: math.exp(-x * x / (2.0 * s2)) / math.sqrt(2.0 * math.pi * s2)
+        trap = lambda f, a, b: T._trapz(f, a, b, intervals)
+        lo, hi = -start * sigma, start * sigma
+        c = [lo + (hi - lo) * (i + 0.5) / L for i in range(L)]
+        rounds, conv = 0, False
+        for _ in range(max_iter):
+            rounds += 1
+            mids = [(c[i] + c[i + 1]) / 2.0 for i in range(L - 1)]
+            edges = [-10.5 * sigma] + mids + [10.5 * sigma]
+            new = [trap(lambda x: x * pdf(x), edges[i], edges[i + 1]) / trap(pdf, edges[i], edges[i + 1])
+                   for i in range(L)]
+            if max(abs(new[i] - c[i]) for i in range(L)) < tol:
+                conv = True
+                if keep_post:
+                    c = new
+                break
+            c = new
+        if info is not None:
+            info.update(rounds=rounds, converged=conv)
+        c = np.array(c)
+        return c, (c[:-1] + c[1:]) / 2.0
+
+    return solver
+
+
+def test_pages_trapz_unchanged_copy_passes(monkeypatch):
+    _patch(monkeypatch, "lloyd_max_pages_trapz", _pages_trapz_variant())
+    for bits in (2, 3, 4):
+        P.test_pages_trapz_against_numpy_trapezoid(bits)
+
+
+@pytest.mark.parametrize("change", [{"intervals": 100}, {"start": 3.0}, {"keep_post": True}])
+def test_pages_trapz_planted_changes_are_caught(monkeypatch, change):
+    _patch(monkeypatch, "lloyd_max_pages_trapz", _pages_trapz_variant(**change))
+    failed = 0
+    for bits in (2, 3, 4):
+        try:
+            P.test_pages_trapz_against_numpy_trapezoid(bits)
+        except AssertionError:
+            failed += 1
+    assert failed > 0, change
+
+
+def test_value_codes_half_to_even_is_caught(monkeypatch):
+    def bad(v, z, s, bits):
+        with np.errstate(all="ignore"):
+            x = (np.asarray(v, np.float64) - np.asarray(z, np.float64)[:, None]) / np.asarray(s, np.float64)[:, None]
+        return np.clip(np.nan_to_num(np.round(x)), 0, (1 << bits) - 1).astype(np.int64)
+
+    _patch(monkeypatch, "value_codes", bad)
+    _fails(P.test_value_codes_exact_definition, 4)

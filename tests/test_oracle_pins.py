@@ -164,6 +164,54 @@ def test_pages_trapz_solver_behaviour():
         assert abs(m - c[i]) < 3e-3 * sigma
 
 
+def _numpy_trapz_round(c, sigma):
+    """One round of the pages' update (boundaries at midpoints, outer cells
+    closed at +-10.5 sigma) with the cell moments from numpy's trapezoid rule
+    over 201 equally spaced points per cell (200 intervals), vectorized."""
+    edges = np.concatenate([[-10.5 * sigma], (c[:-1] + c[1:]) / 2, [10.5 * sigma]])
+    x = np.linspace(edges[:-1], edges[1:], 201, axis=1)  # (cells, 201)
+    pdf = np.exp(-x * x / (2 * sigma * sigma)) / math.sqrt(2 * math.pi * sigma * sigma)
+    return np.trapezoid(x * pdf, x, axis=1) / np.trapezoid(pdf, x, axis=1)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pages_trapz_against_numpy_trapezoid(bits):
+    """The pages' solver re-derived with numpy's trapezoid rule (a library
+    routine) on the same 201-point cell grids: from the stated start (uniform
+    over +-3.5 sigma), iterate until no centroid moves by 1e-10 -- returning
+    the iterate from before that last update -- or for at most 200 rounds.
+    The 2- and 3-bit runs stop on the tolerance; the 4-bit run hits the
+    200-round cap, so its result depends on the start and on every round."""
+    sigma = 1 / math.sqrt(128)
+    L = 1 << bits
+    c = -3.5 * sigma + 7.0 * sigma * (np.arange(L) + 0.5) / L
+    rounds, converged = 0, False
+    for _ in range(200):
+        rounds += 1
+        new = _numpy_trapz_round(c, sigma)
+        if np.max(np.abs(new - c)) < 1e-10:
+            converged = True
+            break
+        c = new
+    info = {}
+    got, gb = O.lloyd_max_pages_trapz(128, bits, info=info)
+    assert info == {"rounds": rounds, "converged": converged}, (info, rounds, converged)
+    assert converged == (bits < 4)
+    np.testing.assert_allclose(got, c, rtol=0, atol=1e-13 * sigma)
+    np.testing.assert_allclose(gb, (c[:-1] + c[1:]) / 2, rtol=0, atol=1e-13 * sigma)
+
+
+def test_pages_trapz_start_and_cap():
+    """Zero rounds return the stated start; the 4-bit iterate is still
+    moving at the cap (one more round moves it by more than the tolerance)."""
+    sigma = 1 / math.sqrt(128)
+    c0, _ = O.lloyd_max_pages_trapz(128, 3, max_iter=0)
+    np.testing.assert_allclose(c0, np.linspace(-3.5 * sigma, 3.5 * sigma, 9)[:-1] + 7 * sigma / 16, rtol=0,
+                               atol=1e-15)
+    c4, _ = O.lloyd_max_pages_trapz(128, 4)
+    assert np.max(np.abs(_numpy_trapz_round(c4, sigma) - c4)) > 1e-10
+
+
 # ---------------------------------------------------------------- signs
 
 
@@ -251,15 +299,14 @@ def test_pack_hand_examples():
 def test_pack_roundtrip_exhaustive(bits):
     L = 1 << bits
     rng = np.random.default_rng(bits)
-    # every code value at every position of a 128-code vector
-    for v in range(L):
-        for pos in range(0, 128, 1):
-            codes = rng.integers(0, L, 128)
-            codes[pos] = v
-            packed = O.pack_lsb(codes, bits)
-            assert packed.shape == (128 * bits // 8,)
-            np.testing.assert_array_equal(O.unpack_lsb(packed, bits, 128), codes)
-            break
+    # every code value at every position of a 128-code vector (one row per
+    # (value, position), the other positions random)
+    codes = rng.integers(0, L, (L * 128, 128))
+    v, pos = np.divmod(np.arange(L * 128), 128)
+    codes[np.arange(L * 128), pos] = v
+    packed = O.pack_lsb(codes, bits)
+    assert packed.shape == (L * 128, 128 * bits // 8)
+    np.testing.assert_array_equal(O.unpack_lsb(packed, bits, 128), codes)
     codes = rng.integers(0, L, (500, 128))
     np.testing.assert_array_equal(O.unpack_lsb(O.pack_lsb(codes, bits), bits, 128), codes)
 
@@ -346,6 +393,57 @@ def test_value_codec_properties():
     # constant vector: scale 0, all codes 0, reconstruction exact
     codes, s16, z16 = O.quantize_values(np.full(D, 3.25), 4)
     assert s16 == 0 and np.all(codes == 0) and float(np.uint16(z16).view(np.float16)) == 3.25
+
+
+def _fp16_nearest_even(q):
+    """Exact rational q -> the nearest binary16 value (ties to the even
+    significand), by comparing q with the representable neighbours."""
+    from fractions import Fraction
+
+    f = np.float16(float(q))  # within one step of the answer
+    cands = sorted({np.nextafter(f, np.float16(-np.inf)), f, np.nextafter(f, np.float16(np.inf))},
+                   key=lambda h: (abs(Fraction(float(h)) - q), int(np.array(h).view(np.uint16)) & 1))
+    return cands[0]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_value_codes_exact_definition(bits):
+    """Value fields and codes equal the definition evaluated in rational
+    arithmetic: zero = fp16(min v), scale = fp16((max - min) / (2^b - 1))
+    (round to nearest even), code = clamp(floor((v - z) / s + 1/2)); ties
+    round up."""
+    from fractions import Fraction
+
+    levels = (1 << bits) - 1
+    rng = np.random.default_rng(40 + bits)
+    for r in range(60):
+        v = O.widen(W.to_bits(rng.standard_normal(D) * rng.uniform(0.001, 50) + rng.uniform(-3, 3), "bf16"), "bf16")
+        codes, s16, z16 = O.quantize_values(v, bits)
+        z = np.uint16(z16).view(np.float16)
+        s = np.uint16(s16).view(np.float16)
+        assert z == _fp16_nearest_even(Fraction(float(v.min())))
+        assert s == _fp16_nearest_even((Fraction(float(v.max())) - Fraction(float(v.min()))) / levels)
+        zf, sf = Fraction(float(z)), Fraction(float(s))
+        for i in range(D):
+            x = (Fraction(float(v[i])) - zf) / sf + Fraction(1, 2)
+            want = min(max(x.numerator // x.denominator, 0), levels)
+            assert codes[i] == want, (r, i, codes[i], want)
+    # exact ties: v - z = (k + 1/2) s rounds up to k + 1; just below stays at k
+    z, s = 0.25, 0.1875  # fp16 values; (k + 1/2) * 0.1875 is exact in float64
+    k = np.arange(levels)
+    ties = z + (k + 0.5) * s
+    vt = np.concatenate([[z], ties, np.nextafter(ties, -np.inf)])
+    got = O.value_codes(vt[None, :], np.array([z]), np.array([s]), bits)[0]
+    np.testing.assert_array_equal(got[1 : 1 + levels], k + 1)
+    np.testing.assert_array_equal(got[1 + levels :], k)
+    assert got[0] == 0
+
+
+def test_workspace_bytes_of_the_pages_layout():
+    """(B, Hq, S, D+1) fp32: 2 641 920 bytes for 4 sequences, 40 query heads,
+    32 splits, head_dim 128 (the long-context decode shape)."""
+    assert O.workspace_bytes(4, 40, 128, 32) == 2641920
+    assert O.workspace_bytes(32, 32, 128, 8) == 32 * 32 * 8 * 129 * 4
 
 
 def test_encode_decode_slot_roundtrip():
