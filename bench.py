@@ -67,6 +67,26 @@ def warm_gpu(torch, fn, ms=150.0):
         spent += a.elapsed_time(b)
 
 
+DIST_REPLAYS = 60  # timed repetitions behind every median / p10 / p90
+
+
+def spread(torch, fn, reps, per_rep):
+    """Run fn() `reps` times back to back on torch's current stream, each
+    bracketed by events; returns {median, p10, p90, mean} in ms per unit of
+    work (one call of fn is `per_rep` units)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array(sorted(a.elapsed_time(b) for a, b in ev)) / per_rep
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)), "p90": float(np.percentile(t, 90)),
+            "mean": float(t.mean()), "reps": reps}
+
+
 MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
 SPARSE_V_GATE = 1e-3
 # head_dim 256 leg: the headline preset, FP8 keys with Lloyd-Max values (the pages' fp8k_turbo3v), 3-bit MSE
@@ -171,7 +191,8 @@ class DecodeBench:
         return g_all, singles
 
     def time_steps(self, steps, warmup):
-        """ms per step over exactly `steps` steps (graph replays)."""
+        """ms per step over exactly `steps` steps (graph replays), then the
+        per-step spread over DIST_REPLAYS further replays of the 3-step graph."""
         torch = self.torch
         g_all, singles = self.graphs()
         for _ in range(max(1, warmup // N_COPIES)):
@@ -185,11 +206,12 @@ class DecodeBench:
             singles[i].replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per step
+        ms = e0.elapsed_time(e1) / steps
+        return ms, spread(torch, g_all.replay, DIST_REPLAYS, N_COPIES)
 
-    def time_decode(self, calls):
-        """ms per tq_decode_attention call (stage 1 + stage 2, no store),
-        from a graph of one call per cache copy replayed back to back."""
+    def decode_graph(self):
+        """One graph of tq_decode_attention calls (stage 1 + stage 2, no
+        store), one per cache copy."""
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -198,30 +220,20 @@ class DecodeBench:
                 self.stage2()
         g.replay()
         torch.cuda.synchronize()
-        reps = max(1, calls // N_COPIES)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * N_COPIES)
+        return g
 
-    def time_stage1(self, launches):
-        """Average stage-1 kernel duration (ms): events on the launch stream
-        around `launches` back-to-back stage-1 launches (rotating caches), so
-        per-launch host overhead is hidden behind the queued kernels."""
-        torch = self.torch
-        for i in range(N_COPIES):
-            self.stage1(i)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(launches):
-            self.stage1(i % N_COPIES)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
+    def time_decode(self, reps=None):
+        """Per tq_decode_attention call: median / p10 / p90 (ms) over `reps`
+        replays of the graph of one call per cache copy."""
+        g = self.decode_graph()
+        return spread(self.torch, g.replay, reps or DIST_REPLAYS, N_COPIES)
+
+    def time_stage1(self, launches=None):
+        """Stage-1 kernel duration: median / p10 / p90 (ms) of `launches`
+        back-to-back launches (rotating caches), each bracketed by events on
+        the launch stream."""
+        it = iter(range(1 << 30))
+        return spread(self.torch, lambda: self.stage1(next(it) % N_COPIES), launches or DIST_REPLAYS, 1)
 
 
 def store_sweep(torch, tq, steps, block_layout="aos", presets=None, head_dim=128):
@@ -254,9 +266,13 @@ def store_sweep(torch, tq, steps, block_layout="aos", presets=None, head_dim=128
     return res
 
 
-def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
-    """The oracle decoding whole (sequence, KV head) groups of the workload,
-    stored by the oracle, until the time budget is spent."""
+def cpu_baseline(w: W.Workload, budget_s: float = 12.0, store_budget_s: float = 6.0):
+    """The oracle, as it stands, on the host cores: (1) decoding whole
+    (sequence, KV head) groups of the workload (stored by the oracle) with
+    all their query heads until `budget_s` of CPU time is spent, in GB/s of
+    compressed cache; (2) storing rows of the store-sweep inputs (encode +
+    slot write) for the headline preset and 3bit_nc until `store_budget_s`
+    each, in Mtok/s (one token = all of its KV heads)."""
     import oracle as O
 
     lay = O.layout(w.preset, 128)
@@ -285,10 +301,29 @@ def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
         if spent >= budget_s:
             break
     cores = len(os.sched_getaffinity(0))
+    # store: chunks of the store sweep's tokens, all 8 KV heads each
+    s = W.STORE_WORKLOAD
+    Ks, Vs, slots_all, nb = W.store_inputs(num_tokens=16384)
+    store = {}
+    for preset in (w.preset, "turboquant_3bit_nc"):
+        sl = O.layout(preset, 128)
+        sc32, sb32 = (None, None) if sl.key_fp8 else O.codebook_tables(128, sl.key_bits)
+        cache = np.zeros((nb, s["block_size"], s["num_kv_heads"], sl.slot_size_aligned), np.uint8)
+        t_spent, toks, chunk = 0.0, 0, 2048
+        while t_spent < store_budget_s and toks < Ks.shape[0]:
+            a = toks
+            t0 = time.perf_counter()
+            O.store_rows(sl, O.widen(Ks[a : a + chunk], s["dtype"]), O.widen(Vs[a : a + chunk], s["dtype"]),
+                         slots_all[a : a + chunk], cache, signs, sc32, sb32)
+            t_spent += time.perf_counter() - t0
+            toks += chunk
+        store[preset] = {"mtok_s": toks / t_spent / 1e6, "tokens": toks, "seconds": t_spent}
     return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{groups} (sequence, KV head) groups of the {w.name} workload ({nbytes} compressed bytes), "
                       f"oracle-stored, decoded with all {g} query heads each; {spent:.1f}s of CPU time; NumPy/BLAS "
-                      f"threads up to the {cores} cores in the affinity mask"}
+                      f"threads up to the {cores} cores in the affinity mask",
+            "store": {"unit": "Mtok/s", "sample": "store-sweep tokens (8 KV heads each, bf16) in chunks of 2048, "
+                                                   "encoded and written by the oracle", **store}}
 
 
 KERNEL_SOURCES = ("quantized_decode_attention_tq_amd/csrc/tq_decode.hip", "quantized_decode_attention_tq_amd/csrc/tq_bits.h",
@@ -324,17 +359,74 @@ def measured_traffic():
         return None
 
 
+def _probe_lib():
+    """libtq_probe.so: the streaming-read and copy kernels used for the
+    bandwidth ceiling and the counter calibration (built with libtq)."""
+    import ctypes
+
+    import torch  # noqa: F401  (torch's HIP runtime first, as for libtq)
+
+    path = os.path.join(ROOT, "quantized_decode_attention_tq_amd", "libtq_probe.so")
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.tq_probe_stream_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]
+    L.tq_probe_copy.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
+    return L
+
+
+STREAM_CHUNK = 64 << 10
+
+
+def stream_ceiling(torch, nbytes):
+    """Median / p10 / p90 of a plain streaming read of `nbytes` (three
+    buffers rotated, so the 256 MB Infinity Cache cannot serve a launch from
+    the previous one), in GB/s: the practical ceiling of the decode's read."""
+    L = _probe_lib()
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(N_COPIES)]
+    out = torch.zeros(-(-nbytes // STREAM_CHUNK), dtype=torch.int32, device="cuda")
+    it = iter(range(1 << 30))
+
+    def launch():
+        st = torch.cuda.current_stream().cuda_stream
+        rc = L.tq_probe_stream_read(bufs[next(it) % N_COPIES].data_ptr(), nbytes, STREAM_CHUNK, out.data_ptr(), st)
+        assert rc == 0, rc
+
+    warm_gpu(torch, launch, 30.0)
+    t = spread(torch, launch, DIST_REPLAYS, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "chunk": STREAM_CHUNK, "us_median": t["median"] * 1e3,
+            "gbs_median": nbytes / (t["median"] * 1e-3) / 1e9, "gbs_p10_time": nbytes / (t["p90"] * 1e-3) / 1e9,
+            "gbs_p90_time": nbytes / (t["p10"] * 1e-3) / 1e9}
+
+
 def calibrate_copy(torch, mib: int = 512, reps: int = 5):
-    """A plain device-to-device copy of known size, for scaling the
-    FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    """A plain device-to-device copy of known size (the probe library's copy
+    kernel), for scaling the FETCH_SIZE / WRITE_SIZE counters (run under
+    rocprofv3 --pmc)."""
+    L = _probe_lib()
     n = mib << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(reps):
-        dst.copy_(src)
+        assert L.tq_probe_copy(src.data_ptr(), dst.data_ptr(), n, 4096, torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
+    assert torch.equal(src, dst)
     print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}))
+
+
+def profile_stage1(torch, tq, name, launches, splits):
+    """Only stage-1 launches of one decode workload (inputs set up and the GPU
+    warmed first), for rocprofv3 counter runs."""
+    S = {"longctx": 32}.get(name, splits)
+    b = DecodeBench(torch, tq, W.WORKLOADS[name], S)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        b.stage1(i % N_COPIES)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": name, "stage1_launches": launches, "num_kv_splits": S}))
 
 
 DEQUANT_TOKENS, DEQUANT_HK, DEQUANT_BS = 131072, 8, 128
@@ -384,6 +476,36 @@ def dequant_sweep(torch, tq, reps, block_layout="aos", presets=None, head_dim=12
     return res
 
 
+def _us(t):
+    return {k: (v * 1e3 if k != "reps" else v) for k, v in t.items()}
+
+
+def decode_leg(torch, tq, w, S, steps=None, warmup=None, **kw):
+    """Stage 1 alone, the decode call (stage 1 + stage 2) and, when `steps`
+    is given, the whole step (store + decode) of one workload: medians and
+    p10 / p90 in us, and GB/s of compressed cache read at the medians."""
+    b = DecodeBench(torch, tq, w, S, **kw)
+    res = {"preset": w.preset, "num_kv_splits": S, "bytes_read": b.bytes_read}
+    if steps is not None:
+        ms, st = b.time_steps(steps, warmup)
+        res["step_ms_exact_k"] = ms
+        res["step_us"] = _us(st)
+        res["step_gbs"] = b.bytes_read / (st["median"] * 1e-3) / 1e9
+    d = b.time_decode()
+    s1 = b.time_stage1()
+    res["decode_call_us"] = _us(d)
+    res["decode_gbs"] = b.bytes_read / (d["median"] * 1e-3) / 1e9
+    res["decode_frac_hbm"] = res["decode_gbs"] / HBM_PEAK_GBS
+    res["stage1_us"] = _us(s1)
+    res["stage1_gbs"] = b.bytes_read / (s1["median"] * 1e-3) / 1e9
+    del b
+    torch.cuda.empty_cache()
+    log(f"[{w.name}{' ' + str(kw) if kw else ''}] decode call {res['decode_call_us']['median']:.1f} us "
+        f"(p10 {res['decode_call_us']['p10']:.1f}, p90 {res['decode_call_us']['p90']:.1f}) -> {res['decode_gbs']:.0f} "
+        f"GB/s; stage 1 {res['stage1_us']['median']:.1f} us -> {res['stage1_gbs']:.0f} GB/s")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +516,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of 512 MiB (counter calibration) and exit")
+    ap.add_argument("--profile", choices=["llama8b", "longctx", "qwen32b"],
+                    help="only launch stage 1 of this workload --steps times (for rocprofv3) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -407,37 +531,24 @@ def main():
         return
     import quantized_decode_attention_tq_amd as tq
 
+    if args.profile:
+        profile_stage1(torch, tq, args.profile, args.steps, args.splits)
+        return
+
     w = W.WORKLOADS["llama8b"]
-    hb = DecodeBench(torch, tq, w, args.splits)
-    ms = hb.time_steps(args.steps, args.warmup)
-    st1_ms = hb.time_stage1(max(30, args.steps // 4))
-    dec_ms = hb.time_decode(max(30, args.steps // 2))
-    gbs = hb.bytes_read / (ms * 1e-3) / 1e9
-    st1_gbs = hb.bytes_read / (st1_ms * 1e-3) / 1e9
-    dec_gbs = hb.bytes_read / (dec_ms * 1e-3) / 1e9
-    log(f"[llama8b] step {ms * 1e3:.1f} us  -> {gbs:.0f} GB/s; decode call {dec_ms * 1e3:.1f} us -> {dec_gbs:.0f} GB/s; "
-        f"stage1 {st1_ms * 1e3:.1f} us -> {st1_gbs:.0f} GB/s")
-    head_bytes = hb.bytes_read
-    del hb
-    torch.cuda.empty_cache()
+    head = decode_leg(torch, tq, w, args.splits, steps=args.steps, warmup=args.warmup)
+    ms = head["step_ms_exact_k"]
+    gbs = head["bytes_read"] / (ms * 1e-3) / 1e9
+    stream = stream_ceiling(torch, head["bytes_read"])
+    log(f"[llama8b] step {ms * 1e3:.1f} us -> {gbs:.0f} GB/s; streaming read of the same bytes "
+        f"{stream['us_median']:.1f} us -> {stream['gbs_median']:.0f} GB/s")
 
     extra = {}
     if args.only == "all":
         for name, S in (("longctx", 32), ("qwen32b", args.splits)):
-            wk = W.WORKLOADS[name]
-            b = DecodeBench(torch, tq, wk, S)
-            m = b.time_steps(max(21, args.steps // 4), max(6, args.warmup // 4))
-            s1 = b.time_stage1(20)
-            d = b.time_decode(30)
-            extra[name] = {"preset": wk.preset, "ms_per_step": m, "step_gbs": b.bytes_read / (m * 1e-3) / 1e9,
-                           "ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
-                           "decode_frac_hbm": b.bytes_read / (d * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "num_kv_splits": S,
-                           "bytes_read": b.bytes_read}
-            log(f"[{name}] step {m * 1e3:.1f} us -> {extra[name]['step_gbs']:.0f} GB/s; decode call {d * 1e3:.1f} us "
-                f"-> {extra[name]['decode_gbs']:.0f} GB/s")
-            del b
-            torch.cuda.empty_cache()
+            extra[name] = decode_leg(torch, tq, W.WORKLOADS[name], S, steps=max(21, args.steps // 4),
+                                     warmup=max(6, args.warmup // 4))
+            extra[name]["stream_read"] = stream_ceiling(torch, extra[name]["bytes_read"])
         extra["store_sweep"] = store_sweep(torch, tq, 50)
         log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items()})}")
         extra["dequant"] = dequant_sweep(torch, tq, 20)
@@ -445,34 +556,17 @@ def main():
         # the same workloads with the cache in the SoA block convention
         soa = {}
         for name, S in (("llama8b", args.splits), ("longctx", 32), ("qwen32b", args.splits)):
-            b = DecodeBench(torch, tq, W.WORKLOADS[name], S, block_layout="soa")
-            s1 = b.time_stage1(30)
-            d = b.time_decode(30)
-            soa[name] = {"ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
-                         "stage1_ms": s1, "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9}
-            log(f"[soa {name}] decode call {d * 1e3:.1f} us -> {soa[name]['decode_gbs']:.0f} GB/s; "
-                f"stage1 {s1 * 1e3:.1f} us")
-            del b
-            torch.cuda.empty_cache()
+            soa[name] = decode_leg(torch, tq, W.WORKLOADS[name], S, block_layout="soa")
         soa["store_sweep"] = store_sweep(torch, tq, 50, "soa")
         soa["dequant"] = dequant_sweep(torch, tq, 20, "soa")
         log(f"[soa store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in soa['store_sweep'].items()})}; "
             f"[soa dequant] {json.dumps({k: round(v['gbs']) for k, v in soa['dequant'].items()})} GB/s")
         extra["soa"] = soa
-        # the further presets (asymmetric pairs, 2-bit) on the llama8b shape
+        # the further presets (asymmetric pairs, 2-bit, Lloyd-Max values) on the llama8b shape
         more = {}
         for preset in MORE_PRESETS:
             wk = W.scaled(W.WORKLOADS["llama8b"], name=f"llama8b/{preset}", preset=preset)
-            b = DecodeBench(torch, tq, wk, args.splits)
-            s1 = b.time_stage1(30)
-            d = b.time_decode(30)
-            more[preset] = {"workload": "llama8b shape", "ms_per_decode_call": d,
-                            "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
-                            "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
-            log(f"[{preset}] llama8b shape: decode call {d * 1e3:.1f} us -> {more[preset]['decode_gbs']:.0f} GB/s; "
-                f"stage1 {s1 * 1e3:.1f} us")
-            del b
-            torch.cuda.empty_cache()
+            more[preset] = decode_leg(torch, tq, wk, args.splits)
         more["store_sweep"] = store_sweep(torch, tq, 50, presets=MORE_PRESETS)
         more["dequant"] = dequant_sweep(torch, tq, 20, presets=MORE_PRESETS)
         log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items()})}; "
@@ -482,62 +576,32 @@ def main():
         h256 = {}
         for preset in HEAD256_PRESETS:
             wk = W.scaled(W.WORKLOADS["hd256"], name=f"hd256/{preset}", preset=preset)
-            b = DecodeBench(torch, tq, wk, args.splits)
-            s1 = b.time_stage1(30)
-            d = b.time_decode(30)
-            h256[preset] = {"workload": "hd256: 64 seqs x 4096 tokens, 16/2 heads, head_dim 256, block 16",
-                            "ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9,
-                            "decode_frac_hbm": b.bytes_read / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, "stage1_ms": s1,
-                            "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
-            log(f"[hd256 {preset}] decode call {d * 1e3:.1f} us -> {h256[preset]['decode_gbs']:.0f} GB/s; "
-                f"stage1 {s1 * 1e3:.1f} us -> {h256[preset]['stage1_gbs']:.0f} GB/s")
-            del b
-            torch.cuda.empty_cache()
+            h256[preset] = decode_leg(torch, tq, wk, args.splits)
         h256["store_sweep"] = store_sweep(torch, tq, 50, presets=HEAD256_PRESETS, head_dim=256)
         h256["dequant"] = dequant_sweep(torch, tq, 20, presets=HEAD256_PRESETS, head_dim=256)
         log(f"[hd256 store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in h256['store_sweep'].items()})}; "
             f"[hd256 dequant] {json.dumps({k: round(v['gbs']) for k, v in h256['dequant'].items()})} GB/s")
         extra["head256"] = h256
-        # the opt-in sparse-V gate at 1e-3 (the pages' threshold) on the three decode workloads
+        # the opt-in sparse-V gate at 1e-3 (the pages' threshold), and with the
+        # softmax scale x4 (attention concentrated on few tokens), gated vs not
         sv = {"value_gate": SPARSE_V_GATE}
         for name, S in (("llama8b", args.splits), ("longctx", 32), ("qwen32b", args.splits)):
-            b = DecodeBench(torch, tq, W.WORKLOADS[name], S, value_gate=SPARSE_V_GATE)
-            s1 = b.time_stage1(30)
-            d = b.time_decode(30)
-            sv[name] = {"ms_per_decode_call": d, "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
-                        "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9}
-            log(f"[sparse-V {name}] decode call {d * 1e3:.1f} us -> {sv[name]['decode_gbs']:.0f} GB/s; "
-                f"stage1 {s1 * 1e3:.1f} us")
-            del b
-            torch.cuda.empty_cache()
-        # concentrated attention (softmax scale x4): most tile pairs fall below the gate
+            sv[name] = decode_leg(torch, tq, W.WORKLOADS[name], S, value_gate=SPARSE_V_GATE)
         for name, S in (("llama8b", args.splits), ("qwen32b", args.splits)):
-            res = {}
-            for gate in (0.0, SPARSE_V_GATE):
-                b = DecodeBench(torch, tq, W.WORKLOADS[name], S, value_gate=gate, scale_mult=4.0)
-                res[gate] = (b.time_stage1(30), b.time_decode(30))
-                del b
-                torch.cuda.empty_cache()
-            sv[f"{name}_scale_x4"] = {"ungated_decode_ms": res[0.0][1], "gated_decode_ms": res[SPARSE_V_GATE][1],
-                                      "ungated_stage1_ms": res[0.0][0], "gated_stage1_ms": res[SPARSE_V_GATE][0]}
-            log(f"[sparse-V {name}, softmax scale x4] decode call {res[0.0][1] * 1e3:.1f} us ungated, "
-                f"{res[SPARSE_V_GATE][1] * 1e3:.1f} us gated")
+            sv[f"{name}_scale_x4"] = {
+                "ungated": decode_leg(torch, tq, W.WORKLOADS[name], S, scale_mult=4.0),
+                "gated": decode_leg(torch, tq, W.WORKLOADS[name], S, value_gate=SPARSE_V_GATE, scale_mult=4.0)}
         extra["sparse_v"] = sv
         # sliding window + attention sinks: long context with an 8192-token window
         wk = W.WORKLOADS["longctx"]
-        b = DecodeBench(torch, tq, wk, 32, sliding_window=8192,
-                        sinks=np.random.default_rng(0).uniform(-2, 6, wk.num_q_heads))
-        s1 = b.time_stage1(30)
-        d = b.time_decode(30)
-        extra["window_sinks"] = {"workload": "longctx, sliding_window 8192, per-head sinks", "ms_per_decode_call": d,
-                                 "decode_gbs": b.bytes_read / (d * 1e-3) / 1e9, "stage1_ms": s1,
-                                 "stage1_gbs": b.bytes_read / (s1 * 1e-3) / 1e9, "bytes_read": b.bytes_read}
-        log(f"[window+sinks] longctx W=8192: decode call {d * 1e3:.1f} us -> "
-            f"{extra['window_sinks']['decode_gbs']:.0f} GB/s; stage1 {s1 * 1e3:.1f} us")
-        del b
-        torch.cuda.empty_cache()
+        extra["window_sinks"] = decode_leg(torch, tq, wk, 32, sliding_window=8192,
+                                           sinks=np.random.default_rng(0).uniform(-2, 6, wk.num_q_heads))
+        extra["window_sinks"]["workload"] = "longctx, sliding_window 8192, per-head sinks"
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    s1 = head["stage1_us"]["median"]
+    st1_gbs = head["bytes_read"] / (s1 * 1e-6) / 1e9
+    dec = head["decode_call_us"]["median"]
     line = {
         "metric": "TQ decode-attn effective HBM GB/s (% of peak) + store Mtok/s, k8v4/3bit_nc",
         "value": gbs,
@@ -553,12 +617,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama8b: k8v4 decode step, 32 seqs x 4096 tokens, 32/8 heads, head_dim 128, block 16",
                    "global_batch": w.batch, "seq_len": int(w.seq_len), "num_kv_splits": args.splits,
-                   "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head_bytes,
-                   "decode_call_us": dec_ms * 1e3, "decode_call_gbs": dec_gbs,
-                   "decode_call_frac_hbm_peak": dec_gbs / HBM_PEAK_GBS},
+                   "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head["bytes_read"],
+                   "step_us": head["step_us"], "decode_call_us": head["decode_call_us"],
+                   "decode_call_gbs": head["decode_gbs"], "decode_call_frac_hbm_peak": head["decode_frac_hbm"],
+                   "decode_call_frac_stream_read": head["decode_gbs"] / stream["gbs_median"]},
         "roofline": {"bound": "hbm", "achieved": st1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": st1_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(), "kernel": "tq_decode_stage1_kernel<k8v4>",
-                     "stage1_us": st1_ms * 1e3},
+                     "frac": st1_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "tq_decode_stage1_kernel<k8v4>", "stage1_us": head["stage1_us"],
+                     "stream_read_gbs": stream["gbs_median"], "frac_of_stream_read": st1_gbs / stream["gbs_median"],
+                     "stream_read": stream},
         "cpu_baseline": cpu,
         "extra": extra,
     }

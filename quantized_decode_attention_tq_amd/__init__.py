@@ -24,7 +24,9 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EPRESET, TQ_EHEADDIM, TQ_EBLOCK, TQ_EGQA, TQ_EWORKSPACE, TQ_EDTYPE, TQ_EHIP, TQ_EUNSUPPORTED = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
-PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc")
+#: every preset of include/tq.h, in preset-id order
+PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc", "turboquant_k8v3",
+           "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
 
 #: every symbol include/tq.h declares
 ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init",

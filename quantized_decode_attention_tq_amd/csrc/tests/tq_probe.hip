@@ -81,18 +81,30 @@ __global__ void cvt_fp8_kernel(const uint32_t* in, uint32_t* out, int n) {
   }
 }
 
-// Streaming read: grid-stride 16-byte loads over n16 chunks; the xor of
-// everything read goes to out[blockIdx] so no load is dead.
-__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ in, int64_t n16,
-                                                          uint32_t* __restrict__ out) {
+// Streaming read, the ceiling the decode's cache read is compared with:
+// workgroup i reads the contiguous 16-byte chunks [i * chunk16, (i + 1) *
+// chunk16) of the buffer with non-temporal loads, four in flight per lane;
+// the xor of everything read decides a store that never happens, so no load
+// is dead.  (64 KB per workgroup measured fastest on the MI355X: 6.25 TB/s on
+// 205 MB, 6.7 TB/s on 1 GB; 256 KB and 1 MB pieces were 12-28% slower on 205 MB.)
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ in, int64_t chunk16,
+                                                          int64_t n16, uint32_t* __restrict__ out) {
   uint32_t x = 0;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const u32x4 v = __builtin_nontemporal_load(in + i);
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk16;
+  const int64_t e = b0 + chunk16 < n16 ? b0 + chunk16 : n16;
+  int64_t i = b0 + threadIdx.x;
+  for (; i + 3 * 256 < e; i += 4 * 256) {
+    const u32x4 a = __builtin_nontemporal_load(in + i);
+    const u32x4 b = __builtin_nontemporal_load(in + i + 256);
+    const u32x4 c = __builtin_nontemporal_load(in + i + 512);
+    const u32x4 d = __builtin_nontemporal_load(in + i + 768);
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
-  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
-  if ((threadIdx.x & 63) == 0) atomicXor(out + blockIdx.x, x);
+  for (; i < e; i += 256) {
+    const u32x4 a = __builtin_nontemporal_load(in + i);
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (x == 0x9E3779B9u) out[blockIdx.x] = x;
 }
 
 // Plain copy of n16 16-byte chunks.
@@ -184,11 +196,16 @@ int tq_probe_cvt_fp8_f16(const uint32_t* in, uint32_t* out, int n) {
   return finish();
 }
 
-// Streaming read of bytes (multiple of 16) from a device buffer; out: device
-// uint32 [blocks]; asynchronous on `stream` (timed by the caller).
-int tq_probe_stream_read(const void* in, int64_t bytes, uint32_t* out, int blocks, void* stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(in), bytes / 16, out);
+// Streaming read of bytes (multiple of 16) from a device buffer in pieces
+// of chunk bytes (a multiple of 16) per workgroup; out: device uint32 with at
+// least ceil(bytes / chunk) entries (written only in a case that does not
+// occur); asynchronous on `stream` (timed by the caller).
+int tq_probe_stream_read(const void* in, int64_t bytes, int64_t chunk, uint32_t* out, void* stream) {
+  if (bytes <= 0 || chunk <= 0 || bytes % 16 || chunk % 16) return -1;
+  const int64_t blocks = (bytes + chunk - 1) / chunk;
+  if (blocks > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(in), chunk / 16, bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 

@@ -295,10 +295,17 @@ __global__ __launch_bounds__(kThreads) void tq_store_kernel(StoreArgs a) {
   const float zf = __half2float(z16);
   const float sf = __half2float(s16);
   if (sf != 0.f) {
-    const float inv = __fdiv_rn(1.0f, sf);
+    // code = floor((v - zero) / scale + 1/2), decided in fp32 through the
+    // reciprocal of the scale, taken 2^-22 high: v, zero and scale are short
+    // binary numbers, so quotients exactly at a half-integer are common, and
+    // the raised reciprocal puts them strictly above it, rounding up as the
+    // definition does.  A quotient within about x * 2^-21 below a
+    // half-integer may round up as well (one step, next to the decision
+    // boundary).
+    const float inv = __fmul_rn(__fdiv_rn(1.0f, sf), 1.0f + 0x1p-22f);
 #pragma unroll
     for (int i = 0; i < kDpl; ++i) {
-      // three fp32 roundings, as defined: no fused multiply-add here
+      // fp32 roundings as written: no fused multiply-add here
 #pragma clang fp contract(off)
       const float q = (v[i] - zf) * inv;
       float r = q + 0.5f;

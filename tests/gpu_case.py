@@ -52,7 +52,7 @@ def gpu_tables(lay_c, signs):
 # ------------------------------------------------------------------ store
 
 
-def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0):
+def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0, n_total=None):
     """got/want: (rows, code bytes + 2) = packed Lloyd-Max codes then the
     fp16 norm of the same rows; rows: (rows, D) float64 inputs.  A code may
     differ only next to a bucket boundary (|u - b| < 1e-6, by one), at most
@@ -70,7 +70,8 @@ def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0
         dist = np.min(np.abs(u[:, None] - np.asarray(bound, np.float64)[None, :]), axis=1)
         assert np.all(dist < BOUNDARY_EPS), f"code mismatch away from a boundary: {dist.max()}"
         assert np.all(np.abs(cg[bad[:, 0], bad[:, 1]] - cw[bad[:, 0], bad[:, 1]]) == 1)
-    assert len(bad) <= max(MISMATCH_FRAC * cg.size, min_allowed), f"{len(bad)} code mismatches of {cg.size}"
+    n_total = cg.size if n_total is None else n_total
+    assert len(bad) <= max(MISMATCH_FRAC * n_total, min_allowed), f"{len(bad)} code mismatches of {n_total}"
     gg = got[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     gw = want[:, nb : nb + 2].copy().view(np.float16).astype(np.float64)[:, 0]
     for r in np.unique(bad[:, 0]) if len(bad) else []:
@@ -81,7 +82,7 @@ def _compare_codes(lay, bits, got, want, rows, R, cent, bound, nc, min_allowed=0
     return len(bad)
 
 
-def _compare_value_codes(lay, got, want, values, min_allowed=0):
+def _compare_value_codes(lay, got, want, values, min_allowed=0, n_total=None):
     """got/want: (rows, value data + 4) = packed uniform value codes, fp16
     scale, fp16 zero of the same rows; values: (rows, D) float64 inputs.
     Scale and zero are bit-exact.  A code may differ from the oracle's exact
@@ -102,7 +103,8 @@ def _compare_value_codes(lay, got, want, values, min_allowed=0):
         dist = np.abs(x - (np.floor(x) + 0.5))
         assert np.all(dist < BOUNDARY_EPS * ((1 << vb) - 1)), f"value code mismatch away from a tie: {dist.max()}"
         assert np.all(np.abs(cg[r, c] - cw[r, c]) == 1)
-    assert len(bad) <= max(MISMATCH_FRAC * cg.size, min_allowed), f"{len(bad)} value code mismatches of {cg.size}"
+    n_total = cg.size if n_total is None else n_total
+    assert len(bad) <= max(MISMATCH_FRAC * n_total, min_allowed), f"{len(bad)} value code mismatches of {n_total}"
     return len(bad)
 
 
@@ -110,9 +112,15 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32,
     """got/want: (rows, slot) bytes of the same rows; keys / values: (rows, D)
     float64 inputs of those rows.  Lloyd-Max codes (MSE keys, Lloyd-Max
     values) follow _compare_codes, uniform value codes _compare_value_codes;
-    FP8 keys, value scale and zero and padding are bit-exact.  Returns the
-    number of code mismatches."""
+    FP8 keys, value scale and zero and padding are bit-exact.  Only rows
+    whose bytes differ are decoded; the mismatch cap counts all rows' codes.
+    Returns the number of code mismatches."""
     assert got.shape == want.shape
+    diff = np.nonzero(np.any(got != want, axis=1))[0]
+    if len(diff) == 0:
+        return 0
+    n_total = got.shape[0] * lay.head_dim
+    got, want, keys, values = got[diff], want[diff], keys[diff], values[diff]
     R = O.rotation(np.asarray(signs, np.float64)) if O.needs_rotation(lay) else None
     kd, vo, vd = lay.key_data_bytes, lay.key_packed_size, lay.value_data_bytes
     n = 0
@@ -120,14 +128,15 @@ def compare_slots(lay, got: np.ndarray, want: np.ndarray, keys, signs, c32, b32,
         np.testing.assert_array_equal(got[:, :kd], want[:, :kd])
     else:
         n += _compare_codes(lay, lay.key_bits, got[:, : kd + 2], want[:, : kd + 2], keys, R, c32, b32,
-                            lay.norm_correction, min_allowed)
+                            lay.norm_correction, min_allowed, n_total)
     if lay.value_lm:
         vc32, vb32 = O.value_tables(lay)
         n += _compare_codes(lay, lay.value_bits, got[:, vo : vo + vd + 2], want[:, vo : vo + vd + 2], values, R,
-                            vc32, vb32, True, min_allowed)
+                            vc32, vb32, True, min_allowed, n_total)
         np.testing.assert_array_equal(got[:, vo + vd + 2 :], want[:, vo + vd + 2 :])
     else:
-        n += _compare_value_codes(lay, got[:, vo : vo + vd + 4], want[:, vo : vo + vd + 4], values, min_allowed)
+        n += _compare_value_codes(lay, got[:, vo : vo + vd + 4], want[:, vo : vo + vd + 4], values, min_allowed,
+                                  n_total)
         np.testing.assert_array_equal(got[:, vo + vd + 4 :], want[:, vo + vd + 4 :])
     return n
 

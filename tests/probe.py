@@ -28,7 +28,7 @@ def lib():
                        ("tq_probe_cvt_fp8_f16", [vp, vp, ctypes.c_int]),
                        ("tq_probe_permlane_swap", [vp, vp]),
                        ("tq_probe_fp8_encode", [vp, vp, ctypes.c_int]),
-                       ("tq_probe_stream_read", [vp, ctypes.c_int64, vp, ctypes.c_int, vp]),
+                       ("tq_probe_stream_read", [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]),
                        ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp])):
         f = getattr(L, name)
         f.restype = ctypes.c_int

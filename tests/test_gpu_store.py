@@ -63,21 +63,24 @@ def test_store_parity_small(preset, dtype):
     check_store_parity(preset, dtype, 1237, 3, 16, 11, 13)
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("preset", O.PRESETS)
-def test_store_parity_full_sweep_sampled(preset):
-    """The store sweep at full size (65536 tokens x 8 KV heads, bs 32), as
-    the benchmark launches it; the oracle checks 4096 sampled rows."""
+def test_store_parity_full_sweep(preset):
+    """The store sweep at full size (65536 tokens x 8 KV heads, bs 32, random
+    slot mapping), as the benchmark launches it: every slot against the
+    oracle's encoding of the same rows."""
     s = W.STORE_WORKLOAD
     lay, K, V, slots, got, signs, c32, b32, shape, _ = _run_store(preset, s["num_tokens"], s["num_kv_heads"],
                                                                  s["block_size"], s["dtype"], s["seed"])
-    rng = np.random.default_rng(99)
-    tok = rng.choice(s["num_tokens"], 512, replace=False)
-    Kr = O.widen(K[tok], s["dtype"]).reshape(-1, G.D)
-    Vr = O.widen(V[tok], s["dtype"]).reshape(-1, G.D)
     R = O.rotation(signs.astype(np.float64)) if O.needs_rotation(lay) else None
-    want = O.encode_slots(lay, Kr, Vr, R, c32, b32)
-    rows = got[slots[tok] // shape[1], slots[tok] % shape[1]].reshape(-1, lay.slot_size_aligned)
-    G.compare_slots(lay, rows, want, Kr, signs, c32, b32, Vr)
+    rows = got[slots // shape[1], slots % shape[1]].reshape(-1, lay.slot_size_aligned)
+    Kr = O.widen(K, s["dtype"]).reshape(-1, G.D)
+    Vr = O.widen(V, s["dtype"]).reshape(-1, G.D)
+    chunk = 65536
+    want = np.concatenate([O.encode_slots(lay, Kr[i : i + chunk], Vr[i : i + chunk], R, c32, b32)
+                           for i in range(0, Kr.shape[0], chunk)])
+    n = G.compare_slots(lay, rows, want, Kr, signs, c32, b32, Vr)
+    G.log(f"store sweep {preset}: {rows.shape[0]} slots, {n} codes differ at decision boundaries")
 
 
 def test_store_edge_cases():
