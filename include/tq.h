@@ -21,10 +21,14 @@
  *     and no memory is touched.
  *   - Ownership: every pointer belongs to the caller.  "device" pointers must
  *     be GPU memory visible to the current HIP device; "host" pointers are
- *     ordinary CPU memory.  The library allocates nothing, keeps no global
- *     state, never synchronizes the stream and never reads device memory
- *     from the host, so calls are reentrant and can be captured in a HIP
- *     graph (no hipMemset is issued).
+ *     ordinary CPU memory.  The library allocates nothing, never
+ *     synchronizes the stream and never reads device memory from the host,
+ *     so calls can be captured in a HIP graph (no hipMemset is issued).  Its
+ *     only process-wide state is one-time set-up cached per device (the
+ *     stage-1 kernels' shared-memory limit, set with hipFuncSetAttribute the
+ *     first time each kernel runs on a device; the scratch address of
+ *     tq_decode_attention_noalloc), kept under a lock: calls from several
+ *     threads are safe, and calls that share no buffers are independent.
  *   - stream: a hipStream_t passed as void* (NULL = the default stream).
  *     Kernels are enqueued on it; results are valid once the stream has
  *     reached them.
@@ -328,6 +332,32 @@ int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype
 int tq_decode_stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits,
                      const float* sinks, const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                      float* lse_out, void* stream);
+
+/* Decode attention that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It makes the same
+ * two launches as tq_decode_attention, with the same results, but the stage-1
+ * sequence table and partial rows live in a scratch array that libtq holds
+ * in device memory for the life of the process: TQ_NOALLOC_SCRATCH_BYTES on
+ * each device the library runs on (a file-scope device array; its address
+ * is looked up once per device, on the first call with that device current,
+ * and cached).  Arguments: as for tq_decode_attention without workspace and
+ * workspace_bytes.  Errors: as for tq_decode_attention, and TQ_EWORKSPACE
+ * (nothing launched) when tq_decode_workspace_bytes(batch, num_q_heads,
+ * head_dim, num_kv_splits) exceeds TQ_NOALLOC_SCRATCH_BYTES; TQ_EHIP if the
+ * scratch address cannot be obtained.  Nothing in the scratch needs to start
+ * at zero (stage 1 writes every entry stage 2 reads).  Every call on a GPU
+ * shares that GPU's scratch and leaves the last call's contents in it: calls
+ * that overlap on one GPU (different streams or threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * No hipMalloc, hipFree or allocating library routine is called. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int tq_decode_attention_noalloc(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
+                                int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
+                                const int32_t* seq_lens, const float* signs, const float* centroids, float scale,
+                                int32_t num_kv_splits, int32_t sliding_window, float value_gate, const float* sinks,
+                                void* out, int32_t out_dtype, float* lse_out, void* stream);
 
 /* Dequantize the cached prefix of one sequence back to dense K and V in the
  * original space, the first step of a continuation prefill ([API]

@@ -33,7 +33,7 @@ ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_fr
                "tq_layout_init_ex", "tq_kv_cache_shape",
                "tq_lloyd_max", "tq_wht_signs", "tq_decode_workspace_bytes", "tq_store", "tq_store_validate",
                "tq_decode_attention", "tq_decode_validate", "tq_decode_stage1", "tq_decode_stage2",
-               "tq_dequant_kv", "tq_dequant_validate")
+               "tq_decode_attention_noalloc", "tq_dequant_kv", "tq_dequant_validate")
 
 
 class TQError(RuntimeError):
@@ -89,6 +89,8 @@ def _load():
         "tq_decode_stage1": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp, fp, i32, i32,
                                             fp, vp, sz, vp]),
         "tq_decode_stage2": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, sz, vp, i32, vp, vp]),
+        "tq_decode_attention_noalloc": (ctypes.c_int, [L, vp, i32, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp, vp,
+                                                       fp, i32, i32, fp, vp, vp, i32, vp, vp]),
         "tq_dequant_kv": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64, vp]),
         "tq_dequant_validate": (ctypes.c_int, [L, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, i64]),
     }
@@ -246,6 +248,27 @@ def decode(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centro
                                     workspace.numel() * workspace.element_size(), out.data_ptr(), _dt(out), _ptr(lse),
                                     _stream(stream, query.device)),
            "tq_decode_attention")
+    return out, lse
+
+
+#: bytes of the device scratch tq_decode_attention_noalloc uses (TQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(layout: Layout, query, kv_cache, block_table, seq_lens, signs, centroids, scale: float,
+                   num_kv_splits: int, out, lse=None, stream=None, sliding_window: int = 0, sinks=None,
+                   value_gate: float = 0.0):
+    """tq_decode_attention_noalloc: decode attention into the caller's `out`
+    (and `lse`, optional) with the library's own device scratch; nothing is
+    allocated.  Same arguments as decode otherwise."""
+    B, Hq, Hk, bt_stride = _decode_common(query, kv_cache, block_table)
+    _check(_lib.tq_decode_attention_noalloc(ctypes.byref(layout), query.data_ptr(), _dt(query), B, Hq, Hk,
+                                            kv_cache.data_ptr(), kv_cache.shape[0], kv_cache.shape[1],
+                                            block_table.data_ptr(), bt_stride, seq_lens.data_ptr(), _ptr(signs),
+                                            _ptr(centroids), float(scale), num_kv_splits, int(sliding_window),
+                                            float(value_gate), _ptr(sinks), out.data_ptr(), _dt(out), _ptr(lse),
+                                            _stream(stream, query.device)),
+           "tq_decode_attention_noalloc")
     return out, lse
 
 

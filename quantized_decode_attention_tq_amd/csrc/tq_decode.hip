@@ -29,6 +29,8 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "tq.h"
 #include "tq_bits.h"
@@ -1697,10 +1699,8 @@ template <int P, int TPW, int PACK, int SOA, int GATE>
 int launch_stage1_g(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds, hipStream_t stream) {
   const void* fn = GATE ? reinterpret_cast<const void*>(&tq_decode_stage1_gated_kernel<P, TPW, PACK, SOA>)
                         : reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>);
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [fn] { attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
-  if (attr != hipSuccess) return tq::hip_status(attr);
+  const int st = tq::set_max_lds_once(fn, kMaxLds);
+  if (st != TQ_OK) return st;
   DecodeArgs arg = a;
   float g = gate;
   void* args[] = {&arg, &g};  // the default kernel reads the first only
@@ -1835,6 +1835,55 @@ int hip_status(int e) {
 
 extern "C" const char* tq_last_hip_error(void) { return hipGetErrorString(tq::g_last_hip_error); }
 
+namespace tq {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_setup_mutex;
+std::vector<std::pair<const void*, int>> g_lds_set;  // (kernel, device) pairs already set up
+void* g_scratch_addr[kMaxDevices] = {};             // device address of `scratch`, per device
+}  // namespace
+
+int set_max_lds_once(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  std::lock_guard<std::mutex> lock(g_setup_mutex);
+  for (const auto& kv : g_lds_set)
+    if (kv.first == fn && kv.second == dev) return TQ_OK;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return hip_status(e);
+  g_lds_set.emplace_back(fn, dev);
+  return TQ_OK;
+}
+}  // namespace tq
+
+// Scratch of tq_decode_attention_noalloc: the stage-1 sequence table and
+// partial rows that tq_decode_attention keeps in its caller's workspace.  In
+// host code `scratch` is only a stand-in for the symbol; kernels get the
+// device address looked up below.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of `scratch` on the current device, looked up on the first
+// call with that device current and cached per device.
+int scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return tq::hip_status(e);
+  if (dev < 0 || dev >= tq::kMaxDevices) return TQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(tq::g_setup_mutex);
+  if (!tq::g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return tq::hip_status(e);
+    if (!p) return TQ_EHIP;
+    tq::g_scratch_addr[dev] = p;
+  }
+  *addr = tq::g_scratch_addr[dev];
+  return TQ_OK;
+}
+}  // namespace
+
 extern "C" int tq_decode_stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, int32_t num_kv_heads, const void* kv_cache, int64_t num_blocks,
                                 int32_t block_size, const int32_t* block_table, int32_t block_table_stride,
@@ -1878,4 +1927,30 @@ extern "C" int tq_decode_attention(const tq_layout* layout, const void* query, i
               workspace, s);
   if (st != TQ_OK) return st;
   return stage2(batch, num_q_heads, layout->head_dim, num_kv_splits, sinks, workspace, out, out_dtype, lse_out, s);
+}
+
+extern "C" int tq_decode_attention_noalloc(const tq_layout* layout, const void* query, int32_t q_dtype,
+                                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                           const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                                           const int32_t* block_table, int32_t block_table_stride,
+                                           const int32_t* seq_lens, const float* signs, const float* centroids,
+                                           float scale, int32_t num_kv_splits, int32_t sliding_window,
+                                           float value_gate, const float* sinks, void* out, int32_t out_dtype,
+                                           float* lse_out, void* stream) {
+  // Every argument is checked against the scratch capacity before the
+  // scratch is looked up (a 256-aligned stand-in address takes the place of
+  // the workspace in the host-only check; it is never dereferenced).
+  void* const stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  int st = tq_decode_validate(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, num_blocks,
+                              block_size, block_table, block_table_stride, seq_lens, signs, centroids, num_kv_splits,
+                              sliding_window, value_gate, stand_in, TQ_NOALLOC_SCRATCH_BYTES, out, out_dtype);
+  if (st != TQ_OK || batch == 0) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = stage1(layout, query, q_dtype, batch, num_q_heads, num_kv_heads, kv_cache, block_size, block_table,
+              block_table_stride, seq_lens, signs, centroids, scale, num_kv_splits, sliding_window, value_gate, ws, s);
+  if (st != TQ_OK) return st;
+  return stage2(batch, num_q_heads, layout->head_dim, num_kv_splits, sinks, ws, out, out_dtype, lse_out, s);
 }

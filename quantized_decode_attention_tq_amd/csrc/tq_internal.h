@@ -12,6 +12,11 @@ namespace tq {
 // thread) and maps it to a status.
 int hip_status(int hip_error);
 
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) the first time
+// fn is launched on the current device (cached per (kernel, device) under a
+// lock; later calls return TQ_OK at once).
+int set_max_lds_once(const void* fn, int bytes);
+
 inline bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
 
 // true when *L equals what tq_layout_init produces for (L->preset, L->head_dim)

@@ -238,3 +238,36 @@ def test_dequant_validation_codes():
     assert _dequant_validate(tq.layout_init("turboquant_k3v4_nc", 64)) == tq.TQ_EHEADDIM
     assert _dequant_validate(tq.layout_init("turboquant_k3v4_nc", 256), stride=2048) == tq.TQ_OK
     assert _dequant_validate(L, n=1 << 28, nb=1 << 30) == tq.TQ_EINVAL  # rows beyond 2^31
+
+
+def _noalloc(L, **kw):
+    args = dict(q=A, qd=tq.TQ_BF16, B=4, Hq=32, Hk=8, cache=A, nb=100, bs=16, bt=A, bts=64, sl=A, signs=A, cent=A,
+                S=8, win=0, gate=0.0, sinks=None, out=A, od=tq.TQ_F32, lse=None)
+    args.update(kw)
+    return tq._lib.tq_decode_attention_noalloc(ctypes.byref(L), args["q"], args["qd"], args["B"], args["Hq"],
+                                               args["Hk"], args["cache"], args["nb"], args["bs"], args["bt"],
+                                               args["bts"], args["sl"], args["signs"], args["cent"], 1.0, args["S"],
+                                               args["win"], args["gate"], args["sinks"], args["out"], args["od"],
+                                               args["lse"], None)
+
+
+def test_noalloc_scratch_limit_and_argument_errors():
+    """tq_decode_attention_noalloc checks every argument, and the workspace
+    its launch needs against the scratch it holds (TQ_NOALLOC_SCRATCH_BYTES),
+    on the host before any HIP call: these calls return before touching a
+    device (fake addresses)."""
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    m = re.search(r"#define TQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tq.NOALLOC_SCRATCH_BYTES
+    L = tq.layout_init("turboquant_k3v4_nc")
+    # the largest case that fits and the smallest that does not, for 64 query heads and 8 splits
+    assert tq.decode_workspace_bytes(64, 64, 128, 8) <= tq.NOALLOC_SCRATCH_BYTES
+    assert tq.decode_workspace_bytes(128, 64, 128, 8) > tq.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(L, B=128, Hq=64) == tq.TQ_EWORKSPACE
+    assert _noalloc(L, B=4, Hq=40, S=1024) == tq.TQ_EWORKSPACE
+    assert _noalloc(L, Hq=33) == tq.TQ_EGQA
+    assert _noalloc(L, bs=8) == tq.TQ_EBLOCK
+    assert _noalloc(L, od=7) == tq.TQ_EDTYPE
+    assert _noalloc(L, out=None) == tq.TQ_EINVAL
+    assert _noalloc(L, gate=1.0) == tq.TQ_EINVAL
+    assert _noalloc(L, B=0, q=None, sl=None, bt=None, out=None) == tq.TQ_OK  # nothing to do
