@@ -12,8 +12,8 @@ decode-attention bandwidth: compressed-cache bytes the step reads
 The same bytes over one tq_decode_attention call alone (no store) are
 reported as ``config.decode_call_gbs``.
 
-Timing: the step is captured in a HIP graph three times in a row, once per
-copy of the cache (3 x 411 MB for the headline, so the 256 MB Infinity Cache
+Timing: twelve steps are captured in one HIP graph, rotating over three
+copies of the cache (3 x 411 MB for the headline, so the 256 MB Infinity Cache
 cannot serve a step's reads from the previous one), the way a multi-layer
 decode graph strings layers together; the graph is replayed on torch's
 current stream and K steps are bracketed by events after a synchronize.  The roofline figure times stage-1
@@ -41,6 +41,12 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 N_COPIES = 3
+# Steps (or decode calls) captured in one graph: four passes over the three
+# cache copies, as a stretch of a multi-layer decode graph strings layers
+# together.  Replaying a graph costs a gap of ~8 us on the GPU before its first
+# kernel (measured in a kernel trace: kernels inside a graph start back to
+# back); over 12 calls that is ~0.7 us per call.
+GRAPH_STEPS = 12
 
 
 def log(msg):
@@ -98,7 +104,8 @@ class DecodeBench:
     tokens, queries, tables, workspace."""
 
     def __init__(self, torch, tq, w: W.Workload, num_kv_splits: int, block_layout: str = "aos",
-                 sliding_window: int = 0, sinks=None, value_gate: float = 0.0, scale_mult: float = 1.0):
+                 sliding_window: int = 0, sinks=None, value_gate: float = 0.0, scale_mult: float = 1.0,
+                 warm: bool = True):
         self.torch, self.tq, self.w = torch, tq, w
         self.S = num_kv_splits
         self.window = sliding_window
@@ -145,8 +152,9 @@ class DecodeBench:
         self.bytes_read = int(seen.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
         self.sinks = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
         torch.cuda.synchronize()
-        it = iter(range(1 << 30))
-        warm_gpu(torch, lambda: self.step(next(it) % N_COPIES))
+        if warm:
+            it = iter(range(1 << 30))
+            warm_gpu(torch, lambda: self.step(next(it) % N_COPIES))
 
     def store(self, i):
         self.tq.store(self.lay, self.knew, self.vnew, self.snew, self.caches[i], self.tab.signs, self.tab.centroids,
@@ -166,9 +174,9 @@ class DecodeBench:
         self.stage2()
 
     def graphs(self):
-        """One graph holding N_COPIES consecutive steps (one per cache copy),
-        like a stretch of a multi-layer decode graph, plus one-step graphs for
-        a remainder."""
+        """One graph holding GRAPH_STEPS consecutive steps (cache copy i % 3
+        for step i), like a stretch of a multi-layer decode graph, plus
+        one-step graphs for a remainder."""
         torch = self.torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -179,8 +187,8 @@ class DecodeBench:
         torch.cuda.synchronize()
         g_all = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_all):
-            for i in range(N_COPIES):
-                self.step(i)
+            for i in range(GRAPH_STEPS):
+                self.step(i % N_COPIES)
         singles = []
         for i in range(N_COPIES):
             g = torch.cuda.CUDAGraph()
@@ -192,31 +200,31 @@ class DecodeBench:
 
     def time_steps(self, steps, warmup):
         """ms per step over exactly `steps` steps (graph replays), then the
-        per-step spread over DIST_REPLAYS further replays of the 3-step graph."""
+        per-step spread over DIST_REPLAYS further replays of the step graph."""
         torch = self.torch
         g_all, singles = self.graphs()
-        for _ in range(max(1, warmup // N_COPIES)):
+        for _ in range(max(1, warmup // GRAPH_STEPS)):
             g_all.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(steps // N_COPIES):
+        for _ in range(steps // GRAPH_STEPS):
             g_all.replay()
-        for i in range(steps % N_COPIES):
-            singles[i].replay()
+        for i in range(steps % GRAPH_STEPS):
+            singles[i % N_COPIES].replay()
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        return ms, spread(torch, g_all.replay, DIST_REPLAYS, N_COPIES)
+        return ms, spread(torch, g_all.replay, DIST_REPLAYS, GRAPH_STEPS)
 
     def decode_graph(self):
-        """One graph of tq_decode_attention calls (stage 1 + stage 2, no
-        store), one per cache copy."""
+        """One graph of GRAPH_STEPS tq_decode_attention calls (stage 1 +
+        stage 2, no store), rotating over the cache copies."""
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(N_COPIES):
-                self.stage1(i)
+            for i in range(GRAPH_STEPS):
+                self.stage1(i % N_COPIES)
                 self.stage2()
         g.replay()
         torch.cuda.synchronize()
@@ -224,9 +232,9 @@ class DecodeBench:
 
     def time_decode(self, reps=None):
         """Per tq_decode_attention call: median / p10 / p90 (ms) over `reps`
-        replays of the graph of one call per cache copy."""
+        replays of the decode graph (GRAPH_STEPS calls each)."""
         g = self.decode_graph()
-        return spread(self.torch, g.replay, reps or DIST_REPLAYS, N_COPIES)
+        return spread(self.torch, g.replay, reps or DIST_REPLAYS, GRAPH_STEPS)
 
     def time_stage1(self, launches=None):
         """Stage-1 kernel duration: median / p10 / p90 (ms) of `launches`
@@ -418,10 +426,10 @@ def calibrate_copy(torch, mib: int = 512, reps: int = 5):
 
 
 def profile_stage1(torch, tq, name, launches, splits):
-    """Only stage-1 launches of one decode workload (inputs set up and the GPU
-    warmed first), for rocprofv3 counter runs."""
+    """Only stage-1 launches of one decode workload (after the inputs are
+    stored; no warm-up launches), for rocprofv3 counter runs."""
     S = {"longctx": 32}.get(name, splits)
-    b = DecodeBench(torch, tq, W.WORKLOADS[name], S)
+    b = DecodeBench(torch, tq, W.WORKLOADS[name], S, warm=False)
     torch.cuda.synchronize()
     for i in range(launches):
         b.stage1(i % N_COPIES)

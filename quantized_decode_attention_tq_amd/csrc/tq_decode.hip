@@ -1154,19 +1154,26 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // GATE: the body honours the sparse-V gate vgate (> 0, on exp(s - running
 // max)); the default kernel is built without its code and keeps a single
 // argument, the gated one takes the gate as a second.
-template <int P, int TPW, int PACK, int SOA, int GATE>
+//
+// FIX: the launch geometry of 8 KV heads at head_dim 128 in combined slots
+// (G = Hk = 8, one phase, a two-entry ring of contiguous 16-row tile
+// images), fixed at compile time: tile-image offsets fold into the LDS read
+// instructions, and the main loop, unrolled over the two ring entries, needs
+// no entry arithmetic and no variable wait counts.
+template <int P, int TPW, int PACK, int SOA, int GATE, int FIX = 0>
 __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   using T = Preset<P>;
   static_assert(T::kNh == 1 || (TPW == 1 && PACK == 0), "head_dim 256: one tile per wave");
+  static_assert(!FIX || (T::kNh == 1 && SOA == 0), "fixed geometry: head_dim 128, combined slots");
   constexpr int kOut = 32 * T::kNh;  // output dims per lane (32 of each half)
   extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = a.G, NP = a.P;
+  const int G = FIX ? 8 : a.G, NP = FIX ? 1 : a.P;
   const int Q = NP * TPW;  // tiles per super-tile
   const int hh = w % G, ph = w / G;
-  const int Hk = a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
+  const int Hk = FIX ? 8 : a.num_kv_heads, Hq = a.num_q_heads, g = a.group;
   int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int hgp = lg % (Hk / G);
   lg /= Hk / G;
@@ -1212,7 +1219,7 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   ImageGeom geo;
   geo.row = static_cast<uint32_t>(Hk * T::kSlot);
   geo.base = static_cast<uint32_t>(hgp * G * T::kSlot);
-  geo.contiguous = a.contiguous != 0;
+  geo.contiguous = FIX ? true : a.contiguous != 0;
   const uint32_t piece = static_cast<uint32_t>(G * T::kSlot);
   // chunks covering row piece r: from its start aligned down to 16 bytes up
   // to its end aligned up, so no chunk crosses the end of its cache block
@@ -1234,7 +1241,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   };
 
   // ---- ring: this wave's DMA slots of each super-tile ----
-  const int spt = a.spt;
+  constexpr int kSpt8 = (8 * T::kSlot + 63) / 64;  // 1 KB slots of a fixed-geometry tile image
+  const int spt = FIX ? kSpt8 : a.spt;
   Ring<P, SOA> ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
   ring.entry = static_cast<uint32_t>(Q * spt) * 1024u;
@@ -1291,7 +1299,7 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
       ring.off[k] = ((geo.base + r * geo.row) & ~15u) + 16 * (c - first);
     }
   }
-  const int R = a.ring_depth;
+  const int R = FIX ? 2 : a.ring_depth;
   const int bs_log2 = 31 - __clz(a.block_size);
   const int64_t blk_bytes = static_cast<int64_t>(a.block_size) * geo.row;
   // Block ids are read with scalar loads (the table is constant while the
@@ -1399,48 +1407,72 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   bool have_pend = false;
 
   // ---- main loop: wait for super-tile u, release the entry of u-1, refill
-  // it with u+R-1, compute this wave's tile of u from LDS ----
-  int entry = 0;
-  for (int u = 0; u < nst; ++u) {
-    vm_wait(TPW * ring.my_loads * min(R - 2, nst - 1 - u));
-    wg_barrier();
-    if (u + R - 1 < nst) {
-      issue(u + R - 1, entry == 0 ? R - 1 : entry - 1, blk_next);
-      blk_next = blocks_of(u + R);
-    }
+  // it with u+R-1, compute this wave's tile(s) of u from the entry at ent ----
+  auto compute = [&](int u, const uint8_t* ent) {
     if constexpr (PACK != 0) {
       // the wave's two tiles of the super-tile, scored together
       const int t = t_begin + u * Q + ph * TPW;
       if (t < t_end) {
-        const uint8_t* img =
-            tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
+        const uint8_t* img = ent + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
         score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, bq,
                                   min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
                                   max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), vgate, sm, acc);
       }
     } else {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int t = t_begin + u * Q + ph * TPW + j;
-      if (t < t_end) {
-        TileRegs<P> r;
-        const uint8_t* img =
-            tq_ring + static_cast<uint32_t>(entry) * ring.entry + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
-        load_tile<P, SOA>(img, off, r);
-        PendingTile<P> cur;
-        score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, sm,
-                           acc, pend, have_pend, cur);
-        if (have_pend) {
-          if (!GATE || pair_has_values(pend, cur)) accumulate_pair<P>(pend, cur, lv, acc);
-          have_pend = false;
-        } else {
-          pend = cur;
-          have_pend = true;
+      for (int j = 0; j < TPW; ++j) {
+        const int t = t_begin + u * Q + ph * TPW + j;
+        if (t < t_end) {
+          TileRegs<P> r;
+          const uint8_t* img = ent + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
+          load_tile<P, SOA>(img, off, r);
+          PendingTile<P> cur;
+          score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, sm,
+                             acc, pend, have_pend, cur);
+          if (have_pend) {
+            if (!GATE || pair_has_values(pend, cur)) accumulate_pair<P>(pend, cur, lv, acc);
+            have_pend = false;
+          } else {
+            pend = cur;
+            have_pend = true;
+          }
         }
       }
     }
+  };
+  if constexpr (FIX != 0) {
+    // two entries: super-tile u in entry u & 1; this wave's loads of u + 1 are
+    // its only ones in flight once u has arrived
+    constexpr uint32_t kEntry = static_cast<uint32_t>(TPW * kSpt8) * 1024u;
+    for (int u = 0; u < nst; u += 2) {
+      vm_wait(0);
+      wg_barrier();
+      if (u + 1 < nst) {
+        issue(u + 1, 1, blk_next);
+        blk_next = blocks_of(u + 2);
+      }
+      compute(u, tq_ring);
+      if (u + 1 >= nst) break;
+      vm_wait(0);
+      wg_barrier();
+      if (u + 2 < nst) {
+        issue(u + 2, 0, blk_next);
+        blk_next = blocks_of(u + 3);
+      }
+      compute(u + 1, tq_ring + kEntry);
     }
-    entry = entry + 1 == R ? 0 : entry + 1;
+  } else {
+    int entry = 0;
+    for (int u = 0; u < nst; ++u) {
+      vm_wait(TPW * ring.my_loads * min(R - 2, nst - 1 - u));
+      wg_barrier();
+      if (u + R - 1 < nst) {
+        issue(u + R - 1, entry == 0 ? R - 1 : entry - 1, blk_next);
+        blk_next = blocks_of(u + R);
+      }
+      compute(u, tq_ring + static_cast<uint32_t>(entry) * ring.entry);
+      entry = entry + 1 == R ? 0 : entry + 1;
+    }
   }
 
   if (have_pend) {  // an odd tile out: pair it with an empty one
@@ -1552,15 +1584,15 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   }
 }
 
-template <int P, int TPW, int PACK, int SOA>
+template <int P, int TPW, int PACK, int SOA, int FIX>
 __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_kernel(DecodeArgs a) {
-  stage1_body<P, TPW, PACK, SOA, 0>(a, 0.f);
+  stage1_body<P, TPW, PACK, SOA, 0, FIX>(a, 0.f);
 }
 
-template <int P, int TPW, int PACK, int SOA>
+template <int P, int TPW, int PACK, int SOA, int FIX>
 __global__ __launch_bounds__(512, Preset<P>::kNh == 2 ? 2 : 4) void tq_decode_stage1_gated_kernel(DecodeArgs a,
                                                                                                    float value_gate) {
-  stage1_body<P, TPW, PACK, SOA, 1>(a, value_gate);
+  stage1_body<P, TPW, PACK, SOA, 1, FIX>(a, value_gate);
 }
 
 // ---------------------------------------------------------------- stage 2
@@ -1581,7 +1613,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // running (max, sum, output) combine through LDS) when rows have many
 // units; otherwise each wave of the workgroup takes its own row (kW = 1).
 template <int kW, int NH>
-__global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
+__global__ __launch_bounds__(kW > 4 ? 64 * kW : 256) void tq_decode_stage2_kernel(const int32_t* __restrict__ table,
                                                                const float* __restrict__ part, int Hq, int rows,
                                                                void* out, int out_dtype, float* lse_out,
                                                                const float* __restrict__ sinks) {
@@ -1695,10 +1727,10 @@ __global__ __launch_bounds__(256) void tq_decode_stage2_kernel(const int32_t* __
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int P, int TPW, int PACK, int SOA, int GATE>
+template <int P, int TPW, int PACK, int SOA, int GATE, int FIX>
 int launch_stage1_g(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds, hipStream_t stream) {
-  const void* fn = GATE ? reinterpret_cast<const void*>(&tq_decode_stage1_gated_kernel<P, TPW, PACK, SOA>)
-                        : reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA>);
+  const void* fn = GATE ? reinterpret_cast<const void*>(&tq_decode_stage1_gated_kernel<P, TPW, PACK, SOA, FIX>)
+                        : reinterpret_cast<const void*>(&tq_decode_stage1_kernel<P, TPW, PACK, SOA, FIX>);
   const int st = tq::set_max_lds_once(fn, kMaxLds);
   if (st != TQ_OK) return st;
   DecodeArgs arg = a;
@@ -1708,11 +1740,20 @@ int launch_stage1_g(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds
       hipLaunchKernel(fn, dim3(static_cast<unsigned>(nblocks)), dim3(64 * a.G * a.P), args, lds, stream));
 }
 
-// The sparse-V gate takes its own kernels.
+// The sparse-V gate takes its own kernels; 8 KV heads at head_dim 128 in
+// combined slots with a two-entry ring take the fixed-geometry ones.
 template <int P, int TPW, int PACK, int SOA>
 int launch_stage1_t(const DecodeArgs& a, float gate, int64_t nblocks, size_t lds, hipStream_t stream) {
-  return gate > 0.f ? launch_stage1_g<P, TPW, PACK, SOA, 1>(a, gate, nblocks, lds, stream)
-                    : launch_stage1_g<P, TPW, PACK, SOA, 0>(a, gate, nblocks, lds, stream);
+  constexpr bool kCanFix = Preset<P>::kNh == 1 && SOA == 0;
+  const bool fix = kCanFix && a.G == 8 && a.num_kv_heads == 8 && a.P == 1 && a.ring_depth == 2 &&
+                   a.contiguous != 0 && a.spt == (8 * Preset<P>::kSlot + 63) / 64;
+  if (fix) {
+    if constexpr (kCanFix)
+      return gate > 0.f ? launch_stage1_g<P, TPW, PACK, SOA, 1, 1>(a, gate, nblocks, lds, stream)
+                        : launch_stage1_g<P, TPW, PACK, SOA, 0, 1>(a, gate, nblocks, lds, stream);
+  }
+  return gate > 0.f ? launch_stage1_g<P, TPW, PACK, SOA, 1, 0>(a, gate, nblocks, lds, stream)
+                    : launch_stage1_g<P, TPW, PACK, SOA, 0, 0>(a, gate, nblocks, lds, stream);
 }
 
 // Two tiles per wave: GQA groups of at most 8 query heads score them packed
@@ -1803,14 +1844,25 @@ int stage2_t(int32_t batch, int32_t num_q_heads, int32_t num_kv_splits, const fl
   const int32_t* table = static_cast<const int32_t*>(workspace);
   const float* part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + tq::table_bytes(batch));
   void* args[] = {&table, &part, &Hq, &rows, &out, &out_dtype, &lse_out, &sinks};
-  // rows of many units share 4 waves; otherwise one wave per row.  The bound
-  // on units per sequence is S_max (balanced units give long sequences more,
-  // so the threshold leaves room).
-  if (tq::max_splits(batch, num_kv_splits) > 24)
-    return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<4, NH>),
-                                          dim3(rows), dim3(256), args, 0, stream));
-  return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<1, NH>),
-                                        dim3((rows + 3) / 4), dim3(256), args, 0, stream));
+  // Rows of many units share several waves (each wave loads up to 16 units
+  // at once, so a row of S_max units takes one round of loads); otherwise
+  // one wave per row, four rows per workgroup.  S_max is the units of a
+  // sequence of a uniform batch (balanced units give long sequences of a
+  // ragged one more, which take further rounds).
+  const int64_t smax = tq::max_splits(batch, num_kv_splits);
+  const void* fn;
+  int waves;
+  if (smax > 64) {
+    fn = reinterpret_cast<const void*>(smax > 128 ? &tq_decode_stage2_kernel<16, NH> : &tq_decode_stage2_kernel<8, NH>);
+    waves = smax > 128 ? 16 : 8;
+  } else if (smax > 16) {
+    fn = reinterpret_cast<const void*>(&tq_decode_stage2_kernel<4, NH>);
+    waves = 4;
+  } else {
+    return tq::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&tq_decode_stage2_kernel<1, NH>),
+                                          dim3((rows + 3) / 4), dim3(256), args, 0, stream));
+  }
+  return tq::hip_status(hipLaunchKernel(fn, dim3(rows), dim3(64 * waves), args, 0, stream));
 }
 
 int stage2(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_kv_splits, const float* sinks,
