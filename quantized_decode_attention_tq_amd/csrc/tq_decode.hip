@@ -537,13 +537,26 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& rr, int hh, uint3
 
 // Online-softmax state of one lane: query head lane % 16; the 4 lane quarters
 // hold disjoint tokens and share the reference maximum m.
+// The MFMA scores come out in units of the lane's query scale: s = f * s'
+// with f = 2^-e chosen per query head when its fp16 operand is built, so the
+// operand's largest value sits in [2^13, 2^14) whatever the query's
+// magnitude (no fp16 overflow for large queries, no subnormals for small
+// ones).  m is in true units; mt = (m + kLazyRescaleLog2) / f is the rescale
+// threshold in the units of the raw scores.
 struct Softmax {
   float m, l, z;  // reference max (log2 domain), sum of p, sum of p * zero
+  float f, fi;    // the lane's score unit 2^-e and its inverse 2^e
+  float mt;       // (m + kLazyRescaleLog2) * fi
 };
 
 // Largest growth of p = 2^(s - m) tolerated before the accumulators are
 // rescaled; p * value_scale must also stay inside fp16.
 constexpr float kLazyRescaleLog2 = 8.0f;
+
+__device__ __forceinline__ void set_max(Softmax& sm, float m) {
+  sm.m = m;
+  sm.mt = (m + kLazyRescaleLog2) * sm.fi;
+}
 
 // A scored tile waiting for its value accumulation: value accumulation runs
 // on 16x16x32 MFMAs over two tiles at once (32 tokens on the reduction
@@ -624,32 +637,32 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
   // four lane quarters exceeds the threshold iff one of the lanes' does.
   const float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
   float p[4], ps[4];
-  bool redo = __any(lmax > sm.m + kLazyRescaleLog2);
+  bool redo = __any(lmax > sm.mt);
   if (!redo) {
     float pmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
       ps[i] = mul_lo16(p[i], sz[i]);
       pmax = fmaxf(pmax, ps[i]);
     }
     redo = __any(pmax > 65504.f);
   }
   if (redo) {  // rescale the accumulators (and the pending tile) to the new maximum
-    const float m_cand = fmaxf(sm.m, quarter_max(lmax));
+    const float m_cand = fmaxf(sm.m, quarter_max(lmax) * sm.f);
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
     for (int n = 0; n < 8 * T::kNh; ++n) acc[n] *= alpha;
     sm.l *= alpha;
     sm.z *= alpha;
-    sm.m = m_cand;
+    set_max(sm, m_cand);
     if (have_pend) {
       const _Float16 ah = static_cast<_Float16>(alpha);
       pend.pv = pend.pv * ah;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
@@ -814,28 +827,28 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
   lmax = fmaxf(lmax, swap8(lmax));  // the head's maximum over both tiles
   float p[4], ps[4];
-  bool redo = __any(lmax > sm.m + kLazyRescaleLog2);
+  bool redo = __any(lmax > sm.mt);
   if (!redo) {
     float pmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
       ps[i] = mul_lo16(p[i], sz[i]);
       pmax = fmaxf(pmax, ps[i]);
     }
     redo = __any(pmax > 65504.f);
   }
   if (redo) {  // rescale the accumulators to the new maximum (same on lanes c and c ^ 8)
-    const float m_cand = fmaxf(sm.m, quarter_max(lmax));
+    const float m_cand = fmaxf(sm.m, quarter_max(lmax) * sm.f);
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] *= alpha;
     sm.l *= alpha;
     sm.z *= alpha;
-    sm.m = m_cand;
+    set_max(sm, m_cand);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sco[i] - sm.m);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
@@ -958,9 +971,21 @@ __device__ __forceinline__ void wht128_quarters(float v[32]) {
 // head_dim 256 the stride 128 between the lane's two halves), everything
 // scaled by softmax scale * log2(e); the values land in fp16 in the order
 // key_operand produces dims.
+// Power-of-two scale fi = 2^e of a query head's fp16 operand, from the
+// lane's largest |value| (before the scale): the head's maximum over its
+// four lane quarters lands in [2^13, 2^14); 1 for an all-zero (or non-finite)
+// head.
+__device__ __forceinline__ float operand_scale(float lane_absmax) {
+  const float mx = quarter_max(lane_absmax);
+  if (!(mx > 0.f) || mx == INFINITY) return 1.f;
+  const int ex = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);  // biased exponent (0: subnormal)
+  const int e = 13 - (max(ex, 1) - 127);                                  // 2^13 <= mx * 2^e < 2^14 (normal mx)
+  return __uint_as_float(static_cast<uint32_t>(min(max(e, -126), 126) + 127) << 23);
+}
+
 template <int P>
 __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk, int h0, int geff, int hl, int q4,
-                                              half8* bq) {
+                                              half8* bq, float& fi) {
   using T = Preset<P>;
   const bool live = hl < geff;
   const uint16_t* qrow =
@@ -983,7 +1008,13 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
         v[hh][16 * h + 2 * j + 1] = widen16(w[j] >> 16, bf);
       }
     }
-    const float qs = live ? a.qscale : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < T::kNh; ++hh)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[hh][j]));
+    fi = operand_scale(live ? amax * a.qscale : 0.f);
+    const float qs = live ? a.qscale * fi : 0.f;
 #pragma unroll
     for (int hh = 0; hh < T::kNh; ++hh)
 #pragma unroll
@@ -1021,7 +1052,14 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
       }
     }
     // 1/sqrt(head_dim) of the rotation
-    const float qs = live ? a.qscale * (T::kNh == 2 ? 0.0625f : 0.08838834764831845f) : 0.f;
+    const float qs0 = a.qscale * (T::kNh == 2 ? 0.0625f : 0.08838834764831845f);
+    float amax = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < T::kNh; ++hh)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[hh][j]));
+    fi = operand_scale(live ? amax * qs0 : 0.f);
+    const float qs = live ? qs0 * fi : 0.f;
 #pragma unroll
     for (int hh = 0; hh < T::kNh; ++hh)
 #pragma unroll
@@ -1352,7 +1390,12 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
 
   // ---- query operand and codebook tables (registers) ----
   half8 bq[4 * T::kNh];
-  query_operand<P>(a, b, hk, h0, geff, hl, q4, bq);
+  float qfi;
+  query_operand<P>(a, b, hk, h0, geff, hl, q4, bq, qfi);
+  if constexpr (PACK != 0) {  // columns 8..15 carry tile B's scores of head c - 8: its units
+    const float fb = swap8(qfi);
+    if (hl >= 8) qfi = fb;
+  }
   // fp16 codebooks for the byte-permute lookups: keys (la, lb), Lloyd-Max
   // values (lv, the value codebook after the key codebook in the table)
   auto lut_bytes = [](const uint32_t* hb, int base, int shift) {
@@ -1399,7 +1442,7 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     off.mm0 = off.sd = off.sm = 0u;
   }
 
-  Softmax sm{-INFINITY, 0.f, 0.f};
+  Softmax sm{-INFINITY, 0.f, 0.f, 1.f / qfi, qfi, -INFINITY};
   f32x4 acc[8 * T::kNh];
 #pragma unroll
   for (int n = 0; n < 8 * T::kNh; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -214,3 +214,24 @@ def test_split_entry_points_match_single_call(preset, S):
     G.check_decode(out2, lse2, ref, rlse, _rows(w))
     np.testing.assert_array_equal(out1, out2)
     np.testing.assert_array_equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("preset", ["turboquant_k8v4", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
+@pytest.mark.parametrize("factor", [3e5, 1e9, 1e-7])
+def test_decode_query_magnitudes(preset, factor):
+    """bf16 queries far outside fp16 range (and far below its normal range):
+    each query head's fp16 operand is scaled by a power of two, so the result
+    still meets the bar (huge queries give one-hot attention, tiny ones
+    near-uniform attention)."""
+    import torch
+
+    w = _small(preset, [40, 300, 16], Hq=8, Hk=2, bs=16, seed=77)
+    c = G.DecodeCase(w)
+    q = O.widen(c.qbits, "bf16") * factor
+    c.qbits = W.to_bits(q, "bf16")
+    c.q = G.dev16(c.qbits, "bf16")
+    G.log(f"decode query x{factor:g} {preset}")
+    out, lse = c.gpu_decode(torch.from_numpy(c.cache_o).cuda(), 3)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
