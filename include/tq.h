@@ -277,13 +277,17 @@ int tq_store_validate(const tq_layout* layout, const void* key, const void* valu
  *                ([TQ+] "nvfp4 dec_after_8K cliff explained": rows whose
  *                softmax factor exp(s - m) falls below the gate contribute
  *                no value; 1e-3 there).  A token whose factor against the
- *                work unit's running maximum is below value_gate keeps its
- *                weight in the softmax denominator (and the lse) but adds no
- *                value; a pair of 16-token tiles whose tokens are all gated
- *                skips its value decode and value products.  The running
- *                maximum never exceeds the final one, so every gated token
- *                has exp(s - max) < value_gate and the output moves by at
- *                most sum over such tokens of (normalized weight) * |v|.
+ *                exact running maximum of its query head (over the tokens
+ *                its work unit has scored so far) is below value_gate keeps
+ *                its weight in the softmax denominator (and the lse) but
+ *                adds no value; a pair of 16-token tiles whose tokens are all
+ *                gated skips its value decode and value products.  The
+ *                running maximum never exceeds the final one, so every gated
+ *                token has exp(s - max) < value_gate and the output moves by
+ *                at most sum over such tokens of (normalized weight) * |v|.
+ *                The cache bytes are read either way (tiles arrive whole),
+ *                so the gate saves no memory traffic; on the workloads
+ *                measured here it costs time rather than saving it.
  *                TQ_EINVAL outside [0, 1) or NaN.
  *   sinks        device fp32 [num_q_heads] attention-sink logits, or NULL
  *                ([API] TurboQuantAttentionImpl.__init__ / _decode_attention

@@ -547,6 +547,7 @@ struct Softmax {
   float m, l, z;  // reference max (log2 domain), sum of p, sum of p * zero
   float f, fi;    // the lane's score unit 2^-e and its inverse 2^e
   float mt;       // (m + kLazyRescaleLog2) * fi
+  float mx;       // exact running maximum (log2 domain; kept by the sparse-V gate only)
 };
 
 // Largest growth of p = 2^(s - m) tolerated before the accumulators are
@@ -568,19 +569,25 @@ struct PendingTile {
   half4 pv;                        // p * value_scale of those tokens, fp16
 };
 
-// The opt-in sparse-V gate (gate > 0, uniform): a token whose factor p =
-// exp(s - m) against the running reference maximum is below the gate keeps
-// p in the softmax sum but adds no value (its value weight ps and its
-// zero-point term drop).  m never exceeds the final maximum, so every gated
-// token also has exp(s - max) < gate.  gated_p: p for the zero-point sum.
-__device__ __forceinline__ void sparse_v_gate(float gate, const float p[4], float ps[4]) {
-  if (gate > 0.f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (p[i] < gate) ps[i] = 0.f;
-  }
+// The opt-in sparse-V gate (gate > 0, uniform; glg = log2(gate)): a token
+// whose factor exp(s - mx) against the exact running maximum mx of its head
+// (over the tokens the work unit has scored so far, this tile included) is
+// below the gate keeps its weight p in the softmax sum but adds no value (its
+// value weight ps and its zero-point term drop).  mx never exceeds the final
+// maximum, so every gated token also has exp(s - max) < gate.  Returns the
+// threshold in raw score units (-inf with the gate off); lmax: the lane's
+// largest raw score of the tile.
+__device__ __forceinline__ float gate_threshold(float gate, float glg, float lmax, Softmax& sm) {
+  if (!(gate > 0.f)) return -INFINITY;
+  sm.mx = fmaxf(sm.mx, quarter_max(lmax) * sm.f);
+  return (sm.mx + glg) * sm.fi;
 }
-__device__ __forceinline__ float gated_p(float gate, float p) { return gate > 0.f && p < gate ? 0.f : p; }
+__device__ __forceinline__ void sparse_v_gate(float gthr, const float sco[4], float ps[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (sco[i] < gthr) ps[i] = 0.f;
+}
+__device__ __forceinline__ float gated_p(float gthr, float sco, float p) { return sco < gthr ? 0.f : p; }
 
 // Whether either tile of a pair has a value weight left (false only when the
 // sparse-V gate dropped every token of both: the pair's value work is skipped).
@@ -598,8 +605,8 @@ __device__ __forceinline__ bool pair_has_values(const PendingTile<P>& x, const P
 template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
                                            const tq::Lut8& lb, const half8* bq, int valid, int skip, float gate,
-                                           Softmax& sm, f32x4* acc, PendingTile<P>& pend, bool have_pend,
-                                           PendingTile<P>& cur) {
+                                           float glg, Softmax& sm, f32x4* acc, PendingTile<P>& pend,
+                                           bool have_pend, PendingTile<P>& cur) {
   using T = Preset<P>;
   // two independent accumulation chains halve the dependent-MFMA latency
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -666,11 +673,12 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
-  sparse_v_gate(gate, p, ps);
+  const float gthr = gate_threshold(gate, glg, lmax, sm);
+  sparse_v_gate(gthr, sco, ps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    if (!T::kVlm) sm.z = fma_hi16(gated_p(gate, p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
+    if (!T::kVlm) sm.z = fma_hi16(gated_p(gthr, sco[i], p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
   half2v ps23 = {static_cast<_Float16>(ps[2]), static_cast<_Float16>(ps[3])};
@@ -771,7 +779,7 @@ template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
                                                   const half8* bq, int validA, int validB, int skipA, int skipB,
-                                                  float gate, Softmax& sm, f32x4* acc) {
+                                                  float gate, float glg, Softmax& sm, f32x4* acc) {
   using T = Preset<P>;
   static_assert(T::kNh == 1, "packed pairs: head_dim 128");
   const int lane = threadIdx.x & 63;
@@ -852,11 +860,12 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
       ps[i] = mul_lo16(p[i], sz[i]);
     }
   }
-  sparse_v_gate(gate, p, ps);
+  const float gthr = gate_threshold(gate, glg, lmax, sm);
+  sparse_v_gate(gthr, sco, ps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sm.l += p[i];
-    if (!T::kVlm) sm.z = fma_hi16(gated_p(gate, p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
+    if (!T::kVlm) sm.z = fma_hi16(gated_p(gthr, sco[i], p[i]), sz[i], sm.z);  // Lloyd-Max values have no zero point
   }
   // value weights: tile A's from this lane, tile B's from lane c + 8
   half2v ps01 = {static_cast<_Float16>(ps[0]), static_cast<_Float16>(ps[1])};
@@ -1189,9 +1198,9 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // the phase-0 wave writes the split's partial rows.  head_dim 256 (two
 // halves: twice the accumulators and query operands) runs one tile per wave
 // and keeps 2 waves per SIMD's registers.
-// GATE: the body honours the sparse-V gate vgate (> 0, on exp(s - running
-// max)); the default kernel is built without its code and keeps a single
-// argument, the gated one takes the gate as a second.
+// GATE: the body honours the sparse-V gate vgate (> 0, on exp(s - exact
+// running max)); the default kernel is built without its code and keeps a
+// single argument, the gated one takes the gate as a second.
 //
 // FIX: the launch geometry of 8 KV heads at head_dim 128 in combined slots
 // (G = Hk = 8, one phase, a two-entry ring of contiguous 16-row tile
@@ -1442,7 +1451,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     off.mm0 = off.sd = off.sm = 0u;
   }
 
-  Softmax sm{-INFINITY, 0.f, 0.f, 1.f / qfi, qfi, -INFINITY};
+  Softmax sm{-INFINITY, 0.f, 0.f, 1.f / qfi, qfi, -INFINITY, -INFINITY};
+  const float vglg = GATE ? __log2f(vgate) : 0.f;  // log2 of the sparse-V gate
   f32x4 acc[8 * T::kNh];
 #pragma unroll
   for (int n = 0; n < 8 * T::kNh; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1459,7 +1469,7 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
         const uint8_t* img = ent + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
         score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, bq,
                                   min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
-                                  max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), vgate, sm, acc);
+                                  max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), vgate, vglg, sm, acc);
       }
     } else {
 #pragma unroll
@@ -1470,8 +1480,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
           const uint8_t* img = ent + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
           load_tile<P, SOA>(img, off, r);
           PendingTile<P> cur;
-          score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, sm,
-                             acc, pend, have_pend, cur);
+          score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, vglg,
+                             sm, acc, pend, have_pend, cur);
           if (have_pend) {
             if (!GATE || pair_has_values(pend, cur)) accumulate_pair<P>(pend, cur, lv, acc);
             have_pend = false;
