@@ -37,6 +37,18 @@ TQ_HD void run_bits_op(int op, const uint32_t* in, uint32_t* out) {
       for (int k = 0; k < 4; ++k) out[k] = tq::key2_selector(in[0], k);
       break;
     case 10: tq::lm_value_selectors(in, out); break;
+    case 11:  // pair fields 8 in[3] .. 8 in[3] + 7 of the stream in[0..2]
+      for (int k = 0; k < 8; ++k) out[k] = tq::key3_pair_field(in[0], in[1], in[2], 8 * (in[3] & 1u) + k);
+      break;
+    case 13:  // windows of pair fields 8 in[3] .. 8 in[3] + 7
+      for (int k = 0; k < 8; ++k) out[k] = tq::key3_pair_window(in[0], in[1], in[2], 8 * (in[3] & 1u) + k);
+      break;
+    case 12: {  // pair-table entries in[8] .. in[8] + 7 of the fp16 codebook in[0..7] (low halves)
+      uint16_t h[8];
+      for (int k = 0; k < 8; ++k) h[k] = static_cast<uint16_t>(in[k]);
+      for (int k = 0; k < 8; ++k) out[k] = tq::key3_pair_entry(h, static_cast<int>((in[8] + k) & 63u));
+      break;
+    }
     case 7: {
       float f;
       uint32_t u = in[0];

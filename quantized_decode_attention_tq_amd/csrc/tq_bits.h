@@ -136,6 +136,39 @@ TQ_HD void lm_value_selectors(const uint32_t w[4], uint32_t sel[8]) {
   key3_selectors(s0, s1, s2, sel);
 }
 
+// 3-bit keys, two dims per lookup: the lane's 32 codes are a 96-bit
+// LSB-first stream {w2:w1:w0}; the 6-bit field at bit 6j holds the codes of
+// dims 2j (bits 0..2) and 2j + 1 (bits 3..5), and indexes a 64-entry table
+// whose entry f is the fp16 pair (c[f & 7], c[f >> 3]).  Fields 5 and 10
+// straddle a dword boundary.
+TQ_HD uint32_t key3_pair_field(uint32_t w0, uint32_t w1, uint32_t w2, int j) {
+  const int b = 6 * j;
+  if (b + 6 <= 32) return (w0 >> b) & 63u;
+  if (b < 32) return ((w0 >> b) | (w1 << (32 - b))) & 63u;
+  if (b + 6 <= 64) return (w1 >> (b - 32)) & 63u;
+  if (b < 64) return ((w1 >> (b - 32)) | (w2 << (64 - b))) & 63u;
+  return (w2 >> (b - 64)) & 63u;
+}
+// The same field at bits 8..13 of a 32-bit window of the stream (other bits
+// hold neighbouring codes): one shift or funnel shift, so that (window &
+// 0x3F00) is the field times a 256-byte table stride.
+TQ_HD uint32_t key3_pair_window(uint32_t w0, uint32_t w1, uint32_t w2, int j) {
+  const int s = 6 * j - 8;  // stream bit at window bit 0
+  if (s < 0) return w0 << (-s);
+  if (s >= 64) return w2 >> (s - 64);
+  const uint32_t lo = s < 32 ? w0 : w1, hi = s < 32 ? w1 : w2;
+  const int r = s & 31;
+  return r == 0 ? lo : ((lo >> r) | (hi << (32 - r)));
+}
+// Table entry f of the pair lookup: fp16 bits of c[f & 7] (low half) and
+// c[f >> 3] (high half), from the 8-entry fp16 codebook h.
+TQ_HD uint32_t key3_pair_entry(const uint16_t h[8], int f) {
+  return static_cast<uint32_t>(h[f & 7]) | (static_cast<uint32_t>(h[f >> 3]) << 16);
+}
+// The pair lookup's MFMA operand order: dword j of the lane's 16 holds dims
+// 2j, 2j + 1, so chunk c element e holds dim 8c + e.
+TQ_HD int key3_pair_dim(int c, int e) { return 8 * c + e; }
+
 // Order of the 32 key dims of a 3-bit lane chunk in the MFMA operand: chunk c
 // (0..3) element e (0..7) holds dim 8*(e & 3) + 2c + (e >> 2).
 TQ_HD int key3_dim(int c, int e) { return 8 * (e & 3) + 2 * c + (e >> 2); }

@@ -203,28 +203,6 @@ __device__ __forceinline__ uint32_t ld32_u(const uint8_t* p) {
 
 __device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
 
-// Position of query dim d in the fp16 query operand image: lane quarter q,
-// MFMA chunk c, element e -> q*32 + c*8 + e, matching the order in which the
-// key operand holds dims (FP8 keys: quarter q loads dims 16q..16q+15 and
-// 64+16q..64+16q+15; 4-bit keys: even dims then odd dims of each byte group;
-// 3-bit keys: the selector order of tq::key3_selectors; 2-bit keys:
-// tq::key2_dim).
-template <int P>
-__device__ __forceinline__ int qh_pos(int d) {
-  using T = Preset<P>;
-  if (T::kFp8) {
-    const int r = d & 63;
-    return (r >> 4) * 32 + ((d >> 6) * 2 + ((r & 15) >> 3)) * 8 + (d & 7);
-  }
-  const int q = d >> 5, dd = d & 31;
-  if (T::kKb == 4) {
-    const int r = dd & 7;
-    return q * 32 + (dd >> 3) * 8 + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
-  }
-  if (T::kKb == 2) return q * 32 + (2 * (dd >> 4) + ((dd & 3) >> 1)) * 8 + ((dd >> 2) & 3) + 4 * (dd & 1);
-  return q * 32 + ((dd & 7) >> 1) * 8 + (dd & 1) * 4 + (dd >> 3);
-}
-
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4a4 v = {a, b, c, d};
   return __builtin_bit_cast(half8, v);
@@ -482,11 +460,30 @@ __device__ __forceinline__ void load_value_words_soa(const uint8_t* tb, const La
   }
 }
 
+static_assert(tq::kKey3LutCopies == 64, "pair table: 256-byte entries (one dword per lane copy)");
+
+// Dword at LDS byte address `addr`.
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+  return *reinterpret_cast<lds_cu32*>(static_cast<size_t>(addr));
+}
+
+// (x & mask) | y in one v_and_or_b32.  The compiler turns an or of disjoint
+// bits into an add, which it then cannot fuse with the and.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t y) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(y));
+  return r;
+}
+
 // Key tile operand for one lane (token = lane % 16, its 32 dims of quarter q
-// in head half hh).  SOA: the key words are aligned (sh unused).
+// in head half hh).  SOA: the key words are aligned (sh unused).  klane: LDS
+// address of the lane's copy of the 3-bit pair table's entry 0 (entry f at
+// klane + 256 f); the table starts at LDS address 0, so klane's bits 8..13
+// are clear and an or places the entry.
 template <int P, int SOA>
 __device__ __forceinline__ void key_operand(const TileRegs<P>& rr, int hh, uint32_t sh, const tq::Lut8& la,
-                                            const tq::Lut8& lb, half8 A[4]) {
+                                            const tq::Lut8& lb, uint32_t klane, half8 A[4]) {
   using T = Preset<P>;
   const uint32_t* k = rr.k[hh];
   if constexpr (T::kFp8 != 0) {
@@ -519,19 +516,18 @@ __device__ __forceinline__ void key_operand(const TileRegs<P>& rr, int hh, uint3
       A[c] = as_half8(a0, a1, b0, b1);
     }
   } else {
-    uint32_t sel[8];
-    if (SOA)
-      tq::key3_selectors(k[0], k[1], k[2], sel);
-    else
-      tq::key3_selectors(tq::alignbyte(k[1], k[0], sh), tq::alignbyte(k[2], k[1], sh),
-                         tq::alignbyte(k[3], k[2], sh), sel);
+    // 3-bit keys: 16 lookups of two dims each in the LDS pair table (a
+    // field extract and an address per lookup, against ~4 VALU operations
+    // per two dims through selector bytes and byte permutes)
+    const uint32_t w0 = SOA ? k[0] : tq::alignbyte(k[1], k[0], sh);
+    const uint32_t w1 = SOA ? k[1] : tq::alignbyte(k[2], k[1], sh);
+    const uint32_t w2 = SOA ? k[2] : tq::alignbyte(k[3], k[2], sh);
+    // one shift (or funnel shift) and one and-or per lookup
+    uint32_t d[16];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t a0, a1, b0, b1;
-      tq::lut8(sel[2 * c], la, a0, a1);
-      tq::lut8(sel[2 * c + 1], la, b0, b1);
-      A[c] = as_half8(a0, a1, b0, b1);
-    }
+    for (int j = 0; j < 16; ++j) d[j] = lds_u32(and_or(tq::key3_pair_window(w0, w1, w2, j), 0x3F00u, klane));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) A[c] = as_half8(d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]);
   }
 }
 
@@ -604,7 +600,8 @@ __device__ __forceinline__ bool pair_has_values(const PendingTile<P>& x, const P
 // per head half; acc: 8 accumulators per head half.
 template <int P, int SOA>
 __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P>& o, const tq::Lut8& la,
-                                           const tq::Lut8& lb, const half8* bq, int valid, int skip, float gate,
+                                           const tq::Lut8& lb, uint32_t klane, const half8* bq, int valid,
+                                           int skip, float gate,
                                            float glg, Softmax& sm, f32x4* acc, PendingTile<P>& pend,
                                            bool have_pend, PendingTile<P>& cur) {
   using T = Preset<P>;
@@ -613,7 +610,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 #pragma unroll
   for (int h = 0; h < T::kNh; ++h) {
     half8 A[4];
-    key_operand<P, SOA>(r, h, o.ksh, la, lb, A);
+    key_operand<P, SOA>(r, h, o.ksh, la, lb, klane, A);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[4 * h], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[4 * h + 1], s1, 0, 0, 0);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[4 * h + 2], s0, 0, 0, 0);
@@ -778,7 +775,7 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
                                                   const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
-                                                  const half8* bq, int validA, int validB, int skipA, int skipB,
+                                                  uint32_t klane, const half8* bq, int validA, int validB, int skipA, int skipB,
                                                   float gate, float glg, Softmax& sm, f32x4* acc) {
   using T = Preset<P>;
   static_assert(T::kNh == 1, "packed pairs: head_dim 128");
@@ -796,13 +793,13 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   }
   // one accumulation chain per tile: the two tiles' chains interleave
   half8 A[4];
-  key_operand<P, SOA>(rA, 0, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rA, 0, o.ksh, la, lb, klane, A);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f};
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], bq[2], sa, 0, 0, 0);
   sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], bq[3], sa, 0, 0, 0);
-  key_operand<P, SOA>(rB, 0, o.ksh, la, lb, A);
+  key_operand<P, SOA>(rB, 0, o.ksh, la, lb, klane, A);
   f32x4 sb = {0.f, 0.f, 0.f, 0.f};
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], bq[0], sb, 0, 0, 0);
   sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], bq[1], sb, 0, 0, 0);
@@ -1076,8 +1073,9 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
       half8 h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // inverse of qh_pos inside the lane's 32 dims
-        const int dd = T::kKb == 4 ? tq::key4_dim(c, e) : (T::kKb == 2 ? tq::key2_dim(c, e) : tq::key3_dim(c, e));
+        // the dim key_operand holds at (chunk c, element e) of the lane's 32
+        const int dd =
+            T::kKb == 4 ? tq::key4_dim(c, e) : (T::kKb == 2 ? tq::key2_dim(c, e) : tq::key3_pair_dim(c, e));
         h[e] = static_cast<_Float16>(v[hh][dd] * qs);
       }
       bq[4 * hh + c] = h;
@@ -1213,7 +1211,10 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   static_assert(T::kNh == 1 || (TPW == 1 && PACK == 0), "head_dim 256: one tile per wave");
   static_assert(!FIX || (T::kNh == 1 && SOA == 0), "fixed geometry: head_dim 128, combined slots");
   constexpr int kOut = 32 * T::kNh;  // output dims per lane (32 of each half)
-  extern __shared__ __attribute__((aligned(1024))) uint8_t tq_ring[];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t tq_lds[];
+  // dynamic LDS: [3-bit key pair table (3-bit MSE keys only)] [ring]
+  constexpr uint32_t kLut = (!T::kFp8 && T::kKb == 3) ? static_cast<uint32_t>(tq::kKey3LutBytes) : 0u;
+  uint8_t* const tq_ring = tq_lds + kLut;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1427,6 +1428,21 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     for (int i = 0; i < 8; ++i) hv[i] = __half_as_ushort(__float2half_rn(vc[i]));
     lv = {lut_bytes(hv, 0, 0), lut_bytes(hv, 4, 0), lut_bytes(hv, 0, 8), lut_bytes(hv, 4, 8)};
   }
+  // 3-bit keys: the pair table, entry f = (c[f & 7], c[f >> 3]) in fp16 at
+  // dword 64 f + copy (one copy per lane); the main loop's first barrier
+  // orders these writes before any lookup
+  if constexpr (kLut != 0) {
+    uint32_t* lut = reinterpret_cast<uint32_t*>(tq_lds);
+    for (int i = static_cast<int>(threadIdx.x); i < 64 * tq::kKey3LutCopies; i += static_cast<int>(blockDim.x)) {
+      const uint32_t f = static_cast<uint32_t>(i / tq::kKey3LutCopies);
+      uint32_t pair, unused;
+      tq::lut8((f & 7u) | ((f >> 3) << 8), la, pair, unused);  // (c[f & 7], c[f >> 3])
+      lut[i] = pair;
+    }
+  }
+  // LDS address of this lane's copy of table entry 0: the kernels declare no
+  // static LDS (the launcher checks), so the dynamic block starts at 0
+  const uint32_t klane = 4u * static_cast<uint32_t>(lane);
   LaneOff<P> off;
   if constexpr (SOA != 0) {
     using S = Soa<P>;
@@ -1467,7 +1483,7 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
       const int t = t_begin + u * Q + ph * TPW;
       if (t < t_end) {
         const uint8_t* img = ent + static_cast<uint32_t>(ph * TPW * spt) * 1024u;
-        score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, bq,
+        score_pair_packed<P, SOA>(img, img + static_cast<uint32_t>(spt) * 1024u, off, la, lb, lv, klane, bq,
                                   min(16, seqlen - t * 16), t + 1 < t_end ? min(16, seqlen - (t + 1) * 16) : 0,
                                   max(0, wstart - t * 16), max(0, wstart - (t + 1) * 16), vgate, vglg, sm, acc);
       }
@@ -1480,8 +1496,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
           const uint8_t* img = ent + static_cast<uint32_t>((ph * TPW + j) * spt) * 1024u;
           load_tile<P, SOA>(img, off, r);
           PendingTile<P> cur;
-          score_tile<P, SOA>(r, off, la, lb, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate, vglg,
-                             sm, acc, pend, have_pend, cur);
+          score_tile<P, SOA>(r, off, la, lb, klane, bq, min(16, seqlen - t * 16), max(0, wstart - t * 16), vgate,
+                             vglg, sm, acc, pend, have_pend, cur);
           if (have_pend) {
             if (!GATE || pair_has_values(pend, cur)) accumulate_pair<P>(pend, cur, lv, acc);
             have_pend = false;
@@ -1955,6 +1971,12 @@ int set_max_lds_once(const void* fn, int bytes) {
   std::lock_guard<std::mutex> lock(g_setup_mutex);
   for (const auto& kv : g_lds_set)
     if (kv.first == fn && kv.second == dev) return TQ_OK;
+  // the 3-bit key table sits at LDS address 0: no static LDS before the
+  // dynamic block
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return hip_status(e);
+  if (attr.sharedSizeBytes != 0) return TQ_EUNSUPPORTED;
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return hip_status(e);
   g_lds_set.emplace_back(fn, dev);

@@ -14,7 +14,8 @@ int hip_status(int hip_error);
 
 // hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) the first time
 // fn is launched on the current device (cached per (kernel, device) under a
-// lock; later calls return TQ_OK at once).
+// lock; later calls return TQ_OK at once).  TQ_EUNSUPPORTED if fn declares
+// static LDS: the stage-1 kernels place a table at LDS address 0.
 int set_max_lds_once(const void* fn, int bytes);
 
 inline bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
@@ -64,6 +65,15 @@ constexpr int kSoaRowPad = 16;
 // rotation, ring fill) needs a few tiles to amortize.
 constexpr int64_t kMinTilesPerUnit = 16;
 constexpr int64_t kPartPad = 4;  // LSE + 3 pad floats after the head_dim outputs
+// 3-bit MSE keys decode through a 64-entry table of fp16 centroid pairs in
+// LDS (two dims per lookup), one copy per lane of the wave so that the 64
+// lanes' reads never share a bank: 64 entries x 64 copies x 4 bytes at the
+// start of a stage-1 workgroup's dynamic LDS, ahead of the ring.
+constexpr int kKey3LutCopies = 64;
+constexpr int kKey3LutBytes = 64 * kKey3LutCopies * 4;
+inline size_t key_lut_bytes(const tq_layout* L) {
+  return (!L->key_fp8 && L->key_bits == 3) ? static_cast<size_t>(kKey3LutBytes) : 0;
+}
 
 inline int64_t table_bytes(int64_t batch) { return (8 * batch + 255) / 256 * 256; }
 
@@ -83,7 +93,7 @@ inline int64_t max_splits(int64_t batch, int64_t num_splits) {
 // split its tiles.  A tile image (16 token rows of the group) takes spt 1 KB
 // slots of LDS; the ring holds R super-tiles of P tiles (two-deep unless a
 // super-tile is small), sized for two
-// workgroups per compute unit.  max_tiles: tiles of the longest possible
+// workgroups per compute unit (after the 3-bit key table, if any).  max_tiles: tiles of the longest possible
 // sequence (block-table width), which caps S_int.
 struct DecodePlan {
   int G, P, R, spt, contiguous;
@@ -181,7 +191,7 @@ inline int decode_plan(const tq_layout* L, int32_t batch, int32_t num_q_heads, i
   p->contiguous = contiguous;
   p->dslots = dslots;
   p->soa_pad = soa ? kSoaRowPad : 0;
-  p->lds = R * entry > merge ? R * entry : merge;
+  p->lds = key_lut_bytes(L) + (R * entry > merge ? R * entry : merge);
   p->units = static_cast<int64_t>(batch) * s_int;
   p->grid = p->units * wg_per_unit;
   const int loads = (spt + G - 1) / G;  // DMA slots per wave per tile of its phase

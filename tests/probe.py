@@ -11,7 +11,9 @@ PATH = os.path.join(ROOT, "quantized_decode_attention_tq_amd", "libtq_probe.so")
 
 N_IN, N_OUT = 12, 8
 OPS = {"perm": 0, "alignbyte": 1, "key3_selectors": 2, "lut8": 3, "lut16": 4, "val4_pairs": 5, "val3_pairs": 6,
-       "f32_to_e4m3": 7, "val2_pairs": 8, "key2_selectors": 9, "lm_value_selectors": 10}
+       "f32_to_e4m3": 7, "val2_pairs": 8, "key2_selectors": 9, "lm_value_selectors": 10,
+       "key3_pair_fields": 11, "key3_pair_entries": 12,
+       "key3_pair_windows": 13}
 
 
 def lib():

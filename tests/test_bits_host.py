@@ -51,6 +51,31 @@ def test_key3_selectors_match_oracle_packing():
             np.testing.assert_array_equal(sb[:, m, g], codes[:, 8 * g + m])
 
 
+def test_key3_pair_fields_match_oracle_packing():
+    """Field j of a lane's 96-bit stream = code of dim 2j | code of dim 2j+1 << 3
+    (fields 5 and 10 straddle a dword)."""
+    codes = RNG.integers(0, 8, (4000, 32))
+    w = _bytes_to_words(O.pack_lsb(codes, 3))  # (n, 3)
+    for half in (0, 1):
+        inp = np.column_stack([w, np.full(len(w), half, np.uint32)])
+        got = probe.bits_host("key3_pair_fields", inp)
+        for k in range(8):
+            j = 8 * half + k
+            np.testing.assert_array_equal(got[:, k], codes[:, 2 * j] | (codes[:, 2 * j + 1] << 3))
+        win = probe.bits_host("key3_pair_windows", inp)
+        np.testing.assert_array_equal((win >> 8) & 63, got)
+
+
+def test_key3_pair_entries_hold_both_centroids():
+    c3, _ = O.codebook_tables(128, 3)
+    h = np.asarray(c3, np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+    for f0 in range(0, 64, 8):
+        got = probe.bits_host("key3_pair_entries", np.concatenate([h, [f0]]).astype(np.uint32)[None, :])[0]
+        for k in range(8):
+            f = f0 + k
+            assert got[k] & 0xFFFF == h[f & 7] and got[k] >> 16 == h[f >> 3]
+
+
 def _f16_table(vals):
     h = np.asarray(vals, np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
     lo = h & 0xFF
