@@ -194,11 +194,37 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
 }
 
-// dword from a 2-byte aligned address: two aligned dwords, realigned.
-__device__ __forceinline__ uint32_t ld32_u(const uint8_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(a & ~static_cast<uintptr_t>(3));
-  return tq::alignbyte(w.y, w.x, static_cast<uint32_t>(a & 3));
+// Dword at a 2-byte aligned LDS address as two 16-bit reads joined by one
+// shift-or.  A dword read there would be unaligned (several times slower on
+// this LDS), and two dwords read as one pair take 8-bit offsets, too short
+// for a ring entry's, so every such read would need an address add.  The
+// upper half is read non-temporally only so that the compiler does not fuse
+// the two halves into one unaligned dword read (LDS has no such hint).
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ uint32_t ld32_even(const uint8_t* p) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));  // LDS offset of p
+  const uint16_t lo = *reinterpret_cast<lds_cu16*>(static_cast<size_t>(a));
+  const uint16_t hi = __builtin_nontemporal_load(reinterpret_cast<lds_u16*>(static_cast<size_t>(a + 2)));
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+// The value-code word (4 bytes; 3-bit codes use the low 3) of a lane at byte
+// vo of the tile image tb.  Tile bases are 32-byte aligned and slots, key
+// parts and 4- or 2-bit words even, so vo is even there (2 mod 4 for half
+// the heads when the slot is 2 mod 4); 3-bit words start at 3 x the lane's
+// row and may sit at any byte: an aligned pair of dwords, realigned.
+template <int P>
+__device__ __forceinline__ uint32_t value_word(const uint8_t* tb, uint32_t vo) {
+  using T = Preset<P>;
+  if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
+    return *reinterpret_cast<const uint32_t*>(tb + vo);
+  } else if constexpr (T::kVb != 3) {
+    return ld32_even(tb + vo);
+  } else {
+    const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
+    return tq::alignbyte(w.y, w.x, vo & 3u);
+  }
 }
 
 __device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
@@ -257,7 +283,7 @@ __device__ __forceinline__ uint32_t meta_rec(const LaneOff<P>& o, int i) {
 template <int P>
 struct TileRegs {
   uint32_t k[Preset<P>::kNh][8];     // per head half
-  uint32_t v[Preset<P>::kNh][4][2];  // per head half
+  uint32_t v[Preset<P>::kNh][4];     // value words, per head half
   uint32_t sz[4];  // fp16 scale | fp16 zero << 16
   uint32_t gm[4];  // fp16 key norm (MSE keys)
 };
@@ -293,36 +319,20 @@ __device__ __forceinline__ void load_tile(const uint8_t* tb, const LaneOff<P>& o
 #pragma unroll
     for (int h = 0; h < T::kNh; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r.v[h][i][0] = vw[h][i];
+      for (int i = 0; i < 4; ++i) r.v[h][i] = vw[h][i];
     return;
   }
   load_keys<P>(tb, o, r);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // value codes of token 4q+i; the row stride may be 2 mod 4, so the
-    // whole in-tile offset is aligned down (tile bases are 32-byte aligned).
-    // Both halves' words share the alignment (half sizes are 4-byte multiples).
 #pragma unroll
-    for (int h = 0; h < T::kNh; ++h) {
-      const uint32_t vo = o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv);
-      if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
-        r.v[h][i][0] = *reinterpret_cast<const uint32_t*>(tb + vo);
-      } else {
-        const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
-        r.v[h][i][0] = w.x;
-        r.v[h][i][1] = w.y;
-      }
-    }
+    for (int h = 0; h < T::kNh; ++h)
+      r.v[h][i] = value_word<P>(tb, o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv));
     const uint8_t* m = tb + o.mo[i];
-    if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
+    if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0)
       r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
-    } else {
-      // 2 mod 4 for half the heads: an aligned pair of dwords, realigned
-      // (an unaligned LDS dword read stalls)
-      const uint32_t so = o.mo[i] + static_cast<uint32_t>(T::kKps + T::kVdata);
-      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (so & ~3u));
-      r.sz[i] = tq::alignbyte(w.y, w.x, so & 3u);
-    }
+    else
+      r.sz[i] = ld32_even(m + T::kKps + T::kVdata);  // 2 mod 4 for half the heads
     if constexpr (T::kFp8 == 0) r.gm[i] = ld16(m + T::kKdata);
   }
 }
@@ -372,10 +382,7 @@ __device__ __forceinline__ void load_token_fields(const uint8_t* tb, const LaneO
     if constexpr (T::kSlot % 4 == 0 && (T::kKps + T::kVdata) % 4 == 0) {
       r.sz[i] = *reinterpret_cast<const uint32_t*>(m + T::kKps + T::kVdata);
     } else {
-      // 2 mod 4 for half the heads: an aligned pair of dwords, realigned
-      const uint32_t so = o.mo[i] + static_cast<uint32_t>(T::kKps + T::kVdata);
-      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (so & ~3u));
-      r.sz[i] = tq::alignbyte(w.y, w.x, so & 3u);
+      r.sz[i] = ld32_even(m + T::kKps + T::kVdata);  // 2 mod 4 for half the heads
     }
     if constexpr (T::kFp8 == 0) r.gm[i] = ld16(m + T::kKdata);
   }
@@ -391,13 +398,7 @@ __device__ __forceinline__ void load_value_words(const uint8_t* tb, const LaneOf
   for (int h = 0; h < T::kNh; ++h)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t vo = o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv);
-    if constexpr (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4) {
-      vw[h][i] = *reinterpret_cast<const uint32_t*>(tb + vo);
-    } else {
-      const u32x2a4 w = *reinterpret_cast<const u32x2a4*>(tb + (vo & ~3u));
-      vw[h][i] = tq::alignbyte(w.y, w.x, vo & 3u);
-    }
+    vw[h][i] = value_word<P>(tb, o.mo[i] + o.vcol + static_cast<uint32_t>(h * T::kHv));
   }
 }
 
@@ -640,19 +641,14 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
   // The rescale test needs no cross-lane maximum: a head's maximum over its
   // four lane quarters exceeds the threshold iff one of the lanes' does.
   const float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
-  float p[4], ps[4];
-  bool redo = __any(lmax > sm.mt);
-  if (!redo) {
-    float pmax = 0.f;
+  float p[4], ps[4], pmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
-      ps[i] = mul_lo16(p[i], sz[i]);
-      pmax = fmaxf(pmax, ps[i]);
-    }
-    redo = __any(pmax > 65504.f);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
+    ps[i] = mul_lo16(p[i], sz[i]);
+    pmax = fmaxf(pmax, ps[i]);
   }
-  if (redo) {  // rescale the accumulators (and the pending tile) to the new maximum
+  if (__any(lmax > sm.mt || pmax > 65504.f)) {  // rescale the accumulators (and the pending tile) to the new maximum
     const float m_cand = fmaxf(sm.m, quarter_max(lmax) * sm.f);
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
@@ -683,12 +679,7 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 #pragma unroll
   for (int h = 0; h < T::kNh; ++h)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (SOA != 0 || (T::kSlot % 4 == 0 && T::kKps % 4 == 0 && T::kVb == 4))
-      cur.vw[h][i] = r.v[h][i][0];
-    else
-      cur.vw[h][i] = tq::alignbyte(r.v[h][i][1], r.v[h][i][0], (o.mo[i] + o.vcol) & 3u);
-  }
+  for (int i = 0; i < 4; ++i) cur.vw[h][i] = r.v[h][i];
 }
 
 // O^T += V^T P^T over two scored tiles, one 128-dim head half (av / bv: the
@@ -831,19 +822,14 @@ __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uin
   }
   float lmax = fmaxf(fmaxf(sco[0], sco[1]), fmaxf(sco[2], sco[3]));
   lmax = fmaxf(lmax, swap8(lmax));  // the head's maximum over both tiles
-  float p[4], ps[4];
-  bool redo = __any(lmax > sm.mt);
-  if (!redo) {
-    float pmax = 0.f;
+  float p[4], ps[4], pmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
-      ps[i] = mul_lo16(p[i], sz[i]);
-      pmax = fmaxf(pmax, ps[i]);
-    }
-    redo = __any(pmax > 65504.f);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(fmaf(sco[i], sm.f, -sm.m));
+    ps[i] = mul_lo16(p[i], sz[i]);
+    pmax = fmaxf(pmax, ps[i]);
   }
-  if (redo) {  // rescale the accumulators to the new maximum (same on lanes c and c ^ 8)
+  if (__any(lmax > sm.mt || pmax > 65504.f)) {  // rescale the accumulators to the new maximum (same on lanes c and c ^ 8)
     const float m_cand = fmaxf(sm.m, quarter_max(lmax) * sm.f);
     const float alpha = __builtin_amdgcn_exp2f(sm.m - m_cand);
 #pragma unroll
