@@ -236,6 +236,28 @@ class DecodeBench:
         g = self.decode_graph()
         return spread(self.torch, g.replay, reps or DIST_REPLAYS, GRAPH_STEPS)
 
+    def time_gather(self, launches=None):
+        """The decode's tile reads alone (the probe library's gather kernel:
+        every 16-token tile of every sequence through the block table, no
+        arithmetic), median / p10 / p90 (ms) of `launches` launches rotating
+        over the cache copies: the ceiling of this read pattern."""
+        torch, w = self.torch, self.w
+        L = _probe_lib()
+        units = max(1, -(-1024 // w.batch))
+        out = torch.empty(4 * w.batch * units, dtype=torch.int32, device="cuda")
+        row = w.num_kv_heads * self.lay.slot_size_aligned
+        it = iter(range(1 << 30))
+
+        def launch():
+            c = self.caches[next(it) % N_COPIES]
+            rc = L.tq_probe_gather_read(c.data_ptr(), self.bt.data_ptr(), self.bt.shape[1], self.sl.data_ptr(),
+                                        w.batch, w.block_size, row, units, out.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, rc
+
+        warm_gpu(torch, launch, 30.0)
+        return spread(torch, launch, launches or DIST_REPLAYS, 1)
+
     def time_stage1(self, launches=None):
         """Stage-1 kernel duration: median / p10 / p90 (ms) of `launches`
         back-to-back launches (rotating caches), each bracketed by events on
@@ -368,8 +390,8 @@ def measured_traffic():
 
 
 def _probe_lib():
-    """libtq_probe.so: the streaming-read and copy kernels used for the
-    bandwidth ceiling and the counter calibration (built with libtq)."""
+    """libtq_probe.so: the streaming-read, tile-gather and copy kernels used
+    for the bandwidth ceilings and the counter calibration (built with libtq)."""
     import ctypes
 
     import torch  # noqa: F401  (torch's HIP runtime first, as for libtq)
@@ -379,6 +401,8 @@ def _probe_lib():
     vp = ctypes.c_void_p
     L.tq_probe_stream_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]
     L.tq_probe_copy.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
+    L.tq_probe_gather_read.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, vp, vp]
     return L
 
 
@@ -506,11 +530,16 @@ def decode_leg(torch, tq, w, S, steps=None, warmup=None, **kw):
     res["decode_frac_hbm"] = res["decode_gbs"] / HBM_PEAK_GBS
     res["stage1_us"] = _us(s1)
     res["stage1_gbs"] = b.bytes_read / (s1["median"] * 1e-3) / 1e9
+    if kw.get("block_layout", "aos") == "aos" and not kw.get("sliding_window"):
+        gr = b.time_gather()
+        res["gather_read_us"] = _us(gr)
+        res["gather_read_gbs"] = b.bytes_read / (gr["median"] * 1e-3) / 1e9
     del b
     torch.cuda.empty_cache()
+    gather = f"; tile reads alone {res['gather_read_gbs']:.0f} GB/s" if "gather_read_gbs" in res else ""
     log(f"[{w.name}{' ' + str(kw) if kw else ''}] decode call {res['decode_call_us']['median']:.1f} us "
         f"(p10 {res['decode_call_us']['p10']:.1f}, p90 {res['decode_call_us']['p90']:.1f}) -> {res['decode_gbs']:.0f} "
-        f"GB/s; stage 1 {res['stage1_us']['median']:.1f} us -> {res['stage1_gbs']:.0f} GB/s")
+        f"GB/s; stage 1 {res['stage1_us']['median']:.1f} us -> {res['stage1_gbs']:.0f} GB/s{gather}")
     return res
 
 
@@ -628,12 +657,14 @@ def main():
                    "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes_read_per_step": head["bytes_read"],
                    "step_us": head["step_us"], "decode_call_us": head["decode_call_us"],
                    "decode_call_gbs": head["decode_gbs"], "decode_call_frac_hbm_peak": head["decode_frac_hbm"],
-                   "decode_call_frac_stream_read": head["decode_gbs"] / stream["gbs_median"]},
+                   "decode_call_frac_stream_read": head["decode_gbs"] / stream["gbs_median"],
+                   "decode_call_frac_gather_read": head["decode_gbs"] / head["gather_read_gbs"]},
         "roofline": {"bound": "hbm", "achieved": st1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": st1_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "tq_decode_stage1_kernel<k8v4>", "stage1_us": head["stage1_us"],
                      "stream_read_gbs": stream["gbs_median"], "frac_of_stream_read": st1_gbs / stream["gbs_median"],
-                     "stream_read": stream},
+                     "stream_read": stream, "gather_read_gbs": head["gather_read_gbs"],
+                     "frac_of_gather_read": st1_gbs / head["gather_read_gbs"]},
         "cpu_baseline": cpu,
         "extra": extra,
     }

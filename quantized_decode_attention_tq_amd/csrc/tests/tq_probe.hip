@@ -119,6 +119,50 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (x == 0x9E3779B9u) out[blockIdx.x] = x;
 }
 
+// The decode's reads without its arithmetic: workgroup (b, u) reads tiles
+// [T u / U, T (u + 1) / U) of sequence b (T = ceil(L_b / 16); a tile is 16
+// consecutive token rows of row16 16-byte chunks inside one cache block,
+// found through the block table), 16-byte non-temporal loads, two tiles at
+// a time.  Wave w of the workgroup writes the XOR of the 32-bit words it
+// read to out[4 * blockIdx.x + w] (so a test can check the bytes covered).
+__global__ __launch_bounds__(256) void gather_read_kernel(const u32x4* __restrict__ cache,
+                                                          const int32_t* __restrict__ block_table, int bt_stride,
+                                                          const int32_t* __restrict__ seq_lens, int block_size,
+                                                          int64_t row16, int units, uint32_t* __restrict__ out) {
+  const int b = blockIdx.x / units, u = blockIdx.x % units;
+  const int T = (seq_lens[b] + 15) / 16;
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * u / units);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (u + 1) / units);
+  const int64_t tile16 = 16 * row16, blk16 = static_cast<int64_t>(block_size) * row16;
+  const int32_t* bt = block_table + static_cast<int64_t>(b) * bt_stride;
+  auto tile_base = [&](int t) {
+    return cache + static_cast<int64_t>(bt[(t * 16) / block_size]) * blk16 +
+           static_cast<int64_t>((t * 16) % block_size) * row16;
+  };
+  uint32_t x = 0;
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    const u32x4* p0 = tile_base(t);
+    const u32x4* p1 = tile_base(t + 1);
+#pragma unroll 2
+    for (int64_t j = threadIdx.x; j < tile16; j += 256) {
+      const u32x4 a = __builtin_nontemporal_load(p0 + j);
+      const u32x4 c = __builtin_nontemporal_load(p1 + j);
+      x ^= a.x ^ a.y ^ a.z ^ a.w ^ c.x ^ c.y ^ c.z ^ c.w;
+    }
+  }
+  if (t < t1) {
+    const u32x4* p0 = tile_base(t);
+    for (int64_t j = threadIdx.x; j < tile16; j += 256) {
+      const u32x4 a = __builtin_nontemporal_load(p0 + j);
+      x ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), m, 64));
+  if ((threadIdx.x & 63) == 0) out[4 * blockIdx.x + (threadIdx.x >> 6)] = x;
+}
+
 // Plain copy of n16 16-byte chunks.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out,
                                                    int64_t n16) {
@@ -218,6 +262,21 @@ int tq_probe_stream_read(const void* in, int64_t bytes, int64_t chunk, uint32_t*
   if (blocks > 0x7FFFFFFF) return -1;
   hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(in), chunk / 16, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+// The decode's tile reads of a paged cache (row_bytes: bytes of one token
+// row, all KV heads; a multiple of 16) by batch x units workgroups; out:
+// device uint32 [4 * batch * units].  Asynchronous on `stream`.
+int tq_probe_gather_read(const void* cache, const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                         int batch, int block_size, int64_t row_bytes, int units, uint32_t* out, void* stream) {
+  if (batch <= 0 || units <= 0 || row_bytes <= 0 || row_bytes % 16 || block_size < 16 || block_size % 16)
+    return -1;
+  const int64_t blocks = static_cast<int64_t>(batch) * units;
+  if (blocks > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(gather_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(cache), block_table, bt_stride,
+                     seq_lens, block_size, row_bytes / 16, units, out);
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 

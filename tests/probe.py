@@ -31,7 +31,9 @@ def lib():
                        ("tq_probe_permlane_swap", [vp, vp]),
                        ("tq_probe_fp8_encode", [vp, vp, ctypes.c_int]),
                        ("tq_probe_stream_read", [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]),
-                       ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp])):
+                       ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp]),
+                       ("tq_probe_gather_read", [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int64, ctypes.c_int, vp, vp])):
         f = getattr(L, name)
         f.restype = ctypes.c_int
         f.argtypes = args
