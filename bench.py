@@ -93,7 +93,8 @@ def spread(torch, fn, reps, per_rep):
             "mean": float(t.mean()), "reps": reps}
 
 
-MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
+MORE_PRESETS = ("turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm",
+                "turboquant_k8v4lm", "turboquant_4bit_lm", "turboquant_2bit_lm")
 SPARSE_V_GATE = 1e-3
 # head_dim 256 leg: the headline preset, FP8 keys with Lloyd-Max values (the pages' fp8k_turbo3v), 3-bit MSE
 HEAD256_PRESETS = ("turboquant_k8v4", "turboquant_k8v3lm", "turboquant_3bit_nc")

@@ -69,8 +69,12 @@ typedef enum {
  * Names "turboquant_k8v3", "turboquant_k4v3_nc", "turboquant_2bit_nc".
  * Lloyd-Max values ([TQ+] "What landed": values take the keys' rotation and
  * Lloyd-Max codebook with the matched-norm correction): k8v3lm = FP8 keys +
- * 3-bit Lloyd-Max values; 3bit_lm = 3-bit keys + 3-bit Lloyd-Max values.
- * Names "turboquant_k8v3lm", "turboquant_3bit_lm". */
+ * 3-bit Lloyd-Max values; 3bit_lm = 3-bit keys + 3-bit Lloyd-Max values;
+ * at the other widths of the pages' turbo2/3/4 family: k8v4lm = FP8 keys +
+ * 4-bit Lloyd-Max values; 4bit_lm = 4-bit keys + 4-bit Lloyd-Max values;
+ * 2bit_lm = 2-bit keys + 2-bit Lloyd-Max values.  Names
+ * "turboquant_k8v3lm", "turboquant_3bit_lm", "turboquant_k8v4lm",
+ * "turboquant_4bit_lm", "turboquant_2bit_lm". */
 typedef enum {
   TQ_K8V4 = 0,
   TQ_4BIT_NC = 1,
@@ -81,7 +85,10 @@ typedef enum {
   TQ_2BIT_NC = 6,
   TQ_K8V3LM = 7,
   TQ_3BIT_LM = 8,
-  TQ_NUM_PRESETS = 9
+  TQ_K8V4LM = 9,
+  TQ_4BIT_LM = 10,
+  TQ_2BIT_LM = 11,
+  TQ_NUM_PRESETS = 12
 } tq_preset;
 
 typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;

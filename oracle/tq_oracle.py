@@ -77,6 +77,13 @@ PRESETS = {
     # width for N(0, 1/D), as for keys.
     "turboquant_k8v3lm": (True, 8, 3, False, True),
     "turboquant_3bit_lm": (False, 3, 3, True, True),
+    # The same value codec at the other widths of the Atlas page's
+    # turbo2/3/4 family ([TQ+] "What landed": 2-, 3- and 4-bit Lloyd-Max
+    # codebooks, asymmetric pairs with FP8 keys): FP8 K + 4-bit V, and the
+    # symmetric 4- and 2-bit codecs.
+    "turboquant_k8v4lm": (True, 8, 4, False, True),
+    "turboquant_4bit_lm": (False, 4, 4, True, True),
+    "turboquant_2bit_lm": (False, 2, 2, True, True),
 }
 
 #: kernel block sizes the backend accepts ([PR] turboquant_attn.py excerpt,

@@ -26,7 +26,8 @@ TQ_OK, TQ_EINVAL, TQ_EPRESET, TQ_EHEADDIM, TQ_EBLOCK, TQ_EGQA, TQ_EWORKSPACE, TQ
 TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
 #: every preset of include/tq.h, in preset-id order
 PRESETS = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc", "turboquant_k8v3",
-           "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm")
+           "turboquant_k4v3_nc", "turboquant_2bit_nc", "turboquant_k8v3lm", "turboquant_3bit_lm",
+           "turboquant_k8v4lm", "turboquant_4bit_lm", "turboquant_2bit_lm")
 
 #: every symbol include/tq.h declares
 ABI_SYMBOLS = ("tq_version", "tq_status_str", "tq_last_hip_error", "tq_preset_from_name", "tq_layout_init",

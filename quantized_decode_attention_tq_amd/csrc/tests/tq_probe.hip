@@ -37,6 +37,8 @@ TQ_HD void run_bits_op(int op, const uint32_t* in, uint32_t* out) {
       for (int k = 0; k < 4; ++k) out[k] = tq::key2_selector(in[0], k);
       break;
     case 10: tq::lm_value_selectors(in, out); break;
+    case 14: tq::lm4_value_selectors(in, out); break;
+    case 15: tq::lm2_value_selectors(in, out); break;
     case 11:  // pair fields 8 in[3] .. 8 in[3] + 7 of the stream in[0..2]
       for (int k = 0; k < 8; ++k) out[k] = tq::key3_pair_field(in[0], in[1], in[2], 8 * (in[3] & 1u) + k);
       break;

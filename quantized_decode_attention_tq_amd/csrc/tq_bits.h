@@ -169,6 +169,33 @@ TQ_HD uint32_t key3_pair_entry(const uint16_t h[8], int f) {
 // 2j, 2j + 1, so chunk c element e holds dim 8c + e.
 TQ_HD int key3_pair_dim(int c, int e) { return 8 * c + e; }
 
+// The same for 4-bit Lloyd-Max value codes: w[g] holds token g's 8 codes
+// (dim 8r + m at bits 4m); sel[m] holds, in byte g, token g's code m (0..15).
+// Bytes k of the four words are gathered into one dword (two permutes per
+// pair of words, then one across the pairs), then split into nibbles.
+TQ_HD void lm4_value_selectors(const uint32_t w[4], uint32_t sel[8]) {
+  const uint32_t a = perm32(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+  const uint32_t b = perm32(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+  const uint32_t c = perm32(w[3], w[2], 0x05010400u);
+  const uint32_t d = perm32(w[3], w[2], 0x07030602u);
+  const uint32_t x[4] = {perm32(c, a, 0x05040100u), perm32(c, a, 0x07060302u), perm32(d, b, 0x05040100u),
+                         perm32(d, b, 0x07060302u)};  // x[k] byte g = byte k of w[g]
+  for (int k = 0; k < 4; ++k) {
+    sel[2 * k] = x[k] & 0x0F0F0F0Fu;
+    sel[2 * k + 1] = (x[k] >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+// 2-bit Lloyd-Max value codes: w[g] holds token g's 8 codes in bits 0..15
+// (dim 8r + m at bits 2m; bits 16..31 are not codes); sel[m] holds, in byte
+// g, token g's code m (0..3).
+TQ_HD void lm2_value_selectors(const uint32_t w[4], uint32_t sel[8]) {
+  const uint32_t a = perm32(w[1], w[0], 0x05010400u);
+  const uint32_t c = perm32(w[3], w[2], 0x05010400u);
+  const uint32_t x0 = perm32(c, a, 0x05040100u), x1 = perm32(c, a, 0x07060302u);
+  for (int m = 0; m < 8; ++m) sel[m] = ((m < 4 ? x0 : x1) >> (2 * (m & 3))) & 0x03030303u;
+}
+
 // Order of the 32 key dims of a 3-bit lane chunk in the MFMA operand: chunk c
 // (0..3) element e (0..7) holds dim 8*(e & 3) + 2c + (e >> 2).
 TQ_HD int key3_dim(int c, int e) { return 8 * (e & 3) + 2 * c + (e >> 2); }

@@ -95,6 +95,18 @@ template <>
 struct Base<TQ_3BIT_LM> {
   static constexpr int kFp8 = 0, kKb = 3, kVb = 3, kKdata = 48, kKps = 50, kVdata = 48, kSlot = 100, kVlm = 1;
 };
+template <>
+struct Base<TQ_K8V4LM> {
+  static constexpr int kFp8 = 1, kKb = 8, kVb = 4, kKdata = 128, kKps = 128, kVdata = 64, kSlot = 194, kVlm = 1;
+};
+template <>
+struct Base<TQ_4BIT_LM> {
+  static constexpr int kFp8 = 0, kKb = 4, kVb = 4, kKdata = 64, kKps = 66, kVdata = 64, kSlot = 132, kVlm = 1;
+};
+template <>
+struct Base<TQ_2BIT_LM> {
+  static constexpr int kFp8 = 0, kKb = 2, kVb = 2, kKdata = 32, kKps = 34, kVdata = 32, kSlot = 68, kVlm = 1;
+};
 
 // The geometry at the head_dim of preset code PD (a preset, plus kHead256
 // for two halves): fields of the whole slot; kHk / kHv are the key / value
@@ -127,14 +139,14 @@ template <int P>
 constexpr bool preset_geometry_ok() {
   using T = Base<P>;
   return T::kKdata == (T::kFp8 ? kD : kD * T::kKb / 8) && T::kKps == (T::kFp8 ? kD : T::kKdata + 2) &&
-         T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + (T::kVlm ? 2 : 4) + 1) / 2) * 2 &&
-         (!T::kVlm || T::kVb == 3);
+         T::kVdata == kD * T::kVb / 8 && T::kSlot == ((T::kKps + T::kVdata + (T::kVlm ? 2 : 4) + 1) / 2) * 2;
 }
 static_assert(preset_geometry_ok<TQ_K8V4>() && preset_geometry_ok<TQ_4BIT_NC>() &&
                   preset_geometry_ok<TQ_K3V4_NC>() && preset_geometry_ok<TQ_3BIT_NC>() &&
                   preset_geometry_ok<TQ_K8V3>() && preset_geometry_ok<TQ_K4V3_NC>() &&
                   preset_geometry_ok<TQ_2BIT_NC>() && preset_geometry_ok<TQ_K8V3LM>() &&
-                  preset_geometry_ok<TQ_3BIT_LM>(),
+                  preset_geometry_ok<TQ_3BIT_LM>() && preset_geometry_ok<TQ_K8V4LM>() &&
+                  preset_geometry_ok<TQ_4BIT_LM>() && preset_geometry_ok<TQ_2BIT_LM>(),
               "slot geometry");
 
 struct DecodeArgs {
@@ -688,20 +700,38 @@ __device__ __forceinline__ void score_tile(const TileRegs<P>& r, const LaneOff<P
 // (j < 4) or token 4q + j - 4 of tile `b`.
 // Lloyd-Max values (lv: their fp16 codebook) go through the byte-permute
 // lookup instead: selector n holds code n (dim 8 * row + n) of the tile's 4
-// tokens, so one lookup yields two tokens' fp16 centroids for that dim.
+// tokens, so one lookup yields two tokens' fp16 centroids for that dim
+// (4-bit codes: two 8-entry tables, picked by bit 3).
+struct ValLut {
+  tq::Lut8 lo, hi;  // fp16 centroids 0..7 and (4-bit codes) 8..15
+};
+
 template <int P>
 __device__ __forceinline__ void accumulate_half(const uint32_t (&av)[4], const uint32_t (&bv)[4], const half8& bp,
-                                                const tq::Lut8& lv, f32x4* acc) {
+                                                const ValLut& lv, f32x4* acc) {
   using T = Preset<P>;
   if constexpr (T::kVlm != 0) {
     uint32_t sa[8], sb[8];
-    tq::lm_value_selectors(av, sa);
-    tq::lm_value_selectors(bv, sb);
+    if constexpr (T::kVb == 4) {
+      tq::lm4_value_selectors(av, sa);
+      tq::lm4_value_selectors(bv, sb);
+    } else if constexpr (T::kVb == 2) {
+      tq::lm2_value_selectors(av, sa);
+      tq::lm2_value_selectors(bv, sb);
+    } else {
+      tq::lm_value_selectors(av, sa);
+      tq::lm_value_selectors(bv, sb);
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       uint32_t a0, a1, b0, b1;
-      tq::lut8(sa[n], lv, a0, a1);
-      tq::lut8(sb[n], lv, b0, b1);
+      if constexpr (T::kVb == 4) {
+        tq::lut16(sa[n], lv.lo, lv.hi, a0, a1);
+        tq::lut16(sb[n], lv.lo, lv.hi, b0, b1);
+      } else {
+        tq::lut8(sa[n], lv.lo, a0, a1);
+        tq::lut8(sb[n], lv.lo, b0, b1);
+      }
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0, a1, b0, b1), bp, acc[n], 0, 0, 0);
     }
   } else if constexpr (T::kVb == 4) {
@@ -734,7 +764,7 @@ __device__ __forceinline__ void accumulate_half(const uint32_t (&av)[4], const u
 // Both head halves of a pair of scored tiles (acc: 8 accumulators per half).
 template <int P>
 __device__ __forceinline__ void accumulate_pair(const PendingTile<P>& a, const PendingTile<P>& b,
-                                                const tq::Lut8& lv, f32x4* acc) {
+                                                const ValLut& lv, f32x4* acc) {
   using T = Preset<P>;
   u32x2a4 pa = __builtin_bit_cast(u32x2a4, a.pv), pb = __builtin_bit_cast(u32x2a4, b.pv);
   const half8 bp = as_half8(pa.x, pa.y, pb.x, pb.y);
@@ -765,7 +795,7 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 // accumulators hold nothing used.
 template <int P, int SOA>
 __device__ __forceinline__ void score_pair_packed(const uint8_t* imgA, const uint8_t* imgB, const LaneOff<P>& o,
-                                                  const tq::Lut8& la, const tq::Lut8& lb, const tq::Lut8& lv,
+                                                  const tq::Lut8& la, const tq::Lut8& lb, const ValLut& lv,
                                                   uint32_t klane, const half8* bq, int validA, int validB, int skipA, int skipB,
                                                   float gate, float glg, Softmax& sm, f32x4* acc) {
   using T = Preset<P>;
@@ -1398,7 +1428,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     return ((hb[base] >> shift) & 0xFF) | (((hb[base + 1] >> shift) & 0xFF) << 8) |
            (((hb[base + 2] >> shift) & 0xFF) << 16) | (((hb[base + 3] >> shift) & 0xFF) << 24);
   };
-  tq::Lut8 la{}, lb{}, lv{};
+  tq::Lut8 la{}, lb{};
+  ValLut lv{};
   if (!T::kFp8) {
     uint32_t hb[16] = {};
 #pragma unroll
@@ -1408,11 +1439,12 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     if (T::kKb == 4) lb = {lut_bytes(hb, 8, 0), lut_bytes(hb, 12, 0), lut_bytes(hb, 8, 8), lut_bytes(hb, 12, 8)};
   }
   if (T::kVlm) {
-    uint32_t hv[8];
+    uint32_t hv[16] = {};
     const float* vc = a.centroids + (T::kFp8 ? 0 : (1 << T::kKb));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hv[i] = __half_as_ushort(__float2half_rn(vc[i]));
-    lv = {lut_bytes(hv, 0, 0), lut_bytes(hv, 4, 0), lut_bytes(hv, 0, 8), lut_bytes(hv, 4, 8)};
+    for (int i = 0; i < (1 << T::kVb); ++i) hv[i] = __half_as_ushort(__float2half_rn(vc[i]));
+    lv.lo = {lut_bytes(hv, 0, 0), lut_bytes(hv, 4, 0), lut_bytes(hv, 0, 8), lut_bytes(hv, 4, 8)};
+    if (T::kVb == 4) lv.hi = {lut_bytes(hv, 8, 0), lut_bytes(hv, 12, 0), lut_bytes(hv, 8, 8), lut_bytes(hv, 12, 8)};
   }
   // 3-bit keys: the pair table, entry f = (c[f & 7], c[f >> 3]) in fp16 at
   // dword 64 f + copy (one copy per lane); the main loop's first barrier
@@ -1887,6 +1919,9 @@ int stage1(const tq_layout* layout, const void* query, int32_t q_dtype, int32_t 
     case TQ_2BIT_NC: return launch_stage1<TQ_2BIT_NC>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
     case TQ_K8V3LM: return launch_stage1<TQ_K8V3LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
     case TQ_3BIT_LM: return launch_stage1<TQ_3BIT_LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_K8V4LM: return launch_stage1<TQ_K8V4LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_4BIT_LM: return launch_stage1<TQ_4BIT_LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
+    case TQ_2BIT_LM: return launch_stage1<TQ_2BIT_LM>(a, value_gate, plan.tpw, soa, d256, nblocks, lds, stream);
   }
   return TQ_EPRESET;
 }

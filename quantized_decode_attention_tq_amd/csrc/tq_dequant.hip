@@ -265,6 +265,9 @@ int launch_preset(int32_t preset, const DequantArgs& a, int32_t out_dtype, hipSt
     case TQ_2BIT_NC: return launch_dequant<D, 0, 2, 2>(a, out_dtype, s);
     case TQ_K8V3LM: return launch_dequant<D, 1, 8, 3, 1>(a, out_dtype, s);
     case TQ_3BIT_LM: return launch_dequant<D, 0, 3, 3, 1>(a, out_dtype, s);
+    case TQ_K8V4LM: return launch_dequant<D, 1, 8, 4, 1>(a, out_dtype, s);
+    case TQ_4BIT_LM: return launch_dequant<D, 0, 4, 4, 1>(a, out_dtype, s);
+    case TQ_2BIT_LM: return launch_dequant<D, 0, 2, 2, 1>(a, out_dtype, s);
   }
   return TQ_EPRESET;
 }

@@ -25,9 +25,10 @@ struct PresetDef {
 
 // [PR] "实现拆解" item 1 (four named presets with key bits, value bits and
 // norm correction); "评论区精华" (k8v4 means FP8 keys and 4-bit values).
-// The last three follow [TQ+] "What landed": asymmetric pairs (FP8 or 4-bit
-// keys over 3-bit values) and the 2-bit codebook, with this library's key
-// and value codecs at those widths.
+// The rest follow [TQ+] "What landed": asymmetric pairs (FP8 or 4-bit keys
+// over 3-bit values), the 2-bit codebook, and Lloyd-Max values (the keys'
+// rotation and codebook family on the value rows) at 2, 3 and 4 bits, with
+// this library's key and value codecs at those widths.
 constexpr PresetDef kPresets[TQ_NUM_PRESETS] = {
     {"turboquant_k8v4", 1, 8, 4, 0, 0},
     {"turboquant_4bit_nc", 0, 4, 4, 1, 0},
@@ -38,6 +39,9 @@ constexpr PresetDef kPresets[TQ_NUM_PRESETS] = {
     {"turboquant_2bit_nc", 0, 2, 2, 1, 0},
     {"turboquant_k8v3lm", 1, 8, 3, 0, 1},
     {"turboquant_3bit_lm", 0, 3, 3, 1, 1},
+    {"turboquant_k8v4lm", 1, 8, 4, 0, 1},
+    {"turboquant_4bit_lm", 0, 4, 4, 1, 1},
+    {"turboquant_2bit_lm", 0, 2, 2, 1, 1},
 };
 
 }  // namespace

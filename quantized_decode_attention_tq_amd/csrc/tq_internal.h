@@ -108,11 +108,12 @@ struct DecodePlan {
 // Direct-to-LDS loads (1 KB each) a stage-1 wave issues per tile: at most
 // this many for any head count (a wave of G waves per tile takes ceil(spt /
 // G) of the tile's spt loads).  head_dim 128: slots of 196 / 134 / 118 / 102
-// / 180 / 118 / 70 / 178 / 100 bytes in preset order; SoA images pad each
+// / 180 / 118 / 70 / 178 / 100 / 194 / 132 / 68 bytes in preset order; SoA images pad each
 // image row by 16 bytes and round the data part and the metadata part up to
 // whole slots separately, which takes one load more with one KV head for
-// k8v4, 4bit_nc, 3bit_nc and 2bit_nc.  head_dim 256: slots of 388 / 262 / 230
-// / 198 / 356 / 230 / 134 / 354 / 196 bytes.
+// k8v4, 4bit_nc, 3bit_nc and 2bit_nc (and their Lloyd-Max-value twins).
+// head_dim 256: slots of 388 / 262 / 230 / 198 / 356 / 230 / 134 / 354 / 196
+// / 386 / 260 / 132 bytes.
 constexpr int max_dma_loads(int preset, bool soa = false, int head_dim = 128) {
   const bool d256 = head_dim == 256;
   switch (preset) {
@@ -125,6 +126,9 @@ constexpr int max_dma_loads(int preset, bool soa = false, int head_dim = 128) {
     case TQ_2BIT_NC: return d256 ? (soa ? 4 : 3) : (soa ? 3 : 2);
     case TQ_K8V3LM: return d256 ? (soa ? 7 : 6) : 4;
     case TQ_3BIT_LM: return d256 ? (soa ? 5 : 4) : (soa ? 3 : 2);
+    case TQ_K8V4LM: return d256 ? (soa ? 8 : 7) : (soa ? 5 : 4);
+    case TQ_4BIT_LM: return d256 ? (soa ? 6 : 5) : (soa ? 4 : 3);
+    case TQ_2BIT_LM: return d256 ? (soa ? 4 : 3) : (soa ? 3 : 2);
   }
   return 0;
 }

@@ -406,6 +406,9 @@ int launch_preset(int32_t preset, const StoreArgs& a, bool bf16, hipStream_t s) 
     case TQ_2BIT_NC: return launch_store<D, 0, 2, 2, 1>(a, bf16, s);
     case TQ_K8V3LM: return launch_store<D, 1, 8, 3, 0, 1>(a, bf16, s);
     case TQ_3BIT_LM: return launch_store<D, 0, 3, 3, 1, 1>(a, bf16, s);
+    case TQ_K8V4LM: return launch_store<D, 1, 8, 4, 0, 1>(a, bf16, s);
+    case TQ_4BIT_LM: return launch_store<D, 0, 4, 4, 1, 1>(a, bf16, s);
+    case TQ_2BIT_LM: return launch_store<D, 0, 2, 2, 1, 1>(a, bf16, s);
   }
   return TQ_EPRESET;
 }

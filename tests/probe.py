@@ -13,7 +13,7 @@ N_IN, N_OUT = 12, 8
 OPS = {"perm": 0, "alignbyte": 1, "key3_selectors": 2, "lut8": 3, "lut16": 4, "val4_pairs": 5, "val3_pairs": 6,
        "f32_to_e4m3": 7, "val2_pairs": 8, "key2_selectors": 9, "lm_value_selectors": 10,
        "key3_pair_fields": 11, "key3_pair_entries": 12,
-       "key3_pair_windows": 13}
+       "key3_pair_windows": 13, "lm4_value_selectors": 14, "lm2_value_selectors": 15}
 
 
 def lib():

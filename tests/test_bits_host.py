@@ -148,3 +148,19 @@ def test_lm_value_selectors_transpose_four_tokens():
     for m in range(8):
         for g in range(4):
             np.testing.assert_array_equal((out[:, m] >> (8 * g)) & 0xFF, codes[:, g, m])
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_lm_value_selectors_at_4_and_2_bits(bits):
+    """Four tokens' 4-bit (32-bit words) or 2-bit (bits 0..15, garbage above)
+    Lloyd-Max code words -> selector m holds token g's code m in byte g."""
+    codes = RNG.integers(0, 1 << bits, (3000, 4, 8))
+    nbytes = 8 * bits // 8
+    w = np.stack([_bytes_to_words(np.concatenate([O.pack_lsb(codes[:, g], bits),
+                                                  RNG.integers(0, 256, (3000, 4 - nbytes)).astype(np.uint8)],
+                                                 axis=1))[:, 0]
+                  for g in range(4)], axis=1)
+    out = probe.bits_host(f"lm{bits}_value_selectors", w)
+    for m in range(8):
+        for g in range(4):
+            np.testing.assert_array_equal((out[:, m] >> (8 * g)) & 0xFF, codes[:, g, m])

@@ -79,7 +79,8 @@ def test_fp8_to_f16_convert_all_codes():
 
 @pytest.mark.parametrize("op", ["perm", "alignbyte", "key3_selectors", "lut8", "lut16", "val4_pairs", "val3_pairs",
                                 "val2_pairs", "key2_selectors", "lm_value_selectors", "key3_pair_fields",
-                                "key3_pair_entries", "key3_pair_windows", "f32_to_e4m3"])
+                                "key3_pair_entries", "key3_pair_windows", "lm4_value_selectors",
+                                "lm2_value_selectors", "f32_to_e4m3"])
 def test_device_bits_match_host_model(op):
     n = 4096
     inp = RNG.integers(0, 2 ** 32, (n, probe.N_IN), dtype=np.uint64).astype(np.uint32)

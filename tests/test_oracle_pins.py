@@ -467,7 +467,8 @@ def test_encode_decode_slot_roundtrip():
             assert np.linalg.norm(kr - k) / np.linalg.norm(k) < {2: 0.45, 3: 0.3}.get(lay.key_bits, 0.2)
             np.testing.assert_allclose(np.linalg.norm(kh), np.linalg.norm(k), rtol=1e-3)
         if lay.value_lm:  # original space already; the matched norm keeps ||v||
-            assert np.linalg.norm(vh - v) / np.linalg.norm(v) < 0.3
+            # Lloyd-Max distortion of N(0, 1) at 2 / 3 / 4 bits: 0.118 / 0.035 / 0.0095
+            assert np.linalg.norm(vh - v) / np.linalg.norm(v) < {2: 0.45, 3: 0.3}.get(lay.value_bits, 0.2)
             np.testing.assert_allclose(np.linalg.norm(vh), np.linalg.norm(v), rtol=1e-3)
         else:
             assert np.max(np.abs(vh - v)) < (np.max(v) - np.min(v)) / ((1 << lay.value_bits) - 1)
@@ -720,6 +721,9 @@ SOA_CONSTANTS = {
     "turboquant_2bit_nc": (32 + 32, 3),
     "turboquant_k8v3lm": (128 + 48, 1),
     "turboquant_3bit_lm": (48 + 48, 2),
+    "turboquant_k8v4lm": (128 + 64, 1),
+    "turboquant_4bit_lm": (64 + 64, 2),
+    "turboquant_2bit_lm": (32 + 32, 2),
 }
 
 
