@@ -151,6 +151,7 @@ class DecodeBench:
         self.scale = scale_mult / math.sqrt(D)
         seen = np.minimum(self.lens, sliding_window) if sliding_window > 0 else self.lens
         self.bytes_read = int(seen.astype(np.int64).sum()) * w.num_kv_heads * self.lay.slot_size_aligned
+        self.row_bytes = w.num_kv_heads * self.lay.slot_size_aligned  # one token row, all KV heads
         self.sinks = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
         torch.cuda.synchronize()
         if warm:
@@ -239,20 +240,23 @@ class DecodeBench:
 
     def time_gather(self, launches=None):
         """The decode's tile reads alone (the probe library's gather kernel:
-        every 16-token tile of every sequence through the block table, no
-        arithmetic), median / p10 / p90 (ms) of `launches` launches rotating
-        over the cache copies: the ceiling of this read pattern."""
+        every 16-token tile of every sequence through the block table, split
+        evenly over 1024 workgroups, no arithmetic), median / p10 / p90 (ms)
+        of `launches` launches rotating
+        over the cache copies: the ceiling of this read pattern.  Token rows
+        must be whole 16-byte chunks (the probe's load width)."""
         torch, w = self.torch, self.w
         L = _probe_lib()
-        units = max(1, -(-1024 // w.batch))
-        out = torch.empty(4 * w.batch * units, dtype=torch.int32, device="cuda")
-        row = w.num_kv_heads * self.lay.slot_size_aligned
+        groups = 1024
+        out = torch.empty(4 * groups, dtype=torch.int32, device="cuda")
+        prefix = torch.from_numpy(np.concatenate([[0], np.cumsum(-(-self.lens // 16))]).astype(np.int32)).cuda()
+        row = self.row_bytes
         it = iter(range(1 << 30))
 
         def launch():
             c = self.caches[next(it) % N_COPIES]
-            rc = L.tq_probe_gather_read(c.data_ptr(), self.bt.data_ptr(), self.bt.shape[1], self.sl.data_ptr(),
-                                        w.batch, w.block_size, row, units, out.data_ptr(),
+            rc = L.tq_probe_gather_read(c.data_ptr(), self.bt.data_ptr(), self.bt.shape[1], prefix.data_ptr(),
+                                        w.batch, w.block_size, row, groups, out.data_ptr(),
                                         torch.cuda.current_stream().cuda_stream)
             assert rc == 0, rc
 
@@ -294,7 +298,37 @@ def store_sweep(torch, tq, steps, block_layout="aos", presets=None, head_dim=128
         res[preset] = {"mtok_s": n / (ms * 1e-3) / 1e6, "ms": ms, "gbs": bytes_moved / (ms * 1e-3) / 1e9,
                        "frac_hbm": bytes_moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del caches
+    torch.cuda.empty_cache()
+    # the ceiling of moving that many bytes: a plain device copy of half of
+    # them (read + write = the store's reads + writes at the first preset)
+    first = res[next(iter(res))]
+    copy = copy_ceiling(torch, int(first["gbs"] * first["ms"] * 1e6) // 2)
+    for k in list(res):
+        res[k]["frac_of_copy"] = res[k]["gbs"] / copy["gbs"]
+    res["copy"] = copy
     return res
+
+
+def copy_ceiling(torch, nbytes, reps=30):
+    """Median rate (read + write bytes per second) of a plain device copy of
+    `nbytes` (the probe library's copy kernel; three buffer pairs rotated so
+    that the 256 MB Infinity Cache cannot serve a copy from the previous)."""
+    L = _probe_lib()
+    nbytes = nbytes // 16 * 16
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(N_COPIES)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(N_COPIES)]
+    it = iter(range(1 << 30))
+
+    def launch():
+        i = next(it) % N_COPIES
+        rc = L.tq_probe_copy(src[i].data_ptr(), dst[i].data_ptr(), nbytes, 4096, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, rc
+
+    warm_gpu(torch, launch, 30.0)
+    t = spread(torch, launch, reps, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_each_way": nbytes, "us_median": t["median"] * 1e3, "gbs": 2 * nbytes / (t["median"] * 1e-3) / 1e9}
 
 
 def cpu_baseline(w: W.Workload, budget_s: float = 12.0, store_budget_s: float = 6.0):
@@ -531,7 +565,7 @@ def decode_leg(torch, tq, w, S, steps=None, warmup=None, **kw):
     res["decode_frac_hbm"] = res["decode_gbs"] / HBM_PEAK_GBS
     res["stage1_us"] = _us(s1)
     res["stage1_gbs"] = b.bytes_read / (s1["median"] * 1e-3) / 1e9
-    if kw.get("block_layout", "aos") == "aos" and not kw.get("sliding_window"):
+    if kw.get("block_layout", "aos") == "aos" and not kw.get("sliding_window") and b.row_bytes % 16 == 0:
         gr = b.time_gather()
         res["gather_read_us"] = _us(gr)
         res["gather_read_gbs"] = b.bytes_read / (gr["median"] * 1e-3) / 1e9
@@ -588,7 +622,7 @@ def main():
                                      warmup=max(6, args.warmup // 4))
             extra[name]["stream_read"] = stream_ceiling(torch, extra[name]["bytes_read"])
         extra["store_sweep"] = store_sweep(torch, tq, 50)
-        log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items()})}")
+        log(f"[store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in extra['store_sweep'].items() if k != 'copy'})}")
         extra["dequant"] = dequant_sweep(torch, tq, 20)
         log(f"[dequant] {json.dumps({k: round(v['gbs']) for k, v in extra['dequant'].items()})} GB/s")
         # the same workloads with the cache in the SoA block convention
@@ -597,7 +631,7 @@ def main():
             soa[name] = decode_leg(torch, tq, W.WORKLOADS[name], S, block_layout="soa")
         soa["store_sweep"] = store_sweep(torch, tq, 50, "soa")
         soa["dequant"] = dequant_sweep(torch, tq, 20, "soa")
-        log(f"[soa store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in soa['store_sweep'].items()})}; "
+        log(f"[soa store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in soa['store_sweep'].items() if k != 'copy'})}; "
             f"[soa dequant] {json.dumps({k: round(v['gbs']) for k, v in soa['dequant'].items()})} GB/s")
         extra["soa"] = soa
         # the further presets (asymmetric pairs, 2-bit, Lloyd-Max values) on the llama8b shape
@@ -607,7 +641,7 @@ def main():
             more[preset] = decode_leg(torch, tq, wk, args.splits)
         more["store_sweep"] = store_sweep(torch, tq, 50, presets=MORE_PRESETS)
         more["dequant"] = dequant_sweep(torch, tq, 20, presets=MORE_PRESETS)
-        log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items()})}; "
+        log(f"[more store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in more['store_sweep'].items() if k != 'copy'})}; "
             f"[more dequant] {json.dumps({k: round(v['gbs']) for k, v in more['dequant'].items()})} GB/s")
         extra["more_presets"] = more
         # head_dim 256: decode on the hd256 shape, store and dequant sweeps
@@ -617,7 +651,7 @@ def main():
             h256[preset] = decode_leg(torch, tq, wk, args.splits)
         h256["store_sweep"] = store_sweep(torch, tq, 50, presets=HEAD256_PRESETS, head_dim=256)
         h256["dequant"] = dequant_sweep(torch, tq, 20, presets=HEAD256_PRESETS, head_dim=256)
-        log(f"[hd256 store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in h256['store_sweep'].items()})}; "
+        log(f"[hd256 store] {json.dumps({k: round(v['mtok_s'], 1) for k, v in h256['store_sweep'].items() if k != 'copy'})}; "
             f"[hd256 dequant] {json.dumps({k: round(v['gbs']) for k, v in h256['dequant'].items()})} GB/s")
         extra["head256"] = h256
         # the opt-in sparse-V gate at 1e-3 (the pages' threshold), and with the

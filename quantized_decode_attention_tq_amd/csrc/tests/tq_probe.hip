@@ -121,25 +121,38 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (x == 0x9E3779B9u) out[blockIdx.x] = x;
 }
 
-// The decode's reads without its arithmetic: workgroup (b, u) reads tiles
-// [T u / U, T (u + 1) / U) of sequence b (T = ceil(L_b / 16); a tile is 16
-// consecutive token rows of row16 16-byte chunks inside one cache block,
-// found through the block table), 16-byte non-temporal loads, two tiles at
-// a time.  Wave w of the workgroup writes the XOR of the 32-bit words it
-// read to out[4 * blockIdx.x + w] (so a test can check the bytes covered).
+// The decode's reads without its arithmetic: the tiles of all sequences in
+// order (a tile is 16 consecutive token rows of row16 16-byte chunks inside
+// one cache block, found through the block table; sequence b holds tiles
+// prefix[b] .. prefix[b + 1] - 1 of the list), split evenly over the
+// workgroups whatever the mix of lengths, 16-byte non-temporal loads, two
+// tiles at a time.  Wave w of a workgroup writes the XOR of the 32-bit
+// words it read to out[4 * blockIdx.x + w] (so a test can check the bytes
+// covered).
 __global__ __launch_bounds__(256) void gather_read_kernel(const u32x4* __restrict__ cache,
                                                           const int32_t* __restrict__ block_table, int bt_stride,
-                                                          const int32_t* __restrict__ seq_lens, int block_size,
-                                                          int64_t row16, int units, uint32_t* __restrict__ out) {
-  const int b = blockIdx.x / units, u = blockIdx.x % units;
-  const int T = (seq_lens[b] + 15) / 16;
-  const int t0 = static_cast<int>(static_cast<int64_t>(T) * u / units);
-  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (u + 1) / units);
+                                                          const int32_t* __restrict__ prefix, int batch,
+                                                          int block_size, int64_t row16, uint32_t* __restrict__ out) {
+  const int64_t T = prefix[batch];
+  const int t0 = static_cast<int>(T * blockIdx.x / gridDim.x);
+  const int t1 = static_cast<int>(T * (blockIdx.x + 1) / gridDim.x);
   const int64_t tile16 = 16 * row16, blk16 = static_cast<int64_t>(block_size) * row16;
-  const int32_t* bt = block_table + static_cast<int64_t>(b) * bt_stride;
+  int b = 0;  // sequence of tile t0: the last b with prefix[b] <= t0
+  for (int lo = 0, hi = batch - 1; lo <= hi;) {
+    const int mid = (lo + hi) / 2;
+    if (prefix[mid] <= t0) {
+      b = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  // base of list tile t (t >= the tile last passed to it)
   auto tile_base = [&](int t) {
-    return cache + static_cast<int64_t>(bt[(t * 16) / block_size]) * blk16 +
-           static_cast<int64_t>((t * 16) % block_size) * row16;
+    while (prefix[b + 1] <= t) ++b;
+    const int j = t - prefix[b];  // tile of sequence b
+    const int32_t blk = block_table[static_cast<int64_t>(b) * bt_stride + (j * 16) / block_size];
+    return cache + static_cast<int64_t>(blk) * blk16 + static_cast<int64_t>((j * 16) % block_size) * row16;
   };
   uint32_t x = 0;
   int t = t0;
@@ -268,17 +281,16 @@ int tq_probe_stream_read(const void* in, int64_t bytes, int64_t chunk, uint32_t*
 }
 
 // The decode's tile reads of a paged cache (row_bytes: bytes of one token
-// row, all KV heads; a multiple of 16) by batch x units workgroups; out:
-// device uint32 [4 * batch * units].  Asynchronous on `stream`.
-int tq_probe_gather_read(const void* cache, const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
-                         int batch, int block_size, int64_t row_bytes, int units, uint32_t* out, void* stream) {
-  if (batch <= 0 || units <= 0 || row_bytes <= 0 || row_bytes % 16 || block_size < 16 || block_size % 16)
+// row, all KV heads, a multiple of 16; prefix: device int32 [batch + 1],
+// prefix[b] = tiles of sequences 0 .. b - 1) by `groups` workgroups; out:
+// device uint32 [4 * groups].  Asynchronous on `stream`.
+int tq_probe_gather_read(const void* cache, const int32_t* block_table, int bt_stride, const int32_t* prefix,
+                         int batch, int block_size, int64_t row_bytes, int groups, uint32_t* out, void* stream) {
+  if (batch <= 0 || groups <= 0 || row_bytes <= 0 || row_bytes % 16 || block_size < 16 || block_size % 16)
     return -1;
-  const int64_t blocks = static_cast<int64_t>(batch) * units;
-  if (blocks > 0x7FFFFFFF) return -1;
-  hipLaunchKernelGGL(gather_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+  hipLaunchKernelGGL(gather_read_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(cache), block_table, bt_stride,
-                     seq_lens, block_size, row_bytes / 16, units, out);
+                     prefix, batch, block_size, row_bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 

@@ -137,18 +137,19 @@ def test_hardware_fp8_encode_matches_software_encoder(kind):
         np.testing.assert_array_equal(out[inr, col], sw[inr])
 
 
-@pytest.mark.parametrize("block_size,row_bytes,units", [(16, 1568, 4), (128, 944, 3), (32, 816, 1)])
-def test_gather_read_covers_the_decode_tiles(block_size, row_bytes, units):
+@pytest.mark.parametrize("block_size,row_bytes,groups", [(16, 1568, 7), (128, 944, 3), (32, 816, 40)])
+def test_gather_read_covers_the_decode_tiles(block_size, row_bytes, groups):
     """The gather-read ceiling probe (the decode's tile reads without its
-    arithmetic, timed by the benchmark) reads exactly the tiles of each
-    sequence through the block table: per workgroup, the XOR of its waves'
-    outputs equals the XOR of every 32-bit word of its tiles."""
+    arithmetic, timed by the benchmark) reads exactly the tiles of every
+    sequence through the block table, split evenly over the workgroups: per
+    workgroup, the XOR of its waves' outputs equals the XOR of every 32-bit
+    word of its share of the tile list (an empty sequence included)."""
     import torch
 
-    lens = np.array([1, 16, 17, 250, 513, 64], np.int32)
+    lens = np.array([1, 16, 0, 17, 250, 513, 64], np.int32)
     B = len(lens)
     bpseq = -(-lens // block_size)
-    width = int(bpseq.max())
+    width = max(1, int(bpseq.max()))
     nb = int(bpseq.sum()) + 3
     perm = RNG.permutation(nb).astype(np.int32)
     table = np.zeros((B, width), np.int32)
@@ -156,23 +157,26 @@ def test_gather_read_covers_the_decode_tiles(block_size, row_bytes, units):
     for b in range(B):
         table[b, : bpseq[b]] = perm[k : k + bpseq[b]]
         k += bpseq[b]
+    tiles = -(-lens // 16)
+    prefix = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32)
     words = RNG.integers(0, 2 ** 32, nb * block_size * row_bytes // 4, dtype=np.uint64).astype(np.uint32)
     cache = torch.from_numpy(words.view(np.int32)).cuda()
-    bt, sl = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
-    out = torch.zeros(4 * B * units, dtype=torch.int32, device="cuda")
-    print(f"probe gather read bs={block_size} row={row_bytes} units={units}", flush=True)
-    rc = probe.lib().tq_probe_gather_read(cache.data_ptr(), bt.data_ptr(), width, sl.data_ptr(), B, block_size,
-                                          row_bytes, units, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    bt, pf = torch.from_numpy(table).cuda(), torch.from_numpy(prefix).cuda()
+    out = torch.zeros(4 * groups, dtype=torch.int32, device="cuda")
+    print(f"probe gather read bs={block_size} row={row_bytes} groups={groups}", flush=True)
+    rc = probe.lib().tq_probe_gather_read(cache.data_ptr(), bt.data_ptr(), width, pf.data_ptr(), B, block_size,
+                                          row_bytes, groups, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()
-    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).reshape(B * units, 4), axis=1)
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).reshape(groups, 4), axis=1)
     rows = words.reshape(nb * block_size, row_bytes // 4)
-    for b in range(B):
-        T = -(-int(lens[b]) // 16)
-        for u in range(units):
-            want = np.uint32(0)
-            for t in range(T * u // units, T * (u + 1) // units):
-                blk = table[b, (t * 16) // block_size]
-                r0 = blk * block_size + (t * 16) % block_size
-                want ^= np.bitwise_xor.reduce(rows[r0 : r0 + 16].ravel())
-            assert got[b * units + u] == want, (b, u)
+    seq_of = np.repeat(np.arange(B), tiles)  # list tile -> sequence
+    T = int(prefix[-1])
+    for g in range(groups):
+        want = np.uint32(0)
+        for t in range(T * g // groups, T * (g + 1) // groups):
+            b = seq_of[t]
+            j = t - prefix[b]
+            r0 = table[b, (j * 16) // block_size] * block_size + (j * 16) % block_size
+            want ^= np.bitwise_xor.reduce(rows[r0 : r0 + 16].ravel())
+        assert got[g] == want, g
