@@ -1212,6 +1212,12 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
 // the phase-0 wave writes the split's partial rows.  head_dim 256 (two
 // halves: twice the accumulators and query operands) runs one tile per wave
 // and keeps 2 waves per SIMD's registers.
+// Pad (bytes) after each 16-token tile-image row of a contiguous image of
+// cache rows of `row` bytes: 16 when the row's dword count is a multiple of
+// 8 modulo 64 (the LDS has 64 banks of 4 bytes; 16 rows would fall on 8
+// bank groups, rows r and r + 8 colliding), else none.
+constexpr uint32_t fix_row_pad(int row) { return ((row / 4) % 64) % 8 == 0 ? 16u : 0u; }
+
 // GATE: the body honours the sparse-V gate vgate (> 0, on exp(s - exact
 // running max)); the default kernel is built without its code and keeps a
 // single argument, the gated one takes the gate as a second.
@@ -1288,9 +1294,14 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   // chunks covering row piece r: from its start aligned down to 16 bytes up
   // to its end aligned up, so no chunk crosses the end of its cache block
   auto piece_chunks = [&](int r) { return (((geo.base + r * geo.row) & 15u) + piece + 15u) >> 4; };
+  // Fixed geometry: the image rows sit kRowPad bytes apart beyond the cache
+  // row, where a cache row's dword count is a multiple of 8 mod 64 (then
+  // lanes reading one column of rows r and r + 8 would share LDS banks)
+  constexpr uint32_t kRowPad = FIX ? fix_row_pad(8 * T::kSlot) : 0u;
+  const uint32_t lrow = geo.row + kRowPad;  // LDS bytes per image row (contiguous images)
   uint32_t tc;  // 16-byte chunks of one tile image
   if (geo.contiguous) {
-    tc = geo.row;  // 16 rows of `row` bytes
+    tc = lrow;  // 16 rows of `lrow` bytes
   } else {
     tc = 0;
     for (int r = 0; r < 16; ++r) tc += piece_chunks(r);
@@ -1298,14 +1309,15 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   // LDS start of token row r: chunk prefix of the rows before it plus the
   // row piece's misalignment
   auto row_start = [&](int r) -> uint32_t {
-    if (geo.contiguous) return r * geo.row;
+    if (geo.contiguous) return r * lrow;
     uint32_t c = 0;
     for (int i = 0; i < r; ++i) c += piece_chunks(i);
     return 16 * c + ((geo.base + r * geo.row) & 15u);
   };
 
   // ---- ring: this wave's DMA slots of each super-tile ----
-  constexpr int kSpt8 = (8 * T::kSlot + 63) / 64;  // 1 KB slots of a fixed-geometry tile image
+  constexpr int kSpt8 = (8 * T::kSlot + kRowPad + 63) / 64;  // 1 KB slots of a fixed-geometry tile image
+  static_assert(!FIX || kSpt8 == (8 * T::kSlot + 63) / 64, "row pad fits the plan's slots");
   const int spt = FIX ? kSpt8 : a.spt;
   Ring<P, SOA> ring;
   ring.lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tq_ring)));
@@ -1349,7 +1361,14 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     }
     uint32_t c = min(static_cast<uint32_t>(64 * n + lane), tc - 1);
     if (geo.contiguous) {
-      ring.off[k] = 16 * c;
+      if constexpr (kRowPad != 0) {
+        // image chunk c = row r, chunk j of lrow / 16; the pad chunks re-read
+        // the row's last chunk (an L2 hit)
+        const uint32_t rc = lrow / 16u, r = c / rc, j = min(c % rc, geo.row / 16u - 1u);
+        ring.off[k] = r * geo.row + 16u * j;
+      } else {
+        ring.off[k] = 16 * c;
+      }
     } else {
       int r = 0;
       uint32_t first = 0;  // first chunk of row r
