@@ -8,16 +8,19 @@
 // G * P wave64s take the range's 16-token tiles (P phases per head) and merge
 // in LDS at the end.  Per tile a wave:
 //   - builds the key tile (16 tokens x 128 dims) as fp16 MFMA operands: FP8
-//     keys by the hardware FP8->fp16 convert, Lloyd-Max codes through a
-//     v_perm byte lookup of the fp16 codebook;
+//     keys by the hardware FP8->fp16 convert, 3-bit Lloyd-Max codes two dims
+//     at a time through an LDS table of fp16 centroid pairs, 2- and 4-bit
+//     codes through a v_perm byte lookup of the fp16 codebook;
 //   - scores S^T = K . Q^T with 4 MFMA 16x16x32 f16 (tokens on rows, query
-//     heads on columns), the query rotated by the same transform and
-//     pre-scaled by scale*log2(e) (MSE presets, [API] _decode_attention);
+//     heads on columns), the query rotated by the same transform (MSE
+//     presets, [API] _decode_attention) and pre-scaled by scale*log2(e) and
+//     a per-head power of two that keeps its fp16 operand in range;
 //   - applies the per-token key norm, an online softmax in base 2, and
-//   - accumulates O^T = V^T . P^T with 8 MFMA 16x16x32 f16 per pair of tiles, the value codes
-//     entering as fp16 subnormals (no conversion) and the per-token value
-//     scale folded into P; the per-token zero point is accumulated on the
-//     VALU as sum(p * zero).
+//   - accumulates O^T = V^T . P^T with 8 MFMA 16x16x32 f16 per pair of
+//     tiles, uniform value codes entering as fp16 subnormals (no conversion)
+//     with the per-token value scale folded into P and the zero point
+//     accumulated on the VALU as sum(p * zero); Lloyd-Max value codes through
+//     a byte lookup of their fp16 codebook.
 // The GQA group rides on the MFMA's 16 columns, so the key/value bytes of a
 // (token, KV head) are read and decoded once for all its query heads.
 // Both block conventions of the cache (combined slots, SoA data + metadata
