@@ -57,6 +57,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef const __attribute__((address_space(4))) int32_t cint32;  // constant (scalar-loadable) memory
+typedef const __attribute__((address_space(4))) float cfloat;
 
 // Slot geometry per preset at head_dim 128 (see tq_layout_init).
 template <int P>
@@ -1008,13 +1009,60 @@ __device__ __forceinline__ float operand_scale(float lane_absmax) {
   return __uint_as_float(static_cast<uint32_t>(min(max(e, -126), 126) + 127) << 23);
 }
 
+// The lane's raw query words (and, for MSE keys, the rotation signs of its
+// dims), loaded apart from the arithmetic so that a workgroup can wait for
+// them before it issues its first tile loads and then compute the operand
+// while those are in flight: the wait a compiler places before a register's
+// first use drains every older vector-memory access, tile loads included.
 template <int P>
-__device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk, int h0, int geff, int hl, int q4,
-                                              half8* bq, float& fi) {
+struct QueryRaw {
+  static constexpr int kN = 4 * Preset<P>::kNh;
+  u32x4a4 w[kN];                                // FP8: [half][dims 64 h + 16 q4 (+8)]; MSE: [half][8 k]
+  f32x4 s[Preset<P>::kFp8 ? 1 : 2 * kN];       // MSE: signs of the dims of w[i], two per word group
+};
+
+template <int P>
+__device__ __forceinline__ void query_load(const DecodeArgs& a, int b, int hk, int h0, bool live, int hl, int q4,
+                                           QueryRaw<P>& r) {
   using T = Preset<P>;
-  const bool live = hl < geff;
   const uint16_t* qrow =
       a.query + (static_cast<int64_t>(b) * a.num_q_heads + hk * a.group + h0 + (live ? hl : 0)) * T::kDim;
+#pragma unroll
+  for (int hh = 0; hh < T::kNh; ++hh) {
+    if constexpr (T::kFp8 != 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        r.w[4 * hh + 2 * h] = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4);
+        r.w[4 * hh + 2 * h + 1] = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4 + 8);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d0 = 128 * hh + 32 * q4 + 8 * k;
+        r.w[4 * hh + k] = *reinterpret_cast<const u32x4a4*>(qrow + d0);
+        r.s[2 * (4 * hh + k)] = *reinterpret_cast<const f32x4*>(a.signs + d0);
+        r.s[2 * (4 * hh + k) + 1] = *reinterpret_cast<const f32x4*>(a.signs + d0 + 4);
+      }
+    }
+  }
+}
+
+// Make the loaded words resident (the compiler waits for them here).
+template <int P>
+__device__ __forceinline__ void query_wait(const QueryRaw<P>& r) {
+#pragma unroll
+  for (int i = 0; i < QueryRaw<P>::kN; ++i) asm volatile("" ::"v"(r.w[i].x), "v"(r.w[i].y), "v"(r.w[i].z), "v"(r.w[i].w));
+  if constexpr (Preset<P>::kFp8 == 0) {
+#pragma unroll
+    for (int i = 0; i < 2 * QueryRaw<P>::kN; ++i)
+      asm volatile("" ::"v"(r.s[i].x), "v"(r.s[i].y), "v"(r.s[i].z), "v"(r.s[i].w));
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void query_operand(const DecodeArgs& a, const QueryRaw<P>& r, bool live, half8* bq,
+                                              float& fi) {
+  using T = Preset<P>;
   const bool bf = a.q_bf16 != 0;
   float v[T::kNh][32];
   if constexpr (T::kFp8 != 0) {
@@ -1024,8 +1072,7 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
     for (int hh = 0; hh < T::kNh; ++hh)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4a4 w0 = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4);
-      const u32x4a4 w1 = *reinterpret_cast<const u32x4a4*>(qrow + 128 * hh + 64 * h + 16 * q4 + 8);
+      const u32x4a4 w0 = r.w[4 * hh + 2 * h], w1 = r.w[4 * hh + 2 * h + 1];
       const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1055,10 +1102,8 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, int b, int hk
     for (int hh = 0; hh < T::kNh; ++hh) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int d0 = 128 * hh + 32 * q4 + 8 * k;
-        const u32x4a4 w = *reinterpret_cast<const u32x4a4*>(qrow + d0);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.signs + d0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.signs + d0 + 4);
+        const u32x4a4 w = r.w[4 * hh + k];
+        const f32x4 s0 = r.s[2 * (4 * hh + k)], s1 = r.s[2 * (4 * hh + k) + 1];
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1128,6 +1173,7 @@ struct UnitRange {
   int b;                 // sequence of the unit, -1 if the unit is idle
   int t_begin, t_end;    // its tiles [t_begin, t_end) of sequence b
   int first_u, count_u;  // units of sequence u (the table entry unit u writes; 0, 0 if u >= batch)
+  int len;               // seq_lens[b] (0 if the unit is idle)
 };
 
 // Every sequence b with tiles_b = ceil(L_b / 16) > 0 gets S_b = ceil(tiles_b
@@ -1141,31 +1187,40 @@ __device__ __forceinline__ int window_start(int seq_len, int window) {
   return window > 0 ? max(0, seq_len - window) : 0;
 }
 
-__device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_lens, int B, int U, int u,
+// l0: seq_lens[lane] (0 for lane >= B), loaded by the caller ahead of time.
+// Up to 64 sequences each lane keeps its own length in a register; longer
+// batches walk seq_lens 64 at a time.  tau is searched between ceil(T / U)
+// and the smallest budget known to fit: sum_b ceil(t_b / tau) < T / tau + B,
+// so tau = ceil(T / (U - B)) fits whenever U > B (and tau = max_b t_b
+// always: one unit per sequence, U >= B).
+__device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_lens, int l0, int B, int U, int u,
                                                int window) {
   const int lane = threadIdx.x & 63;
-  // tiles of sequence bb inside its window (tile indices from the window's first tile)
-  auto tiles = [&](int bb) {
-    if (bb >= B) return 0;
-    const int L = seq_lens[bb];
-    return L > 0 ? ((L + 15) >> 4) - (window_start(L, window) >> 4) : 0;
-  };
-  int T = 0, tmx = 0;
-  for (int bb = lane; bb < B; bb += 64) {
-    const int t = tiles(bb);
-    T += t;
-    tmx = max(tmx, t);
+  const bool one = B <= 64;  // every length in l0
+  auto len_of = [&](int bb) { return bb < B ? seq_lens[bb] : 0; };
+  // tiles of a sequence of length L inside its window (tile indices from the window's first tile)
+  auto tiles_of = [&](int L) { return L > 0 ? ((L + 15) >> 4) - (window_start(L, window) >> 4) : 0; };
+  const int tl0 = tiles_of(l0);
+  int T = tl0, tmx = tl0;
+  if (!one) {
+    for (int bb = lane + 64; bb < B; bb += 64) {
+      const int t = tiles_of(len_of(bb));
+      T += t;
+      tmx = max(tmx, t);
+    }
   }
   T = wave_sum_i(T);
   tmx = wave_max_i(tmx);
   int tau = 1;
   if (T > 0) {
     auto units_for = [&](int tt) {
-      int c = 0;
-      for (int bb = lane; bb < B; bb += 64) c += (tiles(bb) + tt - 1) / tt;
+      int c = (tl0 + tt - 1) / tt;
+      if (!one)
+        for (int bb = lane + 64; bb < B; bb += 64) c += (tiles_of(len_of(bb)) + tt - 1) / tt;
       return wave_sum_i(c);
     };
-    int lo = max(1, (T + U - 1) / U), hi = max(lo, tmx);  // units_for(tmx) <= B <= U
+    int lo = max(1, (T + U - 1) / U), hi = max(lo, tmx);
+    if (U > B) hi = max(lo, min(hi, (T + (U - B) - 1) / (U - B)));
     if (units_for(lo) > U) {
       ++lo;
       while (lo < hi) {
@@ -1178,10 +1233,11 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
     }
     tau = lo;
   }
-  UnitRange r{-1, 0, 0, 0, 0};
+  UnitRange r{-1, 0, 0, 0, 0, 0};
   int base = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
-    const int t = tiles(b0 + lane);
+    const int len = b0 == 0 ? l0 : len_of(b0 + lane);
+    const int t = b0 == 0 ? tl0 : tiles_of(len);
     const int sb = (t + tau - 1) / tau;
     const int incl = wave_incl_scan_i(sb);
     const int total = __shfl(incl, 63, 64);
@@ -1191,12 +1247,13 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
     }
     if (r.b < 0 && u < base + total) {
       const uint64_t m = __ballot(base + incl > u);
-      const int L = __builtin_ctzll(m);
-      const int first = base + __shfl(incl - sb, L, 64);
-      const int nsb = __shfl(sb, L, 64);
-      const int tb = __shfl(t, L, 64);
+      const int lb = __builtin_ctzll(m);  // lane of the unit's sequence
+      const int first = base + __shfl(incl - sb, lb, 64);
+      const int nsb = __shfl(sb, lb, 64);
+      const int tb = __shfl(t, lb, 64);
       const int chunk = (tb + nsb - 1) / nsb;
-      r.b = b0 + L;
+      r.b = b0 + lb;
+      r.len = __shfl(len, lb, 64);
       r.t_begin = min((u - first) * chunk, tb);
       r.t_end = min(r.t_begin + chunk, tb);
     }
@@ -1255,21 +1312,34 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   const int hk = hgp * G + hh;
   const int hl = lane & 15, q4 = lane >> 4;
 
+  // The lengths go out first (the unit search waits on them), then the
+  // codebook values (scalar loads, so that no wait on vector memory covers
+  // them); the tables built from these wait until the first tiles are in flight.
+  const int l0 = lane < a.batch ? a.seq_lens[lane] : 0;
+  const cfloat* cen = (const cfloat*)(a.centroids);
+  constexpr int kNk = T::kFp8 ? 0 : (1 << T::kKb), kNv = T::kVlm ? (1 << T::kVb) : 0;
+  float ck[kNk > 0 ? kNk : 1], cv[kNv > 0 ? kNv : 1];
+#pragma unroll
+  for (int i = 0; i < kNk; ++i) ck[i] = cen[i];
+#pragma unroll
+  for (int i = 0; i < kNv; ++i) cv[i] = cen[kNk + i];
+
   // ---- unit -> (sequence, tile range): length-balanced split ----
-  UnitRange ur = find_unit(a.seq_lens, a.batch, a.num_units, u, a.window);
+  UnitRange ur = find_unit(a.seq_lens, l0, a.batch, a.num_units, u, a.window);
   // uniform by construction (cross-lane results): tell the compiler
   ur.b = __builtin_amdgcn_readfirstlane(ur.b);
   ur.t_begin = __builtin_amdgcn_readfirstlane(ur.t_begin);
   ur.t_end = __builtin_amdgcn_readfirstlane(ur.t_end);
   ur.first_u = __builtin_amdgcn_readfirstlane(ur.first_u);
   ur.count_u = __builtin_amdgcn_readfirstlane(ur.count_u);
+  ur.len = __builtin_amdgcn_readfirstlane(ur.len);
   if (u < a.batch && hgp == 0 && hg == 0 && w == 0 && lane == 0) {  // table entry of sequence u
     a.table[2 * u] = ur.first_u;
     a.table[2 * u + 1] = ur.count_u;
   }
   if (ur.b < 0) return;  // idle unit (uniform over the workgroup)
   const int b = ur.b;
-  const int seqlen = a.seq_lens[b];
+  const int seqlen = ur.len;
   const int wstart = window_start(seqlen, a.window);  // tokens before it are masked out of their tile
   const int t_begin = ur.t_begin + (wstart >> 4);     // absolute tile indices of the sequence
   const int t_end = ur.t_end + (wstart >> 4);
@@ -1287,6 +1357,9 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     }
     return;
   }
+  // the query words: issued now, resident before the first tile loads go out
+  QueryRaw<P> qraw;
+  query_load<P>(a, b, hk, h0, hl < geff, hl, q4, qraw);
 
   // ---- tile image geometry ----
   ImageGeom geo;
@@ -1433,17 +1506,21 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   };
   const int nst = (t_end - t_begin + Q - 1) / Q;
   const int pre = min(R - 1, nst);
-  for (int d = 0; d < pre; ++d) issue(d, d, blocks_of(d));
+  const Blk blk0 = blocks_of(0);
+  query_wait<P>(qraw);
+  issue(0, 0, blk0);
+  for (int d = 1; d < pre; ++d) issue(d, d, blocks_of(d));
   Blk blk_next = blocks_of(R - 1);  // next refill's block ids, fetched a step ahead
 
-  // ---- query operand and codebook tables (registers) ----
+  // ---- query operand (registers), computed while the first tiles load ----
   half8 bq[4 * T::kNh];
   float qfi;
-  query_operand<P>(a, b, hk, h0, geff, hl, q4, bq, qfi);
+  query_operand<P>(a, qraw, hl < geff, bq, qfi);
   if constexpr (PACK != 0) {  // columns 8..15 carry tile B's scores of head c - 8: its units
     const float fb = swap8(qfi);
     if (hl >= 8) qfi = fb;
   }
+
   // fp16 codebooks for the byte-permute lookups: keys (la, lb), Lloyd-Max
   // values (lv, the value codebook after the key codebook in the table)
   auto lut_bytes = [](const uint32_t* hb, int base, int shift) {
@@ -1452,19 +1529,17 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   };
   tq::Lut8 la{}, lb{};
   ValLut lv{};
-  if (!T::kFp8) {
+  if constexpr (kNk > 0) {
     uint32_t hb[16] = {};
 #pragma unroll
-    for (int i = 0; i < (1 << (T::kFp8 ? 0 : T::kKb)); ++i)
-      hb[i] = __half_as_ushort(__float2half_rn(a.centroids[i]));
+    for (int i = 0; i < kNk; ++i) hb[i] = __half_as_ushort(__float2half_rn(ck[i]));
     la = {lut_bytes(hb, 0, 0), lut_bytes(hb, 4, 0), lut_bytes(hb, 0, 8), lut_bytes(hb, 4, 8)};
     if (T::kKb == 4) lb = {lut_bytes(hb, 8, 0), lut_bytes(hb, 12, 0), lut_bytes(hb, 8, 8), lut_bytes(hb, 12, 8)};
   }
-  if (T::kVlm) {
+  if constexpr (kNv > 0) {
     uint32_t hv[16] = {};
-    const float* vc = a.centroids + (T::kFp8 ? 0 : (1 << T::kKb));
 #pragma unroll
-    for (int i = 0; i < (1 << T::kVb); ++i) hv[i] = __half_as_ushort(__float2half_rn(vc[i]));
+    for (int i = 0; i < kNv; ++i) hv[i] = __half_as_ushort(__float2half_rn(cv[i]));
     lv.lo = {lut_bytes(hv, 0, 0), lut_bytes(hv, 4, 0), lut_bytes(hv, 0, 8), lut_bytes(hv, 4, 8)};
     if (T::kVb == 4) lv.hi = {lut_bytes(hv, 8, 0), lut_bytes(hv, 12, 0), lut_bytes(hv, 8, 8), lut_bytes(hv, 12, 8)};
   }
