@@ -960,6 +960,24 @@ __device__ __forceinline__ void vm_wait(int n) {
   }
 }
 
+// Instruction-issue priority of a wave from its progress through its unit:
+// 3 until half of the unit's super-tiles are done, 2 until three quarters,
+// 1 until seven eighths, then 0.  Two workgroups share a CU and hold equal
+// work, but at equal priority issue favours the older waves: the first one
+// runs ahead and the second finishes alone with the CU half used.  Dropping
+// the leader's priority at these marks lets the other catch up at each one.
+__device__ __forceinline__ void progress_prio(int done, int total, int& cur) {
+  const int p = 8 * done >= 7 * total ? 0 : (4 * done >= 3 * total ? 1 : (2 * done >= total ? 2 : 3));
+  if (p == cur) return;
+  cur = p;
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // Workgroup barrier that first drains this wave's LDS reads, so a ring entry
 // released at the barrier has no read of it still in flight.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -1628,7 +1646,9 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     // two entries: super-tile u in entry u & 1; this wave's loads of u + 1 are
     // its only ones in flight once u has arrived
     constexpr uint32_t kEntry = static_cast<uint32_t>(TPW * kSpt8) * 1024u;
+    int prio = -1;
     for (int u = 0; u < nst; u += 2) {
+      progress_prio(u, nst, prio);
       vm_wait(0);
       wg_barrier();
       if (u + 1 < nst) {
@@ -1647,7 +1667,9 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     }
   } else {
     int entry = 0;
+    int prio = -1;
     for (int u = 0; u < nst; ++u) {
+      progress_prio(u, nst, prio);
       vm_wait(TPW * ring.my_loads * min(R - 2, nst - 1 - u));
       wg_barrier();
       if (u + R - 1 < nst) {
