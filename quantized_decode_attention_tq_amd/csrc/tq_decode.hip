@@ -997,14 +997,21 @@ __device__ __forceinline__ void wht128_quarters(float v[32]) {
       }
     }
   }
+  // strides 32 and 64 (lane quarters q4 ^ 1, q4 ^ 2) through the row swaps:
+  // permlane16_swap(v, v) returns (own, partner) in lanes with bit 4 clear
+  // and (partner, own) where it is set, permlane32_swap the same for bit 5;
+  // so r0 + s * r1, s = -1 where the bit is set, is v + partner in the lower
+  // lane of each pair and partner - v in the upper one (exact: one rounding)
+  const float s16 = (threadIdx.x & 16) ? -1.f : 1.f, s32 = (threadIdx.x & 32) ? -1.f : 1.f;
 #pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {  // strides 32 and 64: lane quarters q4 ^ 1, q4 ^ 2
-    const bool upper = (threadIdx.x & m) != 0;
+  for (int j = 0; j < 32; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+    v[j] = fmaf(s16, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float o = __shfl_xor(v[j], m, 64);
-      v[j] = upper ? o - v[j] : v[j] + o;
-    }
+  for (int j = 0; j < 32; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+    v[j] = fmaf(s32, __uint_as_float(r[1]), __uint_as_float(r[0]));
   }
 }
 
@@ -1562,15 +1569,17 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     if (T::kVb == 4) lv.hi = {lut_bytes(hv, 8, 0), lut_bytes(hv, 12, 0), lut_bytes(hv, 8, 8), lut_bytes(hv, 12, 8)};
   }
   // 3-bit keys: the pair table, entry f = (c[f & 7], c[f >> 3]) in fp16 at
-  // dword 64 f + copy (one copy per lane); the main loop's first barrier
-  // orders these writes before any lookup
+  // dword 64 f + copy (one copy per lane), written four equal copies at a
+  // time; the main loop's first barrier orders these writes before any lookup
   if constexpr (kLut != 0) {
-    uint32_t* lut = reinterpret_cast<uint32_t*>(tq_lds);
-    for (int i = static_cast<int>(threadIdx.x); i < 64 * tq::kKey3LutCopies; i += static_cast<int>(blockDim.x)) {
-      const uint32_t f = static_cast<uint32_t>(i / tq::kKey3LutCopies);
+    f32x4* lut = reinterpret_cast<f32x4*>(tq_lds);
+    constexpr int kPer = tq::kKey3LutCopies / 4;  // 16-byte writes per entry
+    for (int i = static_cast<int>(threadIdx.x); i < 64 * kPer; i += static_cast<int>(blockDim.x)) {
+      const uint32_t f = static_cast<uint32_t>(i / kPer);
       uint32_t pair, unused;
       tq::lut8((f & 7u) | ((f >> 3) << 8), la, pair, unused);  // (c[f & 7], c[f >> 3])
-      lut[i] = pair;
+      const float x = __uint_as_float(pair);
+      lut[i] = f32x4{x, x, x, x};
     }
   }
   // LDS address of this lane's copy of table entry 0: the kernels declare no

@@ -99,7 +99,10 @@ def test_device_bits_match_host_model(op):
 def test_permlane_swaps_pair_each_lane_with_its_partner():
     """The decode kernel's quarter reductions rely on permlane16_swap(v, v)
     leaving lane l holding {v[l], v[l ^ 16]} across its two results, and
-    permlane32_swap(v, v) holding {v[l], v[l ^ 32]}."""
+    permlane32_swap(v, v) holding {v[l], v[l ^ 32]}; its Walsh-Hadamard
+    butterflies on which result is which: the first holds the lane's own
+    value where bit 4 (bit 5) of the lane is clear and the partner's where
+    it is set, the second the other one."""
     import torch
 
     v = np.arange(64, dtype=np.uint32) * 7 + 1000
@@ -111,6 +114,10 @@ def test_permlane_swaps_pair_each_lane_with_its_partner():
     for l in range(64):
         assert {int(out[0, l]), int(out[1, l])} == {int(v[l]), int(v[l ^ 16])}, l
         assert {int(out[2, l]), int(out[3, l])} == {int(v[l]), int(v[l ^ 32])}, l
+        for row, bit in ((0, 16), (2, 32)):
+            own, partner = int(v[l]), int(v[l ^ bit])
+            first, second = (partner, own) if l & bit else (own, partner)
+            assert (int(out[row, l]), int(out[row + 1, l])) == (first, second), (l, bit)
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
