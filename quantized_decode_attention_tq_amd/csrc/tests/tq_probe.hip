@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "tq_bits.h"
+#include "tq_wave.h"
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -213,6 +214,18 @@ __global__ void permlane_kernel(const uint32_t* in, uint32_t* out) {
   out[192 + l] = c[1];
 }
 
+// one wave64 per 64 inputs: out[0..63], [64..127], [128..191] = the wave
+// sum, the wave maximum and the inclusive prefix sum of the wave's inputs
+// as each lane holds them (the decode's work search builds on these)
+__global__ void wave_ops_kernel(const int32_t* in, int32_t* out) {
+  const int l = threadIdx.x;
+  const int v = in[64 * blockIdx.x + l];
+  int32_t* o = out + 192 * blockIdx.x;
+  o[l] = tq::wave_sum_i(v);
+  o[64 + l] = tq::wave_max_i(v);
+  o[128 + l] = tq::wave_incl_scan_i(v);
+}
+
 int finish() {
   if (hipGetLastError() != hipSuccess) return -8;
   return hipDeviceSynchronize() == hipSuccess ? 0 : -8;
@@ -244,6 +257,13 @@ int tq_probe_mfma_16x16x32_f16(const uint32_t* a, const uint32_t* b, float* d) {
 // one wave64: a, b device [64][2] dwords, d device [64][4] floats
 int tq_probe_mfma_16x16x16_f16(const uint32_t* a, const uint32_t* b, float* d) {
   hipLaunchKernelGGL(mfma16_kernel, dim3(1), dim3(64), 0, 0, a, b, d);
+  return finish();
+}
+
+// waves wave64s: in device [64 * waves] int32, out device [192 * waves] int32
+int tq_probe_wave_ops(const int32_t* in, int32_t* out, int waves) {
+  if (waves <= 0) return -1;
+  hipLaunchKernelGGL(wave_ops_kernel, dim3(waves), dim3(64), 0, 0, in, out);
   return finish();
 }
 

@@ -38,6 +38,7 @@
 #include "tq.h"
 #include "tq_bits.h"
 #include "tq_internal.h"
+#include "tq_wave.h"
 
 namespace {
 
@@ -1174,25 +1175,9 @@ __device__ __forceinline__ void query_operand(const DecodeArgs& a, const QueryRa
 
 // ---- length-balanced units ----
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan_i(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
+using tq::wave_incl_scan_i;
+using tq::wave_max_i;
+using tq::wave_sum_i;
 
 struct UnitRange {
   int b;                 // sequence of the unit, -1 if the unit is idle
@@ -1265,20 +1250,21 @@ __device__ __forceinline__ UnitRange find_unit(const int32_t* __restrict__ seq_l
     const int t = b0 == 0 ? tl0 : tiles_of(len);
     const int sb = (t + tau - 1) / tau;
     const int incl = wave_incl_scan_i(sb);
-    const int total = __shfl(incl, 63, 64);
+    // (lane indices below are uniform: v_readlane, no LDS crossbar)
+    const int total = __builtin_amdgcn_readlane(incl, 63);
     if (u >= b0 && u < b0 + 64) {  // table entry of sequence u
-      r.first_u = base + __shfl(incl - sb, u - b0, 64);
-      r.count_u = __shfl(sb, u - b0, 64);
+      r.first_u = base + __builtin_amdgcn_readlane(incl - sb, u - b0);
+      r.count_u = __builtin_amdgcn_readlane(sb, u - b0);
     }
     if (r.b < 0 && u < base + total) {
       const uint64_t m = __ballot(base + incl > u);
       const int lb = __builtin_ctzll(m);  // lane of the unit's sequence
-      const int first = base + __shfl(incl - sb, lb, 64);
-      const int nsb = __shfl(sb, lb, 64);
-      const int tb = __shfl(t, lb, 64);
+      const int first = base + __builtin_amdgcn_readlane(incl - sb, lb);
+      const int nsb = __builtin_amdgcn_readlane(sb, lb);
+      const int tb = __builtin_amdgcn_readlane(t, lb);
       const int chunk = (tb + nsb - 1) / nsb;
       r.b = b0 + lb;
-      r.len = __shfl(len, lb, 64);
+      r.len = __builtin_amdgcn_readlane(len, lb);
       r.t_begin = min((u - first) * chunk, tb);
       r.t_end = min(r.t_begin + chunk, tb);
     }

@@ -29,6 +29,7 @@ def lib():
                        ("tq_probe_mfma_16x16x16_f16", [vp, vp, vp]),
                        ("tq_probe_cvt_fp8_f16", [vp, vp, ctypes.c_int]),
                        ("tq_probe_permlane_swap", [vp, vp]),
+                       ("tq_probe_wave_ops", [vp, vp, ctypes.c_int]),
                        ("tq_probe_fp8_encode", [vp, vp, ctypes.c_int]),
                        ("tq_probe_stream_read", [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]),
                        ("tq_probe_copy", [vp, vp, ctypes.c_int64, ctypes.c_int, vp]),

@@ -120,6 +120,30 @@ def test_permlane_swaps_pair_each_lane_with_its_partner():
             assert (int(out[row, l]), int(out[row + 1, l])) == (first, second), (l, bit)
 
 
+def test_wave_reductions_and_scan():
+    """The decode's work search reduces and scans across the 64 lanes of a
+    wave with DPP row operations and the row swaps: every lane gets the
+    wave's sum and maximum, and lane l the sum of lanes 0..l."""
+    import torch
+
+    waves = 64
+    x = RNG.integers(-(2 ** 20), 2 ** 20, (waves, 64)).astype(np.int32)
+    x[0] = np.arange(64)  # a ramp
+    x[1] = 0
+    x[1, 63] = 5  # only the last lane
+    x[2] = -7  # all equal, negative
+    x[3] = RNG.integers(0, 1100, 64)  # work-search sized values
+    din = torch.from_numpy(x.ravel()).cuda()
+    dout = torch.zeros(192 * waves, dtype=torch.int32, device="cuda")
+    print("probe wave ops", flush=True)
+    assert probe.lib().tq_probe_wave_ops(din.data_ptr(), dout.data_ptr(), waves) == 0
+    out = dout.cpu().numpy().reshape(waves, 3, 64).astype(np.int64)
+    xs = x.astype(np.int64)
+    np.testing.assert_array_equal(out[:, 0], np.repeat(xs.sum(1, keepdims=True), 64, 1))
+    np.testing.assert_array_equal(out[:, 1], np.repeat(xs.max(1, keepdims=True), 64, 1))
+    np.testing.assert_array_equal(out[:, 2], np.cumsum(xs, 1))
+
+
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_hardware_fp8_encode_matches_software_encoder(kind):
     """The store kernel encodes FP8 keys with the hardware convert after
