@@ -1066,10 +1066,24 @@ __device__ __forceinline__ void query_load(const DecodeArgs& a, int b, int hk, i
       for (int k = 0; k < 4; ++k) {
         const int d0 = 128 * hh + 32 * q4 + 8 * k;
         r.w[4 * hh + k] = *reinterpret_cast<const u32x4a4*>(qrow + d0);
+      }
+    }
+  }
+}
+
+// MSE keys: the rotation signs of the lane's dims (the same for every unit,
+// so they are loaded before the unit search)
+template <int P>
+__device__ __forceinline__ void query_signs(const DecodeArgs& a, int q4, QueryRaw<P>& r) {
+  if constexpr (Preset<P>::kFp8 == 0) {
+#pragma unroll
+    for (int hh = 0; hh < Preset<P>::kNh; ++hh)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d0 = 128 * hh + 32 * q4 + 8 * k;
         r.s[2 * (4 * hh + k)] = *reinterpret_cast<const f32x4*>(a.signs + d0);
         r.s[2 * (4 * hh + k) + 1] = *reinterpret_cast<const f32x4*>(a.signs + d0 + 4);
       }
-    }
   }
 }
 
@@ -1327,6 +1341,8 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   // codebook values (scalar loads, so that no wait on vector memory covers
   // them); the tables built from these wait until the first tiles are in flight.
   const int l0 = lane < a.batch ? a.seq_lens[lane] : 0;
+  QueryRaw<P> qraw;
+  query_signs<P>(a, q4, qraw);
   const cfloat* cen = (const cfloat*)(a.centroids);
   constexpr int kNk = T::kFp8 ? 0 : (1 << T::kKb), kNv = T::kVlm ? (1 << T::kVb) : 0;
   float ck[kNk > 0 ? kNk : 1], cv[kNv > 0 ? kNv : 1];
@@ -1369,7 +1385,6 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
     return;
   }
   // the query words: issued now, resident before the first tile loads go out
-  QueryRaw<P> qraw;
   query_load<P>(a, b, hk, h0, hl < geff, hl, q4, qraw);
 
   // ---- tile image geometry ----
