@@ -162,13 +162,15 @@ def test_decode_ragged_lengths_balanced_units(preset, S):
     G.check_decode(out, lse, ref, rlse, _rows(w))
 
 
-def test_decode_many_sequences():
+@pytest.mark.parametrize("preset,Hk,g", [("turboquant_k3v4_nc", 1, 2), ("turboquant_k8v4", 8, 4),
+                                         ("turboquant_3bit_nc", 8, 5)])
+def test_decode_many_sequences(preset, Hk, g):
     """More than 64 sequences: the unit search scans the lengths in several
-    64-wide passes."""
+    64-wide passes (8 KV heads: the fixed-geometry kernels)."""
     rng = np.random.default_rng(11)
     lens = [int(x) for x in rng.integers(0, 90, 150)]
-    w = _small("turboquant_k3v4_nc", lens, Hq=2, Hk=1, bs=32, seed=12)
-    G.log("decode 150 sequences")
+    w = _small(preset, lens, Hq=Hk * g, Hk=Hk, bs=32, seed=12)
+    G.log(f"decode 150 sequences {preset} Hk={Hk} g={g}")
     c = G.DecodeCase(w)
     import torch
 
