@@ -179,6 +179,26 @@ def test_decode_many_sequences(preset, Hk, g):
     G.check_decode(out, lse, ref, rlse, _rows(w))
 
 
+@pytest.mark.parametrize("preset,lens,S", [
+    ("turboquant_k8v4", [1200, 40, 700, 16, 0, 333, 1600, 90] * 4, 8),
+    ("turboquant_3bit_nc", [2048, 17, 900, 1500, 64, 300, 1, 1100] * 3, 8),
+    ("turboquant_k3v4_nc", [4000, 100, 2500, 700] * 2, 32),
+])
+def test_ragged_units_cover_every_tile(preset, lens, S):
+    """Ragged batches on the fixed-geometry kernels (8 KV heads): every unit of
+    the length-balanced split is computed and merged.  A workspace filled
+    with 0xFF (NaN partial rows) leaves any unit that no workgroup wrote as
+    NaN in the output."""
+    w = _small(preset, lens, Hq=8 * 4, Hk=8, bs=16, seed=90 + S)
+    G.log(f"ragged pairing {preset} B={len(lens)} S={S}")
+    c = G.DecodeCase(w)
+    import torch
+
+    out, lse = c.gpu_decode_two_stage(torch.from_numpy(c.cache_o).cuda(), S, workspace_fill=0xFF)
+    ref, rlse = c.oracle_decode()
+    G.check_decode(out, lse, ref, rlse, _rows(w))
+
+
 @pytest.mark.parametrize("preset,Hk,g", [
     ("turboquant_4bit_nc", 1, 4),     # one head: 8 phase waves
     ("turboquant_k8v4", 3, 2),        # contiguous group of 3 heads, 2 phases
