@@ -1337,9 +1337,10 @@ __device__ __forceinline__ void stage1_body(DecodeArgs a, const float vgate) {
   const int hk = hgp * G + hh;
   const int hl = lane & 15, q4 = lane >> 4;
 
-  // The lengths go out first (the unit search waits on them), then the
-  // codebook values (scalar loads, so that no wait on vector memory covers
-  // them); the tables built from these wait until the first tiles are in flight.
+  // The lengths go out first (the unit search waits on them), then what no
+  // unit changes: the rotation signs of the lane's dims and the codebook
+  // values (scalar loads, so that no wait on vector memory covers them); the
+  // tables built from these wait until the first tiles are in flight.
   const int l0 = lane < a.batch ? a.seq_lens[lane] : 0;
   QueryRaw<P> qraw;
   query_signs<P>(a, q4, qraw);
