@@ -87,3 +87,23 @@ def test_sparse_v_gate_head256(preset):
     w = _w(preset, [700, 1300], 8, 2, 16, seed=8, D=256)
     G.log(f"sparse-V D=256 {preset}")
     _run(w, 2)
+
+
+@pytest.mark.timeout(240)
+@pytest.mark.parametrize("i", range(0, 96, 4))
+def test_gate_on_random_configurations(i):
+    """The gated kernels on the seeded random configurations of the random
+    parity suite (every fourth: each preset twice, both block conventions,
+    ragged lengths, windows, sinks): the same bound against exact attention
+    on the oracle's cache bytes."""
+    import torch
+
+    from test_gpu_random_shapes import _draw
+
+    w, layout, S, window, sinks, _ = _draw(i)
+    G.log(f"gated random case {i}: {w.preset} D={w.head_dim} Hk={w.num_kv_heads} Hq={w.num_q_heads} "
+          f"bs={w.block_size} {layout} lens={list(w.lens)} S={S} window={window} sinks={sinks is not None}")
+    c = G.DecodeCase(w, block_layout=layout)
+    cache = torch.from_numpy(c.oracle_cache_bytes()).cuda()
+    out, lse = c.gpu_decode(cache, S, sliding_window=window, sinks=sinks, value_gate=GATE)
+    _check_gated(c, out, lse, window, sinks)
