@@ -172,3 +172,24 @@ def test_dequant_long_prefix_sampled(preset):
             Kd = Kd @ R
         _check(k_np[i][None], Kd[None], "f32", exact=lay.key_fp8)
         _check(v_np[i][None], Vd[None], "f32")
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_dequant_random_configurations(i):
+    """Seeded random configurations: preset (each three times), head_dim,
+    KV heads, block size, block convention, prefix length (one-token and
+    block-edge prefixes included), output dtype; the parity bars above."""
+    rng = np.random.default_rng(3000 + i)
+    preset = list(O.PRESETS)[i % len(O.PRESETS)]
+    d = 256 if rng.random() < 0.25 else 128
+    Hk = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    bs = int(rng.choice([16, 32, 64, 128]))
+    n = int(rng.choice([1, bs - 1, bs, bs + 1, int(rng.integers(2, 700)), int(rng.integers(2, 700))]))
+    out = str(rng.choice(["f16", "bf16", "f32"]))
+    layout = "soa" if rng.random() < 0.4 and (Hk <= 8 or Hk % 8 == 0) else "aos"
+    G.log(f"dequant random {i}: {preset} D={d} Hk={Hk} bs={bs} n={n} {out} {layout}")
+    lay, cache, table, s, c32 = _cache(preset, n, Hk, bs, seed=4000 + i, D=d)
+    k, v = _gpu(preset, cache, table, n, s, out, D=d, block_layout=layout)
+    kw, vw = _oracle(lay, cache, table, n, s, c32)
+    _check(k, kw, out, exact=lay.key_fp8)
+    _check(v, vw, out)
